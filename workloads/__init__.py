@@ -1,0 +1,287 @@
+"""Seeded synthetic inputs for batched speculative-decoding verification.
+
+This module only *draws* inputs.  It holds none of the verifier's arithmetic
+(no acceptance test, no residual, no row statistics of the verifier); both the
+HIP path and the CPU oracle consume the arrays it returns, bit for bit.
+
+What the inputs stand in for
+----------------------------
+The pages measure end-to-end decoding of real models (Qwen3-4B/8B, K=7) on
+public benchmarks ("DLite" reading notes, section 3 and Tables 1-4).  Neither
+the weights nor the datasets are available, so these generators produce logits
+of the same *shape* (Qwen3 vocabulary, V=151936; draft length K=7) with simple
+seeded distributions, and draft tokens/trees with a controlled agreement rate.
+
+Workloads (``CONFIGS``)
+-----------------------
+1. sample, B=1, K=4, V=1000, fp32, T=1.0: Lp ~ N(0, 2^2), Lq = Lp + N(0, 0.5^2).
+2. sample, B=32, K=7, V=151936, bf16, T=1.0: Lp ~ N(0, 3^2) with +8 added at 20
+   distinct random ids per row; Lq = Lp + N(0, 1^2).
+3. sample, B=256, K=7, V=151936, bf16, T=0.7: Lp as in 2; per request a noise
+   level sigma_b ~ U(0.1, 3.0); Lq = Lp + N(0, sigma_b^2).
+4. greedy, B=512 (also run at B=256), K=7, V=151936, bf16: Lt ~ N(0, 3^2); the
+   draft for position i+1 equals argmax(row i) with probability 0.8, else a
+   uniform vocabulary id.
+5. tree, B=64, N=33, V=151936, bf16: Lt ~ N(0, 3^2); the AdaPLD-shaped tree of
+   a root, an 8-node main copy path, 12 root branches each with one successor,
+   and 0-3 extra leaves per request; a node's token equals argmax(parent row)
+   with probability 0.7, else a uniform id.
+
+In the sampling workloads the draft tokens are drawn from softmax(Lq/T) of the
+*stored* (rounded) draft logits with the Gumbel-max trick, so the stored q is
+the true proposal distribution.  The verifier's uniforms are drawn as one
+(B, K+1, 2) float32 array in [0, 1): ``[..., :K, 0]`` are the acceptance draws
+and ``[..., :, 1]`` the residual/bonus draws (``[b, K, 0]`` is never used).
+
+Logits are drawn in float32 and rounded to bfloat16 with round-to-nearest-even
+(torch's CPU conversion).  bf16 arrays are returned as ``uint16`` bit patterns.
+
+Seeding: workload ``c`` uses ``numpy.random.SeedSequence(20261202 + c)`` (or the
+caller's seed) spawned into independent streams, further split per block of 64
+rows so the result does not depend on the thread count.
+"""
+
+from __future__ import annotations
+
+import os
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass, field
+
+import numpy as np
+
+VOCAB_QWEN3 = 151936
+BLOCK_ROWS = 64
+
+# Stream indices spawned from each workload's SeedSequence.
+_S_TARGET, _S_SPIKES, _S_NOISE, _S_DRAFTS, _S_UNIF, _S_TREE = range(6)
+
+
+@dataclass
+class Workload:
+    """One seeded batch of verifier inputs (host arrays)."""
+
+    mode: str                       # "sample" | "greedy" | "tree"
+    B: int
+    V: int
+    dtype: str                      # "f32" | "bf16"
+    K: int = 0                      # chain draft length
+    N: int = 0                      # tree nodes
+    T: float = 1.0
+    target: np.ndarray = None       # [B, K+1, V] or [B, N, V]; float32 or uint16 (bf16 bits)
+    draft: np.ndarray = None        # [B, K, V] (sample mode)
+    draft_tokens: np.ndarray = None  # [B, K] int32
+    u_accept: np.ndarray = None     # [B, K] float32
+    u_sample: np.ndarray = None     # [B, K+1] float32
+    node_tokens: np.ndarray = None  # [B, N] int32
+    parents: np.ndarray = None      # [B, N] int32
+    meta: dict = field(default_factory=dict)
+
+    def rows(self) -> int:
+        """Target rows verified per call: B*(K+1) for chains, B*N for trees."""
+        return self.B * (self.N if self.mode == "tree" else self.K + 1)
+
+
+CONFIGS = {
+    1: dict(mode="sample", B=1, K=4, V=1000, dtype="f32", T=1.0),
+    2: dict(mode="sample", B=32, K=7, V=VOCAB_QWEN3, dtype="bf16", T=1.0),
+    3: dict(mode="sample", B=256, K=7, V=VOCAB_QWEN3, dtype="bf16", T=0.7),
+    4: dict(mode="greedy", B=512, K=7, V=VOCAB_QWEN3, dtype="bf16"),
+    5: dict(mode="tree", B=64, N=33, V=VOCAB_QWEN3, dtype="bf16"),
+}
+
+
+def _threads() -> int:
+    n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round float32 to bfloat16 (round-to-nearest-even); return uint16 bits."""
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Exact widening of bf16 bit patterns to float32."""
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def _normal_rows(seed: np.random.SeedSequence, rows: int, V: int, sigma, out: np.ndarray):
+    """Fill out[rows, V] (float32) with N(0, sigma^2); sigma scalar or per-row array."""
+    nblk = (rows + BLOCK_ROWS - 1) // BLOCK_ROWS
+    seeds = seed.spawn(nblk)
+    sig = np.broadcast_to(np.asarray(sigma, dtype=np.float32), (rows,))
+
+    def job(k):
+        r0, r1 = k * BLOCK_ROWS, min(rows, (k + 1) * BLOCK_ROWS)
+        blk = out[r0:r1]
+        np.random.default_rng(seeds[k]).standard_normal(dtype=np.float32, out=blk)
+        blk *= sig[r0:r1, None]
+
+    with ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(job, range(nblk)))
+
+
+def _add_spikes(seed, rows_f32: np.ndarray, count: int, height: float):
+    """Add `height` at `count` distinct uniformly chosen ids of every row."""
+    rng = np.random.default_rng(seed)
+    R, V = rows_f32.shape
+    for r in range(R):
+        ids = np.unique(rng.integers(0, V, size=count))
+        while ids.size < count:
+            ids = np.unique(np.concatenate([ids, rng.integers(0, V, size=count - ids.size)]))
+        rows_f32[r, ids] += np.float32(height)
+
+
+def _gumbel_draws(seed, logits_f32: np.ndarray, T: float) -> np.ndarray:
+    """One draw per row from softmax(logits/T) via argmax(logits/T + Gumbel)."""
+    rows = logits_f32.shape[0]
+    nblk = (rows + BLOCK_ROWS - 1) // BLOCK_ROWS
+    seeds = seed.spawn(nblk)
+    out = np.empty(rows, dtype=np.int32)
+
+    def job(k):
+        r0, r1 = k * BLOCK_ROWS, min(rows, (k + 1) * BLOCK_ROWS)
+        rng = np.random.default_rng(seeds[k])
+        for r in range(r0, r1):
+            g = -np.log(rng.standard_exponential(logits_f32.shape[1]))
+            out[r] = int(np.argmax(logits_f32[r].astype(np.float64) / T + g))
+
+    with ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(job, range(nblk)))
+    return out
+
+
+def _uniforms(seed, B: int, K: int):
+    u = np.random.default_rng(seed).random((B, K + 1, 2), dtype=np.float32)
+    return np.ascontiguousarray(u[:, :K, 0]), np.ascontiguousarray(u[:, :, 1])
+
+
+def _stored(a_f32: np.ndarray, dtype: str) -> np.ndarray:
+    return to_bf16_bits(a_f32) if dtype == "bf16" else np.ascontiguousarray(a_f32, np.float32)
+
+
+def _as_f32(stored: np.ndarray, dtype: str) -> np.ndarray:
+    return bf16_bits_to_f32(stored) if dtype == "bf16" else stored
+
+
+def make_sample(B, K, V, dtype="bf16", T=1.0, target_sigma=3.0, spikes=20, spike_height=8.0,
+                noise_sigma=1.0, noise_sigma_range=None, seed=0) -> Workload:
+    """Stochastic-chain inputs: target [B,K+1,V], draft [B,K,V], drafts ~ softmax(Lq/T)."""
+    ss = seed if isinstance(seed, np.random.SeedSequence) else np.random.SeedSequence(seed)
+    st = ss.spawn(6)
+    tgt = np.empty((B * (K + 1), V), dtype=np.float32)
+    _normal_rows(st[_S_TARGET], tgt.shape[0], V, target_sigma, tgt)
+    if spikes:
+        _add_spikes(st[_S_SPIKES], tgt, spikes, spike_height)
+    tgt = tgt.reshape(B, K + 1, V)
+    nrng = st[_S_NOISE].spawn(2)
+    if noise_sigma_range is not None:
+        lo, hi = noise_sigma_range
+        sig_b = np.random.default_rng(nrng[0]).uniform(lo, hi, size=B).astype(np.float32)
+    else:
+        sig_b = np.full(B, noise_sigma, dtype=np.float32)
+    dr = np.empty((B * K, V), dtype=np.float32)
+    _normal_rows(nrng[1], B * K, V, np.repeat(sig_b, K), dr)
+    dr = dr.reshape(B, K, V)
+    dr += tgt[:, :K, :]
+    del_tgt = _stored(tgt, dtype)
+    del tgt
+    stored_dr = _stored(dr, dtype)
+    del dr
+    drafts = _gumbel_draws(st[_S_DRAFTS], _as_f32(stored_dr.reshape(B * K, V), dtype), T)
+    ua, us = _uniforms(st[_S_UNIF], B, K)
+    return Workload(mode="sample", B=B, K=K, V=V, dtype=dtype, T=float(T), target=del_tgt,
+                    draft=stored_dr, draft_tokens=drafts.reshape(B, K), u_accept=ua,
+                    u_sample=us, meta=dict(sigma_b=sig_b))
+
+
+def _argmax_rows(rows_f32: np.ndarray) -> np.ndarray:
+    """numpy.argmax per row (first occurrence of the maximum)."""
+    return np.argmax(rows_f32, axis=-1).astype(np.int32)
+
+
+def make_greedy(B, K, V, dtype="bf16", sigma=3.0, p_match=0.8, seed=0) -> Workload:
+    """Greedy-chain inputs: target [B,K+1,V]; draft i+1 = argmax(row i) w.p. p_match."""
+    ss = seed if isinstance(seed, np.random.SeedSequence) else np.random.SeedSequence(seed)
+    st = ss.spawn(6)
+    tgt = np.empty((B * (K + 1), V), dtype=np.float32)
+    _normal_rows(st[_S_TARGET], tgt.shape[0], V, sigma, tgt)
+    stored = _stored(tgt, dtype)
+    del tgt
+    am = _argmax_rows(_as_f32(stored, dtype)).reshape(B, K + 1)
+    rng = np.random.default_rng(st[_S_DRAFTS])
+    hit = rng.random((B, K)) < p_match
+    rnd = rng.integers(0, V, size=(B, K), dtype=np.int64).astype(np.int32)
+    drafts = np.where(hit, am[:, :K], rnd).astype(np.int32)
+    return Workload(mode="greedy", B=B, K=K, V=V, dtype=dtype, target=stored.reshape(B, K + 1, V),
+                    draft_tokens=drafts, meta=dict(argmax=am))
+
+
+def adapld_parents(extra: int, n_main: int = 8, n_branch: int = 12, rng=None) -> np.ndarray:
+    """Parent array of an AdaPLD-shaped draft tree (topologically ordered).
+
+    Node 0 is the root, nodes 1..n_main the main copy path, then n_branch
+    branches under the root, then one successor per branch.  The last `extra`
+    successor slots become extra leaves whose parent is drawn uniformly among
+    the earlier nodes (root included).
+    """
+    N = 1 + n_main + 2 * n_branch
+    par = np.empty(N, dtype=np.int32)
+    par[0] = -1
+    for k in range(1, n_main + 1):
+        par[k] = k - 1
+    b0 = 1 + n_main
+    for k in range(n_branch):
+        par[b0 + k] = 0
+        par[b0 + n_branch + k] = b0 + k
+    for e in range(extra):
+        slot = N - 1 - e
+        par[slot] = int(rng.integers(0, slot))
+    return par
+
+
+def make_tree(B, V, dtype="bf16", sigma=3.0, p_match=0.7, n_main=8, n_branch=12,
+              max_extra=3, seed=0) -> Workload:
+    """Greedy-tree inputs: target [B,N,V]; node token = argmax(parent row) w.p. p_match."""
+    ss = seed if isinstance(seed, np.random.SeedSequence) else np.random.SeedSequence(seed)
+    st = ss.spawn(6)
+    N = 1 + n_main + 2 * n_branch
+    rng = np.random.default_rng(st[_S_TREE])
+    parents = np.stack([adapld_parents(int(rng.integers(0, max_extra + 1)), n_main, n_branch, rng)
+                        for _ in range(B)])
+    tgt = np.empty((B * N, V), dtype=np.float32)
+    _normal_rows(st[_S_TARGET], tgt.shape[0], V, sigma, tgt)
+    stored = _stored(tgt, dtype)
+    del tgt
+    am = _argmax_rows(_as_f32(stored, dtype)).reshape(B, N)
+    hit = rng.random((B, N)) < p_match
+    rnd = rng.integers(0, V, size=(B, N), dtype=np.int64).astype(np.int32)
+    par_am = np.take_along_axis(am, np.maximum(parents, 0), axis=1)
+    tok = np.where(hit, par_am, rnd).astype(np.int32)
+    tok[:, 0] = rnd[:, 0]
+    return Workload(mode="tree", B=B, N=N, V=V, dtype=dtype, target=stored.reshape(B, N, V),
+                    node_tokens=tok, parents=parents, meta=dict(argmax=am))
+
+
+def make_config(c: int, seed=None, B=None) -> Workload:
+    """Workload c (1..5) of ``CONFIGS``; `B` overrides the batch (e.g. 256 for workload 4)."""
+    cfg = dict(CONFIGS[c])
+    ss = np.random.SeedSequence(20261202 + c if seed is None else seed)
+    if B is not None:
+        cfg["B"] = B
+    if c == 1:
+        return make_sample(cfg["B"], cfg["K"], cfg["V"], "f32", 1.0, target_sigma=2.0, spikes=0,
+                           noise_sigma=0.5, seed=ss)
+    if c == 2:
+        return make_sample(cfg["B"], cfg["K"], cfg["V"], "bf16", 1.0, noise_sigma=1.0, seed=ss)
+    if c == 3:
+        return make_sample(cfg["B"], cfg["K"], cfg["V"], "bf16", 0.7,
+                           noise_sigma_range=(0.1, 3.0), seed=ss)
+    if c == 4:
+        return make_greedy(cfg["B"], cfg["K"], cfg["V"], "bf16", seed=ss)
+    if c == 5:
+        return make_tree(cfg["B"], cfg["V"], "bf16", seed=ss)
+    raise ValueError(f"unknown workload {c}")
