@@ -1,0 +1,322 @@
+#!/usr/bin/env python3
+"""Throughput of batched speculative-decoding verification on one MI355X.
+
+One step = one pass of the whole verification path over one batch of seeded
+synthetic inputs (Qwen3-vocabulary-shaped logits, V = 151936, bf16, K = 7):
+
+  * stochastic chain: spec_verify_sample on B=256, K=7, T=0.7 (per-request
+    draft noise sigma ~ U(0.1, 3.0), so acceptance runs from near 1 to near 0);
+  * greedy chain:     spec_verify_greedy on B=256, K=7 (drafts match the target
+    argmax with probability 0.8);
+  * greedy tree:      spec_verify_tree on B=64 AdaPLD-shaped 33-node trees.
+
+value = target rows verified per second over the whole step
+(B*(K+1) + B*(K+1) + B*N = 6208 rows per step).  Inputs are resident in HBM
+before timing starts; outputs and workspaces are preallocated.  Per-kernel
+durations come from HIP events the library records around each launch on the
+stream it launches on (sv_trace_begin/sv_trace_end), over the timed steps.
+
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--mode all|sample|greedy|tree]
+                       [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "verified draft rows/sec + achieved HBM GB/s (% of peak), B=256 K=7 V=151936"
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, vendor figure
+KERNEL_SOURCES = {
+    "rowstats": ["draft_token_verification_04_amd/csrc/sv_sample.hip",
+                 "draft_token_verification_04_amd/csrc/sv_device.hpp",
+                 "draft_token_verification_04_amd/csrc/sv_internal.hpp"],
+    "argmax": ["draft_token_verification_04_amd/csrc/sv_greedy.hip",
+               "draft_token_verification_04_amd/csrc/sv_device.hpp",
+               "draft_token_verification_04_amd/csrc/sv_internal.hpp"],
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--mode", choices=("all", "sample", "greedy", "tree"), default="all")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (default: up to 16)")
+    return ap.parse_args()
+
+
+def source_hash(kernel: str) -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES.get(kernel, []):
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(kernel: str):
+    """HBM bytes per launch measured with rocprofv3 counters (profiles/traffic.json),
+    used only while the kernel's source is unchanged since the measurement."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f).get(kernel)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha") != source_hash(kernel):
+        return None
+    return rec
+
+
+class Calls:
+    """Preallocated device buffers and ctypes calls for one step."""
+
+    def __init__(self, sv, torch, w3, w4, w5, dev):
+        self.sv, self.torch, self.dev = sv, torch, dev
+        lib = sv.load_library()
+        self.lib = lib
+
+        def logits(a):
+            import numpy as np
+
+            if a.dtype == np.uint16:
+                return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+            return torch.from_numpy(a).to(dev)
+
+        def ints(a):
+            return torch.from_numpy(a).to(dev)
+
+        i32 = dict(dtype=torch.int32, device=dev)
+        f32 = dict(dtype=torch.float32, device=dev)
+        self.w3, self.w4, self.w5 = w3, w4, w5
+        # stochastic chain
+        self.s_t, self.s_d = logits(w3.target), logits(w3.draft)
+        self.s_x, self.s_ua, self.s_us = ints(w3.draft_tokens), ints(w3.u_accept), ints(w3.u_sample)
+        B, K, V = w3.B, w3.K, w3.V
+        self.s_n = torch.empty(B, **i32)
+        self.s_tok = torch.empty((B, K + 1), **i32)
+        self.s_lt = torch.empty((B, K + 1), **f32)
+        self.s_ld = torch.empty((B, K), **f32)
+        self.s_st = torch.empty(B, **i32)
+        nb = lib.sv_sample_workspace_bytes(B, K, V, sv.SV_BF16)
+        self.s_ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+        # greedy chain
+        self.g_t, self.g_x = logits(w4.target), ints(w4.draft_tokens)
+        self.g_n = torch.empty(w4.B, **i32)
+        self.g_tok = torch.empty((w4.B, w4.K + 1), **i32)
+        self.g_st = torch.empty(w4.B, **i32)
+        nb = lib.sv_greedy_workspace_bytes(w4.B, w4.K + 1, w4.V, sv.SV_BF16)
+        self.g_ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+        # greedy tree
+        self.t_t, self.t_tok, self.t_par = logits(w5.target), ints(w5.node_tokens), ints(w5.parents)
+        self.t_n = torch.empty(w5.B, **i32)
+        self.t_path = torch.empty((w5.B, w5.N), **i32)
+        self.t_out = torch.empty((w5.B, w5.N), **i32)
+        self.t_st = torch.empty(w5.B, **i32)
+        nb = lib.sv_greedy_workspace_bytes(w5.B, w5.N, w5.V, sv.SV_BF16)
+        self.t_ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+        self.stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+        P = lambda t: ctypes.c_void_p(t.data_ptr())
+        self.sample_args = (P(self.s_t), P(self.s_d), P(self.s_x), P(self.s_ua), P(self.s_us), B, K, V,
+                            sv.SV_BF16, ctypes.c_float(w3.T), P(self.s_n), P(self.s_tok), P(self.s_lt),
+                            P(self.s_ld), P(self.s_st), P(self.s_ws), self.s_ws.numel(), self.stream)
+        self.greedy_args = (P(self.g_t), P(self.g_x), w4.B, w4.K, w4.V, sv.SV_BF16, P(self.g_n),
+                            P(self.g_tok), P(self.g_st), P(self.g_ws), self.g_ws.numel(), self.stream)
+        self.tree_args = (P(self.t_t), P(self.t_tok), P(self.t_par), w5.B, w5.N, w5.V, sv.SV_BF16,
+                          P(self.t_n), P(self.t_path), P(self.t_out), P(self.t_st), P(self.t_ws),
+                          self.t_ws.numel(), self.stream)
+
+    def sample(self):
+        rc = self.lib.spec_verify_sample(*self.sample_args)
+        if rc:
+            raise RuntimeError(f"spec_verify_sample failed: {rc}")
+
+    def greedy(self):
+        rc = self.lib.spec_verify_greedy(*self.greedy_args)
+        if rc:
+            raise RuntimeError(f"spec_verify_greedy failed: {rc}")
+
+    def tree(self):
+        rc = self.lib.spec_verify_tree(*self.tree_args)
+        if rc:
+            raise RuntimeError(f"spec_verify_tree failed: {rc}")
+
+
+def cpu_baseline(w3, w4, w5, mode, threads):
+    """The oracle, as it stands, on the same step's inputs (wall time, median of 3)."""
+    import oracle
+
+    times = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        if mode in ("all", "sample"):
+            oracle.verify_sample(w3.target, w3.draft, w3.draft_tokens, w3.u_accept, w3.u_sample, w3.T,
+                                 threads=threads)
+        if mode in ("all", "greedy"):
+            oracle.verify_greedy(w4.target, w4.draft_tokens, threads=threads)
+        if mode in ("all", "tree"):
+            oracle.verify_tree(w5.target, w5.node_tokens, w5.parents, threads=threads)
+        times.append(time.perf_counter() - t0)
+    return statistics.median(times)
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: verification shards over requests with no "
+              "exchange, so there is no multi-GPU step to time (use --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import __graft_entry__
+    import draft_token_verification_04_amd as sv
+    import workloads
+
+    __graft_entry__._ensure_built()
+    if not torch.cuda.is_available():
+        raise RuntimeError("bench.py needs a GPU")
+    dev = torch.device("cuda:0")
+
+    t_gen = time.perf_counter()
+    w3 = workloads.make_config(3)
+    w4 = workloads.make_config(4, B=256)
+    w5 = workloads.make_config(5)
+    print(f"[bench] inputs generated in {time.perf_counter() - t_gen:.1f}s", file=sys.stderr, flush=True)
+    calls = Calls(sv, torch, w3, w4, w5, dev)
+    parts = {"sample": calls.sample, "greedy": calls.greedy, "tree": calls.tree}
+    active = list(parts) if args.mode == "all" else [args.mode]
+
+    def step():
+        for m in active:
+            parts[m]()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    sv.trace_begin(max(64, args.steps * 8 + 16))
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    recs = sv.trace_end(args.steps * 8 + 16)
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    per_kernel = {}
+    for name, ms in recs:
+        per_kernel.setdefault(name, []).append(ms)
+    kmean = {k: statistics.mean(v) for k, v in per_kernel.items()}
+
+    R = w3.V * 2  # bytes of one bf16 row
+    n3 = calls.s_n.cpu().numpy()
+    resid_rows = int(np.sum(np.where(n3 < w3.K, 2, 1)))
+    bytes_mode = {
+        "sample": (w3.B * (2 * w3.K + 1) + resid_rows) * R,
+        "greedy": w4.B * (w4.K + 1) * R,
+        "tree": w5.B * w5.N * R,
+    }
+    rows_mode = {"sample": w3.B * (w3.K + 1), "greedy": w4.B * (w4.K + 1), "tree": w5.B * w5.N}
+    kernels_mode = {"sample": ["rowstats", "accept", "resid_mass", "resid_select"],
+                    "greedy": ["argmax", "match"], "tree": ["argmax", "tree"]}
+    rows_step = sum(rows_mode[m] for m in active)
+    bytes_step = sum(bytes_mode[m] for m in active)
+    value = rows_step / (ms_per_step * 1e-3)
+    hbm_gbps = bytes_step / (ms_per_step * 1e-3) / 1e9
+
+    # dominant kernel: the row-statistics pass of the stochastic chain, else argmax
+    if "sample" in active:
+        dom, dom_bytes, dom_ms = "rowstats", w3.B * (2 * w3.K + 1) * R, kmean.get("rowstats")
+    else:
+        dom = "argmax"
+        dom_bytes = bytes_mode[active[0]]
+        dom_ms = statistics.mean(per_kernel["argmax"]) if "argmax" in per_kernel else None
+    roof = None
+    if dom_ms:
+        ach = dom_bytes / (dom_ms * 1e-3) / 1e9
+        tr = stored_traffic(dom)
+        roof = {"bound": "hbm", "kernel": dom, "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4),
+                "traffic": tr["bytes_per_launch"] if tr else None,
+                "bytes_per_launch": dom_bytes, "avg_launch_ms": round(dom_ms, 5)}
+    extra = {}
+    if "argmax" in per_kernel and dom != "argmax":
+        a = per_kernel["argmax"]
+        # greedy (B=256, K=7) and tree (B=64, N=33) launches alternate
+        g_ms = statistics.mean(a[0::2]) if "greedy" in active and "tree" in active else statistics.mean(a)
+        gb = bytes_mode["greedy"] if "greedy" in active else bytes_mode["tree"]
+        extra = {"kernel": "argmax", "workload": "greedy chain B=256 K=7" if "greedy" in active else "tree",
+                 "achieved": round(gb / (g_ms * 1e-3) / 1e9, 1), "unit": "GB/s",
+                 "frac": round(gb / (g_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                 "avg_launch_ms": round(g_ms, 5), "bytes_per_launch": gb}
+
+    modes = {}
+    for m in active:
+        ks = kernels_mode[m]
+        if m == "greedy" and "tree" in active:
+            kt = statistics.mean(per_kernel["argmax"][0::2]) + kmean.get("match", 0.0)
+        elif m == "tree" and "greedy" in active:
+            kt = statistics.mean(per_kernel["argmax"][1::2]) + kmean.get("tree", 0.0)
+        else:
+            kt = sum(kmean.get(k, 0.0) for k in ks)
+        modes[m] = {"rows": rows_mode[m], "bytes": bytes_mode[m], "kernel_ms": round(kt, 5),
+                    "rows_per_s": round(rows_mode[m] / (kt * 1e-3), 1),
+                    "gbps": round(bytes_mode[m] / (kt * 1e-3) / 1e9, 1)}
+    if "sample" in modes:
+        modes["sample"]["mean_tokens_per_round"] = round(float(n3.mean() + 1), 4)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        threads = args.cpu_threads or max(1, min(16, os.cpu_count() or 1))
+        secs = cpu_baseline(w3, w4, w5, args.mode, threads)
+        cpu = {"value": round(rows_step / secs, 1), "unit": "rows/s", "cores": threads,
+               "kind": "oracle",
+               "sample": f"one full step ({rows_step} rows: {', '.join(active)}), median of 3 runs, "
+                         f"{secs:.2f}s wall each"}
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": ("verification step: stochastic chain B=256 K=7 V=151936 bf16 T=0.7, "
+                         "greedy chain B=256 K=7, greedy tree B=64 N=33")
+            if args.mode == "all" else f"{args.mode} only",
+            "B": 256, "K": 7, "V": 151936, "logits": "bf16", "modes": active,
+            "rows_per_step": rows_step, "bytes_per_step": bytes_step,
+        },
+        "hbm_gbps": round(hbm_gbps, 1),
+        "hbm_frac_of_peak": round(hbm_gbps / HBM_PEAK_GBPS, 4),
+        "roofline": roof,
+        "roofline_argmax": extra or None,
+        "modes": modes,
+        "kernel_ms": {k: round(v, 5) for k, v in kmean.items()},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,279 @@
+"""Python binding of libspecverify (batched speculative-decoding verification
+on MI355X).
+
+Argument marshalling only: every step of verification runs in the HIP kernels
+of ``libspecverify.so``; this module checks tensor shapes/dtypes/devices,
+allocates outputs and workspace with PyTorch, and passes raw device pointers
+and the current HIP stream through the C ABI declared in
+``include/spec_verify.h``.  There is no CPU fallback: if the library is not
+built, or no GPU is visible, calls raise.
+
+Entry points (same names as the C ABI):
+
+* ``spec_verify_sample(target, draft, draft_tokens, u_accept, u_sample, T)``
+* ``spec_verify_greedy(target, draft_tokens)``
+* ``spec_verify_tree(target, node_tokens, parents)``
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libspecverify.so")
+
+SV_OK, SV_ERR_INVALID_ARG, SV_ERR_UNSUPPORTED, SV_ERR_WORKSPACE, SV_ERR_HIP = range(5)
+SV_F32, SV_BF16 = 0, 1
+SV_MAX_TREE_NODES = 2048
+KERNELS = ("rowstats", "accept", "resid_mass", "resid_select", "argmax", "match", "tree")
+
+EXPORTS = ("sv_sample_workspace_bytes", "sv_greedy_workspace_bytes", "spec_verify_sample",
+           "spec_verify_greedy", "spec_verify_tree", "sv_status_string", "sv_version",
+           "sv_trace_begin", "sv_trace_end", "sv_kernel_name")
+
+
+class SpecVerifyError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+
+
+class KernelTime(ctypes.Structure):
+    _fields_ = [("kernel", ctypes.c_int), ("ms", ctypes.c_float)]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libspecverify.so and declare its signatures (no GPU needed)."""
+    global _lib
+    if _lib is not None and path == LIB_PATH:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run __graft_entry__.build() first")
+    lib = ctypes.CDLL(path)
+    P, I, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    lib.sv_sample_workspace_bytes.argtypes = [I, I, I, I]
+    lib.sv_sample_workspace_bytes.restype = Z
+    lib.sv_greedy_workspace_bytes.argtypes = [I, I, I, I]
+    lib.sv_greedy_workspace_bytes.restype = Z
+    lib.spec_verify_sample.argtypes = [P, P, P, P, P, I, I, I, I, ctypes.c_float, P, P, P, P, P, P, Z, P]
+    lib.spec_verify_sample.restype = I
+    lib.spec_verify_greedy.argtypes = [P, P, I, I, I, I, P, P, P, P, Z, P]
+    lib.spec_verify_greedy.restype = I
+    lib.spec_verify_tree.argtypes = [P, P, P, I, I, I, I, P, P, P, P, P, Z, P]
+    lib.spec_verify_tree.restype = I
+    lib.sv_status_string.argtypes = [I]
+    lib.sv_status_string.restype = ctypes.c_char_p
+    lib.sv_version.argtypes = []
+    lib.sv_version.restype = ctypes.c_char_p
+    lib.sv_trace_begin.argtypes = [I]
+    lib.sv_trace_begin.restype = I
+    lib.sv_trace_end.argtypes = [ctypes.POINTER(KernelTime), I]
+    lib.sv_trace_end.restype = I
+    lib.sv_kernel_name.argtypes = [I]
+    lib.sv_kernel_name.restype = ctypes.c_char_p
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    try:
+        return load_library().sv_status_string(status).decode()
+    except RuntimeError:
+        return "unknown"
+
+
+def version() -> str:
+    return load_library().sv_version().decode()
+
+
+# ---- helpers -------------------------------------------------------------------
+
+def _torch():
+    import torch
+
+    if not torch.cuda.is_available():
+        raise RuntimeError("specverify needs a ROCm GPU; none is visible")
+    return torch
+
+
+def _dtype_code(t) -> int:
+    import torch
+
+    if t.dtype == torch.bfloat16:
+        return SV_BF16
+    if t.dtype == torch.float32:
+        return SV_F32
+    raise TypeError(f"logits must be bfloat16 or float32, got {t.dtype}")
+
+
+def _check(t, name, ndim=None, dtype=None, device=None):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got shape {tuple(t.shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(torch, device, stream):
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _workspace(torch, nbytes, device, workspace):
+    if workspace is None:
+        return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+    _check(workspace, "workspace", device=device)
+    if workspace.numel() * workspace.element_size() < nbytes:
+        raise SpecVerifyError(SV_ERR_WORKSPACE, "workspace")
+    return workspace
+
+
+# ---- entry points ----------------------------------------------------------------
+
+def sample_workspace_bytes(B, K, V, dtype_code) -> int:
+    return int(load_library().sv_sample_workspace_bytes(B, K, V, dtype_code))
+
+
+def greedy_workspace_bytes(B, rows_per_req, V, dtype_code) -> int:
+    return int(load_library().sv_greedy_workspace_bytes(B, rows_per_req, V, dtype_code))
+
+
+def spec_verify_sample(target, draft, draft_tokens, u_accept, u_sample, temperature, *,
+                       lse=True, status=True, workspace=None, stream=None):
+    """Stochastic chain verification.
+
+    target [B,K+1,V] and draft [B,K,V] logits (bf16 or f32, same dtype),
+    draft_tokens [B,K] int32, u_accept [B,K] and u_sample [B,K+1] float32 in
+    [0,1).  Returns a dict with ``accept_len`` [B], ``tokens`` [B,K+1] and,
+    when requested, ``lse_target`` [B,K+1], ``lse_draft`` [B,K], ``status`` [B].
+    """
+    torch = _torch()
+    lib = load_library()
+    _check(target, "target", 3)
+    dev = target.device
+    B, K1, V = target.shape
+    K = K1 - 1
+    dt = _dtype_code(target)
+    if K > 0:
+        _check(draft, "draft", 3, target.dtype, dev)
+        if tuple(draft.shape) != (B, K, V):
+            raise ValueError(f"draft must be [{B},{K},{V}], got {tuple(draft.shape)}")
+        _check(draft_tokens, "draft_tokens", 2, torch.int32, dev)
+        _check(u_accept, "u_accept", 2, torch.float32, dev)
+        if tuple(draft_tokens.shape) != (B, K) or tuple(u_accept.shape) != (B, K):
+            raise ValueError("draft_tokens and u_accept must be [B, K]")
+    _check(u_sample, "u_sample", 2, torch.float32, dev)
+    if tuple(u_sample.shape) != (B, K + 1):
+        raise ValueError("u_sample must be [B, K+1]")
+    out = dict(accept_len=torch.empty(B, dtype=torch.int32, device=dev),
+               tokens=torch.empty((B, K + 1), dtype=torch.int32, device=dev))
+    if lse:
+        out["lse_target"] = torch.empty((B, K + 1), dtype=torch.float32, device=dev)
+        out["lse_draft"] = torch.empty((B, K), dtype=torch.float32, device=dev)
+    if status:
+        out["status"] = torch.empty(B, dtype=torch.int32, device=dev)
+    nbytes = lib.sv_sample_workspace_bytes(B, K, V, dt)
+    ws = _workspace(torch, nbytes, dev, workspace)
+    with torch.cuda.device(dev):
+        rc = lib.spec_verify_sample(
+            _ptr(target), _ptr(draft if K > 0 else None), _ptr(draft_tokens if K > 0 else None),
+            _ptr(u_accept if K > 0 else None), _ptr(u_sample), B, K, V, dt, float(temperature),
+            _ptr(out["accept_len"]), _ptr(out["tokens"]), _ptr(out.get("lse_target")),
+            _ptr(out.get("lse_draft")), _ptr(out.get("status")), _ptr(ws),
+            ws.numel() * ws.element_size(), _stream(torch, dev, stream))
+    if rc != SV_OK:
+        raise SpecVerifyError(rc, "spec_verify_sample")
+    return out
+
+
+def spec_verify_greedy(target, draft_tokens, *, status=True, workspace=None, stream=None):
+    """Greedy chain verification: target [B,K+1,V], draft_tokens [B,K] int32.
+    Returns ``accept_len`` [B], ``tokens`` [B,K+1] and ``status`` [B]."""
+    torch = _torch()
+    lib = load_library()
+    _check(target, "target", 3)
+    dev = target.device
+    B, K1, V = target.shape
+    K = K1 - 1
+    dt = _dtype_code(target)
+    if K > 0:
+        _check(draft_tokens, "draft_tokens", 2, torch.int32, dev)
+        if tuple(draft_tokens.shape) != (B, K):
+            raise ValueError("draft_tokens must be [B, K]")
+    out = dict(accept_len=torch.empty(B, dtype=torch.int32, device=dev),
+               tokens=torch.empty((B, K + 1), dtype=torch.int32, device=dev))
+    if status:
+        out["status"] = torch.empty(B, dtype=torch.int32, device=dev)
+    ws = _workspace(torch, lib.sv_greedy_workspace_bytes(B, K + 1, V, dt), dev, workspace)
+    with torch.cuda.device(dev):
+        rc = lib.spec_verify_greedy(
+            _ptr(target), _ptr(draft_tokens if K > 0 else None), B, K, V, dt,
+            _ptr(out["accept_len"]), _ptr(out["tokens"]), _ptr(out.get("status")), _ptr(ws),
+            ws.numel() * ws.element_size(), _stream(torch, dev, stream))
+    if rc != SV_OK:
+        raise SpecVerifyError(rc, "spec_verify_greedy")
+    return out
+
+
+def spec_verify_tree(target, node_tokens, parents, *, status=True, workspace=None, stream=None):
+    """Greedy tree verification: target [B,N,V], node_tokens [B,N] and
+    parents [B,N] int32.  Returns ``accept_len`` [B], ``path`` [B,N],
+    ``tokens`` [B,N] and ``status`` [B]."""
+    torch = _torch()
+    lib = load_library()
+    _check(target, "target", 3)
+    dev = target.device
+    B, N, V = target.shape
+    dt = _dtype_code(target)
+    _check(node_tokens, "node_tokens", 2, torch.int32, dev)
+    _check(parents, "parents", 2, torch.int32, dev)
+    if tuple(node_tokens.shape) != (B, N) or tuple(parents.shape) != (B, N):
+        raise ValueError("node_tokens and parents must be [B, N]")
+    out = dict(accept_len=torch.empty(B, dtype=torch.int32, device=dev),
+               path=torch.empty((B, N), dtype=torch.int32, device=dev),
+               tokens=torch.empty((B, N), dtype=torch.int32, device=dev))
+    if status:
+        out["status"] = torch.empty(B, dtype=torch.int32, device=dev)
+    ws = _workspace(torch, lib.sv_greedy_workspace_bytes(B, N, V, dt), dev, workspace)
+    with torch.cuda.device(dev):
+        rc = lib.spec_verify_tree(
+            _ptr(target), _ptr(node_tokens), _ptr(parents), B, N, V, dt, _ptr(out["accept_len"]),
+            _ptr(out["path"]), _ptr(out["tokens"]), _ptr(out.get("status")), _ptr(ws),
+            ws.numel() * ws.element_size(), _stream(torch, dev, stream))
+    if rc != SV_OK:
+        raise SpecVerifyError(rc, "spec_verify_tree")
+    return out
+
+
+# ---- per-kernel timing -----------------------------------------------------------
+
+def trace_begin(capacity: int = 4096) -> None:
+    rc = load_library().sv_trace_begin(capacity)
+    if rc != SV_OK:
+        raise SpecVerifyError(rc, "sv_trace_begin")
+
+
+def trace_end(max_records: int = 1 << 16):
+    """Stop tracing; return [(kernel_name, ms), ...] in launch order."""
+    lib = load_library()
+    recs = (KernelTime * max_records)()
+    n = lib.sv_trace_end(recs, max_records)
+    return [(lib.sv_kernel_name(recs[i].kernel).decode(), float(recs[i].ms))
+            for i in range(min(n, max_records))]

@@ -1,0 +1,44 @@
+"""Build libspecverify.so (the HIP library) in-tree for gfx950 with hipcc."""
+
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(HERE, "libspecverify.so")
+SOURCES = ["sv_api.hip", "sv_sample.hip", "sv_greedy.hip"]
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found; a ROCm toolchain is required to build libspecverify")
+
+
+def flags() -> list:
+    return [
+        f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared", "-Wall",
+        # no packed fp32 instructions (v_pk_*_f32) anywhere in device code
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        f"-I{INCLUDE}", f"-I{CSRC}",
+    ]
+
+
+def build(out: str = LIB, extra=()) -> str:
+    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    tmp = out + ".tmp"
+    cmd = [hipcc(), *flags(), *extra, *srcs, "-o", tmp]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+if __name__ == "__main__":
+    print(build())

@@ -1,0 +1,324 @@
+// sv_api.hip -- the C ABI of libspecverify: argument checks, workspace layout,
+// kernel launches on the caller's stream, and per-kernel event tracing.
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+#include <mutex>
+#include <vector>
+
+#include "sv_device.hpp"
+#include "sv_internal.hpp"
+
+namespace sv {
+
+RowGeom row_geom(int V, sv_dtype dt, bool ptrs_aligned) {
+    RowGeom g;
+    g.per_vec = dt == SV_BF16 ? 8 : 4;
+    g.nvec = (V + g.per_vec - 1) / g.per_vec;
+    const int per_wave = kWave * kStreamVecsPerLane;
+    g.segs = (g.nvec + per_wave - 1) / per_wave;
+    if (g.segs < 1) g.segs = 1;
+    g.ntiles = (g.nvec + kWave - 1) / kWave;
+    g.aligned = ptrs_aligned && (V % g.per_vec) == 0;
+    return g;
+}
+
+static size_t align_up(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+SampleWs sample_ws_layout(int B, int K, const RowGeom &g) {
+    SampleWs w;
+    const size_t rows = static_cast<size_t>(B) * static_cast<size_t>(2 * K + 1);
+    const size_t parts = rows * static_cast<size_t>(g.segs);
+    size_t o = 0;
+    w.part_R = o;
+    o = align_up(o + parts * sizeof(float));
+    w.part_s = o;
+    o = align_up(o + parts * sizeof(double));
+    w.L2 = o;
+    o = align_up(o + rows * sizeof(double));
+    w.rp = o;
+    o = align_up(o + static_cast<size_t>(B) * sizeof(ResidParam));
+    w.tiles = o;
+    o = align_up(o + static_cast<size_t>(B) * static_cast<size_t>(g.ntiles) * sizeof(double));
+    w.total = o;
+    return w;
+}
+
+GreedyWs greedy_ws_layout(long long rows, const RowGeom &g) {
+    GreedyWs w;
+    const size_t parts = static_cast<size_t>(rows) * static_cast<size_t>(g.segs);
+    size_t o = 0;
+    w.part_v = o;
+    o = align_up(o + parts * sizeof(float));
+    w.part_i = o;
+    o = align_up(o + parts * sizeof(int32_t));
+    w.total = o;
+    return w;
+}
+
+Scale make_scale(double T) {
+    Scale s;
+    s.c = 1.4426950408889634073599246810018921 / T;  // log2(e) / T
+    float hi = static_cast<float>(s.c);
+    if (static_cast<double>(hi) >= s.c) hi = nextafterf(hi, 0.0f);
+    s.c_hi = hi;
+    s.c_lo = static_cast<float>(s.c - static_cast<double>(hi));
+    return s;
+}
+
+// ---- tracing ---------------------------------------------------------------------
+
+namespace {
+struct TraceRec {
+    int kernel;
+    hipEvent_t start, stop;
+};
+struct Tracer {
+    std::mutex mu;
+    bool on = false;
+    int capacity = 0;
+    int used = 0;
+    std::vector<TraceRec> recs;
+    int pending = -1;  // index of the record whose stop event is due
+};
+Tracer &tracer() {
+    static Tracer t;
+    return t;
+}
+}  // namespace
+
+void trace_pre(int kernel, hipStream_t s) {
+    Tracer &t = tracer();
+    std::lock_guard<std::mutex> g(t.mu);
+    t.pending = -1;
+    if (!t.on || t.used >= t.capacity) return;
+    TraceRec &r = t.recs[t.used];
+    r.kernel = kernel;
+    if (hipEventRecord(r.start, s) != hipSuccess) return;
+    t.pending = t.used++;
+}
+
+void trace_post(hipStream_t s) {
+    Tracer &t = tracer();
+    std::lock_guard<std::mutex> g(t.mu);
+    if (t.pending < 0) return;
+    (void)hipEventRecord(t.recs[t.pending].stop, s);
+    t.pending = -1;
+}
+
+}  // namespace sv
+
+using namespace sv;
+
+namespace {
+
+bool valid_dtype(sv_dtype dt) { return dt == SV_F32 || dt == SV_BF16; }
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned256(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
+
+// Every launch goes through here so tracing sees it.
+template <typename F>
+hipError_t traced(int kernel, hipStream_t s, F &&f) {
+    trace_pre(kernel, s);
+    const hipError_t e = f();
+    trace_post(s);
+    return e;
+}
+
+// Element counts must stay addressable with 64-bit offsets and int32 row lengths.
+bool sizes_ok(long long B, long long rows_per_req, long long V) {
+    if (B < 0 || rows_per_req < 0 || V < 1 || V > 0x7fffffffLL / 8) return false;
+    const double elems = static_cast<double>(B) * static_cast<double>(rows_per_req) * static_cast<double>(V);
+    return elems < 9.0e15;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t sv_sample_workspace_bytes(int B, int K, int V, sv_dtype dt) {
+    if (B < 0 || K < 0 || K > kMaxSampleK || !valid_dtype(dt) || !sizes_ok(B, 2LL * K + 1, V)) return 0;
+    const RowGeom g = row_geom(V, dt, true);
+    return sample_ws_layout(B, K, g).total;
+}
+
+size_t sv_greedy_workspace_bytes(int B, int rows_per_req, int V, sv_dtype dt) {
+    if (B < 0 || rows_per_req < 1 || !valid_dtype(dt) || !sizes_ok(B, rows_per_req, V)) return 0;
+    const RowGeom g = row_geom(V, dt, true);
+    return greedy_ws_layout(static_cast<long long>(B) * rows_per_req, g).total;
+}
+
+sv_status spec_verify_sample(const void *target_logits, const void *draft_logits,
+                             const int32_t *draft_tokens, const float *u_accept,
+                             const float *u_sample, int B, int K, int V, sv_dtype dt,
+                             float temperature, int32_t *accept_len, int32_t *out_tokens,
+                             float *lse_target, float *lse_draft, int32_t *req_status,
+                             void *workspace, size_t workspace_bytes, void *stream) {
+    if (!valid_dtype(dt)) return SV_ERR_UNSUPPORTED;
+    if (B < 0 || K < 0 || V < 1 || !(temperature > 0.0f) || !isfinite(temperature))
+        return SV_ERR_INVALID_ARG;
+    if (K > kMaxSampleK || !sizes_ok(B, 2LL * K + 1, V)) return SV_ERR_UNSUPPORTED;
+    if (B == 0) return SV_OK;
+    if (!target_logits || !u_sample || !accept_len || !out_tokens || !workspace)
+        return SV_ERR_INVALID_ARG;
+    if (K > 0 && (!draft_logits || !draft_tokens || !u_accept)) return SV_ERR_INVALID_ARG;
+    if (!aligned256(workspace)) return SV_ERR_INVALID_ARG;
+    const bool ptr_al = aligned16(target_logits) && (K == 0 || aligned16(draft_logits));
+    const RowGeom g = row_geom(V, dt, ptr_al);
+    const SampleWs L = sample_ws_layout(B, K, g);
+    if (workspace_bytes < L.total) return SV_ERR_WORKSPACE;
+
+    char *ws = static_cast<char *>(workspace);
+    float *part_R = reinterpret_cast<float *>(ws + L.part_R);
+    double *part_s = reinterpret_cast<double *>(ws + L.part_s);
+    double *L2 = reinterpret_cast<double *>(ws + L.L2);
+    ResidParam *rp = reinterpret_cast<ResidParam *>(ws + L.rp);
+    double *tiles = reinterpret_cast<double *>(ws + L.tiles);
+    const Scale sc = make_scale(static_cast<double>(temperature));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const long long rows_t = static_cast<long long>(B) * (K + 1);
+    const long long rows_total = rows_t + static_cast<long long>(B) * K;
+
+    hipError_t e = traced(SV_K_ROWSTATS, s, [&] {
+        return launch_rowstats(target_logits, draft_logits, rows_t, rows_total, V, g, dt, sc, part_R,
+                               part_s, s);
+    });
+    if (e == hipSuccess)
+        e = traced(SV_K_ACCEPT, s, [&] {
+            return launch_accept(target_logits, draft_logits, draft_tokens, u_accept, u_sample, B, K,
+                                 V, g, dt, sc, part_R, part_s, L2, accept_len, out_tokens,
+                                 lse_target, lse_draft, req_status, rp, s);
+        });
+    if (e == hipSuccess)
+        e = traced(SV_K_RESID_MASS, s, [&] {
+            return launch_resid_mass(target_logits, draft_logits, B, V, g, dt, sc, rp, tiles, s);
+        });
+    if (e == hipSuccess)
+        e = traced(SV_K_RESID_SELECT, s, [&] {
+            return launch_resid_select(target_logits, draft_logits, B, K, V, g, dt, sc, rp, tiles,
+                                       out_tokens, s);
+        });
+    return e == hipSuccess ? SV_OK : SV_ERR_HIP;
+}
+
+sv_status spec_verify_greedy(const void *target_logits, const int32_t *draft_tokens, int B, int K,
+                             int V, sv_dtype dt, int32_t *accept_len, int32_t *out_tokens,
+                             int32_t *req_status, void *workspace, size_t workspace_bytes,
+                             void *stream) {
+    if (!valid_dtype(dt)) return SV_ERR_UNSUPPORTED;
+    if (B < 0 || K < 0 || V < 1) return SV_ERR_INVALID_ARG;
+    if (!sizes_ok(B, static_cast<long long>(K) + 1, V) || K > 0x7ffffff0) return SV_ERR_UNSUPPORTED;
+    if (B == 0) return SV_OK;
+    if (!target_logits || !accept_len || !out_tokens || !workspace) return SV_ERR_INVALID_ARG;
+    if (K > 0 && !draft_tokens) return SV_ERR_INVALID_ARG;
+    if (!aligned256(workspace)) return SV_ERR_INVALID_ARG;
+    const RowGeom g = row_geom(V, dt, aligned16(target_logits));
+    const long long rows = static_cast<long long>(B) * (K + 1);
+    const GreedyWs L = greedy_ws_layout(rows, g);
+    if (workspace_bytes < L.total) return SV_ERR_WORKSPACE;
+    char *ws = static_cast<char *>(workspace);
+    float *pv = reinterpret_cast<float *>(ws + L.part_v);
+    int32_t *pi = reinterpret_cast<int32_t *>(ws + L.part_i);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = traced(SV_K_ARGMAX, s, [&] { return launch_argmax(target_logits, rows, V, g, dt, pv, pi, s); });
+    if (e == hipSuccess)
+        e = traced(SV_K_MATCH, s, [&] {
+            return launch_match(pv, pi, draft_tokens, B, K, V, g, accept_len, out_tokens, req_status, s);
+        });
+    return e == hipSuccess ? SV_OK : SV_ERR_HIP;
+}
+
+sv_status spec_verify_tree(const void *target_logits, const int32_t *node_tokens,
+                           const int32_t *parents, int B, int N, int V, sv_dtype dt,
+                           int32_t *accept_len, int32_t *path_nodes, int32_t *out_tokens,
+                           int32_t *req_status, void *workspace, size_t workspace_bytes,
+                           void *stream) {
+    if (!valid_dtype(dt)) return SV_ERR_UNSUPPORTED;
+    if (B < 0 || N < 1 || V < 1) return SV_ERR_INVALID_ARG;
+    if (N > SV_MAX_TREE_NODES || !sizes_ok(B, N, V)) return SV_ERR_UNSUPPORTED;
+    if (B == 0) return SV_OK;
+    if (!target_logits || !node_tokens || !parents || !accept_len || !path_nodes || !out_tokens ||
+        !workspace)
+        return SV_ERR_INVALID_ARG;
+    if (!aligned256(workspace)) return SV_ERR_INVALID_ARG;
+    const RowGeom g = row_geom(V, dt, aligned16(target_logits));
+    const long long rows = static_cast<long long>(B) * N;
+    const GreedyWs L = greedy_ws_layout(rows, g);
+    if (workspace_bytes < L.total) return SV_ERR_WORKSPACE;
+    char *ws = static_cast<char *>(workspace);
+    float *pv = reinterpret_cast<float *>(ws + L.part_v);
+    int32_t *pi = reinterpret_cast<int32_t *>(ws + L.part_i);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = traced(SV_K_ARGMAX, s, [&] { return launch_argmax(target_logits, rows, V, g, dt, pv, pi, s); });
+    if (e == hipSuccess)
+        e = traced(SV_K_TREE, s, [&] {
+            return launch_tree(pv, pi, node_tokens, parents, B, N, V, g, accept_len, path_nodes,
+                               out_tokens, req_status, s);
+        });
+    return e == hipSuccess ? SV_OK : SV_ERR_HIP;
+}
+
+const char *sv_status_string(sv_status st) {
+    switch (st) {
+        case SV_OK: return "ok";
+        case SV_ERR_INVALID_ARG: return "invalid argument";
+        case SV_ERR_UNSUPPORTED: return "unsupported dtype or size";
+        case SV_ERR_WORKSPACE: return "workspace too small";
+        case SV_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+const char *sv_version(void) { return "specverify 0.1.0 (gfx950)"; }
+
+const char *sv_kernel_name(int k) {
+    static const char *names[SV_K_COUNT] = {"rowstats", "accept", "resid_mass", "resid_select",
+                                            "argmax", "match", "tree"};
+    return (k >= 0 && k < SV_K_COUNT) ? names[k] : "unknown";
+}
+
+sv_status sv_trace_begin(int capacity) {
+    if (capacity < 1) return SV_ERR_INVALID_ARG;
+    Tracer &t = tracer();
+    std::lock_guard<std::mutex> g(t.mu);
+    for (auto &r : t.recs) {
+        (void)hipEventDestroy(r.start);
+        (void)hipEventDestroy(r.stop);
+    }
+    t.recs.assign(static_cast<size_t>(capacity), TraceRec{});
+    for (auto &r : t.recs) {
+        if (hipEventCreate(&r.start) != hipSuccess || hipEventCreate(&r.stop) != hipSuccess) {
+            t.recs.clear();
+            t.on = false;
+            return SV_ERR_HIP;
+        }
+    }
+    t.capacity = capacity;
+    t.used = 0;
+    t.pending = -1;
+    t.on = true;
+    return SV_OK;
+}
+
+int sv_trace_end(sv_kernel_time *records, int max_records) {
+    Tracer &t = tracer();
+    std::lock_guard<std::mutex> g(t.mu);
+    const int n = t.used;
+    for (int i = 0; i < n; ++i) {
+        float ms = -1.0f;
+        if (hipEventSynchronize(t.recs[i].stop) == hipSuccess)
+            (void)hipEventElapsedTime(&ms, t.recs[i].start, t.recs[i].stop);
+        if (records && i < max_records) records[i] = sv_kernel_time{t.recs[i].kernel, ms};
+    }
+    for (auto &r : t.recs) {
+        (void)hipEventDestroy(r.start);
+        (void)hipEventDestroy(r.stop);
+    }
+    t.recs.clear();
+    t.on = false;
+    t.used = t.capacity = 0;
+    return n;
+}
+
+}  // extern "C"

@@ -1,0 +1,157 @@
+// sv_device.hpp -- device-side building blocks shared by the verification kernels:
+// 16-byte logit loaders, bf16 widening, and wave64 reductions / scans.
+//
+// All reductions here are fixed-order (butterfly or Hillis-Steele over lane
+// ids), so every kernel built on them is deterministic.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sv {
+
+constexpr int kWave = 64;
+constexpr int kBlock = 256;
+constexpr int kWavesPerBlock = kBlock / kWave;
+
+// Element type tags: logits are either IEEE binary32 or bfloat16 bit patterns.
+struct F32 {
+    using storage = float;
+    static constexpr int kPerVec = 4;                   // elements per 16-byte vector
+    static constexpr uint32_t kNegInfWord = 0xff800000u;  // one -inf per dword
+};
+struct BF16 {
+    using storage = uint16_t;
+    static constexpr int kPerVec = 8;
+    static constexpr uint32_t kNegInfWord = 0xff80ff80u;  // two bf16 -inf per dword
+};
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+    return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(uint16_t h) { return bf16_to_f32(h); }
+
+// Unpack one 16-byte vector into kPerVec floats (exact widening).
+__device__ __forceinline__ void unpack(const uint4 &w, float (&x)[4]) {
+    x[0] = __uint_as_float(w.x);
+    x[1] = __uint_as_float(w.y);
+    x[2] = __uint_as_float(w.z);
+    x[3] = __uint_as_float(w.w);
+}
+__device__ __forceinline__ void unpack(const uint4 &w, float (&x)[8]) {
+    // bf16 pairs: the low half is the earlier element.
+    x[0] = __uint_as_float(w.x << 16);
+    x[1] = __uint_as_float(w.x & 0xffff0000u);
+    x[2] = __uint_as_float(w.y << 16);
+    x[3] = __uint_as_float(w.y & 0xffff0000u);
+    x[4] = __uint_as_float(w.z << 16);
+    x[5] = __uint_as_float(w.z & 0xffff0000u);
+    x[6] = __uint_as_float(w.w << 16);
+    x[7] = __uint_as_float(w.w & 0xffff0000u);
+}
+
+// Vector j (kPerVec consecutive elements) of a row of V logits.  ALIGNED means
+// the row starts on a 16-byte boundary and V is a multiple of kPerVec, so the
+// vector is one 16-byte load.  Otherwise elements are loaded one by one and
+// those at or past V read as -inf.
+template <typename E, bool ALIGNED>
+__device__ __forceinline__ void load_vec(const typename E::storage *__restrict__ row, int V, int j,
+                                         float (&x)[E::kPerVec]) {
+    if constexpr (ALIGNED) {
+        const uint4 w = reinterpret_cast<const uint4 *>(row)[j];
+        unpack(w, x);
+    } else {
+#pragma unroll
+        for (int e = 0; e < E::kPerVec; ++e) {
+            const int idx = j * E::kPerVec + e;
+            x[e] = idx < V ? to_f32(row[idx]) : -__builtin_huge_valf();
+        }
+    }
+}
+
+// A 16-byte vector held in registers between its load and its use, so a wave
+// can issue all of its loads before consuming any of them.  The aligned form
+// keeps the raw 16 bytes (4 VGPRs); the general form keeps widened floats.
+template <typename E, bool ALIGNED>
+struct Staged;
+
+template <typename E>
+struct Staged<E, true> {
+    uint4 w;
+    __device__ __forceinline__ void load(const typename E::storage *__restrict__ row, int, int j) {
+        w = reinterpret_cast<const uint4 *>(row)[j];
+    }
+    __device__ __forceinline__ void set_neg_inf() {
+        w = make_uint4(E::kNegInfWord, E::kNegInfWord, E::kNegInfWord, E::kNegInfWord);
+    }
+    __device__ __forceinline__ void get(float (&x)[E::kPerVec]) const { unpack(w, x); }
+};
+
+template <typename E>
+struct Staged<E, false> {
+    float v[E::kPerVec];
+    __device__ __forceinline__ void load(const typename E::storage *__restrict__ row, int V, int j) {
+        load_vec<E, false>(row, V, j, v);
+    }
+    __device__ __forceinline__ void set_neg_inf() {
+#pragma unroll
+        for (int e = 0; e < E::kPerVec; ++e) v[e] = -__builtin_huge_valf();
+    }
+    __device__ __forceinline__ void get(float (&x)[E::kPerVec]) const {
+#pragma unroll
+        for (int e = 0; e < E::kPerVec; ++e) x[e] = v[e];
+    }
+};
+
+// Fixed-order pairwise sum of a small array.
+template <int P>
+__device__ __forceinline__ float pairwise_sum(float (&a)[P]) {
+#pragma unroll
+    for (int w = P / 2; w >= 1; w /= 2) {
+#pragma unroll
+        for (int i = 0; i < w; ++i) a[i] = a[i] + a[i + w];
+    }
+    return a[0];
+}
+
+// ---- wave64 reductions ------------------------------------------------------
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+    return v;
+}
+
+__device__ __forceinline__ int wave_min(int v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o, kWave));
+    return v;
+}
+
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+
+// Inclusive prefix sum over lanes (Hillis-Steele; fixed order).
+__device__ __forceinline__ double wave_incl_scan(double v, int lane) {
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const double y = __shfl_up(v, o, kWave);
+        if (lane >= o) v += y;
+    }
+    return v;
+}
+
+__device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
+
+// Lowest / highest set lane of a non-zero mask.
+__device__ __forceinline__ int first_lane(uint64_t m) { return __ffsll(static_cast<long long>(m)) - 1; }
+__device__ __forceinline__ int last_lane(uint64_t m) { return 63 - __clzll(static_cast<long long>(m)); }
+
+// exp2 on the hardware transcendental unit (v_exp_f32); -inf gives 0.
+__device__ __forceinline__ float fast_exp2(float a) { return __builtin_amdgcn_exp2f(a); }
+
+}  // namespace sv

@@ -1,0 +1,495 @@
+// sv_sample.hip -- stochastic chain verification (speculative sampling).
+//
+// What is computed follows the speculative-decoding tutorial page, sections
+// "一轮推测解码究竟发生什么" (accept draft x_i with probability
+// min(1, p_i(x_i)/q_i(x_i)), discard every later draft at the first rejection,
+// then draw one target token: from the corrected residual at the rejected
+// position, or from the next-position distribution when all drafts pass) and
+// "为什么“猜错再改”不会偏离目标分布" (residual norm(max(0, p - q))).
+//
+// Four kernels, all on the caller's stream:
+//   k_rowstats     one streaming pass over every target row [B,K+1,V] and draft
+//                  row [B,K,V]; each wave reduces a segment of a row to a
+//                  partial (R, s) with s = sum 2^(x c - R), c = log2(e)/T.
+//   k_accept       one wave per request: merges the partials of its 2K+1 rows
+//                  into L2 = log2 sum_v 2^(x c), gathers L[x_i] for every draft,
+//                  forms p_i(x_i)/q_i(x_i) in fp64 and finds the first
+//                  rejection; writes accept_len, the accepted tokens, lse.
+//   k_resid_mass   for the one row (pair) each request draws from, the mass of
+//                  max(0, p - q) (or p for the bonus) per 64-vector tile.
+//   k_resid_select one wave per request: prefix over tile masses, then over
+//                  lanes of the chosen tile, then over the elements of the
+//                  chosen lane; writes the drawn token.
+//
+// Precision: per-element exponentials run in fp32 on v_exp_f32 with the
+// exponent formed by two fused multiply-adds against c = c_hi + c_lo, so the
+// temperature scale carries no systematic rounding; every accumulation across
+// elements, the row merges, the acceptance ratios and the running masses of the
+// inverse CDF are fp64.
+#include "sv_device.hpp"
+#include "sv_internal.hpp"
+
+namespace sv {
+namespace {
+
+constexpr double kLn2 = 0.6931471805599453094172321214581766;
+
+// ---- S1: per-segment row statistics ---------------------------------------------
+
+template <typename E, bool ALIGNED, int U>
+__global__ __launch_bounds__(kBlock) void k_rowstats(
+    const typename E::storage *__restrict__ tgt, const typename E::storage *__restrict__ drf,
+    long long rows_t, long long nwaves, int V, int nvec, int segs, float c_hi, float c_lo,
+    float *__restrict__ part_R, double *__restrict__ part_s) {
+    constexpr int P = E::kPerVec;
+    const int lane = threadIdx.x & (kWave - 1);
+    const long long wave = static_cast<long long>(blockIdx.x) * kWavesPerBlock + (threadIdx.x >> 6);
+    if (wave >= nwaves) return;
+    const long long row = wave / segs;
+    const int seg = static_cast<int>(wave - row * segs);
+    const typename E::storage *base =
+        row < rows_t ? tgt + row * static_cast<long long>(V) : drf + (row - rows_t) * static_cast<long long>(V);
+    const int v0 = static_cast<int>((static_cast<long long>(seg) * nvec) / segs);
+    const int v1 = static_cast<int>((static_cast<long long>(seg + 1) * nvec) / segs);
+
+    Staged<E, ALIGNED> st[U];
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+        const int j = v0 + k * kWave + lane;
+        if (j < v1)
+            st[k].load(base, V, j);
+        else
+            st[k].set_neg_inf();
+    }
+    float m = -__builtin_huge_valf();
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+        float x[P];
+        st[k].get(x);
+#pragma unroll
+        for (int e = 0; e < P; ++e) m = fmaxf(m, x[e]);
+    }
+    m = wave_max(m);
+
+    float R = -__builtin_huge_valf();
+    double s = 0.0;
+    if (m != -__builtin_huge_valf()) {
+        R = m * c_hi;
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            float x[P];
+            st[k].get(x);
+#pragma unroll
+            for (int e = 0; e < P; ++e) x[e] = fast_exp2(fmaf(x[e], c_lo, fmaf(x[e], c_hi, -R)));
+            s += static_cast<double>(pairwise_sum(x));
+        }
+        s = wave_sum(s);
+    }
+    if (lane == 0) {
+        part_R[wave] = R;
+        part_s[wave] = s;
+    }
+}
+
+// ---- S2/S3: merge, gather, acceptance scan ----------------------------------------
+
+template <typename E>
+__global__ __launch_bounds__(kWave) void k_accept(
+    const typename E::storage *__restrict__ tgt, const typename E::storage *__restrict__ drf,
+    const int32_t *__restrict__ drafts, const float *__restrict__ ua, const float *__restrict__ us,
+    int B, int K, int V, int segs, double c, const float *__restrict__ part_R,
+    const double *__restrict__ part_s, double *__restrict__ L2out, int32_t *__restrict__ accept_len,
+    int32_t *__restrict__ out_tokens, float *__restrict__ lse_t, float *__restrict__ lse_d,
+    int32_t *__restrict__ status, ResidParam *__restrict__ rp) {
+    extern __shared__ double sL2[];  // 2K+1 row log2-normalisers of this request
+    const int b = blockIdx.x;
+    const int lane = threadIdx.x;
+    const long long rows_t = static_cast<long long>(B) * (K + 1);
+    const int nrows = 2 * K + 1;
+    const double inf = __builtin_huge_val();
+
+    for (int r = 0; r < nrows; ++r) {
+        const long long g = r <= K ? static_cast<long long>(b) * (K + 1) + r
+                                   : rows_t + static_cast<long long>(b) * K + (r - K - 1);
+        const float *pR = part_R + g * segs;
+        const double *pS = part_s + g * segs;
+        float Rm = -__builtin_huge_valf();
+        for (int s = lane; s < segs; s += kWave) Rm = fmaxf(Rm, pR[s]);
+        Rm = wave_max(Rm);
+        double acc = 0.0;
+        if (Rm != -__builtin_huge_valf()) {
+            for (int s = lane; s < segs; s += kWave) {
+                const double ss = pS[s];
+                if (ss > 0.0) acc += ss * exp2(static_cast<double>(pR[s]) - static_cast<double>(Rm));
+            }
+        }
+        acc = wave_sum(acc);
+        const double l2 = acc > 0.0 ? static_cast<double>(Rm) + log2(acc) : -inf;
+        if (lane == 0) {
+            sL2[r] = l2;
+            L2out[static_cast<long long>(b) * nrows + r] = l2;
+            if (r <= K) {
+                if (lse_t) lse_t[static_cast<long long>(b) * (K + 1) + r] = static_cast<float>(l2 * kLn2);
+            } else if (lse_d) {
+                lse_d[static_cast<long long>(b) * K + (r - K - 1)] = static_cast<float>(l2 * kLn2);
+            }
+        }
+    }
+    __syncthreads();
+
+    // p_i(x_i) / q_i(x_i) for every position at once; the first failing test wins.
+    int n = K;
+    bool bad = false;
+    for (int i0 = 0; i0 < K; i0 += kWave) {
+        const int i = i0 + lane;
+        bool rej = false;
+        if (i < K) {
+            const int x = drafts[static_cast<long long>(b) * K + i];
+            double r = 0.0;
+            if (x >= 0 && x < V) {
+                const double xp = to_f32(tgt[(static_cast<long long>(b) * (K + 1) + i) * V + x]);
+                const double xq = to_f32(drf[(static_cast<long long>(b) * K + i) * V + x]);
+                const double px = exp2(xp * c - sL2[i]);
+                const double qx = exp2(xq * c - sL2[K + 1 + i]);
+                r = qx == 0.0 ? inf : px / qx;
+            } else {
+                bad = true;
+            }
+            const double u = static_cast<double>(ua[static_cast<long long>(b) * K + i]);
+            rej = !(u < r);
+        }
+        const uint64_t mk = ballot(rej);
+        if (mk != 0 && n == K) n = i0 + first_lane(mk);
+    }
+    const bool any_bad = ballot(bad) != 0;
+
+    int32_t *tok = out_tokens + static_cast<long long>(b) * (K + 1);
+    for (int i = lane; i <= K; i += kWave) tok[i] = i < n ? drafts[static_cast<long long>(b) * K + i] : -1;
+    if (lane == 0) {
+        accept_len[b] = n;
+        if (status) status[b] = any_bad ? 1 : 0;
+        ResidParam P;
+        P.pos = n;
+        P.u = static_cast<double>(us[static_cast<long long>(b) * (K + 1) + n]);
+        P.row_p = static_cast<long long>(b) * (K + 1) + n;
+        P.L2p = sL2[n];
+        if (n < K) {
+            P.mode = 1;
+            P.row_q = static_cast<long long>(b) * K + n;
+            P.L2q = sL2[K + 1 + n];
+        } else {
+            P.mode = 0;
+            P.row_q = 0;
+            P.L2q = 0.0;
+        }
+        rp[b] = P;
+    }
+}
+
+// ---- S4/S5: the drawn token -------------------------------------------------------
+
+// Per-request constants of the draw: p(v) = 2^(x c - L2p), split so that
+// x*c_hi - Rp_hi and x*c_lo - Rp_lo are each one correctly rounded fma.
+struct Draw {
+    float c_hi, c_lo, Rp_hi, Rp_lo, Rq_hi, Rq_lo;
+    int mode;
+};
+
+__device__ __forceinline__ Draw make_draw(const ResidParam &P, float c_hi, float c_lo, int mode) {
+    Draw d;
+    d.c_hi = c_hi;
+    d.c_lo = c_lo;
+    d.Rp_hi = static_cast<float>(P.L2p);
+    d.Rp_lo = static_cast<float>(P.L2p - static_cast<double>(d.Rp_hi));
+    d.Rq_hi = static_cast<float>(P.L2q);
+    d.Rq_lo = static_cast<float>(P.L2q - static_cast<double>(d.Rq_hi));
+    d.mode = mode;
+    return d;
+}
+
+// Mass of each element of one vector: max(0, p - q) (mode 1) or p (mode 0).
+template <int P>
+__device__ __forceinline__ void masses(const float (&xp)[P], const float (&xq)[P], const Draw &D,
+                                       float (&d)[P]) {
+#pragma unroll
+    for (int e = 0; e < P; ++e) {
+        const float p = fast_exp2(fmaf(xp[e], D.c_hi, -D.Rp_hi) + fmaf(xp[e], D.c_lo, -D.Rp_lo));
+        if (D.mode) {
+            const float q = fast_exp2(fmaf(xq[e], D.c_hi, -D.Rq_hi) + fmaf(xq[e], D.c_lo, -D.Rq_lo));
+            d[e] = fmaxf(p - q, 0.0f);
+        } else {
+            d[e] = p;
+        }
+    }
+}
+
+template <int P>
+__device__ __forceinline__ double lane_total(const float (&d)[P]) {
+    float t[P];
+#pragma unroll
+    for (int e = 0; e < P; ++e) t[e] = d[e];
+    return static_cast<double>(pairwise_sum(t));
+}
+
+template <typename E, bool ALIGNED, int TPW>
+__global__ __launch_bounds__(kBlock) void k_resid_mass(
+    const typename E::storage *__restrict__ tgt, const typename E::storage *__restrict__ drf,
+    int B, int V, int nvec, int ntiles, int wpr, float c_hi, float c_lo,
+    const ResidParam *__restrict__ rp, double *__restrict__ tile_mass) {
+    constexpr int P = E::kPerVec;
+    const int lane = threadIdx.x & (kWave - 1);
+    const long long wave = static_cast<long long>(blockIdx.x) * kWavesPerBlock + (threadIdx.x >> 6);
+    if (wave >= static_cast<long long>(B) * wpr) return;
+    const int b = static_cast<int>(wave / wpr);
+    const int w = static_cast<int>(wave - static_cast<long long>(b) * wpr);
+    const ResidParam Pm = rp[b];
+    const Draw D = make_draw(Pm, c_hi, c_lo, Pm.mode);
+    const typename E::storage *prow = tgt + Pm.row_p * static_cast<long long>(V);
+    const typename E::storage *qrow = D.mode ? drf + Pm.row_q * static_cast<long long>(V) : nullptr;
+    const int t0 = w * TPW;
+
+    Staged<E, ALIGNED> sp[TPW], sq[TPW];
+#pragma unroll
+    for (int k = 0; k < TPW; ++k) {
+        const int j = (t0 + k) * kWave + lane;
+        if (t0 + k < ntiles && j < nvec) {
+            sp[k].load(prow, V, j);
+            if (D.mode)
+                sq[k].load(qrow, V, j);
+            else
+                sq[k].set_neg_inf();
+        } else {
+            sp[k].set_neg_inf();
+            sq[k].set_neg_inf();
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < TPW; ++k) {
+        if (t0 + k >= ntiles) break;
+        float xp[P], xq[P], d[P];
+        sp[k].get(xp);
+        sq[k].get(xq);
+        masses(xp, xq, D, d);
+        const double incl = wave_incl_scan(lane_total(d), lane);
+        if (lane == kWave - 1) tile_mass[static_cast<long long>(b) * ntiles + t0 + k] = incl;
+    }
+}
+
+template <typename E, bool ALIGNED>
+__global__ __launch_bounds__(kWave) void k_resid_select(
+    const typename E::storage *__restrict__ tgt, const typename E::storage *__restrict__ drf,
+    int B, int K, int V, int nvec, int ntiles, float c_hi, float c_lo,
+    const ResidParam *__restrict__ rp, double *__restrict__ tile_mass, int32_t *__restrict__ out_tokens) {
+    constexpr int P = E::kPerVec;
+    const int b = blockIdx.x;
+    const int lane = threadIdx.x;
+    const ResidParam Pm = rp[b];
+    Draw D = make_draw(Pm, c_hi, c_lo, Pm.mode);
+    const typename E::storage *prow = tgt + Pm.row_p * static_cast<long long>(V);
+    const typename E::storage *qrow = D.mode ? drf + Pm.row_q * static_cast<long long>(V) : nullptr;
+    double *tm = tile_mass + static_cast<long long>(b) * ntiles;
+    int32_t *dst = out_tokens + static_cast<long long>(b) * (K + 1) + Pm.pos;
+
+    // tiles [lt0, lt1) belong to this lane; prefix over lanes in tile order
+    const int tpl = (ntiles + kWave - 1) / kWave;
+    const int lt0 = min(ntiles, lane * tpl), lt1 = min(ntiles, lt0 + tpl);
+    double ls = 0.0;
+    for (int t = lt0; t < lt1; ++t) ls += tm[t];
+    double incl = wave_incl_scan(ls, lane);
+    double Z = __shfl(incl, kWave - 1, kWave);
+
+    if (!(Z > 0.0) && D.mode) {
+        // The residual vanished through rounding: draw from p alone with the
+        // same uniform (a tile pass over the row, rare).
+        D.mode = 0;
+        for (int t = 0; t < ntiles; ++t) {
+            const int j = t * kWave + lane;
+            float xp[P], d[P];
+            if (j < nvec)
+                load_vec<E, ALIGNED>(prow, V, j, xp);
+            else
+#pragma unroll
+                for (int e = 0; e < P; ++e) xp[e] = -__builtin_huge_valf();
+            masses(xp, xp, D, d);
+            const double inc = wave_incl_scan(lane_total(d), lane);
+            if (lane == kWave - 1) tm[t] = inc;
+        }
+        __syncthreads();
+        ls = 0.0;
+        for (int t = lt0; t < lt1; ++t) ls += tm[t];
+        incl = wave_incl_scan(ls, lane);
+        Z = __shfl(incl, kWave - 1, kWave);
+    }
+    if (!(Z > 0.0)) {  // no finite logit in the row: nothing can be drawn
+        if (lane == 0) *dst = -1;
+        return;
+    }
+    const double target = Pm.u * Z;
+
+    // 1. the lane whose tiles hold the crossing
+    const double up = __shfl_up(incl, 1, kWave);
+    const double excl = lane > 0 ? up : 0.0;
+    uint64_t mk = ballot(ls > 0.0 && incl > target);
+    const uint64_t pos_lanes_t = ballot(ls > 0.0);
+    const int L = mk ? first_lane(mk) : (pos_lanes_t ? last_lane(pos_lanes_t) : -1);
+    // 2. the tile, walked in order by that lane
+    int tsel = -1;
+    double trel = 0.0;
+    if (L >= 0 && lane == L) {
+        double run = excl, run_last = 0.0;
+        int last = -1;
+        for (int t = lt0; t < lt1; ++t) {
+            const double m = tm[t];
+            if (m > 0.0) {
+                if (run + m > target) {
+                    tsel = t;
+                    trel = target - run;
+                    break;
+                }
+                last = t;
+                run_last = run;
+            }
+            run += m;
+        }
+        if (tsel < 0) {
+            tsel = last;
+            trel = target - run_last;
+        }
+    }
+    tsel = __shfl(tsel, L < 0 ? 0 : L, kWave);
+    trel = __shfl(trel, L < 0 ? 0 : L, kWave);
+    if (L < 0 || tsel < 0 || tsel >= ntiles) {  // unreachable for finite rows; never index with it
+        if (lane == 0) *dst = -1;
+        return;
+    }
+
+    // 3. the lane of that tile, then the element of that lane
+    const int j = tsel * kWave + lane;
+    float xp[P], xq[P], d[P];
+    if (j < nvec) {
+        load_vec<E, ALIGNED>(prow, V, j, xp);
+        if (D.mode)
+            load_vec<E, ALIGNED>(qrow, V, j, xq);
+        else
+#pragma unroll
+            for (int e = 0; e < P; ++e) xq[e] = -__builtin_huge_valf();
+    } else {
+#pragma unroll
+        for (int e = 0; e < P; ++e) xp[e] = xq[e] = -__builtin_huge_valf();
+    }
+    masses(xp, xq, D, d);
+    const double lm = lane_total(d);
+    const double inc2 = wave_incl_scan(lm, lane);
+    const double ex2 = __shfl_up(inc2, 1, kWave);
+    mk = ballot(lm > 0.0 && inc2 > trel);
+    const uint64_t pos_lanes = ballot(lm > 0.0);
+    const int L2 = mk ? first_lane(mk) : (pos_lanes ? last_lane(pos_lanes) : -1);
+    if (L2 < 0) {
+        if (lane == 0) *dst = -1;
+        return;
+    }
+    if (lane == L2) {
+        double run = lane > 0 ? ex2 : 0.0;
+        int pick = -1, last = -1;
+#pragma unroll
+        for (int e = 0; e < P; ++e) {
+            run += static_cast<double>(d[e]);
+            if (d[e] > 0.0f) {
+                last = e;
+                if (pick < 0 && run > trel) pick = e;
+            }
+        }
+        if (pick < 0) pick = last;
+        *dst = j * P + pick;
+    }
+}
+
+template <typename E, bool ALIGNED>
+hipError_t rowstats_t(const void *tgt, const void *drf, long long rows_t, long long rows_total, int V,
+                      const RowGeom &g, const Scale &sc, float *part_R, double *part_s,
+                      hipStream_t s) {
+    using T = typename E::storage;
+    const long long nwaves = rows_total * g.segs;
+    const long long blocks = (nwaves + kWavesPerBlock - 1) / kWavesPerBlock;
+    k_rowstats<E, ALIGNED, kStreamVecsPerLane><<<dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0, s>>>(
+        static_cast<const T *>(tgt), static_cast<const T *>(drf), rows_t, nwaves, V, g.nvec,
+        g.segs, sc.c_hi, sc.c_lo, part_R, part_s);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_rowstats(const void *tgt, const void *drf, long long rows_t, long long rows_total,
+                           int V, const RowGeom &g, sv_dtype dt, const Scale &sc, float *part_R,
+                           double *part_s, hipStream_t s) {
+    if (dt == SV_BF16)
+        return g.aligned ? rowstats_t<BF16, true>(tgt, drf, rows_t, rows_total, V, g, sc, part_R, part_s, s)
+                         : rowstats_t<BF16, false>(tgt, drf, rows_t, rows_total, V, g, sc, part_R, part_s, s);
+    return g.aligned ? rowstats_t<F32, true>(tgt, drf, rows_t, rows_total, V, g, sc, part_R, part_s, s)
+                     : rowstats_t<F32, false>(tgt, drf, rows_t, rows_total, V, g, sc, part_R, part_s, s);
+}
+
+hipError_t launch_accept(const void *tgt, const void *drf, const int32_t *drafts, const float *ua,
+                         const float *us, int B, int K, int V, const RowGeom &g, sv_dtype dt,
+                         const Scale &sc, const float *part_R, const double *part_s, double *L2,
+                         int32_t *accept_len, int32_t *out_tokens, float *lse_t, float *lse_d,
+                         int32_t *status, ResidParam *rp, hipStream_t s) {
+    const size_t lds = sizeof(double) * static_cast<size_t>(2 * K + 1);
+    if (dt == SV_BF16)
+        k_accept<BF16><<<dim3(B), dim3(kWave), lds, s>>>(
+            static_cast<const uint16_t *>(tgt), static_cast<const uint16_t *>(drf), drafts, ua, us,
+            B, K, V, g.segs, sc.c, part_R, part_s, L2, accept_len, out_tokens, lse_t, lse_d, status, rp);
+    else
+        k_accept<F32><<<dim3(B), dim3(kWave), lds, s>>>(
+            static_cast<const float *>(tgt), static_cast<const float *>(drf), drafts, ua, us, B, K,
+            V, g.segs, sc.c, part_R, part_s, L2, accept_len, out_tokens, lse_t, lse_d, status, rp);
+    return hipGetLastError();
+}
+
+namespace {
+template <typename E, bool ALIGNED>
+hipError_t resid_mass_t(const void *tgt, const void *drf, int B, int V, const RowGeom &g,
+                        const Scale &sc, const ResidParam *rp, double *tile_mass, hipStream_t s) {
+    using T = typename E::storage;
+    const int wpr = (g.ntiles + kTilesPerWave - 1) / kTilesPerWave;
+    const long long nwaves = static_cast<long long>(B) * wpr;
+    const long long blocks = (nwaves + kWavesPerBlock - 1) / kWavesPerBlock;
+    k_resid_mass<E, ALIGNED, kTilesPerWave><<<dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0, s>>>(
+        static_cast<const T *>(tgt), static_cast<const T *>(drf), B, V, g.nvec, g.ntiles, wpr,
+        sc.c_hi, sc.c_lo, rp, tile_mass);
+    return hipGetLastError();
+}
+template <typename E, bool ALIGNED>
+hipError_t resid_select_t(const void *tgt, const void *drf, int B, int K, int V, const RowGeom &g,
+                          const Scale &sc, const ResidParam *rp, double *tile_mass,
+                          int32_t *out_tokens, hipStream_t s) {
+    using T = typename E::storage;
+    k_resid_select<E, ALIGNED><<<dim3(B), dim3(kWave), 0, s>>>(
+        static_cast<const T *>(tgt), static_cast<const T *>(drf), B, K, V, g.nvec, g.ntiles,
+        sc.c_hi, sc.c_lo, rp, tile_mass, out_tokens);
+    return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_resid_mass(const void *tgt, const void *drf, int B, int V, const RowGeom &g,
+                             sv_dtype dt, const Scale &sc, const ResidParam *rp, double *tile_mass,
+                             hipStream_t s) {
+    if (dt == SV_BF16)
+        return g.aligned ? resid_mass_t<BF16, true>(tgt, drf, B, V, g, sc, rp, tile_mass, s)
+                         : resid_mass_t<BF16, false>(tgt, drf, B, V, g, sc, rp, tile_mass, s);
+    return g.aligned ? resid_mass_t<F32, true>(tgt, drf, B, V, g, sc, rp, tile_mass, s)
+                     : resid_mass_t<F32, false>(tgt, drf, B, V, g, sc, rp, tile_mass, s);
+}
+
+hipError_t launch_resid_select(const void *tgt, const void *drf, int B, int K, int V,
+                               const RowGeom &g, sv_dtype dt, const Scale &sc,
+                               const ResidParam *rp, double *tile_mass, int32_t *out_tokens,
+                               hipStream_t s) {
+    if (dt == SV_BF16)
+        return g.aligned ? resid_select_t<BF16, true>(tgt, drf, B, K, V, g, sc, rp, tile_mass, out_tokens, s)
+                         : resid_select_t<BF16, false>(tgt, drf, B, K, V, g, sc, rp, tile_mass, out_tokens, s);
+    return g.aligned ? resid_select_t<F32, true>(tgt, drf, B, K, V, g, sc, rp, tile_mass, out_tokens, s)
+                     : resid_select_t<F32, false>(tgt, drf, B, K, V, g, sc, rp, tile_mass, out_tokens, s);
+}
+
+}  // namespace sv

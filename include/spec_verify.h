@@ -1,0 +1,192 @@
+/*
+ * spec_verify.h -- C ABI of libspecverify, batched speculative-decoding
+ * verification on AMD MI355X (gfx950).
+ *
+ * What is computed (the pages this follows):
+ *   - "推测解码：先猜几个 token，为什么答案仍然没变" (speculative-decoding tutorial),
+ *     section "一轮推测解码究竟发生什么": the target scores gamma+1 positions in one
+ *     pass; drafts are examined left to right, draft x_i is accepted with
+ *     probability min(1, p_i(x_i)/q_i(x_i)); at the first rejection every later
+ *     draft is discarded and one token is drawn from the corrected residual
+ *     distribution; if all are accepted one extra token is drawn from the
+ *     target's next-position distribution.  A round emits 1..gamma+1 tokens.
+ *   - same page, section "为什么“猜错再改”不会偏离目标分布": residual
+ *     p'(x) = norm(max(0, p(x) - q(x))); greedy decoding accepts a draft while
+ *     it equals the target argmax and emits the target token at the first
+ *     mismatch.
+ *   - "AdaPLD" page, section 3.3 and Algorithm 1: a draft token tree (main copy
+ *     path, branches, successors) verified in one target pass; the accepted
+ *     tokens end with the bonus token, and an empty acceptance is one
+ *     autoregressive step.
+ *
+ * Conventions shared by all entry points:
+ *   - Every pointer argument is a DEVICE pointer owned by the caller; the
+ *     library keeps no reference after the call returns.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; 0 = the null stream).
+ *     They return after enqueueing; results are valid once the stream reaches
+ *     that point.
+ *   - Scalar and pointer arguments are checked on the host before anything is
+ *     launched; on failure the call returns SV_ERR_INVALID_ARG (or
+ *     SV_ERR_UNSUPPORTED / SV_ERR_WORKSPACE) and launches nothing.
+ *   - Logit tensors are row-major, contiguous in V; dtype SV_F32 (IEEE binary32)
+ *     or SV_BF16 (bfloat16).  Logits must not be NaN or +inf; -inf entries are
+ *     allowed and mean probability 0, but every row needs a finite entry.
+ *     Logit pointers aligned to 16 bytes with V*sizeof(dtype) a multiple of 16
+ *     take the vectorised path; other layouts are supported at lower speed.
+ *   - Token ids outside [0, V) are never used as addresses: a chain draft id
+ *     outside [0, V) is rejected at its position (stochastic: its ratio is 0;
+ *     greedy: it never matches) and reported in req_status.
+ *   - Argmax ties are broken to the lowest vocabulary index.
+ *   - The same inputs give bit-identical outputs (no floating-point atomics).
+ *   - The workspace is scratch device memory supplied by the caller, of at
+ *     least the size returned by the matching *_workspace_bytes query, aligned
+ *     to 256 bytes.  It holds no state between calls; concurrent calls must
+ *     not share one workspace.
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SV_OK = 0,
+    SV_ERR_INVALID_ARG = 1, /* bad scalar, NULL required pointer, misaligned workspace */
+    SV_ERR_UNSUPPORTED = 2, /* dtype other than SV_F32/SV_BF16, or a size above a limit */
+    SV_ERR_WORKSPACE = 3,   /* workspace_bytes below the required size */
+    SV_ERR_HIP = 4          /* the HIP runtime reported an error while enqueueing */
+} sv_status;
+
+typedef enum { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
+
+/* Largest tree (nodes per request) spec_verify_tree accepts. */
+#define SV_MAX_TREE_NODES 2048
+
+/* Workspace bytes needed by spec_verify_sample for these sizes (0 if the sizes
+ * are invalid). */
+size_t sv_sample_workspace_bytes(int B, int K, int V, sv_dtype dt);
+
+/* Workspace bytes needed by spec_verify_greedy (rows_per_req = K+1) or
+ * spec_verify_tree (rows_per_req = N). */
+size_t sv_greedy_workspace_bytes(int B, int rows_per_req, int V, sv_dtype dt);
+
+/*
+ * Stochastic chain verification (speculative sampling).
+ *
+ *   target_logits [B][K+1][V]  row i (i < K) is the target distribution that
+ *                              scores draft i+1; row K is the bonus row.
+ *   draft_logits  [B][K][V]    row i is the draft distribution that proposed
+ *                              draft i+1 (may be NULL when K = 0).
+ *   draft_tokens  [B][K]       int32 draft ids.
+ *   u_accept      [B][K]       float32 uniforms in [0,1): draft i is accepted
+ *                              iff u_accept[b][i] < p_i(x)/q_i(x).
+ *   u_sample      [B][K+1]     float32 uniforms in [0,1); entry n is used for
+ *                              the token drawn at row n (residual if n < K,
+ *                              bonus if n = K); other entries are ignored.
+ *   temperature   T > 0, finite; p = softmax(target/T), q = softmax(draft/T).
+ *
+ * Outputs:
+ *   accept_len [B]       n_b in [0, K], accepted drafts.
+ *   out_tokens [B][K+1]  the n_b accepted drafts, then the drawn token, then -1.
+ *   lse_target [B][K+1]  optional (NULL = not written): log sum_v exp(L[v]/T).
+ *   lse_draft  [B][K]    optional: the same for the draft rows.
+ *   req_status [B]       optional: 0, or 1 if a draft id of the request is
+ *                        outside [0, V).
+ *
+ * The drawn token is the smallest id v with positive mass m(v) whose running
+ * mass sum_{w <= v} m(w) exceeds u * Z, Z the total mass (if none, the largest
+ * id with positive mass), where m = max(0, p_n - q_n) after a rejection and
+ * m = p_K for the bonus.  If rounding leaves a zero residual after a rejection
+ * the token is drawn from p_n with the same uniform.
+ */
+sv_status spec_verify_sample(const void *target_logits, const void *draft_logits,
+                             const int32_t *draft_tokens, const float *u_accept,
+                             const float *u_sample, int B, int K, int V, sv_dtype dt,
+                             float temperature, int32_t *accept_len, int32_t *out_tokens,
+                             float *lse_target, float *lse_draft, int32_t *req_status,
+                             void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Greedy chain verification.
+ *
+ *   target_logits [B][K+1][V], draft_tokens [B][K] (K >= 0).
+ *   accept_len [B]      n_b = first i with draft_tokens[b][i] != argmax(row i),
+ *                       else K.
+ *   out_tokens [B][K+1] drafts 0..n_b-1, argmax(row n_b), then -1.
+ *   req_status [B]      optional: 0, or 1 if a draft id is outside [0, V).
+ */
+sv_status spec_verify_greedy(const void *target_logits, const int32_t *draft_tokens, int B, int K,
+                             int V, sv_dtype dt, int32_t *accept_len, int32_t *out_tokens,
+                             int32_t *req_status, void *workspace, size_t workspace_bytes,
+                             void *stream);
+
+/*
+ * Greedy tree verification (AdaPLD-style draft trees).
+ *
+ *   target_logits [B][N][V]  row j is the target prediction after the path
+ *                            that ends at node j.
+ *   node_tokens   [B][N]     node 0 is the root (its token is not verified).
+ *   parents       [B][N]     parents[b][0] = -1 and 0 <= parents[b][j] < j.
+ *   1 <= N <= SV_MAX_TREE_NODES.
+ *
+ * Node j >= 1 is accepted iff its parent is accepted and node_tokens[b][j] ==
+ * argmax(row parents[b][j]); the root is accepted.  The chosen node is the
+ * deepest accepted node (lowest index among equals).
+ *   accept_len [B]      depth of the chosen node, or -1 if the parent array is
+ *                       malformed (then path_nodes and out_tokens are all -1).
+ *   path_nodes [B][N]   node ids on the path from depth 1 to the chosen node,
+ *                       then -1 (for compacting the target's cache).
+ *   out_tokens [B][N]   tokens of those nodes, then argmax(row of the chosen
+ *                       node) as the bonus, then -1.
+ *   req_status [B]      optional: 0, 1 if a node id (j >= 1) is outside
+ *                       [0, V), 2 if the parent array is malformed.
+ */
+sv_status spec_verify_tree(const void *target_logits, const int32_t *node_tokens,
+                           const int32_t *parents, int B, int N, int V, sv_dtype dt,
+                           int32_t *accept_len, int32_t *path_nodes, int32_t *out_tokens,
+                           int32_t *req_status, void *workspace, size_t workspace_bytes,
+                           void *stream);
+
+/* Human-readable name of a status code (static storage). */
+const char *sv_status_string(sv_status s);
+
+/* Library version string (static storage). */
+const char *sv_version(void);
+
+/*
+ * Per-kernel timing.  Between sv_trace_begin(capacity) and sv_trace_end(), every
+ * kernel the library launches is bracketed by a pair of HIP events recorded on
+ * the stream it runs on (up to `capacity` launches; later ones are not timed).
+ * sv_trace_end waits for the recorded events, writes up to `max_records`
+ * records (kernel id, elapsed milliseconds) and returns how many launches were
+ * recorded.  Not thread-safe; meant for benchmarking.
+ */
+typedef struct {
+    int kernel; /* an sv_kernel_id */
+    float ms;   /* elapsed time between the two events */
+} sv_kernel_time;
+
+typedef enum {
+    SV_K_ROWSTATS = 0,     /* per-row max / sum-exp partials of target and draft rows */
+    SV_K_ACCEPT = 1,       /* merge partials, acceptance scan, lse outputs */
+    SV_K_RESID_MASS = 2,   /* residual / bonus mass per tile of the chosen row */
+    SV_K_RESID_SELECT = 3, /* inverse-CDF selection of the drawn token */
+    SV_K_ARGMAX = 4,       /* per-row argmax partials */
+    SV_K_MATCH = 5,        /* greedy chain acceptance */
+    SV_K_TREE = 6,         /* greedy tree walk */
+    SV_K_COUNT = 7
+} sv_kernel_id;
+
+sv_status sv_trace_begin(int capacity);
+int sv_trace_end(sv_kernel_time *records, int max_records);
+const char *sv_kernel_name(int kernel);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_VERIFY_H */

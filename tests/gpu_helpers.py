@@ -1,0 +1,109 @@
+"""Shared helpers of the GPU parity tests: move seeded host inputs to the GPU,
+run the HIP path through the C ABI, run the oracle, and compare.
+
+Comparison rules:
+* greedy chains and trees: every output bit-exact;
+* stochastic chains: accept_len and tokens exact for every request whose
+  oracle margin (distance of a consumed uniform to its acceptance ratio or
+  inverse-CDF cell edge) exceeds 1e-6; such "flagged" requests are counted;
+* row log-sum-exp: |gpu - oracle| <= 1e-5 |oracle| (+1e-6 absolute floor for
+  values near zero).
+"""
+
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import draft_token_verification_04_amd as sv
+import oracle
+
+FLAG_EPS = 1e-6
+LSE_RTOL = 1e-5
+
+
+def dev():
+    if not torch.cuda.is_available():
+        raise RuntimeError("GPU tests need a visible ROCm GPU")
+    return torch.device("cuda:0")
+
+
+def note(msg: str) -> None:
+    """Name the case on stdout before its GPU step (survives a crash)."""
+    print(f"[case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def logits_to_dev(a: np.ndarray) -> torch.Tensor:
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev())
+    return torch.from_numpy(a.astype(np.float32, copy=False)).to(dev())
+
+
+def ints_to_dev(a) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev())
+
+
+def f32_to_dev(a) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev())
+
+
+def gpu_sample(w, **kw):
+    g = sv.spec_verify_sample(logits_to_dev(w.target), logits_to_dev(w.draft) if w.K else None,
+                              ints_to_dev(w.draft_tokens), f32_to_dev(w.u_accept),
+                              f32_to_dev(w.u_sample), w.T, **kw)
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy() for k, v in g.items()}
+
+
+def gpu_greedy(w, **kw):
+    g = sv.spec_verify_greedy(logits_to_dev(w.target), ints_to_dev(w.draft_tokens), **kw)
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy() for k, v in g.items()}
+
+
+def gpu_tree(w, **kw):
+    g = sv.spec_verify_tree(logits_to_dev(w.target), ints_to_dev(w.node_tokens),
+                            ints_to_dev(w.parents), **kw)
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy() for k, v in g.items()}
+
+
+def oracle_sample(w):
+    return oracle.verify_sample(w.target, w.draft if w.K else np.zeros((w.B, 0, w.V), w.target.dtype),
+                                w.draft_tokens, w.u_accept, w.u_sample, w.T)
+
+
+def check_lse(gpu, ref):
+    gpu = np.asarray(gpu, np.float64)
+    tol = LSE_RTOL * np.abs(ref) + 1e-6
+    bad = np.abs(gpu - ref) > tol
+    assert not bad.any(), f"lse mismatch at {np.argwhere(bad)[:5]}: {gpu[bad][:5]} vs {ref[bad][:5]}"
+
+
+def check_sample(w, g, o):
+    """Assert parity; return (#unflagged compared, #flagged, #flagged that differ)."""
+    flagged = o["margin"] <= FLAG_EPS
+    ok = ~flagged
+    na = np.nonzero(ok & (g["accept_len"] != o["accept_len"]))[0]
+    assert na.size == 0, (f"accept_len differs at {na[:8]}: gpu {g['accept_len'][na[:8]]} "
+                          f"oracle {o['accept_len'][na[:8]]} margins {o['margin'][na[:8]]}")
+    nt = np.nonzero(ok & (g["tokens"] != o["tokens"]).any(1))[0]
+    assert nt.size == 0, (f"tokens differ at {nt[:8]}: gpu {g['tokens'][nt[:4]]} "
+                          f"oracle {o['tokens'][nt[:4]]} margins {o['margin'][nt[:8]]} Z {o['Z'][nt[:8]]}")
+    if "lse_target" in g:
+        check_lse(g["lse_target"], o["lse_target"])
+        check_lse(g["lse_draft"], o["lse_draft"])
+    if "status" in g:
+        assert np.array_equal(g["status"], o["status"])
+    diff = flagged & ((g["accept_len"] != o["accept_len"]) | (g["tokens"] != o["tokens"]).any(1))
+    return int(ok.sum()), int(flagged.sum()), int(diff.sum())
+
+
+def check_exact(g, o, keys):
+    for k in keys:
+        bad = np.nonzero((np.asarray(g[k]) != np.asarray(o[k])).reshape(len(g[k]), -1).any(1))[0]
+        assert bad.size == 0, f"{k} differs at requests {bad[:8]}: gpu {g[k][bad[:3]]} oracle {o[k][bad[:3]]}"

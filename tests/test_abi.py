@@ -1,0 +1,129 @@
+"""The C-ABI library loads and exports what include/spec_verify.h declares;
+host-side argument checks return their status codes (CPU only: nothing here
+launches a kernel or touches a GPU)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import draft_token_verification_04_amd as sv
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                      "spec_verify.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\**\s*([a-z_][a-z0-9_]*)\s*\(",
+                       text, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return sv.load_library()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert set(names) >= {"spec_verify_sample", "spec_verify_greedy", "spec_verify_tree"}
+    assert set(names) == set(sv.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings(lib):
+    assert b"gfx950" in lib.sv_version()
+    for code in range(5):
+        assert lib.sv_status_string(code)
+    assert lib.sv_kernel_name(0) == b"rowstats"
+    assert lib.sv_kernel_name(99) == b"unknown"
+
+
+def test_workspace_queries(lib):
+    V = 151936
+    a = lib.sv_sample_workspace_bytes(256, 7, V, sv.SV_BF16)
+    assert a > 0 and a % 256 == 0
+    assert lib.sv_sample_workspace_bytes(256, 7, V, 9) == 0
+    assert lib.sv_sample_workspace_bytes(-1, 7, V, sv.SV_BF16) == 0
+    assert lib.sv_sample_workspace_bytes(1, 5000, V, sv.SV_BF16) == 0
+    g = lib.sv_greedy_workspace_bytes(512, 8, V, sv.SV_BF16)
+    assert g > 0 and lib.sv_greedy_workspace_bytes(512, 0, V, sv.SV_BF16) == 0
+    # workspace grows with B
+    assert lib.sv_greedy_workspace_bytes(1024, 8, V, sv.SV_BF16) > g
+
+
+FAKE = ctypes.c_void_p(1 << 20)  # a non-null, 256-aligned address that is never dereferenced
+
+
+def _sample(lib, **kw):
+    a = dict(t=FAKE, d=FAKE, x=FAKE, ua=FAKE, us=FAKE, B=2, K=3, V=100, dt=sv.SV_BF16, T=1.0,
+             n=FAKE, tok=FAKE, lt=None, ld=None, st=None, ws=FAKE, wsb=0, s=None)
+    a.update(kw)
+    return lib.spec_verify_sample(a["t"], a["d"], a["x"], a["ua"], a["us"], a["B"], a["K"], a["V"],
+                                  a["dt"], a["T"], a["n"], a["tok"], a["lt"], a["ld"], a["st"],
+                                  a["ws"], a["wsb"], a["s"])
+
+
+def test_sample_argument_checks(lib):
+    assert _sample(lib, dt=5) == sv.SV_ERR_UNSUPPORTED
+    assert _sample(lib, B=-1) == sv.SV_ERR_INVALID_ARG
+    assert _sample(lib, K=-1) == sv.SV_ERR_INVALID_ARG
+    assert _sample(lib, V=0) == sv.SV_ERR_INVALID_ARG
+    assert _sample(lib, T=0.0) == sv.SV_ERR_INVALID_ARG
+    assert _sample(lib, T=-1.0) == sv.SV_ERR_INVALID_ARG
+    assert _sample(lib, T=float("nan")) == sv.SV_ERR_INVALID_ARG
+    assert _sample(lib, T=float("inf")) == sv.SV_ERR_INVALID_ARG
+    assert _sample(lib, K=5000) == sv.SV_ERR_UNSUPPORTED
+    assert _sample(lib, t=None) == sv.SV_ERR_INVALID_ARG
+    assert _sample(lib, d=None) == sv.SV_ERR_INVALID_ARG
+    assert _sample(lib, us=None) == sv.SV_ERR_INVALID_ARG
+    assert _sample(lib, n=None) == sv.SV_ERR_INVALID_ARG
+    assert _sample(lib, ws=None) == sv.SV_ERR_INVALID_ARG
+    assert _sample(lib, ws=ctypes.c_void_p((1 << 20) + 16)) == sv.SV_ERR_INVALID_ARG
+    assert _sample(lib, wsb=0) == sv.SV_ERR_WORKSPACE
+    need = lib.sv_sample_workspace_bytes(2, 3, 100, sv.SV_BF16)
+    assert _sample(lib, wsb=need - 1) == sv.SV_ERR_WORKSPACE
+    # K = 0 needs no draft tensors; B = 0 is an empty batch (no launch)
+    assert _sample(lib, K=0, d=None, x=None, ua=None, wsb=0) == sv.SV_ERR_WORKSPACE
+    assert _sample(lib, B=0, t=None, ws=None) == sv.SV_OK
+
+
+def test_greedy_and_tree_argument_checks(lib):
+    g = lambda **k: lib.spec_verify_greedy(k.get("t", FAKE), k.get("x", FAKE), k.get("B", 2),
+                                           k.get("K", 3), k.get("V", 100), k.get("dt", 1),
+                                           k.get("n", FAKE), k.get("tok", FAKE), None,
+                                           k.get("ws", FAKE), k.get("wsb", 0), None)
+    assert g(dt=3) == sv.SV_ERR_UNSUPPORTED
+    assert g(B=-2) == sv.SV_ERR_INVALID_ARG
+    assert g(V=-5) == sv.SV_ERR_INVALID_ARG
+    assert g(x=None) == sv.SV_ERR_INVALID_ARG
+    assert g(tok=None) == sv.SV_ERR_INVALID_ARG
+    assert g() == sv.SV_ERR_WORKSPACE
+    assert g(K=0, x=None) == sv.SV_ERR_WORKSPACE
+    assert g(B=0, t=None) == sv.SV_OK
+    t = lambda **k: lib.spec_verify_tree(k.get("t", FAKE), k.get("tok", FAKE), k.get("par", FAKE),
+                                         k.get("B", 2), k.get("N", 33), k.get("V", 100),
+                                         k.get("dt", 1), FAKE, FAKE, FAKE, None,
+                                         k.get("ws", FAKE), k.get("wsb", 0), None)
+    assert t(N=0) == sv.SV_ERR_INVALID_ARG
+    assert t(N=sv.SV_MAX_TREE_NODES + 1) == sv.SV_ERR_UNSUPPORTED
+    assert t(par=None) == sv.SV_ERR_INVALID_ARG
+    assert t() == sv.SV_ERR_WORKSPACE
+    assert t(B=0) == sv.SV_OK
+
+
+def test_trace_end_without_begin_is_empty(lib):
+    assert sv.trace_end() == []
+
+
+def test_binding_refuses_without_gpu():
+    import torch
+
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible")
+    with pytest.raises(RuntimeError):
+        sv.spec_verify_greedy(torch.zeros(1, 2, 8), torch.zeros(1, 1, dtype=torch.int32))

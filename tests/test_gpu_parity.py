@@ -1,0 +1,273 @@
+"""HIP path vs the CPU oracle, through the C ABI (needs an MI355X).
+
+Sizes: small grids that span several segments/tiles with ragged tails
+(including V not a multiple of the 16-byte vector, and misaligned pointers),
+then the five workloads at full size in the launch configuration the
+benchmark times.
+"""
+
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import draft_token_verification_04_amd as sv
+import golden_cases as gc
+import oracle
+import workloads
+from gpu_helpers import (check_exact, check_lse, check_sample, dev, gpu_greedy, gpu_sample,
+                         gpu_tree, ints_to_dev, logits_to_dev, f32_to_dev, note, oracle_sample)
+
+pytestmark = pytest.mark.gpu
+
+
+def test_library_is_the_hip_build():
+    note("library load")
+    assert torch.cuda.is_available()
+    assert "gfx950" in sv.version()
+    assert "gfx950" in torch.cuda.get_device_properties(0).gcnArchName
+
+
+SAMPLE_GRID = [
+    # B, K, V, dtype, T, spikes, noise
+    (1, 1, 8, "f32", 1.0, 0, 0.5),
+    (3, 4, 1000, "f32", 1.0, 0, 0.5),
+    (5, 3, 1001, "bf16", 0.7, 0, 1.0),      # ragged, unaligned bf16 rows
+    (7, 7, 4100, "bf16", 1.3, 5, 1.0),      # V % 8 = 4: unaligned for bf16
+    (4, 7, 4100, "f32", 0.9, 5, 2.0),       # aligned for f32
+    (33, 2, 37, "bf16", 1.0, 0, 3.0),
+    (2, 7, 151936, "bf16", 0.7, 20, 0.3),   # many segments and tiles per row
+    (9, 1, 70001, "f32", 1.0, 3, 0.1),      # high acceptance, ragged
+    (16, 0, 5000, "bf16", 1.0, 0, 1.0),     # K = 0: bonus draw only
+]
+
+
+@pytest.mark.parametrize("case", SAMPLE_GRID, ids=lambda c: "B{}K{}V{}{}T{}".format(*c[:5]))
+def test_sample_grid(case):
+    B, K, V, dt, T, spikes, noise = case
+    note(f"sample grid {case}")
+    w = workloads.make_sample(B, K, V, dt, T, target_sigma=3.0, spikes=spikes, noise_sigma=noise,
+                              seed=zlib.crc32(repr(case).encode()))
+    o = oracle_sample(w)
+    g = gpu_sample(w)
+    ncmp, nflag, ndiff = check_sample(w, g, o)
+    assert ncmp + nflag == B
+
+
+@pytest.mark.parametrize("c", [1, 2, 3])
+def test_sample_workloads_full_size(c):
+    note(f"sample workload {c}")
+    w = workloads.make_config(c)
+    o = oracle_sample(w)
+    g = gpu_sample(w)
+    ncmp, nflag, ndiff = check_sample(w, g, o)
+    print(f"workload {c}: compared {ncmp}, flagged {nflag}, flagged-and-different {ndiff}, "
+          f"mean accept {g['accept_len'].mean():.3f}")
+
+
+GREEDY_GRID = [(1, 0, 8, "f32"), (5, 3, 1000, "bf16"), (6, 7, 1001, "bf16"), (33, 7, 4100, "f32"),
+               (3, 7, 151936, "bf16"), (64, 70, 333, "bf16"), (2, 1, 1, "f32")]
+
+
+@pytest.mark.parametrize("case", GREEDY_GRID, ids=lambda c: "B{}K{}V{}{}".format(*c))
+def test_greedy_grid(case):
+    B, K, V, dt = case
+    note(f"greedy grid {case}")
+    w = workloads.make_greedy(B, K, V, dt, seed=B * 1000 + K)
+    o = oracle.verify_greedy(w.target, w.draft_tokens)
+    g = gpu_greedy(w)
+    check_exact(g, o, ("accept_len", "tokens", "status"))
+
+
+def test_greedy_ties_and_signed_zeros():
+    note("greedy ties")
+    rng = np.random.default_rng(5)
+    B, K, V = 256, 5, 3000
+    L = rng.integers(-3, 4, size=(B, K + 1, V)).astype(np.float32)
+    L[:8] = -0.0
+    L[8:16] = 0.0
+    L[8:16, :, ::7] = -0.0
+    am = np.argmax(L, -1)
+    x = np.where(rng.random((B, K)) < 0.7, am[:, :K], rng.integers(0, V, (B, K))).astype(np.int32)
+    for dt in ("f32", "bf16"):
+        LL = L if dt == "f32" else workloads.to_bf16_bits(L)
+        w = workloads.Workload(mode="greedy", B=B, K=K, V=V, dtype=dt, target=LL, draft_tokens=x)
+        check_exact(gpu_greedy(w), oracle.verify_greedy(LL, x), ("accept_len", "tokens", "status"))
+
+
+@pytest.mark.parametrize("B", [512, 256])
+def test_greedy_workload_full_size(B):
+    note(f"greedy workload 4 B={B}")
+    w = workloads.make_config(4, B=B)
+    o = oracle.verify_greedy(w.target, w.draft_tokens)
+    g = gpu_greedy(w)
+    check_exact(g, o, ("accept_len", "tokens", "status"))
+
+
+def test_tree_small_random_and_degenerate():
+    note("tree small")
+    rng = np.random.default_rng(12)
+    for (B, N, V, dt) in [(50, 12, 4, "f32"), (40, 33, 1001, "bf16"), (8, 300, 64, "bf16"),
+                          (3, 1, 100, "f32")]:
+        L = rng.integers(-1, 2, size=(B, N, V)).astype(np.float32) if V < 10 else \
+            rng.standard_normal((B, N, V)).astype(np.float32)
+        LL = L if dt == "f32" else workloads.to_bf16_bits(L)
+        par = np.empty((B, N), np.int32)
+        par[:, 0] = -1
+        for j in range(1, N):
+            par[:, j] = rng.integers(0, j, size=B)
+        if B >= 20:
+            par[:5] = np.arange(-1, N - 1)    # chains
+            par[5:10, 1:] = 0                 # stars
+        am = oracle.argmax(LL)
+        pam = np.take_along_axis(am, np.maximum(par, 0), 1)
+        tok = np.where(rng.random((B, N)) < 0.6, pam, rng.integers(0, V, (B, N))).astype(np.int32)
+        if B >= 20:
+            tok[10, 3] = V + 5                # out-of-range node id
+            par[11, 4] = 9 if N > 9 else -1   # malformed parent array
+            par[12, 0] = 0
+        w = workloads.Workload(mode="tree", B=B, N=N, V=V, dtype=dt, target=LL, node_tokens=tok,
+                               parents=par)
+        check_exact(gpu_tree(w), oracle.verify_tree(LL, tok, par),
+                    ("accept_len", "path", "tokens", "status"))
+
+
+def test_tree_workload_full_size():
+    note("tree workload 5")
+    w = workloads.make_config(5)
+    o = oracle.verify_tree(w.target, w.node_tokens, w.parents)
+    check_exact(gpu_tree(w), o, ("accept_len", "path", "tokens", "status"))
+
+
+def test_chain_shaped_tree_equals_greedy_chain():
+    note("chain tree")
+    w = workloads.make_greedy(64, 9, 2000, "bf16", seed=3)
+    par = np.tile(np.arange(-1, 9, dtype=np.int32), (64, 1))
+    tok = np.concatenate([np.zeros((64, 1), np.int32), w.draft_tokens], 1)
+    t = gpu_tree(workloads.Workload(mode="tree", B=64, N=10, V=2000, dtype="bf16",
+                                    target=w.target, node_tokens=tok, parents=par))
+    g = gpu_greedy(w)
+    assert np.array_equal(t["accept_len"], g["accept_len"])
+    assert np.array_equal(t["tokens"], g["tokens"])
+
+
+def test_hand_worked_examples_on_gpu():
+    note("golden")
+    g = gc.load()
+    for c in g["sample"]:
+        tgt, dr, x, ua, us = gc.sample_arrays(c)
+        K = x.shape[1]
+        o = sv.spec_verify_sample(logits_to_dev(tgt), logits_to_dev(dr) if K else None,
+                                  ints_to_dev(x), f32_to_dev(ua), f32_to_dev(us), 1.0)
+        assert int(o["accept_len"][0]) == c["accept_len"], c["name"]
+        assert o["tokens"][0].tolist() == c["tokens"], c["name"]
+    for c in g["greedy"]:
+        tgt, x = gc.greedy_arrays(c)
+        o = sv.spec_verify_greedy(logits_to_dev(tgt), ints_to_dev(x))
+        assert int(o["accept_len"][0]) == c["accept_len"], c["name"]
+        assert o["tokens"][0].tolist() == c["tokens"], c["name"]
+    for c in g["tree"]:
+        tgt, tok, par = gc.tree_arrays(c)
+        o = sv.spec_verify_tree(logits_to_dev(tgt), ints_to_dev(tok), ints_to_dev(par))
+        assert int(o["accept_len"][0]) == c["accept_len"], c["name"]
+        assert o["path"][0].tolist() == c["path"], c["name"]
+        assert o["tokens"][0].tolist() == c["tokens"], c["name"]
+
+
+def test_masked_vocabulary_and_out_of_range_drafts():
+    note("masked vocab / OOR drafts")
+    rng = np.random.default_rng(21)
+    B, K, V = 24, 4, 3000
+    w = workloads.make_sample(B, K, V, "f32", 1.0, spikes=0, noise_sigma=0.7, seed=9)
+    mask = rng.random((B, K + 1, V)) < 0.3
+    w.target[mask] = -np.inf
+    w.draft[mask[:, :K]] = -np.inf
+    w.draft_tokens[3, 1] = V + 7
+    w.draft_tokens[4, 0] = -2
+    w.u_accept[:] = 0.0  # accept everything that can be accepted
+    o = oracle_sample(w)
+    g = gpu_sample(w)
+    check_sample(w, g, o)
+    assert g["status"][3] == 1 and g["status"][4] == 1 and g["accept_len"][4] == 0
+    # masked ids are never drawn
+    for b in range(B):
+        n = g["accept_len"][b]
+        t = g["tokens"][b, n]
+        assert not mask[b, n, t]
+
+
+def test_empty_batch_and_determinism():
+    note("empty batch / determinism")
+    w = workloads.make_sample(0, 3, 100, "bf16", 1.0, seed=1)
+    g = gpu_sample(w)
+    assert g["accept_len"].shape == (0,)
+    w = workloads.make_sample(12, 7, 20000, "bf16", 0.8, spikes=20, noise_sigma=1.0, seed=2)
+    a, b = gpu_sample(w), gpu_sample(w)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+    wg = workloads.make_greedy(12, 7, 20000, "bf16", seed=2)
+    a, b = gpu_greedy(wg), gpu_greedy(wg)
+    assert np.array_equal(a["tokens"], b["tokens"])
+
+
+def test_misaligned_pointers_take_the_general_path():
+    note("misaligned pointers")
+    w = workloads.make_sample(6, 3, 4096, "bf16", 1.0, spikes=3, noise_sigma=1.0, seed=4)
+    o = oracle_sample(w)
+    base_t = torch.empty(w.target.size + 1, dtype=torch.bfloat16, device=dev())
+    base_d = torch.empty(w.draft.size + 1, dtype=torch.bfloat16, device=dev())
+    t = base_t[1:].view(w.target.shape)
+    d = base_d[1:].view(w.draft.shape)
+    t.copy_(logits_to_dev(w.target))
+    d.copy_(logits_to_dev(w.draft))
+    assert t.data_ptr() % 16 != 0
+    g = sv.spec_verify_sample(t, d, ints_to_dev(w.draft_tokens), f32_to_dev(w.u_accept),
+                              f32_to_dev(w.u_sample), w.T)
+    g = {k: v.cpu().numpy() for k, v in g.items()}
+    check_sample(w, g, o)
+    wg = workloads.make_greedy(6, 3, 4096, "bf16", seed=4)
+    base = torch.empty(wg.target.size + 1, dtype=torch.bfloat16, device=dev())
+    tt = base[1:].view(wg.target.shape)
+    tt.copy_(logits_to_dev(wg.target))
+    gg = sv.spec_verify_greedy(tt, ints_to_dev(wg.draft_tokens))
+    check_exact({k: v.cpu().numpy() for k, v in gg.items()},
+                oracle.verify_greedy(wg.target, wg.draft_tokens), ("accept_len", "tokens"))
+
+
+def test_lse_only_rows_and_temperature_extremes():
+    note("lse temperature extremes")
+    for T in (0.05, 0.7, 4.0):
+        w = workloads.make_sample(4, 2, 9000, "bf16", T, spikes=4, noise_sigma=0.5, seed=int(T * 100))
+        o = oracle_sample(w)
+        g = gpu_sample(w)
+        check_lse(g["lse_target"], o["lse_target"])
+        check_sample(w, g, o)
+
+
+def test_workspace_reuse_with_shrinking_batches():
+    note("workspace reuse")
+    big = workloads.make_sample(40, 7, 8000, "bf16", 1.0, spikes=5, noise_sigma=1.0, seed=31)
+    need = sv.sample_workspace_bytes(40, 7, 8000, sv.SV_BF16)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev())
+    for B in (40, 17, 3):
+        w = workloads.make_sample(B, 7, 8000, "bf16", 1.0, spikes=5, noise_sigma=1.0, seed=B)
+        g = sv.spec_verify_sample(logits_to_dev(w.target), logits_to_dev(w.draft),
+                                  ints_to_dev(w.draft_tokens), f32_to_dev(w.u_accept),
+                                  f32_to_dev(w.u_sample), w.T, workspace=ws)
+        g = {k: v.cpu().numpy() for k, v in g.items()}
+        check_sample(w, g, oracle_sample(w))
+    with pytest.raises(sv.SpecVerifyError):
+        sv.spec_verify_sample(logits_to_dev(big.target), logits_to_dev(big.draft),
+                              ints_to_dev(big.draft_tokens), f32_to_dev(big.u_accept),
+                              f32_to_dev(big.u_sample), big.T, workspace=ws[:1024])
+
+
+def test_trace_records_each_kernel():
+    note("trace")
+    w = workloads.make_sample(8, 3, 5000, "bf16", 1.0, seed=5)
+    sv.trace_begin(64)
+    gpu_sample(w)
+    recs = sv.trace_end()
+    assert [r[0] for r in recs] == ["rowstats", "accept", "resid_mass", "resid_select"]
+    assert all(ms > 0 for _, ms in recs)
