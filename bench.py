@@ -54,6 +54,9 @@ def parse():
     ap.add_argument("--mode", choices=("all", "sample", "greedy", "tree"), default="all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (default: up to 16)")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="before timing, run a plain elementwise copy (negation) kernel that reads "
+                         "and writes this many MiB, as the reference for HBM counter scaling")
     return ap.parse_args()
 
 
@@ -204,6 +207,13 @@ def main():
         for m in active:
             parts[m]()
 
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
