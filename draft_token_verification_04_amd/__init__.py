@@ -69,7 +69,7 @@ def load_library(path: str = LIB_PATH):
     lib.sv_status_string.restype = ctypes.c_char_p
     lib.sv_version.argtypes = []
     lib.sv_version.restype = ctypes.c_char_p
-    lib.sv_trace_begin.argtypes = [I]
+    lib.sv_trace_begin.argtypes = [I, ctypes.c_uint]
     lib.sv_trace_begin.restype = I
     lib.sv_trace_end.argtypes = [ctypes.POINTER(KernelTime), I]
     lib.sv_trace_end.restype = I
@@ -264,8 +264,12 @@ def spec_verify_tree(target, node_tokens, parents, *, status=True, workspace=Non
 
 # ---- per-kernel timing -----------------------------------------------------------
 
-def trace_begin(capacity: int = 4096) -> None:
-    rc = load_library().sv_trace_begin(capacity)
+def trace_begin(capacity: int = 4096, kernels=None) -> None:
+    """Time every launch (kernels=None) or only the named kernels."""
+    mask = 0
+    for k in kernels or ():
+        mask |= 1 << KERNELS.index(k)
+    rc = load_library().sv_trace_begin(capacity, mask)
     if rc != SV_OK:
         raise SpecVerifyError(rc, "sv_trace_begin")
 

@@ -4,6 +4,7 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include <algorithm>
 #include <mutex>
 #include <vector>
 
@@ -12,11 +13,11 @@
 
 namespace sv {
 
-RowGeom row_geom(int V, sv_dtype dt, bool ptrs_aligned) {
+RowGeom row_geom(int V, sv_dtype dt, bool ptrs_aligned, int vecs_per_lane) {
     RowGeom g;
     g.per_vec = dt == SV_BF16 ? 8 : 4;
     g.nvec = (V + g.per_vec - 1) / g.per_vec;
-    const int per_wave = kWave * kStreamVecsPerLane;
+    const int per_wave = kWave * vecs_per_lane;
     g.segs = (g.nvec + per_wave - 1) / per_wave;
     if (g.segs < 1) g.segs = 1;
     g.ntiles = (g.nvec + kWave - 1) / kWave;
@@ -45,14 +46,19 @@ SampleWs sample_ws_layout(int B, int K, const RowGeom &g) {
     return w;
 }
 
+int resid_tiles_per_wave(int B, int ntiles) {
+    const long long total = static_cast<long long>(B) * ntiles;
+    long long t = (total + kResidTargetWaves - 1) / kResidTargetWaves;
+    t = ((t + kResidGroup - 1) / kResidGroup) * kResidGroup;
+    return static_cast<int>(std::max<long long>(kResidGroup, std::min<long long>(t, 64)));
+}
+
 GreedyWs greedy_ws_layout(long long rows, const RowGeom &g) {
     GreedyWs w;
     const size_t parts = static_cast<size_t>(rows) * static_cast<size_t>(g.segs);
     size_t o = 0;
-    w.part_v = o;
-    o = align_up(o + parts * sizeof(float));
-    w.part_i = o;
-    o = align_up(o + parts * sizeof(int32_t));
+    w.part_k = o;
+    o = align_up(o + parts * sizeof(uint64_t));
     w.total = o;
     return w;
 }
@@ -79,8 +85,9 @@ struct Tracer {
     bool on = false;
     int capacity = 0;
     int used = 0;
+    unsigned mask = 0;
+    int next_kernel = -1;
     std::vector<TraceRec> recs;
-    int pending = -1;  // index of the record whose stop event is due
 };
 Tracer &tracer() {
     static Tracer t;
@@ -88,23 +95,24 @@ Tracer &tracer() {
 }
 }  // namespace
 
-void trace_pre(int kernel, hipStream_t s) {
+void trace_select(int kernel) {
     Tracer &t = tracer();
     std::lock_guard<std::mutex> g(t.mu);
-    t.pending = -1;
-    if (!t.on || t.used >= t.capacity) return;
-    TraceRec &r = t.recs[t.used];
-    r.kernel = kernel;
-    if (hipEventRecord(r.start, s) != hipSuccess) return;
-    t.pending = t.used++;
+    t.next_kernel = kernel;
 }
 
-void trace_post(hipStream_t s) {
+bool trace_events(hipEvent_t *start, hipEvent_t *stop) {
     Tracer &t = tracer();
     std::lock_guard<std::mutex> g(t.mu);
-    if (t.pending < 0) return;
-    (void)hipEventRecord(t.recs[t.pending].stop, s);
-    t.pending = -1;
+    const int k = t.next_kernel;
+    t.next_kernel = -1;
+    if (!t.on || k < 0 || t.used >= t.capacity) return false;
+    if (t.mask != 0 && !(t.mask & (1u << k))) return false;
+    TraceRec &r = t.recs[t.used++];
+    r.kernel = k;
+    *start = r.start;
+    *stop = r.stop;
+    return true;
 }
 
 }  // namespace sv
@@ -117,13 +125,11 @@ bool valid_dtype(sv_dtype dt) { return dt == SV_F32 || dt == SV_BF16; }
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned256(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
 
-// Every launch goes through here so tracing sees it.
+// Every launch goes through here so tracing knows which kernel it is.
 template <typename F>
-hipError_t traced(int kernel, hipStream_t s, F &&f) {
-    trace_pre(kernel, s);
-    const hipError_t e = f();
-    trace_post(s);
-    return e;
+hipError_t traced(int kernel, hipStream_t, F &&f) {
+    trace_select(kernel);
+    return f();
 }
 
 // Element counts must stay addressable with 64-bit offsets and int32 row lengths.
@@ -138,14 +144,14 @@ bool sizes_ok(long long B, long long rows_per_req, long long V) {
 extern "C" {
 
 size_t sv_sample_workspace_bytes(int B, int K, int V, sv_dtype dt) {
-    if (B < 0 || K < 0 || K > kMaxSampleK || !valid_dtype(dt) || !sizes_ok(B, 2LL * K + 1, V)) return 0;
-    const RowGeom g = row_geom(V, dt, true);
+    if (B < 0 || K < 0 || K > SV_MAX_DRAFT_LEN || !valid_dtype(dt) || !sizes_ok(B, 2LL * K + 1, V)) return 0;
+    const RowGeom g = row_geom(V, dt, true, kStatsVecsPerLane);
     return sample_ws_layout(B, K, g).total;
 }
 
 size_t sv_greedy_workspace_bytes(int B, int rows_per_req, int V, sv_dtype dt) {
     if (B < 0 || rows_per_req < 1 || !valid_dtype(dt) || !sizes_ok(B, rows_per_req, V)) return 0;
-    const RowGeom g = row_geom(V, dt, true);
+    const RowGeom g = row_geom(V, dt, true, kArgmaxVecsPerLane);
     return greedy_ws_layout(static_cast<long long>(B) * rows_per_req, g).total;
 }
 
@@ -158,14 +164,14 @@ sv_status spec_verify_sample(const void *target_logits, const void *draft_logits
     if (!valid_dtype(dt)) return SV_ERR_UNSUPPORTED;
     if (B < 0 || K < 0 || V < 1 || !(temperature > 0.0f) || !isfinite(temperature))
         return SV_ERR_INVALID_ARG;
-    if (K > kMaxSampleK || !sizes_ok(B, 2LL * K + 1, V)) return SV_ERR_UNSUPPORTED;
+    if (K > SV_MAX_DRAFT_LEN || !sizes_ok(B, 2LL * K + 1, V)) return SV_ERR_UNSUPPORTED;
     if (B == 0) return SV_OK;
     if (!target_logits || !u_sample || !accept_len || !out_tokens || !workspace)
         return SV_ERR_INVALID_ARG;
     if (K > 0 && (!draft_logits || !draft_tokens || !u_accept)) return SV_ERR_INVALID_ARG;
     if (!aligned256(workspace)) return SV_ERR_INVALID_ARG;
     const bool ptr_al = aligned16(target_logits) && (K == 0 || aligned16(draft_logits));
-    const RowGeom g = row_geom(V, dt, ptr_al);
+    const RowGeom g = row_geom(V, dt, ptr_al, kStatsVecsPerLane);
     const SampleWs L = sample_ws_layout(B, K, g);
     if (workspace_bytes < L.total) return SV_ERR_WORKSPACE;
 
@@ -208,23 +214,21 @@ sv_status spec_verify_greedy(const void *target_logits, const int32_t *draft_tok
                              void *stream) {
     if (!valid_dtype(dt)) return SV_ERR_UNSUPPORTED;
     if (B < 0 || K < 0 || V < 1) return SV_ERR_INVALID_ARG;
-    if (!sizes_ok(B, static_cast<long long>(K) + 1, V) || K > 0x7ffffff0) return SV_ERR_UNSUPPORTED;
+    if (K > SV_MAX_DRAFT_LEN || !sizes_ok(B, static_cast<long long>(K) + 1, V)) return SV_ERR_UNSUPPORTED;
     if (B == 0) return SV_OK;
     if (!target_logits || !accept_len || !out_tokens || !workspace) return SV_ERR_INVALID_ARG;
     if (K > 0 && !draft_tokens) return SV_ERR_INVALID_ARG;
     if (!aligned256(workspace)) return SV_ERR_INVALID_ARG;
-    const RowGeom g = row_geom(V, dt, aligned16(target_logits));
+    const RowGeom g = row_geom(V, dt, aligned16(target_logits), kArgmaxVecsPerLane);
     const long long rows = static_cast<long long>(B) * (K + 1);
     const GreedyWs L = greedy_ws_layout(rows, g);
     if (workspace_bytes < L.total) return SV_ERR_WORKSPACE;
-    char *ws = static_cast<char *>(workspace);
-    float *pv = reinterpret_cast<float *>(ws + L.part_v);
-    int32_t *pi = reinterpret_cast<int32_t *>(ws + L.part_i);
+    uint64_t *pk = reinterpret_cast<uint64_t *>(static_cast<char *>(workspace) + L.part_k);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = traced(SV_K_ARGMAX, s, [&] { return launch_argmax(target_logits, rows, V, g, dt, pv, pi, s); });
+    hipError_t e = traced(SV_K_ARGMAX, s, [&] { return launch_argmax(target_logits, rows, V, g, dt, pk, s); });
     if (e == hipSuccess)
         e = traced(SV_K_MATCH, s, [&] {
-            return launch_match(pv, pi, draft_tokens, B, K, V, g, accept_len, out_tokens, req_status, s);
+            return launch_match(pk, draft_tokens, B, K, V, g, accept_len, out_tokens, req_status, s);
         });
     return e == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
@@ -242,18 +246,16 @@ sv_status spec_verify_tree(const void *target_logits, const int32_t *node_tokens
         !workspace)
         return SV_ERR_INVALID_ARG;
     if (!aligned256(workspace)) return SV_ERR_INVALID_ARG;
-    const RowGeom g = row_geom(V, dt, aligned16(target_logits));
+    const RowGeom g = row_geom(V, dt, aligned16(target_logits), kArgmaxVecsPerLane);
     const long long rows = static_cast<long long>(B) * N;
     const GreedyWs L = greedy_ws_layout(rows, g);
     if (workspace_bytes < L.total) return SV_ERR_WORKSPACE;
-    char *ws = static_cast<char *>(workspace);
-    float *pv = reinterpret_cast<float *>(ws + L.part_v);
-    int32_t *pi = reinterpret_cast<int32_t *>(ws + L.part_i);
+    uint64_t *pk = reinterpret_cast<uint64_t *>(static_cast<char *>(workspace) + L.part_k);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = traced(SV_K_ARGMAX, s, [&] { return launch_argmax(target_logits, rows, V, g, dt, pv, pi, s); });
+    hipError_t e = traced(SV_K_ARGMAX, s, [&] { return launch_argmax(target_logits, rows, V, g, dt, pk, s); });
     if (e == hipSuccess)
         e = traced(SV_K_TREE, s, [&] {
-            return launch_tree(pv, pi, node_tokens, parents, B, N, V, g, accept_len, path_nodes,
+            return launch_tree(pk, node_tokens, parents, B, N, V, g, accept_len, path_nodes,
                                out_tokens, req_status, s);
         });
     return e == hipSuccess ? SV_OK : SV_ERR_HIP;
@@ -278,7 +280,7 @@ const char *sv_kernel_name(int k) {
     return (k >= 0 && k < SV_K_COUNT) ? names[k] : "unknown";
 }
 
-sv_status sv_trace_begin(int capacity) {
+sv_status sv_trace_begin(int capacity, unsigned kernel_mask) {
     if (capacity < 1) return SV_ERR_INVALID_ARG;
     Tracer &t = tracer();
     std::lock_guard<std::mutex> g(t.mu);
@@ -295,8 +297,9 @@ sv_status sv_trace_begin(int capacity) {
         }
     }
     t.capacity = capacity;
+    t.mask = kernel_mask;
     t.used = 0;
-    t.pending = -1;
+    t.next_kernel = -1;
     t.on = true;
     return SV_OK;
 }

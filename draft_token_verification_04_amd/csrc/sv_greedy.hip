@@ -11,14 +11,18 @@
 //
 // Kernels:
 //   k_argmax  one streaming pass over the target rows; each wave reduces a
-//             segment to (max value, lowest index of that value).
-//   k_match   one wave per request: merges segment partials in index order
-//             (strictly greater replaces, so ties keep the lower segment) and
-//             finds the first mismatch with a ballot.
-//   k_tree    one workgroup per request: partial merge per node, parent-array
-//             check in parallel, then the walk in index order (parents precede
-//             children) and the path write-out.
+//             segment to (max value, lowest index of that value), packed in one
+//             64-bit key whose maximum is the row argmax with ties to the
+//             lowest index.
+//   k_match   one workgroup per request: stages the row keys in LDS, one wave
+//             per row reduces them, then a ballot finds the first mismatch.
+//   k_tree    one workgroup per request: the same key merge per node, the
+//             parent-array check in parallel, acceptance and depth of every
+//             node by pointer jumping (log2 N rounds), the deepest accepted
+//             node by an LDS max, then the path write-out.
 #include <limits.h>
+
+#include <algorithm>
 
 #include "sv_device.hpp"
 #include "sv_internal.hpp"
@@ -29,8 +33,7 @@ namespace {
 template <typename E, bool ALIGNED, int U>
 __global__ __launch_bounds__(kBlock) void k_argmax(const typename E::storage *__restrict__ L,
                                                    long long nwaves, int V, int nvec, int segs,
-                                                   float *__restrict__ part_v,
-                                                   int32_t *__restrict__ part_i) {
+                                                   uint64_t *__restrict__ part_k) {
     constexpr int P = E::kPerVec;
     const int lane = threadIdx.x & (kWave - 1);
     const long long wave = static_cast<long long>(blockIdx.x) * kWavesPerBlock + (threadIdx.x >> 6);
@@ -71,106 +74,120 @@ __global__ __launch_bounds__(kBlock) void k_argmax(const typename E::storage *__
             if (j < v1 && x[e] == m) cand = j * P + e;
     }
     cand = wave_min(cand);
-    if (lane == 0) {
-        part_v[wave] = m;
-        part_i[wave] = cand;
-    }
+    if (lane == 0) part_k[wave] = argmax_key(m, cand);
 }
 
-// Argmax of one row from its segment partials (segments are in index order).
-__device__ __forceinline__ int merge_argmax(const float *__restrict__ pv, const int32_t *__restrict__ pi,
-                                            int segs) {
-    float bv = pv[0];
-    int bi = pi[0];
-    for (int s = 1; s < segs; ++s) {
-        const float v = pv[s];
-        if (v > bv) {
-            bv = v;
-            bi = pi[s];
+// Argmax of `nrows` consecutive rows whose segment keys start at `keys`
+// (segs keys per row), written to out[0..nrows).  The keys of up to
+// `lds_rows` rows at a time are first copied into LDS with every load in
+// flight; then each wave reduces whole rows.  lds_rows = 0 reads global memory
+// directly (rows with too many segments to stage).
+__device__ __forceinline__ void merge_rows(const uint64_t *__restrict__ keys, int nrows, int segs,
+                                           int lds_rows, uint64_t *stage, int *out) {
+    const int tid = threadIdx.x, wid = tid >> 6, lane = tid & (kWave - 1);
+    const int nw = blockDim.x >> 6;
+    const int chunk = lds_rows > 0 ? lds_rows : nrows;
+    for (int r0 = 0; r0 < nrows; r0 += chunk) {
+        const int nr = min(chunk, nrows - r0);
+        const uint64_t *src = keys + static_cast<long long>(r0) * segs;
+        if (lds_rows > 0) {
+            for (int i = tid; i < nr * segs; i += blockDim.x) stage[i] = src[i];
+            __syncthreads();
+            src = stage;
         }
+        for (int rr = wid; rr < nr; rr += nw) {
+            uint64_t mk = 0;
+            for (int s = lane; s < segs; s += kWave) {
+                const uint64_t k = src[rr * segs + s];
+                mk = k > mk ? k : mk;
+            }
+            mk = wave_max_u64(mk);
+            if (lane == 0) out[r0 + rr] = argmax_key_index(mk);
+        }
+        __syncthreads();
     }
-    return bi;
 }
 
-__global__ __launch_bounds__(kWave) void k_match(const float *__restrict__ part_v,
-                                                 const int32_t *__restrict__ part_i, int segs,
-                                                 const int32_t *__restrict__ drafts, int B, int K,
-                                                 int V, int32_t *__restrict__ accept_len,
-                                                 int32_t *__restrict__ out_tokens,
-                                                 int32_t *__restrict__ status) {
+__global__ __launch_bounds__(kBlock) void k_match(const uint64_t *__restrict__ part_k, int segs,
+                                                  int lds_rows, const int32_t *__restrict__ drafts,
+                                                  int B, int K, int V,
+                                                  int32_t *__restrict__ accept_len,
+                                                  int32_t *__restrict__ out_tokens,
+                                                  int32_t *__restrict__ status) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    uint64_t *stage = reinterpret_cast<uint64_t *>(smem);
+    int *s_a = reinterpret_cast<int *>(stage + static_cast<size_t>(lds_rows) * segs);
     const int b = blockIdx.x;
-    const int lane = threadIdx.x;
-    int n = -1, a_n = -1;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1);
+    const int32_t *xb = drafts + static_cast<long long>(b) * K;
+    const int x0 = tid < K ? xb[tid] : -1;  // first 64 drafts, fetched while the keys are merged
+    merge_rows(part_k + static_cast<long long>(b) * (K + 1) * segs, K + 1, segs, lds_rows, stage, s_a);
+    if (tid >= kWave) return;
+    int n = K;
     bool bad = false;
-    for (int i0 = 0; i0 <= K; i0 += kWave) {
+    for (int i0 = 0; i0 < K; i0 += kWave) {
         const int i = i0 + lane;
-        int a = -1;
         bool stop = false;
-        if (i <= K) {
-            const long long g = (static_cast<long long>(b) * (K + 1) + i) * segs;
-            a = merge_argmax(part_v + g, part_i + g, segs);
-            if (i < K) {
-                const int x = drafts[static_cast<long long>(b) * K + i];
-                if (x < 0 || x >= V) bad = true;
-                stop = x != a;
-            } else {
-                stop = true;  // the bonus row ends every chain
-            }
+        if (i < K) {
+            const int x = i0 == 0 ? x0 : xb[i];
+            if (x < 0 || x >= V) bad = true;
+            stop = x != s_a[i];
         }
         const uint64_t mk = ballot(stop);
-        if (n < 0 && mk != 0) {  // uniform: every lane takes this branch together
-            const int l = first_lane(mk);
-            n = i0 + l;
-            a_n = __shfl(a, l, kWave);
-        }
+        if (mk != 0 && n == K) n = i0 + first_lane(mk);
     }
     const bool any_bad = ballot(bad) != 0;
     int32_t *tok = out_tokens + static_cast<long long>(b) * (K + 1);
     for (int i = lane; i <= K; i += kWave)
-        tok[i] = i < n ? drafts[static_cast<long long>(b) * K + i] : (i == n ? a_n : -1);
+        tok[i] = i < n ? (i < kWave ? x0 : xb[i]) : (i == n ? s_a[n] : -1);
     if (lane == 0) {
         accept_len[b] = n;
         if (status) status[b] = any_bad ? 1 : 0;
     }
 }
 
-__global__ __launch_bounds__(kBlock) void k_tree(const float *__restrict__ part_v,
-                                                 const int32_t *__restrict__ part_i, int segs,
+// Nodes per thread in the tree kernel (SV_MAX_TREE_NODES / kBlock).
+constexpr int kTreeNodesPerThread = (SV_MAX_TREE_NODES + kBlock - 1) / kBlock;
+
+__global__ __launch_bounds__(kBlock) void k_tree(const uint64_t *__restrict__ part_k, int segs,
+                                                 int lds_rows,
                                                  const int32_t *__restrict__ node_tokens,
                                                  const int32_t *__restrict__ parents, int B, int N,
                                                  int V, int32_t *__restrict__ accept_len,
                                                  int32_t *__restrict__ path_nodes,
                                                  int32_t *__restrict__ out_tokens,
                                                  int32_t *__restrict__ status) {
-    extern __shared__ int smem[];
-    int *s_a = smem;          // argmax of each node's row
+    extern __shared__ __align__(16) unsigned char smem[];
+    uint64_t *stage = reinterpret_cast<uint64_t *>(smem);
+    int *s_a = reinterpret_cast<int *>(stage + static_cast<size_t>(lds_rows) * segs);  // argmax per node
     int *s_par = s_a + N;     // parents
     int *s_tok = s_par + N;   // node tokens
-    int *s_ok = s_tok + N;    // accepted flag
+    int *s_ok = s_tok + N;    // accepted along the whole path to the root
     int *s_dep = s_ok + N;    // depth
-    int *s_path = s_dep + N;  // chosen path, depth 1 first
-    __shared__ int s_bad, s_oor, s_best, s_d;
+    int *s_anc = s_dep + N;   // pointer-jumping ancestor, then the chosen path
+    __shared__ int s_bad, s_oor;
+    __shared__ unsigned s_key;
     const int b = blockIdx.x;
     const int tid = threadIdx.x;
     if (tid == 0) {
         s_bad = 0;
         s_oor = 0;
+        s_key = 0;
     }
-    __syncthreads();
     const long long base = static_cast<long long>(b) * N;
-    for (int j = tid; j < N; j += blockDim.x) {
-        const long long g = (base + j) * segs;
-        s_a[j] = merge_argmax(part_v + g, part_i + g, segs);
-        const int p = parents[base + j];
-        const int t = node_tokens[base + j];
-        s_par[j] = p;
-        s_tok[j] = t;
+    for (int j = tid; j < N; j += kBlock) {
+        s_par[j] = parents[base + j];
+        s_tok[j] = node_tokens[base + j];
+    }
+    merge_rows(part_k + base * segs, N, segs, lds_rows, stage, s_a);  // ends with a barrier
+    for (int j = tid; j < N; j += kBlock) {
+        const int p = s_par[j];
         if (j == 0 ? p != -1 : (p < 0 || p >= j)) atomicOr(&s_bad, 1);
-        if (j > 0 && (t < 0 || t >= V)) atomicOr(&s_oor, 1);
+        if (j > 0 && (s_tok[j] < 0 || s_tok[j] >= V)) atomicOr(&s_oor, 1);
     }
     __syncthreads();
     if (s_bad) {
-        for (int k = tid; k < N; k += blockDim.x) {
+        for (int k = tid; k < N; k += kBlock) {
             path_nodes[base + k] = -1;
             out_tokens[base + k] = -1;
         }
@@ -180,28 +197,51 @@ __global__ __launch_bounds__(kBlock) void k_tree(const float *__restrict__ part_
         }
         return;
     }
-    if (tid == 0) {
-        s_ok[0] = 1;
-        s_dep[0] = 0;
-        int best = 0;
-        for (int j = 1; j < N; ++j) {
-            const int p = s_par[j];
-            const int ok = s_ok[p] && s_tok[j] == s_a[p];
-            const int d = s_dep[p] + 1;
-            s_ok[j] = ok;
-            s_dep[j] = d;
-            if (ok && d > s_dep[best]) best = j;
-        }
-        const int d = s_dep[best];
-        for (int j = best, k = d - 1; j != 0; j = s_par[j], --k) s_path[k] = j;
-        s_best = best;
-        s_d = d;
+    // Pointer jumping: after round r every node has folded in the acceptance
+    // and depth of its 2^r nearest ancestors; the root is the fixed point.
+    for (int j = tid; j < N; j += kBlock) {
+        const int p = s_par[j];
+        s_anc[j] = j == 0 ? 0 : p;
+        s_ok[j] = j == 0 ? 1 : (s_tok[j] == s_a[p] ? 1 : 0);
+        s_dep[j] = j == 0 ? 0 : 1;
     }
     __syncthreads();
-    const int d = s_d;
-    for (int k = tid; k < N; k += blockDim.x) {
-        path_nodes[base + k] = k < d ? s_path[k] : -1;
-        out_tokens[base + k] = k < d ? s_tok[s_path[k]] : (k == d ? s_a[s_best] : -1);
+    for (int span = 1; span < N; span <<= 1) {
+        int ok2[kTreeNodesPerThread], d2[kTreeNodesPerThread], a2[kTreeNodesPerThread];
+#pragma unroll
+        for (int t = 0; t < kTreeNodesPerThread; ++t) {
+            const int j = tid + t * kBlock;
+            if (j < N) {
+                const int a = s_anc[j];
+                ok2[t] = s_ok[a];
+                d2[t] = s_dep[a];
+                a2[t] = s_anc[a];
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int t = 0; t < kTreeNodesPerThread; ++t) {
+            const int j = tid + t * kBlock;
+            if (j < N) {
+                s_ok[j] &= ok2[t];
+                s_dep[j] += d2[t];
+                s_anc[j] = a2[t];
+            }
+        }
+        __syncthreads();
+    }
+    // deepest accepted node, lowest index among equals (the root always qualifies)
+    for (int j = tid; j < N; j += kBlock)
+        if (s_ok[j]) atomicMax(&s_key, (static_cast<unsigned>(s_dep[j]) << 16) | (0xffffu - static_cast<unsigned>(j)));
+    __syncthreads();
+    const int best = static_cast<int>(0xffffu - (s_key & 0xffffu));
+    const int d = static_cast<int>(s_key >> 16);
+    if (tid == 0)
+        for (int j = best, k = d - 1; j != 0; j = s_par[j], --k) s_anc[k] = j;  // the path, depth 1 first
+    __syncthreads();
+    for (int k = tid; k < N; k += kBlock) {
+        path_nodes[base + k] = k < d ? s_anc[k] : -1;
+        out_tokens[base + k] = k < d ? s_tok[s_anc[k]] : (k == d ? s_a[best] : -1);
     }
     if (tid == 0) {
         accept_len[b] = d;
@@ -210,43 +250,52 @@ __global__ __launch_bounds__(kBlock) void k_tree(const float *__restrict__ part_
 }
 
 template <typename E, bool ALIGNED>
-hipError_t argmax_t(const void *L, long long rows, int V, const RowGeom &g, float *part_v,
-                    int32_t *part_i, hipStream_t s) {
+hipError_t argmax_t(const void *L, long long rows, int V, const RowGeom &g, uint64_t *part_k,
+                    hipStream_t s) {
     using T = typename E::storage;
     const long long nwaves = rows * g.segs;
     const long long blocks = (nwaves + kWavesPerBlock - 1) / kWavesPerBlock;
-    k_argmax<E, ALIGNED, kStreamVecsPerLane><<<dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0, s>>>(
-        static_cast<const T *>(L), nwaves, V, g.nvec, g.segs, part_v, part_i);
-    return hipGetLastError();
+    return launch_kernel(k_argmax<E, ALIGNED, kArgmaxVecsPerLane>, dim3(static_cast<unsigned>(blocks)),
+                         dim3(kBlock), 0, s, static_cast<const T *>(L), nwaves, V, g.nvec, g.segs, part_k);
+}
+
+// Rows whose segment keys fit the LDS budget together (0: read them from global memory).
+int stage_rows(int segs, int rows, size_t budget) {
+    const size_t per_row = static_cast<size_t>(segs) * sizeof(uint64_t);
+    if (per_row > budget) return 0;
+    return static_cast<int>(std::min<size_t>(static_cast<size_t>(rows), budget / per_row));
 }
 
 }  // namespace
 
 hipError_t launch_argmax(const void *L, long long rows, int V, const RowGeom &g, sv_dtype dt,
-                         float *part_v, int32_t *part_i, hipStream_t s) {
+                         uint64_t *part_k, hipStream_t s) {
     if (dt == SV_BF16)
-        return g.aligned ? argmax_t<BF16, true>(L, rows, V, g, part_v, part_i, s)
-                         : argmax_t<BF16, false>(L, rows, V, g, part_v, part_i, s);
-    return g.aligned ? argmax_t<F32, true>(L, rows, V, g, part_v, part_i, s)
-                     : argmax_t<F32, false>(L, rows, V, g, part_v, part_i, s);
+        return g.aligned ? argmax_t<BF16, true>(L, rows, V, g, part_k, s)
+                         : argmax_t<BF16, false>(L, rows, V, g, part_k, s);
+    return g.aligned ? argmax_t<F32, true>(L, rows, V, g, part_k, s)
+                     : argmax_t<F32, false>(L, rows, V, g, part_k, s);
 }
 
-hipError_t launch_match(const float *part_v, const int32_t *part_i, const int32_t *drafts, int B,
-                        int K, int V, const RowGeom &g, int32_t *accept_len, int32_t *out_tokens,
-                        int32_t *status, hipStream_t s) {
-    k_match<<<dim3(B), dim3(kWave), 0, s>>>(part_v, part_i, g.segs, drafts, B, K, V, accept_len,
-                                            out_tokens, status);
-    return hipGetLastError();
+hipError_t launch_match(const uint64_t *part_k, const int32_t *drafts, int B, int K, int V,
+                        const RowGeom &g, int32_t *accept_len, int32_t *out_tokens, int32_t *status,
+                        hipStream_t s) {
+    const int lr = stage_rows(g.segs, K + 1, kMergeLdsBytes);
+    const size_t lds = static_cast<size_t>(lr) * g.segs * sizeof(uint64_t) + sizeof(int) * static_cast<size_t>(K + 1);
+    return launch_kernel(k_match, dim3(B), dim3(kBlock), lds, s, part_k, g.segs, lr, drafts, B, K, V,
+                         accept_len, out_tokens, status);
 }
 
-hipError_t launch_tree(const float *part_v, const int32_t *part_i, const int32_t *node_tokens,
-                       const int32_t *parents, int B, int N, int V, const RowGeom &g,
-                       int32_t *accept_len, int32_t *path_nodes, int32_t *out_tokens,
-                       int32_t *status, hipStream_t s) {
-    const size_t lds = sizeof(int) * 6 * static_cast<size_t>(N);
-    k_tree<<<dim3(B), dim3(kBlock), lds, s>>>(part_v, part_i, g.segs, node_tokens, parents, B, N,
-                                              V, accept_len, path_nodes, out_tokens, status);
-    return hipGetLastError();
+hipError_t launch_tree(const uint64_t *part_k, const int32_t *node_tokens, const int32_t *parents,
+                       int B, int N, int V, const RowGeom &g, int32_t *accept_len,
+                       int32_t *path_nodes, int32_t *out_tokens, int32_t *status, hipStream_t s) {
+    const size_t node_bytes = sizeof(int) * 6 * static_cast<size_t>(N);
+    const size_t cap = 60 * 1024;
+    const size_t budget = node_bytes < cap ? std::min<size_t>(kMergeLdsBytes, cap - node_bytes) : 0;
+    const int lr = stage_rows(g.segs, N, budget);
+    const size_t lds = static_cast<size_t>(lr) * g.segs * sizeof(uint64_t) + node_bytes;
+    return launch_kernel(k_tree, dim3(B), dim3(kBlock), lds, s, part_k, g.segs, lr, node_tokens,
+                         parents, B, N, V, accept_len, path_nodes, out_tokens, status);
 }
 
 }  // namespace sv

@@ -2,6 +2,7 @@
 // shared by the C-ABI entry points and the kernel translation units.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -10,13 +11,27 @@
 
 namespace sv {
 
-// 16-byte vectors per lane held in registers by one streaming wave.
-constexpr int kStreamVecsPerLane = 8;
-// Tiles (64 vectors each) per wave in the residual-mass pass.
-constexpr int kTilesPerWave = 8;
-// Longest draft chain accepted by spec_verify_sample (row statistics of one
-// request are kept in LDS by the acceptance kernel).
-constexpr int kMaxSampleK = 1024;
+// Tuning knobs (compile-time; the defaults are the measured best on MI355X).
+#ifndef SV_STATS_VECS
+#define SV_STATS_VECS 16
+#endif
+#ifndef SV_ARGMAX_VECS
+#define SV_ARGMAX_VECS 8
+#endif
+#ifndef SV_RESID_GROUP
+#define SV_RESID_GROUP 2
+#endif
+// 16-byte vectors per lane held in registers by one streaming wave of the
+// row-statistics and argmax passes (a wave covers 64 * this many vectors).
+constexpr int kStatsVecsPerLane = SV_STATS_VECS;
+constexpr int kArgmaxVecsPerLane = SV_ARGMAX_VECS;
+// Tiles (64 vectors each) loaded together by the residual-mass pass; a wave
+// walks its tiles in such groups, loading the next group before summing one.
+constexpr int kResidGroup = SV_RESID_GROUP;
+// Waves the residual-mass pass aims for (about two per SIMD).
+constexpr int kResidTargetWaves = 4096;
+// Bytes of LDS the per-request merge kernels use to stage row partials.
+constexpr int kMergeLdsBytes = 24 * 1024;
 
 // How one row of V logits is cut into per-wave segments.
 struct RowGeom {
@@ -27,7 +42,7 @@ struct RowGeom {
     bool aligned;  // 16-byte loads (rows 16-byte aligned, V % per_vec == 0)
 };
 
-RowGeom row_geom(int V, sv_dtype dt, bool ptrs_aligned);
+RowGeom row_geom(int V, sv_dtype dt, bool ptrs_aligned, int vecs_per_lane);
 
 // Parameters of the one token drawn per request, written by the acceptance
 // kernel and read by the residual kernels.
@@ -46,9 +61,10 @@ struct SampleWs {
     size_t part_R, part_s, L2, rp, tiles, total;
 };
 struct GreedyWs {
-    size_t part_v, part_i, total;
+    size_t part_k, total;
 };
 SampleWs sample_ws_layout(int B, int K, const RowGeom &g);
+int resid_tiles_per_wave(int B, int ntiles);
 GreedyWs greedy_ws_layout(long long rows, const RowGeom &g);
 
 // Temperature scale c = log2(e)/T split as c_hi + c_lo with both floats and
@@ -59,9 +75,25 @@ struct Scale {
 };
 Scale make_scale(double T);
 
-// Kernel-launch tracing (events around each launch when enabled).
-void trace_pre(int kernel, hipStream_t s);
-void trace_post(hipStream_t s);
+// Kernel-launch tracing.  trace_select() names the kernel the next launch is;
+// trace_events() hands out the event pair that launch should carry (false when
+// tracing is off, full, or masked for that kernel).
+void trace_select(int kernel);
+bool trace_events(hipEvent_t *start, hipEvent_t *stop);
+
+// Launch `k` on `s`; when tracing claims it, the launch carries start/stop
+// events stamped by the dispatch itself (hipExtLaunchKernelGGL).
+template <typename... KArgs, typename... Args>
+inline hipError_t launch_kernel(void (*k)(KArgs...), dim3 grid, dim3 block, size_t lds,
+                                hipStream_t s, Args... args) {
+    hipEvent_t e0, e1;
+    if (trace_events(&e0, &e1))
+        hipExtLaunchKernelGGL(k, grid, block, static_cast<uint32_t>(lds), s, e0, e1, 0u,
+                              static_cast<KArgs>(args)...);
+    else
+        hipLaunchKernelGGL(k, grid, block, lds, s, static_cast<KArgs>(args)...);
+    return hipGetLastError();
+}
 
 // ---- launchers (each enqueues one kernel on `s`) --------------------------------
 hipError_t launch_rowstats(const void *tgt, const void *drf, long long rows_t, long long rows_total,
@@ -80,11 +112,11 @@ hipError_t launch_resid_select(const void *tgt, const void *drf, int B, int K, i
                                const ResidParam *rp, double *tile_mass, int32_t *out_tokens,
                                hipStream_t s);
 hipError_t launch_argmax(const void *L, long long rows, int V, const RowGeom &g, sv_dtype dt,
-                         float *part_v, int32_t *part_i, hipStream_t s);
-hipError_t launch_match(const float *part_v, const int32_t *part_i, const int32_t *drafts, int B,
-                        int K, int V, const RowGeom &g, int32_t *accept_len, int32_t *out_tokens,
-                        int32_t *status, hipStream_t s);
-hipError_t launch_tree(const float *part_v, const int32_t *part_i, const int32_t *node_tokens,
+                         uint64_t *part_k, hipStream_t s);
+hipError_t launch_match(const uint64_t *part_k, const int32_t *drafts, int B, int K, int V,
+                        const RowGeom &g, int32_t *accept_len, int32_t *out_tokens, int32_t *status,
+                        hipStream_t s);
+hipError_t launch_tree(const uint64_t *part_k, const int32_t *node_tokens,
                        const int32_t *parents, int B, int N, int V, const RowGeom &g,
                        int32_t *accept_len, int32_t *path_nodes, int32_t *out_tokens,
                        int32_t *status, hipStream_t s);

@@ -11,8 +11,9 @@
 //   k_rowstats     one streaming pass over every target row [B,K+1,V] and draft
 //                  row [B,K,V]; each wave reduces a segment of a row to a
 //                  partial (R, s) with s = sum 2^(x c - R), c = log2(e)/T.
-//   k_accept       one wave per request: merges the partials of its 2K+1 rows
-//                  into L2 = log2 sum_v 2^(x c), gathers L[x_i] for every draft,
+//   k_accept       one workgroup per request: stages the partials of its 2K+1
+//                  rows in LDS, merges each row (one wave per row) into
+//                  L2 = log2 sum_v 2^(x c), gathers L[x_i] for every draft,
 //                  forms p_i(x_i)/q_i(x_i) in fp64 and finds the first
 //                  rejection; writes accept_len, the accepted tokens, lse.
 //   k_resid_mass   for the one row (pair) each request draws from, the mass of
@@ -26,6 +27,8 @@
 // temperature scale carries no systematic rounding; every accumulation across
 // elements, the row merges, the acceptance ratios and the running masses of the
 // inverse CDF are fp64.
+#include <algorithm>
+
 #include "sv_device.hpp"
 #include "sv_internal.hpp"
 
@@ -93,62 +96,107 @@ __global__ __launch_bounds__(kBlock) void k_rowstats(
 
 // ---- S2/S3: merge, gather, acceptance scan ----------------------------------------
 
+// Row r of request b (0..K target rows, then K draft rows) as a global row id.
+__device__ __forceinline__ long long req_row(int b, int K, long long rows_t, int r) {
+    return r <= K ? static_cast<long long>(b) * (K + 1) + r
+                  : rows_t + static_cast<long long>(b) * K + (r - K - 1);
+}
+
 template <typename E>
-__global__ __launch_bounds__(kWave) void k_accept(
+__global__ __launch_bounds__(kBlock) void k_accept(
     const typename E::storage *__restrict__ tgt, const typename E::storage *__restrict__ drf,
     const int32_t *__restrict__ drafts, const float *__restrict__ ua, const float *__restrict__ us,
-    int B, int K, int V, int segs, double c, const float *__restrict__ part_R,
+    int B, int K, int V, int segs, int lds_rows, double c, const float *__restrict__ part_R,
     const double *__restrict__ part_s, double *__restrict__ L2out, int32_t *__restrict__ accept_len,
     int32_t *__restrict__ out_tokens, float *__restrict__ lse_t, float *__restrict__ lse_d,
     int32_t *__restrict__ status, ResidParam *__restrict__ rp) {
-    extern __shared__ double sL2[];  // 2K+1 row log2-normalisers of this request
-    const int b = blockIdx.x;
-    const int lane = threadIdx.x;
-    const long long rows_t = static_cast<long long>(B) * (K + 1);
+    // LDS: the 2K+1 row log2-normalisers, then staged partials of lds_rows rows
+    extern __shared__ __align__(16) unsigned char smem[];
     const int nrows = 2 * K + 1;
+    double *sL2 = reinterpret_cast<double *>(smem);
+    double *stS = sL2 + nrows;
+    float *stR = reinterpret_cast<float *>(stS + static_cast<size_t>(lds_rows) * segs);
+    const int b = blockIdx.x;
+    const int tid = threadIdx.x, wid = tid >> 6, lane = tid & (kWave - 1);
+    const long long rows_t = static_cast<long long>(B) * (K + 1);
     const double inf = __builtin_huge_val();
 
-    for (int r = 0; r < nrows; ++r) {
-        const long long g = r <= K ? static_cast<long long>(b) * (K + 1) + r
-                                   : rows_t + static_cast<long long>(b) * K + (r - K - 1);
-        const float *pR = part_R + g * segs;
-        const double *pS = part_s + g * segs;
-        float Rm = -__builtin_huge_valf();
-        for (int s = lane; s < segs; s += kWave) Rm = fmaxf(Rm, pR[s]);
-        Rm = wave_max(Rm);
-        double acc = 0.0;
-        if (Rm != -__builtin_huge_valf()) {
-            for (int s = lane; s < segs; s += kWave) {
-                const double ss = pS[s];
-                if (ss > 0.0) acc += ss * exp2(static_cast<double>(pR[s]) - static_cast<double>(Rm));
-            }
-        }
-        acc = wave_sum(acc);
-        const double l2 = acc > 0.0 ? static_cast<double>(Rm) + log2(acc) : -inf;
-        if (lane == 0) {
-            sL2[r] = l2;
-            L2out[static_cast<long long>(b) * nrows + r] = l2;
-            if (r <= K) {
-                if (lse_t) lse_t[static_cast<long long>(b) * (K + 1) + r] = static_cast<float>(l2 * kLn2);
-            } else if (lse_d) {
-                lse_d[static_cast<long long>(b) * K + (r - K - 1)] = static_cast<float>(l2 * kLn2);
-            }
+    // The drafts and the two logits each one is scored with, fetched for the
+    // first 64 positions while the partials are merged.
+    const int32_t *xb = drafts + static_cast<long long>(b) * K;
+    int x0 = -1;
+    float xp0 = 0.0f, xq0 = 0.0f;
+    if (tid < K) {
+        x0 = xb[tid];
+        if (x0 >= 0 && x0 < V) {
+            xp0 = to_f32(tgt[(static_cast<long long>(b) * (K + 1) + tid) * V + x0]);
+            xq0 = to_f32(drf[(static_cast<long long>(b) * K + tid) * V + x0]);
         }
     }
-    __syncthreads();
 
-    // p_i(x_i) / q_i(x_i) for every position at once; the first failing test wins.
+    // 1. row normalisers L2 = Rmax + log2 sum_s s_s 2^(R_s - Rmax)
+    const int chunk = lds_rows > 0 ? lds_rows : nrows;
+    for (int r0 = 0; r0 < nrows; r0 += chunk) {
+        const int nr = min(chunk, nrows - r0);
+        if (lds_rows > 0) {
+            for (int i = tid; i < nr * segs; i += kBlock) {
+                const int rr = i / segs, sg = i - rr * segs;
+                const long long g = req_row(b, K, rows_t, r0 + rr) * segs + sg;
+                stR[i] = part_R[g];
+                stS[i] = part_s[g];
+            }
+            __syncthreads();
+        }
+        for (int rr = wid; rr < nr; rr += kWavesPerBlock) {
+            const int r = r0 + rr;
+            const float *pR;
+            const double *pS;
+            if (lds_rows > 0) {
+                pR = stR + rr * segs;
+                pS = stS + rr * segs;
+            } else {
+                const long long g = req_row(b, K, rows_t, r) * segs;
+                pR = part_R + g;
+                pS = part_s + g;
+            }
+            float Rm = -__builtin_huge_valf();
+            for (int sg = lane; sg < segs; sg += kWave) Rm = fmaxf(Rm, pR[sg]);
+            Rm = wave_max(Rm);
+            double acc = 0.0;
+            if (Rm != -__builtin_huge_valf()) {
+                for (int sg = lane; sg < segs; sg += kWave) {
+                    const double ss = pS[sg];
+                    if (ss > 0.0) acc += ss * exp2(static_cast<double>(pR[sg]) - static_cast<double>(Rm));
+                }
+            }
+            acc = wave_sum(acc);
+            const double l2 = acc > 0.0 ? static_cast<double>(Rm) + log2(acc) : -inf;
+            if (lane == 0) {
+                sL2[r] = l2;
+                L2out[static_cast<long long>(b) * nrows + r] = l2;
+                if (r <= K) {
+                    if (lse_t) lse_t[static_cast<long long>(b) * (K + 1) + r] = static_cast<float>(l2 * kLn2);
+                } else if (lse_d) {
+                    lse_d[static_cast<long long>(b) * K + (r - K - 1)] = static_cast<float>(l2 * kLn2);
+                }
+            }
+        }
+        __syncthreads();
+    }
+    if (wid != 0) return;
+
+    // 2. p_i(x_i) / q_i(x_i) for every position at once; the first failing test wins.
     int n = K;
     bool bad = false;
     for (int i0 = 0; i0 < K; i0 += kWave) {
         const int i = i0 + lane;
         bool rej = false;
         if (i < K) {
-            const int x = drafts[static_cast<long long>(b) * K + i];
+            const int x = i0 == 0 ? x0 : xb[i];
             double r = 0.0;
             if (x >= 0 && x < V) {
-                const double xp = to_f32(tgt[(static_cast<long long>(b) * (K + 1) + i) * V + x]);
-                const double xq = to_f32(drf[(static_cast<long long>(b) * K + i) * V + x]);
+                const double xp = i0 == 0 ? xp0 : to_f32(tgt[(static_cast<long long>(b) * (K + 1) + i) * V + x]);
+                const double xq = i0 == 0 ? xq0 : to_f32(drf[(static_cast<long long>(b) * K + i) * V + x]);
                 const double px = exp2(xp * c - sL2[i]);
                 const double qx = exp2(xq * c - sL2[K + 1 + i]);
                 r = qx == 0.0 ? inf : px / qx;
@@ -164,7 +212,7 @@ __global__ __launch_bounds__(kWave) void k_accept(
     const bool any_bad = ballot(bad) != 0;
 
     int32_t *tok = out_tokens + static_cast<long long>(b) * (K + 1);
-    for (int i = lane; i <= K; i += kWave) tok[i] = i < n ? drafts[static_cast<long long>(b) * K + i] : -1;
+    for (int i = lane; i <= K; i += kWave) tok[i] = i < n ? (i < kWave ? x0 : xb[i]) : -1;
     if (lane == 0) {
         accept_len[b] = n;
         if (status) status[b] = any_bad ? 1 : 0;
@@ -231,10 +279,13 @@ __device__ __forceinline__ double lane_total(const float (&d)[P]) {
     return static_cast<double>(pairwise_sum(t));
 }
 
-template <typename E, bool ALIGNED, int TPW>
+// Residual (or bonus) mass of each 64-vector tile of the row each request
+// draws from.  A wave owns `tpw` consecutive tiles of one request and walks
+// them in groups of G, loading the next group before it sums the current one.
+template <typename E, bool ALIGNED, int G>
 __global__ __launch_bounds__(kBlock) void k_resid_mass(
     const typename E::storage *__restrict__ tgt, const typename E::storage *__restrict__ drf,
-    int B, int V, int nvec, int ntiles, int wpr, float c_hi, float c_lo,
+    int B, int V, int nvec, int ntiles, int wpr, int tpw, float c_hi, float c_lo,
     const ResidParam *__restrict__ rp, double *__restrict__ tile_mass) {
     constexpr int P = E::kPerVec;
     const int lane = threadIdx.x & (kWave - 1);
@@ -246,32 +297,46 @@ __global__ __launch_bounds__(kBlock) void k_resid_mass(
     const Draw D = make_draw(Pm, c_hi, c_lo, Pm.mode);
     const typename E::storage *prow = tgt + Pm.row_p * static_cast<long long>(V);
     const typename E::storage *qrow = D.mode ? drf + Pm.row_q * static_cast<long long>(V) : nullptr;
-    const int t0 = w * TPW;
+    const int t_begin = w * tpw;
+    const int t_end = min(ntiles, t_begin + tpw);
+    double *out = tile_mass + static_cast<long long>(b) * ntiles;
 
-    Staged<E, ALIGNED> sp[TPW], sq[TPW];
+    auto load = [&](Staged<E, ALIGNED>(&sp)[G], Staged<E, ALIGNED>(&sq)[G], int t0) {
 #pragma unroll
-    for (int k = 0; k < TPW; ++k) {
-        const int j = (t0 + k) * kWave + lane;
-        if (t0 + k < ntiles && j < nvec) {
-            sp[k].load(prow, V, j);
-            if (D.mode)
-                sq[k].load(qrow, V, j);
-            else
+        for (int k = 0; k < G; ++k) {
+            const int j = (t0 + k) * kWave + lane;
+            if (t0 + k < t_end && j < nvec) {
+                sp[k].load(prow, V, j);
+                if (D.mode)
+                    sq[k].load(qrow, V, j);
+                else
+                    sq[k].set_neg_inf();
+            } else {
+                sp[k].set_neg_inf();
                 sq[k].set_neg_inf();
-        } else {
-            sp[k].set_neg_inf();
-            sq[k].set_neg_inf();
+            }
         }
-    }
+    };
+    auto sum = [&](const Staged<E, ALIGNED>(&sp)[G], const Staged<E, ALIGNED>(&sq)[G], int t0) {
 #pragma unroll
-    for (int k = 0; k < TPW; ++k) {
-        if (t0 + k >= ntiles) break;
-        float xp[P], xq[P], d[P];
-        sp[k].get(xp);
-        sq[k].get(xq);
-        masses(xp, xq, D, d);
-        const double incl = wave_incl_scan(lane_total(d), lane);
-        if (lane == kWave - 1) tile_mass[static_cast<long long>(b) * ntiles + t0 + k] = incl;
+        for (int k = 0; k < G; ++k) {
+            if (t0 + k < t_end) {  // uniform across the wave
+                float xp[P], xq[P], d[P];
+                sp[k].get(xp);
+                sq[k].get(xq);
+                masses(xp, xq, D, d);
+                const double incl = wave_incl_scan(lane_total(d), lane);
+                if (lane == kWave - 1) out[t0 + k] = incl;
+            }
+        }
+    };
+    Staged<E, ALIGNED> ap[G], aq[G], bp[G], bq[G];
+    load(ap, aq, t_begin);
+    for (int t0 = t_begin; t0 < t_end; t0 += 2 * G) {
+        load(bp, bq, t0 + G);
+        sum(ap, aq, t0);
+        load(ap, aq, t0 + 2 * G);
+        sum(bp, bq, t0 + G);
     }
 }
 
@@ -411,10 +476,9 @@ hipError_t rowstats_t(const void *tgt, const void *drf, long long rows_t, long l
     using T = typename E::storage;
     const long long nwaves = rows_total * g.segs;
     const long long blocks = (nwaves + kWavesPerBlock - 1) / kWavesPerBlock;
-    k_rowstats<E, ALIGNED, kStreamVecsPerLane><<<dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0, s>>>(
-        static_cast<const T *>(tgt), static_cast<const T *>(drf), rows_t, nwaves, V, g.nvec,
-        g.segs, sc.c_hi, sc.c_lo, part_R, part_s);
-    return hipGetLastError();
+    return launch_kernel(k_rowstats<E, ALIGNED, kStatsVecsPerLane>, dim3(static_cast<unsigned>(blocks)),
+                         dim3(kBlock), 0, s, static_cast<const T *>(tgt), static_cast<const T *>(drf),
+                         rows_t, nwaves, V, g.nvec, g.segs, sc.c_hi, sc.c_lo, part_R, part_s);
 }
 
 }  // namespace
@@ -434,16 +498,20 @@ hipError_t launch_accept(const void *tgt, const void *drf, const int32_t *drafts
                          const Scale &sc, const float *part_R, const double *part_s, double *L2,
                          int32_t *accept_len, int32_t *out_tokens, float *lse_t, float *lse_d,
                          int32_t *status, ResidParam *rp, hipStream_t s) {
-    const size_t lds = sizeof(double) * static_cast<size_t>(2 * K + 1);
+    const int nrows = 2 * K + 1;
+    const size_t per_row = static_cast<size_t>(g.segs) * (sizeof(float) + sizeof(double));
+    const int lr = per_row > static_cast<size_t>(kMergeLdsBytes)
+                       ? 0
+                       : static_cast<int>(std::min<size_t>(nrows, kMergeLdsBytes / per_row));
+    const size_t lds = sizeof(double) * static_cast<size_t>(nrows) + static_cast<size_t>(lr) * per_row;
     if (dt == SV_BF16)
-        k_accept<BF16><<<dim3(B), dim3(kWave), lds, s>>>(
-            static_cast<const uint16_t *>(tgt), static_cast<const uint16_t *>(drf), drafts, ua, us,
-            B, K, V, g.segs, sc.c, part_R, part_s, L2, accept_len, out_tokens, lse_t, lse_d, status, rp);
-    else
-        k_accept<F32><<<dim3(B), dim3(kWave), lds, s>>>(
-            static_cast<const float *>(tgt), static_cast<const float *>(drf), drafts, ua, us, B, K,
-            V, g.segs, sc.c, part_R, part_s, L2, accept_len, out_tokens, lse_t, lse_d, status, rp);
-    return hipGetLastError();
+        return launch_kernel(k_accept<BF16>, dim3(B), dim3(kBlock), lds, s,
+                             static_cast<const uint16_t *>(tgt), static_cast<const uint16_t *>(drf),
+                             drafts, ua, us, B, K, V, g.segs, lr, sc.c, part_R, part_s, L2,
+                             accept_len, out_tokens, lse_t, lse_d, status, rp);
+    return launch_kernel(k_accept<F32>, dim3(B), dim3(kBlock), lds, s, static_cast<const float *>(tgt),
+                         static_cast<const float *>(drf), drafts, ua, us, B, K, V, g.segs, lr, sc.c,
+                         part_R, part_s, L2, accept_len, out_tokens, lse_t, lse_d, status, rp);
 }
 
 namespace {
@@ -451,23 +519,22 @@ template <typename E, bool ALIGNED>
 hipError_t resid_mass_t(const void *tgt, const void *drf, int B, int V, const RowGeom &g,
                         const Scale &sc, const ResidParam *rp, double *tile_mass, hipStream_t s) {
     using T = typename E::storage;
-    const int wpr = (g.ntiles + kTilesPerWave - 1) / kTilesPerWave;
+    const int tpw = resid_tiles_per_wave(B, g.ntiles);
+    const int wpr = (g.ntiles + tpw - 1) / tpw;
     const long long nwaves = static_cast<long long>(B) * wpr;
     const long long blocks = (nwaves + kWavesPerBlock - 1) / kWavesPerBlock;
-    k_resid_mass<E, ALIGNED, kTilesPerWave><<<dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0, s>>>(
-        static_cast<const T *>(tgt), static_cast<const T *>(drf), B, V, g.nvec, g.ntiles, wpr,
-        sc.c_hi, sc.c_lo, rp, tile_mass);
-    return hipGetLastError();
+    return launch_kernel(k_resid_mass<E, ALIGNED, kResidGroup>, dim3(static_cast<unsigned>(blocks)),
+                         dim3(kBlock), 0, s, static_cast<const T *>(tgt), static_cast<const T *>(drf),
+                         B, V, g.nvec, g.ntiles, wpr, tpw, sc.c_hi, sc.c_lo, rp, tile_mass);
 }
 template <typename E, bool ALIGNED>
 hipError_t resid_select_t(const void *tgt, const void *drf, int B, int K, int V, const RowGeom &g,
                           const Scale &sc, const ResidParam *rp, double *tile_mass,
                           int32_t *out_tokens, hipStream_t s) {
     using T = typename E::storage;
-    k_resid_select<E, ALIGNED><<<dim3(B), dim3(kWave), 0, s>>>(
-        static_cast<const T *>(tgt), static_cast<const T *>(drf), B, K, V, g.nvec, g.ntiles,
-        sc.c_hi, sc.c_lo, rp, tile_mass, out_tokens);
-    return hipGetLastError();
+    return launch_kernel(k_resid_select<E, ALIGNED>, dim3(B), dim3(kWave), 0, s,
+                         static_cast<const T *>(tgt), static_cast<const T *>(drf), B, K, V, g.nvec,
+                         g.ntiles, sc.c_hi, sc.c_lo, rp, tile_mass, out_tokens);
 }
 }  // namespace
 

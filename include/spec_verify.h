@@ -65,6 +65,8 @@ typedef enum { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
 
 /* Largest tree (nodes per request) spec_verify_tree accepts. */
 #define SV_MAX_TREE_NODES 2048
+/* Longest draft chain (K) spec_verify_sample and spec_verify_greedy accept. */
+#define SV_MAX_DRAFT_LEN 1024
 
 /* Workspace bytes needed by spec_verify_sample for these sizes (0 if the sizes
  * are invalid). */
@@ -88,6 +90,7 @@ size_t sv_greedy_workspace_bytes(int B, int rows_per_req, int V, sv_dtype dt);
  *                              the token drawn at row n (residual if n < K,
  *                              bonus if n = K); other entries are ignored.
  *   temperature   T > 0, finite; p = softmax(target/T), q = softmax(draft/T).
+ *   0 <= K <= SV_MAX_DRAFT_LEN.
  *
  * Outputs:
  *   accept_len [B]       n_b in [0, K], accepted drafts.
@@ -113,7 +116,7 @@ sv_status spec_verify_sample(const void *target_logits, const void *draft_logits
 /*
  * Greedy chain verification.
  *
- *   target_logits [B][K+1][V], draft_tokens [B][K] (K >= 0).
+ *   target_logits [B][K+1][V], draft_tokens [B][K] (0 <= K <= SV_MAX_DRAFT_LEN).
  *   accept_len [B]      n_b = first i with draft_tokens[b][i] != argmax(row i),
  *                       else K.
  *   out_tokens [B][K+1] drafts 0..n_b-1, argmax(row n_b), then -1.
@@ -158,12 +161,15 @@ const char *sv_status_string(sv_status s);
 const char *sv_version(void);
 
 /*
- * Per-kernel timing.  Between sv_trace_begin(capacity) and sv_trace_end(), every
- * kernel the library launches is bracketed by a pair of HIP events recorded on
- * the stream it runs on (up to `capacity` launches; later ones are not timed).
- * sv_trace_end waits for the recorded events, writes up to `max_records`
- * records (kernel id, elapsed milliseconds) and returns how many launches were
- * recorded.  Not thread-safe; meant for benchmarking.
+ * Per-kernel timing.  Between sv_trace_begin(capacity, kernel_mask) and
+ * sv_trace_end(), every kernel the library launches whose id bit is set in
+ * kernel_mask (0 = all kernels) is bracketed by a pair of HIP events recorded
+ * on the stream it runs on (up to `capacity` launches; later ones are not
+ * timed).  An event pair measures from the start event to the stop event, so
+ * it includes the launch latency of that kernel.  sv_trace_end waits for the
+ * recorded events, writes up to `max_records` records (kernel id, elapsed
+ * milliseconds) and returns how many launches were recorded.  Not
+ * thread-safe; meant for benchmarking.
  */
 typedef struct {
     int kernel; /* an sv_kernel_id */
@@ -181,7 +187,7 @@ typedef enum {
     SV_K_COUNT = 7
 } sv_kernel_id;
 
-sv_status sv_trace_begin(int capacity);
+sv_status sv_trace_begin(int capacity, unsigned kernel_mask);
 int sv_trace_end(sv_kernel_time *records, int max_records);
 const char *sv_kernel_name(int kernel);
 
