@@ -147,6 +147,15 @@ class Calls:
         if rc:
             raise RuntimeError(f"spec_verify_sample failed: {rc}")
 
+    def sample_skip(self):
+        """The same verification without lse outputs: rows after each request's
+        first rejection are never read."""
+        a = list(self.sample_args)
+        a[12] = a[13] = None
+        rc = self.lib.spec_verify_sample(*a)
+        if rc:
+            raise RuntimeError(f"spec_verify_sample (no lse) failed: {rc}")
+
     def greedy(self):
         rc = self.lib.spec_verify_greedy(*self.greedy_args)
         if rc:
@@ -302,6 +311,39 @@ def main():
     if "sample" in modes:
         modes["sample"]["mean_tokens_per_round"] = round(float(n3.mean() + 1), 4)
 
+    # each call on its own, back to back (launch gaps included)
+    def per_call(fn, reps):
+        for _ in range(5):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / reps
+
+    reps = max(20, args.steps // 2)
+    calls_alone = {}
+    if "sample" in active:
+        calls.sample_skip()
+        torch.cuda.synchronize()
+        n_skip = calls.s_n.cpu().numpy()
+        assert np.array_equal(n_skip, n3), "skip path disagrees with the full-read path"
+        K3 = w3.K
+        rows_read = np.where(n_skip < K3, 2 * (n_skip + 1) + 2, 2 * K3 + 2)
+        skip_bytes = int(rows_read.sum()) * R
+        for name, fn, nbytes in (("sample_full", calls.sample, bytes_mode["sample"]),
+                                 ("sample_skip", calls.sample_skip, skip_bytes)):
+            ms = per_call(fn, reps)
+            calls_alone[name] = {"ms": round(ms, 5), "rows_per_s": round(rows_mode["sample"] / (ms * 1e-3), 1),
+                                 "bytes_read": nbytes, "gbps": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+    for name, fn in (("greedy", calls.greedy), ("tree", calls.tree)):
+        if name in active:
+            ms = per_call(fn, reps)
+            calls_alone[name] = {"ms": round(ms, 5), "rows_per_s": round(rows_mode[name] / (ms * 1e-3), 1),
+                                 "bytes_read": bytes_mode[name],
+                                 "gbps": round(bytes_mode[name] / (ms * 1e-3) / 1e9, 1)}
+
     cpu = None
     if not args.no_cpu_baseline:
         threads = args.cpu_threads or max(1, min(16, os.cpu_count() or 1))
@@ -337,6 +379,7 @@ def main():
         "roofline_argmax": extra or None,
         "modes": modes,
         "kernel_ms": {k: round(v, 5) for k, v in kmean.items()},
+        "calls_alone": calls_alone,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -26,7 +26,8 @@ LIB_PATH = os.path.join(HERE, "libspecverify.so")
 SV_OK, SV_ERR_INVALID_ARG, SV_ERR_UNSUPPORTED, SV_ERR_WORKSPACE, SV_ERR_HIP = range(5)
 SV_F32, SV_BF16 = 0, 1
 SV_MAX_TREE_NODES = 2048
-KERNELS = ("rowstats", "accept", "resid_mass", "resid_select", "argmax", "match", "tree")
+KERNELS = ("rowstats", "accept", "resid_mass", "resid_select", "argmax", "match", "tree",
+           "skip_stats")
 
 EXPORTS = ("sv_sample_workspace_bytes", "sv_greedy_workspace_bytes", "spec_verify_sample",
            "spec_verify_greedy", "spec_verify_tree", "sv_status_string", "sv_version",
@@ -163,6 +164,8 @@ def spec_verify_sample(target, draft, draft_tokens, u_accept, u_sample, temperat
     draft_tokens [B,K] int32, u_accept [B,K] and u_sample [B,K+1] float32 in
     [0,1).  Returns a dict with ``accept_len`` [B], ``tokens`` [B,K+1] and,
     when requested, ``lse_target`` [B,K+1], ``lse_draft`` [B,K], ``status`` [B].
+    With lse=False (and K <= 31) the library skips the rows of positions after
+    a request's first rejection (same outputs, fewer bytes).
     """
     torch = _torch()
     lib = load_library()

@@ -30,7 +30,10 @@ static size_t align_up(size_t x) { return (x + 255) & ~static_cast<size_t>(255);
 SampleWs sample_ws_layout(int B, int K, const RowGeom &g) {
     SampleWs w;
     const size_t rows = static_cast<size_t>(B) * static_cast<size_t>(2 * K + 1);
-    const size_t parts = rows * static_cast<size_t>(g.segs);
+    // partials of either pass: full read (g) or row skipping (its own segments)
+    const int skip_segs = row_geom(g.nvec * g.per_vec, g.per_vec == 8 ? SV_BF16 : SV_F32, true,
+                                   kSkipVecsPerLane * kSkipChunks).segs;
+    const size_t parts = rows * static_cast<size_t>(std::max(g.segs, skip_segs));
     size_t o = 0;
     w.part_R = o;
     o = align_up(o + parts * sizeof(float));
@@ -42,6 +45,8 @@ SampleWs sample_ws_layout(int B, int K, const RowGeom &g) {
     o = align_up(o + static_cast<size_t>(B) * sizeof(ResidParam));
     w.tiles = o;
     o = align_up(o + static_cast<size_t>(B) * static_cast<size_t>(g.ntiles) * sizeof(double));
+    w.skipctl = o;
+    o = align_up(o + skip_ctl_bytes(B, K));
     w.total = o;
     return w;
 }
@@ -53,9 +58,9 @@ int resid_tiles_per_wave(int B, int ntiles) {
     return static_cast<int>(std::max<long long>(kResidGroup, std::min<long long>(t, 64)));
 }
 
-GreedyWs greedy_ws_layout(long long rows, const RowGeom &g) {
+GreedyWs greedy_ws_layout(int B, int rows_per_req, const RowGeom &g) {
     GreedyWs w;
-    const size_t parts = static_cast<size_t>(rows) * static_cast<size_t>(g.segs);
+    const size_t parts = static_cast<size_t>(B) * static_cast<size_t>(rows_per_req) * static_cast<size_t>(g.segs);
     size_t o = 0;
     w.part_k = o;
     o = align_up(o + parts * sizeof(uint64_t));
@@ -152,7 +157,7 @@ size_t sv_sample_workspace_bytes(int B, int K, int V, sv_dtype dt) {
 size_t sv_greedy_workspace_bytes(int B, int rows_per_req, int V, sv_dtype dt) {
     if (B < 0 || rows_per_req < 1 || !valid_dtype(dt) || !sizes_ok(B, rows_per_req, V)) return 0;
     const RowGeom g = row_geom(V, dt, true, kArgmaxVecsPerLane);
-    return greedy_ws_layout(static_cast<long long>(B) * rows_per_req, g).total;
+    return greedy_ws_layout(B, rows_per_req, g).total;
 }
 
 sv_status spec_verify_sample(const void *target_logits, const void *draft_logits,
@@ -186,16 +191,25 @@ sv_status spec_verify_sample(const void *target_logits, const void *draft_logits
     const long long rows_t = static_cast<long long>(B) * (K + 1);
     const long long rows_total = rows_t + static_cast<long long>(B) * K;
 
-    hipError_t e = traced(SV_K_ROWSTATS, s, [&] {
-        return launch_rowstats(target_logits, draft_logits, rows_t, rows_total, V, g, dt, sc, part_R,
-                               part_s, s);
-    });
-    if (e == hipSuccess)
-        e = traced(SV_K_ACCEPT, s, [&] {
-            return launch_accept(target_logits, draft_logits, draft_tokens, u_accept, u_sample, B, K,
-                                 V, g, dt, sc, part_R, part_s, L2, accept_len, out_tokens,
-                                 lse_target, lse_draft, req_status, rp, s);
+    hipError_t e = hipSuccess;
+    if (lse_target || lse_draft || !skip_supported(K)) {
+        // every row is read (its statistics feed the lse outputs)
+        e = traced(SV_K_ROWSTATS, s, [&] {
+            return launch_rowstats(target_logits, draft_logits, rows_t, rows_total, V, g, dt, sc, part_R,
+                                   part_s, s);
         });
+        if (e == hipSuccess)
+            e = traced(SV_K_ACCEPT, s, [&] {
+                return launch_accept(target_logits, draft_logits, draft_tokens, u_accept, u_sample, B, K,
+                                     V, g, dt, sc, part_R, part_s, L2, accept_len, out_tokens,
+                                     lse_target, lse_draft, req_status, rp, s);
+            });
+    } else {
+        // rows of positions after each request's first rejection are not read
+        const RowGeom gs = row_geom(V, dt, ptr_al, kSkipVecsPerLane * kSkipChunks);
+        e = launch_skip(target_logits, draft_logits, draft_tokens, u_accept, u_sample, B, K, V, gs, dt, sc,
+                        part_R, part_s, L2, ws + L.skipctl, accept_len, out_tokens, req_status, rp, s);
+    }
     if (e == hipSuccess)
         e = traced(SV_K_RESID_MASS, s, [&] {
             return launch_resid_mass(target_logits, draft_logits, B, V, g, dt, sc, rp, tiles, s);
@@ -221,7 +235,7 @@ sv_status spec_verify_greedy(const void *target_logits, const int32_t *draft_tok
     if (!aligned256(workspace)) return SV_ERR_INVALID_ARG;
     const RowGeom g = row_geom(V, dt, aligned16(target_logits), kArgmaxVecsPerLane);
     const long long rows = static_cast<long long>(B) * (K + 1);
-    const GreedyWs L = greedy_ws_layout(rows, g);
+    const GreedyWs L = greedy_ws_layout(B, K + 1, g);
     if (workspace_bytes < L.total) return SV_ERR_WORKSPACE;
     uint64_t *pk = reinterpret_cast<uint64_t *>(static_cast<char *>(workspace) + L.part_k);
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -248,7 +262,7 @@ sv_status spec_verify_tree(const void *target_logits, const int32_t *node_tokens
     if (!aligned256(workspace)) return SV_ERR_INVALID_ARG;
     const RowGeom g = row_geom(V, dt, aligned16(target_logits), kArgmaxVecsPerLane);
     const long long rows = static_cast<long long>(B) * N;
-    const GreedyWs L = greedy_ws_layout(rows, g);
+    const GreedyWs L = greedy_ws_layout(B, N, g);
     if (workspace_bytes < L.total) return SV_ERR_WORKSPACE;
     uint64_t *pk = reinterpret_cast<uint64_t *>(static_cast<char *>(workspace) + L.part_k);
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -276,7 +290,7 @@ const char *sv_version(void) { return "specverify 0.1.0 (gfx950)"; }
 
 const char *sv_kernel_name(int k) {
     static const char *names[SV_K_COUNT] = {"rowstats", "accept", "resid_mass", "resid_select",
-                                            "argmax", "match", "tree"};
+                                            "argmax", "match", "tree", "skip_stats"};
     return (k >= 0 && k < SV_K_COUNT) ? names[k] : "unknown";
 }
 

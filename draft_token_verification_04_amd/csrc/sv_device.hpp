@@ -187,4 +187,46 @@ __device__ __forceinline__ int last_lane(uint64_t m) { return 63 - __clzll(stati
 // exp2 on the hardware transcendental unit (v_exp_f32); -inf gives 0.
 __device__ __forceinline__ float fast_exp2(float a) { return __builtin_amdgcn_exp2f(a); }
 
+// ---- cross-wave hand-off inside one kernel ----------------------------------------
+//
+// Waves of one launch that pass words to each other (segment partials, row
+// normalisers, a request's decision state) use device-scope atomic loads and
+// stores for those words: the hardware keeps them coherent across the XCDs'
+// separate L2 caches without the whole-cache write-back and invalidation a
+// device-scope fence costs there (tens of microseconds per fence, measured).
+// The one ordering needed - a wave's shared stores complete before its next
+// counter update - comes from waiting on the wave's own outstanding memory
+// operations.  No wave ever waits for another.
+
+template <typename T>
+__device__ __forceinline__ void shared_store(T *p, T v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ T shared_load(T *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void wait_own_stores() { __builtin_amdgcn_s_waitcnt(0); }
+
+// Values every lane holds alike, moved to a scalar register so branches on
+// them are uniform.
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ unsigned uniform(unsigned v) {
+    return static_cast<unsigned>(__builtin_amdgcn_readfirstlane(static_cast<int>(v)));
+}
+__device__ __forceinline__ uint64_t uniform(uint64_t v) {
+    const unsigned lo = uniform(static_cast<unsigned>(v)), hi = uniform(static_cast<unsigned>(v >> 32));
+    return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+// Count one arrival at *t once this wave's shared stores are complete; true
+// for the arrival that completes `total` (all earlier arrivals' shared
+// stores are complete by then).
+__device__ __forceinline__ bool wave_arrive(unsigned *t, unsigned total, int lane) {
+    wait_own_stores();
+    unsigned old = 0;
+    if (lane == 0) old = __hip_atomic_fetch_add(t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return uniform(static_cast<unsigned>(__shfl(static_cast<int>(old), 0, kWave))) + 1 == total;
+}
+
 }  // namespace sv

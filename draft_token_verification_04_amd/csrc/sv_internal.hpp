@@ -21,6 +21,12 @@ namespace sv {
 #ifndef SV_RESID_GROUP
 #define SV_RESID_GROUP 2
 #endif
+#ifndef SV_SKIP_VECS
+#define SV_SKIP_VECS 8
+#endif
+#ifndef SV_SKIP_CHUNKS
+#define SV_SKIP_CHUNKS 4
+#endif
 // 16-byte vectors per lane held in registers by one streaming wave of the
 // row-statistics and argmax passes (a wave covers 64 * this many vectors).
 constexpr int kStatsVecsPerLane = SV_STATS_VECS;
@@ -28,6 +34,11 @@ constexpr int kArgmaxVecsPerLane = SV_ARGMAX_VECS;
 // Tiles (64 vectors each) loaded together by the residual-mass pass; a wave
 // walks its tiles in such groups, loading the next group before summing one.
 constexpr int kResidGroup = SV_RESID_GROUP;
+// The row-skipping pass: a wave streams SV_SKIP_CHUNKS chunks of
+// SV_SKIP_VECS vectors per lane, loading each chunk while it sums the last,
+// so its fixed costs (the request flag, the hand-off) cover more bytes.
+constexpr int kSkipVecsPerLane = SV_SKIP_VECS;
+constexpr int kSkipChunks = SV_SKIP_CHUNKS;
 // Waves the residual-mass pass aims for (about two per SIMD).
 constexpr int kResidTargetWaves = 4096;
 // Bytes of LDS the per-request merge kernels use to stage row partials.
@@ -58,14 +69,14 @@ struct ResidParam {
 
 // Byte offsets of the workspace regions.
 struct SampleWs {
-    size_t part_R, part_s, L2, rp, tiles, total;
+    size_t part_R, part_s, L2, rp, tiles, skipctl, total;
 };
 struct GreedyWs {
     size_t part_k, total;
 };
 SampleWs sample_ws_layout(int B, int K, const RowGeom &g);
 int resid_tiles_per_wave(int B, int ntiles);
-GreedyWs greedy_ws_layout(long long rows, const RowGeom &g);
+GreedyWs greedy_ws_layout(int B, int rows_per_req, const RowGeom &g);
 
 // Temperature scale c = log2(e)/T split as c_hi + c_lo with both floats and
 // c_lo > 0, so x*c_hi + x*c_lo reproduces x*c to ~2^-48 and -inf*c stays -inf.
@@ -104,6 +115,13 @@ hipError_t launch_accept(const void *tgt, const void *drf, const int32_t *drafts
                          sv_dtype dt, const Scale &sc, const float *part_R, const double *part_s,
                          double *L2, int32_t *accept_len, int32_t *out_tokens, float *lse_t,
                          float *lse_d, int32_t *status, ResidParam *rp, hipStream_t s);
+bool skip_supported(int K);
+size_t skip_ctl_bytes(int B, int K);
+hipError_t launch_skip(const void *tgt, const void *drf, const int32_t *drafts, const float *ua,
+                       const float *us, int B, int K, int V, const RowGeom &g, sv_dtype dt,
+                       const Scale &sc, float *part_R, double *part_s, double *L2, void *ctl_base,
+                       int32_t *accept_len, int32_t *out_tokens, int32_t *status, ResidParam *rp,
+                       hipStream_t s);
 hipError_t launch_resid_mass(const void *tgt, const void *drf, int B, int V, const RowGeom &g,
                              sv_dtype dt, const Scale &sc, const ResidParam *rp, double *tile_mass,
                              hipStream_t s);

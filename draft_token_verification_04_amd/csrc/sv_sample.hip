@@ -39,22 +39,14 @@ constexpr double kLn2 = 0.6931471805599453094172321214581766;
 
 // ---- S1: per-segment row statistics ---------------------------------------------
 
+// One wave's (R, s) over vectors [v0, v1) of a row: R = fp32(max * c_hi) and
+// s = sum 2^(x c - R) with the exponent formed by two fused multiply-adds.
+// A segment that is all -inf yields (-inf, 0).
 template <typename E, bool ALIGNED, int U>
-__global__ __launch_bounds__(kBlock) void k_rowstats(
-    const typename E::storage *__restrict__ tgt, const typename E::storage *__restrict__ drf,
-    long long rows_t, long long nwaves, int V, int nvec, int segs, float c_hi, float c_lo,
-    float *__restrict__ part_R, double *__restrict__ part_s) {
+__device__ __forceinline__ void segment_stats(const typename E::storage *__restrict__ base, int V,
+                                              int v0, int v1, float c_hi, float c_lo, int lane,
+                                              float &R, double &s) {
     constexpr int P = E::kPerVec;
-    const int lane = threadIdx.x & (kWave - 1);
-    const long long wave = static_cast<long long>(blockIdx.x) * kWavesPerBlock + (threadIdx.x >> 6);
-    if (wave >= nwaves) return;
-    const long long row = wave / segs;
-    const int seg = static_cast<int>(wave - row * segs);
-    const typename E::storage *base =
-        row < rows_t ? tgt + row * static_cast<long long>(V) : drf + (row - rows_t) * static_cast<long long>(V);
-    const int v0 = static_cast<int>((static_cast<long long>(seg) * nvec) / segs);
-    const int v1 = static_cast<int>((static_cast<long long>(seg + 1) * nvec) / segs);
-
     Staged<E, ALIGNED> st[U];
 #pragma unroll
     for (int k = 0; k < U; ++k) {
@@ -73,9 +65,8 @@ __global__ __launch_bounds__(kBlock) void k_rowstats(
         for (int e = 0; e < P; ++e) m = fmaxf(m, x[e]);
     }
     m = wave_max(m);
-
-    float R = -__builtin_huge_valf();
-    double s = 0.0;
+    R = -__builtin_huge_valf();
+    s = 0.0;
     if (m != -__builtin_huge_valf()) {
         R = m * c_hi;
 #pragma unroll
@@ -88,9 +79,97 @@ __global__ __launch_bounds__(kBlock) void k_rowstats(
         }
         s = wave_sum(s);
     }
+}
+
+// (R, s) of vectors [v0, v1) walked in chunks of 64*U vectors, the next
+// chunk's loads issued before the current chunk is summed.  Each chunk gets
+// its own reference R_k; the chunks are combined in fp64 at the end.
+template <typename E, bool ALIGNED, int U, int CH>
+__device__ __forceinline__ void segment_stats_chunked(const typename E::storage *__restrict__ base, int V,
+                                                      int v0, int v1, float c_hi, float c_lo, int lane,
+                                                      float &R, double &s) {
+    constexpr int P = E::kPerVec;
+    float Rk[CH];
+    double sk[CH];
+    Staged<E, ALIGNED> a[U], b[U];
+    auto load = [&](Staged<E, ALIGNED>(&st)[U], int c0) {
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            const int j = c0 + k * kWave + lane;
+            if (j < v1)
+                st[k].load(base, V, j);
+            else
+                st[k].set_neg_inf();
+        }
+    };
+    auto sum = [&](const Staged<E, ALIGNED>(&st)[U], int ch) {
+        float m = -__builtin_huge_valf();
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            float x[P];
+            st[k].get(x);
+#pragma unroll
+            for (int e = 0; e < P; ++e) m = fmaxf(m, x[e]);
+        }
+        m = wave_max(m);
+        float r = -__builtin_huge_valf();
+        double t = 0.0;
+        if (m != -__builtin_huge_valf()) {
+            r = m * c_hi;
+#pragma unroll
+            for (int k = 0; k < U; ++k) {
+                float x[P];
+                st[k].get(x);
+#pragma unroll
+                for (int e = 0; e < P; ++e) x[e] = fast_exp2(fmaf(x[e], c_lo, fmaf(x[e], c_hi, -r)));
+                t += static_cast<double>(pairwise_sum(x));
+            }
+        }
+        Rk[ch] = r;
+        sk[ch] = t;
+    };
+    constexpr int step = kWave * U;
+    load(a, v0);
+#pragma unroll
+    for (int ch = 0; ch < CH; ch += 2) {
+        if (ch + 1 < CH) load(b, v0 + (ch + 1) * step);
+        sum(a, ch);
+        if (ch + 2 < CH) load(a, v0 + (ch + 2) * step);
+        if (ch + 1 < CH) sum(b, ch + 1);
+    }
+    float Rm = -__builtin_huge_valf();
+#pragma unroll
+    for (int ch = 0; ch < CH; ++ch) Rm = fmaxf(Rm, Rk[ch]);
+    double t = 0.0;
+    if (Rm != -__builtin_huge_valf()) {
+#pragma unroll
+        for (int ch = 0; ch < CH; ++ch)
+            if (sk[ch] > 0.0) t += sk[ch] * exp2(static_cast<double>(Rk[ch]) - static_cast<double>(Rm));
+    }
+    R = Rm;
+    s = wave_sum(t);
+}
+
+template <typename E, bool ALIGNED, int U>
+__global__ __launch_bounds__(kBlock) void k_rowstats(
+    const typename E::storage *__restrict__ tgt, const typename E::storage *__restrict__ drf,
+    long long rows_t, long long nwaves, int V, int nvec, int segs, float c_hi, float c_lo,
+    float *__restrict__ part_R, double *__restrict__ part_s) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const long long wave = static_cast<long long>(blockIdx.x) * kWavesPerBlock + (threadIdx.x >> 6);
+    if (wave >= nwaves) return;
+    const long long row = wave / segs;
+    const int seg = static_cast<int>(wave - row * segs);
+    const typename E::storage *base =
+        row < rows_t ? tgt + row * static_cast<long long>(V) : drf + (row - rows_t) * static_cast<long long>(V);
+    const int v0 = static_cast<int>((static_cast<long long>(seg) * nvec) / segs);
+    const int v1 = static_cast<int>((static_cast<long long>(seg + 1) * nvec) / segs);
+    float R;
+    double sum;
+    segment_stats<E, ALIGNED, U>(base, V, v0, v1, c_hi, c_lo, lane, R, sum);
     if (lane == 0) {
         part_R[wave] = R;
-        part_s[wave] = s;
+        part_s[wave] = sum;
     }
 }
 
@@ -469,6 +548,188 @@ __global__ __launch_bounds__(kWave) void k_resid_select(
     }
 }
 
+// ---- dead-row skipping (stochastic chains without lse outputs) --------------------
+//
+// One launch over every (position p, request b, row kind, segment) in
+// position-major order, so the segments of position p are handed out before
+// those of p+1.  A wave first reads its request's `finished` flag and skips its
+// segment when the request is already decided.  The last wave to finish the
+// segments of (b, p) takes the acceptance decision of position p (the same
+// fp64 merge, gather and ratio test as the full-read path) and records it in
+// the request's mask: bit p = "position p decided", bit 32+p = "draft p
+// rejected" (position K's bit means its bonus row is merged).  The request is
+// decided once the mask holds a rejection with every earlier position decided,
+// or every position 0..K decided without one; whichever decider completes that
+// prefix finishes the request (one winner by compare-and-swap) and raises the
+// flag.  Rows of positions after the first rejection are read only by waves
+// that started before the decision was known.  Nothing waits.
+
+// Largest K this path handles (decided and rejected bits share one 64-bit word).
+constexpr int kSkipMaxK = 31;
+
+struct SkipCtl {
+    unsigned *ticket;    // [B*(K+1)] segments finished per (request, position)
+    uint64_t *mask;      // [B] decided | rejected << 32
+    unsigned *won;       // [B] 1 once a decider has claimed finishing the request
+    unsigned *finished;  // [B] raised after the request's outputs are written
+};
+
+__global__ __launch_bounds__(kBlock) void k_zero_words(uint32_t *__restrict__ p, long long n) {
+    for (long long i = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+         i += static_cast<long long>(gridDim.x) * blockDim.x)
+        p[i] = 0;
+}
+
+// log2 sum_v 2^(L[v] c) of one row from segment partials read as shared words.
+__device__ __forceinline__ double merge_row_shared(float *pR, double *pS, int segs, int lane) {
+    float Rm = -__builtin_huge_valf();
+    for (int sg = lane; sg < segs; sg += kWave) Rm = fmaxf(Rm, shared_load(&pR[sg]));
+    Rm = wave_max(Rm);
+    double acc = 0.0;
+    if (Rm != -__builtin_huge_valf()) {
+        for (int sg = lane; sg < segs; sg += kWave) {
+            const double ss = shared_load(&pS[sg]);
+            if (ss > 0.0) acc += ss * exp2(static_cast<double>(shared_load(&pR[sg])) - static_cast<double>(Rm));
+        }
+    }
+    acc = wave_sum(acc);
+    return acc > 0.0 ? static_cast<double>(Rm) + log2(acc) : -__builtin_huge_val();
+}
+
+// Outputs of request b decided at n (mode 1: rejection at n, residual of
+// rows n; mode 0: bonus from target row K), written by one wave.
+__device__ __forceinline__ void skip_finish(const int32_t *__restrict__ xb, const float *__restrict__ us,
+                                            int b, int K, int V, int n, int mode, double L2p, double L2q,
+                                            int32_t *__restrict__ accept_len,
+                                            int32_t *__restrict__ out_tokens,
+                                            int32_t *__restrict__ status, ResidParam *__restrict__ rp,
+                                            int lane) {
+    bool bad = false;
+    int32_t *tok = out_tokens + static_cast<long long>(b) * (K + 1);
+    for (int i = lane; i <= K; i += kWave) {
+        const int x = i < K ? xb[i] : 0;
+        if (i < K && (x < 0 || x >= V)) bad = true;
+        tok[i] = i < n ? x : -1;
+    }
+    const bool any_bad = ballot(bad) != 0;
+    if (lane == 0) {
+        accept_len[b] = n;
+        if (status) status[b] = any_bad ? 1 : 0;
+        ResidParam P;
+        P.pos = n;
+        P.u = static_cast<double>(us[static_cast<long long>(b) * (K + 1) + n]);
+        P.row_p = static_cast<long long>(b) * (K + 1) + n;
+        P.L2p = L2p;
+        P.mode = mode;
+        P.row_q = mode ? static_cast<long long>(b) * K + n : 0;
+        P.L2q = mode ? L2q : 0.0;
+        rp[b] = P;
+    }
+}
+
+template <typename E, bool ALIGNED, int U>
+__global__ __launch_bounds__(kBlock) void k_skip_stats(
+    const typename E::storage *__restrict__ tgt, const typename E::storage *__restrict__ drf,
+    const int32_t *__restrict__ drafts, const float *__restrict__ ua, const float *__restrict__ us,
+    int B, int K, int V, int nvec, int segs, double c, float c_hi, float c_lo, float *part_R,
+    double *part_s, double *L2, SkipCtl ctl, int32_t *__restrict__ accept_len,
+    int32_t *__restrict__ out_tokens, int32_t *__restrict__ status, ResidParam *__restrict__ rp) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const long long wave = static_cast<long long>(blockIdx.x) * kWavesPerBlock + (threadIdx.x >> 6);
+    const long long per_pos = static_cast<long long>(B) * 2 * segs;
+    if (wave >= per_pos * (K + 1)) return;
+    const int p = static_cast<int>(wave / per_pos);
+    const long long rem = wave - static_cast<long long>(p) * per_pos;
+    const int b = static_cast<int>(rem / (2 * segs));
+    const int r = static_cast<int>(rem - static_cast<long long>(b) * 2 * segs);
+    const int kind = r / segs, sg = r - kind * segs;
+    if (kind == 1 && p == K) return;  // no draft row at the bonus position
+    if (uniform(shared_load(&ctl.finished[b]))) return;
+
+    const long long rows_t = static_cast<long long>(B) * (K + 1);
+    const long long gt = static_cast<long long>(b) * (K + 1) + p;
+    const long long gd = rows_t + static_cast<long long>(b) * K + p;
+    const long long g = kind == 0 ? gt : gd;
+    const typename E::storage *base = kind == 0 ? tgt + gt * static_cast<long long>(V)
+                                                : drf + (static_cast<long long>(b) * K + p) * static_cast<long long>(V);
+    const int v0 = static_cast<int>((static_cast<long long>(sg) * nvec) / segs);
+    const int v1 = static_cast<int>((static_cast<long long>(sg + 1) * nvec) / segs);
+    float R;
+    double sum;
+    segment_stats_chunked<E, ALIGNED, U, kSkipChunks>(base, V, v0, v1, c_hi, c_lo, lane, R, sum);
+    if (lane == 0) {
+        shared_store(&part_R[g * segs + sg], R);
+        shared_store(&part_s[g * segs + sg], sum);
+    }
+    const unsigned parts = static_cast<unsigned>((p < K ? 2 : 1) * segs);
+    if (!wave_arrive(&ctl.ticket[gt], parts, lane)) return;
+
+    // last segment of (b, p): decide position p
+    const int nrows = 2 * K + 1;
+    double *L2b = L2 + static_cast<long long>(b) * nrows;
+    const double L2p = merge_row_shared(part_R + gt * segs, part_s + gt * segs, segs, lane);
+    uint64_t bits = 1ull << p;
+    if (p < K) {
+        const double L2q = merge_row_shared(part_R + gd * segs, part_s + gd * segs, segs, lane);
+        const int x = uniform(drafts[static_cast<long long>(b) * K + p]);
+        double ratio = 0.0;
+        if (x >= 0 && x < V) {
+            const double px = exp2(static_cast<double>(to_f32(tgt[gt * V + x])) * c - L2p);
+            const double qx = exp2(static_cast<double>(to_f32(drf[(static_cast<long long>(b) * K + p) * V + x])) * c - L2q);
+            ratio = qx == 0.0 ? __builtin_huge_val() : px / qx;
+        }
+        const double u = static_cast<double>(ua[static_cast<long long>(b) * K + p]);
+        if (!(u < ratio)) bits |= 1ull << (32 + p);
+        if (lane == 0) shared_store(&L2b[K + 1 + p], L2q);
+    }
+    if (lane == 0) shared_store(&L2b[p], L2p);
+    wait_own_stores();
+    uint64_t old = 0;
+    if (lane == 0) old = __hip_atomic_fetch_or(&ctl.mask[b], bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t m = uniform(static_cast<uint64_t>(__shfl(static_cast<long long>(old), 0, kWave))) | bits;
+    const unsigned decided = static_cast<unsigned>(m), rejected = static_cast<unsigned>(m >> 32);
+    int n = -1;
+    if (rejected) {
+        const int rj = __ffs(static_cast<int>(rejected)) - 1;
+        const unsigned below = rj == 0 ? 0u : (0xffffffffu >> (32 - rj));
+        if ((decided & below) == below) n = rj;
+    } else {
+        const unsigned all = K == 31 ? 0xffffffffu : ((1u << (K + 1)) - 1u);
+        if ((decided & all) == all) n = K;
+    }
+    if (n < 0) return;
+    unsigned prev = 1;
+    if (lane == 0) {
+        unsigned expect = 0;
+        prev = __hip_atomic_compare_exchange_strong(&ctl.won[b], &expect, 1u, __ATOMIC_RELAXED,
+                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                   ? 0u
+                   : 1u;
+    }
+    if (uniform(static_cast<unsigned>(__shfl(static_cast<int>(prev), 0, kWave))) != 0) return;
+    const double L2pn = shared_load(&L2b[n]);
+    const double L2qn = n < K ? shared_load(&L2b[K + 1 + n]) : 0.0;
+    skip_finish(drafts + static_cast<long long>(b) * K, us, b, K, V, n, n < K ? 1 : 0, L2pn, L2qn,
+                accept_len, out_tokens, status, rp, lane);
+    wait_own_stores();
+    if (lane == 0) shared_store(&ctl.finished[b], 1u);
+}
+
+template <typename E, bool ALIGNED>
+hipError_t skip_stats_t(const void *tgt, const void *drf, const int32_t *drafts, const float *ua,
+                        const float *us, int B, int K, int V, const RowGeom &g, const Scale &sc,
+                        float *part_R, double *part_s, double *L2, const SkipCtl &ctl,
+                        int32_t *accept_len, int32_t *out_tokens, int32_t *status, ResidParam *rp,
+                        hipStream_t s) {
+    using T = typename E::storage;
+    const long long nwaves = static_cast<long long>(K + 1) * B * 2 * g.segs;
+    const long long blocks = (nwaves + kWavesPerBlock - 1) / kWavesPerBlock;
+    return launch_kernel(k_skip_stats<E, ALIGNED, kSkipVecsPerLane>, dim3(static_cast<unsigned>(blocks)),
+                         dim3(kBlock), 0, s, static_cast<const T *>(tgt), static_cast<const T *>(drf),
+                         drafts, ua, us, B, K, V, g.nvec, g.segs, sc.c, sc.c_hi, sc.c_lo, part_R, part_s,
+                         L2, ctl, accept_len, out_tokens, status, rp);
+}
+
 template <typename E, bool ALIGNED>
 hipError_t rowstats_t(const void *tgt, const void *drf, long long rows_t, long long rows_total, int V,
                       const RowGeom &g, const Scale &sc, float *part_R, double *part_s,
@@ -491,6 +752,37 @@ hipError_t launch_rowstats(const void *tgt, const void *drf, long long rows_t, l
                          : rowstats_t<BF16, false>(tgt, drf, rows_t, rows_total, V, g, sc, part_R, part_s, s);
     return g.aligned ? rowstats_t<F32, true>(tgt, drf, rows_t, rows_total, V, g, sc, part_R, part_s, s)
                      : rowstats_t<F32, false>(tgt, drf, rows_t, rows_total, V, g, sc, part_R, part_s, s);
+}
+
+bool skip_supported(int K) { return K <= kSkipMaxK; }
+
+size_t skip_ctl_bytes(int B, int K) {
+    return sizeof(unsigned) * static_cast<size_t>(B) * (K + 1) + sizeof(uint64_t) * B + 2 * sizeof(unsigned) * B;
+}
+
+hipError_t launch_skip(const void *tgt, const void *drf, const int32_t *drafts, const float *ua,
+                       const float *us, int B, int K, int V, const RowGeom &g, sv_dtype dt,
+                       const Scale &sc, float *part_R, double *part_s, double *L2, void *ctl_base,
+                       int32_t *accept_len, int32_t *out_tokens, int32_t *status, ResidParam *rp,
+                       hipStream_t s) {
+    SkipCtl ctl;
+    char *q = static_cast<char *>(ctl_base);
+    ctl.mask = reinterpret_cast<uint64_t *>(q);
+    ctl.ticket = reinterpret_cast<unsigned *>(ctl.mask + B);
+    ctl.won = ctl.ticket + static_cast<size_t>(B) * (K + 1);
+    ctl.finished = ctl.won + B;
+    const long long words = static_cast<long long>(skip_ctl_bytes(B, K) / sizeof(uint32_t));
+    const long long zb = std::max<long long>(1, std::min<long long>(1024, (words + kBlock - 1) / kBlock));
+    trace_select(-1);
+    hipLaunchKernelGGL(k_zero_words, dim3(static_cast<unsigned>(zb)), dim3(kBlock), 0, s,
+                       reinterpret_cast<uint32_t *>(ctl_base), words);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    trace_select(SV_K_SKIP_STATS);
+#define SV_SK(E, A) skip_stats_t<E, A>(tgt, drf, drafts, ua, us, B, K, V, g, sc, part_R, part_s, L2, ctl, accept_len, out_tokens, status, rp, s)
+    if (dt == SV_BF16) return g.aligned ? SV_SK(BF16, true) : SV_SK(BF16, false);
+    return g.aligned ? SV_SK(F32, true) : SV_SK(F32, false);
+#undef SV_SK
 }
 
 hipError_t launch_accept(const void *tgt, const void *drf, const int32_t *drafts, const float *ua,

@@ -100,6 +100,11 @@ size_t sv_greedy_workspace_bytes(int B, int rows_per_req, int V, sv_dtype dt);
  *   req_status [B]       optional: 0, or 1 if a draft id of the request is
  *                        outside [0, V).
  *
+ * Rows read: when lse_target and lse_draft are both NULL (and K <= 31), the
+ * rows of positions after each request's first rejection are skipped, except
+ * by segments already in flight when that rejection is decided; otherwise
+ * every row is read once for its log-sum-exp.  The outputs are the same.
+ *
  * The drawn token is the smallest id v with positive mass m(v) whose running
  * mass sum_{w <= v} m(w) exceeds u * Z, Z the total mass (if none, the largest
  * id with positive mass), where m = max(0, p_n - q_n) after a rejection and
@@ -184,7 +189,8 @@ typedef enum {
     SV_K_ARGMAX = 4,       /* per-row argmax partials */
     SV_K_MATCH = 5,        /* greedy chain acceptance */
     SV_K_TREE = 6,         /* greedy tree walk */
-    SV_K_COUNT = 7
+    SV_K_SKIP_STATS = 7,   /* row statistics + acceptance, skipping rows after a rejection */
+    SV_K_COUNT = 8
 } sv_kernel_id;
 
 sv_status sv_trace_begin(int capacity, unsigned kernel_mask);

@@ -43,26 +43,30 @@ SAMPLE_GRID = [
 ]
 
 
+# lse=True reads every row (its statistics feed the lse outputs); lse=False
+# takes the path that never reads rows after a request's first rejection.
+@pytest.mark.parametrize("lse", [True, False], ids=["full", "skip"])
 @pytest.mark.parametrize("case", SAMPLE_GRID, ids=lambda c: "B{}K{}V{}{}T{}".format(*c[:5]))
-def test_sample_grid(case):
+def test_sample_grid(case, lse):
     B, K, V, dt, T, spikes, noise = case
-    note(f"sample grid {case}")
+    note(f"sample grid {case} lse={lse}")
     w = workloads.make_sample(B, K, V, dt, T, target_sigma=3.0, spikes=spikes, noise_sigma=noise,
                               seed=zlib.crc32(repr(case).encode()))
     o = oracle_sample(w)
-    g = gpu_sample(w)
+    g = gpu_sample(w, lse=lse)
     ncmp, nflag, ndiff = check_sample(w, g, o)
     assert ncmp + nflag == B
 
 
+@pytest.mark.parametrize("lse", [True, False], ids=["full", "skip"])
 @pytest.mark.parametrize("c", [1, 2, 3])
-def test_sample_workloads_full_size(c):
-    note(f"sample workload {c}")
+def test_sample_workloads_full_size(c, lse):
+    note(f"sample workload {c} lse={lse}")
     w = workloads.make_config(c)
     o = oracle_sample(w)
-    g = gpu_sample(w)
+    g = gpu_sample(w, lse=lse)
     ncmp, nflag, ndiff = check_sample(w, g, o)
-    print(f"workload {c}: compared {ncmp}, flagged {nflag}, flagged-and-different {ndiff}, "
+    print(f"workload {c} lse={lse}: compared {ncmp}, flagged {nflag}, flagged-and-different {ndiff}, "
           f"mean accept {g['accept_len'].mean():.3f}")
 
 
@@ -187,14 +191,15 @@ def test_masked_vocabulary_and_out_of_range_drafts():
     w.draft_tokens[4, 0] = -2
     w.u_accept[:] = 0.0  # accept everything that can be accepted
     o = oracle_sample(w)
-    g = gpu_sample(w)
-    check_sample(w, g, o)
-    assert g["status"][3] == 1 and g["status"][4] == 1 and g["accept_len"][4] == 0
-    # masked ids are never drawn
-    for b in range(B):
-        n = g["accept_len"][b]
-        t = g["tokens"][b, n]
-        assert not mask[b, n, t]
+    for lse in (True, False):
+        g = gpu_sample(w, lse=lse)
+        check_sample(w, g, o)
+        assert g["status"][3] == 1 and g["status"][4] == 1 and g["accept_len"][4] == 0
+        # masked ids are never drawn
+        for b in range(B):
+            n = g["accept_len"][b]
+            t = g["tokens"][b, n]
+            assert not mask[b, n, t]
 
 
 def test_empty_batch_and_determinism():
@@ -206,6 +211,10 @@ def test_empty_batch_and_determinism():
     a, b = gpu_sample(w), gpu_sample(w)
     for k in a:
         assert np.array_equal(a[k], b[k]), k
+    c, d = gpu_sample(w, lse=False), gpu_sample(w, lse=False)
+    for k in c:
+        assert np.array_equal(c[k], d[k]), k
+        assert np.array_equal(a[k], c[k]), k  # both paths agree bit for bit
     wg = workloads.make_greedy(12, 7, 20000, "bf16", seed=2)
     a, b = gpu_greedy(wg), gpu_greedy(wg)
     assert np.array_equal(a["tokens"], b["tokens"])
@@ -271,3 +280,7 @@ def test_trace_records_each_kernel():
     recs = sv.trace_end()
     assert [r[0] for r in recs] == ["rowstats", "accept", "resid_mass", "resid_select"]
     assert all(ms > 0 for _, ms in recs)
+    sv.trace_begin(64)
+    gpu_sample(w, lse=False)
+    recs = sv.trace_end()
+    assert [r[0] for r in recs] == ["skip_stats", "resid_mass", "resid_select"]
