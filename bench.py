@@ -15,8 +15,10 @@ value = target rows verified per second over the whole step
 before timing starts; outputs and workspaces are preallocated.  Per-kernel
 durations come from HIP events the library records around each launch on the
 stream it launches on (sv_trace_begin/sv_trace_end): the timed steps carry
-events around the two streaming kernels (row statistics, argmax) only; the
-per-kernel breakdown of the small kernels comes from a separate traced pass.
+events around the streaming kernels (row statistics, argmax, and the greedy
+chain's row-skipping argmax) only; the per-kernel breakdown of the small kernels
+comes from a separate traced pass.  The greedy chain (K = 7 <= 31) reads only
+rows 0..n_b of each request, so its algorithmic bytes are sum_b (n_b + 1) rows.
 
 Usage: python bench.py [--gpus 1] [--steps 200] [--warmup 50] [--mode all|sample|greedy|tree]
                        [--no-cpu-baseline]
@@ -45,6 +47,10 @@ KERNEL_SOURCES = {
     "argmax": ["draft_token_verification_04_amd/csrc/sv_greedy.hip",
                "draft_token_verification_04_amd/csrc/sv_device.hpp",
                "draft_token_verification_04_amd/csrc/sv_internal.hpp"],
+    "skip_argmax": ["draft_token_verification_04_amd/csrc/sv_greedy.hip",
+                    "draft_token_verification_04_amd/csrc/sv_skip.hpp",
+                    "draft_token_verification_04_amd/csrc/sv_device.hpp",
+                    "draft_token_verification_04_amd/csrc/sv_internal.hpp"],
 }
 
 
@@ -228,8 +234,9 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    # timed region: events only around the two streaming kernels the roofline is quoted on
-    sv.trace_begin(max(64, args.steps * 4 + 16), kernels=("rowstats", "argmax"))
+    # timed region: events only around the streaming kernels the rooflines are quoted on
+    timed_kernels = ("rowstats", "argmax", "skip_argmax")
+    sv.trace_begin(max(64, args.steps * 4 + 16), kernels=timed_kernels)
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step()
@@ -254,62 +261,56 @@ def main():
 
     R = w3.V * 2  # bytes of one bf16 row
     n3 = calls.s_n.cpu().numpy()
+    n4 = calls.g_n.cpu().numpy()
     resid_rows = int(np.sum(np.where(n3 < w3.K, 2, 1)))
+    # algorithmic bytes: the stochastic chain with lse outputs reads every row once
+    # plus the drawn row (pair); the greedy chain needs rows 0..n_b of each request
     bytes_mode = {
         "sample": (w3.B * (2 * w3.K + 1) + resid_rows) * R,
-        "greedy": w4.B * (w4.K + 1) * R,
+        "greedy": int(np.sum(n4 + 1)) * R,
         "tree": w5.B * w5.N * R,
     }
     rows_mode = {"sample": w3.B * (w3.K + 1), "greedy": w4.B * (w4.K + 1), "tree": w5.B * w5.N}
     kernels_mode = {"sample": ["rowstats", "accept", "resid_mass", "resid_select"],
-                    "greedy": ["argmax", "match"], "tree": ["argmax", "tree"]}
+                    "greedy": ["skip_argmax"], "tree": ["argmax", "tree"]}
     rows_step = sum(rows_mode[m] for m in active)
     bytes_step = sum(bytes_mode[m] for m in active)
     value = rows_step / (ms_per_step * 1e-3)
     hbm_gbps = bytes_step / (ms_per_step * 1e-3) / 1e9
 
-    # dominant kernel: the row-statistics pass of the stochastic chain, else argmax
-    if "sample" in active:
-        dom, dom_bytes, dom_ms = "rowstats", w3.B * (2 * w3.K + 1) * R, kmean.get("rowstats")
-    else:
-        dom = "argmax"
-        dom_bytes = bytes_mode[active[0]]
-        dom_ms = statistics.mean(per_kernel["argmax"]) if "argmax" in per_kernel else None
-    roof = None
-    if dom_ms:
-        ach = dom_bytes / (dom_ms * 1e-3) / 1e9
-        tr = stored_traffic(dom)
-        roof = {"bound": "hbm", "kernel": dom, "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS,
-                "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4),
+    def roofline(kernel, nbytes, workload):
+        ms = kmean.get(kernel)
+        if not ms:
+            return None
+        ach = nbytes / (ms * 1e-3) / 1e9
+        tr = stored_traffic(kernel)
+        return {"bound": "hbm", "kernel": kernel, "workload": workload, "achieved": round(ach, 1),
+                "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4),
                 "traffic": tr["bytes_per_launch"] if tr else None,
-                "bytes_per_launch": dom_bytes, "avg_launch_ms": round(dom_ms, 5)}
-    extra = {}
-    if "argmax" in per_kernel and dom != "argmax":
-        a = per_kernel["argmax"]
-        # greedy (B=256, K=7) and tree (B=64, N=33) launches alternate
-        g_ms = statistics.mean(a[0::2]) if "greedy" in active and "tree" in active else statistics.mean(a)
-        gb = bytes_mode["greedy"] if "greedy" in active else bytes_mode["tree"]
-        extra = {"kernel": "argmax", "workload": "greedy chain B=256 K=7" if "greedy" in active else "tree",
-                 "achieved": round(gb / (g_ms * 1e-3) / 1e9, 1), "unit": "GB/s",
-                 "frac": round(gb / (g_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-                 "avg_launch_ms": round(g_ms, 5), "bytes_per_launch": gb}
+                "bytes_per_launch": nbytes, "avg_launch_ms": round(ms, 5)}
+
+    others = {}
+    if "sample" in active:
+        roof = roofline("rowstats", w3.B * (2 * w3.K + 1) * R, "stochastic chain B=256 K=7")
+    if "tree" in active:
+        others["argmax"] = roofline("argmax", bytes_mode["tree"], "greedy tree B=64 N=33")
+    if "greedy" in active:
+        others["skip_argmax"] = roofline("skip_argmax", bytes_mode["greedy"],
+                                         "greedy chain B=256 K=7 (rows 0..n_b per request)")
+    if "sample" not in active:
+        roof = others.pop("argmax" if "tree" in active else "skip_argmax")
 
     modes = {}
     for m in active:
-        ks = kernels_mode[m]
-        if m == "greedy" and "tree" in active:
-            kt = statistics.mean(per_kernel["argmax"][0::2]) + kmean.get("match", 0.0)
-        elif m == "tree" and "greedy" in active:
-            kt = statistics.mean(per_kernel["argmax"][1::2]) + kmean.get("tree", 0.0)
-        elif m in ("greedy", "tree"):
-            kt = statistics.mean(per_kernel["argmax"]) + kmean.get("match" if m == "greedy" else "tree", 0.0)
-        else:
-            kt = sum(kmean.get(k, 0.0) for k in ks)
+        kt = sum(kmean.get(k, 0.0) for k in kernels_mode[m])
         modes[m] = {"rows": rows_mode[m], "bytes": bytes_mode[m], "kernel_ms": round(kt, 5),
                     "rows_per_s": round(rows_mode[m] / (kt * 1e-3), 1),
                     "gbps": round(bytes_mode[m] / (kt * 1e-3) / 1e9, 1)}
     if "sample" in modes:
         modes["sample"]["mean_tokens_per_round"] = round(float(n3.mean() + 1), 4)
+    if "greedy" in modes:
+        modes["greedy"]["mean_tokens_per_round"] = round(float(n4.mean() + 1), 4)
+        modes["greedy"]["dense_bytes"] = w4.B * (w4.K + 1) * R
 
     # each call on its own, back to back (launch gaps included)
     def per_call(fn, reps):
@@ -376,7 +377,7 @@ def main():
         "hbm_gbps": round(hbm_gbps, 1),
         "hbm_frac_of_peak": round(hbm_gbps / HBM_PEAK_GBPS, 4),
         "roofline": roof,
-        "roofline_argmax": extra or None,
+        "roofline_others": others or None,
         "modes": modes,
         "kernel_ms": {k: round(v, 5) for k, v in kmean.items()},
         "calls_alone": calls_alone,

@@ -27,7 +27,7 @@ SV_OK, SV_ERR_INVALID_ARG, SV_ERR_UNSUPPORTED, SV_ERR_WORKSPACE, SV_ERR_HIP = ra
 SV_F32, SV_BF16 = 0, 1
 SV_MAX_TREE_NODES = 2048
 KERNELS = ("rowstats", "accept", "resid_mass", "resid_select", "argmax", "match", "tree",
-           "skip_stats")
+           "skip_stats", "skip_argmax")
 
 EXPORTS = ("sv_sample_workspace_bytes", "sv_greedy_workspace_bytes", "spec_verify_sample",
            "spec_verify_greedy", "spec_verify_tree", "sv_status_string", "sv_version",

@@ -60,10 +60,19 @@ int resid_tiles_per_wave(int B, int ntiles) {
 
 GreedyWs greedy_ws_layout(int B, int rows_per_req, const RowGeom &g) {
     GreedyWs w;
-    const size_t parts = static_cast<size_t>(B) * static_cast<size_t>(rows_per_req) * static_cast<size_t>(g.segs);
+    // chains short enough for row skipping also hold that pass's keys and control words
+    const bool skip = skip_supported(rows_per_req - 1);
+    const int skip_segs = skip ? row_geom(g.nvec * g.per_vec, g.per_vec == 8 ? SV_BF16 : SV_F32, true,
+                                          kGSkipVecsPerLane * kGSkipChunks).segs
+                               : 0;
+    const size_t rows = static_cast<size_t>(B) * static_cast<size_t>(rows_per_req);
     size_t o = 0;
     w.part_k = o;
-    o = align_up(o + parts * sizeof(uint64_t));
+    o = align_up(o + rows * static_cast<size_t>(std::max(g.segs, skip_segs)) * sizeof(uint64_t));
+    w.amax = o;
+    if (skip) o = align_up(o + rows * sizeof(int32_t));
+    w.skipctl = o;
+    if (skip) o = align_up(o + skip_ctl_bytes(B, rows_per_req - 1));
     w.total = o;
     return w;
 }
@@ -237,13 +246,23 @@ sv_status spec_verify_greedy(const void *target_logits, const int32_t *draft_tok
     const long long rows = static_cast<long long>(B) * (K + 1);
     const GreedyWs L = greedy_ws_layout(B, K + 1, g);
     if (workspace_bytes < L.total) return SV_ERR_WORKSPACE;
-    uint64_t *pk = reinterpret_cast<uint64_t *>(static_cast<char *>(workspace) + L.part_k);
+    char *ws = static_cast<char *>(workspace);
+    uint64_t *pk = reinterpret_cast<uint64_t *>(ws + L.part_k);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = traced(SV_K_ARGMAX, s, [&] { return launch_argmax(target_logits, rows, V, g, dt, pk, s); });
-    if (e == hipSuccess)
-        e = traced(SV_K_MATCH, s, [&] {
-            return launch_match(pk, draft_tokens, B, K, V, g, accept_len, out_tokens, req_status, s);
-        });
+    hipError_t e = hipSuccess;
+    if (SV_GREEDY_SKIP && skip_supported(K)) {
+        // rows of positions after each request's first mismatch are not read
+        const RowGeom gs = row_geom(V, dt, aligned16(target_logits), kGSkipVecsPerLane * kGSkipChunks);
+        e = launch_skip_match(target_logits, draft_tokens, B, K, V, gs, dt, pk,
+                              reinterpret_cast<int32_t *>(ws + L.amax), ws + L.skipctl, accept_len,
+                              out_tokens, req_status, s);
+    } else {
+        e = traced(SV_K_ARGMAX, s, [&] { return launch_argmax(target_logits, rows, V, g, dt, pk, s); });
+        if (e == hipSuccess)
+            e = traced(SV_K_MATCH, s, [&] {
+                return launch_match(pk, draft_tokens, B, K, V, g, accept_len, out_tokens, req_status, s);
+            });
+    }
     return e == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 
@@ -290,7 +309,8 @@ const char *sv_version(void) { return "specverify 0.1.0 (gfx950)"; }
 
 const char *sv_kernel_name(int k) {
     static const char *names[SV_K_COUNT] = {"rowstats", "accept", "resid_mass", "resid_select",
-                                            "argmax", "match", "tree", "skip_stats"};
+                                            "argmax", "match", "tree", "skip_stats",
+                                            "skip_argmax"};
     return (k >= 0 && k < SV_K_COUNT) ? names[k] : "unknown";
 }
 

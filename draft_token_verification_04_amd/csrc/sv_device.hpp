@@ -168,6 +168,7 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 
 __device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
 
+
 // (value, index) packed so that the larger key has the larger value and, among
 // equal values, the lower index.  -0 is folded into +0 so that the two compare
 // equal, as floats do; NaN is not ordered meaningfully (inputs are finite or -inf).

@@ -20,12 +20,17 @@
 //             parent-array check in parallel, acceptance and depth of every
 //             node by pointer jumping (log2 N rounds), the deepest accepted
 //             node by an LDS max, then the path write-out.
+//   k_skip_argmax  chains with K <= 31 in one launch that does not read the
+//             rows after each request's first mismatch (the protocol is
+//             described with SkipCtl); the decision of position p is the row
+//             argmax compared with draft p.
 #include <limits.h>
 
 #include <algorithm>
 
 #include "sv_device.hpp"
 #include "sv_internal.hpp"
+#include "sv_skip.hpp"
 
 namespace sv {
 namespace {
@@ -249,6 +254,132 @@ __global__ __launch_bounds__(kBlock) void k_tree(const uint64_t *__restrict__ pa
     }
 }
 
+// Argmax key of vectors [v0, v1) of one row, read in CH chunks of U vectors
+// per lane, each chunk loaded while the previous one is scanned.  A lane visits
+// its vectors in increasing index and keeps the first whose maximum is strictly
+// greater than every earlier one (-0 and +0 compare equal), together with that
+// vector's raw contents; the lowest element of the kept vector equal to the
+// maximum is then the lane's argmax.  The wave's largest key is the segment
+// maximum with the lowest index among equals.  A lane whose elements are all
+// -inf keeps its first element, as the full-read pass does.
+template <typename E, bool ALIGNED, int U, int CH>
+__device__ __forceinline__ uint64_t segment_argmax_chunked(const typename E::storage *__restrict__ base,
+                                                           int V, int v0, int v1, int lane) {
+    constexpr int P = E::kPerVec;
+    Staged<E, ALIGNED> a[U], b[U], keep;
+    keep.set_neg_inf();
+    float best = -__builtin_huge_valf();
+    int bk = 0;  // kept vector, counted in steps of kWave vectors from v0 + lane
+    auto load = [&](Staged<E, ALIGNED>(&st)[U], int c0) {
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            const int j = c0 + k * kWave + lane;
+            if (j < v1)
+                st[k].load(base, V, j);
+            else
+                st[k].set_neg_inf();
+        }
+    };
+    auto scan = [&](const Staged<E, ALIGNED>(&st)[U], int ch) {
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            float x[P];
+            st[k].get(x);
+            float vm = x[0];
+#pragma unroll
+            for (int e = 1; e < P; ++e) vm = fmaxf(vm, x[e]);
+            if (vm > best) {
+                best = vm;
+                bk = ch * U + k;
+                keep = st[k];
+            }
+        }
+    };
+    constexpr int step = kWave * U;
+    load(a, v0);
+#pragma unroll
+    for (int ch = 0; ch < CH; ch += 2) {
+        if (ch + 1 < CH) load(b, v0 + (ch + 1) * step);
+        scan(a, ch);
+        if (ch + 2 < CH) load(a, v0 + (ch + 2) * step);
+        if (ch + 1 < CH) scan(b, ch + 1);
+    }
+    float x[P];
+    keep.get(x);
+    int e0 = P - 1;
+#pragma unroll
+    for (int e = P - 2; e >= 0; --e)
+        if (x[e] == best) e0 = e;
+    const int idx = v0 + lane < v1 ? (v0 + lane + bk * kWave) * P + e0 : INT_MAX;
+    return wave_max_u64(argmax_key(best, idx));
+}
+
+template <typename E, bool ALIGNED, int U>
+__global__ __launch_bounds__(kBlock) void k_skip_argmax(const typename E::storage *__restrict__ L,
+                                                        const int32_t *__restrict__ drafts, int B, int K,
+                                                        int V, int nvec, int segs, uint64_t *part_k,
+                                                        int32_t *amax, SkipCtl ctl,
+                                                        int32_t *__restrict__ accept_len,
+                                                        int32_t *__restrict__ out_tokens,
+                                                        int32_t *__restrict__ status) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const long long wave = static_cast<long long>(blockIdx.x) * kWavesPerBlock + (threadIdx.x >> 6);
+    const long long per_pos = static_cast<long long>(B) * segs;
+    if (wave >= per_pos * (K + 1)) return;
+    const int p = static_cast<int>(wave / per_pos);
+    const long long rem = wave - static_cast<long long>(p) * per_pos;
+    const int b = static_cast<int>(rem / segs);
+    const int sg = static_cast<int>(rem - static_cast<long long>(b) * segs);
+    if (uniform(shared_load(&ctl.finished[b]))) return;
+
+    const long long row = static_cast<long long>(b) * (K + 1) + p;
+    const int v0 = static_cast<int>((static_cast<long long>(sg) * nvec) / segs);
+    const int v1 = static_cast<int>((static_cast<long long>(sg + 1) * nvec) / segs);
+    const uint64_t key = segment_argmax_chunked<E, ALIGNED, U, kGSkipChunks>(L + row * V, V, v0, v1, lane);
+    if (lane == 0) shared_store(&part_k[row * segs + sg], key);
+    if (!wave_arrive(&ctl.ticket[row], static_cast<unsigned>(segs), lane)) return;
+
+    // last segment of (b, p): the row argmax decides position p
+    uint64_t mk = 0;
+    for (int s = lane; s < segs; s += kWave) {
+        const uint64_t k = shared_load(&part_k[row * segs + s]);
+        mk = k > mk ? k : mk;
+    }
+    const int a = uniform(argmax_key_index(wave_max_u64(mk)));
+    const int32_t *xb = drafts + static_cast<long long>(b) * K;
+    uint64_t bits = 1ull << p;
+    if (p < K && uniform(xb[p]) != a) bits |= 1ull << (32 + p);
+    if (lane == 0) shared_store(&amax[row], a);
+    const int n = skip_decide(ctl, b, K, bits, lane);
+    if (n < 0) return;
+    const int an = n == p ? a : uniform(shared_load(&amax[static_cast<long long>(b) * (K + 1) + n]));
+    bool bad = false;
+    int32_t *tok = out_tokens + static_cast<long long>(b) * (K + 1);
+    for (int i = lane; i <= K; i += kWave) {
+        const int x = i < K ? xb[i] : 0;
+        if (i < K && (x < 0 || x >= V)) bad = true;
+        tok[i] = i < n ? x : (i == n ? an : -1);
+    }
+    const bool any_bad = ballot(bad) != 0;
+    if (lane == 0) {
+        accept_len[b] = n;
+        if (status) status[b] = any_bad ? 1 : 0;
+    }
+    skip_finished(ctl, b, lane);
+}
+
+template <typename E, bool ALIGNED>
+hipError_t skip_argmax_t(const void *L, const int32_t *drafts, int B, int K, int V, const RowGeom &g,
+                         uint64_t *part_k, int32_t *amax, const SkipCtl &ctl, int32_t *accept_len,
+                         int32_t *out_tokens, int32_t *status, hipStream_t s) {
+    using T = typename E::storage;
+    const long long nwaves = static_cast<long long>(K + 1) * B * g.segs;
+    const long long blocks = (nwaves + kWavesPerBlock - 1) / kWavesPerBlock;
+    return launch_kernel(k_skip_argmax<E, ALIGNED, kGSkipVecsPerLane>, dim3(static_cast<unsigned>(blocks)),
+                         dim3(kBlock), 0, s, static_cast<const T *>(L), drafts, B, K, V, g.nvec, g.segs,
+                         part_k, amax, ctl, accept_len, out_tokens, status);
+}
+
 template <typename E, bool ALIGNED>
 hipError_t argmax_t(const void *L, long long rows, int V, const RowGeom &g, uint64_t *part_k,
                     hipStream_t s) {
@@ -275,6 +406,20 @@ hipError_t launch_argmax(const void *L, long long rows, int V, const RowGeom &g,
                          : argmax_t<BF16, false>(L, rows, V, g, part_k, s);
     return g.aligned ? argmax_t<F32, true>(L, rows, V, g, part_k, s)
                      : argmax_t<F32, false>(L, rows, V, g, part_k, s);
+}
+
+hipError_t launch_skip_match(const void *L, const int32_t *drafts, int B, int K, int V,
+                             const RowGeom &g, sv_dtype dt, uint64_t *part_k, int32_t *amax,
+                             void *ctl_base, int32_t *accept_len, int32_t *out_tokens,
+                             int32_t *status, hipStream_t s) {
+    SkipCtl ctl;
+    hipError_t e = skip_ctl_init(ctl_base, B, K, &ctl, s);
+    if (e != hipSuccess) return e;
+    trace_select(SV_K_SKIP_ARGMAX);
+#define SV_SK(E, A) skip_argmax_t<E, A>(L, drafts, B, K, V, g, part_k, amax, ctl, accept_len, out_tokens, status, s)
+    if (dt == SV_BF16) return g.aligned ? SV_SK(BF16, true) : SV_SK(BF16, false);
+    return g.aligned ? SV_SK(F32, true) : SV_SK(F32, false);
+#undef SV_SK
 }
 
 hipError_t launch_match(const uint64_t *part_k, const int32_t *drafts, int B, int K, int V,

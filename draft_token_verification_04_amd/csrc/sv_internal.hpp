@@ -27,6 +27,10 @@ namespace sv {
 #ifndef SV_SKIP_CHUNKS
 #define SV_SKIP_CHUNKS 4
 #endif
+// Greedy chains with K <= 31 take the row-skipping pass (0: always read every row).
+#ifndef SV_GREEDY_SKIP
+#define SV_GREEDY_SKIP 1
+#endif
 // 16-byte vectors per lane held in registers by one streaming wave of the
 // row-statistics and argmax passes (a wave covers 64 * this many vectors).
 constexpr int kStatsVecsPerLane = SV_STATS_VECS;
@@ -39,6 +43,17 @@ constexpr int kResidGroup = SV_RESID_GROUP;
 // so its fixed costs (the request flag, the hand-off) cover more bytes.
 constexpr int kSkipVecsPerLane = SV_SKIP_VECS;
 constexpr int kSkipChunks = SV_SKIP_CHUNKS;
+// The same shape for the greedy chain's row-skipping pass (its waves are best
+// kept short: a position's segments then finish, and its decisions land,
+// sooner, so fewer rows past each mismatch are read).
+#ifndef SV_GSKIP_VECS
+#define SV_GSKIP_VECS 8
+#endif
+#ifndef SV_GSKIP_CHUNKS
+#define SV_GSKIP_CHUNKS 2
+#endif
+constexpr int kGSkipVecsPerLane = SV_GSKIP_VECS;
+constexpr int kGSkipChunks = SV_GSKIP_CHUNKS;
 // Waves the residual-mass pass aims for (about two per SIMD).
 constexpr int kResidTargetWaves = 4096;
 // Bytes of LDS the per-request merge kernels use to stage row partials.
@@ -72,7 +87,7 @@ struct SampleWs {
     size_t part_R, part_s, L2, rp, tiles, skipctl, total;
 };
 struct GreedyWs {
-    size_t part_k, total;
+    size_t part_k, amax, skipctl, total;  // amax/skipctl: chains of K <= 31 only
 };
 SampleWs sample_ws_layout(int B, int K, const RowGeom &g);
 int resid_tiles_per_wave(int B, int ntiles);
@@ -131,6 +146,10 @@ hipError_t launch_resid_select(const void *tgt, const void *drf, int B, int K, i
                                hipStream_t s);
 hipError_t launch_argmax(const void *L, long long rows, int V, const RowGeom &g, sv_dtype dt,
                          uint64_t *part_k, hipStream_t s);
+hipError_t launch_skip_match(const void *L, const int32_t *drafts, int B, int K, int V,
+                             const RowGeom &g, sv_dtype dt, uint64_t *part_k, int32_t *amax,
+                             void *ctl_base, int32_t *accept_len, int32_t *out_tokens,
+                             int32_t *status, hipStream_t s);
 hipError_t launch_match(const uint64_t *part_k, const int32_t *drafts, int B, int K, int V,
                         const RowGeom &g, int32_t *accept_len, int32_t *out_tokens, int32_t *status,
                         hipStream_t s);

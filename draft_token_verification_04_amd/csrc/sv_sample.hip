@@ -31,6 +31,7 @@
 
 #include "sv_device.hpp"
 #include "sv_internal.hpp"
+#include "sv_skip.hpp"
 
 namespace sv {
 namespace {
@@ -550,29 +551,9 @@ __global__ __launch_bounds__(kWave) void k_resid_select(
 
 // ---- dead-row skipping (stochastic chains without lse outputs) --------------------
 //
-// One launch over every (position p, request b, row kind, segment) in
-// position-major order, so the segments of position p are handed out before
-// those of p+1.  A wave first reads its request's `finished` flag and skips its
-// segment when the request is already decided.  The last wave to finish the
-// segments of (b, p) takes the acceptance decision of position p (the same
-// fp64 merge, gather and ratio test as the full-read path) and records it in
-// the request's mask: bit p = "position p decided", bit 32+p = "draft p
-// rejected" (position K's bit means its bonus row is merged).  The request is
-// decided once the mask holds a rejection with every earlier position decided,
-// or every position 0..K decided without one; whichever decider completes that
-// prefix finishes the request (one winner by compare-and-swap) and raises the
-// flag.  Rows of positions after the first rejection are read only by waves
-// that started before the decision was known.  Nothing waits.
-
-// Largest K this path handles (decided and rejected bits share one 64-bit word).
-constexpr int kSkipMaxK = 31;
-
-struct SkipCtl {
-    unsigned *ticket;    // [B*(K+1)] segments finished per (request, position)
-    uint64_t *mask;      // [B] decided | rejected << 32
-    unsigned *won;       // [B] 1 once a decider has claimed finishing the request
-    unsigned *finished;  // [B] raised after the request's outputs are written
-};
+// The protocol is described with SkipCtl.  Here the segments of position p are
+// those of target row p and draft row p; its decision is the same fp64 merge,
+// gather and ratio test as the full-read path.
 
 __global__ __launch_bounds__(kBlock) void k_zero_words(uint32_t *__restrict__ p, long long n) {
     for (long long i = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
@@ -683,36 +664,13 @@ __global__ __launch_bounds__(kBlock) void k_skip_stats(
         if (lane == 0) shared_store(&L2b[K + 1 + p], L2q);
     }
     if (lane == 0) shared_store(&L2b[p], L2p);
-    wait_own_stores();
-    uint64_t old = 0;
-    if (lane == 0) old = __hip_atomic_fetch_or(&ctl.mask[b], bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const uint64_t m = uniform(static_cast<uint64_t>(__shfl(static_cast<long long>(old), 0, kWave))) | bits;
-    const unsigned decided = static_cast<unsigned>(m), rejected = static_cast<unsigned>(m >> 32);
-    int n = -1;
-    if (rejected) {
-        const int rj = __ffs(static_cast<int>(rejected)) - 1;
-        const unsigned below = rj == 0 ? 0u : (0xffffffffu >> (32 - rj));
-        if ((decided & below) == below) n = rj;
-    } else {
-        const unsigned all = K == 31 ? 0xffffffffu : ((1u << (K + 1)) - 1u);
-        if ((decided & all) == all) n = K;
-    }
+    const int n = skip_decide(ctl, b, K, bits, lane);
     if (n < 0) return;
-    unsigned prev = 1;
-    if (lane == 0) {
-        unsigned expect = 0;
-        prev = __hip_atomic_compare_exchange_strong(&ctl.won[b], &expect, 1u, __ATOMIC_RELAXED,
-                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                   ? 0u
-                   : 1u;
-    }
-    if (uniform(static_cast<unsigned>(__shfl(static_cast<int>(prev), 0, kWave))) != 0) return;
     const double L2pn = shared_load(&L2b[n]);
     const double L2qn = n < K ? shared_load(&L2b[K + 1 + n]) : 0.0;
     skip_finish(drafts + static_cast<long long>(b) * K, us, b, K, V, n, n < K ? 1 : 0, L2pn, L2qn,
                 accept_len, out_tokens, status, rp, lane);
-    wait_own_stores();
-    if (lane == 0) shared_store(&ctl.finished[b], 1u);
+    skip_finished(ctl, b, lane);
 }
 
 template <typename E, bool ALIGNED>
@@ -757,7 +715,21 @@ hipError_t launch_rowstats(const void *tgt, const void *drf, long long rows_t, l
 bool skip_supported(int K) { return K <= kSkipMaxK; }
 
 size_t skip_ctl_bytes(int B, int K) {
-    return sizeof(unsigned) * static_cast<size_t>(B) * (K + 1) + sizeof(uint64_t) * B + 2 * sizeof(unsigned) * B;
+    return sizeof(uint64_t) * B + sizeof(unsigned) * static_cast<size_t>(B) * (K + 1) + 2 * sizeof(unsigned) * B;
+}
+
+hipError_t skip_ctl_init(void *base, int B, int K, SkipCtl *ctl, hipStream_t s) {
+    char *q = static_cast<char *>(base);
+    ctl->mask = reinterpret_cast<uint64_t *>(q);
+    ctl->ticket = reinterpret_cast<unsigned *>(ctl->mask + B);
+    ctl->won = ctl->ticket + static_cast<size_t>(B) * (K + 1);
+    ctl->finished = ctl->won + B;
+    const long long words = static_cast<long long>(skip_ctl_bytes(B, K) / sizeof(uint32_t));
+    const long long zb = std::max<long long>(1, std::min<long long>(1024, (words + kBlock - 1) / kBlock));
+    trace_select(-1);  // the clearing launch is not traced
+    hipLaunchKernelGGL(k_zero_words, dim3(static_cast<unsigned>(zb)), dim3(kBlock), 0, s,
+                       reinterpret_cast<uint32_t *>(base), words);
+    return hipGetLastError();
 }
 
 hipError_t launch_skip(const void *tgt, const void *drf, const int32_t *drafts, const float *ua,
@@ -766,17 +738,7 @@ hipError_t launch_skip(const void *tgt, const void *drf, const int32_t *drafts, 
                        int32_t *accept_len, int32_t *out_tokens, int32_t *status, ResidParam *rp,
                        hipStream_t s) {
     SkipCtl ctl;
-    char *q = static_cast<char *>(ctl_base);
-    ctl.mask = reinterpret_cast<uint64_t *>(q);
-    ctl.ticket = reinterpret_cast<unsigned *>(ctl.mask + B);
-    ctl.won = ctl.ticket + static_cast<size_t>(B) * (K + 1);
-    ctl.finished = ctl.won + B;
-    const long long words = static_cast<long long>(skip_ctl_bytes(B, K) / sizeof(uint32_t));
-    const long long zb = std::max<long long>(1, std::min<long long>(1024, (words + kBlock - 1) / kBlock));
-    trace_select(-1);
-    hipLaunchKernelGGL(k_zero_words, dim3(static_cast<unsigned>(zb)), dim3(kBlock), 0, s,
-                       reinterpret_cast<uint32_t *>(ctl_base), words);
-    hipError_t e = hipGetLastError();
+    hipError_t e = skip_ctl_init(ctl_base, B, K, &ctl, s);
     if (e != hipSuccess) return e;
     trace_select(SV_K_SKIP_STATS);
 #define SV_SK(E, A) skip_stats_t<E, A>(tgt, drf, drafts, ua, us, B, K, V, g, sc, part_R, part_s, L2, ctl, accept_len, out_tokens, status, rp, s)

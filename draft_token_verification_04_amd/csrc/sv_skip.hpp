@@ -1,0 +1,78 @@
+// sv_skip.hpp -- control words and the decision protocol shared by the
+// row-skipping passes of the stochastic and greedy chains.
+//
+// A chain's outputs never depend on the rows after its first rejected (or
+// mismatched) draft: every draft after it is discarded, and the one drawn token
+// comes from the rejected position's row.  A row-skipping pass is one launch
+// over every (position p, request b, segment) in position-major order, so the
+// segments of position p are handed out before those of p+1.  A wave first
+// reads its request's `finished` flag and skips its segment when the request
+// is already decided.  The last wave to finish the segments of (b, p), found by
+// a per-(b, p) ticket, takes the decision of position p and records it in the
+// request's mask: bit p = "position p decided", bit 32+p = "draft p rejected"
+// (position K's bit means its bonus row is ready).  The request is decided once
+// the mask holds a rejection with every earlier position decided, or every
+// position 0..K decided without one; whichever decider completes that prefix
+// finishes the request (one winner by compare-and-swap) and raises the flag.
+// Rows of positions after the first rejection are read only by waves that
+// started before the decision was known.  Nothing waits.
+#pragma once
+
+#include "sv_device.hpp"
+#include "sv_internal.hpp"
+
+namespace sv {
+
+// Largest K the row-skipping passes handle (decided and rejected bits share one
+// 64-bit word per request).
+constexpr int kSkipMaxK = 31;
+
+struct SkipCtl {
+    unsigned *ticket;    // [B*(K+1)] segments finished per (request, position)
+    uint64_t *mask;      // [B] decided | rejected << 32
+    unsigned *won;       // [B] 1 once a decider has claimed finishing the request
+    unsigned *finished;  // [B] raised after the request's outputs are written
+};
+
+// Carves the control words of a B x K chain out of `base` (skip_ctl_bytes
+// bytes, 8-byte aligned) and enqueues the launch that zeroes them.
+hipError_t skip_ctl_init(void *base, int B, int K, SkipCtl *ctl, hipStream_t s);
+
+// Records position p's decision `bits` (1 << p, plus 1 << (32 + p) for a
+// rejection) in request b's mask, once this wave's shared stores are complete.
+// Returns the request's accepted length n when this wave completes the decided
+// prefix and wins the right to finish the request; -1 otherwise.  Uniform.
+__device__ __forceinline__ int skip_decide(const SkipCtl &ctl, int b, int K, uint64_t bits, int lane) {
+    wait_own_stores();
+    uint64_t old = 0;
+    if (lane == 0) old = __hip_atomic_fetch_or(&ctl.mask[b], bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t m = uniform(static_cast<uint64_t>(__shfl(static_cast<long long>(old), 0, kWave))) | bits;
+    const unsigned decided = static_cast<unsigned>(m), rejected = static_cast<unsigned>(m >> 32);
+    int n = -1;
+    if (rejected) {
+        const int rj = __ffs(static_cast<int>(rejected)) - 1;
+        const unsigned below = rj == 0 ? 0u : (0xffffffffu >> (32 - rj));
+        if ((decided & below) == below) n = rj;
+    } else {
+        const unsigned all = K == 31 ? 0xffffffffu : ((1u << (K + 1)) - 1u);
+        if ((decided & all) == all) n = K;
+    }
+    if (n < 0) return -1;
+    unsigned lost = 1;
+    if (lane == 0) {
+        unsigned expect = 0;
+        lost = __hip_atomic_compare_exchange_strong(&ctl.won[b], &expect, 1u, __ATOMIC_RELAXED,
+                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                   ? 0u
+                   : 1u;
+    }
+    return uniform(static_cast<unsigned>(__shfl(static_cast<int>(lost), 0, kWave))) != 0 ? -1 : n;
+}
+
+// Raises request b's flag once this wave's output stores are complete.
+__device__ __forceinline__ void skip_finished(const SkipCtl &ctl, int b, int lane) {
+    wait_own_stores();
+    if (lane == 0) shared_store(&ctl.finished[b], 1u);
+}
+
+}  // namespace sv

@@ -126,6 +126,10 @@ sv_status spec_verify_sample(const void *target_logits, const void *draft_logits
  *                       else K.
  *   out_tokens [B][K+1] drafts 0..n_b-1, argmax(row n_b), then -1.
  *   req_status [B]      optional: 0, or 1 if a draft id is outside [0, V).
+ *
+ * Rows read: for K <= 31 the rows of positions after each request's first
+ * mismatch are skipped, except by segments already in flight when that
+ * mismatch is decided; for larger K every row is read.
  */
 sv_status spec_verify_greedy(const void *target_logits, const int32_t *draft_tokens, int B, int K,
                              int V, sv_dtype dt, int32_t *accept_len, int32_t *out_tokens,
@@ -190,7 +194,8 @@ typedef enum {
     SV_K_MATCH = 5,        /* greedy chain acceptance */
     SV_K_TREE = 6,         /* greedy tree walk */
     SV_K_SKIP_STATS = 7,   /* row statistics + acceptance, skipping rows after a rejection */
-    SV_K_COUNT = 8
+    SV_K_SKIP_ARGMAX = 8,  /* row argmax + greedy chain acceptance, skipping rows after a mismatch */
+    SV_K_COUNT = 9
 } sv_kernel_id;
 
 sv_status sv_trace_begin(int capacity, unsigned kernel_mask);

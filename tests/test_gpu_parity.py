@@ -70,8 +70,10 @@ def test_sample_workloads_full_size(c, lse):
           f"mean accept {g['accept_len'].mean():.3f}")
 
 
+# K <= 31 takes the row-skipping pass, larger K the full read (argmax + match).
 GREEDY_GRID = [(1, 0, 8, "f32"), (5, 3, 1000, "bf16"), (6, 7, 1001, "bf16"), (33, 7, 4100, "f32"),
-               (3, 7, 151936, "bf16"), (64, 70, 333, "bf16"), (2, 1, 1, "f32")]
+               (3, 7, 151936, "bf16"), (64, 70, 333, "bf16"), (2, 1, 1, "f32"),
+               (40, 31, 2500, "bf16"), (40, 32, 2500, "bf16"), (7, 31, 20001, "f32")]
 
 
 @pytest.mark.parametrize("case", GREEDY_GRID, ids=lambda c: "B{}K{}V{}{}".format(*c))
@@ -98,6 +100,18 @@ def test_greedy_ties_and_signed_zeros():
         LL = L if dt == "f32" else workloads.to_bf16_bits(L)
         w = workloads.Workload(mode="greedy", B=B, K=K, V=V, dtype=dt, target=LL, draft_tokens=x)
         check_exact(gpu_greedy(w), oracle.verify_greedy(LL, x), ("accept_len", "tokens", "status"))
+
+
+@pytest.mark.parametrize("p_match", [1.0, 0.0, 0.5])
+def test_greedy_acceptance_extremes(p_match):
+    # every draft accepted (every row decides), none (only row 0 decides), mixed
+    note(f"greedy p_match={p_match}")
+    w = workloads.make_greedy(96, 7, 30011, "bf16", p_match=p_match, seed=11)
+    o = oracle.verify_greedy(w.target, w.draft_tokens)
+    g = gpu_greedy(w)
+    check_exact(g, o, ("accept_len", "tokens", "status"))
+    if p_match == 1.0:
+        assert (o["accept_len"] == 7).all()
 
 
 @pytest.mark.parametrize("B", [512, 256])
@@ -284,3 +298,13 @@ def test_trace_records_each_kernel():
     gpu_sample(w, lse=False)
     recs = sv.trace_end()
     assert [r[0] for r in recs] == ["skip_stats", "resid_mass", "resid_select"]
+    wg = workloads.make_greedy(8, 3, 5000, "bf16", seed=6)
+    sv.trace_begin(64)
+    gpu_greedy(wg)
+    recs = sv.trace_end()
+    assert [r[0] for r in recs] == ["skip_argmax"]
+    wg = workloads.make_greedy(4, 32, 5000, "bf16", seed=7)
+    sv.trace_begin(64)
+    gpu_greedy(wg)
+    recs = sv.trace_end()
+    assert [r[0] for r in recs] == ["argmax", "match"]
