@@ -345,6 +345,47 @@ def main():
                                  "bytes_read": bytes_mode[name],
                                  "gbps": round(bytes_mode[name] / (ms * 1e-3) / 1e9, 1)}
 
+    # beyond the verification step: committing the tree's accepted paths in a
+    # KV cache shaped like a 36-layer target (K and V, 8 heads x 128 bf16 = 2 KB rows)
+    extras = {}
+    if "tree" in active:
+        G, S_slots = 72, 64
+        kv = torch.randn((G, w5.B, S_slots, 1024), dtype=torch.bfloat16, device=dev)
+        i32 = dict(dtype=torch.int32, device=dev)
+        tb = torch.full((w5.B,), 20, **i32)
+        cb = tb + 1
+        st = torch.empty(w5.B, **i32)
+        commit_args = (ctypes.c_void_p(kv.data_ptr()), ctypes.c_void_p(kv.data_ptr()), G, w5.B, S_slots,
+                       2048, ctypes.c_void_p(tb.data_ptr()), ctypes.c_void_p(cb.data_ptr()),
+                       ctypes.c_void_p(calls.t_n.data_ptr()), ctypes.c_void_p(calls.t_path.data_ptr()),
+                       w5.N, ctypes.c_void_p(st.data_ptr()), calls.stream)
+
+        def commit():
+            rc = calls.lib.spec_commit_tree_kv(*commit_args)
+            if rc:
+                raise RuntimeError(f"spec_commit_tree_kv failed: {rc}")
+
+        calls.tree()
+        torch.cuda.synchronize()
+        d5 = calls.t_n.cpu().numpy()
+        moved = 2 * G * int(d5.sum()) * 2048  # each committed row read once and written once
+        ms = per_call(commit, reps)
+        sv.trace_begin(64, kernels=("commit",))
+        for _ in range(20):
+            commit()
+        torch.cuda.synchronize()
+        kms = statistics.mean(t for _, t in sv.trace_end(64))
+        assert int((st.cpu() != 0).sum()) == 0
+        extras["commit_tree_kv"] = {
+            "workload": "accepted paths of the tree workload (B=64 N=33) in a 72 x 64 x 64-slot cache "
+                        "of 2 KB rows, in place after the root",
+            "rows_committed": int(d5.sum()) * G, "bytes_moved": moved, "call_ms": round(ms, 5),
+            "kernel_ms": round(kms, 5),
+            "roofline": {"bound": "hbm", "kernel": "commit", "achieved": round(moved / (kms * 1e-3) / 1e9, 1),
+                         "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": round(moved / (kms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}}
+        del kv
+
     cpu = None
     if not args.no_cpu_baseline:
         threads = args.cpu_threads or max(1, min(16, os.cpu_count() or 1))
@@ -381,6 +422,7 @@ def main():
         "modes": modes,
         "kernel_ms": {k: round(v, 5) for k, v in kmean.items()},
         "calls_alone": calls_alone,
+        "extras": extras or None,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

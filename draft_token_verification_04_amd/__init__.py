@@ -27,10 +27,11 @@ SV_OK, SV_ERR_INVALID_ARG, SV_ERR_UNSUPPORTED, SV_ERR_WORKSPACE, SV_ERR_HIP = ra
 SV_F32, SV_BF16 = 0, 1
 SV_MAX_TREE_NODES = 2048
 KERNELS = ("rowstats", "accept", "resid_mass", "resid_select", "argmax", "match", "tree",
-           "skip_stats", "skip_argmax")
+           "skip_stats", "skip_argmax", "commit")
 
 EXPORTS = ("sv_sample_workspace_bytes", "sv_greedy_workspace_bytes", "spec_verify_sample",
-           "spec_verify_greedy", "spec_verify_tree", "sv_status_string", "sv_version",
+           "spec_verify_greedy", "spec_verify_tree", "spec_commit_tree_kv", "sv_status_string",
+           "sv_version",
            "sv_trace_begin", "sv_trace_end", "sv_kernel_name")
 
 
@@ -66,6 +67,8 @@ def load_library(path: str = LIB_PATH):
     lib.spec_verify_greedy.restype = I
     lib.spec_verify_tree.argtypes = [P, P, P, I, I, I, I, P, P, P, P, P, Z, P]
     lib.spec_verify_tree.restype = I
+    lib.spec_commit_tree_kv.argtypes = [P, P, I, I, I, I, P, P, P, P, I, P, P]
+    lib.spec_commit_tree_kv.restype = I
     lib.sv_status_string.argtypes = [I]
     lib.sv_status_string.restype = ctypes.c_char_p
     lib.sv_version.argtypes = []
@@ -263,6 +266,45 @@ def spec_verify_tree(target, node_tokens, parents, *, status=True, workspace=Non
     if rc != SV_OK:
         raise SpecVerifyError(rc, "spec_verify_tree")
     return out
+
+
+def spec_commit_tree_kv(kv, tree_base, commit_base, accept_len, path, *, out=None, status=True,
+                        stream=None):
+    """Move the KV rows of each request's accepted tree path into consecutive
+    slots.  kv: [G, B, S, ...] GPU tensor (any dtype; the trailing dimensions
+    of one slot form a row of a multiple of 16 bytes); tree_base, commit_base,
+    accept_len [B] and path [B, N] int32 (accept_len and path as returned by
+    spec_verify_tree).  In place when ``out`` is None, else into ``out`` (same
+    shape and dtype as kv).  Returns the per-request status [B] (or None)."""
+    torch = _torch()
+    lib = load_library()
+    if kv is None or kv.dim() < 3:
+        raise ValueError("kv must be [G, B, S, ...]")
+    _check(kv, "kv")
+    dev = kv.device
+    G, B, S = kv.shape[:3]
+    row_bytes = kv[0, 0, 0].numel() * kv.element_size() if kv.numel() else 0
+    dst = kv if out is None else out
+    if out is not None:
+        _check(out, "out", kv.dim(), kv.dtype, dev)
+        if tuple(out.shape) != tuple(kv.shape):
+            raise ValueError("out must have the shape of kv")
+    for name, t in (("tree_base", tree_base), ("commit_base", commit_base), ("accept_len", accept_len)):
+        _check(t, name, 1, torch.int32, dev)
+        if t.shape[0] != B:
+            raise ValueError(f"{name} must be [B]")
+    _check(path, "path", 2, torch.int32, dev)
+    if path.shape[0] != B:
+        raise ValueError("path must be [B, N]")
+    N = path.shape[1]
+    st = torch.empty(B, dtype=torch.int32, device=dev) if status else None
+    with torch.cuda.device(dev):
+        rc = lib.spec_commit_tree_kv(_ptr(kv), _ptr(dst), G, B, S, row_bytes, _ptr(tree_base),
+                                     _ptr(commit_base), _ptr(accept_len), _ptr(path), N, _ptr(st),
+                                     _stream(torch, dev, stream))
+    if rc != SV_OK:
+        raise SpecVerifyError(rc, "spec_commit_tree_kv")
+    return st
 
 
 # ---- per-kernel timing -----------------------------------------------------------

@@ -294,6 +294,29 @@ sv_status spec_verify_tree(const void *target_logits, const int32_t *node_tokens
     return e == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 
+sv_status spec_commit_tree_kv(const void *src_kv, void *dst_kv, int G, int B, int S, int row_bytes,
+                              const int32_t *tree_base, const int32_t *commit_base,
+                              const int32_t *accept_len, const int32_t *path_nodes, int N,
+                              int32_t *req_status, void *stream) {
+    if (G < 1 || B < 0 || S < 1 || N < 1 || row_bytes < 16 || row_bytes % 16 != 0)
+        return SV_ERR_INVALID_ARG;
+    if (N > SV_MAX_TREE_NODES || static_cast<long long>(G) * B > 0x7fffffffLL ||
+        static_cast<long long>(N) * (row_bytes / 16) > 0x7fffffffLL)
+        return SV_ERR_UNSUPPORTED;
+    const double bytes = static_cast<double>(G) * B * static_cast<double>(S) * row_bytes;
+    if (bytes >= 9.0e18) return SV_ERR_UNSUPPORTED;
+    if (B == 0) return SV_OK;
+    if (!src_kv || !dst_kv || !tree_base || !commit_base || !accept_len || !path_nodes)
+        return SV_ERR_INVALID_ARG;
+    if (!aligned16(src_kv) || !aligned16(dst_kv)) return SV_ERR_INVALID_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const hipError_t e = traced(SV_K_COMMIT, s, [&] {
+        return launch_commit(src_kv, dst_kv, G, B, S, row_bytes, tree_base, commit_base, accept_len,
+                             path_nodes, N, req_status, s);
+    });
+    return e == hipSuccess ? SV_OK : SV_ERR_HIP;
+}
+
 const char *sv_status_string(sv_status st) {
     switch (st) {
         case SV_OK: return "ok";
@@ -310,7 +333,7 @@ const char *sv_version(void) { return "specverify 0.1.0 (gfx950)"; }
 const char *sv_kernel_name(int k) {
     static const char *names[SV_K_COUNT] = {"rowstats", "accept", "resid_mass", "resid_select",
                                             "argmax", "match", "tree", "skip_stats",
-                                            "skip_argmax"};
+                                            "skip_argmax", "commit"};
     return (k >= 0 && k < SV_K_COUNT) ? names[k] : "unknown";
 }
 

@@ -163,6 +163,39 @@ sv_status spec_verify_tree(const void *target_logits, const int32_t *node_tokens
                            int32_t *req_status, void *workspace, size_t workspace_bytes,
                            void *stream);
 
+/*
+ * Commit of a verified draft tree's accepted path in the target's KV cache
+ * (AdaPLD page, Algorithm 1: the accepted tokens are appended and the context
+ * updated; section 3.3: the whole tree is verified in one target pass, which
+ * leaves one KV row per tree node).  Moves the rows of the accepted nodes,
+ * depth 1 first, into consecutive slots.
+ *
+ *   src_kv, dst_kv  [G][B][S][row_bytes] bytes on the device, 16-byte
+ *                   aligned, row_bytes a positive multiple of 16.  G counts
+ *                   independent row groups (e.g. layers x {K, V}).  dst_kv
+ *                   may be src_kv (in place); otherwise the two must not
+ *                   overlap.
+ *   tree_base [B]   slot of tree node 0 of each request.
+ *   commit_base [B] slot that receives the first accepted node.
+ *   accept_len [B], path_nodes [B][N]  as written by spec_verify_tree.
+ *   req_status [B]  optional: 0 committed (accept_len 0 commits nothing);
+ *                   1 a slot outside [0, S); 2 accept_len outside [0, N-1],
+ *                   or a path node outside [1, N) or not strictly increasing;
+ *                   3 in place with commit_base in [tree_base + 2,
+ *                   tree_base + N), where a write could land on a source row
+ *                   still to be read.  A request with a non-zero status is
+ *                   left untouched.
+ *
+ * For every group g, request b and k < accept_len[b]:
+ *   dst[g][b][commit_base[b] + k] = src[g][b][tree_base[b] + path_nodes[b][k]]
+ * with every source row read as it was on entry.  The usual in-place call has
+ * commit_base = tree_base + 1 (the root's row stays where it is).
+ */
+sv_status spec_commit_tree_kv(const void *src_kv, void *dst_kv, int G, int B, int S, int row_bytes,
+                              const int32_t *tree_base, const int32_t *commit_base,
+                              const int32_t *accept_len, const int32_t *path_nodes, int N,
+                              int32_t *req_status, void *stream);
+
 /* Human-readable name of a status code (static storage). */
 const char *sv_status_string(sv_status s);
 
@@ -195,7 +228,8 @@ typedef enum {
     SV_K_TREE = 6,         /* greedy tree walk */
     SV_K_SKIP_STATS = 7,   /* row statistics + acceptance, skipping rows after a rejection */
     SV_K_SKIP_ARGMAX = 8,  /* row argmax + greedy chain acceptance, skipping rows after a mismatch */
-    SV_K_COUNT = 9
+    SV_K_COMMIT = 9,       /* KV rows of accepted tree paths moved to consecutive slots */
+    SV_K_COUNT = 10
 } sv_kernel_id;
 
 sv_status sv_trace_begin(int capacity, unsigned kernel_mask);

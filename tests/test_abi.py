@@ -127,3 +127,26 @@ def test_binding_refuses_without_gpu():
         pytest.skip("a GPU is visible")
     with pytest.raises(RuntimeError):
         sv.spec_verify_greedy(torch.zeros(1, 2, 8), torch.zeros(1, 1, dtype=torch.int32))
+
+
+def _commit(lib, **kw):
+    a = dict(src=FAKE, dst=FAKE, G=2, B=3, S=64, rb=2048, tb=FAKE, cb=FAKE, d=FAKE, p=FAKE, N=33,
+             st=None, s=None)
+    a.update(kw)
+    return lib.spec_commit_tree_kv(a["src"], a["dst"], a["G"], a["B"], a["S"], a["rb"], a["tb"], a["cb"],
+                                   a["d"], a["p"], a["N"], a["st"], a["s"])
+
+
+def test_commit_argument_checks(lib):
+    assert _commit(lib, G=0) == sv.SV_ERR_INVALID_ARG
+    assert _commit(lib, B=-1) == sv.SV_ERR_INVALID_ARG
+    assert _commit(lib, S=0) == sv.SV_ERR_INVALID_ARG
+    assert _commit(lib, N=0) == sv.SV_ERR_INVALID_ARG
+    assert _commit(lib, rb=8) == sv.SV_ERR_INVALID_ARG
+    assert _commit(lib, rb=24) == sv.SV_ERR_INVALID_ARG
+    assert _commit(lib, N=sv.SV_MAX_TREE_NODES + 1) == sv.SV_ERR_UNSUPPORTED
+    assert _commit(lib, G=1 << 20, B=1 << 12) == sv.SV_ERR_UNSUPPORTED
+    assert _commit(lib, src=None) == sv.SV_ERR_INVALID_ARG
+    assert _commit(lib, p=None) == sv.SV_ERR_INVALID_ARG
+    assert _commit(lib, dst=ctypes.c_void_p((1 << 20) + 8)) == sv.SV_ERR_INVALID_ARG
+    assert _commit(lib, B=0, src=None, dst=None) == sv.SV_OK
