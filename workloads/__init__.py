@@ -74,11 +74,13 @@ class Workload:
     u_sample: np.ndarray = None     # [B, K+1] float32
     node_tokens: np.ndarray = None  # [B, N] int32
     parents: np.ndarray = None      # [B, N] int32
+    hidden: np.ndarray = None       # [B, K+1 or N, D] uint16 (bf16 bits): LM-head workloads
+    lm_head: np.ndarray = None      # [V, D] uint16 (bf16 bits)
     meta: dict = field(default_factory=dict)
 
     def rows(self) -> int:
         """Target rows verified per call: B*(K+1) for chains, B*N for trees."""
-        return self.B * (self.N if self.mode == "tree" else self.K + 1)
+        return self.B * (self.N if self.mode.startswith("tree") else self.K + 1)
 
 
 CONFIGS = {
@@ -285,3 +287,80 @@ def make_config(c: int, seed=None, B=None) -> Workload:
     if c == 5:
         return make_tree(cfg["B"], cfg["V"], "bf16", seed=ss)
     raise ValueError(f"unknown workload {c}")
+
+
+# ---- LM-head workloads: hidden states and a vocabulary projection ----------------
+#
+# The fused LM-head path takes the target's final hidden states H [rows, D] and
+# the projection W [V, D] instead of logits.  Shapes follow Qwen3-8B (D = 4096,
+# V = 151936).  Two value recipes:
+#   exact:   H entries k/8 and W entries k/64 with k uniform in [-8, 8].  Every
+#            product is a multiple of 2^-9 and every partial sum of D <= 8192
+#            products is below 2^10 in magnitude, so an fp32 accumulation in
+#            any order is exact; logits have std ~ 3.2 and exact ties occur.
+#   general: H ~ N(0, 1), W ~ N(0, (3 / sqrt(D))^2), rounded to bf16; logits have
+#            std ~ 3 and fp32 accumulation rounds.
+# Drafts (chains) and node tokens (trees) equal the argmax of the row they are
+# checked against with probability p_match, else a uniform id; p_match=None
+# draws them all uniformly (no logits are formed).
+
+LMHEAD_SHAPE = dict(B=256, K=7, D=4096, V=VOCAB_QWEN3)
+
+
+def _lmhead_values(seed, rows: int, D: int, V: int, exact: bool):
+    sh, sw = seed.spawn(2)
+    rh, rw = np.random.default_rng(sh), np.random.default_rng(sw)
+    if exact:
+        H = rh.integers(-8, 9, size=(rows, D)).astype(np.float32) / 8
+        W = rw.integers(-8, 9, size=(V, D)).astype(np.float32) / 64
+    else:
+        H = rh.standard_normal((rows, D), dtype=np.float32)
+        W = rw.standard_normal((V, D), dtype=np.float32) * np.float32(3.0 / np.sqrt(D))
+    return to_bf16_bits(H), to_bf16_bits(W)
+
+
+def _lmhead_argmax(Hb: np.ndarray, Wb: np.ndarray, exact: bool) -> np.ndarray:
+    """Row argmax of H W^T, for planting matching drafts (blocks of 64 rows)."""
+    dt = np.float32 if exact else np.float64
+    W = bf16_bits_to_f32(Wb).astype(dt)
+    out = np.empty(Hb.shape[0], dtype=np.int64)
+    for r0 in range(0, Hb.shape[0], BLOCK_ROWS):
+        h = bf16_bits_to_f32(Hb[r0:r0 + BLOCK_ROWS]).astype(dt)
+        out[r0:r0 + BLOCK_ROWS] = np.argmax(h @ W.T, axis=1)
+    return out
+
+
+def make_greedy_lmhead(B, K, D, V, exact=True, p_match=0.8, seed=0) -> Workload:
+    """Greedy-chain inputs for the fused LM-head path: hidden [B,K+1,D], lm_head [V,D]."""
+    ss = seed if isinstance(seed, np.random.SeedSequence) else np.random.SeedSequence(seed)
+    st = ss.spawn(6)
+    Hb, Wb = _lmhead_values(st[_S_TARGET], B * (K + 1), D, V, exact)
+    rng = np.random.default_rng(st[_S_DRAFTS])
+    x = rng.integers(0, V, size=(B, K)).astype(np.int32)
+    if p_match is not None and K > 0:
+        am = _lmhead_argmax(Hb, Wb, exact).reshape(B, K + 1)
+        hit = rng.random((B, K)) < p_match
+        x = np.where(hit, am[:, :K], x).astype(np.int32)
+    return Workload(mode="greedy_lmhead", B=B, K=K, V=V, dtype="bf16", draft_tokens=x,
+                    hidden=Hb.reshape(B, K + 1, D), lm_head=Wb,
+                    meta=dict(D=D, exact=exact, p_match=p_match))
+
+
+def make_tree_lmhead(B, D, V, exact=True, p_match=0.7, n_main=8, n_branch=12, max_extra=3,
+                     seed=0) -> Workload:
+    """Greedy-tree inputs for the fused LM-head path: hidden [B,N,D], lm_head [V,D]."""
+    ss = seed if isinstance(seed, np.random.SeedSequence) else np.random.SeedSequence(seed)
+    st = ss.spawn(6)
+    N = 1 + n_main + 2 * n_branch
+    rng = np.random.default_rng(st[_S_TREE])
+    parents = np.stack([adapld_parents(int(rng.integers(0, max_extra + 1)), n_main, n_branch, rng)
+                        for _ in range(B)])
+    Hb, Wb = _lmhead_values(st[_S_TARGET], B * N, D, V, exact)
+    tok = rng.integers(0, V, size=(B, N)).astype(np.int32)
+    if p_match is not None:
+        am = _lmhead_argmax(Hb, Wb, exact).reshape(B, N)
+        hit = rng.random((B, N)) < p_match
+        tok = np.where(hit, np.take_along_axis(am, np.maximum(parents, 0), 1), tok).astype(np.int32)
+    return Workload(mode="tree_lmhead", B=B, N=N, V=V, dtype="bf16", node_tokens=tok,
+                    parents=parents.astype(np.int32), hidden=Hb.reshape(B, N, D), lm_head=Wb,
+                    meta=dict(D=D, exact=exact, p_match=p_match))
