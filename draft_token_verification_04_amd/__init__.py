@@ -27,11 +27,12 @@ SV_OK, SV_ERR_INVALID_ARG, SV_ERR_UNSUPPORTED, SV_ERR_WORKSPACE, SV_ERR_HIP = ra
 SV_F32, SV_BF16 = 0, 1
 SV_MAX_TREE_NODES = 2048
 KERNELS = ("rowstats", "accept", "resid_mass", "resid_select", "argmax", "match", "tree",
-           "skip_stats", "skip_argmax", "commit")
+           "skip_stats", "skip_argmax", "commit", "lmhead")
 
 EXPORTS = ("sv_sample_workspace_bytes", "sv_greedy_workspace_bytes", "spec_verify_sample",
            "spec_verify_greedy", "spec_verify_tree", "spec_commit_tree_kv", "sv_status_string",
-           "sv_version",
+           "sv_version", "sv_lmhead_workspace_bytes", "spec_verify_greedy_lmhead",
+           "spec_verify_tree_lmhead",
            "sv_trace_begin", "sv_trace_end", "sv_kernel_name")
 
 
@@ -69,6 +70,12 @@ def load_library(path: str = LIB_PATH):
     lib.spec_verify_tree.restype = I
     lib.spec_commit_tree_kv.argtypes = [P, P, I, I, I, I, P, P, P, P, I, P, P]
     lib.spec_commit_tree_kv.restype = I
+    lib.sv_lmhead_workspace_bytes.argtypes = [I, I]
+    lib.sv_lmhead_workspace_bytes.restype = Z
+    lib.spec_verify_greedy_lmhead.argtypes = [P, P, P, I, I, I, I, P, P, P, P, Z, P]
+    lib.spec_verify_greedy_lmhead.restype = I
+    lib.spec_verify_tree_lmhead.argtypes = [P, P, P, P, I, I, I, I, P, P, P, P, P, Z, P]
+    lib.spec_verify_tree_lmhead.restype = I
     lib.sv_status_string.argtypes = [I]
     lib.sv_status_string.restype = ctypes.c_char_p
     lib.sv_version.argtypes = []
@@ -265,6 +272,75 @@ def spec_verify_tree(target, node_tokens, parents, *, status=True, workspace=Non
             ws.numel() * ws.element_size(), _stream(torch, dev, stream))
     if rc != SV_OK:
         raise SpecVerifyError(rc, "spec_verify_tree")
+    return out
+
+
+def _lmhead_operands(torch, hidden, lm_head, lead):
+    _check(hidden, "hidden", len(lead) + 1, torch.bfloat16)
+    dev = hidden.device
+    _check(lm_head, "lm_head", 2, torch.bfloat16, dev)
+    D = hidden.shape[-1]
+    V = lm_head.shape[0]
+    if lm_head.shape[1] != D:
+        raise ValueError(f"lm_head must be [V, {D}], got {tuple(lm_head.shape)}")
+    return dev, D, V
+
+
+def spec_verify_greedy_lmhead(hidden, lm_head, draft_tokens, *, status=True, workspace=None,
+                              stream=None):
+    """Greedy chain verification on the logits hidden @ lm_head.T, which are
+    never materialised: hidden [B, K+1, D] bf16, lm_head [V, D] bf16,
+    draft_tokens [B, K] int32.  Returns ``accept_len`` [B], ``tokens`` [B, K+1]
+    and ``status`` [B]."""
+    torch = _torch()
+    lib = load_library()
+    dev, D, V = _lmhead_operands(torch, hidden, lm_head, (0, 0))
+    B, R = hidden.shape[:2]
+    K = R - 1
+    _check(draft_tokens, "draft_tokens", 2, torch.int32, dev)
+    if tuple(draft_tokens.shape) != (B, K):
+        raise ValueError(f"draft_tokens must be [{B}, {K}]")
+    out = dict(accept_len=torch.empty(B, dtype=torch.int32, device=dev),
+               tokens=torch.empty((B, K + 1), dtype=torch.int32, device=dev))
+    if status:
+        out["status"] = torch.empty(B, dtype=torch.int32, device=dev)
+    ws = _workspace(torch, lib.sv_lmhead_workspace_bytes(B * R, V), dev, workspace)
+    with torch.cuda.device(dev):
+        rc = lib.spec_verify_greedy_lmhead(
+            _ptr(hidden), _ptr(lm_head), _ptr(draft_tokens) if K else None, B, K, D, V,
+            _ptr(out["accept_len"]), _ptr(out["tokens"]), _ptr(out.get("status")), _ptr(ws),
+            ws.numel() * ws.element_size(), _stream(torch, dev, stream))
+    if rc != SV_OK:
+        raise SpecVerifyError(rc, "spec_verify_greedy_lmhead")
+    return out
+
+
+def spec_verify_tree_lmhead(hidden, lm_head, node_tokens, parents, *, status=True, workspace=None,
+                            stream=None):
+    """Greedy tree verification on the logits hidden @ lm_head.T (never
+    materialised): hidden [B, N, D] bf16, lm_head [V, D] bf16, node_tokens and
+    parents [B, N] int32.  Returns ``accept_len``, ``path``, ``tokens``, ``status``."""
+    torch = _torch()
+    lib = load_library()
+    dev, D, V = _lmhead_operands(torch, hidden, lm_head, (0, 0))
+    B, N = hidden.shape[:2]
+    _check(node_tokens, "node_tokens", 2, torch.int32, dev)
+    _check(parents, "parents", 2, torch.int32, dev)
+    if tuple(node_tokens.shape) != (B, N) or tuple(parents.shape) != (B, N):
+        raise ValueError("node_tokens and parents must be [B, N]")
+    out = dict(accept_len=torch.empty(B, dtype=torch.int32, device=dev),
+               path=torch.empty((B, N), dtype=torch.int32, device=dev),
+               tokens=torch.empty((B, N), dtype=torch.int32, device=dev))
+    if status:
+        out["status"] = torch.empty(B, dtype=torch.int32, device=dev)
+    ws = _workspace(torch, lib.sv_lmhead_workspace_bytes(B * N, V), dev, workspace)
+    with torch.cuda.device(dev):
+        rc = lib.spec_verify_tree_lmhead(
+            _ptr(hidden), _ptr(lm_head), _ptr(node_tokens), _ptr(parents), B, N, D, V,
+            _ptr(out["accept_len"]), _ptr(out["path"]), _ptr(out["tokens"]), _ptr(out.get("status")),
+            _ptr(ws), ws.numel() * ws.element_size(), _stream(torch, dev, stream))
+    if rc != SV_OK:
+        raise SpecVerifyError(rc, "spec_verify_tree_lmhead")
     return out
 
 

@@ -294,6 +294,83 @@ sv_status spec_verify_tree(const void *target_logits, const int32_t *node_tokens
     return e == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 
+// ---- greedy verification fused with the LM-head projection ----------------------
+
+static bool lmhead_sizes_ok(long long rows, int D, int V) {
+    // element offsets of H and W rows stay within int32 inside the kernel
+    return rows >= 1 && V >= 1 && D >= 64 && D % 64 == 0 && rows * (D / 8) < 0x7fffffffLL &&
+           static_cast<long long>(V) * (D / 8) < 0x7fffffffLL;
+}
+
+size_t sv_lmhead_workspace_bytes(int rows, int V) {
+    if (rows < 1 || V < 1) return 0;
+    return align_up(static_cast<size_t>(rows) * static_cast<size_t>(lmhead_segs(V)) * sizeof(uint64_t));
+}
+
+static RowGeom lmhead_geom(int V) {
+    RowGeom g;
+    g.per_vec = 8;
+    g.nvec = (V + 7) / 8;
+    g.segs = lmhead_segs(V);
+    g.ntiles = 0;
+    g.aligned = true;
+    return g;
+}
+
+sv_status spec_verify_greedy_lmhead(const void *hidden, const void *lm_head,
+                                    const int32_t *draft_tokens, int B, int K, int D, int V,
+                                    int32_t *accept_len, int32_t *out_tokens, int32_t *req_status,
+                                    void *workspace, size_t workspace_bytes, void *stream) {
+    if (B < 0 || K < 0 || V < 1 || D < 1) return SV_ERR_INVALID_ARG;
+    if (K > SV_MAX_DRAFT_LEN) return SV_ERR_UNSUPPORTED;
+    if (B == 0) return SV_OK;
+    const long long rows = static_cast<long long>(B) * (K + 1);
+    if (!lmhead_sizes_ok(rows, D, V)) return SV_ERR_UNSUPPORTED;
+    if (!hidden || !lm_head || !accept_len || !out_tokens || !workspace) return SV_ERR_INVALID_ARG;
+    if (K > 0 && !draft_tokens) return SV_ERR_INVALID_ARG;
+    if (!aligned16(hidden) || !aligned16(lm_head) || !aligned256(workspace)) return SV_ERR_INVALID_ARG;
+    if (workspace_bytes < sv_lmhead_workspace_bytes(static_cast<int>(rows), V)) return SV_ERR_WORKSPACE;
+    uint64_t *pk = static_cast<uint64_t *>(workspace);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = traced(SV_K_LMHEAD, s, [&] {
+        return launch_lmhead_argmax(hidden, lm_head, static_cast<int>(rows), D, V, pk, s);
+    });
+    if (e == hipSuccess)
+        e = traced(SV_K_MATCH, s, [&] {
+            return launch_match(pk, draft_tokens, B, K, V, lmhead_geom(V), accept_len, out_tokens,
+                                req_status, s);
+        });
+    return e == hipSuccess ? SV_OK : SV_ERR_HIP;
+}
+
+sv_status spec_verify_tree_lmhead(const void *hidden, const void *lm_head,
+                                  const int32_t *node_tokens, const int32_t *parents, int B, int N,
+                                  int D, int V, int32_t *accept_len, int32_t *path_nodes,
+                                  int32_t *out_tokens, int32_t *req_status, void *workspace,
+                                  size_t workspace_bytes, void *stream) {
+    if (B < 0 || N < 1 || V < 1 || D < 1) return SV_ERR_INVALID_ARG;
+    if (N > SV_MAX_TREE_NODES) return SV_ERR_UNSUPPORTED;
+    if (B == 0) return SV_OK;
+    const long long rows = static_cast<long long>(B) * N;
+    if (!lmhead_sizes_ok(rows, D, V)) return SV_ERR_UNSUPPORTED;
+    if (!hidden || !lm_head || !node_tokens || !parents || !accept_len || !path_nodes || !out_tokens ||
+        !workspace)
+        return SV_ERR_INVALID_ARG;
+    if (!aligned16(hidden) || !aligned16(lm_head) || !aligned256(workspace)) return SV_ERR_INVALID_ARG;
+    if (workspace_bytes < sv_lmhead_workspace_bytes(static_cast<int>(rows), V)) return SV_ERR_WORKSPACE;
+    uint64_t *pk = static_cast<uint64_t *>(workspace);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = traced(SV_K_LMHEAD, s, [&] {
+        return launch_lmhead_argmax(hidden, lm_head, static_cast<int>(rows), D, V, pk, s);
+    });
+    if (e == hipSuccess)
+        e = traced(SV_K_TREE, s, [&] {
+            return launch_tree(pk, node_tokens, parents, B, N, V, lmhead_geom(V), accept_len, path_nodes,
+                               out_tokens, req_status, s);
+        });
+    return e == hipSuccess ? SV_OK : SV_ERR_HIP;
+}
+
 sv_status spec_commit_tree_kv(const void *src_kv, void *dst_kv, int G, int B, int S, int row_bytes,
                               const int32_t *tree_base, const int32_t *commit_base,
                               const int32_t *accept_len, const int32_t *path_nodes, int N,
@@ -333,7 +410,7 @@ const char *sv_version(void) { return "specverify 0.1.0 (gfx950)"; }
 const char *sv_kernel_name(int k) {
     static const char *names[SV_K_COUNT] = {"rowstats", "accept", "resid_mass", "resid_select",
                                             "argmax", "match", "tree", "skip_stats",
-                                            "skip_argmax", "commit"};
+                                            "skip_argmax", "commit", "lmhead"};
     return (k >= 0 && k < SV_K_COUNT) ? names[k] : "unknown";
 }
 

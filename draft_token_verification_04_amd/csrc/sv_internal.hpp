@@ -150,6 +150,9 @@ hipError_t launch_skip_match(const void *L, const int32_t *drafts, int B, int K,
                              const RowGeom &g, sv_dtype dt, uint64_t *part_k, int32_t *amax,
                              void *ctl_base, int32_t *accept_len, int32_t *out_tokens,
                              int32_t *status, hipStream_t s);
+int lmhead_segs(int V);
+hipError_t launch_lmhead_argmax(const void *H, const void *W, int M, int D, int V, uint64_t *part_k,
+                                hipStream_t s);
 hipError_t launch_commit(const void *src, void *dst, int G, int B, int S, int row_bytes,
                          const int32_t *tree_base, const int32_t *commit_base,
                          const int32_t *accept_len, const int32_t *path_nodes, int N,

@@ -164,6 +164,37 @@ sv_status spec_verify_tree(const void *target_logits, const int32_t *node_tokens
                            void *stream);
 
 /*
+ * Greedy verification fused with the target's LM-head projection: the logits
+ * of every verified position, H W^T, are formed on the matrix cores and reduced
+ * to their row argmax at once; they are never written.  (The speculative-
+ * decoding tutorial page, section "一轮推测解码究竟发生什么": the target scores
+ * every draft position in one parallel pass; the DLite notes, section 2: the
+ * D x V vocabulary projection is the per-position cost.)
+ *
+ *   hidden   [rows][D] bf16: the target's final hidden state of every
+ *            verified position, rows = B*(K+1) for a chain (request-major,
+ *            position-minor) or B*N for a tree (node-minor).
+ *   lm_head  [V][D] bf16: the projection, one row per vocabulary id.
+ *   D a positive multiple of 64; both pointers 16-byte aligned.
+ * The logit of id v at a row is the fp32 sum over k of hidden[k] * lm_head[v][k]
+ * (products exact, fp32 accumulation in an unspecified order).  Everything
+ * else is exactly spec_verify_greedy / spec_verify_tree on those logits.
+ * Workspace: sv_lmhead_workspace_bytes(rows, V).
+ */
+size_t sv_lmhead_workspace_bytes(int rows, int V);
+
+sv_status spec_verify_greedy_lmhead(const void *hidden, const void *lm_head,
+                                    const int32_t *draft_tokens, int B, int K, int D, int V,
+                                    int32_t *accept_len, int32_t *out_tokens, int32_t *req_status,
+                                    void *workspace, size_t workspace_bytes, void *stream);
+
+sv_status spec_verify_tree_lmhead(const void *hidden, const void *lm_head,
+                                  const int32_t *node_tokens, const int32_t *parents, int B, int N,
+                                  int D, int V, int32_t *accept_len, int32_t *path_nodes,
+                                  int32_t *out_tokens, int32_t *req_status, void *workspace,
+                                  size_t workspace_bytes, void *stream);
+
+/*
  * Commit of a verified draft tree's accepted path in the target's KV cache
  * (AdaPLD page, Algorithm 1: the accepted tokens are appended and the context
  * updated; section 3.3: the whole tree is verified in one target pass, which
@@ -229,7 +260,8 @@ typedef enum {
     SV_K_SKIP_STATS = 7,   /* row statistics + acceptance, skipping rows after a rejection */
     SV_K_SKIP_ARGMAX = 8,  /* row argmax + greedy chain acceptance, skipping rows after a mismatch */
     SV_K_COMMIT = 9,       /* KV rows of accepted tree paths moved to consecutive slots */
-    SV_K_COUNT = 10
+    SV_K_LMHEAD = 10,      /* LM-head projection on the matrix cores + row argmax partials */
+    SV_K_COUNT = 11
 } sv_kernel_id;
 
 sv_status sv_trace_begin(int capacity, unsigned kernel_mask);

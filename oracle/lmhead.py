@@ -44,11 +44,34 @@ def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
     return (np.asarray(bits).astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
 
 
+# Vocabulary rows widened to fp64 at a time, blocks on threads (memory and
+# time only: each logit is still one full fp64 dot product).
+_V_BLOCK = 8192
+
+
+def _project(hidden_bits: np.ndarray, lm_head_bits: np.ndarray, absolute: bool) -> np.ndarray:
+    from concurrent.futures import ThreadPoolExecutor
+
+    H = bf16_to_f64(hidden_bits)
+    if absolute:
+        H = np.abs(H)
+    V = lm_head_bits.shape[0]
+    out = np.empty(H.shape[:-1] + (V,), dtype=np.float64)
+
+    def block(v0):
+        W = bf16_to_f64(lm_head_bits[v0:v0 + _V_BLOCK])
+        out[..., v0:v0 + W.shape[0]] = H @ (np.abs(W) if absolute else W).T
+
+    from threadpoolctl import threadpool_limits
+
+    with threadpool_limits(1), ThreadPoolExecutor(8) as ex:
+        list(ex.map(block, range(0, V, _V_BLOCK)))
+    return out
+
+
 def logits(hidden_bits: np.ndarray, lm_head_bits: np.ndarray) -> np.ndarray:
     """fp64 H W^T for hidden [..., D] and lm_head [V, D] (bf16 bits)."""
-    H = bf16_to_f64(hidden_bits)
-    W = bf16_to_f64(lm_head_bits)
-    return H @ W.T
+    return _project(hidden_bits, lm_head_bits, False)
 
 
 def accumulation_bound(hidden_bits: np.ndarray, lm_head_bits: np.ndarray) -> np.ndarray:
@@ -56,7 +79,7 @@ def accumulation_bound(hidden_bits: np.ndarray, lm_head_bits: np.ndarray) -> np.
     D = hidden_bits.shape[-1]
     n = D - 1
     gamma = n * U32 / (1.0 - n * U32)
-    return gamma * (np.abs(bf16_to_f64(hidden_bits)) @ np.abs(bf16_to_f64(lm_head_bits)).T)
+    return gamma * _project(hidden_bits, lm_head_bits, True)
 
 
 def row_argmax(L: np.ndarray, E: np.ndarray | None):

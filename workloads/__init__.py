@@ -307,48 +307,82 @@ def make_config(c: int, seed=None, B=None) -> Workload:
 LMHEAD_SHAPE = dict(B=256, K=7, D=4096, V=VOCAB_QWEN3)
 
 
-def _lmhead_values(seed, rows: int, D: int, V: int, exact: bool):
-    sh, sw = seed.spawn(2)
-    rh, rw = np.random.default_rng(sh), np.random.default_rng(sw)
-    if exact:
-        H = rh.integers(-8, 9, size=(rows, D)).astype(np.float32) / 8
-        W = rw.integers(-8, 9, size=(V, D)).astype(np.float32) / 64
-    else:
-        H = rh.standard_normal((rows, D), dtype=np.float32)
-        W = rw.standard_normal((V, D), dtype=np.float32) * np.float32(3.0 / np.sqrt(D))
-    return to_bf16_bits(H), to_bf16_bits(W)
+_LM_BLOCK = 4096  # rows per seeded block of the LM-head operands
 
 
-def _lmhead_argmax(Hb: np.ndarray, Wb: np.ndarray, exact: bool) -> np.ndarray:
-    """Row argmax of H W^T, for planting matching drafts (blocks of 64 rows)."""
-    dt = np.float32 if exact else np.float64
-    W = bf16_bits_to_f32(Wb).astype(dt)
-    out = np.empty(Hb.shape[0], dtype=np.int64)
-    for r0 in range(0, Hb.shape[0], BLOCK_ROWS):
-        h = bf16_bits_to_f32(Hb[r0:r0 + BLOCK_ROWS]).astype(dt)
-        out[r0:r0 + BLOCK_ROWS] = np.argmax(h @ W.T, axis=1)
+def _lmhead_rows(seed, rows: int, D: int, exact: bool, scale: float) -> np.ndarray:
+    """bf16 bits [rows, D]: exact recipe k * scale (k uniform in [-8, 8]) or
+    N(0, scale^2), drawn in seeded blocks of _LM_BLOCK rows on threads."""
+    out = np.empty((rows, D), dtype=np.uint16)
+    nblk = (rows + _LM_BLOCK - 1) // _LM_BLOCK
+    seeds = seed.spawn(nblk)
+    table = to_bf16_bits(np.arange(-8, 9, dtype=np.float32) * np.float32(scale))
+
+    def job(k):
+        r0, r1 = k * _LM_BLOCK, min(rows, (k + 1) * _LM_BLOCK)
+        rng = np.random.default_rng(seeds[k])
+        if exact:
+            out[r0:r1] = table[rng.integers(0, 17, size=(r1 - r0, D), dtype=np.int8)]
+        else:
+            out[r0:r1] = to_bf16_bits(rng.standard_normal((r1 - r0, D), dtype=np.float32) * np.float32(scale))
+
+    with ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(job, range(nblk)))
     return out
 
 
-def make_greedy_lmhead(B, K, D, V, exact=True, p_match=0.8, seed=0) -> Workload:
-    """Greedy-chain inputs for the fused LM-head path: hidden [B,K+1,D], lm_head [V,D]."""
+def _lmhead_values(seed, rows: int, D: int, V: int, exact: bool):
+    sh, sw = seed.spawn(2)
+    if exact:
+        return _lmhead_rows(sh, rows, D, True, 1 / 8), _lmhead_rows(sw, V, D, True, 1 / 64)
+    return _lmhead_rows(sh, rows, D, False, 1.0), _lmhead_rows(sw, V, D, False, 3.0 / np.sqrt(D))
+
+
+def _lmhead_argmax(Hb: np.ndarray, Wb: np.ndarray, exact: bool) -> np.ndarray:
+    """Row argmax of H W^T, for planting matching drafts (the exact recipe is
+    exact in fp32; the general one uses fp64)."""
+    dt = np.float32 if exact else np.float64
+    h = bf16_bits_to_f32(Hb).astype(dt)
+    V = Wb.shape[0]
+    nblk = (V + _LM_BLOCK - 1) // _LM_BLOCK
+    best = np.full((nblk, Hb.shape[0]), -np.inf)
+    arg = np.zeros((nblk, Hb.shape[0]), dtype=np.int64)
+
+    def job(k):
+        v0 = k * _LM_BLOCK
+        L = h @ bf16_bits_to_f32(Wb[v0:v0 + _LM_BLOCK]).astype(dt).T
+        arg[k] = v0 + np.argmax(L, axis=1)
+        best[k] = L.max(axis=1)
+
+    with ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(job, range(nblk)))
+    return arg[np.argmax(best, axis=0), np.arange(Hb.shape[0])]
+
+
+def make_greedy_lmhead(B, K, D, V, exact=True, p_match=0.8, seed=0, plant=None) -> Workload:
+    """Greedy-chain inputs for the fused LM-head path: hidden [B,K+1,D], lm_head [V,D].
+    `plant` limits the matching drafts to those requests (the others draw
+    uniform drafts), so large shapes need logits of a few rows only."""
     ss = seed if isinstance(seed, np.random.SeedSequence) else np.random.SeedSequence(seed)
     st = ss.spawn(6)
     Hb, Wb = _lmhead_values(st[_S_TARGET], B * (K + 1), D, V, exact)
     rng = np.random.default_rng(st[_S_DRAFTS])
     x = rng.integers(0, V, size=(B, K)).astype(np.int32)
+    hit = rng.random((B, K)) < (p_match or 0.0)
     if p_match is not None and K > 0:
-        am = _lmhead_argmax(Hb, Wb, exact).reshape(B, K + 1)
-        hit = rng.random((B, K)) < p_match
-        x = np.where(hit, am[:, :K], x).astype(np.int32)
+        reqs = np.arange(B) if plant is None else np.asarray(plant)
+        H3 = Hb.reshape(B, K + 1, D)
+        am = _lmhead_argmax(H3[reqs].reshape(-1, D), Wb, exact).reshape(len(reqs), K + 1)
+        x[reqs] = np.where(hit[reqs], am[:, :K], x[reqs])
     return Workload(mode="greedy_lmhead", B=B, K=K, V=V, dtype="bf16", draft_tokens=x,
                     hidden=Hb.reshape(B, K + 1, D), lm_head=Wb,
                     meta=dict(D=D, exact=exact, p_match=p_match))
 
 
 def make_tree_lmhead(B, D, V, exact=True, p_match=0.7, n_main=8, n_branch=12, max_extra=3,
-                     seed=0) -> Workload:
-    """Greedy-tree inputs for the fused LM-head path: hidden [B,N,D], lm_head [V,D]."""
+                     seed=0, plant=None) -> Workload:
+    """Greedy-tree inputs for the fused LM-head path: hidden [B,N,D], lm_head [V,D]
+    (`plant` as for chains)."""
     ss = seed if isinstance(seed, np.random.SeedSequence) else np.random.SeedSequence(seed)
     st = ss.spawn(6)
     N = 1 + n_main + 2 * n_branch
@@ -357,10 +391,12 @@ def make_tree_lmhead(B, D, V, exact=True, p_match=0.7, n_main=8, n_branch=12, ma
                         for _ in range(B)])
     Hb, Wb = _lmhead_values(st[_S_TARGET], B * N, D, V, exact)
     tok = rng.integers(0, V, size=(B, N)).astype(np.int32)
+    hit = rng.random((B, N)) < (p_match or 0.0)
     if p_match is not None:
-        am = _lmhead_argmax(Hb, Wb, exact).reshape(B, N)
-        hit = rng.random((B, N)) < p_match
-        tok = np.where(hit, np.take_along_axis(am, np.maximum(parents, 0), 1), tok).astype(np.int32)
+        reqs = np.arange(B) if plant is None else np.asarray(plant)
+        am = _lmhead_argmax(Hb.reshape(B, N, D)[reqs].reshape(-1, D), Wb, exact).reshape(len(reqs), N)
+        want = np.take_along_axis(am, np.maximum(parents[reqs], 0), 1)
+        tok[reqs] = np.where(hit[reqs], want, tok[reqs])
     return Workload(mode="tree_lmhead", B=B, N=N, V=V, dtype="bf16", node_tokens=tok,
                     parents=parents.astype(np.int32), hidden=Hb.reshape(B, N, D), lm_head=Wb,
                     meta=dict(D=D, exact=exact, p_match=p_match))
