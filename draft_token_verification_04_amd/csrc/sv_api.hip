@@ -298,7 +298,7 @@ sv_status spec_verify_tree(const void *target_logits, const int32_t *node_tokens
 
 static bool lmhead_sizes_ok(long long rows, int D, int V) {
     // element offsets of H and W rows stay within int32 inside the kernel
-    return rows >= 1 && V >= 1 && D >= 64 && D % 64 == 0 && rows * (D / 8) < 0x7fffffffLL &&
+    return rows >= 1 && V >= 1 && D >= 128 && D % 128 == 0 && rows * (D / 8) < 0x7fffffffLL &&
            static_cast<long long>(V) * (D / 8) < 0x7fffffffLL;
 }
 

@@ -11,16 +11,20 @@
 //
 // k_lmhead_argmax: C[m][n] = sum_k H[m][k] W[n][k] with H [M][D] and W [V][D]
 // bf16, both k-contiguous.  A workgroup of 4 waves owns a 256 x 256 tile of C
-// and walks D in steps of 64: the next step's H and W slabs are loaded into
-// registers while the current one is multiplied out of LDS (two LDS buffers,
-// rows padded to 144 bytes so the fragment reads hit distinct banks), then
-// stored to the other buffer; one barrier per step.  Each wave holds a
+// and walks D in steps of 32.  The H and W slabs of a step go straight from
+// global memory into LDS (global_load_lds, 16 bytes per lane, no registers),
+// issued three steps ahead into a ring of four LDS buffers; a step waits only
+// for its own loads (vmcnt), then one barrier.  LDS rows are 64 bytes with the
+// four 16-byte chunks of row r stored in the order c ^ ((r >> 2) & 3), so the
+// fragment reads of 16 consecutive rows hit distinct banks.  Each wave holds a
 // 128 x 128 quarter as 4 x 4 tiles of v_mfma_f32_32x32x16_bf16 accumulators
-// (fp32).  Workgroups are numbered so that the 8 row tiles of one column tile
+// (fp32).  Workgroups are numbered so that the row tiles of one column tile
 // run together on one XCD (consecutive workgroup ids go to consecutive XCDs):
 // the column tile's W slab is then read from HBM once and shared through that
 // XCD's L2.
 #include <limits.h>
+
+#include <type_traits>
 
 #include "sv_device.hpp"
 #include "sv_internal.hpp"
@@ -30,23 +34,37 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+#define SV_LDS __attribute__((address_space(3)))
 
 constexpr int kXcds = 8;
-constexpr int kTM = 256, kTN = 256, kTK = 64;  // workgroup tile and D step
-constexpr int kRowBytes = kTK * 2 + 16;        // LDS bytes per tile row (padded)
-constexpr int kTileBytes = kTM * kRowBytes;    // one operand slab in LDS
+constexpr int kTM = 256, kTN = 256, kTK = 32;  // workgroup tile and D step
+constexpr int kSlab = kTM * kTK * 2;           // bytes of one operand slab (64-byte rows)
 constexpr int kSegCols = 128;                  // columns per argmax key (one wave's width)
-constexpr int kLoadsPerThread = kTM * kTK * 2 / 16 / kBlock;  // 16-byte chunks per operand
+constexpr int kStages = 4;                     // LDS ring; loads run kStages - 1 steps ahead
+constexpr int kLoadsPerStep = 2 * kSlab / 16 / kBlock;  // DMA loads per thread per step (8)
 
-__device__ __forceinline__ bf16x8 lds_frag(const char *p) {
-    return *reinterpret_cast<const bf16x8 *>(p);
+// One array per ring slot and operand, so the compiler can tell which slot a
+// fragment read touches and waits only for that slot's loads.
+__shared__ __align__(1024) char sA0[kSlab], sA1[kSlab], sA2[kSlab], sA3[kSlab];
+__shared__ __align__(1024) char sB0[kSlab], sB1[kSlab], sB2[kSlab], sB3[kSlab];
+template <int S> __device__ __forceinline__ char *slab_a() {
+    return S == 0 ? sA0 : S == 1 ? sA1 : S == 2 ? sA2 : sA3;
+}
+template <int S> __device__ __forceinline__ char *slab_b() {
+    return S == 0 ? sB0 : S == 1 ? sB1 : S == 2 ? sB2 : sB3;
+}
+template <int S> using Slot = std::integral_constant<int, S>;
+
+// vmcnt(n) with the other counters left alone (gfx9 encoding).
+template <int N> __device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
 __global__ __launch_bounds__(kBlock, 1) void k_lmhead_argmax(const uint4 *__restrict__ H,
                                                              const uint4 *__restrict__ W, int M, int D,
                                                              int V, int mtiles, int ntiles,
                                                              uint64_t *__restrict__ part_k, int segs) {
-    __shared__ __align__(16) char lds[4 * kTileBytes];  // [stage][A|B]
     const int bid = blockIdx.x;
     const int xcd = bid % kXcds, j = bid / kXcds;
     const int mt = j % mtiles;
@@ -57,17 +75,29 @@ __global__ __launch_bounds__(kBlock, 1) void k_lmhead_argmax(const uint4 *__rest
     const int wm = w >> 1, wn = w & 1;
     const int dv = D / 8;  // 16-byte chunks per row
 
-    // global -> register staging: chunk q = tid + kBlock*i is row q/8, column
-    // chunk q%8; offsets are 32-bit element counts from the uniform bases
-    // (H and W rows past M or V read the last row instead)
-    const int r0 = tid >> 3, c0 = tid & 7;
-    int ga[kLoadsPerThread], gb[kLoadsPerThread];
+    // DMA mapping: instruction i of wave w fills slab rows 16 q .. 16 q + 15,
+    // q = 4 i + w; lane l writes 16 bytes at 16 l, i.e. row 16 q + l / 4,
+    // stored chunk l % 4, which holds the row's logical chunk (l % 4) ^ ((r >> 2) & 3).
+    // Offsets are 32-bit 16-byte-chunk counts; rows past M or V read the last row.
+    int ga[4], gb[4];
 #pragma unroll
-    for (int i = 0; i < kLoadsPerThread; ++i) {
-        ga[i] = min(m0 + r0 + 32 * i, M - 1) * dv + c0;
-        gb[i] = min(n0 + r0 + 32 * i, V - 1) * dv + c0;
+    for (int i = 0; i < 4; ++i) {
+        const int r = 16 * (4 * i + w) + (lane >> 2);
+        const int c = (lane & 3) ^ ((r >> 2) & 3);
+        ga[i] = min(m0 + r, M - 1) * dv + c;
+        gb[i] = min(n0 + r, V - 1) * dv + c;
     }
-    char *const st0 = lds + r0 * kRowBytes + c0 * 16;  // this thread's slot in stage 0's A slab
+    auto issue = [&](auto slot, int step) {
+        constexpr int S = decltype(slot)::value;
+        const int k0 = step * (kTK / 8);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            __builtin_amdgcn_global_load_lds(H + ga[i] + k0, (SV_LDS void *)(slab_a<S>() + (4 * i + w) * 1024),
+                                             16, 0, 0);
+            __builtin_amdgcn_global_load_lds(W + gb[i] + k0, (SV_LDS void *)(slab_b<S>() + (4 * i + w) * 1024),
+                                             16, 0, 0);
+        }
+    };
 
     f32x16 acc[4][4];
 #pragma unroll
@@ -75,38 +105,19 @@ __global__ __launch_bounds__(kBlock, 1) void k_lmhead_argmax(const uint4 *__rest
 #pragma unroll
         for (int b = 0; b < 4; ++b) acc[a][b] = f32x16{};
 
-    // fragment offsets: lane reads 8 k-values of row (l % 32) at k offset 8 (l / 32)
-    const int fa = (wm * 128 + (lane & 31)) * kRowBytes + (lane >> 5) * 16;
-    const int fb = (wn * 128 + (lane & 31)) * kRowBytes + (lane >> 5) * 16;
-    const int nk = D / kTK;
-    uint4 ra[kLoadsPerThread], rb[kLoadsPerThread];
-#pragma unroll
-    for (int i = 0; i < kLoadsPerThread; ++i) {
-        ra[i] = H[ga[i]];
-        rb[i] = W[gb[i]];
-    }
-#pragma unroll
-    for (int i = 0; i < kLoadsPerThread; ++i) {
-        *reinterpret_cast<uint4 *>(st0 + i * 32 * kRowBytes) = ra[i];
-        *reinterpret_cast<uint4 *>(st0 + kTileBytes + i * 32 * kRowBytes) = rb[i];
-    }
-    __syncthreads();
-    for (int s = 0; s < nk; ++s) {
-        // the next step's slabs (the last step loads its own again; never read)
-        const int kn = min(s + 1, nk - 1) * (kTK / 8);
-#pragma unroll
-        for (int i = 0; i < kLoadsPerThread; ++i) {
-            ra[i] = H[ga[i] + kn];
-            rb[i] = W[gb[i] + kn];
-        }
-        const char *sa = lds + (s & 1) * 2 * kTileBytes, *sb = sa + kTileBytes;
+    // fragment reads: lane reads the 8 k-values of row (l % 32) at k offset 8 (l / 32)
+    auto compute = [&](auto slot) {
+        constexpr int S = decltype(slot)::value;
 #pragma unroll
         for (int kk = 0; kk < kTK / 16; ++kk) {
             bf16x8 af[4], bfr[4];
+            const int c = kk * 2 + (lane >> 5);
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-                af[t] = lds_frag(sa + fa + t * 32 * kRowBytes + kk * 32);
-                bfr[t] = lds_frag(sb + fb + t * 32 * kRowBytes + kk * 32);
+                const int ra = wm * 128 + t * 32 + (lane & 31);
+                const int rb = wn * 128 + t * 32 + (lane & 31);
+                af[t] = *reinterpret_cast<const bf16x8 *>(slab_a<S>() + ra * 64 + ((c ^ ((ra >> 2) & 3)) << 4));
+                bfr[t] = *reinterpret_cast<const bf16x8 *>(slab_b<S>() + rb * 64 + ((c ^ ((rb >> 2) & 3)) << 4));
             }
 #pragma unroll
             for (int a = 0; a < 4; ++a)
@@ -114,14 +125,29 @@ __global__ __launch_bounds__(kBlock, 1) void k_lmhead_argmax(const uint4 *__rest
                 for (int b = 0; b < 4; ++b)
                     acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a], bfr[b], acc[a][b], 0, 0, 0);
         }
-        char *dn = st0 + ((s + 1) & 1) * 2 * kTileBytes;
-#pragma unroll
-        for (int i = 0; i < kLoadsPerThread; ++i) {
-            *reinterpret_cast<uint4 *>(dn + i * 32 * kRowBytes) = ra[i];
-            *reinterpret_cast<uint4 *>(dn + kTileBytes + i * 32 * kRowBytes) = rb[i];
-        }
-        __syncthreads();
+    };
+
+    const int nk = D / kTK;  // a multiple of kStages (D % 128 == 0)
+    issue(Slot<0>{}, 0);
+    issue(Slot<1>{}, 1);
+    issue(Slot<2>{}, 2);
+    // step s: its loads are done once at most the 2 later steps' loads are
+    // outstanding; the barrier then also means every wave has finished step
+    // s - 1, whose slot the loads of step s + 3 reuse (past the end, the last
+    // step is loaded again into a slot nobody reads)
+#define SV_STEP(S)                                                            \
+    wait_vm<2 * kLoadsPerStep>();                                             \
+    __builtin_amdgcn_s_barrier();                                             \
+    issue(Slot<(S + 3) % kStages>{}, min(s + S + 3, nk - 1));                  \
+    compute(Slot<S>{});
+    for (int s = 0; s < nk; s += kStages) {
+        SV_STEP(0)
+        SV_STEP(1)
+        SV_STEP(2)
+        SV_STEP(3)
     }
+#undef SV_STEP
+    wait_vm<0>();  // no DMA may still target LDS when the workgroup ends
 
     // epilogue: per row, the first maximum over this wave's 128 columns
     const int seg = (n0 + wn * 128) / kSegCols;

@@ -175,7 +175,8 @@ sv_status spec_verify_tree(const void *target_logits, const int32_t *node_tokens
  *            verified position, rows = B*(K+1) for a chain (request-major,
  *            position-minor) or B*N for a tree (node-minor).
  *   lm_head  [V][D] bf16: the projection, one row per vocabulary id.
- *   D a positive multiple of 64; both pointers 16-byte aligned.
+ *   D a positive multiple of 128 (else SV_ERR_UNSUPPORTED); both pointers
+ *   16-byte aligned.
  * The logit of id v at a row is the fp32 sum over k of hidden[k] * lm_head[v][k]
  * (products exact, fp32 accumulation in an unspecified order).  Everything
  * else is exactly spec_verify_greedy / spec_verify_tree on those logits.

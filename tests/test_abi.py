@@ -150,3 +150,22 @@ def test_commit_argument_checks(lib):
     assert _commit(lib, p=None) == sv.SV_ERR_INVALID_ARG
     assert _commit(lib, dst=ctypes.c_void_p((1 << 20) + 8)) == sv.SV_ERR_INVALID_ARG
     assert _commit(lib, B=0, src=None, dst=None) == sv.SV_OK
+
+
+def test_lmhead_argument_checks(lib):
+    def chain(**kw):
+        a = dict(h=FAKE, w=FAKE, x=FAKE, B=2, K=3, D=256, V=100, n=FAKE, tok=FAKE, st=None, ws=FAKE,
+                 wsb=1 << 30, s=None)
+        a.update(kw)
+        return lib.spec_verify_greedy_lmhead(a["h"], a["w"], a["x"], a["B"], a["K"], a["D"], a["V"], a["n"],
+                                             a["tok"], a["st"], a["ws"], a["wsb"], a["s"])
+    assert chain(D=64) == sv.SV_ERR_UNSUPPORTED       # D must be a multiple of 128
+    assert chain(D=200) == sv.SV_ERR_UNSUPPORTED
+    assert chain(B=-1) == sv.SV_ERR_INVALID_ARG
+    assert chain(V=0) == sv.SV_ERR_INVALID_ARG
+    assert chain(h=None) == sv.SV_ERR_INVALID_ARG
+    assert chain(x=None) == sv.SV_ERR_INVALID_ARG
+    assert chain(wsb=16) == sv.SV_ERR_WORKSPACE
+    assert chain(B=0) == sv.SV_OK
+    assert lib.sv_lmhead_workspace_bytes(2048, 151936) == 2048 * 1187 * 8
+    assert lib.sv_lmhead_workspace_bytes(0, 10) == 0

@@ -43,8 +43,8 @@ def compare(g, o, keys, reqs=None, flagged=None):
         assert np.array_equal(g[k][reqs][keep], o[k][keep]), k
 
 
-CHAIN_EXACT = [(3, 2, 64, 77), (5, 3, 128, 1000), (7, 7, 192, 1001), (40, 7, 256, 5000), (2, 0, 64, 300),
-               (33, 7, 128, 256), (1, 1, 64, 1)]
+CHAIN_EXACT = [(3, 2, 128, 77), (5, 3, 128, 1000), (7, 7, 384, 1001), (40, 7, 256, 5000), (2, 0, 128, 300),
+               (33, 7, 128, 256), (1, 1, 128, 1), (9, 3, 2560, 700)]
 
 
 @pytest.mark.parametrize("case", CHAIN_EXACT, ids=lambda c: "B{}K{}D{}V{}".format(*c))
@@ -65,7 +65,7 @@ def test_chain_general_recipe():
     compare(gpu_chain(w), o, ("accept_len", "tokens", "status"), flagged=o["flagged"])
 
 
-@pytest.mark.parametrize("case", [(10, 128, 2000), (3, 64, 130)], ids=lambda c: "B{}D{}V{}".format(*c))
+@pytest.mark.parametrize("case", [(10, 128, 2000), (3, 256, 130)], ids=lambda c: "B{}D{}V{}".format(*c))
 def test_tree_exact(case):
     B, D, V = case
     note(f"lmhead tree exact {case}")
@@ -76,13 +76,13 @@ def test_tree_exact(case):
 
 def test_out_of_range_drafts_and_bad_parents():
     note("lmhead bad inputs")
-    w = workloads.make_greedy_lmhead(6, 4, 64, 500, exact=True, seed=3)
+    w = workloads.make_greedy_lmhead(6, 4, 128, 500, exact=True, seed=3)
     w.draft_tokens[1, 0] = -3
     w.draft_tokens[2, 2] = 500
     o = lmhead.verify_greedy(w.hidden, w.lm_head, w.draft_tokens, exact=True)
     assert o["status"][1] == 1 and o["status"][2] == 1
     compare(gpu_chain(w), o, ("accept_len", "tokens", "status"))
-    t = workloads.make_tree_lmhead(4, 64, 500, exact=True, seed=4)
+    t = workloads.make_tree_lmhead(4, 128, 500, exact=True, seed=4)
     t.parents[2, 9] = 12
     o = lmhead.verify_tree(t.hidden, t.lm_head, t.node_tokens, t.parents, exact=True)
     assert o["status"][2] == 2
