@@ -47,6 +47,12 @@ KERNEL_SOURCES = {
     "argmax": ["draft_token_verification_04_amd/csrc/sv_greedy.hip",
                "draft_token_verification_04_amd/csrc/sv_device.hpp",
                "draft_token_verification_04_amd/csrc/sv_internal.hpp"],
+    "lmhead": ["draft_token_verification_04_amd/csrc/sv_lmhead.hip",
+               "draft_token_verification_04_amd/csrc/sv_device.hpp",
+               "draft_token_verification_04_amd/csrc/sv_internal.hpp"],
+    "commit": ["draft_token_verification_04_amd/csrc/sv_commit.hip",
+               "draft_token_verification_04_amd/csrc/sv_device.hpp",
+               "draft_token_verification_04_amd/csrc/sv_internal.hpp"],
     "skip_argmax": ["draft_token_verification_04_amd/csrc/sv_greedy.hip",
                     "draft_token_verification_04_amd/csrc/sv_skip.hpp",
                     "draft_token_verification_04_amd/csrc/sv_device.hpp",
@@ -61,6 +67,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--mode", choices=("all", "sample", "greedy", "tree"), default="all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-lmhead", action="store_true", help="skip the fused LM-head extra")
     ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (default: up to 16)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="before timing, run a plain elementwise copy (negation) kernel that reads "
@@ -189,6 +196,94 @@ def cpu_baseline(w3, w4, w5, mode, threads):
             oracle.verify_tree(w5.target, w5.node_tokens, w5.parents, threads=threads)
         times.append(time.perf_counter() - t0)
     return statistics.median(times)
+
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, vendor figure
+
+
+def bench_lmhead(sv, torch, workloads, dev, reps):
+    """spec_verify_greedy_lmhead on seeded exact-recipe operands (random drafts:
+    the fused kernel's work does not depend on acceptance), beside the unfused
+    reference: a library GEMM (torch.matmul) writing the logits, then
+    spec_verify_greedy reading them."""
+    import numpy as np
+
+    shp = workloads.LMHEAD_SHAPE
+    B, K, D, V = shp["B"], shp["K"], shp["D"], shp["V"]
+    t0 = time.perf_counter()
+    w = workloads.make_greedy_lmhead(B, K, D, V, exact=True, p_match=None, seed=20261206)
+    H = torch.from_numpy(w.hidden.view(np.int16)).view(torch.bfloat16).to(dev)
+    Wt = torch.from_numpy(w.lm_head.view(np.int16)).view(torch.bfloat16).to(dev)
+    x = torch.from_numpy(w.draft_tokens).to(dev)
+    print(f"[bench] lm-head operands ready in {time.perf_counter() - t0:.1f}s", file=sys.stderr, flush=True)
+    lib = sv.load_library()
+    M = B * (K + 1)
+    ws = torch.empty(lib.sv_lmhead_workspace_bytes(M, V), dtype=torch.uint8, device=dev)
+    n = torch.empty(B, dtype=torch.int32, device=dev)
+    tok = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    args = (P(H), P(Wt), P(x), B, K, D, V, P(n), P(tok), None, P(ws), ws.numel(), stream)
+
+    def fused():
+        rc = lib.spec_verify_greedy_lmhead(*args)
+        if rc:
+            raise RuntimeError(f"spec_verify_greedy_lmhead failed: {rc}")
+
+    for _ in range(3):
+        fused()
+    torch.cuda.synchronize()
+    r = max(5, reps // 10)
+    t0 = time.perf_counter()
+    for _ in range(r):
+        fused()
+    torch.cuda.synchronize()
+    call_ms = (time.perf_counter() - t0) * 1e3 / r
+    sv.trace_begin(64, kernels=("lmhead", "match"))
+    for _ in range(r):
+        fused()
+    torch.cuda.synchronize()
+    per = {}
+    for name, ms in sv.trace_end(64):
+        per.setdefault(name, []).append(ms)
+    k_ms = statistics.mean(per["lmhead"])
+    flop = 2.0 * M * D * V
+
+    # unfused reference: logits written by the library GEMM, then read by the verifier
+    L = torch.empty((B, K + 1, V), dtype=torch.bfloat16, device=dev)
+    Hm = H.reshape(M, D)
+    Lm = L.view(M, V)
+    g_ws = torch.empty(lib.sv_greedy_workspace_bytes(B, K + 1, V, sv.SV_BF16), dtype=torch.uint8, device=dev)
+    g_args = (P(L), P(x), B, K, V, sv.SV_BF16, P(n), P(tok), None, P(g_ws), g_ws.numel(), stream)
+
+    def unfused():
+        torch.matmul(Hm, Wt.t(), out=Lm)
+        rc = lib.spec_verify_greedy(*g_args)
+        if rc:
+            raise RuntimeError(f"spec_verify_greedy failed: {rc}")
+
+    for _ in range(3):
+        unfused()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(r):
+        unfused()
+    torch.cuda.synchronize()
+    unfused_ms = (time.perf_counter() - t0) * 1e3 / r
+    del L, Lm
+    return {
+        "workload": f"greedy chain with the LM-head projection fused: B={B} K={K} D={D} V={V}, bf16 "
+                    "operands (exact recipe), logits never written",
+        "rows": M, "flop": flop, "call_ms": round(call_ms, 5), "kernel_ms": round(k_ms, 5),
+        "match_ms": round(statistics.mean(per["match"]), 5),
+        "rows_per_s": round(M / (call_ms * 1e-3), 1),
+        "roofline": {"bound": "mfma", "kernel": "lmhead", "achieved": round(flop / (k_ms * 1e-3) * 1e-12, 1),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(flop / (k_ms * 1e-3) * 1e-12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": (stored_traffic("lmhead") or {}).get("bytes_per_launch")},
+        "unfused_reference": {"what": "torch.matmul (bf16 logits written to HBM) + spec_verify_greedy",
+                              "call_ms": round(unfused_ms, 5)},
+    }
 
 
 def main():
@@ -383,8 +478,14 @@ def main():
             "kernel_ms": round(kms, 5),
             "roofline": {"bound": "hbm", "kernel": "commit", "achieved": round(moved / (kms * 1e-3) / 1e9, 1),
                          "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                         "frac": round(moved / (kms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}}
+                         "frac": round(moved / (kms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                         "traffic": (stored_traffic("commit") or {}).get("bytes_per_launch")}}
         del kv
+
+    # the greedy chain with the LM-head projection fused in (hidden states in,
+    # logits never written), at the Qwen3-8B shape B=256 K=7 D=4096 V=151936
+    if "greedy" in active and not args.no_lmhead:
+        extras["greedy_lmhead"] = bench_lmhead(sv, torch, workloads, dev, reps)
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -10,18 +10,18 @@
 // the cost a drafter avoids repeating per position).
 //
 // k_lmhead_argmax: C[m][n] = sum_k H[m][k] W[n][k] with H [M][D] and W [V][D]
-// bf16, both k-contiguous.  A workgroup of 4 waves owns a 256 x 256 tile of C
-// and walks D in steps of 32.  The H and W slabs of a step go straight from
-// global memory into LDS (global_load_lds, 16 bytes per lane, no registers),
-// issued three steps ahead into a ring of four LDS buffers; a step waits only
-// for its own loads (vmcnt), then one barrier.  LDS rows are 64 bytes with the
-// four 16-byte chunks of row r stored in the order c ^ ((r >> 2) & 3), so the
-// fragment reads of 16 consecutive rows hit distinct banks.  Each wave holds a
-// 128 x 128 quarter as 4 x 4 tiles of v_mfma_f32_32x32x16_bf16 accumulators
-// (fp32).  Workgroups are numbered so that the row tiles of one column tile
-// run together on one XCD (consecutive workgroup ids go to consecutive XCDs):
-// the column tile's W slab is then read from HBM once and shared through that
-// XCD's L2.
+// bf16, both k-contiguous.  A workgroup of 8 waves (two per SIMD) owns a
+// 256 x 256 tile of C and walks D in steps of 32.  The H and W slabs of a step
+// go straight from global memory into LDS (global_load_lds, 16 bytes per lane,
+// no registers), issued three steps ahead into a ring of four LDS buffers; a
+// step waits only for its own loads (vmcnt), then one barrier.  LDS rows are
+// 64 bytes with the four 16-byte chunks of row r stored in the order
+// c ^ ((r >> 2) & 3), so the fragment reads of 16 consecutive rows hit
+// distinct banks.  Each wave holds a 64 x 128 part as 2 x 4 tiles of
+// v_mfma_f32_32x32x16_bf16 accumulators (fp32).  Workgroups are numbered so
+// that the row tiles of one column tile run together on one XCD (consecutive
+// workgroup ids go to consecutive XCDs): the column tile's W slab is then read
+// from HBM once and shared through that XCD's L2.
 #include <limits.h>
 
 #include <type_traits>
@@ -38,15 +38,32 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kXcds = 8;
 constexpr int kTM = 256, kTN = 256, kTK = 32;  // workgroup tile and D step
-constexpr int kSlab = kTM * kTK * 2;           // bytes of one operand slab (64-byte rows)
+constexpr int kRowB = kTK * 2;                 // LDS bytes per slab row
+constexpr int kChunks = kRowB / 16;            // 16-byte chunks per slab row (4)
+constexpr int kRowsPerDma = 1024 / kRowB;      // slab rows one wave-wide DMA fills (16)
+constexpr int kSlab = kTM * kRowB;             // bytes of one operand slab
 constexpr int kSegCols = 128;                  // columns per argmax key (one wave's width)
-constexpr int kStages = 4;                     // LDS ring; loads run kStages - 1 steps ahead
-constexpr int kLoadsPerStep = 2 * kSlab / 16 / kBlock;  // DMA loads per thread per step (8)
+constexpr int kStages = 4;  // LDS ring slots; loads run kStages - 1 steps ahead
+// Waves per workgroup: 4 (one per SIMD, 128 x 128 each) or 8 (two per SIMD,
+// 64 x 128 each, so one wave's waits can hide behind the other's MFMAs).
+#ifndef SV_LMHEAD_WAVES
+#define SV_LMHEAD_WAVES 8
+#endif
+constexpr int kLmWaves = SV_LMHEAD_WAVES;
+constexpr int kLmThreads = kLmWaves * kWave;
+constexpr int kWavesM = kLmWaves / 2;          // waves along M (2 along N)
+constexpr int kTilesA = kTM / kWavesM / 32;    // 32-row MFMA tiles per wave along M
+constexpr int kDmaPerOperand = kSlab / 1024 / kLmWaves;  // 1 KB DMA instructions per wave per operand
+constexpr int kLoadsPerStep = 2 * kDmaPerOperand;        // DMA loads per thread per step
 
 // One array per ring slot and operand, so the compiler can tell which slot a
 // fragment read touches and waits only for that slot's loads.
 __shared__ __align__(1024) char sA0[kSlab], sA1[kSlab], sA2[kSlab], sA3[kSlab];
 __shared__ __align__(1024) char sB0[kSlab], sB1[kSlab], sB2[kSlab], sB3[kSlab];
+// Stored position of logical 16-byte chunk c of slab row r: consecutive rows
+// rotate their chunks so that 16 lanes reading one logical chunk of 16
+// consecutive rows hit 16 distinct 4-bank groups (measured: no bank conflicts).
+__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 2) & 3); }
 template <int S> __device__ __forceinline__ char *slab_a() {
     return S == 0 ? sA0 : S == 1 ? sA1 : S == 2 ? sA2 : sA3;
 }
@@ -61,7 +78,7 @@ template <int N> __device__ __forceinline__ void wait_vm() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-__global__ __launch_bounds__(kBlock, 1) void k_lmhead_argmax(const uint4 *__restrict__ H,
+__global__ __launch_bounds__(kLmThreads, 1) void k_lmhead_argmax(const uint4 *__restrict__ H,
                                                              const uint4 *__restrict__ W, int M, int D,
                                                              int V, int mtiles, int ntiles,
                                                              uint64_t *__restrict__ part_k, int segs) {
@@ -75,15 +92,16 @@ __global__ __launch_bounds__(kBlock, 1) void k_lmhead_argmax(const uint4 *__rest
     const int wm = w >> 1, wn = w & 1;
     const int dv = D / 8;  // 16-byte chunks per row
 
-    // DMA mapping: instruction i of wave w fills slab rows 16 q .. 16 q + 15,
-    // q = 4 i + w; lane l writes 16 bytes at 16 l, i.e. row 16 q + l / 4,
-    // stored chunk l % 4, which holds the row's logical chunk (l % 4) ^ ((r >> 2) & 3).
+    // DMA mapping: instruction i of wave w fills slab rows kRowsPerDma q ..,
+    // q = kLmWaves i + w; lane l writes 16 bytes at 16 l, i.e. row
+    // kRowsPerDma q + l / kChunks, stored chunk l % kChunks, which holds the
+    // row's logical chunk swz(r, l % kChunks) (the swizzle is an involution).
     // Offsets are 32-bit 16-byte-chunk counts; rows past M or V read the last row.
-    int ga[4], gb[4];
+    int ga[kDmaPerOperand], gb[kDmaPerOperand];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = 16 * (4 * i + w) + (lane >> 2);
-        const int c = (lane & 3) ^ ((r >> 2) & 3);
+    for (int i = 0; i < kDmaPerOperand; ++i) {
+        const int r = kRowsPerDma * (kLmWaves * i + w) + lane / kChunks;
+        const int c = swz(r, lane % kChunks);
         ga[i] = min(m0 + r, M - 1) * dv + c;
         gb[i] = min(n0 + r, V - 1) * dv + c;
     }
@@ -91,17 +109,16 @@ __global__ __launch_bounds__(kBlock, 1) void k_lmhead_argmax(const uint4 *__rest
         constexpr int S = decltype(slot)::value;
         const int k0 = step * (kTK / 8);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            __builtin_amdgcn_global_load_lds(H + ga[i] + k0, (SV_LDS void *)(slab_a<S>() + (4 * i + w) * 1024),
-                                             16, 0, 0);
-            __builtin_amdgcn_global_load_lds(W + gb[i] + k0, (SV_LDS void *)(slab_b<S>() + (4 * i + w) * 1024),
-                                             16, 0, 0);
+        for (int i = 0; i < kDmaPerOperand; ++i) {
+            const int q = kLmWaves * i + w;
+            __builtin_amdgcn_global_load_lds(H + ga[i] + k0, (SV_LDS void *)(slab_a<S>() + q * 1024), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(W + gb[i] + k0, (SV_LDS void *)(slab_b<S>() + q * 1024), 16, 0, 0);
         }
     };
 
-    f32x16 acc[4][4];
+    f32x16 acc[kTilesA][4];
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < kTilesA; ++a)
 #pragma unroll
         for (int b = 0; b < 4; ++b) acc[a][b] = f32x16{};
 
@@ -110,17 +127,20 @@ __global__ __launch_bounds__(kBlock, 1) void k_lmhead_argmax(const uint4 *__rest
         constexpr int S = decltype(slot)::value;
 #pragma unroll
         for (int kk = 0; kk < kTK / 16; ++kk) {
-            bf16x8 af[4], bfr[4];
+            bf16x8 af[kTilesA], bfr[4];
             const int c = kk * 2 + (lane >> 5);
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const int ra = wm * 128 + t * 32 + (lane & 31);
-                const int rb = wn * 128 + t * 32 + (lane & 31);
-                af[t] = *reinterpret_cast<const bf16x8 *>(slab_a<S>() + ra * 64 + ((c ^ ((ra >> 2) & 3)) << 4));
-                bfr[t] = *reinterpret_cast<const bf16x8 *>(slab_b<S>() + rb * 64 + ((c ^ ((rb >> 2) & 3)) << 4));
+            for (int t = 0; t < kTilesA; ++t) {
+                const int ra = wm * (kTilesA * 32) + t * 32 + (lane & 31);
+                af[t] = *reinterpret_cast<const bf16x8 *>(slab_a<S>() + ra * kRowB + (swz(ra, c) << 4));
             }
 #pragma unroll
-            for (int a = 0; a < 4; ++a)
+            for (int t = 0; t < 4; ++t) {
+                const int rb = wn * 128 + t * 32 + (lane & 31);
+                bfr[t] = *reinterpret_cast<const bf16x8 *>(slab_b<S>() + rb * kRowB + (swz(rb, c) << 4));
+            }
+#pragma unroll
+            for (int a = 0; a < kTilesA; ++a)
 #pragma unroll
                 for (int b = 0; b < 4; ++b)
                     acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a], bfr[b], acc[a][b], 0, 0, 0);
@@ -131,15 +151,16 @@ __global__ __launch_bounds__(kBlock, 1) void k_lmhead_argmax(const uint4 *__rest
     issue(Slot<0>{}, 0);
     issue(Slot<1>{}, 1);
     issue(Slot<2>{}, 2);
-    // step s: its loads are done once at most the 2 later steps' loads are
-    // outstanding; the barrier then also means every wave has finished step
-    // s - 1, whose slot the loads of step s + 3 reuse (past the end, the last
-    // step is loaded again into a slot nobody reads)
+    // step s: its loads are done once at most the kStages - 2 later steps'
+    // loads are outstanding; the barrier then also means every wave has
+    // finished step s - 1, whose slot the loads of step s + kStages - 1 reuse
+    // (past the end, the last step is loaded again into a slot nobody reads)
 #define SV_STEP(S)                                                            \
-    wait_vm<2 * kLoadsPerStep>();                                             \
+    wait_vm<(kStages - 2) * kLoadsPerStep>();                                 \
     __builtin_amdgcn_s_barrier();                                             \
-    issue(Slot<(S + 3) % kStages>{}, min(s + S + 3, nk - 1));                  \
+    issue(Slot<(S + kStages - 1) % kStages>{}, min(s + S + kStages - 1, nk - 1)); \
     compute(Slot<S>{});
+    // no branches inside the ring (a branch makes the compiler wait for every load)
     for (int s = 0; s < nk; s += kStages) {
         SV_STEP(0)
         SV_STEP(1)
@@ -154,7 +175,7 @@ __global__ __launch_bounds__(kBlock, 1) void k_lmhead_argmax(const uint4 *__rest
     if (seg >= segs) return;
     const int cbase = n0 + wn * 128 + (lane & 31);
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
+    for (int a = 0; a < kTilesA; ++a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             float best = -__builtin_huge_valf();
@@ -174,7 +195,7 @@ __global__ __launch_bounds__(kBlock, 1) void k_lmhead_argmax(const uint4 *__rest
                 const uint64_t y = __shfl_xor(key, o, kWave);
                 key = y > key ? y : key;
             }
-            const int row = m0 + wm * 128 + a * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+            const int row = m0 + wm * (kTilesA * 32) + a * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
             if ((lane & 31) == 0 && row < M) part_k[static_cast<long long>(row) * segs + seg] = key;
         }
     }
@@ -189,7 +210,7 @@ hipError_t launch_lmhead_argmax(const void *H, const void *W, int M, int D, int 
     const int mtiles = (M + kTM - 1) / kTM;
     const int ntiles = (V + kTN - 1) / kTN;
     const long long blocks = static_cast<long long>(kXcds) * mtiles * ((ntiles + kXcds - 1) / kXcds);
-    return launch_kernel(k_lmhead_argmax, dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0, s,
+    return launch_kernel(k_lmhead_argmax, dim3(static_cast<unsigned>(blocks)), dim3(kLmThreads), 0, s,
                          static_cast<const uint4 *>(H), static_cast<const uint4 *>(W), M, D, V, mtiles,
                          ntiles, part_k, lmhead_segs(V));
 }
