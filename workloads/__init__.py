@@ -400,3 +400,57 @@ def make_tree_lmhead(B, D, V, exact=True, p_match=0.7, n_main=8, n_branch=12, ma
     return Workload(mode="tree_lmhead", B=B, N=N, V=V, dtype="bf16", node_tokens=tok,
                     parents=parents.astype(np.int32), hidden=Hb.reshape(B, N, D), lm_head=Wb,
                     meta=dict(D=D, exact=exact, p_match=p_match))
+
+
+# ---- token streams for lexical retrieval --------------------------------------
+#
+# AdaPLD reuses spans of its own context (prompt plus generated text), which in
+# agent and code workloads repeats heavily.  These streams imitate that: each
+# request's context is built from segments that either copy an earlier span
+# of the same context (probability p_copy, 8..64 tokens) or draw fresh tokens
+# from a Zipf-like distribution over a working vocabulary of `working` ids
+# spread over the full vocabulary.  The query is the last n tokens of the
+# context (the current prefix's tail), so the self-match at the end is
+# excluded by the retrieval's own rule (no continuation).
+
+NGRAM_SHAPE = dict(B=256, L=32768, n=3, cap=64)
+
+
+def make_ngram(B, L, n, lengths=None, p_copy=0.3, p_tail_copy=0.6, working=4000, V=VOCAB_QWEN3,
+               seed=0) -> dict:
+    """Token streams [B, L] with lengths [B] and queries [B, n] (see above).  The
+    last segment of a context is a copy with probability p_tail_copy, so the
+    query tail often occurs earlier, as when generation repeats its context."""
+    ss = seed if isinstance(seed, np.random.SeedSequence) else np.random.SeedSequence(seed)
+    seeds = ss.spawn(B + 1)
+    rng0 = np.random.default_rng(seeds[B])
+    if lengths is None:
+        lengths = rng0.integers(L // 4, L + 1, size=B)
+    lengths = np.asarray(lengths, dtype=np.int32)
+    ids = rng0.choice(V, size=working, replace=False).astype(np.int32)
+    zipf = 1.0 / np.arange(1, working + 1)
+    zipf /= zipf.sum()
+    ctx = np.zeros((B, L), dtype=np.int32)
+
+    def job(b):
+        rng = np.random.default_rng(seeds[b])
+        ln = int(lengths[b])
+        row = ctx[b]
+        t = 0
+        tail_copy = rng.random() < p_tail_copy
+        while t < ln:
+            seg = int(rng.integers(8, 65))
+            seg = min(seg, ln - t)
+            last = t + seg >= ln
+            if t > 64 and ((last and tail_copy) or rng.random() < p_copy):
+                src = int(rng.integers(0, t - seg)) if t - seg > 0 else 0
+                row[t:t + seg] = row[src:src + seg]
+            else:
+                row[t:t + seg] = ids[rng.choice(working, size=seg, p=zipf)]
+            t += seg
+
+    with ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(job, range(B)))
+    q = np.stack([ctx[b, max(0, lengths[b] - n):lengths[b]] if lengths[b] >= n
+                  else np.zeros(n, np.int32) for b in range(B)]).astype(np.int32)
+    return dict(context=ctx, lengths=lengths, queries=q, n=n)
