@@ -50,6 +50,9 @@ KERNEL_SOURCES = {
     "lmhead": ["draft_token_verification_04_amd/csrc/sv_lmhead.hip",
                "draft_token_verification_04_amd/csrc/sv_device.hpp",
                "draft_token_verification_04_amd/csrc/sv_internal.hpp"],
+    "ngram": ["draft_token_verification_04_amd/csrc/sv_ngram.hip",
+              "draft_token_verification_04_amd/csrc/sv_device.hpp",
+              "draft_token_verification_04_amd/csrc/sv_internal.hpp"],
     "commit": ["draft_token_verification_04_amd/csrc/sv_commit.hip",
                "draft_token_verification_04_amd/csrc/sv_device.hpp",
                "draft_token_verification_04_amd/csrc/sv_internal.hpp"],
@@ -196,6 +199,59 @@ def cpu_baseline(w3, w4, w5, mode, threads):
             oracle.verify_tree(w5.target, w5.node_tokens, w5.parents, threads=threads)
         times.append(time.perf_counter() - t0)
     return statistics.median(times)
+
+
+def bench_ngram(sv, torch, workloads, dev, reps):
+    """spec_ngram_candidates on seeded repetitive token streams (B=256, up to
+    L=32768 tokens, 3-gram queries, 64 positions kept)."""
+    shp = workloads.NGRAM_SHAPE
+    B, L, n, cap = shp["B"], shp["L"], shp["n"], shp["cap"]
+    w = workloads.make_ngram(B, L, n, seed=20261207)
+    ctx = torch.from_numpy(w["context"]).to(dev)
+    lens = torch.from_numpy(w["lengths"]).to(dev)
+    q = torch.from_numpy(w["queries"]).to(dev)
+    lib = sv.load_library()
+    ws = torch.empty(lib.sv_ngram_workspace_bytes(B, L), dtype=torch.uint8, device=dev)
+    cnt = torch.empty(B, dtype=torch.int32, device=dev)
+    pos = torch.empty((B, cap), dtype=torch.int32, device=dev)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    args = (P(ctx), B, L, P(lens), P(q), n, cap, P(cnt), P(pos), None, P(ws), ws.numel(),
+            ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream))
+
+    def call():
+        rc = lib.spec_ngram_candidates(*args)
+        if rc:
+            raise RuntimeError(f"spec_ngram_candidates failed: {rc}")
+
+    for _ in range(5):
+        call()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        call()
+    torch.cuda.synchronize()
+    call_ms = (time.perf_counter() - t0) * 1e3 / reps
+    sv.trace_begin(4 * reps + 16, kernels=("ngram_count", "ngram_emit"))
+    for _ in range(reps):
+        call()
+    torch.cuda.synchronize()
+    per = {}
+    for name, ms in sv.trace_end(4 * reps + 16):
+        per.setdefault(name, []).append(ms)
+    tokens = int(w["lengths"].sum())
+    nbytes = tokens * 4  # every token read once
+    kc, ke = statistics.mean(per["ngram_count"]), statistics.mean(per["ngram_emit"])
+    return {
+        "workload": f"AdaPLD lexical retrieval: B={B} token streams of {L // 4}..{L} tokens, {n}-gram queries, "
+                    f"first {cap} candidates kept",
+        "tokens": tokens, "bytes": nbytes, "call_ms": round(call_ms, 5),
+        "count_ms": round(kc, 5), "emit_ms": round(ke, 5),
+        "mean_candidates": round(float(cnt.float().mean().item()), 3),
+        "roofline": {"bound": "hbm", "kernel": "ngram_count", "achieved": round(nbytes / (kc * 1e-3) / 1e9, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(nbytes / (kc * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                     "traffic": (stored_traffic("ngram") or {}).get("bytes_per_launch")},
+    }
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, vendor figure
@@ -481,6 +537,10 @@ def main():
                          "frac": round(moved / (kms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
                          "traffic": (stored_traffic("commit") or {}).get("bytes_per_launch")}}
         del kv
+
+    # AdaPLD lexical retrieval over 256 token streams of up to 32K tokens
+    if "tree" in active:
+        extras["ngram_candidates"] = bench_ngram(sv, torch, workloads, dev, reps)
 
     # the greedy chain with the LM-head projection fused in (hidden states in,
     # logits never written), at the Qwen3-8B shape B=256 K=7 D=4096 V=151936

@@ -27,12 +27,12 @@ SV_OK, SV_ERR_INVALID_ARG, SV_ERR_UNSUPPORTED, SV_ERR_WORKSPACE, SV_ERR_HIP = ra
 SV_F32, SV_BF16 = 0, 1
 SV_MAX_TREE_NODES = 2048
 KERNELS = ("rowstats", "accept", "resid_mass", "resid_select", "argmax", "match", "tree",
-           "skip_stats", "skip_argmax", "commit", "lmhead")
+           "skip_stats", "skip_argmax", "commit", "lmhead", "ngram_count", "ngram_emit")
 
 EXPORTS = ("sv_sample_workspace_bytes", "sv_greedy_workspace_bytes", "spec_verify_sample",
            "spec_verify_greedy", "spec_verify_tree", "spec_commit_tree_kv", "sv_status_string",
            "sv_version", "sv_lmhead_workspace_bytes", "spec_verify_greedy_lmhead",
-           "spec_verify_tree_lmhead",
+           "spec_verify_tree_lmhead", "sv_ngram_workspace_bytes", "spec_ngram_candidates",
            "sv_trace_begin", "sv_trace_end", "sv_kernel_name")
 
 
@@ -70,6 +70,10 @@ def load_library(path: str = LIB_PATH):
     lib.spec_verify_tree.restype = I
     lib.spec_commit_tree_kv.argtypes = [P, P, I, I, I, I, P, P, P, P, I, P, P]
     lib.spec_commit_tree_kv.restype = I
+    lib.sv_ngram_workspace_bytes.argtypes = [I, I]
+    lib.sv_ngram_workspace_bytes.restype = Z
+    lib.spec_ngram_candidates.argtypes = [P, I, I, P, P, I, I, P, P, P, P, Z, P]
+    lib.spec_ngram_candidates.restype = I
     lib.sv_lmhead_workspace_bytes.argtypes = [I, I]
     lib.sv_lmhead_workspace_bytes.restype = Z
     lib.spec_verify_greedy_lmhead.argtypes = [P, P, P, I, I, I, I, P, P, P, P, Z, P]
@@ -341,6 +345,35 @@ def spec_verify_tree_lmhead(hidden, lm_head, node_tokens, parents, *, status=Tru
             _ptr(ws), ws.numel() * ws.element_size(), _stream(torch, dev, stream))
     if rc != SV_OK:
         raise SpecVerifyError(rc, "spec_verify_tree_lmhead")
+    return out
+
+
+def spec_ngram_candidates(context, lengths, queries, cap, *, status=True, workspace=None, stream=None):
+    """AdaPLD lexical retrieval: context [B, L], lengths [B], queries [B, n]
+    (int32 GPU tensors).  Returns ``count`` [B], ``positions`` [B, cap]
+    (ascending, -1 padded) and ``status`` [B]."""
+    torch = _torch()
+    lib = load_library()
+    _check(context, "context", 2, torch.int32)
+    dev = context.device
+    B, L = context.shape
+    _check(lengths, "lengths", 1, torch.int32, dev)
+    _check(queries, "queries", 2, torch.int32, dev)
+    if lengths.shape[0] != B or queries.shape[0] != B:
+        raise ValueError("lengths and queries must have B rows")
+    n = queries.shape[1]
+    out = dict(count=torch.empty(B, dtype=torch.int32, device=dev),
+               positions=torch.empty((B, cap), dtype=torch.int32, device=dev))
+    if status:
+        out["status"] = torch.empty(B, dtype=torch.int32, device=dev)
+    ws = _workspace(torch, lib.sv_ngram_workspace_bytes(B, L), dev, workspace)
+    with torch.cuda.device(dev):
+        rc = lib.spec_ngram_candidates(_ptr(context), B, L, _ptr(lengths), _ptr(queries), n, cap,
+                                       _ptr(out["count"]), _ptr(out["positions"]) if cap else None,
+                                       _ptr(out.get("status")), _ptr(ws), ws.numel() * ws.element_size(),
+                                       _stream(torch, dev, stream))
+    if rc != SV_OK:
+        raise SpecVerifyError(rc, "spec_ngram_candidates")
     return out
 
 

@@ -11,7 +11,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libspecverify.so")
-SOURCES = ["sv_api.hip", "sv_sample.hip", "sv_greedy.hip", "sv_commit.hip", "sv_lmhead.hip"]
+SOURCES = ["sv_api.hip", "sv_sample.hip", "sv_greedy.hip", "sv_commit.hip", "sv_lmhead.hip",
+           "sv_ngram.hip"]
 ARCH = "gfx950"
 
 

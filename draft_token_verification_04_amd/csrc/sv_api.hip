@@ -371,6 +371,30 @@ sv_status spec_verify_tree_lmhead(const void *hidden, const void *lm_head,
     return e == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 
+// ---- AdaPLD lexical retrieval ----------------------------------------------------
+
+size_t sv_ngram_workspace_bytes(int B, int L) {
+    if (B < 0 || L < 1) return 0;
+    return align_up(static_cast<size_t>(B) * static_cast<size_t>(ngram_chunks(L)) * sizeof(int32_t));
+}
+
+sv_status spec_ngram_candidates(const int32_t *context, int B, int L, const int32_t *lengths,
+                                const int32_t *queries, int n, int cap, int32_t *count,
+                                int32_t *positions, int32_t *req_status, void *workspace,
+                                size_t workspace_bytes, void *stream) {
+    if (B < 0 || L < 1 || n < 1 || cap < 0) return SV_ERR_INVALID_ARG;
+    if (n > 64 || static_cast<long long>(B) * ngram_chunks(L) > 0x7fffffffLL) return SV_ERR_UNSUPPORTED;
+    if (B == 0) return SV_OK;
+    if (!context || !lengths || !queries || !count || (cap > 0 && !positions) || !workspace)
+        return SV_ERR_INVALID_ARG;
+    if (!aligned256(workspace)) return SV_ERR_INVALID_ARG;
+    if (workspace_bytes < sv_ngram_workspace_bytes(B, L)) return SV_ERR_WORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const hipError_t e = launch_ngram(context, B, L, lengths, queries, n, cap, static_cast<int32_t *>(workspace),
+                                      count, positions, req_status, s);
+    return e == hipSuccess ? SV_OK : SV_ERR_HIP;
+}
+
 sv_status spec_commit_tree_kv(const void *src_kv, void *dst_kv, int G, int B, int S, int row_bytes,
                               const int32_t *tree_base, const int32_t *commit_base,
                               const int32_t *accept_len, const int32_t *path_nodes, int N,
@@ -410,7 +434,8 @@ const char *sv_version(void) { return "specverify 0.1.0 (gfx950)"; }
 const char *sv_kernel_name(int k) {
     static const char *names[SV_K_COUNT] = {"rowstats", "accept", "resid_mass", "resid_select",
                                             "argmax", "match", "tree", "skip_stats",
-                                            "skip_argmax", "commit", "lmhead"};
+                                            "skip_argmax", "commit", "lmhead", "ngram_count",
+                                            "ngram_emit"};
     return (k >= 0 && k < SV_K_COUNT) ? names[k] : "unknown";
 }
 

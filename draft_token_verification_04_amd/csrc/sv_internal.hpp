@@ -150,6 +150,10 @@ hipError_t launch_skip_match(const void *L, const int32_t *drafts, int B, int K,
                              const RowGeom &g, sv_dtype dt, uint64_t *part_k, int32_t *amax,
                              void *ctl_base, int32_t *accept_len, int32_t *out_tokens,
                              int32_t *status, hipStream_t s);
+int ngram_chunks(int L);
+hipError_t launch_ngram(const int32_t *ctx, int B, int L, const int32_t *lens, const int32_t *queries,
+                        int n, int cap, int32_t *counts, int32_t *count, int32_t *positions,
+                        int32_t *status, hipStream_t s);
 int lmhead_segs(int V);
 hipError_t launch_lmhead_argmax(const void *H, const void *W, int M, int D, int V, uint64_t *part_k,
                                 hipStream_t s);

@@ -228,6 +228,31 @@ sv_status spec_commit_tree_kv(const void *src_kv, void *dst_kv, int G, int B, in
                               const int32_t *accept_len, const int32_t *path_nodes, int N,
                               int32_t *req_status, void *stream);
 
+/*
+ * AdaPLD lexical retrieval (AdaPLD page, section 3.2 and Algorithm 1,
+ * LexicalRetrieval): the positions of each request's reuse context where the
+ * last n tokens of its current prefix occur, each with at least one token
+ * after it to copy as a draft.
+ *
+ *   context   [B][L] int32 token ids; request b uses its first lengths[b].
+ *   lengths   [B] int32 (device).
+ *   queries   [B][n] int32: the last n tokens of each prefix (query[n-1] is
+ *             the newest token), 1 <= n <= 64.
+ *   count     [B] int32: number of candidates p, n-1 <= p <= lengths[b]-2,
+ *             with context[b][p-k] == queries[b][n-1-k] for every k < n.
+ *   positions [B][cap] int32: the first min(count, cap) candidates in
+ *             ascending order, then -1 (may be NULL when cap == 0).
+ *   req_status [B] optional: 0, or 1 if lengths[b] is outside [0, L] (then
+ *             count 0).
+ * Workspace: sv_ngram_workspace_bytes(B, L).
+ */
+size_t sv_ngram_workspace_bytes(int B, int L);
+
+sv_status spec_ngram_candidates(const int32_t *context, int B, int L, const int32_t *lengths,
+                                const int32_t *queries, int n, int cap, int32_t *count,
+                                int32_t *positions, int32_t *req_status, void *workspace,
+                                size_t workspace_bytes, void *stream);
+
 /* Human-readable name of a status code (static storage). */
 const char *sv_status_string(sv_status s);
 
@@ -262,7 +287,9 @@ typedef enum {
     SV_K_SKIP_ARGMAX = 8,  /* row argmax + greedy chain acceptance, skipping rows after a mismatch */
     SV_K_COMMIT = 9,       /* KV rows of accepted tree paths moved to consecutive slots */
     SV_K_LMHEAD = 10,      /* LM-head projection on the matrix cores + row argmax partials */
-    SV_K_COUNT = 11
+    SV_K_NGRAM_COUNT = 11, /* lexical retrieval: candidates per chunk */
+    SV_K_NGRAM_EMIT = 12,  /* lexical retrieval: candidate positions in order */
+    SV_K_COUNT = 13
 } sv_kernel_id;
 
 sv_status sv_trace_begin(int capacity, unsigned kernel_mask);

@@ -169,3 +169,20 @@ def test_lmhead_argument_checks(lib):
     assert chain(B=0) == sv.SV_OK
     assert lib.sv_lmhead_workspace_bytes(2048, 151936) == 2048 * 1187 * 8
     assert lib.sv_lmhead_workspace_bytes(0, 10) == 0
+
+
+def test_ngram_argument_checks(lib):
+    def call(**kw):
+        a = dict(c=FAKE, B=2, L=100, ln=FAKE, q=FAKE, n=3, cap=4, cnt=FAKE, pos=FAKE, st=None, ws=FAKE,
+                 wsb=1 << 20, s=None)
+        a.update(kw)
+        return lib.spec_ngram_candidates(a["c"], a["B"], a["L"], a["ln"], a["q"], a["n"], a["cap"], a["cnt"],
+                                         a["pos"], a["st"], a["ws"], a["wsb"], a["s"])
+    assert call(n=0) == sv.SV_ERR_INVALID_ARG
+    assert call(n=65) == sv.SV_ERR_UNSUPPORTED
+    assert call(L=0) == sv.SV_ERR_INVALID_ARG
+    assert call(cap=-1) == sv.SV_ERR_INVALID_ARG
+    assert call(pos=None) == sv.SV_ERR_INVALID_ARG
+    assert call(wsb=0) == sv.SV_ERR_WORKSPACE
+    assert call(B=0) == sv.SV_OK
+    assert lib.sv_ngram_workspace_bytes(256, 32768) == 256 * 32 * 4
