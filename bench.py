@@ -56,6 +56,10 @@ KERNEL_SOURCES = {
     "commit": ["draft_token_verification_04_amd/csrc/sv_commit.hip",
                "draft_token_verification_04_amd/csrc/sv_device.hpp",
                "draft_token_verification_04_amd/csrc/sv_internal.hpp"],
+    "skip_tree": ["draft_token_verification_04_amd/csrc/sv_greedy.hip",
+                  "draft_token_verification_04_amd/csrc/sv_skip.hpp",
+                  "draft_token_verification_04_amd/csrc/sv_device.hpp",
+                  "draft_token_verification_04_amd/csrc/sv_internal.hpp"],
     "skip_argmax": ["draft_token_verification_04_amd/csrc/sv_greedy.hip",
                     "draft_token_verification_04_amd/csrc/sv_skip.hpp",
                     "draft_token_verification_04_amd/csrc/sv_device.hpp",
@@ -181,6 +185,23 @@ class Calls:
         rc = self.lib.spec_verify_tree(*self.tree_args)
         if rc:
             raise RuntimeError(f"spec_verify_tree failed: {rc}")
+
+
+def tree_needed_rows(torch, target, w5):
+    """Rows a tree verification must read: the root's and every accepted node's
+    (row argmax by torch.argmax, first maximum on ties; for reporting only)."""
+    import numpy as np
+
+    a = torch.argmax(target.float(), dim=-1).cpu().numpy()
+    par, tok = w5.parents, w5.node_tokens
+    rows = 0
+    for b in range(w5.B):
+        ok = np.zeros(w5.N, bool)
+        ok[0] = True
+        for j in range(1, w5.N):
+            ok[j] = ok[par[b, j]] and tok[b, j] == a[b, par[b, j]]
+        rows += int(ok.sum())
+    return rows
 
 
 def cpu_baseline(w3, w4, w5, mode, threads):
@@ -386,7 +407,7 @@ def main():
         step()
     torch.cuda.synchronize()
     # timed region: events only around the streaming kernels the rooflines are quoted on
-    timed_kernels = ("rowstats", "argmax", "skip_argmax")
+    timed_kernels = ("rowstats", "skip_argmax", "skip_tree")
     sv.trace_begin(max(64, args.steps * 4 + 16), kernels=timed_kernels)
     t0 = time.perf_counter()
     for _ in range(args.steps):
@@ -415,15 +436,16 @@ def main():
     n4 = calls.g_n.cpu().numpy()
     resid_rows = int(np.sum(np.where(n3 < w3.K, 2, 1)))
     # algorithmic bytes: the stochastic chain with lse outputs reads every row once
-    # plus the drawn row (pair); the greedy chain needs rows 0..n_b of each request
+    # plus the drawn row (pair); the greedy chain needs rows 0..n_b of each request;
+    # the tree needs the rows of the root and of every accepted node
     bytes_mode = {
         "sample": (w3.B * (2 * w3.K + 1) + resid_rows) * R,
         "greedy": int(np.sum(n4 + 1)) * R,
-        "tree": w5.B * w5.N * R,
+        "tree": tree_needed_rows(torch, calls.t_t, w5) * R,
     }
     rows_mode = {"sample": w3.B * (w3.K + 1), "greedy": w4.B * (w4.K + 1), "tree": w5.B * w5.N}
     kernels_mode = {"sample": ["rowstats", "accept", "resid_mass", "resid_select"],
-                    "greedy": ["skip_argmax"], "tree": ["argmax", "tree"]}
+                    "greedy": ["skip_argmax"], "tree": ["skip_tree"]}
     rows_step = sum(rows_mode[m] for m in active)
     bytes_step = sum(bytes_mode[m] for m in active)
     value = rows_step / (ms_per_step * 1e-3)
@@ -444,12 +466,13 @@ def main():
     if "sample" in active:
         roof = roofline("rowstats", w3.B * (2 * w3.K + 1) * R, "stochastic chain B=256 K=7")
     if "tree" in active:
-        others["argmax"] = roofline("argmax", bytes_mode["tree"], "greedy tree B=64 N=33")
+        others["skip_tree"] = roofline("skip_tree", bytes_mode["tree"],
+                                       "greedy tree B=64 N=33 (rows of the root and accepted nodes)")
     if "greedy" in active:
         others["skip_argmax"] = roofline("skip_argmax", bytes_mode["greedy"],
                                          "greedy chain B=256 K=7 (rows 0..n_b per request)")
     if "sample" not in active:
-        roof = others.pop("argmax" if "tree" in active else "skip_argmax")
+        roof = others.pop("skip_tree" if "tree" in active else "skip_argmax")
 
     modes = {}
     for m in active:
@@ -461,6 +484,8 @@ def main():
         modes["sample"]["mean_tokens_per_round"] = round(float(n3.mean() + 1), 4)
     if "greedy" in modes:
         modes["greedy"]["mean_tokens_per_round"] = round(float(n4.mean() + 1), 4)
+    if "tree" in modes:
+        modes["tree"]["dense_bytes"] = w5.B * w5.N * R
         modes["greedy"]["dense_bytes"] = w4.B * (w4.K + 1) * R
 
     # each call on its own, back to back (launch gaps included)

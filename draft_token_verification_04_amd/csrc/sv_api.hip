@@ -60,8 +60,10 @@ int resid_tiles_per_wave(int B, int ntiles) {
 
 GreedyWs greedy_ws_layout(int B, int rows_per_req, const RowGeom &g) {
     GreedyWs w;
-    // chains short enough for row skipping also hold that pass's keys and control words
-    const bool skip = skip_supported(rows_per_req - 1);
+    // requests short enough for a row-skipping pass (chains of K <= 31, trees
+    // of N <= 64) also hold that pass's keys, per-row argmax and control words
+    const bool chain = skip_supported(rows_per_req - 1), tree = tree_skip_supported(rows_per_req);
+    const bool skip = chain || tree;
     const int skip_segs = skip ? row_geom(g.nvec * g.per_vec, g.per_vec == 8 ? SV_BF16 : SV_F32, true,
                                           kGSkipVecsPerLane * kGSkipChunks).segs
                                : 0;
@@ -72,7 +74,9 @@ GreedyWs greedy_ws_layout(int B, int rows_per_req, const RowGeom &g) {
     w.amax = o;
     if (skip) o = align_up(o + rows * sizeof(int32_t));
     w.skipctl = o;
-    if (skip) o = align_up(o + skip_ctl_bytes(B, rows_per_req - 1));
+    const size_t ctl = std::max(chain ? skip_ctl_bytes(B, rows_per_req - 1) : 0,
+                                tree ? tree_ctl_bytes(B, rows_per_req) : 0);
+    if (skip) o = align_up(o + ctl);
     w.total = o;
     return w;
 }
@@ -283,14 +287,24 @@ sv_status spec_verify_tree(const void *target_logits, const int32_t *node_tokens
     const long long rows = static_cast<long long>(B) * N;
     const GreedyWs L = greedy_ws_layout(B, N, g);
     if (workspace_bytes < L.total) return SV_ERR_WORKSPACE;
-    uint64_t *pk = reinterpret_cast<uint64_t *>(static_cast<char *>(workspace) + L.part_k);
+    char *ws = static_cast<char *>(workspace);
+    uint64_t *pk = reinterpret_cast<uint64_t *>(ws + L.part_k);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = traced(SV_K_ARGMAX, s, [&] { return launch_argmax(target_logits, rows, V, g, dt, pk, s); });
-    if (e == hipSuccess)
-        e = traced(SV_K_TREE, s, [&] {
-            return launch_tree(pk, node_tokens, parents, B, N, V, g, accept_len, path_nodes,
-                               out_tokens, req_status, s);
-        });
+    hipError_t e = hipSuccess;
+    if (SV_GREEDY_SKIP && tree_skip_supported(N)) {
+        // rows of rejected nodes are not read
+        const RowGeom gs = row_geom(V, dt, aligned16(target_logits), kGSkipVecsPerLane * kGSkipChunks);
+        e = launch_skip_tree(target_logits, node_tokens, parents, B, N, V, gs, dt, pk,
+                             reinterpret_cast<int32_t *>(ws + L.amax), ws + L.skipctl, accept_len, path_nodes,
+                             out_tokens, req_status, s);
+    } else {
+        e = traced(SV_K_ARGMAX, s, [&] { return launch_argmax(target_logits, rows, V, g, dt, pk, s); });
+        if (e == hipSuccess)
+            e = traced(SV_K_TREE, s, [&] {
+                return launch_tree(pk, node_tokens, parents, B, N, V, g, accept_len, path_nodes,
+                                   out_tokens, req_status, s);
+            });
+    }
     return e == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 
@@ -435,7 +449,7 @@ const char *sv_kernel_name(int k) {
     static const char *names[SV_K_COUNT] = {"rowstats", "accept", "resid_mass", "resid_select",
                                             "argmax", "match", "tree", "skip_stats",
                                             "skip_argmax", "commit", "lmhead", "ngram_count",
-                                            "ngram_emit"};
+                                            "ngram_emit", "skip_tree"};
     return (k >= 0 && k < SV_K_COUNT) ? names[k] : "unknown";
 }
 

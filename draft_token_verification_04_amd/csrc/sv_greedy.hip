@@ -368,6 +368,181 @@ __global__ __launch_bounds__(kBlock) void k_skip_argmax(const typename E::storag
     skip_finished(ctl, b, lane);
 }
 
+// ---- trees: rows of rejected nodes are not read (N <= 64) ------------------------
+//
+// A node's row is needed only when the node is accepted: its argmax decides its
+// children and, for the chosen node, the bonus.  One launch over every (node j,
+// request b, segment) in node order (parents come before children).  A wave
+// skips its segment when node j is already known rejected.  The last wave of a
+// row (found by a ticket) takes its argmax a_j, marks the row done, and
+// rejects every child whose token differs from a_j together with the
+// descendants of every rejected node (parents, tokens and states of the
+// request's nodes held one per lane, the rejection closed over the tree by
+// ballots).  Each node is resolved once - row done or rejected, whichever is
+// first - and counted; the wave whose count completes the request's N nodes
+// walks the tree (every node that is not rejected has its row's argmax) and
+// writes the outputs, exactly as the full-read walk would.  Nothing waits.
+
+constexpr unsigned kRowDone = 1u, kRejected = 2u;
+constexpr int kTreeSkipMaxN = kWave;
+
+struct TreeCtl {
+    unsigned *ticket;    // [B*N] segments finished per node row
+    unsigned *state;     // [B*N] kRowDone | kRejected
+    unsigned *resolved;  // [B] nodes resolved
+};
+
+// Node j's outputs of request b once every node is resolved (one wave).
+__device__ __forceinline__ void tree_finish(const int32_t *__restrict__ tok, const int32_t *__restrict__ par,
+                                            const int32_t *amax, const TreeCtl &ctl, int b, int N, int V,
+                                            int32_t *__restrict__ accept_len, int32_t *__restrict__ path_nodes,
+                                            int32_t *__restrict__ out_tokens, int32_t *__restrict__ status,
+                                            int lane) {
+    const long long base = static_cast<long long>(b) * N;
+    const bool in = lane < N;
+    const int p = in ? par[base + lane] : 0;
+    const int t = in ? tok[base + lane] : 0;
+    const unsigned st = in ? shared_load(&ctl.state[base + lane]) : 0u;
+    const int a = in && (st & kRowDone) ? shared_load(const_cast<int32_t *>(&amax[base + lane])) : -1;
+    const bool bad_par = ballot(in && (lane == 0 ? p != -1 : (p < 0 || p >= lane))) != 0;
+    const bool oor = ballot(in && lane > 0 && (t < 0 || t >= V)) != 0;
+    if (bad_par) {
+        for (int k = lane; k < N; k += kWave) {
+            path_nodes[base + k] = -1;
+            out_tokens[base + k] = -1;
+        }
+        if (lane == 0) {
+            accept_len[b] = -1;
+            if (status) status[b] = 2;
+        }
+        return;
+    }
+    // acceptance and depth by pointer jumping over the lanes
+    const int pa = __shfl(a, lane == 0 ? 0 : p, kWave);  // argmax of the parent's row
+    bool ok = lane == 0 ? true : (in && t == pa && pa >= 0);
+    int dep = lane == 0 ? 0 : 1;
+    int anc = lane == 0 ? 0 : p;
+    for (int span = 1; span < N; span <<= 1) {
+        const bool ok2 = __shfl(ok ? 1 : 0, anc, kWave) != 0;
+        const int d2 = __shfl(dep, anc, kWave);
+        const int a2 = __shfl(anc, anc, kWave);
+        ok = ok && ok2;
+        dep += d2;
+        anc = a2;
+    }
+    // deepest accepted node, lowest index among equals (the root qualifies)
+    const unsigned key = in && ok ? ((static_cast<unsigned>(dep) << 16) | (0xffffu - static_cast<unsigned>(lane))) : 0u;
+    unsigned mk = key;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const unsigned y = static_cast<unsigned>(__shfl_xor(static_cast<int>(mk), o, kWave));
+        mk = y > mk ? y : mk;
+    }
+    const int best = static_cast<int>(0xffffu - (uniform(mk) & 0xffffu));
+    const int d = static_cast<int>(uniform(mk) >> 16);
+    // the path: lane k (k < d) holds the ancestor of `best` at depth k + 1
+    int node = best, walked = d;
+    int mine = -1;
+    while (walked > 0) {  // uniform: every lane walks the same chain
+        if (lane == walked - 1) mine = node;
+        node = __shfl(p, node, kWave);
+        --walked;
+    }
+    const int mine_tok = __shfl(t, mine < 0 ? 0 : mine, kWave);
+    const int bonus = __shfl(a, best, kWave);
+    for (int k = lane; k < N; k += kWave) {
+        path_nodes[base + k] = k < d ? mine : -1;
+        out_tokens[base + k] = k < d ? mine_tok : (k == d ? bonus : -1);
+    }
+    if (lane == 0) {
+        accept_len[b] = d;
+        if (status) status[b] = oor ? 1 : 0;
+    }
+}
+
+template <typename E, bool ALIGNED, int U>
+__global__ __launch_bounds__(kBlock) void k_skip_tree(const typename E::storage *__restrict__ L,
+                                                      const int32_t *__restrict__ tok,
+                                                      const int32_t *__restrict__ par, int B, int N, int V,
+                                                      int nvec, int segs, uint64_t *part_k, int32_t *amax,
+                                                      TreeCtl ctl, int32_t *__restrict__ accept_len,
+                                                      int32_t *__restrict__ path_nodes,
+                                                      int32_t *__restrict__ out_tokens,
+                                                      int32_t *__restrict__ status) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const long long wave = static_cast<long long>(blockIdx.x) * kWavesPerBlock + (threadIdx.x >> 6);
+    const long long per_node = static_cast<long long>(B) * segs;
+    if (wave >= per_node * N) return;
+    const int j = static_cast<int>(wave / per_node);
+    const long long rem = wave - static_cast<long long>(j) * per_node;
+    const int b = static_cast<int>(rem / segs);
+    const int sg = static_cast<int>(rem - static_cast<long long>(b) * segs);
+    const long long base = static_cast<long long>(b) * N;
+    if (uniform(shared_load(&ctl.state[base + j])) & kRejected) return;
+
+    const long long row = base + j;
+    const int v0 = static_cast<int>((static_cast<long long>(sg) * nvec) / segs);
+    const int v1 = static_cast<int>((static_cast<long long>(sg + 1) * nvec) / segs);
+    const uint64_t key = segment_argmax_chunked<E, ALIGNED, U, kGSkipChunks>(L + row * V, V, v0, v1, lane);
+    if (lane == 0) shared_store(&part_k[row * segs + sg], key);
+    if (!wave_arrive(&ctl.ticket[row], static_cast<unsigned>(segs), lane)) return;
+
+    // last segment of node j's row: its argmax decides j's children
+    uint64_t mk = 0;
+    for (int s = lane; s < segs; s += kWave) {
+        const uint64_t k = shared_load(&part_k[row * segs + s]);
+        mk = k > mk ? k : mk;
+    }
+    const int a = uniform(argmax_key_index(wave_max_u64(mk)));
+    if (lane == 0) shared_store(&amax[row], a);
+    wait_own_stores();
+    const bool in = lane < N;
+    const int p = in ? par[base + lane] : -1;
+    const int t = in ? tok[base + lane] : 0;
+    // states as they stand, plus this row done and this row's mismatching children
+    unsigned st = in ? shared_load(&ctl.state[base + lane]) : 0u;
+    uint64_t rej = ballot(in && ((st & kRejected) || (lane > 0 && p == j && t != a)));
+    // close the rejection over the tree: a node under a rejected parent is rejected
+    for (int it = 0; it < N; ++it) {
+        const bool under = in && p >= 0 && p < lane && ((rej >> p) & 1ull);
+        const uint64_t r2 = rej | ballot(under);
+        if (r2 == rej) break;  // uniform
+        rej = r2;
+    }
+    unsigned mark = 0;
+    if (lane == j) mark |= kRowDone;
+    if (in && ((rej >> lane) & 1ull)) mark |= kRejected;
+    int newly = 0;
+    if (mark) {
+        const unsigned old = __hip_atomic_fetch_or(&ctl.state[base + lane], mark, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+        newly = old == 0 ? 1 : 0;
+    }
+    const int cnt = __popcll(ballot(newly != 0));
+    if (cnt == 0) return;
+    wait_own_stores();
+    unsigned before = 0;
+    if (lane == 0)
+        before = __hip_atomic_fetch_add(&ctl.resolved[b], static_cast<unsigned>(cnt), __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT);
+    before = uniform(static_cast<unsigned>(__shfl(static_cast<int>(before), 0, kWave)));
+    if (before + static_cast<unsigned>(cnt) != static_cast<unsigned>(N)) return;
+    tree_finish(tok, par, amax, ctl, b, N, V, accept_len, path_nodes, out_tokens, status, lane);
+}
+
+template <typename E, bool ALIGNED>
+hipError_t skip_tree_t(const void *L, const int32_t *tok, const int32_t *par, int B, int N, int V,
+                       const RowGeom &g, uint64_t *part_k, int32_t *amax, const TreeCtl &ctl,
+                       int32_t *accept_len, int32_t *path_nodes, int32_t *out_tokens, int32_t *status,
+                       hipStream_t s) {
+    using T = typename E::storage;
+    const long long nwaves = static_cast<long long>(N) * B * g.segs;
+    const long long blocks = (nwaves + kWavesPerBlock - 1) / kWavesPerBlock;
+    return launch_kernel(k_skip_tree<E, ALIGNED, kGSkipVecsPerLane>, dim3(static_cast<unsigned>(blocks)),
+                         dim3(kBlock), 0, s, static_cast<const T *>(L), tok, par, B, N, V, g.nvec, g.segs,
+                         part_k, amax, ctl, accept_len, path_nodes, out_tokens, status);
+}
+
 template <typename E, bool ALIGNED>
 hipError_t skip_argmax_t(const void *L, const int32_t *drafts, int B, int K, int V, const RowGeom &g,
                          uint64_t *part_k, int32_t *amax, const SkipCtl &ctl, int32_t *accept_len,
@@ -420,6 +595,27 @@ hipError_t launch_skip_match(const void *L, const int32_t *drafts, int B, int K,
     if (dt == SV_BF16) return g.aligned ? SV_SK(BF16, true) : SV_SK(BF16, false);
     return g.aligned ? SV_SK(F32, true) : SV_SK(F32, false);
 #undef SV_SK
+}
+
+bool tree_skip_supported(int N) { return N <= kTreeSkipMaxN; }
+
+size_t tree_ctl_bytes(int B, int N) { return sizeof(unsigned) * (2 * static_cast<size_t>(B) * N + B); }
+
+hipError_t launch_skip_tree(const void *L, const int32_t *node_tokens, const int32_t *parents, int B, int N,
+                            int V, const RowGeom &g, sv_dtype dt, uint64_t *part_k, int32_t *amax,
+                            void *ctl_base, int32_t *accept_len, int32_t *path_nodes, int32_t *out_tokens,
+                            int32_t *status, hipStream_t s) {
+    TreeCtl ctl;
+    ctl.ticket = static_cast<unsigned *>(ctl_base);
+    ctl.state = ctl.ticket + static_cast<size_t>(B) * N;
+    ctl.resolved = ctl.state + static_cast<size_t>(B) * N;
+    hipError_t e = clear_words(ctl_base, tree_ctl_bytes(B, N), s);
+    if (e != hipSuccess) return e;
+    trace_select(SV_K_SKIP_TREE);
+#define SV_ST(E, A) skip_tree_t<E, A>(L, node_tokens, parents, B, N, V, g, part_k, amax, ctl, accept_len, path_nodes, out_tokens, status, s)
+    if (dt == SV_BF16) return g.aligned ? SV_ST(BF16, true) : SV_ST(BF16, false);
+    return g.aligned ? SV_ST(F32, true) : SV_ST(F32, false);
+#undef SV_ST
 }
 
 hipError_t launch_match(const uint64_t *part_k, const int32_t *drafts, int B, int K, int V,

@@ -161,6 +161,14 @@ hipError_t launch_commit(const void *src, void *dst, int G, int B, int S, int ro
                          const int32_t *tree_base, const int32_t *commit_base,
                          const int32_t *accept_len, const int32_t *path_nodes, int N,
                          int32_t *status, hipStream_t s);
+// Zeroes `bytes` (a multiple of 4) at `base` with an untraced launch.
+hipError_t clear_words(void *base, size_t bytes, hipStream_t s);
+bool tree_skip_supported(int N);
+size_t tree_ctl_bytes(int B, int N);
+hipError_t launch_skip_tree(const void *L, const int32_t *node_tokens, const int32_t *parents, int B, int N,
+                            int V, const RowGeom &g, sv_dtype dt, uint64_t *part_k, int32_t *amax,
+                            void *ctl_base, int32_t *accept_len, int32_t *path_nodes, int32_t *out_tokens,
+                            int32_t *status, hipStream_t s);
 hipError_t launch_match(const uint64_t *part_k, const int32_t *drafts, int B, int K, int V,
                         const RowGeom &g, int32_t *accept_len, int32_t *out_tokens, int32_t *status,
                         hipStream_t s);

@@ -718,18 +718,22 @@ size_t skip_ctl_bytes(int B, int K) {
     return sizeof(uint64_t) * B + sizeof(unsigned) * static_cast<size_t>(B) * (K + 1) + 2 * sizeof(unsigned) * B;
 }
 
+hipError_t clear_words(void *base, size_t bytes, hipStream_t s) {
+    const long long words = static_cast<long long>(bytes / sizeof(uint32_t));
+    const long long zb = std::max<long long>(1, std::min<long long>(1024, (words + kBlock - 1) / kBlock));
+    trace_select(-1);  // the clearing launch is not traced
+    hipLaunchKernelGGL(k_zero_words, dim3(static_cast<unsigned>(zb)), dim3(kBlock), 0, s,
+                       reinterpret_cast<uint32_t *>(base), words);
+    return hipGetLastError();
+}
+
 hipError_t skip_ctl_init(void *base, int B, int K, SkipCtl *ctl, hipStream_t s) {
     char *q = static_cast<char *>(base);
     ctl->mask = reinterpret_cast<uint64_t *>(q);
     ctl->ticket = reinterpret_cast<unsigned *>(ctl->mask + B);
     ctl->won = ctl->ticket + static_cast<size_t>(B) * (K + 1);
     ctl->finished = ctl->won + B;
-    const long long words = static_cast<long long>(skip_ctl_bytes(B, K) / sizeof(uint32_t));
-    const long long zb = std::max<long long>(1, std::min<long long>(1024, (words + kBlock - 1) / kBlock));
-    trace_select(-1);  // the clearing launch is not traced
-    hipLaunchKernelGGL(k_zero_words, dim3(static_cast<unsigned>(zb)), dim3(kBlock), 0, s,
-                       reinterpret_cast<uint32_t *>(base), words);
-    return hipGetLastError();
+    return clear_words(base, skip_ctl_bytes(B, K), s);
 }
 
 hipError_t launch_skip(const void *tgt, const void *drf, const int32_t *drafts, const float *ua,

@@ -156,6 +156,11 @@ sv_status spec_verify_greedy(const void *target_logits, const int32_t *draft_tok
  *                       node) as the bonus, then -1.
  *   req_status [B]      optional: 0, 1 if a node id (j >= 1) is outside
  *                       [0, V), 2 if the parent array is malformed.
+ *
+ * Rows read: for N <= 64 the rows of nodes known to be rejected (a node whose
+ * token differs from its parent row's argmax, and its descendants) are
+ * skipped, except by segments already in flight when that is decided; for
+ * larger N every row is read.
  */
 sv_status spec_verify_tree(const void *target_logits, const int32_t *node_tokens,
                            const int32_t *parents, int B, int N, int V, sv_dtype dt,
@@ -289,7 +294,8 @@ typedef enum {
     SV_K_LMHEAD = 10,      /* LM-head projection on the matrix cores + row argmax partials */
     SV_K_NGRAM_COUNT = 11, /* lexical retrieval: candidates per chunk */
     SV_K_NGRAM_EMIT = 12,  /* lexical retrieval: candidate positions in order */
-    SV_K_COUNT = 13
+    SV_K_SKIP_TREE = 13,   /* node-row argmax + tree walk, skipping rows of rejected nodes */
+    SV_K_COUNT = 14
 } sv_kernel_id;
 
 sv_status sv_trace_begin(int capacity, unsigned kernel_mask);

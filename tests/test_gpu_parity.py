@@ -126,8 +126,10 @@ def test_greedy_workload_full_size(B):
 def test_tree_small_random_and_degenerate():
     note("tree small")
     rng = np.random.default_rng(12)
+    # N <= 64 takes the row-skipping pass, larger N the full read (argmax + tree walk)
     for (B, N, V, dt) in [(50, 12, 4, "f32"), (40, 33, 1001, "bf16"), (8, 300, 64, "bf16"),
-                          (3, 1, 100, "f32")]:
+                          (3, 1, 100, "f32"), (30, 64, 500, "bf16"), (30, 65, 500, "bf16"),
+                          (15, 2, 7, "f32")]:
         L = rng.integers(-1, 2, size=(B, N, V)).astype(np.float32) if V < 10 else \
             rng.standard_normal((B, N, V)).astype(np.float32)
         LL = L if dt == "f32" else workloads.to_bf16_bits(L)
@@ -149,6 +151,17 @@ def test_tree_small_random_and_degenerate():
                                parents=par)
         check_exact(gpu_tree(w), oracle.verify_tree(LL, tok, par),
                     ("accept_len", "path", "tokens", "status"))
+
+
+@pytest.mark.parametrize("p_match", [1.0, 0.0])
+def test_tree_acceptance_extremes(p_match):
+    # every node accepted (every row needed) or none (only the root row)
+    note(f"tree p_match={p_match}")
+    w = workloads.make_tree(48, 20011, "bf16", p_match=p_match, seed=31)
+    o = oracle.verify_tree(w.target, w.node_tokens, w.parents)
+    check_exact(gpu_tree(w), o, ("accept_len", "path", "tokens", "status"))
+    if p_match == 0.0:
+        assert (o["accept_len"] <= 1).all()
 
 
 def test_tree_workload_full_size():
@@ -308,3 +321,8 @@ def test_trace_records_each_kernel():
     gpu_greedy(wg)
     recs = sv.trace_end()
     assert [r[0] for r in recs] == ["argmax", "match"]
+    wt = workloads.make_tree(4, 5000, "bf16", seed=8)
+    sv.trace_begin(64)
+    gpu_tree(wt)
+    recs = sv.trace_end()
+    assert [r[0] for r in recs] == ["skip_tree"]
