@@ -13,15 +13,28 @@
 // bf16, both k-contiguous.  A workgroup of 8 waves (two per SIMD) owns a
 // 256 x 256 tile of C and walks D in steps of 32.  The H and W slabs of a step
 // go straight from global memory into LDS (global_load_lds, 16 bytes per lane,
-// no registers), issued three steps ahead into a ring of four LDS buffers; a
-// step waits only for its own loads (vmcnt), then one barrier.  LDS rows are
-// 64 bytes with the four 16-byte chunks of row r stored in the order
+// no registers), issued three steps ahead into a ring of four LDS slots.  LDS
+// rows are 64 bytes with the four 16-byte chunks of row r stored in the order
 // c ^ ((r >> 2) & 3), so the fragment reads of 16 consecutive rows hit
 // distinct banks.  Each wave holds a 64 x 128 part as 2 x 4 tiles of
-// v_mfma_f32_32x32x16_bf16 accumulators (fp32).  Workgroups are numbered so
-// that the row tiles of one column tile run together on one XCD (consecutive
-// workgroup ids go to consecutive XCDs): the column tile's W slab is then read
-// from HBM once and shared through that XCD's L2.
+// v_mfma_f32_32x32x16_bf16 accumulators (fp32).
+//
+// Schedule of step s (two 16-deep halves, h0 and h1):
+//   read the h1 fragments of s; wait for the h0 fragments; MFMAs of h0;
+//   wait for this wave's loads of step s + 1; barrier;
+//   loads of step s + 3 into the slot of step s - 1; read the h0 fragments of
+//   s + 1; wait for the h1 fragments of s; MFMAs of h1.
+// The fragment reads of one half are thus always in flight under the MFMAs
+// of the other, across the barrier too.  They are issued as inline ds_read
+// instructions with explicit lgkmcnt waits tied to the fragment registers:
+// with LDS DMA in flight the compiler would otherwise wait for every LDS read
+// before each group of MFMAs.  The barrier of step s also means every wave
+// has finished its reads of step s - 1, so that slot can be reloaded.
+//
+// Workgroups are numbered so that the row tiles of one column tile run
+// together on one XCD (consecutive workgroup ids go to consecutive XCDs): the
+// column tile's W slab is then read from HBM once and shared through that
+// XCD's L2.
 #include <limits.h>
 
 #include <type_traits>
@@ -39,44 +52,40 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int kXcds = 8;
 constexpr int kTM = 256, kTN = 256, kTK = 32;  // workgroup tile and D step
 constexpr int kRowB = kTK * 2;                 // LDS bytes per slab row
-constexpr int kChunks = kRowB / 16;            // 16-byte chunks per slab row (4)
-constexpr int kRowsPerDma = 1024 / kRowB;      // slab rows one wave-wide DMA fills (16)
-constexpr int kSlab = kTM * kRowB;             // bytes of one operand slab
+constexpr int kSlab = kTM * kRowB;             // bytes of one operand slab (16 KB)
+constexpr int kSlot = 2 * kSlab;               // one ring slot: the H slab, then the W slab
+constexpr int kStages = 4;                     // ring slots; loads run kStages - 1 steps ahead
 constexpr int kSegCols = 128;                  // columns per argmax key (one wave's width)
-constexpr int kStages = 4;  // LDS ring slots; loads run kStages - 1 steps ahead
-// Waves per workgroup: 4 (one per SIMD, 128 x 128 each) or 8 (two per SIMD,
-// 64 x 128 each, so one wave's waits can hide behind the other's MFMAs).
-#ifndef SV_LMHEAD_WAVES
-#define SV_LMHEAD_WAVES 8
-#endif
-constexpr int kLmWaves = SV_LMHEAD_WAVES;
+constexpr int kLmWaves = 8;
 constexpr int kLmThreads = kLmWaves * kWave;
-constexpr int kWavesM = kLmWaves / 2;          // waves along M (2 along N)
-constexpr int kTilesA = kTM / kWavesM / 32;    // 32-row MFMA tiles per wave along M
-constexpr int kDmaPerOperand = kSlab / 1024 / kLmWaves;  // 1 KB DMA instructions per wave per operand
-constexpr int kLoadsPerStep = 2 * kDmaPerOperand;        // DMA loads per thread per step
+constexpr int kTileRows = 32;                  // rows (and columns) of one MFMA tile
+constexpr int kLoadsPerStep = 4;               // 1 KB DMA instructions per wave per step
 
-// One array per ring slot and operand, so the compiler can tell which slot a
-// fragment read touches and waits only for that slot's loads.
-__shared__ __align__(1024) char sA0[kSlab], sA1[kSlab], sA2[kSlab], sA3[kSlab];
-__shared__ __align__(1024) char sB0[kSlab], sB1[kSlab], sB2[kSlab], sB3[kSlab];
-// Stored position of logical 16-byte chunk c of slab row r: consecutive rows
-// rotate their chunks so that 16 lanes reading one logical chunk of 16
-// consecutive rows hit 16 distinct 4-bank groups (measured: no bank conflicts).
-__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 2) & 3); }
-template <int S> __device__ __forceinline__ char *slab_a() {
-    return S == 0 ? sA0 : S == 1 ? sA1 : S == 2 ? sA2 : sA3;
-}
-template <int S> __device__ __forceinline__ char *slab_b() {
-    return S == 0 ? sB0 : S == 1 ? sB1 : S == 2 ? sB2 : sB3;
-}
-template <int S> using Slot = std::integral_constant<int, S>;
+__shared__ __align__(1024) char ring[kStages * kSlot];
+
+template <int N> using IC = std::integral_constant<int, N>;
 
 // vmcnt(n) with the other counters left alone (gfx9 encoding).
 template <int N> __device__ __forceinline__ void wait_vm() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
+
+// One 16-byte fragment read at LDS byte address addr + OFF.  The result is not
+// valid until an lgkmcnt wait that names it (LDS_WAIT below).
+template <int OFF> __device__ __forceinline__ bf16x8 lds_read(uint32_t addr, IC<OFF>) {
+    static_assert(OFF >= 0 && OFF < 65536, "ds offset range");
+    bf16x8 r;
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+    return r;
+}
+
+// Wait until at most 6 LDS reads are outstanding (the six issued after the
+// named fragments), and make the named fragments depend on that wait.
+#define LDS_WAIT6(a0, a1, b0, b1, b2, b3) \
+    asm volatile("s_waitcnt lgkmcnt(6)" : "+v"(a0), "+v"(a1), "+v"(b0), "+v"(b1), "+v"(b2), "+v"(b3))
+#define LDS_WAIT0(a0, a1, b0, b1, b2, b3) \
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a0), "+v"(a1), "+v"(b0), "+v"(b1), "+v"(b2), "+v"(b3))
 
 __global__ __launch_bounds__(kLmThreads, 1) void k_lmhead_argmax(const uint4 *__restrict__ H,
                                                              const uint4 *__restrict__ W, int M, int D,
@@ -92,74 +101,92 @@ __global__ __launch_bounds__(kLmThreads, 1) void k_lmhead_argmax(const uint4 *__
     const int wm = w >> 1, wn = w & 1;
     const int dv = D / 8;  // 16-byte chunks per row
 
-    // DMA mapping: instruction i of wave w fills slab rows kRowsPerDma q ..,
-    // q = kLmWaves i + w; lane l writes 16 bytes at 16 l, i.e. row
-    // kRowsPerDma q + l / kChunks, stored chunk l % kChunks, which holds the
-    // row's logical chunk swz(r, l % kChunks) (the swizzle is an involution).
+    // DMA mapping: the two instructions per operand of wave w fill slab rows
+    // 16 q .. 16 q + 15 for q = w and q = 8 + w; lane l writes 16 bytes at
+    // 16 l, i.e. row 16 q + l / 4, stored chunk l % 4, which holds the row's
+    // logical chunk (l % 4) ^ ((row >> 2) & 3) (the swizzle is an involution).
     // Offsets are 32-bit 16-byte-chunk counts; rows past M or V read the last row.
-    int ga[kDmaPerOperand], gb[kDmaPerOperand];
-#pragma unroll
-    for (int i = 0; i < kDmaPerOperand; ++i) {
-        const int r = kRowsPerDma * (kLmWaves * i + w) + lane / kChunks;
-        const int c = swz(r, lane % kChunks);
-        ga[i] = min(m0 + r, M - 1) * dv + c;
-        gb[i] = min(n0 + r, V - 1) * dv + c;
+    int ga0, ga1, gb0, gb1;
+    {
+        const int r0 = 16 * w + lane / 4, r1 = 16 * (8 + w) + lane / 4;
+        const int c0 = (lane % 4) ^ ((r0 >> 2) & 3), c1 = (lane % 4) ^ ((r1 >> 2) & 3);
+        ga0 = min(m0 + r0, M - 1) * dv + c0;
+        ga1 = min(m0 + r1, M - 1) * dv + c1;
+        gb0 = min(n0 + r0, V - 1) * dv + c0;
+        gb1 = min(n0 + r1, V - 1) * dv + c1;
     }
-    auto issue = [&](auto slot, int step) {
-        constexpr int S = decltype(slot)::value;
-        const int k0 = step * (kTK / 8);
-#pragma unroll
-        for (int i = 0; i < kDmaPerOperand; ++i) {
-            const int q = kLmWaves * i + w;
-            __builtin_amdgcn_global_load_lds(H + ga[i] + k0, (SV_LDS void *)(slab_a<S>() + q * 1024), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(W + gb[i] + k0, (SV_LDS void *)(slab_b<S>() + q * 1024), 16, 0, 0);
-        }
-    };
-
-    f32x16 acc[kTilesA][4];
-#pragma unroll
-    for (int a = 0; a < kTilesA; ++a)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] = f32x16{};
-
-    // fragment reads: lane reads the 8 k-values of row (l % 32) at k offset 8 (l / 32)
-    auto compute = [&](auto slot) {
-        constexpr int S = decltype(slot)::value;
-#pragma unroll
-        for (int kk = 0; kk < kTK / 16; ++kk) {
-            bf16x8 af[kTilesA], bfr[4];
-            const int c = kk * 2 + (lane >> 5);
-#pragma unroll
-            for (int t = 0; t < kTilesA; ++t) {
-                const int ra = wm * (kTilesA * 32) + t * 32 + (lane & 31);
-                af[t] = *reinterpret_cast<const bf16x8 *>(slab_a<S>() + ra * kRowB + (swz(ra, c) << 4));
-            }
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const int rb = wn * 128 + t * 32 + (lane & 31);
-                bfr[t] = *reinterpret_cast<const bf16x8 *>(slab_b<S>() + rb * kRowB + (swz(rb, c) << 4));
-            }
-#pragma unroll
-            for (int a = 0; a < kTilesA; ++a)
-#pragma unroll
-                for (int b = 0; b < 4; ++b)
-                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a], bfr[b], acc[a][b], 0, 0, 0);
-        }
-    };
-
     const int nk = D / kTK;  // a multiple of kStages (D % 128 == 0)
-    issue(Slot<0>{}, 0);
-    issue(Slot<1>{}, 1);
-    issue(Slot<2>{}, 2);
-    // step s: its loads are done once at most the kStages - 2 later steps'
-    // loads are outstanding; the barrier then also means every wave has
-    // finished step s - 1, whose slot the loads of step s + kStages - 1 reuse
-    // (past the end, the last step is loaded again into a slot nobody reads)
-#define SV_STEP(S)                                                            \
-    wait_vm<(kStages - 2) * kLoadsPerStep>();                                 \
-    __builtin_amdgcn_s_barrier();                                             \
-    issue(Slot<(S + kStages - 1) % kStages>{}, min(s + S + kStages - 1, nk - 1)); \
-    compute(Slot<S>{});
+#define SV_ISSUE(S, step)                                                                                \
+    {                                                                                                    \
+        const int k0 = (step) * (kTK / 8);                                                               \
+        char *sl = ring + (S) * kSlot;                                                                   \
+        __builtin_amdgcn_global_load_lds(H + ga0 + k0, (SV_LDS void *)(sl + w * 1024), 16, 0, 0);        \
+        __builtin_amdgcn_global_load_lds(W + gb0 + k0, (SV_LDS void *)(sl + kSlab + w * 1024), 16, 0, 0); \
+        __builtin_amdgcn_global_load_lds(H + ga1 + k0, (SV_LDS void *)(sl + (8 + w) * 1024), 16, 0, 0);  \
+        __builtin_amdgcn_global_load_lds(W + gb1 + k0, (SV_LDS void *)(sl + kSlab + (8 + w) * 1024), 16,   \
+                                         0, 0);                                                          \
+    }
+
+    // Fragment addresses.  Lane l reads the 8 k-values of row (l % 32) of a
+    // tile at k offset 8 (l / 32) within the half: logical chunk 2 h + l / 32,
+    // stored at chunk (2 h + l / 32) ^ ((l >> 2) & 3) (tile rows are multiples
+    // of 32, so the swizzle depends on the lane only).  Tile t of a slab sits
+    // 2048 t bytes further; slot S adds S * kSlot, taken as an immediate offset
+    // from a base for slots 0-1 and one 64 KB higher for slots 2-3.
+    const uint32_t lbase = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((SV_LDS char *)ring));
+    const int sw = (lane >> 2) & 3;
+    const uint32_t rowpart = static_cast<uint32_t>((lane & 31) * kRowB);
+    const uint32_t a_h0 = lbase + wm * 64 * kRowB + rowpart + (((0 + (lane >> 5)) ^ sw) << 4);
+    const uint32_t a_h1 = lbase + wm * 64 * kRowB + rowpart + (((2 + (lane >> 5)) ^ sw) << 4);
+    const uint32_t b_h0 = lbase + kSlab + wn * 128 * kRowB + rowpart + (((0 + (lane >> 5)) ^ sw) << 4);
+    const uint32_t b_h1 = lbase + kSlab + wn * 128 * kRowB + rowpart + (((2 + (lane >> 5)) ^ sw) << 4);
+    const uint32_t a_h0_hi = a_h0 + 2 * kSlot, a_h1_hi = a_h1 + 2 * kSlot;
+    const uint32_t b_h0_hi = b_h0 + 2 * kSlot, b_h1_hi = b_h1 + 2 * kSlot;
+
+    f32x16 c00{}, c01{}, c02{}, c03{}, c10{}, c11{}, c12{}, c13{};
+    bf16x8 p0, p1, q0, q1, q2, q3;  // fragments of the half in flight (A tiles 0-1, B tiles 0-3)
+    bf16x8 r0, r1, t0, t1, t2, t3;  // fragments of the other half
+#define SV_READ(S, HALF, A0, A1, B0, B1, B2, B3)                                                  \
+    {                                                                                            \
+        const uint32_t ab = ((S) < 2) ? ((HALF) ? a_h1 : a_h0) : ((HALF) ? a_h1_hi : a_h0_hi);  \
+        const uint32_t bb = ((S) < 2) ? ((HALF) ? b_h1 : b_h0) : ((HALF) ? b_h1_hi : b_h0_hi);  \
+        constexpr int so = ((S) & 1) * kSlot;                                                    \
+        A0 = lds_read(ab, IC<so + 0 * 2048>{});                                                 \
+        A1 = lds_read(ab, IC<so + 1 * 2048>{});                                                 \
+        B0 = lds_read(bb, IC<so + 0 * 2048>{});                                                 \
+        B1 = lds_read(bb, IC<so + 1 * 2048>{});                                                 \
+        B2 = lds_read(bb, IC<so + 2 * 2048>{});                                                 \
+        B3 = lds_read(bb, IC<so + 3 * 2048>{});                                                 \
+    }
+#define SV_MFMA(A0, A1, B0, B1, B2, B3)                                          \
+    c00 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A0, B0, c00, 0, 0, 0);        \
+    c01 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A0, B1, c01, 0, 0, 0);        \
+    c02 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A0, B2, c02, 0, 0, 0);        \
+    c03 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A0, B3, c03, 0, 0, 0);        \
+    c10 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A1, B0, c10, 0, 0, 0);        \
+    c11 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A1, B1, c11, 0, 0, 0);        \
+    c12 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A1, B2, c12, 0, 0, 0);        \
+    c13 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A1, B3, c13, 0, 0, 0);
+#define SV_BARRIER() asm volatile("s_barrier" ::: "memory")
+
+    SV_ISSUE(0, 0)
+    SV_ISSUE(1, 1)
+    SV_ISSUE(2, 2)
+    wait_vm<2 * kLoadsPerStep>();  // this wave's loads of step 0 are done
+    SV_BARRIER();                  // and every wave's
+    SV_READ(0, 0, p0, p1, q0, q1, q2, q3)
+    // step s in slot S (past the end, the last step is loaded again into a
+    // slot nobody reads, and the h0 reads of the step after it are discarded)
+#define SV_STEP(S)                                                        \
+    SV_READ(S, 1, r0, r1, t0, t1, t2, t3)                                 \
+    LDS_WAIT6(p0, p1, q0, q1, q2, q3);                                    \
+    SV_MFMA(p0, p1, q0, q1, q2, q3)                                       \
+    wait_vm<kLoadsPerStep>();                                             \
+    SV_BARRIER();                                                         \
+    SV_ISSUE(((S) + 3) % kStages, min(s + (S) + 3, nk - 1))               \
+    SV_READ(((S) + 1) % kStages, 0, p0, p1, q0, q1, q2, q3)               \
+    LDS_WAIT6(r0, r1, t0, t1, t2, t3);                                    \
+    SV_MFMA(r0, r1, t0, t1, t2, t3)
     // no branches inside the ring (a branch makes the compiler wait for every load)
     for (int s = 0; s < nk; s += kStages) {
         SV_STEP(0)
@@ -168,21 +195,26 @@ __global__ __launch_bounds__(kLmThreads, 1) void k_lmhead_argmax(const uint4 *__
         SV_STEP(3)
     }
 #undef SV_STEP
-    wait_vm<0>();  // no DMA may still target LDS when the workgroup ends
+#undef SV_MFMA
+#undef SV_READ
+#undef SV_ISSUE
+    LDS_WAIT0(p0, p1, q0, q1, q2, q3);  // no LDS read still in flight
+    wait_vm<0>();                       // no DMA may still target LDS when the workgroup ends
 
     // epilogue: per row, the first maximum over this wave's 128 columns
     const int seg = (n0 + wn * 128) / kSegCols;
     if (seg >= segs) return;
     const int cbase = n0 + wn * 128 + (lane & 31);
+    const f32x16 acc[2][4] = {{c00, c01, c02, c03}, {c10, c11, c12, c13}};
 #pragma unroll
-    for (int a = 0; a < kTilesA; ++a) {
+    for (int a = 0; a < 2; ++a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             float best = -__builtin_huge_valf();
             int bi = INT_MAX;
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
-                const int col = cbase + b * 32;
+                const int col = cbase + b * kTileRows;
                 const float x = col < V ? acc[a][b][r] : -__builtin_huge_valf();
                 if (x > best || (bi == INT_MAX && col < V)) {
                     best = x;
@@ -195,7 +227,7 @@ __global__ __launch_bounds__(kLmThreads, 1) void k_lmhead_argmax(const uint4 *__
                 const uint64_t y = __shfl_xor(key, o, kWave);
                 key = y > key ? y : key;
             }
-            const int row = m0 + wm * (kTilesA * 32) + a * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+            const int row = m0 + wm * 64 + a * kTileRows + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
             if ((lane & 31) == 0 && row < M) part_k[static_cast<long long>(row) * segs + seg] = key;
         }
     }
