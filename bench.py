@@ -204,12 +204,23 @@ def tree_needed_rows(torch, target, w5):
     return rows
 
 
-def cpu_baseline(w3, w4, w5, mode, threads):
-    """The oracle, as it stands, on the same step's inputs (wall time, median of 3)."""
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w3, w4, w5, mode, threads, runs=3):
+    """The oracle, as it stands, on the same step's inputs (wall time, median of `runs`)."""
     import oracle
 
     times = []
-    for _ in range(3):
+    for _ in range(runs):
         t0 = time.perf_counter()
         if mode in ("all", "sample"):
             oracle.verify_sample(w3.target, w3.draft, w3.draft_tokens, w3.u_accept, w3.u_sample, w3.T,
@@ -276,6 +287,45 @@ def bench_ngram(sv, torch, workloads, dev, reps):
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, vendor figure
+
+
+def bench_greedy_b512(sv, torch, workloads, dev, per_call, with_cold, reps):
+    """spec_verify_greedy on the greedy workload at its own batch (B=512 K=7)."""
+    import numpy as np
+
+    w = workloads.make_config(4)
+    lib = sv.load_library()
+    t = torch.from_numpy(w.target.view(np.int16)).view(torch.bfloat16).to(dev)
+    x = torch.from_numpy(w.draft_tokens).to(dev)
+    i32 = dict(dtype=torch.int32, device=dev)
+    n = torch.empty(w.B, **i32)
+    tok = torch.empty((w.B, w.K + 1), **i32)
+    st = torch.empty(w.B, **i32)
+    ws = torch.empty(lib.sv_greedy_workspace_bytes(w.B, w.K + 1, w.V, sv.SV_BF16), dtype=torch.uint8,
+                     device=dev)
+    P = lambda a: ctypes.c_void_p(a.data_ptr())
+    args = (P(t), P(x), w.B, w.K, w.V, sv.SV_BF16, P(n), P(tok), P(st), P(ws), ws.numel(),
+            ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream))
+
+    def call():
+        rc = lib.spec_verify_greedy(*args)
+        if rc:
+            raise RuntimeError(f"spec_verify_greedy failed: {rc}")
+
+    call()
+    torch.cuda.synchronize()
+    n_b = n.cpu().numpy()
+    R = w.V * 2
+    nbytes = int(np.sum(n_b + 1)) * R
+    rows = w.B * (w.K + 1)
+    ms = per_call(call, reps)
+    entry = {"workload": f"greedy chain B={w.B} K={w.K} V={w.V} bf16", "ms": round(ms, 5),
+             "rows_per_s": round(rows / (ms * 1e-3), 1), "bytes_read": nbytes,
+             "dense_bytes": rows * R, "gbps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+             "mean_tokens_per_round": round(float(n_b.mean() + 1), 4)}
+    with_cold(entry, call, nbytes, rows)
+    del t
+    return entry
 
 
 def bench_lmhead(sv, torch, workloads, dev, reps):
@@ -499,6 +549,33 @@ def main():
         torch.cuda.synchronize()
         return (time.perf_counter() - t0) * 1e3 / reps
 
+    # cold calls: before each, an untimed 1 GiB write evicts the L2s and the
+    # 256 MB Infinity Cache; each call is bracketed by events on its stream
+    evict = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+
+    def cold_calls(fn, reps=100):
+        for _ in range(3):
+            fn()
+        ev = []
+        for i in range(reps):
+            evict.fill_(i & 0xFF)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            ev.append((e0, e1))
+        torch.cuda.synchronize()
+        t = np.array([a.elapsed_time(b) for a, b in ev])
+        return {"median": round(float(np.median(t)), 5), "p10": round(float(np.percentile(t, 10)), 5),
+                "p90": round(float(np.percentile(t, 90)), 5), "calls": reps}
+
+    def with_cold(entry, fn, nbytes, rows):
+        c = cold_calls(fn)
+        entry["cold_ms"] = c
+        entry["cold_rows_per_s"] = round(rows / (c["median"] * 1e-3), 1)
+        entry["cold_gbps"] = round(nbytes / (c["median"] * 1e-3) / 1e9, 1)
+        return entry
+
     reps = max(20, args.steps // 2)
     calls_alone = {}
     if "sample" in active:
@@ -512,14 +589,35 @@ def main():
         for name, fn, nbytes in (("sample_full", calls.sample, bytes_mode["sample"]),
                                  ("sample_skip", calls.sample_skip, skip_bytes)):
             ms = per_call(fn, reps)
-            calls_alone[name] = {"ms": round(ms, 5), "rows_per_s": round(rows_mode["sample"] / (ms * 1e-3), 1),
-                                 "bytes_read": nbytes, "gbps": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+            calls_alone[name] = with_cold(
+                {"ms": round(ms, 5), "rows_per_s": round(rows_mode["sample"] / (ms * 1e-3), 1),
+                 "bytes_read": nbytes, "gbps": round(nbytes / (ms * 1e-3) / 1e9, 1)},
+                fn, nbytes, rows_mode["sample"])
     for name, fn in (("greedy", calls.greedy), ("tree", calls.tree)):
         if name in active:
             ms = per_call(fn, reps)
-            calls_alone[name] = {"ms": round(ms, 5), "rows_per_s": round(rows_mode[name] / (ms * 1e-3), 1),
-                                 "bytes_read": bytes_mode[name],
-                                 "gbps": round(bytes_mode[name] / (ms * 1e-3) / 1e9, 1)}
+            calls_alone[name] = with_cold(
+                {"ms": round(ms, 5), "rows_per_s": round(rows_mode[name] / (ms * 1e-3), 1),
+                 "bytes_read": bytes_mode[name], "gbps": round(bytes_mode[name] / (ms * 1e-3) / 1e9, 1)},
+                fn, bytes_mode[name], rows_mode[name])
+    if "greedy" in active:
+        calls_alone["greedy_b512"] = bench_greedy_b512(sv, torch, workloads, dev, per_call, with_cold, reps)
+    del evict
+
+    # the read rate this device reaches: a read-only stream of 4 GiB of random
+    # bytes with the same loads as the row passes
+    probe = torch.randint(-2**31, 2**31 - 1, (1 << 30,), dtype=torch.int32, device=dev)
+    folds = sv.sv_read_probe(probe)
+    for _ in range(2):
+        sv.sv_read_probe(probe, folds=folds)
+    torch.cuda.synchronize()
+    sv.trace_begin(64, kernels=("read_probe",))
+    for _ in range(20):
+        sv.sv_read_probe(probe, folds=folds)
+    torch.cuda.synchronize()
+    probe_ms = statistics.mean(t for _, t in sv.trace_end(64))
+    read_ceiling = probe.numel() * 4 / (probe_ms * 1e-3) / 1e9
+    del probe
 
     # beyond the verification step: committing the tree's accepted paths in a
     # KV cache shaped like a 36-layer target (K and V, 8 heads x 128 bf16 = 2 KB rows)
@@ -576,10 +674,14 @@ def main():
     if not args.no_cpu_baseline:
         threads = args.cpu_threads or max(1, min(16, os.cpu_count() or 1))
         secs = cpu_baseline(w3, w4, w5, args.mode, threads)
+        secs1 = cpu_baseline(w3, w4, w5, args.mode, 1, runs=1)
         cpu = {"value": round(rows_step / secs, 1), "unit": "rows/s", "cores": threads,
                "kind": "oracle",
                "sample": f"one full step ({rows_step} rows: {', '.join(active)}), median of 3 runs, "
-                         f"{secs:.2f}s wall each"}
+                         f"{secs:.2f}s wall each",
+               "single_thread": {"value": round(rows_step / secs1, 1), "unit": "rows/s",
+                                 "sample": f"the same step once, {secs1:.2f}s wall"},
+               "cpu_model": cpu_model()}
 
     out = {
         "metric": METRIC,
@@ -603,6 +705,9 @@ def main():
         },
         "hbm_gbps": round(hbm_gbps, 1),
         "hbm_frac_of_peak": round(hbm_gbps / HBM_PEAK_GBPS, 4),
+        "read_ceiling": {"gbps": round(read_ceiling, 1), "kernel": "read_probe",
+                         "what": "read-only stream of 4 GiB of random bytes, mean of 20 launches",
+                         "frac_of_peak": round(read_ceiling / HBM_PEAK_GBPS, 4)},
         "roofline": roof,
         "roofline_others": others or None,
         "modes": modes,
@@ -611,6 +716,9 @@ def main():
         "extras": extras or None,
         "cpu_baseline": cpu,
     }
+    for r in [roof, *others.values()]:
+        if r and r.get("unit") == "GB/s":
+            r["frac_of_read_ceiling"] = round(r["achieved"] / read_ceiling, 4)
     print(json.dumps(out), flush=True)
 
 

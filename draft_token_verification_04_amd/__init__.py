@@ -28,13 +28,13 @@ SV_F32, SV_BF16 = 0, 1
 SV_MAX_TREE_NODES = 2048
 KERNELS = ("rowstats", "accept", "resid_mass", "resid_select", "argmax", "match", "tree",
            "skip_stats", "skip_argmax", "commit", "lmhead", "ngram_count", "ngram_emit",
-           "skip_tree")
+           "skip_tree", "read_probe")
 
 EXPORTS = ("sv_sample_workspace_bytes", "sv_greedy_workspace_bytes", "spec_verify_sample",
            "spec_verify_greedy", "spec_verify_tree", "spec_commit_tree_kv", "sv_status_string",
            "sv_version", "sv_lmhead_workspace_bytes", "spec_verify_greedy_lmhead",
            "spec_verify_tree_lmhead", "sv_ngram_workspace_bytes", "spec_ngram_candidates",
-           "sv_trace_begin", "sv_trace_end", "sv_kernel_name")
+           "sv_read_probe", "sv_read_probe_folds", "sv_trace_begin", "sv_trace_end", "sv_kernel_name")
 
 
 class SpecVerifyError(RuntimeError):
@@ -81,6 +81,10 @@ def load_library(path: str = LIB_PATH):
     lib.spec_verify_greedy_lmhead.restype = I
     lib.spec_verify_tree_lmhead.argtypes = [P, P, P, P, I, I, I, I, P, P, P, P, P, Z, P]
     lib.spec_verify_tree_lmhead.restype = I
+    lib.sv_read_probe.argtypes = [P, Z, P, P]
+    lib.sv_read_probe.restype = I
+    lib.sv_read_probe_folds.argtypes = [Z]
+    lib.sv_read_probe_folds.restype = Z
     lib.sv_status_string.argtypes = [I]
     lib.sv_status_string.restype = ctypes.c_char_p
     lib.sv_version.argtypes = []
@@ -415,6 +419,27 @@ def spec_commit_tree_kv(kv, tree_base, commit_base, accept_len, path, *, out=Non
     if rc != SV_OK:
         raise SpecVerifyError(rc, "spec_commit_tree_kv")
     return st
+
+
+def sv_read_probe(buf, *, folds=None, stream=None):
+    """Read every byte of the GPU tensor ``buf`` once (a measurement aid: the
+    read rate this device reaches).  Returns ``folds`` (int32), entry i the XOR
+    of the 32-bit words of the buffer's i-th 16 KB."""
+    torch = _torch()
+    lib = load_library()
+    _check(buf, "buf")
+    dev = buf.device
+    nbytes = buf.numel() * buf.element_size()
+    nf = lib.sv_read_probe_folds(nbytes)
+    if folds is None:
+        folds = torch.empty(max(nf, 1), dtype=torch.int32, device=dev)
+    elif folds.numel() < nf or folds.dtype != torch.int32 or folds.device != dev:
+        raise ValueError(f"folds must be int32 on {dev} with at least {nf} entries")
+    with torch.cuda.device(dev):
+        rc = lib.sv_read_probe(_ptr(buf), nbytes, _ptr(folds), _stream(torch, dev, stream))
+    if rc != SV_OK:
+        raise SpecVerifyError(rc, "sv_read_probe")
+    return folds
 
 
 # ---- per-kernel timing -----------------------------------------------------------

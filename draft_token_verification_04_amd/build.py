@@ -12,7 +12,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libspecverify.so")
 SOURCES = ["sv_api.hip", "sv_sample.hip", "sv_greedy.hip", "sv_commit.hip", "sv_lmhead.hip",
-           "sv_ngram.hip"]
+           "sv_ngram.hip", "sv_probe.hip"]
 ARCH = "gfx950"
 
 

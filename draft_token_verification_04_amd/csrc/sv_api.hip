@@ -432,6 +432,22 @@ sv_status spec_commit_tree_kv(const void *src_kv, void *dst_kv, int G, int B, in
     return e == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 
+size_t sv_read_probe_folds(size_t bytes) {
+    return static_cast<size_t>(read_probe_waves(static_cast<long long>(bytes / 16)));
+}
+
+sv_status sv_read_probe(const void *buf, size_t bytes, unsigned *folds, void *stream) {
+    if (bytes % 16 != 0) return SV_ERR_INVALID_ARG;
+    if (bytes / 16 > (1ull << 40)) return SV_ERR_UNSUPPORTED;
+    if (bytes == 0) return SV_OK;
+    if (!buf || !folds || !aligned16(buf)) return SV_ERR_INVALID_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const hipError_t e = traced(SV_K_READ_PROBE, s, [&] {
+        return launch_read_probe(buf, static_cast<long long>(bytes / 16), folds, s);
+    });
+    return e == hipSuccess ? SV_OK : SV_ERR_HIP;
+}
+
 const char *sv_status_string(sv_status st) {
     switch (st) {
         case SV_OK: return "ok";
@@ -449,7 +465,7 @@ const char *sv_kernel_name(int k) {
     static const char *names[SV_K_COUNT] = {"rowstats", "accept", "resid_mass", "resid_select",
                                             "argmax", "match", "tree", "skip_stats",
                                             "skip_argmax", "commit", "lmhead", "ngram_count",
-                                            "ngram_emit", "skip_tree"};
+                                            "ngram_emit", "skip_tree", "read_probe"};
     return (k >= 0 && k < SV_K_COUNT) ? names[k] : "unknown";
 }
 

@@ -165,6 +165,8 @@ hipError_t launch_commit(const void *src, void *dst, int G, int B, int S, int ro
 hipError_t clear_words(void *base, size_t bytes, hipStream_t s);
 bool tree_skip_supported(int N);
 size_t tree_ctl_bytes(int B, int N);
+long long read_probe_waves(long long n16);
+hipError_t launch_read_probe(const void *buf, long long n16, unsigned *folds, hipStream_t s);
 hipError_t launch_skip_tree(const void *L, const int32_t *node_tokens, const int32_t *parents, int B, int N,
                             int V, const RowGeom &g, sv_dtype dt, uint64_t *part_k, int32_t *amax,
                             void *ctl_base, int32_t *accept_len, int32_t *path_nodes, int32_t *out_tokens,

@@ -258,6 +258,18 @@ sv_status spec_ngram_candidates(const int32_t *context, int B, int L, const int3
                                 int32_t *positions, int32_t *req_status, void *workspace,
                                 size_t workspace_bytes, void *stream);
 
+/*
+ * Measurement aid, not a step of the method: reads the `bytes` bytes at `buf`
+ * (device memory, 16-byte aligned, bytes a multiple of 16) once, with the
+ * same non-temporal coalesced 16-byte loads as the row passes.  folds[i]
+ * (device uint32, sv_read_probe_folds(bytes) entries) receives the XOR of the
+ * 32-bit words in bytes [16384 i, 16384 (i + 1)) of the buffer, so every load
+ * is used and the writes are 1/4096 of the bytes read.  Timed with the tracer
+ * (kernel SV_K_READ_PROBE) it gives the read rate this device reaches.
+ */
+size_t sv_read_probe_folds(size_t bytes);
+sv_status sv_read_probe(const void *buf, size_t bytes, unsigned *folds, void *stream);
+
 /* Human-readable name of a status code (static storage). */
 const char *sv_status_string(sv_status s);
 
@@ -295,7 +307,8 @@ typedef enum {
     SV_K_NGRAM_COUNT = 11, /* lexical retrieval: candidates per chunk */
     SV_K_NGRAM_EMIT = 12,  /* lexical retrieval: candidate positions in order */
     SV_K_SKIP_TREE = 13,   /* node-row argmax + tree walk, skipping rows of rejected nodes */
-    SV_K_COUNT = 14
+    SV_K_READ_PROBE = 14,  /* read-only stream (measurement aid) */
+    SV_K_COUNT = 15
 } sv_kernel_id;
 
 sv_status sv_trace_begin(int capacity, unsigned kernel_mask);

@@ -186,3 +186,14 @@ def test_ngram_argument_checks(lib):
     assert call(wsb=0) == sv.SV_ERR_WORKSPACE
     assert call(B=0) == sv.SV_OK
     assert lib.sv_ngram_workspace_bytes(256, 32768) == 256 * 32 * 4
+
+
+def test_read_probe_argument_checks(lib):
+    assert lib.sv_read_probe(FAKE, 0, FAKE, None) == sv.SV_OK
+    assert lib.sv_read_probe(FAKE, 24, FAKE, None) == sv.SV_ERR_INVALID_ARG
+    assert lib.sv_read_probe(None, 32, FAKE, None) == sv.SV_ERR_INVALID_ARG
+    assert lib.sv_read_probe(FAKE, 32, None, None) == sv.SV_ERR_INVALID_ARG
+    assert lib.sv_read_probe_folds(16) == 1
+    assert lib.sv_read_probe_folds(16384) == 1
+    assert lib.sv_read_probe_folds(16384 + 16) == 2
+    assert lib.sv_kernel_name(14) == b"read_probe"
