@@ -11,25 +11,30 @@
 //
 // k_lmhead_argmax: C[m][n] = sum_k H[m][k] W[n][k] with H [M][D] and W [V][D]
 // bf16, both k-contiguous.  A workgroup of 8 waves (two per SIMD) owns a
-// 256 x 256 tile of C and walks D in steps of 32.  The H and W slabs of a step
-// go straight from global memory into LDS (global_load_lds, 16 bytes per lane,
-// no registers), issued three steps ahead into a ring of four LDS slots.  LDS
-// rows are 64 bytes with the four 16-byte chunks of row r stored in the order
-// c ^ ((r >> 2) & 3), so the fragment reads of 16 consecutive rows hit
-// distinct banks.  Each wave holds a 64 x 128 part as 2 x 4 tiles of
-// v_mfma_f32_32x32x16_bf16 accumulators (fp32).
+// 256 x 256 tile of C and walks D in steps of 64, each computed as four
+// 16-deep quarters.  The H and W slabs of a step go straight from global
+// memory into LDS (global_load_lds, 16 bytes per lane, no registers); a slab
+// row is one whole 128-byte cache line, which the L2 serves at about twice the
+// rate of half lines.  LDS holds two H slots and three W slots (160 KB): H is
+// loaded two steps ahead and W, which misses to HBM more often, three.  The
+// eight 16-byte chunks of row r are stored in the order c ^ ((r >> 1) & 7), so
+// the fragment reads of 16 consecutive rows hit distinct banks.  Each wave
+// holds a 64 x 128 part as 2 x 4 tiles of v_mfma_f32_32x32x16_bf16
+// accumulators (fp32).
 //
-// Schedule of step s (two 16-deep halves, h0 and h1):
-//   read the h1 fragments of s; wait for the h0 fragments; MFMAs of h0;
-//   wait for this wave's loads of step s + 1; barrier;
-//   loads of step s + 3 into the slot of step s - 1; read the h0 fragments of
-//   s + 1; wait for the h1 fragments of s; MFMAs of h1.
-// The fragment reads of one half are thus always in flight under the MFMAs
-// of the other, across the barrier too.  They are issued as inline ds_read
-// instructions with explicit lgkmcnt waits tied to the fragment registers:
-// with LDS DMA in flight the compiler would otherwise wait for every LDS read
-// before each group of MFMAs.  The barrier of step s also means every wave
-// has finished its reads of step s - 1, so that slot can be reloaded.
+// Schedule of step s, quarters q0..q3, fragments double-buffered:
+//   q0: read q1's fragments; wait for q0's; MFMAs of q0
+//   q1: read q2's; wait for q1's; MFMAs of q1
+//   q2: read q3's; wait for q2's; wait for this wave's loads of step s + 1;
+//       barrier; MFMAs of q2
+//   q3: read q0's of step s + 1; wait for q3's; barrier (every wave is done
+//       with step s's slots); loads of H(s + 2) and W(s + 3) into them;
+//       MFMAs of q3
+// The fragment reads of one quarter are always in flight under the MFMAs of
+// the previous one, across the barriers too.  They are issued as inline
+// ds_read instructions with explicit lgkmcnt waits tied to the fragment
+// registers: with LDS DMA in flight the compiler would otherwise wait for
+// every LDS read before each group of MFMAs.
 //
 // Workgroups are numbered so that the row tiles of one column tile run
 // together on one XCD (consecutive workgroup ids go to consecutive XCDs): the
@@ -50,18 +55,19 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 #define SV_LDS __attribute__((address_space(3)))
 
 constexpr int kXcds = 8;
-constexpr int kTM = 256, kTN = 256, kTK = 32;  // workgroup tile and D step
-constexpr int kRowB = kTK * 2;                 // LDS bytes per slab row
-constexpr int kSlab = kTM * kRowB;             // bytes of one operand slab (16 KB)
-constexpr int kSlot = 2 * kSlab;               // one ring slot: the H slab, then the W slab
-constexpr int kStages = 4;                     // ring slots; loads run kStages - 1 steps ahead
+constexpr int kTM = 256, kTN = 256, kTK = 64;  // workgroup tile and D step
+constexpr int kRowB = kTK * 2;                 // LDS bytes per slab row (one cache line)
+constexpr int kChunks = kRowB / 16;            // 16-byte chunks per slab row (8)
+constexpr int kSlab = kTM * kRowB;             // bytes of one operand slab (32 KB)
+constexpr int kHSlots = 2, kWSlots = 3;        // H loaded 2 steps ahead, W 3
 constexpr int kSegCols = 128;                  // columns per argmax key (one wave's width)
 constexpr int kLmWaves = 8;
 constexpr int kLmThreads = kLmWaves * kWave;
 constexpr int kTileRows = 32;                  // rows (and columns) of one MFMA tile
-constexpr int kLoadsPerStep = 4;               // 1 KB DMA instructions per wave per step
+constexpr int kDmaPerOperand = kSlab / 1024 / kLmWaves;  // 1 KB DMA instructions per wave (4)
 
-__shared__ __align__(1024) char ring[kStages * kSlot];
+// H slots first, then W slots
+__shared__ __align__(1024) char ring[(kHSlots + kWSlots) * kSlab];
 
 template <int N> using IC = std::integral_constant<int, N>;
 
@@ -86,6 +92,7 @@ template <int OFF> __device__ __forceinline__ bf16x8 lds_read(uint32_t addr, IC<
     asm volatile("s_waitcnt lgkmcnt(6)" : "+v"(a0), "+v"(a1), "+v"(b0), "+v"(b1), "+v"(b2), "+v"(b3))
 #define LDS_WAIT0(a0, a1, b0, b1, b2, b3) \
     asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a0), "+v"(a1), "+v"(b0), "+v"(b1), "+v"(b2), "+v"(b3))
+#define SV_BARRIER() asm volatile("s_barrier" ::: "memory")
 
 __global__ __launch_bounds__(kLmThreads, 1) void k_lmhead_argmax(const uint4 *__restrict__ H,
                                                              const uint4 *__restrict__ W, int M, int D,
@@ -101,62 +108,64 @@ __global__ __launch_bounds__(kLmThreads, 1) void k_lmhead_argmax(const uint4 *__
     const int wm = w >> 1, wn = w & 1;
     const int dv = D / 8;  // 16-byte chunks per row
 
-    // DMA mapping: the two instructions per operand of wave w fill slab rows
-    // 16 q .. 16 q + 15 for q = w and q = 8 + w; lane l writes 16 bytes at
-    // 16 l, i.e. row 16 q + l / 4, stored chunk l % 4, which holds the row's
-    // logical chunk (l % 4) ^ ((row >> 2) & 3) (the swizzle is an involution).
-    // Offsets are 32-bit 16-byte-chunk counts; rows past M or V read the last row.
-    int ga0, ga1, gb0, gb1;
-    {
-        const int r0 = 16 * w + lane / 4, r1 = 16 * (8 + w) + lane / 4;
-        const int c0 = (lane % 4) ^ ((r0 >> 2) & 3), c1 = (lane % 4) ^ ((r1 >> 2) & 3);
-        ga0 = min(m0 + r0, M - 1) * dv + c0;
-        ga1 = min(m0 + r1, M - 1) * dv + c1;
-        gb0 = min(n0 + r0, V - 1) * dv + c0;
-        gb1 = min(n0 + r1, V - 1) * dv + c1;
+    // DMA mapping: instruction i of wave w fills slab rows 8 q .. 8 q + 7 for
+    // q = 8 i + w; lane l writes 16 bytes at 16 l, i.e. row 8 q + l / 8,
+    // stored chunk l % 8, which holds the row's logical chunk
+    // (l % 8) ^ ((row >> 1) & 7) (the swizzle is an involution).  Offsets are
+    // 32-bit 16-byte-chunk counts; rows past M or V read the last row.
+    int ga0, ga1, ga2, ga3, gb0, gb1, gb2, gb3;
+#define SV_GOFF(i, GA, GB)                                        \
+    {                                                             \
+        const int r = 8 * (kLmWaves * (i) + w) + lane / kChunks;  \
+        const int c = (lane % kChunks) ^ ((r >> 1) & 7);          \
+        GA = min(m0 + r, M - 1) * dv + c;                         \
+        GB = min(n0 + r, V - 1) * dv + c;                         \
     }
-    const int nk = D / kTK;  // a multiple of kStages (D % 128 == 0)
-#define SV_ISSUE(S, step)                                                                                \
-    {                                                                                                    \
-        const int k0 = (step) * (kTK / 8);                                                               \
-        char *sl = ring + (S) * kSlot;                                                                   \
-        __builtin_amdgcn_global_load_lds(H + ga0 + k0, (SV_LDS void *)(sl + w * 1024), 16, 0, 0);        \
-        __builtin_amdgcn_global_load_lds(W + gb0 + k0, (SV_LDS void *)(sl + kSlab + w * 1024), 16, 0, 0); \
-        __builtin_amdgcn_global_load_lds(H + ga1 + k0, (SV_LDS void *)(sl + (8 + w) * 1024), 16, 0, 0);  \
-        __builtin_amdgcn_global_load_lds(W + gb1 + k0, (SV_LDS void *)(sl + kSlab + (8 + w) * 1024), 16,   \
-                                         0, 0);                                                          \
+    SV_GOFF(0, ga0, gb0)
+    SV_GOFF(1, ga1, gb1)
+    SV_GOFF(2, ga2, gb2)
+    SV_GOFF(3, ga3, gb3)
+#undef SV_GOFF
+    static_assert(kDmaPerOperand == 4, "four DMA instructions per operand per wave");
+    const int nk = D / kTK;
+#define SV_ISSUE(SRC, G0, G1, G2, G3, slab, step)                                                    \
+    {                                                                                                \
+        const int k0 = (step) * kChunks;                                                             \
+        char *sl = ring + (slab) * kSlab;                                                            \
+        __builtin_amdgcn_global_load_lds(SRC + G0 + k0, (SV_LDS void *)(sl + (0 + w) * 1024), 16, 0, 0);  \
+        __builtin_amdgcn_global_load_lds(SRC + G1 + k0, (SV_LDS void *)(sl + (8 + w) * 1024), 16, 0, 0);  \
+        __builtin_amdgcn_global_load_lds(SRC + G2 + k0, (SV_LDS void *)(sl + (16 + w) * 1024), 16, 0, 0); \
+        __builtin_amdgcn_global_load_lds(SRC + G3 + k0, (SV_LDS void *)(sl + (24 + w) * 1024), 16, 0, 0); \
     }
+#define SV_ISSUE_H(slot, step) SV_ISSUE(H, ga0, ga1, ga2, ga3, (slot), step)
+#define SV_ISSUE_W(slot, step) SV_ISSUE(W, gb0, gb1, gb2, gb3, kHSlots + (slot), step)
 
-    // Fragment addresses.  Lane l reads the 8 k-values of row (l % 32) of a
-    // tile at k offset 8 (l / 32) within the half: logical chunk 2 h + l / 32,
-    // stored at chunk (2 h + l / 32) ^ ((l >> 2) & 3) (tile rows are multiples
-    // of 32, so the swizzle depends on the lane only).  Tile t of a slab sits
-    // 2048 t bytes further; slot S adds S * kSlot, taken as an immediate offset
-    // from a base for slots 0-1 and one 64 KB higher for slots 2-3.
+    // Fragment addresses per quarter q: lane l reads the 8 k-values of row
+    // (l % 32) of a tile at logical chunk 2 q + l / 32, stored at that
+    // ^ (((l % 32) >> 1) & 7) (tile rows are multiples of 32, so the swizzle
+    // depends on the lane only).  Tile t of a slab sits 32 t rows further (an
+    // immediate offset); the slot's byte offset is added per read group.
     const uint32_t lbase = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((SV_LDS char *)ring));
-    const int sw = (lane >> 2) & 3;
-    const uint32_t rowpart = static_cast<uint32_t>((lane & 31) * kRowB);
-    const uint32_t a_h0 = lbase + wm * 64 * kRowB + rowpart + (((0 + (lane >> 5)) ^ sw) << 4);
-    const uint32_t a_h1 = lbase + wm * 64 * kRowB + rowpart + (((2 + (lane >> 5)) ^ sw) << 4);
-    const uint32_t b_h0 = lbase + kSlab + wn * 128 * kRowB + rowpart + (((0 + (lane >> 5)) ^ sw) << 4);
-    const uint32_t b_h1 = lbase + kSlab + wn * 128 * kRowB + rowpart + (((2 + (lane >> 5)) ^ sw) << 4);
-    const uint32_t a_h0_hi = a_h0 + 2 * kSlot, a_h1_hi = a_h1 + 2 * kSlot;
-    const uint32_t b_h0_hi = b_h0 + 2 * kSlot, b_h1_hi = b_h1 + 2 * kSlot;
+    const int sw = ((lane & 31) >> 1) & 7;
+    const uint32_t rowA = lbase + (wm * 64 + (lane & 31)) * kRowB;
+    const uint32_t rowB = lbase + kHSlots * kSlab + (wn * 128 + (lane & 31)) * kRowB;
+#define SV_CH(q) ((((2 * (q)) + (lane >> 5)) ^ sw) << 4)
+    const uint32_t a0 = rowA + SV_CH(0), a1 = rowA + SV_CH(1), a2 = rowA + SV_CH(2), a3 = rowA + SV_CH(3);
+    const uint32_t b0 = rowB + SV_CH(0), b1 = rowB + SV_CH(1), b2 = rowB + SV_CH(2), b3 = rowB + SV_CH(3);
+#undef SV_CH
 
     f32x16 c00{}, c01{}, c02{}, c03{}, c10{}, c11{}, c12{}, c13{};
-    bf16x8 p0, p1, q0, q1, q2, q3;  // fragments of the half in flight (A tiles 0-1, B tiles 0-3)
-    bf16x8 r0, r1, t0, t1, t2, t3;  // fragments of the other half
-#define SV_READ(S, HALF, A0, A1, B0, B1, B2, B3)                                                  \
-    {                                                                                            \
-        const uint32_t ab = ((S) < 2) ? ((HALF) ? a_h1 : a_h0) : ((HALF) ? a_h1_hi : a_h0_hi);  \
-        const uint32_t bb = ((S) < 2) ? ((HALF) ? b_h1 : b_h0) : ((HALF) ? b_h1_hi : b_h0_hi);  \
-        constexpr int so = ((S) & 1) * kSlot;                                                    \
-        A0 = lds_read(ab, IC<so + 0 * 2048>{});                                                 \
-        A1 = lds_read(ab, IC<so + 1 * 2048>{});                                                 \
-        B0 = lds_read(bb, IC<so + 0 * 2048>{});                                                 \
-        B1 = lds_read(bb, IC<so + 1 * 2048>{});                                                 \
-        B2 = lds_read(bb, IC<so + 2 * 2048>{});                                                 \
-        B3 = lds_read(bb, IC<so + 3 * 2048>{});                                                 \
+    bf16x8 p0, p1, q0, q1, q2, q3;  // fragments of one quarter (A tiles 0-1, B tiles 0-3)
+    bf16x8 r0, r1, t0, t1, t2, t3;  // fragments of the next
+#define SV_READ(AB, BB, A0, A1, B0, B1, B2, B3)                    \
+    {                                                              \
+        const uint32_t ab = (AB), bb = (BB);                       \
+        A0 = lds_read(ab, IC<0>{});                                \
+        A1 = lds_read(ab, IC<1 * kTileRows * kRowB>{});            \
+        B0 = lds_read(bb, IC<0>{});                                \
+        B1 = lds_read(bb, IC<1 * kTileRows * kRowB>{});            \
+        B2 = lds_read(bb, IC<2 * kTileRows * kRowB>{});            \
+        B3 = lds_read(bb, IC<3 * kTileRows * kRowB>{});            \
     }
 #define SV_MFMA(A0, A1, B0, B1, B2, B3)                                          \
     c00 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A0, B0, c00, 0, 0, 0);        \
@@ -167,36 +176,51 @@ __global__ __launch_bounds__(kLmThreads, 1) void k_lmhead_argmax(const uint4 *__
     c11 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A1, B1, c11, 0, 0, 0);        \
     c12 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A1, B2, c12, 0, 0, 0);        \
     c13 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A1, B3, c13, 0, 0, 0);
-#define SV_BARRIER() asm volatile("s_barrier" ::: "memory")
 
-    SV_ISSUE(0, 0)
-    SV_ISSUE(1, 1)
-    SV_ISSUE(2, 2)
-    wait_vm<2 * kLoadsPerStep>();  // this wave's loads of step 0 are done
-    SV_BARRIER();                  // and every wave's
-    SV_READ(0, 0, p0, p1, q0, q1, q2, q3)
-    // step s in slot S (past the end, the last step is loaded again into a
-    // slot nobody reads, and the h0 reads of the step after it are discarded)
-#define SV_STEP(S)                                                        \
-    SV_READ(S, 1, r0, r1, t0, t1, t2, t3)                                 \
-    LDS_WAIT6(p0, p1, q0, q1, q2, q3);                                    \
-    SV_MFMA(p0, p1, q0, q1, q2, q3)                                       \
-    wait_vm<kLoadsPerStep>();                                             \
-    SV_BARRIER();                                                         \
-    SV_ISSUE(((S) + 3) % kStages, min(s + (S) + 3, nk - 1))               \
-    SV_READ(((S) + 1) % kStages, 0, p0, p1, q0, q1, q2, q3)               \
-    LDS_WAIT6(r0, r1, t0, t1, t2, t3);                                    \
-    SV_MFMA(r0, r1, t0, t1, t2, t3)
-    // no branches inside the ring (a branch makes the compiler wait for every load)
-    for (int s = 0; s < nk; s += kStages) {
-        SV_STEP(0)
-        SV_STEP(1)
-        SV_STEP(2)
-        SV_STEP(3)
+    // prologue, in the order the steady state keeps (H(s + 2) then W(s + 3) per step)
+    SV_ISSUE_W(0, 0)
+    SV_ISSUE_H(0, 0)
+    SV_ISSUE_W(1, min(1, nk - 1))
+    SV_ISSUE_H(1, min(1, nk - 1))
+    SV_ISSUE_W(2, min(2, nk - 1))
+    wait_vm<3 * kDmaPerOperand>();  // this wave's W(0) and H(0) are in
+    SV_BARRIER();                   // and every wave's
+    uint32_t ho = 0, wo = 0;        // byte offsets of step s's H and W slots
+    int hs = 0, ws = 0;             // their slot numbers
+    SV_READ(a0 + ho, b0 + wo, p0, p1, q0, q1, q2, q3)
+    // past the end, the last step is loaded again into slots nobody reads, and
+    // the first quarter's reads of the step after the last are discarded
+    for (int s = 0; s < nk; ++s) {
+        const int hs_n = hs ^ 1, ws_n = ws == kWSlots - 1 ? 0 : ws + 1;
+        const uint32_t ho_n = static_cast<uint32_t>(hs_n * kSlab), wo_n = static_cast<uint32_t>(ws_n * kSlab);
+        SV_READ(a1 + ho, b1 + wo, r0, r1, t0, t1, t2, t3)
+        LDS_WAIT6(p0, p1, q0, q1, q2, q3);
+        SV_MFMA(p0, p1, q0, q1, q2, q3)
+        SV_READ(a2 + ho, b2 + wo, p0, p1, q0, q1, q2, q3)
+        LDS_WAIT6(r0, r1, t0, t1, t2, t3);
+        SV_MFMA(r0, r1, t0, t1, t2, t3)
+        SV_READ(a3 + ho, b3 + wo, r0, r1, t0, t1, t2, t3)
+        LDS_WAIT6(p0, p1, q0, q1, q2, q3);
+        // this wave's H(s + 1) and W(s + 1) are in: only W(s + 2), issued
+        // after them, may still be outstanding
+        wait_vm<kDmaPerOperand>();
+        SV_BARRIER();
+        SV_MFMA(p0, p1, q0, q1, q2, q3)
+        SV_READ(a0 + ho_n, b0 + wo_n, p0, p1, q0, q1, q2, q3)
+        LDS_WAIT6(r0, r1, t0, t1, t2, t3);
+        SV_BARRIER();  // every wave is done with step s's slots
+        SV_ISSUE_H(hs, min(s + 2, nk - 1))
+        SV_ISSUE_W(ws, min(s + 3, nk - 1))
+        SV_MFMA(r0, r1, t0, t1, t2, t3)
+        hs = hs_n;
+        ws = ws_n;
+        ho = ho_n;
+        wo = wo_n;
     }
-#undef SV_STEP
 #undef SV_MFMA
 #undef SV_READ
+#undef SV_ISSUE_W
+#undef SV_ISSUE_H
 #undef SV_ISSUE
     LDS_WAIT0(p0, p1, q0, q1, q2, q3);  // no LDS read still in flight
     wait_vm<0>();                       // no DMA may still target LDS when the workgroup ends
