@@ -357,25 +357,6 @@ def bench_lmhead(sv, torch, workloads, dev, reps):
         if rc:
             raise RuntimeError(f"spec_verify_greedy_lmhead failed: {rc}")
 
-    for _ in range(3):
-        fused()
-    torch.cuda.synchronize()
-    r = max(5, reps // 10)
-    t0 = time.perf_counter()
-    for _ in range(r):
-        fused()
-    torch.cuda.synchronize()
-    call_ms = (time.perf_counter() - t0) * 1e3 / r
-    sv.trace_begin(64, kernels=("lmhead", "match"))
-    for _ in range(r):
-        fused()
-    torch.cuda.synchronize()
-    per = {}
-    for name, ms in sv.trace_end(64):
-        per.setdefault(name, []).append(ms)
-    k_ms = statistics.mean(per["lmhead"])
-    flop = 2.0 * M * D * V
-
     # unfused reference: logits written by the library GEMM, then read by the verifier
     L = torch.empty((B, K + 1, V), dtype=torch.bfloat16, device=dev)
     Hm = H.reshape(M, D)
@@ -389,14 +370,33 @@ def bench_lmhead(sv, torch, workloads, dev, reps):
         if rc:
             raise RuntimeError(f"spec_verify_greedy failed: {rc}")
 
+    def timed(fn, r):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(r):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / r
+
+    # both run near the board's power limit, so the clock drifts with the work:
+    # warm both up, then alternate and keep each one's best of three rounds
+    for _ in range(10):
+        fused()
+        unfused()
+    r = max(10, reps // 5)
+    call_ms, unfused_ms = float("inf"), float("inf")
     for _ in range(3):
-        unfused()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
+        call_ms = min(call_ms, timed(fused, r))
+        unfused_ms = min(unfused_ms, timed(unfused, r))
+    sv.trace_begin(64, kernels=("lmhead", "match"))
     for _ in range(r):
-        unfused()
+        fused()
     torch.cuda.synchronize()
-    unfused_ms = (time.perf_counter() - t0) * 1e3 / r
+    per = {}
+    for name, ms in sv.trace_end(64):
+        per.setdefault(name, []).append(ms)
+    k_ms = statistics.mean(per["lmhead"])
+    flop = 2.0 * M * D * V
     del L, Lm
     return {
         "workload": f"greedy chain with the LM-head projection fused: B={B} K={K} D={D} V={V}, bf16 "
@@ -410,6 +410,7 @@ def bench_lmhead(sv, torch, workloads, dev, reps):
                      "traffic": (stored_traffic("lmhead") or {}).get("bytes_per_launch")},
         "unfused_reference": {"what": "torch.matmul (bf16 logits written to HBM) + spec_verify_greedy",
                               "call_ms": round(unfused_ms, 5)},
+        "timing": f"best of 3 rounds of {r} back-to-back calls each, fused and unfused alternating",
     }
 
 
