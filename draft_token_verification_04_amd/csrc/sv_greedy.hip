@@ -371,26 +371,66 @@ __global__ __launch_bounds__(kBlock) void k_skip_argmax(const typename E::storag
 // ---- trees: rows of rejected nodes are not read (N <= 64) ------------------------
 //
 // A node's row is needed only when the node is accepted: its argmax decides its
-// children and, for the chosen node, the bonus.  One launch over every (node j,
-// request b, segment) in node order (parents come before children).  A wave
-// skips its segment when node j is already known rejected.  The last wave of a
-// row (found by a ticket) takes its argmax a_j, marks the row done, and
-// rejects every child whose token differs from a_j together with the
-// descendants of every rejected node (parents, tokens and states of the
-// request's nodes held one per lane, the rejection closed over the tree by
-// ballots).  Each node is resolved once - row done or rejected, whichever is
-// first - and counted; the wave whose count completes the request's N nodes
-// walks the tree (every node that is not rejected has its row's argmax) and
-// writes the outputs, exactly as the full-read walk would.  Nothing waits.
+// children and, for the chosen node, the bonus.  A first small launch
+// (k_tree_prep, one wave per request) clears the control words and ranks each
+// request's nodes by (depth, index): slot i of the request holds the node of
+// rank i.  The main launch runs over every (slot i, request b, segment) in
+// slot order, so every node of depth d is read before any of depth d + 1 and
+// the decisions about a level have usually landed before the next level's
+// waves start (in plain index order, a deep chain listed early would be read
+// before its first node is decided).  A wave skips its segment when the node of
+// its slot is already known rejected.  The last wave of a row (found by a
+// ticket) takes its argmax a_j, marks the row done, and rejects every child
+// whose token differs from a_j together with the descendants of every rejected
+// node (parents, tokens and states of the request's nodes held one per lane,
+// the rejection closed over the tree by ballots).  Each node is resolved once -
+// row done or rejected, whichever is first - and counted; the wave whose count
+// completes the request's N nodes walks the tree (every node that is not
+// rejected has its row's argmax) and writes the outputs, exactly as the
+// full-read walk would.  Nothing waits.
 
 constexpr unsigned kRowDone = 1u, kRejected = 2u;
 constexpr int kTreeSkipMaxN = kWave;
 
 struct TreeCtl {
-    unsigned *ticket;    // [B*N] segments finished per node row
-    unsigned *state;     // [B*N] kRowDone | kRejected
+    unsigned *ticket;    // [B*N] segments finished, per slot
+    unsigned *state;     // [B*N] kRowDone | kRejected of the node in each slot
     unsigned *resolved;  // [B] nodes resolved
+    int32_t *order;      // [B*N] node of each slot (ascending depth, then index)
+    int32_t *rank;       // [B*N] slot of each node
 };
+
+// Per request (one wave): clear its control words and rank its nodes by
+// (depth, index).  Depths come from pointer jumping over the lanes; a parent
+// outside [0, j) counts as the root here (the walk flags such a request), so
+// the slots are always a permutation of the nodes.
+__global__ __launch_bounds__(kBlock) void k_tree_prep(const int32_t *__restrict__ par, int B, int N,
+                                                      TreeCtl ctl) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int b = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+    if (b >= B) return;
+    const long long base = static_cast<long long>(b) * N;
+    const bool in = lane < N;
+    const int p = in ? par[base + lane] : 0;
+    int anc = (lane == 0 || !in || p < 0 || p >= lane) ? 0 : p;
+    int dep = (lane == 0 || !in) ? 0 : 1;
+    for (int span = 1; span < N; span <<= 1) {
+        const int d2 = __shfl(dep, anc, kWave);
+        const int a2 = __shfl(anc, anc, kWave);
+        dep += d2;
+        anc = a2;
+    }
+    const unsigned key = in ? ((static_cast<unsigned>(dep) << 8) | static_cast<unsigned>(lane)) : 0xffffffffu;
+    int rk = 0;
+    for (int o = 0; o < N; ++o) rk += static_cast<unsigned>(__shfl(static_cast<int>(key), o, kWave)) < key;
+    if (in) {
+        ctl.order[base + rk] = lane;
+        ctl.rank[base + lane] = rk;
+        ctl.ticket[base + lane] = 0u;
+        ctl.state[base + lane] = 0u;
+    }
+    if (lane == 0) ctl.resolved[b] = 0u;
+}
 
 // Node j's outputs of request b once every node is resolved (one wave).
 __device__ __forceinline__ void tree_finish(const int32_t *__restrict__ tok, const int32_t *__restrict__ par,
@@ -402,7 +442,8 @@ __device__ __forceinline__ void tree_finish(const int32_t *__restrict__ tok, con
     const bool in = lane < N;
     const int p = in ? par[base + lane] : 0;
     const int t = in ? tok[base + lane] : 0;
-    const unsigned st = in ? shared_load(&ctl.state[base + lane]) : 0u;
+    const int rk = in ? ctl.rank[base + lane] : 0;
+    const unsigned st = in ? shared_load(&ctl.state[base + rk]) : 0u;
     const int a = in && (st & kRowDone) ? shared_load(const_cast<int32_t *>(&amax[base + lane])) : -1;
     const bool bad_par = ballot(in && (lane == 0 ? p != -1 : (p < 0 || p >= lane))) != 0;
     const bool oor = ballot(in && lane > 0 && (t < 0 || t >= V)) != 0;
@@ -471,21 +512,22 @@ __global__ __launch_bounds__(kBlock) void k_skip_tree(const typename E::storage 
                                                       int32_t *__restrict__ status) {
     const int lane = threadIdx.x & (kWave - 1);
     const long long wave = static_cast<long long>(blockIdx.x) * kWavesPerBlock + (threadIdx.x >> 6);
-    const long long per_node = static_cast<long long>(B) * segs;
-    if (wave >= per_node * N) return;
-    const int j = static_cast<int>(wave / per_node);
-    const long long rem = wave - static_cast<long long>(j) * per_node;
+    const long long per_slot = static_cast<long long>(B) * segs;
+    if (wave >= per_slot * N) return;
+    const int slot = static_cast<int>(wave / per_slot);
+    const long long rem = wave - static_cast<long long>(slot) * per_slot;
     const int b = static_cast<int>(rem / segs);
     const int sg = static_cast<int>(rem - static_cast<long long>(b) * segs);
     const long long base = static_cast<long long>(b) * N;
-    if (uniform(shared_load(&ctl.state[base + j])) & kRejected) return;
+    const int j = uniform(ctl.order[base + slot]);  // issued beside the state load
+    if (uniform(shared_load(&ctl.state[base + slot])) & kRejected) return;
 
     const long long row = base + j;
     const int v0 = static_cast<int>((static_cast<long long>(sg) * nvec) / segs);
     const int v1 = static_cast<int>((static_cast<long long>(sg + 1) * nvec) / segs);
     const uint64_t key = segment_argmax_chunked<E, ALIGNED, U, kGSkipChunks>(L + row * V, V, v0, v1, lane);
     if (lane == 0) shared_store(&part_k[row * segs + sg], key);
-    if (!wave_arrive(&ctl.ticket[row], static_cast<unsigned>(segs), lane)) return;
+    if (!wave_arrive(&ctl.ticket[base + slot], static_cast<unsigned>(segs), lane)) return;
 
     // last segment of node j's row: its argmax decides j's children
     uint64_t mk = 0;
@@ -499,8 +541,9 @@ __global__ __launch_bounds__(kBlock) void k_skip_tree(const typename E::storage 
     const bool in = lane < N;
     const int p = in ? par[base + lane] : -1;
     const int t = in ? tok[base + lane] : 0;
+    const int rk = in ? ctl.rank[base + lane] : 0;
     // states as they stand, plus this row done and this row's mismatching children
-    unsigned st = in ? shared_load(&ctl.state[base + lane]) : 0u;
+    unsigned st = in ? shared_load(&ctl.state[base + rk]) : 0u;
     uint64_t rej = ballot(in && ((st & kRejected) || (lane > 0 && p == j && t != a)));
     // close the rejection over the tree: a node under a rejected parent is rejected
     for (int it = 0; it < N; ++it) {
@@ -514,7 +557,7 @@ __global__ __launch_bounds__(kBlock) void k_skip_tree(const typename E::storage 
     if (in && ((rej >> lane) & 1ull)) mark |= kRejected;
     int newly = 0;
     if (mark) {
-        const unsigned old = __hip_atomic_fetch_or(&ctl.state[base + lane], mark, __ATOMIC_RELAXED,
+        const unsigned old = __hip_atomic_fetch_or(&ctl.state[base + rk], mark, __ATOMIC_RELAXED,
                                                    __HIP_MEMORY_SCOPE_AGENT);
         newly = old == 0 ? 1 : 0;
     }
@@ -599,17 +642,23 @@ hipError_t launch_skip_match(const void *L, const int32_t *drafts, int B, int K,
 
 bool tree_skip_supported(int N) { return N <= kTreeSkipMaxN; }
 
-size_t tree_ctl_bytes(int B, int N) { return sizeof(unsigned) * (2 * static_cast<size_t>(B) * N + B); }
+size_t tree_ctl_bytes(int B, int N) { return sizeof(unsigned) * (4 * static_cast<size_t>(B) * N + B); }
 
 hipError_t launch_skip_tree(const void *L, const int32_t *node_tokens, const int32_t *parents, int B, int N,
                             int V, const RowGeom &g, sv_dtype dt, uint64_t *part_k, int32_t *amax,
                             void *ctl_base, int32_t *accept_len, int32_t *path_nodes, int32_t *out_tokens,
                             int32_t *status, hipStream_t s) {
     TreeCtl ctl;
+    const size_t bn = static_cast<size_t>(B) * N;
     ctl.ticket = static_cast<unsigned *>(ctl_base);
-    ctl.state = ctl.ticket + static_cast<size_t>(B) * N;
-    ctl.resolved = ctl.state + static_cast<size_t>(B) * N;
-    hipError_t e = clear_words(ctl_base, tree_ctl_bytes(B, N), s);
+    ctl.state = ctl.ticket + bn;
+    ctl.order = reinterpret_cast<int32_t *>(ctl.state + bn);
+    ctl.rank = ctl.order + bn;
+    ctl.resolved = reinterpret_cast<unsigned *>(ctl.rank + bn);
+    trace_select(-1);  // the preparing launch is not traced
+    hipLaunchKernelGGL(k_tree_prep, dim3(static_cast<unsigned>((B + kWavesPerBlock - 1) / kWavesPerBlock)),
+                       dim3(kBlock), 0, s, parents, B, N, ctl);
+    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     trace_select(SV_K_SKIP_TREE);
 #define SV_ST(E, A) skip_tree_t<E, A>(L, node_tokens, parents, B, N, V, g, part_k, amax, ctl, accept_len, path_nodes, out_tokens, status, s)
