@@ -531,13 +531,18 @@ def main():
         modes[m] = {"rows": rows_mode[m], "bytes": bytes_mode[m], "kernel_ms": round(kt, 5),
                     "rows_per_s": round(rows_mode[m] / (kt * 1e-3), 1),
                     "gbps": round(bytes_mode[m] / (kt * 1e-3) / 1e9, 1)}
-    if "sample" in modes:
-        modes["sample"]["mean_tokens_per_round"] = round(float(n3.mean() + 1), 4)
+    # tokens emitted per request: the accepted drafts plus the one target token
+    emitted = {"sample": n3 + 1, "greedy": n4 + 1, "tree": calls.t_n.cpu().numpy() + 1}
+    batch = {"sample": w3.B, "greedy": w4.B, "tree": w5.B}
+    for m in active:
+        kt = modes[m]["kernel_ms"] * 1e-3
+        modes[m]["mean_tokens_per_round"] = round(float(emitted[m].mean()), 4)
+        modes[m]["requests_per_s"] = round(batch[m] / kt, 1)
+        modes[m]["tokens_per_s"] = round(float(emitted[m].sum()) / kt, 1)
     if "greedy" in modes:
-        modes["greedy"]["mean_tokens_per_round"] = round(float(n4.mean() + 1), 4)
+        modes["greedy"]["dense_bytes"] = w4.B * (w4.K + 1) * R
     if "tree" in modes:
         modes["tree"]["dense_bytes"] = w5.B * w5.N * R
-        modes["greedy"]["dense_bytes"] = w4.B * (w4.K + 1) * R
 
     # each call on its own, back to back (launch gaps included)
     def per_call(fn, reps):
