@@ -54,8 +54,9 @@ constexpr int kSkipChunks = SV_SKIP_CHUNKS;
 #endif
 constexpr int kGSkipVecsPerLane = SV_GSKIP_VECS;
 constexpr int kGSkipChunks = SV_GSKIP_CHUNKS;
-// Waves the residual-mass pass aims for (about two per SIMD).
-constexpr int kResidTargetWaves = 4096;
+// Waves the residual-mass pass aims for: short waves of a few tiles each
+// (measured: 28 us per pass at B=256 against 32 us with 4096 longer waves).
+constexpr int kResidTargetWaves = 32768;
 // Bytes of LDS the per-request merge kernels use to stage row partials.
 constexpr int kMergeLdsBytes = 24 * 1024;
 
