@@ -227,37 +227,57 @@ __global__ __launch_bounds__(kBlock) void k_accept(
             }
             __syncthreads();
         }
-        for (int rr = wid; rr < nr; rr += kWavesPerBlock) {
-            const int r = r0 + rr;
-            const float *pR;
-            const double *pS;
-            if (lds_rows > 0) {
-                pR = stR + rr * segs;
-                pS = stS + rr * segs;
-            } else {
-                const long long g = req_row(b, K, rows_t, r) * segs;
-                pR = part_R + g;
-                pS = part_s + g;
+        // a wave merges kMergeILP rows at once (rows wid, wid + 4, ...): the
+        // rows are independent, so their loads, exponentials and reductions
+        // overlap; each row is still reduced in the same order
+        constexpr int kMergeILP = 4;
+        for (int rb = wid; rb < nr; rb += kMergeILP * kWavesPerBlock) {
+            const float *pR[kMergeILP];
+            const double *pS[kMergeILP];
+            bool ok[kMergeILP];
+            float Rm[kMergeILP];
+            double acc[kMergeILP];
+#pragma unroll
+            for (int q = 0; q < kMergeILP; ++q) {
+                const int rr = rb + q * kWavesPerBlock;
+                ok[q] = rr < nr;
+                const int rc = ok[q] ? rr : rb;
+                if (lds_rows > 0) {
+                    pR[q] = stR + rc * segs;
+                    pS[q] = stS + rc * segs;
+                } else {
+                    const long long g = req_row(b, K, rows_t, r0 + rc) * segs;
+                    pR[q] = part_R + g;
+                    pS[q] = part_s + g;
+                }
+                Rm[q] = -__builtin_huge_valf();
+                for (int sg = lane; sg < segs; sg += kWave) Rm[q] = fmaxf(Rm[q], pR[q][sg]);
             }
-            float Rm = -__builtin_huge_valf();
-            for (int sg = lane; sg < segs; sg += kWave) Rm = fmaxf(Rm, pR[sg]);
-            Rm = wave_max(Rm);
-            double acc = 0.0;
-            if (Rm != -__builtin_huge_valf()) {
-                for (int sg = lane; sg < segs; sg += kWave) {
-                    const double ss = pS[sg];
-                    if (ss > 0.0) acc += ss * exp2(static_cast<double>(pR[sg]) - static_cast<double>(Rm));
+#pragma unroll
+            for (int q = 0; q < kMergeILP; ++q) {
+                Rm[q] = wave_max(Rm[q]);
+                acc[q] = 0.0;
+                if (Rm[q] != -__builtin_huge_valf()) {
+                    for (int sg = lane; sg < segs; sg += kWave) {
+                        const double ss = pS[q][sg];
+                        if (ss > 0.0)
+                            acc[q] += ss * exp2(static_cast<double>(pR[q][sg]) - static_cast<double>(Rm[q]));
+                    }
                 }
             }
-            acc = wave_sum(acc);
-            const double l2 = acc > 0.0 ? static_cast<double>(Rm) + log2(acc) : -inf;
-            if (lane == 0) {
-                sL2[r] = l2;
-                L2out[static_cast<long long>(b) * nrows + r] = l2;
-                if (r <= K) {
-                    if (lse_t) lse_t[static_cast<long long>(b) * (K + 1) + r] = static_cast<float>(l2 * kLn2);
-                } else if (lse_d) {
-                    lse_d[static_cast<long long>(b) * K + (r - K - 1)] = static_cast<float>(l2 * kLn2);
+#pragma unroll
+            for (int q = 0; q < kMergeILP; ++q) {
+                acc[q] = wave_sum(acc[q]);
+                const int r = r0 + rb + q * kWavesPerBlock;
+                const double l2 = acc[q] > 0.0 ? static_cast<double>(Rm[q]) + log2(acc[q]) : -inf;
+                if (ok[q] && lane == 0) {
+                    sL2[r] = l2;
+                    L2out[static_cast<long long>(b) * nrows + r] = l2;
+                    if (r <= K) {
+                        if (lse_t) lse_t[static_cast<long long>(b) * (K + 1) + r] = static_cast<float>(l2 * kLn2);
+                    } else if (lse_d) {
+                        lse_d[static_cast<long long>(b) * K + (r - K - 1)] = static_cast<float>(l2 * kLn2);
+                    }
                 }
             }
         }
