@@ -14,9 +14,10 @@
 // the lanes whose token is the anchor; only when one does are the other n - 1
 // tokens of each window fetched from neighbouring lanes by shuffles.
 //   k_ngram<false>  counts the candidates of each (request, chunk);
-//   k_ngram<true>   sums the counts of the earlier chunks of its request and
-//                   writes its candidates at that offset, in ascending order;
-//                   the wave of chunk 0 writes the request's total and status.
+//   k_ngram<true>   skips a chunk whose count is zero; otherwise sums the
+//                   counts of the earlier chunks of its request and writes its
+//                   candidates at that offset, in ascending order; the wave of
+//                   chunk 0 writes the request's total and status.
 #include "sv_device.hpp"
 #include "sv_internal.hpp"
 
@@ -61,6 +62,8 @@ __global__ __launch_bounds__(kBlock) void k_ngram(const int32_t *__restrict__ ct
         if (!EMIT && lane == 0) counts[static_cast<long long>(b) * nchunks + chunk] = 0;
         return;
     }
+    // a chunk without candidates has nothing to emit (most chunks: candidates are rare)
+    if (EMIT && uniform(counts[static_cast<long long>(b) * nchunks + chunk]) == 0) return;
     const int32_t *row = ctx + static_cast<long long>(b) * L;
     const int qreg = lane < n ? queries[static_cast<long long>(b) * n + lane] : 0;
     const int anchor = uniform(__shfl(qreg, n - 1, kWave));
