@@ -326,3 +326,40 @@ def test_trace_records_each_kernel():
     gpu_tree(wt)
     recs = sv.trace_end()
     assert [r[0] for r in recs] == ["skip_tree"]
+
+
+def test_maximum_draft_length_and_tree_size():
+    # the largest chain (K = SV_MAX_DRAFT_LEN) and tree (N = SV_MAX_TREE_NODES) the
+    # library accepts, on a short vocabulary so the oracle stays quick
+    K, N = 1024, sv.SV_MAX_TREE_NODES
+    note(f"max sizes K={K} N={N}")
+    for noise, seed in ((0.0, 51), (0.05, 52)):   # q = p (every draft accepted), then some rejections
+        w = workloads.make_sample(3, K, 64, "f32", 1.0, spikes=0, noise_sigma=noise, seed=seed)
+        o = oracle_sample(w)
+        for lse in (True, False):
+            g = gpu_sample(w, lse=lse)
+            check_sample(w, g, o)
+        if noise == 0.0:
+            assert (o["accept_len"] == K).all()
+    for p_match, seed in ((1.0, 53), (0.998, 54)):
+        wg = workloads.make_greedy(3, K, 50, "f32", p_match=p_match, seed=seed)
+        og = oracle.verify_greedy(wg.target, wg.draft_tokens)
+        check_exact(gpu_greedy(wg), og, ("accept_len", "tokens", "status"))
+        if p_match == 1.0:
+            assert (og["accept_len"] == K).all()
+    rng = np.random.default_rng(55)
+    B, V = 3, 40
+    L = rng.standard_normal((B, N, V)).astype(np.float32)
+    par = np.empty((B, N), np.int32)
+    par[:, 0] = -1
+    par[0, 1:] = np.arange(N - 1)                      # one chain through every node
+    for j in range(1, N):
+        par[1:, j] = rng.integers(max(0, j - 8), j, size=B - 1)
+    am = oracle.argmax(L)
+    pam = np.take_along_axis(am, np.maximum(par, 0), 1)
+    tok = np.where(rng.random((B, N)) < 0.97, pam, rng.integers(0, V, (B, N))).astype(np.int32)
+    tok[0] = pam[0]                                   # the chain is accepted to its end
+    w = workloads.Workload(mode="tree", B=B, N=N, V=V, dtype="f32", target=L, node_tokens=tok, parents=par)
+    ot = oracle.verify_tree(L, tok, par)
+    check_exact(gpu_tree(w), ot, ("accept_len", "path", "tokens", "status"))
+    assert ot["accept_len"][0] == N - 1
