@@ -1,0 +1,84 @@
+"""The entry points inside a captured HIP graph: every launch they make is a
+kernel (their control words are cleared by kernels, never by memsets), so a
+captured verification step replays correctly.  Each replay, with eager work and
+synchronisation between replays and the inputs rewritten in place, must equal
+an eager call on the same inputs."""
+
+import numpy as np
+import torch
+
+import draft_token_verification_04_amd as sv
+import workloads
+from gpu_helpers import dev, f32_to_dev, ints_to_dev, logits_to_dev, note
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+
+def _np(d):
+    return {k: v.cpu().numpy() for k, v in d.items()}
+
+
+def test_verification_step_replays_inside_a_graph():
+    note("graph capture and replay")
+    w3 = workloads.make_sample(32, 7, 20000, "bf16", 0.8, spikes=10, noise_sigma=1.0, seed=61)
+    w3b = workloads.make_sample(32, 7, 20000, "bf16", 0.8, spikes=10, noise_sigma=2.0, seed=62)
+    w4 = workloads.make_greedy(32, 7, 20000, "bf16", seed=63)
+    w4b = workloads.make_greedy(32, 7, 20000, "bf16", p_match=0.5, seed=64)
+    w5 = workloads.make_tree(16, 20000, "bf16", seed=65)
+    w5b = workloads.make_tree(16, 20000, "bf16", p_match=0.4, seed=66)
+    assert w5b.N == w5.N
+    # static inputs, rewritten in place between replays
+    s_t, s_d = logits_to_dev(w3.target), logits_to_dev(w3.draft)
+    s_x, s_ua, s_us = ints_to_dev(w3.draft_tokens), f32_to_dev(w3.u_accept), f32_to_dev(w3.u_sample)
+    g_t, g_x = logits_to_dev(w4.target), ints_to_dev(w4.draft_tokens)
+    t_t, t_tok, t_par = logits_to_dev(w5.target), ints_to_dev(w5.node_tokens), ints_to_dev(w5.parents)
+
+    def load(a, b, c):
+        s_t.copy_(logits_to_dev(a.target))
+        s_d.copy_(logits_to_dev(a.draft))
+        s_x.copy_(ints_to_dev(a.draft_tokens))
+        s_ua.copy_(f32_to_dev(a.u_accept))
+        s_us.copy_(f32_to_dev(a.u_sample))
+        g_t.copy_(logits_to_dev(b.target))
+        g_x.copy_(ints_to_dev(b.draft_tokens))
+        t_t.copy_(logits_to_dev(c.target))
+        t_tok.copy_(ints_to_dev(c.node_tokens))
+        t_par.copy_(ints_to_dev(c.parents))
+
+    def step():
+        return dict(
+            sample=sv.spec_verify_sample(s_t, s_d, s_x, s_ua, s_us, w3.T),
+            sample_skip=sv.spec_verify_sample(s_t, s_d, s_x, s_ua, s_us, w3.T, lse=False),
+            greedy=sv.spec_verify_greedy(g_t, g_x),
+            tree=sv.spec_verify_tree(t_t, t_tok, t_par))
+
+    def eager():
+        out = step()
+        torch.cuda.synchronize()
+        return {k: _np(v) for k, v in out.items()}
+
+    want = {}
+    for name, sets in (("a", (w3, w4, w5)), ("b", (w3b, w4b, w5b))):
+        load(*sets)
+        want[name] = eager()
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        captured = step()
+    for rep, name in enumerate(("a", "b", "a", "b")):
+        load(*((w3, w4, w5) if name == "a" else (w3b, w4b, w5b)))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = {k: _np(v) for k, v in captured.items()}
+        for call, outs in want[name].items():
+            for key, ref in outs.items():
+                assert np.array_equal(got[call][key], ref), (rep, call, key)
+        eager()  # eager work between replays
