@@ -162,6 +162,17 @@ class Calls:
                           P(self.t_n), P(self.t_path), P(self.t_out), P(self.t_st), P(self.t_ws),
                           self.t_ws.numel(), self.stream)
 
+    def on_stream(self, stream_ptr):
+        """The same calls (same buffers) enqueued on another stream."""
+        import copy
+
+        c = copy.copy(self)
+        c.stream = ctypes.c_void_p(stream_ptr)
+        c.sample_args = self.sample_args[:-1] + (c.stream,)
+        c.greedy_args = self.greedy_args[:-1] + (c.stream,)
+        c.tree_args = self.tree_args[:-1] + (c.stream,)
+        return c
+
     def sample(self):
         rc = self.lib.spec_verify_sample(*self.sample_args)
         if rc:
@@ -470,6 +481,31 @@ def main():
     per_kernel = {}
     for name, ms in recs:
         per_kernel.setdefault(name, []).append(ms)
+
+    # the same step captured once in a HIP graph and replayed (launch overhead
+    # out of the host's hands); reported beside the eager figure
+    gstream = torch.cuda.Stream()
+    gcalls = calls.on_stream(gstream.cuda_stream)
+    gparts = {"sample": gcalls.sample, "greedy": gcalls.greedy, "tree": gcalls.tree}
+    gstream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(gstream):
+        for _ in range(3):
+            for m in active:
+                gparts[m]()
+    torch.cuda.current_stream().wait_stream(gstream)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=gstream):
+        for m in active:
+            gparts[m]()
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    tg0 = time.perf_counter()
+    for _ in range(args.steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    graph_ms_per_step = (time.perf_counter() - tg0) * 1e3 / args.steps
     # breakdown of every kernel from a separate, untimed traced pass
     nb = max(3, min(args.steps, 10))
     sv.trace_begin(nb * 8 + 16)
@@ -697,6 +733,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
+        "graph_ms_per_step": round(graph_ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
