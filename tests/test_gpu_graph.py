@@ -82,3 +82,32 @@ def test_verification_step_replays_inside_a_graph():
             for key, ref in outs.items():
                 assert np.array_equal(got[call][key], ref), (rep, call, key)
         eager()  # eager work between replays
+
+
+def test_concurrent_calls_on_two_streams():
+    # separate workspaces make calls on different streams independent, including
+    # the row-skipping passes whose control words live in the workspace
+    note("two streams")
+    ws = [workloads.make_greedy(48, 7, 30000, "bf16", seed=71 + i) for i in range(2)]
+    wt = [workloads.make_tree(24, 30000, "bf16", seed=73 + i) for i in range(2)]
+    ins = [(logits_to_dev(w.target), ints_to_dev(w.draft_tokens)) for w in ws]
+    tins = [(logits_to_dev(w.target), ints_to_dev(w.node_tokens), ints_to_dev(w.parents)) for w in wt]
+    want = []
+    for (t, x), (tt, tok, par) in zip(ins, tins):
+        a, b = sv.spec_verify_greedy(t, x), sv.spec_verify_tree(tt, tok, par)
+        torch.cuda.synchronize()
+        want.append((_np(a), _np(b)))
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    for rep in range(5):
+        outs = []
+        for s, (t, x), (tt, tok, par) in zip(streams, ins, tins):
+            with torch.cuda.stream(s):
+                outs.append((sv.spec_verify_greedy(t, x), sv.spec_verify_tree(tt, tok, par)))
+        torch.cuda.synchronize()
+        for (a, b), (wa, wb) in zip(outs, want):
+            for k in wa:
+                assert np.array_equal(_np(a)[k], wa[k]), (rep, k)
+            for k in wb:
+                assert np.array_equal(_np(b)[k], wb[k]), (rep, k)
