@@ -197,3 +197,31 @@ def test_read_probe_argument_checks(lib):
     assert lib.sv_read_probe_folds(16384) == 1
     assert lib.sv_read_probe_folds(16384 + 16) == 2
     assert lib.sv_kernel_name(14) == b"read_probe"
+
+
+def test_header_is_plain_c_and_links(tmp_path):
+    # the boundary is a C ABI: the header compiles as C99 with warnings as errors,
+    # and a C program links against the library and calls its host-only queries
+    import shutil
+    import subprocess
+
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    src = tmp_path / "abi.c"
+    src.write_text(
+        '#include "spec_verify.h"\n'
+        "#include <stdio.h>\n"
+        "int main(void) {\n"
+        "    size_t a = sv_sample_workspace_bytes(256, 7, 151936, SV_BF16);\n"
+        "    size_t b = sv_greedy_workspace_bytes(64, 33, 151936, SV_BF16);\n"
+        "    printf(\"%s %zu %zu %s\\n\", sv_version(), a, b, sv_status_string(SV_ERR_WORKSPACE));\n"
+        "    return (a > 0 && b > 0) ? 0 : 1;\n"
+        "}\n")
+    exe = tmp_path / "abi"
+    libdir = os.path.dirname(sv.LIB_PATH)
+    subprocess.run([cc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic", f"-I{os.path.dirname(HEADER)}",
+                    str(src), "-o", str(exe), f"-L{libdir}", "-lspecverify", f"-Wl,-rpath,{libdir}"],
+                   check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout
+    assert "gfx950" in out and "workspace too small" in out
