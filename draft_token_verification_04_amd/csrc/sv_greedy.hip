@@ -24,6 +24,10 @@
 //             rows after each request's first mismatch (the protocol is
 //             described with SkipCtl); the decision of position p is the row
 //             argmax compared with draft p.
+//   k_tree_prep, k_skip_tree  trees with N <= 64: a small launch clears the
+//             control words and ranks each request's nodes by depth, then one
+//             launch reads the node rows level by level, skipping the rows of
+//             nodes already known rejected (described with TreeCtl).
 #include <limits.h>
 
 #include <algorithm>
