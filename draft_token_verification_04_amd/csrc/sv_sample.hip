@@ -7,12 +7,13 @@
 // position, or from the next-position distribution when all drafts pass) and
 // "为什么“猜错再改”不会偏离目标分布" (residual norm(max(0, p - q))).
 //
-// Four kernels, all on the caller's stream:
+// Kernels, all on the caller's stream:
 //   k_rowstats     one streaming pass over every target row [B,K+1,V] and draft
 //                  row [B,K,V]; each wave reduces a segment of a row to a
 //                  partial (R, s) with s = sum 2^(x c - R), c = log2(e)/T.
 //   k_accept       one workgroup per request: stages the partials of its 2K+1
-//                  rows in LDS, merges each row (one wave per row) into
+//                  rows in LDS, merges each row (a wave merges four rows at
+//                  once) into
 //                  L2 = log2 sum_v 2^(x c), gathers L[x_i] for every draft,
 //                  forms p_i(x_i)/q_i(x_i) in fp64 and finds the first
 //                  rejection; writes accept_len, the accepted tokens, lse.
@@ -21,6 +22,10 @@
 //   k_resid_select one wave per request: prefix over tile masses, then over
 //                  lanes of the chosen tile, then over the elements of the
 //                  chosen lane; writes the drawn token.
+//   k_skip_stats   without lse outputs and for K <= 31, k_rowstats and the
+//                  acceptance in one launch that does not read the rows of
+//                  positions after each request's first rejection (protocol in
+//                  sv_skip.hpp); the residual kernels then run as above.
 //
 // Precision: per-element exponentials run in fp32 on v_exp_f32 with the
 // exponent formed by two fused multiply-adds against c = c_hi + c_lo, so the
