@@ -506,6 +506,25 @@ def main():
         graph.replay()
     torch.cuda.synchronize()
     graph_ms_per_step = (time.perf_counter() - tg0) * 1e3 / args.steps
+
+    # the same step when no lse output is wanted: the stochastic chain then
+    # skips the rows after each request's first rejection too
+    step_no_lse = None
+    if "sample" in active:
+        nparts = dict(parts, sample=calls.sample_skip)
+        for _ in range(args.warmup):
+            for m in active:
+                nparts[m]()
+        torch.cuda.synchronize()
+        tn0 = time.perf_counter()
+        for _ in range(args.steps):
+            for m in active:
+                nparts[m]()
+        torch.cuda.synchronize()
+        ms_nl = (time.perf_counter() - tn0) * 1e3 / args.steps
+        step_no_lse = {"ms_per_step": round(ms_nl, 5),
+                       "rows_per_s": round(sum({"sample": w3.B * (w3.K + 1), "greedy": w4.B * (w4.K + 1),
+                                                "tree": w5.B * w5.N}[m] for m in active) / (ms_nl * 1e-3), 1)}
     # breakdown of every kernel from a separate, untimed traced pass
     nb = max(3, min(args.steps, 10))
     sv.trace_begin(nb * 8 + 16)
@@ -734,6 +753,7 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
         "graph_ms_per_step": round(graph_ms_per_step, 5),
+        "step_without_lse": step_no_lse,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
