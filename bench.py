@@ -425,6 +425,71 @@ def bench_lmhead(sv, torch, workloads, dev, reps):
     }
 
 
+def time_graph_step(torch, calls, active, args):
+    """ms per step when the step is captured once in a HIP graph and replayed
+    (launch overhead out of the host's hands)."""
+    gstream = torch.cuda.Stream()
+    gcalls = calls.on_stream(gstream.cuda_stream)
+    gparts = {"sample": gcalls.sample, "greedy": gcalls.greedy, "tree": gcalls.tree}
+    gstream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(gstream):
+        for _ in range(3):
+            for m in active:
+                gparts[m]()
+    torch.cuda.current_stream().wait_stream(gstream)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=gstream):
+        for m in active:
+            gparts[m]()
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / args.steps
+
+
+def time_step_without_lse(torch, calls, parts, active, args, w3, w4, w5):
+    """The step with the stochastic chain called without lse outputs (its
+    row-skipping pass runs); None when the stochastic chain is not in the step."""
+    if "sample" not in active:
+        return None
+    nparts = dict(parts, sample=calls.sample_skip)
+    for _ in range(args.warmup):
+        for m in active:
+            nparts[m]()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        for m in active:
+            nparts[m]()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    rows = {"sample": w3.B * (w3.K + 1), "greedy": w4.B * (w4.K + 1), "tree": w5.B * w5.N}
+    return {"ms_per_step": round(ms, 5),
+            "rows_per_s": round(sum(rows[m] for m in active) / (ms * 1e-3), 1)}
+
+
+def read_ceiling(sv, torch, dev):
+    """GB/s of sv_read_probe over 4 GiB of random bytes (mean of 20 launches)."""
+    probe = torch.randint(-2**31, 2**31 - 1, (1 << 30,), dtype=torch.int32, device=dev)
+    folds = sv.sv_read_probe(probe)
+    for _ in range(2):
+        sv.sv_read_probe(probe, folds=folds)
+    torch.cuda.synchronize()
+    sv.trace_begin(64, kernels=("read_probe",))
+    for _ in range(20):
+        sv.sv_read_probe(probe, folds=folds)
+    torch.cuda.synchronize()
+    ms = statistics.mean(t for _, t in sv.trace_end(64))
+    gbps = probe.numel() * 4 / (ms * 1e-3) / 1e9
+    del probe
+    return gbps
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -482,49 +547,10 @@ def main():
     for name, ms in recs:
         per_kernel.setdefault(name, []).append(ms)
 
-    # the same step captured once in a HIP graph and replayed (launch overhead
-    # out of the host's hands); reported beside the eager figure
-    gstream = torch.cuda.Stream()
-    gcalls = calls.on_stream(gstream.cuda_stream)
-    gparts = {"sample": gcalls.sample, "greedy": gcalls.greedy, "tree": gcalls.tree}
-    gstream.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(gstream):
-        for _ in range(3):
-            for m in active:
-                gparts[m]()
-    torch.cuda.current_stream().wait_stream(gstream)
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph, stream=gstream):
-        for m in active:
-            gparts[m]()
-    for _ in range(args.warmup):
-        graph.replay()
-    torch.cuda.synchronize()
-    tg0 = time.perf_counter()
-    for _ in range(args.steps):
-        graph.replay()
-    torch.cuda.synchronize()
-    graph_ms_per_step = (time.perf_counter() - tg0) * 1e3 / args.steps
+    graph_ms_per_step = time_graph_step(torch, calls, active, args)
 
-    # the same step when no lse output is wanted: the stochastic chain then
-    # skips the rows after each request's first rejection too
-    step_no_lse = None
-    if "sample" in active:
-        nparts = dict(parts, sample=calls.sample_skip)
-        for _ in range(args.warmup):
-            for m in active:
-                nparts[m]()
-        torch.cuda.synchronize()
-        tn0 = time.perf_counter()
-        for _ in range(args.steps):
-            for m in active:
-                nparts[m]()
-        torch.cuda.synchronize()
-        ms_nl = (time.perf_counter() - tn0) * 1e3 / args.steps
-        step_no_lse = {"ms_per_step": round(ms_nl, 5),
-                       "rows_per_s": round(sum({"sample": w3.B * (w3.K + 1), "greedy": w4.B * (w4.K + 1),
-                                                "tree": w5.B * w5.N}[m] for m in active) / (ms_nl * 1e-3), 1)}
+    step_no_lse = time_step_without_lse(torch, calls, parts, active, args, w3, w4, w5)
+
     # breakdown of every kernel from a separate, untimed traced pass
     nb = max(3, min(args.steps, 10))
     sv.trace_begin(nb * 8 + 16)
@@ -665,20 +691,8 @@ def main():
         calls_alone["greedy_b512"] = bench_greedy_b512(sv, torch, workloads, dev, per_call, with_cold, reps)
     del evict
 
-    # the read rate this device reaches: a read-only stream of 4 GiB of random
-    # bytes with the same loads as the row passes
-    probe = torch.randint(-2**31, 2**31 - 1, (1 << 30,), dtype=torch.int32, device=dev)
-    folds = sv.sv_read_probe(probe)
-    for _ in range(2):
-        sv.sv_read_probe(probe, folds=folds)
-    torch.cuda.synchronize()
-    sv.trace_begin(64, kernels=("read_probe",))
-    for _ in range(20):
-        sv.sv_read_probe(probe, folds=folds)
-    torch.cuda.synchronize()
-    probe_ms = statistics.mean(t for _, t in sv.trace_end(64))
-    read_ceiling = probe.numel() * 4 / (probe_ms * 1e-3) / 1e9
-    del probe
+    # the read rate this device reaches: a read-only stream with the same loads
+    read_ceiling_gbps = read_ceiling(sv, torch, dev)
 
     # beyond the verification step: committing the tree's accepted paths in a
     # KV cache shaped like a 36-layer target (K and V, 8 heads x 128 bf16 = 2 KB rows)
@@ -768,9 +782,9 @@ def main():
         },
         "hbm_gbps": round(hbm_gbps, 1),
         "hbm_frac_of_peak": round(hbm_gbps / HBM_PEAK_GBPS, 4),
-        "read_ceiling": {"gbps": round(read_ceiling, 1), "kernel": "read_probe",
+        "read_ceiling": {"gbps": round(read_ceiling_gbps, 1), "kernel": "read_probe",
                          "what": "read-only stream of 4 GiB of random bytes, mean of 20 launches",
-                         "frac_of_peak": round(read_ceiling / HBM_PEAK_GBPS, 4)},
+                         "frac_of_peak": round(read_ceiling_gbps / HBM_PEAK_GBPS, 4)},
         "roofline": roof,
         "roofline_others": others or None,
         "modes": modes,
@@ -781,7 +795,7 @@ def main():
     }
     for r in [roof, *others.values()]:
         if r and r.get("unit") == "GB/s":
-            r["frac_of_read_ceiling"] = round(r["achieved"] / read_ceiling, 4)
+            r["frac_of_read_ceiling"] = round(r["achieved"] / read_ceiling_gbps, 4)
     print(json.dumps(out), flush=True)
 
 
