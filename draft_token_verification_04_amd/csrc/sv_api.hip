@@ -104,26 +104,32 @@ struct Tracer {
     int capacity = 0;
     int used = 0;
     unsigned mask = 0;
-    int next_kernel = -1;
     std::vector<TraceRec> recs;
 };
 Tracer &tracer() {
     static Tracer t;
     return t;
 }
+// The kernel the calling thread launches next: per thread, so that host threads
+// launching at the same time never label each other's launches.
+thread_local int t_next_kernel = -1;
+
+void destroy_events(std::vector<TraceRec> &recs) {
+    for (auto &r : recs) {
+        if (r.start) (void)hipEventDestroy(r.start);
+        if (r.stop) (void)hipEventDestroy(r.stop);
+    }
+    recs.clear();
+}
 }  // namespace
 
-void trace_select(int kernel) {
-    Tracer &t = tracer();
-    std::lock_guard<std::mutex> g(t.mu);
-    t.next_kernel = kernel;
-}
+void trace_select(int kernel) { t_next_kernel = kernel; }
 
 bool trace_events(hipEvent_t *start, hipEvent_t *stop) {
+    const int k = t_next_kernel;
+    t_next_kernel = -1;
     Tracer &t = tracer();
     std::lock_guard<std::mutex> g(t.mu);
-    const int k = t.next_kernel;
-    t.next_kernel = -1;
     if (!t.on || k < 0 || t.used >= t.capacity) return false;
     if (t.mask != 0 && !(t.mask & (1u << k))) return false;
     TraceRec &r = t.recs[t.used++];
@@ -200,6 +206,7 @@ sv_status spec_verify_sample(const void *target_logits, const void *draft_logits
     ResidParam *rp = reinterpret_cast<ResidParam *>(ws + L.rp);
     double *tiles = reinterpret_cast<double *>(ws + L.tiles);
     const Scale sc = make_scale(static_cast<double>(temperature));
+    if (!(sc.c < 0x1p127)) return SV_ERR_UNSUPPORTED;  // T below ~1e-38: log2(e)/T beyond fp32 range
     hipStream_t s = static_cast<hipStream_t>(stream);
     const long long rows_t = static_cast<long long>(B) * (K + 1);
     const long long rows_total = rows_t + static_cast<long long>(B) * K;
@@ -473,22 +480,18 @@ sv_status sv_trace_begin(int capacity, unsigned kernel_mask) {
     if (capacity < 1) return SV_ERR_INVALID_ARG;
     Tracer &t = tracer();
     std::lock_guard<std::mutex> g(t.mu);
-    for (auto &r : t.recs) {
-        (void)hipEventDestroy(r.start);
-        (void)hipEventDestroy(r.stop);
-    }
-    t.recs.assign(static_cast<size_t>(capacity), TraceRec{});
+    destroy_events(t.recs);
+    t.on = false;
+    t.used = t.capacity = 0;
+    t.recs.assign(static_cast<size_t>(capacity), TraceRec{-1, nullptr, nullptr});
     for (auto &r : t.recs) {
         if (hipEventCreate(&r.start) != hipSuccess || hipEventCreate(&r.stop) != hipSuccess) {
-            t.recs.clear();
-            t.on = false;
+            destroy_events(t.recs);
             return SV_ERR_HIP;
         }
     }
     t.capacity = capacity;
     t.mask = kernel_mask;
-    t.used = 0;
-    t.next_kernel = -1;
     t.on = true;
     return SV_OK;
 }
@@ -503,11 +506,7 @@ int sv_trace_end(sv_kernel_time *records, int max_records) {
             (void)hipEventElapsedTime(&ms, t.recs[i].start, t.recs[i].stop);
         if (records && i < max_records) records[i] = sv_kernel_time{t.recs[i].kernel, ms};
     }
-    for (auto &r : t.recs) {
-        (void)hipEventDestroy(r.start);
-        (void)hipEventDestroy(r.stop);
-    }
-    t.recs.clear();
+    destroy_events(t.recs);
     t.on = false;
     t.used = t.capacity = 0;
     return n;

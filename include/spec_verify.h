@@ -90,6 +90,10 @@ size_t sv_greedy_workspace_bytes(int B, int rows_per_req, int V, sv_dtype dt);
  *                              the token drawn at row n (residual if n < K,
  *                              bonus if n = K); other entries are ignored.
  *   temperature   T > 0, finite; p = softmax(target/T), q = softmax(draft/T).
+ *                 T so small that log2(e)/T overflows float32 (below about
+ *                 1e-38) returns SV_ERR_UNSUPPORTED.  Scaled logits are
+ *                 formed in float32, so every finite logit needs
+ *                 |L| * log2(e) / T < 2^128.
  *   0 <= K <= SV_MAX_DRAFT_LEN.
  *
  * Outputs:
@@ -284,8 +288,10 @@ const char *sv_version(void);
  * timed).  An event pair measures from the start event to the stop event, so
  * it includes the launch latency of that kernel.  sv_trace_end waits for the
  * recorded events, writes up to `max_records` records (kernel id, elapsed
- * milliseconds) and returns how many launches were recorded.  Not
- * thread-safe; meant for benchmarking.
+ * milliseconds) and returns how many launches were recorded.  Launches from
+ * several host threads are each recorded under their own kernel id, but
+ * sv_trace_begin and sv_trace_end must not overlap launches.  Meant for
+ * benchmarking.
  */
 typedef struct {
     int kernel; /* an sv_kernel_id */

@@ -87,6 +87,8 @@ def test_sample_argument_checks(lib):
     assert _sample(lib, wsb=0) == sv.SV_ERR_WORKSPACE
     need = lib.sv_sample_workspace_bytes(2, 3, 100, sv.SV_BF16)
     assert _sample(lib, wsb=need - 1) == sv.SV_ERR_WORKSPACE
+    # a temperature whose log2(e)/T overflows float32 is refused before any launch
+    assert _sample(lib, T=1e-40, wsb=need) == sv.SV_ERR_UNSUPPORTED
     # K = 0 needs no draft tensors; B = 0 is an empty batch (no launch)
     assert _sample(lib, K=0, d=None, x=None, ua=None, wsb=0) == sv.SV_ERR_WORKSPACE
     assert _sample(lib, B=0, t=None, ws=None) == sv.SV_OK
