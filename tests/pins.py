@@ -252,10 +252,11 @@ def pin_expected_accept_length_mc(lib, trials=200_000, seed=3):
 
 # --------------------------------------------------------------- chi-square test
 
-def pin_chi_square(lib, trials=1_000_000, seed=7, V=8, T=1.0):
-    """10^6 rounds with K = 2 on prefix-dependent toy models: the first emitted
-    token follows p(.|prefix) and the accept-length histogram follows the exact
-    law obtained from the overlap identity (chi-square p > 1e-3)."""
+def chi_square_case(trials=1_000_000, seed=7, V=8, T=1.0):
+    """Inputs of ``trials`` rounds with K = 2 on prefix-dependent toy models
+    (drafts drawn from the draft model), with the laws they must follow: the
+    first emitted token ~ p(.|prefix), and the accept-length law obtained from
+    the overlap identity, P(n >= 1) = sum min(p0, q0), then position by position."""
     rng = np.random.default_rng(seed)
     tp = {(): (rng.standard_normal(V)).astype(F32)}
     tq = {(): (tp[()] + rng.standard_normal(V) * 0.8).astype(F32)}
@@ -266,7 +267,6 @@ def pin_chi_square(lib, trials=1_000_000, seed=7, V=8, T=1.0):
     P0, Q0 = softmax64(tp[()], T), softmax64(tq[()], T)
     P1 = np.stack([softmax64(tp[(a,)], T) for a in range(V)])
     Q1 = np.stack([softmax64(tq[(a,)], T) for a in range(V)])
-    # drafts drawn from the draft model
     x1 = rng.choice(V, size=trials, p=Q0)
     cq = np.cumsum(Q1, axis=1)
     x2 = np.minimum((cq[x1] <= rng.random(trials)[:, None]).sum(1), V - 1)
@@ -280,14 +280,29 @@ def pin_chi_square(lib, trials=1_000_000, seed=7, V=8, T=1.0):
     x = np.stack([x1, x2], 1).astype(np.int32)
     ua = rng.random((trials, 2), dtype=F32)
     us = rng.random((trials, 3), dtype=F32)
-    o = oracle.verify_sample(tgt, dr, x, ua, us, T, lib=lib)
-    first = np.bincount(o["tokens"][:, 0], minlength=V)
-    assert stats.chisquare(first, P0 * trials).pvalue > 1e-3
     a0 = np.minimum(P0, Q0)
     a1 = np.minimum(P1, Q1).sum(1)
-    pn = np.array([1 - a0.sum(), (a0 * (1 - a1)).sum(), (a0 * a1).sum()])
-    hist = np.bincount(o["accept_len"], minlength=3)
-    assert stats.chisquare(hist, pn * trials).pvalue > 1e-3
+    law_n = np.array([1 - a0.sum(), (a0 * (1 - a1)).sum(), (a0 * a1).sum()])
+    return dict(target=tgt, draft=dr, x=x, u_accept=ua, u_sample=us, T=T, V=V, P0=P0, law_n=law_n)
+
+
+def check_chi_square(case, tokens, accept_len, pmin=1e-3):
+    """The first emitted token follows P0 and the accept lengths follow their
+    exact law (chi-square p-values above ``pmin``)."""
+    trials, V = len(accept_len), case["V"]
+    first = np.bincount(tokens[:, 0], minlength=V)
+    assert stats.chisquare(first, case["P0"] * trials).pvalue > pmin
+    hist = np.bincount(accept_len, minlength=3)
+    assert stats.chisquare(hist, case["law_n"] * trials).pvalue > pmin
+
+
+def pin_chi_square(lib, trials=1_000_000, seed=7, V=8, T=1.0):
+    """10^6 rounds with K = 2 on prefix-dependent toy models: the oracle's
+    first emitted token follows p(.|prefix) and its accept-length histogram
+    follows the exact law obtained from the overlap identity."""
+    c = chi_square_case(trials, seed, V, T)
+    o = oracle.verify_sample(c["target"], c["draft"], c["x"], c["u_accept"], c["u_sample"], T, lib=lib)
+    check_chi_square(c, o["tokens"], o["accept_len"])
 
 
 # ---------------------------------------------------------------- special cases
