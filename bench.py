@@ -50,6 +50,9 @@ KERNEL_SOURCES = {
     "lmhead": ["draft_token_verification_04_amd/csrc/sv_lmhead.hip",
                "draft_token_verification_04_amd/csrc/sv_device.hpp",
                "draft_token_verification_04_amd/csrc/sv_internal.hpp"],
+    "lmhead_stats": ["draft_token_verification_04_amd/csrc/sv_lmhead.hip",
+                     "draft_token_verification_04_amd/csrc/sv_device.hpp",
+                     "draft_token_verification_04_amd/csrc/sv_internal.hpp"],
     "ngram": ["draft_token_verification_04_amd/csrc/sv_ngram.hip",
               "draft_token_verification_04_amd/csrc/sv_device.hpp",
               "draft_token_verification_04_amd/csrc/sv_internal.hpp"],
@@ -339,6 +342,40 @@ def bench_greedy_b512(sv, torch, workloads, dev, per_call, with_cold, reps):
     return entry
 
 
+def alternate_best(torch, fused, unfused, r):
+    """ms per call of two callables, each the best of three rounds of r
+    back-to-back calls.  Both run near the board's power limit, so the clock
+    drifts with the work: both are warmed up, then the rounds alternate."""
+    def timed(fn):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(r):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / r
+
+    for _ in range(10):
+        fused()
+        unfused()
+    a, b = float("inf"), float("inf")
+    for _ in range(3):
+        a = min(a, timed(fused))
+        b = min(b, timed(unfused))
+    return a, b
+
+
+def kernel_means(sv, torch, fn, r, kernels):
+    """Mean event-timed ms per launch of the named library kernels over r calls of fn."""
+    sv.trace_begin(16 * r, kernels=kernels)
+    for _ in range(r):
+        fn()
+    torch.cuda.synchronize()
+    per = {}
+    for name, ms in sv.trace_end(16 * r):
+        per.setdefault(name, []).append(ms)
+    return {k: statistics.mean(v) for k, v in per.items()}
+
+
 def bench_lmhead(sv, torch, workloads, dev, reps):
     """spec_verify_greedy_lmhead on seeded Gaussian operands (random drafts:
     the fused kernel's work does not depend on acceptance), beside the unfused
@@ -383,45 +420,101 @@ def bench_lmhead(sv, torch, workloads, dev, reps):
         if rc:
             raise RuntimeError(f"spec_verify_greedy failed: {rc}")
 
-    def timed(fn, r):
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(r):
-            fn()
-        torch.cuda.synchronize()
-        return (time.perf_counter() - t0) * 1e3 / r
-
-    # both run near the board's power limit, so the clock drifts with the work:
-    # warm both up, then alternate and keep each one's best of three rounds
-    for _ in range(10):
-        fused()
-        unfused()
     r = max(10, reps // 5)
-    call_ms, unfused_ms = float("inf"), float("inf")
-    for _ in range(3):
-        call_ms = min(call_ms, timed(fused, r))
-        unfused_ms = min(unfused_ms, timed(unfused, r))
-    sv.trace_begin(64, kernels=("lmhead", "match"))
-    for _ in range(r):
-        fused()
-    torch.cuda.synchronize()
-    per = {}
-    for name, ms in sv.trace_end(64):
-        per.setdefault(name, []).append(ms)
-    k_ms = statistics.mean(per["lmhead"])
+    call_ms, unfused_ms = alternate_best(torch, fused, unfused, r)
+    per = kernel_means(sv, torch, fused, r, ("lmhead", "match"))
+    k_ms = per["lmhead"]
     flop = 2.0 * M * D * V
     del L, Lm
     return {
         "workload": f"greedy chain with the LM-head projection fused: B={B} K={K} D={D} V={V}, bf16 "
                     "operands (Gaussian, general recipe), logits never written",
         "rows": M, "flop": flop, "call_ms": round(call_ms, 5), "kernel_ms": round(k_ms, 5),
-        "match_ms": round(statistics.mean(per["match"]), 5),
+        "match_ms": round(per["match"], 5),
         "rows_per_s": round(M / (call_ms * 1e-3), 1),
         "roofline": {"bound": "mfma", "kernel": "lmhead", "achieved": round(flop / (k_ms * 1e-3) * 1e-12, 1),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(flop / (k_ms * 1e-3) * 1e-12 / MFMA_BF16_PEAK_TFLOPS, 4),
                      "traffic": (stored_traffic("lmhead") or {}).get("bytes_per_launch")},
         "unfused_reference": {"what": "torch.matmul (bf16 logits written to HBM) + spec_verify_greedy",
+                              "call_ms": round(unfused_ms, 5)},
+        "timing": f"best of 3 rounds of {r} back-to-back calls each, fused and unfused alternating",
+    }
+
+
+def bench_sample_lmhead(sv, torch, workloads, dev, reps):
+    """spec_verify_sample_lmhead (speculative sampling on the projection, lse
+    outputs on) on seeded Gaussian operands and independent bf16 draft logits
+    with drafts drawn from them, beside the unfused reference: a library GEMM
+    writing bf16 logits, then spec_verify_sample reading them."""
+    import numpy as np
+
+    shp = workloads.LMHEAD_SHAPE
+    B, K, D, V = shp["B"], shp["K"], shp["D"], shp["V"]
+    T = 0.7
+    t0 = time.perf_counter()
+    w = workloads.make_sample_lmhead(B, K, D, V, exact=False, dtype="bf16", T=T, seed=20261207,
+                                     plant=np.array([], dtype=np.int64))
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    H, Wt, Dr = bf(w.hidden), bf(w.lm_head), bf(w.draft)
+    x = torch.from_numpy(w.draft_tokens).to(dev)
+    ua = torch.from_numpy(w.u_accept).to(dev)
+    us = torch.from_numpy(w.u_sample).to(dev)
+    print(f"[bench] sampling lm-head operands ready in {time.perf_counter() - t0:.1f}s", file=sys.stderr,
+          flush=True)
+    lib = sv.load_library()
+    M = B * (K + 1)
+    ws = torch.empty(lib.sv_sample_lmhead_workspace_bytes(B, K, D, V, sv.SV_BF16), dtype=torch.uint8,
+                     device=dev)
+    n = torch.empty(B, dtype=torch.int32, device=dev)
+    tok = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
+    lt = torch.empty((B, K + 1), dtype=torch.float32, device=dev)
+    ld = torch.empty((B, K), dtype=torch.float32, device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    args = (P(H), P(Wt), P(Dr), P(x), P(ua), P(us), B, K, D, V, sv.SV_BF16, ctypes.c_float(T), P(n), P(tok),
+            P(lt), P(ld), None, P(ws), ws.numel(), stream)
+
+    def fused():
+        rc = lib.spec_verify_sample_lmhead(*args)
+        if rc:
+            raise RuntimeError(f"spec_verify_sample_lmhead failed: {rc}")
+
+    L = torch.empty((B, K + 1, V), dtype=torch.bfloat16, device=dev)
+    Hm, Lm = H.reshape(M, D), L.view(M, V)
+    s_ws = torch.empty(lib.sv_sample_workspace_bytes(B, K, V, sv.SV_BF16), dtype=torch.uint8, device=dev)
+    s_args = (P(L), P(Dr), P(x), P(ua), P(us), B, K, V, sv.SV_BF16, ctypes.c_float(T), P(n), P(tok), P(lt),
+              P(ld), None, P(s_ws), s_ws.numel(), stream)
+
+    def unfused():
+        torch.matmul(Hm, Wt.t(), out=Lm)
+        rc = lib.spec_verify_sample(*s_args)
+        if rc:
+            raise RuntimeError(f"spec_verify_sample failed: {rc}")
+
+    r = max(10, reps // 5)
+    call_ms, unfused_ms = alternate_best(torch, fused, unfused, r)
+    fused()
+    torch.cuda.synchronize()
+    mean_tokens = float(n.float().mean().item()) + 1.0
+    kern = ("lmhead_stats", "rowstats", "accept", "lmhead_rows", "gather_rows", "resid_mass", "resid_select")
+    per = kernel_means(sv, torch, fused, r, kern)
+    k_ms = per["lmhead_stats"]
+    flop = 2.0 * M * D * V
+    del L, Lm
+    return {
+        "workload": f"stochastic chain with the LM-head projection fused: B={B} K={K} D={D} V={V} T={T}, "
+                    "bf16 operands (Gaussian, general recipe), bf16 draft logits, lse outputs on; target "
+                    "rows never written (the one row per request a token is drawn from is formed again)",
+        "rows": M, "flop": flop, "call_ms": round(call_ms, 5),
+        "kernel_ms": {k: round(per[k], 5) for k in kern if k in per},
+        "rows_per_s": round(M / (call_ms * 1e-3), 1), "mean_tokens_per_round": round(mean_tokens, 4),
+        "roofline": {"bound": "mfma", "kernel": "lmhead_stats",
+                     "achieved": round(flop / (k_ms * 1e-3) * 1e-12, 1),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(flop / (k_ms * 1e-3) * 1e-12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": (stored_traffic("lmhead_stats") or {}).get("bytes_per_launch")},
+        "unfused_reference": {"what": "torch.matmul (bf16 logits written to HBM) + spec_verify_sample",
                               "call_ms": round(unfused_ms, 5)},
         "timing": f"best of 3 rounds of {r} back-to-back calls each, fused and unfused alternating",
     }
@@ -746,6 +839,7 @@ def main():
     # logits never written), at the Qwen3-8B shape B=256 K=7 D=4096 V=151936
     if "greedy" in active and not args.no_lmhead:
         extras["greedy_lmhead"] = bench_lmhead(sv, torch, workloads, dev, reps)
+        extras["sample_lmhead"] = bench_sample_lmhead(sv, torch, workloads, dev, reps)
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -13,6 +13,10 @@ Entry points (same names as the C ABI):
 * ``spec_verify_sample(target, draft, draft_tokens, u_accept, u_sample, T)``
 * ``spec_verify_greedy(target, draft_tokens)``
 * ``spec_verify_tree(target, node_tokens, parents)``
+* ``spec_verify_greedy_lmhead``, ``spec_verify_tree_lmhead`` and
+  ``spec_verify_sample_lmhead``: the same from the target's hidden states and
+  LM head (logits formed on the matrix cores, never written)
+* ``spec_commit_tree_kv``, ``spec_ngram_candidates``, ``sv_read_probe``
 """
 
 from __future__ import annotations
@@ -28,13 +32,14 @@ SV_F32, SV_BF16 = 0, 1
 SV_MAX_TREE_NODES = 2048
 KERNELS = ("rowstats", "accept", "resid_mass", "resid_select", "argmax", "match", "tree",
            "skip_stats", "skip_argmax", "commit", "lmhead", "ngram_count", "ngram_emit",
-           "skip_tree", "read_probe")
+           "skip_tree", "read_probe", "lmhead_stats", "lmhead_rows", "gather_rows")
 
 EXPORTS = ("sv_sample_workspace_bytes", "sv_greedy_workspace_bytes", "spec_verify_sample",
            "spec_verify_greedy", "spec_verify_tree", "spec_commit_tree_kv", "sv_status_string",
            "sv_version", "sv_lmhead_workspace_bytes", "spec_verify_greedy_lmhead",
            "spec_verify_tree_lmhead", "sv_ngram_workspace_bytes", "spec_ngram_candidates",
-           "sv_read_probe", "sv_read_probe_folds", "sv_trace_begin", "sv_trace_end", "sv_kernel_name")
+           "sv_read_probe", "sv_read_probe_folds", "sv_trace_begin", "sv_trace_end", "sv_kernel_name",
+           "sv_sample_lmhead_workspace_bytes", "spec_verify_sample_lmhead")
 
 
 class SpecVerifyError(RuntimeError):
@@ -81,6 +86,11 @@ def load_library(path: str = LIB_PATH):
     lib.spec_verify_greedy_lmhead.restype = I
     lib.spec_verify_tree_lmhead.argtypes = [P, P, P, P, I, I, I, I, P, P, P, P, P, Z, P]
     lib.spec_verify_tree_lmhead.restype = I
+    lib.sv_sample_lmhead_workspace_bytes.argtypes = [I, I, I, I, I]
+    lib.sv_sample_lmhead_workspace_bytes.restype = Z
+    lib.spec_verify_sample_lmhead.argtypes = [P, P, P, P, P, P, I, I, I, I, I, ctypes.c_float, P, P, P, P,
+                                              P, P, Z, P]
+    lib.spec_verify_sample_lmhead.restype = I
     lib.sv_read_probe.argtypes = [P, Z, P, P]
     lib.sv_read_probe.restype = I
     lib.sv_read_probe_folds.argtypes = [Z]
@@ -350,6 +360,50 @@ def spec_verify_tree_lmhead(hidden, lm_head, node_tokens, parents, *, status=Tru
             _ptr(ws), ws.numel() * ws.element_size(), _stream(torch, dev, stream))
     if rc != SV_OK:
         raise SpecVerifyError(rc, "spec_verify_tree_lmhead")
+    return out
+
+
+def spec_verify_sample_lmhead(hidden, lm_head, draft, draft_tokens, u_accept, u_sample, temperature, *,
+                              lse=True, status=True, workspace=None, stream=None):
+    """Stochastic chain verification on the target logits hidden @ lm_head.T,
+    never materialised: hidden [B, K+1, D] bf16, lm_head [V, D] bf16, draft
+    [B, K, V] logits (bf16 or f32), draft_tokens [B, K] int32, u_accept [B, K]
+    and u_sample [B, K+1] float32.  Returns what spec_verify_sample returns."""
+    torch = _torch()
+    lib = load_library()
+    dev, D, V = _lmhead_operands(torch, hidden, lm_head, (0, 0))
+    B, R = hidden.shape[:2]
+    K = R - 1
+    dt = SV_BF16
+    if K > 0:
+        _check(draft, "draft", 3, device=dev)
+        dt = _dtype_code(draft)
+        if tuple(draft.shape) != (B, K, V):
+            raise ValueError(f"draft must be [{B},{K},{V}], got {tuple(draft.shape)}")
+        _check(draft_tokens, "draft_tokens", 2, torch.int32, dev)
+        _check(u_accept, "u_accept", 2, torch.float32, dev)
+        if tuple(draft_tokens.shape) != (B, K) or tuple(u_accept.shape) != (B, K):
+            raise ValueError("draft_tokens and u_accept must be [B, K]")
+    _check(u_sample, "u_sample", 2, torch.float32, dev)
+    if tuple(u_sample.shape) != (B, K + 1):
+        raise ValueError("u_sample must be [B, K+1]")
+    out = dict(accept_len=torch.empty(B, dtype=torch.int32, device=dev),
+               tokens=torch.empty((B, K + 1), dtype=torch.int32, device=dev))
+    if lse:
+        out["lse_target"] = torch.empty((B, K + 1), dtype=torch.float32, device=dev)
+        out["lse_draft"] = torch.empty((B, K), dtype=torch.float32, device=dev)
+    if status:
+        out["status"] = torch.empty(B, dtype=torch.int32, device=dev)
+    ws = _workspace(torch, lib.sv_sample_lmhead_workspace_bytes(B, K, D, V, dt), dev, workspace)
+    with torch.cuda.device(dev):
+        rc = lib.spec_verify_sample_lmhead(
+            _ptr(hidden), _ptr(lm_head), _ptr(draft if K > 0 else None),
+            _ptr(draft_tokens if K > 0 else None), _ptr(u_accept if K > 0 else None), _ptr(u_sample),
+            B, K, D, V, dt, float(temperature), _ptr(out["accept_len"]), _ptr(out["tokens"]),
+            _ptr(out.get("lse_target")), _ptr(out.get("lse_draft")), _ptr(out.get("status")), _ptr(ws),
+            ws.numel() * ws.element_size(), _stream(torch, dev, stream))
+    if rc != SV_OK:
+        raise SpecVerifyError(rc, "spec_verify_sample_lmhead")
     return out
 
 

@@ -220,9 +220,11 @@ sv_status spec_verify_sample(const void *target_logits, const void *draft_logits
         });
         if (e == hipSuccess)
             e = traced(SV_K_ACCEPT, s, [&] {
+                const PartRows pt{part_R, part_s, g.segs};
+                const PartRows pd{part_R + rows_t * g.segs, part_s + rows_t * g.segs, g.segs};
                 return launch_accept(target_logits, draft_logits, draft_tokens, u_accept, u_sample, B, K,
-                                     V, g, dt, sc, part_R, part_s, L2, accept_len, out_tokens,
-                                     lse_target, lse_draft, req_status, rp, s);
+                                     V, dt, sc, pt, pd, nullptr, L2, accept_len, out_tokens, lse_target,
+                                     lse_draft, req_status, rp, s);
             });
     } else {
         // rows of positions after each request's first rejection are not read
@@ -392,7 +394,138 @@ sv_status spec_verify_tree_lmhead(const void *hidden, const void *lm_head,
     return e == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 
+}  // extern "C"
+
+// ---- speculative sampling fused with the LM-head projection ----------------------
+
+namespace {
+struct SampleLmWs {
+    size_t part_Rt, part_st, xlog, part_Rd, part_sd, L2, rp, rows_p, rows_q, tiles, total;
+};
+// gd: the draft rows' streaming geometry; gr: the fp32 rows the draw reads.
+SampleLmWs sample_lm_ws_layout(int B, int K, int V, const RowGeom &gd, const RowGeom &gr) {
+    SampleLmWs w;
+    const size_t rows_t = static_cast<size_t>(B) * (K + 1), rows_d = static_cast<size_t>(B) * K;
+    const size_t pt = rows_t * static_cast<size_t>(lmhead_segs(V)), pd = rows_d * static_cast<size_t>(gd.segs);
+    const size_t row_bytes = static_cast<size_t>(V) * sizeof(float);
+    size_t o = 0;
+    w.part_Rt = o;
+    o = align_up(o + pt * sizeof(float));
+    w.part_st = o;
+    o = align_up(o + pt * sizeof(double));
+    w.xlog = o;
+    o = align_up(o + rows_t * sizeof(float));
+    w.part_Rd = o;
+    o = align_up(o + pd * sizeof(float));
+    w.part_sd = o;
+    o = align_up(o + pd * sizeof(double));
+    w.L2 = o;
+    o = align_up(o + static_cast<size_t>(B) * (2 * K + 1) * sizeof(double));
+    w.rp = o;
+    o = align_up(o + static_cast<size_t>(B) * sizeof(ResidParam));
+    w.rows_p = o;
+    o = align_up(o + static_cast<size_t>(B) * row_bytes);
+    w.rows_q = o;
+    o = align_up(o + (K > 0 ? static_cast<size_t>(B) * row_bytes : 0));
+    w.tiles = o;
+    o = align_up(o + static_cast<size_t>(B) * static_cast<size_t>(gr.ntiles) * sizeof(double));
+    w.total = o;
+    return w;
+}
+}  // namespace
+
+extern "C" {
+
+size_t sv_sample_lmhead_workspace_bytes(int B, int K, int D, int V, sv_dtype dt) {
+    if (B < 1 || K < 0 || K > SV_MAX_DRAFT_LEN || !valid_dtype(dt) || V < 1 ||
+        !lmhead_sizes_ok(static_cast<long long>(B) * (K + 1), D, V) || !sizes_ok(B, 2LL * K + 1, V))
+        return 0;
+    const RowGeom gd = row_geom(V, dt, true, kStatsVecsPerLane);
+    const RowGeom gr = row_geom(V, SV_F32, true, kStatsVecsPerLane);
+    return sample_lm_ws_layout(B, K, V, gd, gr).total;
+}
+
+sv_status spec_verify_sample_lmhead(const void *hidden, const void *lm_head, const void *draft_logits,
+                                    const int32_t *draft_tokens, const float *u_accept,
+                                    const float *u_sample, int B, int K, int D, int V, sv_dtype dt,
+                                    float temperature, int32_t *accept_len, int32_t *out_tokens,
+                                    float *lse_target, float *lse_draft, int32_t *req_status,
+                                    void *workspace, size_t workspace_bytes, void *stream) {
+    if (!valid_dtype(dt)) return SV_ERR_UNSUPPORTED;
+    if (B < 0 || K < 0 || V < 1 || D < 1 || !(temperature > 0.0f) || !isfinite(temperature))
+        return SV_ERR_INVALID_ARG;
+    if (K > SV_MAX_DRAFT_LEN) return SV_ERR_UNSUPPORTED;
+    if (B == 0) return SV_OK;
+    const long long rows_t = static_cast<long long>(B) * (K + 1);
+    if (!lmhead_sizes_ok(rows_t, D, V) || !sizes_ok(B, 2LL * K + 1, V)) return SV_ERR_UNSUPPORTED;
+    if (!hidden || !lm_head || !u_sample || !accept_len || !out_tokens || !workspace)
+        return SV_ERR_INVALID_ARG;
+    if (K > 0 && (!draft_logits || !draft_tokens || !u_accept)) return SV_ERR_INVALID_ARG;
+    if (!aligned16(hidden) || !aligned16(lm_head) || !aligned256(workspace)) return SV_ERR_INVALID_ARG;
+    const RowGeom gd = row_geom(V, dt, K == 0 || aligned16(draft_logits), kStatsVecsPerLane);
+    const RowGeom gr = row_geom(V, SV_F32, true, kStatsVecsPerLane);
+    const SampleLmWs L = sample_lm_ws_layout(B, K, V, gd, gr);
+    if (workspace_bytes < L.total) return SV_ERR_WORKSPACE;
+    const Scale sc = make_scale(static_cast<double>(temperature));
+    if (!(sc.c < 0x1p127)) return SV_ERR_UNSUPPORTED;
+
+    char *ws = static_cast<char *>(workspace);
+    float *part_Rt = reinterpret_cast<float *>(ws + L.part_Rt);
+    double *part_st = reinterpret_cast<double *>(ws + L.part_st);
+    float *xlog = reinterpret_cast<float *>(ws + L.xlog);
+    float *part_Rd = reinterpret_cast<float *>(ws + L.part_Rd);
+    double *part_sd = reinterpret_cast<double *>(ws + L.part_sd);
+    double *L2 = reinterpret_cast<double *>(ws + L.L2);
+    ResidParam *rp = reinterpret_cast<ResidParam *>(ws + L.rp);
+    float *rows_p = reinterpret_cast<float *>(ws + L.rows_p);
+    float *rows_q = reinterpret_cast<float *>(ws + L.rows_q);
+    double *tiles = reinterpret_cast<double *>(ws + L.tiles);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+
+    // 1. target rows: partials and the logit at each draft, from H W^T
+    hipError_t e = traced(SV_K_LMHEAD_STATS, s, [&] {
+        return launch_lmhead_stats(hidden, lm_head, B, K, D, V, draft_tokens, sc, part_Rt, part_st, xlog, s);
+    });
+    // 2. draft rows: the streaming statistics pass
+    if (e == hipSuccess && K > 0)
+        e = traced(SV_K_ROWSTATS, s, [&] {
+            return launch_rowstats(nullptr, draft_logits, 0, static_cast<long long>(B) * K, V, gd, dt, sc,
+                                   part_Rd, part_sd, s);
+        });
+    // 3. merge, acceptance scan, lse outputs, draw parameters
+    if (e == hipSuccess)
+        e = traced(SV_K_ACCEPT, s, [&] {
+            const PartRows pt{part_Rt, part_st, lmhead_segs(V)};
+            const PartRows pd{part_Rd, part_sd, gd.segs};
+            return launch_accept(nullptr, draft_logits, draft_tokens, u_accept, u_sample, B, K, V, dt, sc, pt,
+                                 pd, xlog, L2, accept_len, out_tokens, lse_target, lse_draft, req_status, rp, s);
+        });
+    // 4. the row each request draws from, formed again and written in fp32,
+    //    with its draft row beside it
+    if (e == hipSuccess)
+        e = traced(SV_K_LMHEAD_ROWS, s,
+                   [&] { return launch_lmhead_rows(hidden, lm_head, B, K, D, V, rp, rows_p, s); });
+    if (e == hipSuccess && K > 0)
+        e = traced(SV_K_GATHER_ROWS, s,
+                   [&] { return launch_gather_draft_rows(draft_logits, dt, B, K, V, rp, rows_q, s); });
+    // 5. the draw
+    if (e == hipSuccess)
+        e = traced(SV_K_RESID_MASS, s, [&] {
+            return launch_resid_mass(rows_p, rows_q, B, V, gr, SV_F32, sc, rp, tiles, s);
+        });
+    if (e == hipSuccess)
+        e = traced(SV_K_RESID_SELECT, s, [&] {
+            return launch_resid_select(rows_p, rows_q, B, K, V, gr, SV_F32, sc, rp, tiles, out_tokens, s);
+        });
+    return e == hipSuccess ? SV_OK : SV_ERR_HIP;
+}
+
+}  // extern "C"
+
 // ---- AdaPLD lexical retrieval ----------------------------------------------------
+
+extern "C" {
+
 
 size_t sv_ngram_workspace_bytes(int B, int L) {
     if (B < 0 || L < 1) return 0;
@@ -472,7 +605,8 @@ const char *sv_kernel_name(int k) {
     static const char *names[SV_K_COUNT] = {"rowstats", "accept", "resid_mass", "resid_select",
                                             "argmax", "match", "tree", "skip_stats",
                                             "skip_argmax", "commit", "lmhead", "ngram_count",
-                                            "ngram_emit", "skip_tree", "read_probe"};
+                                            "ngram_emit", "skip_tree", "read_probe", "lmhead_stats",
+                                            "lmhead_rows", "gather_rows"};
     return (k >= 0 && k < SV_K_COUNT) ? names[k] : "unknown";
 }
 

@@ -126,11 +126,22 @@ inline hipError_t launch_kernel(void (*k)(KArgs...), dim3 grid, dim3 block, size
 hipError_t launch_rowstats(const void *tgt, const void *drf, long long rows_t, long long rows_total,
                            int V, const RowGeom &g, sv_dtype dt, const Scale &sc, float *part_R,
                            double *part_s, hipStream_t s);
-hipError_t launch_accept(const void *tgt, const void *drf, const int32_t *drafts,
-                         const float *ua, const float *us, int B, int K, int V, const RowGeom &g,
-                         sv_dtype dt, const Scale &sc, const float *part_R, const double *part_s,
-                         double *L2, int32_t *accept_len, int32_t *out_tokens, float *lse_t,
-                         float *lse_d, int32_t *status, ResidParam *rp, hipStream_t s);
+// Segment partials (R, s) of a set of rows, `segs` per row, row-major.
+struct PartRows {
+    const float *R;
+    const double *s;
+    int segs;
+};
+// Merge, acceptance scan and draw parameters.  pt holds the B (K+1) target
+// rows' partials and pd the B K draft rows'.  xlog non-null selects the fused
+// form: the target logit at each draft is read from xlog [B (K+1)] instead of
+// the target rows (tgt is then unused), and the draw's rows are numbered per
+// request (row b of the buffers the draw reads).
+hipError_t launch_accept(const void *tgt, const void *drf, const int32_t *drafts, const float *ua,
+                         const float *us, int B, int K, int V, sv_dtype dt, const Scale &sc,
+                         const PartRows &pt, const PartRows &pd, const float *xlog, double *L2,
+                         int32_t *accept_len, int32_t *out_tokens, float *lse_t, float *lse_d,
+                         int32_t *status, ResidParam *rp, hipStream_t s);
 bool skip_supported(int K);
 size_t skip_ctl_bytes(int B, int K);
 hipError_t launch_skip(const void *tgt, const void *drf, const int32_t *drafts, const float *ua,
@@ -158,6 +169,19 @@ hipError_t launch_ngram(const int32_t *ctx, int B, int L, const int32_t *lens, c
 int lmhead_segs(int V);
 hipError_t launch_lmhead_argmax(const void *H, const void *W, int M, int D, int V, uint64_t *part_k,
                                 hipStream_t s);
+// Rows b (K+1) + i of H [B (K+1)][D] projected on W [V][D]: per row and
+// 128-column segment the (R, s) partials at scale sc, and in xlog the logit at
+// draft i (drafts [B][K]) for i < K.
+hipError_t launch_lmhead_stats(const void *H, const void *W, int B, int K, int D, int V,
+                               const int32_t *drafts, const Scale &sc, float *part_R, double *part_s,
+                               float *xlog, hipStream_t s);
+// Row b of rows [B][V] (fp32) = the logits of H row b (K+1) + rp[b].pos.
+hipError_t launch_lmhead_rows(const void *H, const void *W, int B, int K, int D, int V,
+                              const ResidParam *rp, float *rows, hipStream_t s);
+// Row b of out [B][V] (fp32) = draft row b K + rp[b].pos widened, for requests
+// whose draw is a residual (rp[b].mode = 1); other rows are left alone.
+hipError_t launch_gather_draft_rows(const void *drf, sv_dtype dt, int B, int K, int V,
+                                    const ResidParam *rp, float *out, hipStream_t s);
 hipError_t launch_commit(const void *src, void *dst, int G, int B, int S, int row_bytes,
                          const int32_t *tree_base, const int32_t *commit_base,
                          const int32_t *accept_len, const int32_t *path_nodes, int N,

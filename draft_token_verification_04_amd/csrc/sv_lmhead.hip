@@ -1,7 +1,13 @@
-// sv_lmhead.hip -- the target's LM-head projection fused with the row argmax
-// of greedy verification: logits = H W^T are formed tile by tile on the matrix
-// cores and reduced at once to (max, lowest index) keys per 128-column segment;
-// the logits are never written.
+// sv_lmhead.hip -- the target's LM-head projection fused with what verification
+// needs of its rows: logits = H W^T are formed tile by tile on the matrix cores
+// and reduced at once, per row and 128-column segment, to
+//   - (max, lowest index) keys, for greedy verification (k_lmhead<kEpiArgmax>);
+//   - (R, s) statistics in the form the streaming row-statistics pass makes
+//     (R = fp32(max * c_hi), s = sum 2^(x c - R)), plus the logit at the row's
+//     draft token, for speculative sampling (k_lmhead<kEpiStats>);
+// so the logits are never written.  The one row per request a sampled token is
+// drawn from is formed again afterwards and written (k_lmhead<kEpiRows>, its H
+// rows picked by the acceptance kernel's result).
 //
 // What it feeds: the speculative-decoding tutorial page, section
 // "一轮推测解码究竟发生什么" (the target scores all gamma+1 positions in one
@@ -9,7 +15,7 @@
 // argmax), and the DLite notes, section 2 (the D x V vocabulary projection is
 // the cost a drafter avoids repeating per position).
 //
-// k_lmhead_argmax: C[m][n] = sum_k H[m][k] W[n][k] with H [M][D] and W [V][D]
+// k_lmhead: C[m][n] = sum_k H[m][k] W[n][k] with H [M][D] and W [V][D]
 // bf16, both k-contiguous.  A workgroup of 8 waves (two per SIMD) owns a
 // 256 x 256 tile of C and walks D in steps of 64, each computed as four
 // 16-deep quarters.  The H and W slabs of a step go straight from global
@@ -94,10 +100,25 @@ template <int OFF> __device__ __forceinline__ bf16x8 lds_read(uint32_t addr, IC<
     asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a0), "+v"(a1), "+v"(b0), "+v"(b1), "+v"(b2), "+v"(b3))
 #define SV_BARRIER() asm volatile("s_barrier" ::: "memory")
 
-__global__ __launch_bounds__(kLmThreads, 1) void k_lmhead_argmax(const uint4 *__restrict__ H,
-                                                             const uint4 *__restrict__ W, int M, int D,
-                                                             int V, int mtiles, int ntiles,
-                                                             uint64_t *__restrict__ part_k, int segs) {
+// What the epilogue makes of a finished tile.
+enum LmEpi { kEpiArgmax = 0, kEpiStats = 1, kEpiRows = 2 };
+struct LmOut {
+    int segs;               // 128-column segments per row
+    uint64_t *keys;         // argmax: [M][segs] keys
+    float *part_R;          // stats: [M][segs] R
+    double *part_s;         // stats: [M][segs] s
+    float *xlog;            // stats: [M] the logit at each row's draft token
+    const int32_t *drafts;  // stats: [M / (K+1)][K] draft ids (row i of a request scores draft i)
+    int K;
+    float c_hi, c_lo;       // stats: log2(e)/T split in two floats
+    float *rows;            // rows: [M][V] fp32 logits
+    const ResidParam *rp;   // rows: output row m projects H row m (K+1) + rp[m].pos
+};
+
+template <int EPI>
+__global__ __launch_bounds__(kLmThreads, 1) void k_lmhead(const uint4 *__restrict__ H,
+                                                      const uint4 *__restrict__ W, int M, int D, int V,
+                                                      int mtiles, int ntiles, LmOut o) {
     const int bid = blockIdx.x;
     const int xcd = bid % kXcds, j = bid / kXcds;
     const int mt = j % mtiles;
@@ -112,13 +133,20 @@ __global__ __launch_bounds__(kLmThreads, 1) void k_lmhead_argmax(const uint4 *__
     // q = 8 i + w; lane l writes 16 bytes at 16 l, i.e. row 8 q + l / 8,
     // stored chunk l % 8, which holds the row's logical chunk
     // (l % 8) ^ ((row >> 1) & 7) (the swizzle is an involution).  Offsets are
-    // 32-bit 16-byte-chunk counts; rows past M or V read the last row.
+    // 32-bit 16-byte-chunk counts; rows past M or V read the last row.  For
+    // kEpiRows, tile row m is H row m (K + 1) + rp[m].pos.
+    auto hrow = [&](int m) {
+        if constexpr (EPI == kEpiRows)
+            return m * (o.K + 1) + o.rp[m].pos;
+        else
+            return m;
+    };
     int ga0, ga1, ga2, ga3, gb0, gb1, gb2, gb3;
 #define SV_GOFF(i, GA, GB)                                        \
     {                                                             \
         const int r = 8 * (kLmWaves * (i) + w) + lane / kChunks;  \
         const int c = (lane % kChunks) ^ ((r >> 1) & 7);          \
-        GA = min(m0 + r, M - 1) * dv + c;                         \
+        GA = hrow(min(m0 + r, M - 1)) * dv + c;                   \
         GB = min(n0 + r, V - 1) * dv + c;                         \
     }
     SV_GOFF(0, ga0, gb0)
@@ -225,36 +253,105 @@ __global__ __launch_bounds__(kLmThreads, 1) void k_lmhead_argmax(const uint4 *__
     LDS_WAIT0(p0, p1, q0, q1, q2, q3);  // no LDS read still in flight
     wait_vm<0>();                       // no DMA may still target LDS when the workgroup ends
 
-    // epilogue: per row, the first maximum over this wave's 128 columns
-    const int seg = (n0 + wn * 128) / kSegCols;
-    if (seg >= segs) return;
-    const int cbase = n0 + wn * 128 + (lane & 31);
+    // epilogue over this wave's 64 x 128 part: lanes l and l + 32 hold rows 4
+    // apart, and lane l % 32 holds columns cb + l % 32 + 32 b, b = 0..3
+    const int cb = n0 + wn * 128;
+    const int lc = lane & 31;
     const f32x16 acc[2][4] = {{c00, c01, c02, c03}, {c10, c11, c12, c13}};
+    const float ninf = -__builtin_huge_valf();
+    if constexpr (EPI == kEpiRows) {
+#pragma unroll
+        for (int a = 0; a < 2; ++a) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = m0 + wm * 64 + a * kTileRows + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                if (row >= M) continue;
+                float *dst = o.rows + static_cast<long long>(row) * V;
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const int col = cb + b * kTileRows + lc;
+                    if (col < V) dst[col] = acc[a][b][r];
+                }
+            }
+        }
+        return;
+    }
+    const int seg = cb / kSegCols;
+    if (seg >= o.segs) return;
 #pragma unroll
     for (int a = 0; a < 2; ++a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            float best = -__builtin_huge_valf();
-            int bi = INT_MAX;
+            const int row = m0 + wm * 64 + a * kTileRows + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+            if constexpr (EPI == kEpiArgmax) {
+                // the first maximum of the row's 128 columns
+                float best = ninf;
+                int bi = INT_MAX;
 #pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                const int col = cbase + b * kTileRows;
-                const float x = col < V ? acc[a][b][r] : -__builtin_huge_valf();
-                if (x > best || (bi == INT_MAX && col < V)) {
-                    best = x;
-                    bi = col;
+                for (int b = 0; b < 4; ++b) {
+                    const int col = cb + lc + b * kTileRows;
+                    const float x = col < V ? acc[a][b][r] : ninf;
+                    if (x > best || (bi == INT_MAX && col < V)) {
+                        best = x;
+                        bi = col;
+                    }
+                }
+                uint64_t key = argmax_key(best, bi);
+#pragma unroll
+                for (int off = 1; off < 32; off <<= 1) {
+                    const uint64_t y = __shfl_xor(key, off, kWave);
+                    key = y > key ? y : key;
+                }
+                if (lc == 0 && row < M) o.keys[static_cast<long long>(row) * o.segs + seg] = key;
+            } else {
+                // (R, s) of the row's 128 columns: each lane's four terms summed
+                // pairwise in fp32, the 32 lanes in fp64 (every lane shuffles)
+                float x[4];
+                float m = ninf;
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    x[b] = cb + lc + b * kTileRows < V ? acc[a][b][r] : ninf;
+                    m = fmaxf(m, x[b]);
+                }
+#pragma unroll
+                for (int off = 1; off < 32; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, kWave));
+                const float R = m == ninf ? 0.0f : m * o.c_hi;  // all -inf: every term is 0
+#pragma unroll
+                for (int b = 0; b < 4; ++b) x[b] = fast_exp2(fmaf(x[b], o.c_lo, fmaf(x[b], o.c_hi, -R)));
+                double sum = static_cast<double>(pairwise_sum(x));
+#pragma unroll
+                for (int off = 1; off < 32; off <<= 1) sum += __shfl_xor(sum, off, kWave);
+                if (row < M) {
+                    if (lc == 0) {
+                        const long long at = static_cast<long long>(row) * o.segs + seg;
+                        o.part_R[at] = m == ninf ? ninf : R;
+                        o.part_s[at] = sum;
+                    }
+                    // the logit at draft i, if it falls in this wave's columns
+                    const int req = row / (o.K + 1), i = row - req * (o.K + 1);
+                    if (i < o.K) {
+                        const int xt = o.drafts[static_cast<long long>(req) * o.K + i];
+                        const int rel = xt - cb;
+                        if (rel >= 0 && rel < 128 && xt < V && lc == (rel & 31)) {
+                            const int bb = rel >> 5;
+                            o.xlog[row] = bb == 0 ? acc[a][0][r] : bb == 1 ? acc[a][1][r]
+                                        : bb == 2 ? acc[a][2][r] : acc[a][3][r];
+                        }
+                    }
                 }
             }
-            uint64_t key = argmax_key(best, bi);
-#pragma unroll
-            for (int o = 1; o < 32; o <<= 1) {
-                const uint64_t y = __shfl_xor(key, o, kWave);
-                key = y > key ? y : key;
-            }
-            const int row = m0 + wm * 64 + a * kTileRows + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-            if ((lane & 31) == 0 && row < M) part_k[static_cast<long long>(row) * segs + seg] = key;
         }
     }
+}
+
+template <int EPI>
+hipError_t lm_launch(const void *H, const void *W, int M, int D, int V, const LmOut &o, hipStream_t s) {
+    const int mtiles = (M + kTM - 1) / kTM;
+    const int ntiles = (V + kTN - 1) / kTN;
+    const long long blocks = static_cast<long long>(kXcds) * mtiles * ((ntiles + kXcds - 1) / kXcds);
+    return launch_kernel(k_lmhead<EPI>, dim3(static_cast<unsigned>(blocks)), dim3(kLmThreads), 0, s,
+                         static_cast<const uint4 *>(H), static_cast<const uint4 *>(W), M, D, V, mtiles,
+                         ntiles, o);
 }
 
 }  // namespace
@@ -263,12 +360,35 @@ int lmhead_segs(int V) { return (V + kSegCols - 1) / kSegCols; }
 
 hipError_t launch_lmhead_argmax(const void *H, const void *W, int M, int D, int V, uint64_t *part_k,
                                 hipStream_t s) {
-    const int mtiles = (M + kTM - 1) / kTM;
-    const int ntiles = (V + kTN - 1) / kTN;
-    const long long blocks = static_cast<long long>(kXcds) * mtiles * ((ntiles + kXcds - 1) / kXcds);
-    return launch_kernel(k_lmhead_argmax, dim3(static_cast<unsigned>(blocks)), dim3(kLmThreads), 0, s,
-                         static_cast<const uint4 *>(H), static_cast<const uint4 *>(W), M, D, V, mtiles,
-                         ntiles, part_k, lmhead_segs(V));
+    LmOut o{};
+    o.segs = lmhead_segs(V);
+    o.keys = part_k;
+    return lm_launch<kEpiArgmax>(H, W, M, D, V, o, s);
+}
+
+hipError_t launch_lmhead_stats(const void *H, const void *W, int B, int K, int D, int V,
+                               const int32_t *drafts, const Scale &sc, float *part_R, double *part_s,
+                               float *xlog, hipStream_t s) {
+    LmOut o{};
+    o.segs = lmhead_segs(V);
+    o.part_R = part_R;
+    o.part_s = part_s;
+    o.xlog = xlog;
+    o.drafts = drafts;
+    o.K = K;
+    o.c_hi = sc.c_hi;
+    o.c_lo = sc.c_lo;
+    return lm_launch<kEpiStats>(H, W, B * (K + 1), D, V, o, s);
+}
+
+hipError_t launch_lmhead_rows(const void *H, const void *W, int B, int K, int D, int V,
+                              const ResidParam *rp, float *rows, hipStream_t s) {
+    LmOut o{};
+    o.segs = lmhead_segs(V);
+    o.K = K;
+    o.rp = rp;
+    o.rows = rows;
+    return lm_launch<kEpiRows>(H, W, B, D, V, o, s);
 }
 
 }  // namespace sv

@@ -181,30 +181,45 @@ __global__ __launch_bounds__(kBlock) void k_rowstats(
 
 // ---- S2/S3: merge, gather, acceptance scan ----------------------------------------
 
-// Row r of request b (0..K target rows, then K draft rows) as a global row id.
-__device__ __forceinline__ long long req_row(int b, int K, long long rows_t, int r) {
-    return r <= K ? static_cast<long long>(b) * (K + 1) + r
-                  : rows_t + static_cast<long long>(b) * K + (r - K - 1);
-}
-
-template <typename E>
+// FUSED: the target rows were never written (their partials come from the
+// LM-head projection, which also kept the logit at each draft in xlog), and
+// the row each request draws from is formed afterwards at row b of a
+// per-request buffer, as is its draft row.
+template <typename E, bool FUSED>
 __global__ __launch_bounds__(kBlock) void k_accept(
     const typename E::storage *__restrict__ tgt, const typename E::storage *__restrict__ drf,
     const int32_t *__restrict__ drafts, const float *__restrict__ ua, const float *__restrict__ us,
-    int B, int K, int V, int segs, int lds_rows, double c, const float *__restrict__ part_R,
-    const double *__restrict__ part_s, double *__restrict__ L2out, int32_t *__restrict__ accept_len,
-    int32_t *__restrict__ out_tokens, float *__restrict__ lse_t, float *__restrict__ lse_d,
-    int32_t *__restrict__ status, ResidParam *__restrict__ rp) {
+    int B, int K, int V, PartRows pt, PartRows pd, int lds_rows, double c, const float *__restrict__ xlog,
+    double *__restrict__ L2out, int32_t *__restrict__ accept_len, int32_t *__restrict__ out_tokens,
+    float *__restrict__ lse_t, float *__restrict__ lse_d, int32_t *__restrict__ status,
+    ResidParam *__restrict__ rp) {
     // LDS: the 2K+1 row log2-normalisers, then staged partials of lds_rows rows
+    // (staging only when target and draft rows have the same segment count)
     extern __shared__ __align__(16) unsigned char smem[];
     const int nrows = 2 * K + 1;
+    const int segs = pt.segs;
     double *sL2 = reinterpret_cast<double *>(smem);
     double *stS = sL2 + nrows;
     float *stR = reinterpret_cast<float *>(stS + static_cast<size_t>(lds_rows) * segs);
     const int b = blockIdx.x;
     const int tid = threadIdx.x, wid = tid >> 6, lane = tid & (kWave - 1);
-    const long long rows_t = static_cast<long long>(B) * (K + 1);
     const double inf = __builtin_huge_val();
+    // partials of row r of this request: target rows 0..K, then draft rows
+    auto row_R = [&](int r) {
+        return r <= K ? pt.R + (static_cast<long long>(b) * (K + 1) + r) * pt.segs
+                      : pd.R + (static_cast<long long>(b) * K + (r - K - 1)) * pd.segs;
+    };
+    auto row_s = [&](int r) {
+        return r <= K ? pt.s + (static_cast<long long>(b) * (K + 1) + r) * pt.segs
+                      : pd.s + (static_cast<long long>(b) * K + (r - K - 1)) * pd.segs;
+    };
+    // the target logit at draft i (its row scores draft i)
+    auto tgt_at = [&](int i, int x) {
+        if constexpr (FUSED)
+            return xlog[static_cast<long long>(b) * (K + 1) + i];
+        else
+            return to_f32(tgt[(static_cast<long long>(b) * (K + 1) + i) * V + x]);
+    };
 
     // The drafts and the two logits each one is scored with, fetched for the
     // first 64 positions while the partials are merged.
@@ -214,7 +229,7 @@ __global__ __launch_bounds__(kBlock) void k_accept(
     if (tid < K) {
         x0 = xb[tid];
         if (x0 >= 0 && x0 < V) {
-            xp0 = to_f32(tgt[(static_cast<long long>(b) * (K + 1) + tid) * V + x0]);
+            xp0 = tgt_at(tid, x0);
             xq0 = to_f32(drf[(static_cast<long long>(b) * K + tid) * V + x0]);
         }
     }
@@ -226,9 +241,8 @@ __global__ __launch_bounds__(kBlock) void k_accept(
         if (lds_rows > 0) {
             for (int i = tid; i < nr * segs; i += kBlock) {
                 const int rr = i / segs, sg = i - rr * segs;
-                const long long g = req_row(b, K, rows_t, r0 + rr) * segs + sg;
-                stR[i] = part_R[g];
-                stS[i] = part_s[g];
+                stR[i] = row_R(r0 + rr)[sg];
+                stS[i] = row_s(r0 + rr)[sg];
             }
             __syncthreads();
         }
@@ -239,6 +253,7 @@ __global__ __launch_bounds__(kBlock) void k_accept(
         for (int rb = wid; rb < nr; rb += kMergeILP * kWavesPerBlock) {
             const float *pR[kMergeILP];
             const double *pS[kMergeILP];
+            int ns[kMergeILP];
             bool ok[kMergeILP];
             float Rm[kMergeILP];
             double acc[kMergeILP];
@@ -250,20 +265,21 @@ __global__ __launch_bounds__(kBlock) void k_accept(
                 if (lds_rows > 0) {
                     pR[q] = stR + rc * segs;
                     pS[q] = stS + rc * segs;
+                    ns[q] = segs;
                 } else {
-                    const long long g = req_row(b, K, rows_t, r0 + rc) * segs;
-                    pR[q] = part_R + g;
-                    pS[q] = part_s + g;
+                    pR[q] = row_R(r0 + rc);
+                    pS[q] = row_s(r0 + rc);
+                    ns[q] = r0 + rc <= K ? pt.segs : pd.segs;
                 }
                 Rm[q] = -__builtin_huge_valf();
-                for (int sg = lane; sg < segs; sg += kWave) Rm[q] = fmaxf(Rm[q], pR[q][sg]);
+                for (int sg = lane; sg < ns[q]; sg += kWave) Rm[q] = fmaxf(Rm[q], pR[q][sg]);
             }
 #pragma unroll
             for (int q = 0; q < kMergeILP; ++q) {
                 Rm[q] = wave_max(Rm[q]);
                 acc[q] = 0.0;
                 if (Rm[q] != -__builtin_huge_valf()) {
-                    for (int sg = lane; sg < segs; sg += kWave) {
+                    for (int sg = lane; sg < ns[q]; sg += kWave) {
                         const double ss = pS[q][sg];
                         if (ss > 0.0)
                             acc[q] += ss * exp2(static_cast<double>(pR[q][sg]) - static_cast<double>(Rm[q]));
@@ -300,7 +316,7 @@ __global__ __launch_bounds__(kBlock) void k_accept(
             const int x = i0 == 0 ? x0 : xb[i];
             double r = 0.0;
             if (x >= 0 && x < V) {
-                const double xp = i0 == 0 ? xp0 : to_f32(tgt[(static_cast<long long>(b) * (K + 1) + i) * V + x]);
+                const double xp = i0 == 0 ? xp0 : tgt_at(i, x);
                 const double xq = i0 == 0 ? xq0 : to_f32(drf[(static_cast<long long>(b) * K + i) * V + x]);
                 const double px = exp2(xp * c - sL2[i]);
                 const double qx = exp2(xq * c - sL2[K + 1 + i]);
@@ -324,11 +340,11 @@ __global__ __launch_bounds__(kBlock) void k_accept(
         ResidParam P;
         P.pos = n;
         P.u = static_cast<double>(us[static_cast<long long>(b) * (K + 1) + n]);
-        P.row_p = static_cast<long long>(b) * (K + 1) + n;
+        P.row_p = FUSED ? b : static_cast<long long>(b) * (K + 1) + n;
         P.L2p = sL2[n];
         if (n < K) {
             P.mode = 1;
-            P.row_q = static_cast<long long>(b) * K + n;
+            P.row_q = FUSED ? b : static_cast<long long>(b) * K + n;
             P.L2q = sL2[K + 1 + n];
         } else {
             P.mode = 0;
@@ -574,6 +590,35 @@ __global__ __launch_bounds__(kWave) void k_resid_select(
     }
 }
 
+// Draft row b K + pos of each request that draws a residual, widened to fp32
+// into row b of out (the fused LM-head form, whose draw reads fp32 rows).  A
+// thread moves one 16-byte input vector.
+template <typename E, bool ALIGNED>
+__global__ __launch_bounds__(kBlock) void k_gather_draft_rows(const typename E::storage *__restrict__ drf,
+                                                              int K, int V, int nvec,
+                                                              const ResidParam *__restrict__ rp,
+                                                              float *__restrict__ out) {
+    constexpr int P = E::kPerVec;
+    const int b = blockIdx.y;
+    const int mode = rp[b].mode, pos = rp[b].pos;
+    if (mode != 1) return;
+    const typename E::storage *src = drf + (static_cast<long long>(b) * K + pos) * V;
+    float *dst = out + static_cast<long long>(b) * V;
+    for (int j = blockIdx.x * kBlock + threadIdx.x; j < nvec; j += gridDim.x * kBlock) {
+        float x[P];
+        load_vec<E, ALIGNED>(src, V, j, x);
+        if constexpr (ALIGNED) {
+#pragma unroll
+            for (int e = 0; e < P; e += 4)
+                *reinterpret_cast<float4 *>(dst + j * P + e) = make_float4(x[e], x[e + 1], x[e + 2], x[e + 3]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < P; ++e)
+                if (j * P + e < V) dst[j * P + e] = x[e];
+        }
+    }
+}
+
 // ---- dead-row skipping (stochastic chains without lse outputs) --------------------
 //
 // The protocol is described with SkipCtl.  Here the segments of position p are
@@ -777,24 +822,24 @@ hipError_t launch_skip(const void *tgt, const void *drf, const int32_t *drafts, 
 }
 
 hipError_t launch_accept(const void *tgt, const void *drf, const int32_t *drafts, const float *ua,
-                         const float *us, int B, int K, int V, const RowGeom &g, sv_dtype dt,
-                         const Scale &sc, const float *part_R, const double *part_s, double *L2,
+                         const float *us, int B, int K, int V, sv_dtype dt, const Scale &sc,
+                         const PartRows &pt, const PartRows &pd, const float *xlog, double *L2,
                          int32_t *accept_len, int32_t *out_tokens, float *lse_t, float *lse_d,
                          int32_t *status, ResidParam *rp, hipStream_t s) {
     const int nrows = 2 * K + 1;
-    const size_t per_row = static_cast<size_t>(g.segs) * (sizeof(float) + sizeof(double));
-    const int lr = per_row > static_cast<size_t>(kMergeLdsBytes)
+    const size_t per_row = static_cast<size_t>(pt.segs) * (sizeof(float) + sizeof(double));
+    const int lr = (K > 0 && pd.segs != pt.segs) || per_row > static_cast<size_t>(kMergeLdsBytes)
                        ? 0
                        : static_cast<int>(std::min<size_t>(nrows, kMergeLdsBytes / per_row));
     const size_t lds = sizeof(double) * static_cast<size_t>(nrows) + static_cast<size_t>(lr) * per_row;
-    if (dt == SV_BF16)
-        return launch_kernel(k_accept<BF16>, dim3(B), dim3(kBlock), lds, s,
-                             static_cast<const uint16_t *>(tgt), static_cast<const uint16_t *>(drf),
-                             drafts, ua, us, B, K, V, g.segs, lr, sc.c, part_R, part_s, L2,
-                             accept_len, out_tokens, lse_t, lse_d, status, rp);
-    return launch_kernel(k_accept<F32>, dim3(B), dim3(kBlock), lds, s, static_cast<const float *>(tgt),
-                         static_cast<const float *>(drf), drafts, ua, us, B, K, V, g.segs, lr, sc.c,
-                         part_R, part_s, L2, accept_len, out_tokens, lse_t, lse_d, status, rp);
+#define SV_ACC(E, FUSED)                                                                                  \
+    launch_kernel(k_accept<E, FUSED>, dim3(B), dim3(kBlock), lds, s,                                       \
+                  static_cast<const typename E::storage *>(tgt), static_cast<const typename E::storage *>(drf), \
+                  drafts, ua, us, B, K, V, pt, pd, lr, sc.c, xlog, L2, accept_len, out_tokens, lse_t, lse_d, \
+                  status, rp)
+    if (dt == SV_BF16) return xlog ? SV_ACC(BF16, true) : SV_ACC(BF16, false);
+    return xlog ? SV_ACC(F32, true) : SV_ACC(F32, false);
+#undef SV_ACC
 }
 
 namespace {
@@ -820,6 +865,21 @@ hipError_t resid_select_t(const void *tgt, const void *drf, int B, int K, int V,
                          g.ntiles, sc.c_hi, sc.c_lo, rp, tile_mass, out_tokens);
 }
 }  // namespace
+
+hipError_t launch_gather_draft_rows(const void *drf, sv_dtype dt, int B, int K, int V,
+                                    const ResidParam *rp, float *out, hipStream_t s) {
+    // aligned: 16-byte input vectors, and 16-byte aligned fp32 output rows
+    const bool al = (reinterpret_cast<uintptr_t>(drf) & 15u) == 0 && (reinterpret_cast<uintptr_t>(out) & 15u) == 0 &&
+                    V % (dt == SV_BF16 ? 8 : 4) == 0;
+    const int P = dt == SV_BF16 ? 8 : 4;
+    const int nvec = (V + P - 1) / P;
+    const dim3 grid(static_cast<unsigned>(std::min(64, (nvec + kBlock - 1) / kBlock)), static_cast<unsigned>(B));
+#define SV_GD(E, A) launch_kernel(k_gather_draft_rows<E, A>, grid, dim3(kBlock), 0, s, \
+                                  static_cast<const typename E::storage *>(drf), K, V, nvec, rp, out)
+    if (dt == SV_BF16) return al ? SV_GD(BF16, true) : SV_GD(BF16, false);
+    return al ? SV_GD(F32, true) : SV_GD(F32, false);
+#undef SV_GD
+}
 
 hipError_t launch_resid_mass(const void *tgt, const void *drf, int B, int V, const RowGeom &g,
                              sv_dtype dt, const Scale &sc, const ResidParam *rp, double *tile_mass,

@@ -205,6 +205,38 @@ sv_status spec_verify_tree_lmhead(const void *hidden, const void *lm_head,
                                   size_t workspace_bytes, void *stream);
 
 /*
+ * Stochastic chain verification (speculative sampling) fused with the target's
+ * LM-head projection: the target rows are the logits H W^T, formed on the
+ * matrix cores and reduced at once to the row statistics the acceptance test
+ * and the lse outputs need (and to the logit at each draft), so the B*(K+1)
+ * target rows are never written.  The one row per request that a token is
+ * drawn from is formed again afterwards (B rows of V fp32 logits, in the
+ * workspace).  Same pages and sections as spec_verify_sample and
+ * spec_verify_greedy_lmhead.
+ *
+ *   hidden        [B][K+1][D] bf16, lm_head [V][D] bf16, D a positive multiple
+ *                 of 128, both 16-byte aligned (as for spec_verify_greedy_lmhead).
+ *   draft_logits  [B][K][V] of dtype dt (the draft model's own logits).
+ *   draft_tokens, u_accept, u_sample, temperature, and every output: as for
+ *                 spec_verify_sample.
+ * The target logit of id v at a row is the fp32 sum over k of
+ * hidden[k] * lm_head[v][k] (products exact, fp32 accumulation in an
+ * unspecified order, the same for both passes over a row); everything else is
+ * spec_verify_sample on those logits.  Every target row is formed whether or
+ * not lse outputs are requested.
+ * Workspace: sv_sample_lmhead_workspace_bytes(B, K, D, V, dt) (0 for invalid
+ * or unsupported sizes).
+ */
+size_t sv_sample_lmhead_workspace_bytes(int B, int K, int D, int V, sv_dtype dt);
+
+sv_status spec_verify_sample_lmhead(const void *hidden, const void *lm_head, const void *draft_logits,
+                                    const int32_t *draft_tokens, const float *u_accept,
+                                    const float *u_sample, int B, int K, int D, int V, sv_dtype dt,
+                                    float temperature, int32_t *accept_len, int32_t *out_tokens,
+                                    float *lse_target, float *lse_draft, int32_t *req_status,
+                                    void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Commit of a verified draft tree's accepted path in the target's KV cache
  * (AdaPLD page, Algorithm 1: the accepted tokens are appended and the context
  * updated; section 3.3: the whole tree is verified in one target pass, which
@@ -314,7 +346,10 @@ typedef enum {
     SV_K_NGRAM_EMIT = 12,  /* lexical retrieval: candidate positions in order */
     SV_K_SKIP_TREE = 13,   /* node-row argmax + tree walk, skipping rows of rejected nodes */
     SV_K_READ_PROBE = 14,  /* read-only stream (measurement aid) */
-    SV_K_COUNT = 15
+    SV_K_LMHEAD_STATS = 15, /* LM-head projection + row statistics partials and draft logits */
+    SV_K_LMHEAD_ROWS = 16,  /* LM-head projection of the rows tokens are drawn from, written */
+    SV_K_GATHER_ROWS = 17,  /* draft rows of residual draws, widened to fp32 */
+    SV_K_COUNT = 18
 } sv_kernel_id;
 
 sv_status sv_trace_begin(int capacity, unsigned kernel_mask);

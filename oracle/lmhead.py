@@ -1,4 +1,4 @@
-"""CPU oracle for greedy verification fused with the LM-head projection (test
+"""CPU oracle for verification fused with the LM-head projection (test
 infrastructure: only the tests, ``__graft_entry__``'s smoke check and
 ``bench.py``'s CPU baseline may use it).
 
@@ -14,7 +14,11 @@ for trees.
 
 The oracle forms the logits in fp64 from the bf16 inputs (products and sums
 of bf16 values: the only rounding is fp64's), takes the first maximum of each
-row, and applies the chain or tree rule written out below.
+row, and applies the chain or tree rule written out below.  Speculative
+sampling on those logits (``verify_sample``) is the sampling oracle of
+``oracle/sv_oracle.c`` applied to them, rounded to fp32 on the way in: exact
+for the exact recipe, whose logits are fp32 numbers, and within half an fp32
+ulp of the product otherwise.
 
 The device path accumulates in fp32 in an order it does not fix.  With
 products of bf16 values exact in fp32, any order's error on a logit is at
@@ -178,3 +182,31 @@ def verify_tree(hidden_bits, lm_head_bits, node_tokens, parents, exact=False):
     out["flagged"] = ~certain.all(axis=1)
     out["argmax"] = a
     return out
+
+
+def sample_flag_eps(hidden_bits, lm_head_bits, T):
+    """Draw-margin threshold below which a sampled request may differ from a
+    device result whose logits carry fp32 accumulation error (the bound above).
+    With E the largest bound of any logit, every p(v) = exp(L[v]/T - lse) is
+    off by a factor within exp(+-2E/T) (2E: the logit and its row's lse), so a
+    ratio p/q near u <= 1 moves by at most eps = exp(2E/T) - 1, and a cell edge
+    C/Z of an inverse CDF by at most 2 eps / Z.  Returns eps; a request is
+    flagged when its margin is at most max(eps, 2 eps / Z)."""
+    E = accumulation_bound(hidden_bits, lm_head_bits).max()
+    return float(np.expm1(2.0 * E / T))
+
+
+def verify_sample(hidden_bits, lm_head_bits, draft, draft_tokens, u_accept, u_sample, T, lib=None):
+    """Speculative sampling (stochastic chain) on the target logits H W^T:
+    hidden [B, K+1, D] and lm_head [V, D] bf16 bits, draft [B, K, V] logits
+    (bf16 bits or float32).  Returns the sampling oracle's outputs (accept_len,
+    tokens, lse_target, lse_draft, status, margin, Z)."""
+    from . import verify_sample as sample_on_logits
+
+    L = logits(hidden_bits, lm_head_bits).astype(np.float32)
+    B, R, V = L.shape
+    d = np.asarray(draft)
+    if d.dtype == np.uint16:
+        d = (d.astype(np.uint32) << np.uint32(16)).view(np.float32)  # exact widening
+    d = np.ascontiguousarray(d, dtype=np.float32).reshape(B, R - 1, V)
+    return sample_on_logits(L, d, draft_tokens, u_accept, u_sample, T, lib=lib)

@@ -173,6 +173,41 @@ def test_lmhead_argument_checks(lib):
     assert lib.sv_lmhead_workspace_bytes(0, 10) == 0
 
 
+def test_sample_lmhead_argument_checks(lib):
+    def f(**kw):
+        a = dict(h=FAKE, w=FAKE, d=FAKE, x=FAKE, ua=FAKE, us=FAKE, B=2, K=3, D=128, V=100, dt=sv.SV_BF16,
+                 T=1.0, n=FAKE, tok=FAKE, ws=FAKE, wsb=0)
+        a.update(kw)
+        return lib.spec_verify_sample_lmhead(a["h"], a["w"], a["d"], a["x"], a["ua"], a["us"], a["B"], a["K"],
+                                             a["D"], a["V"], a["dt"], a["T"], a["n"], a["tok"], None, None,
+                                             None, a["ws"], a["wsb"], None)
+
+    assert f(dt=4) == sv.SV_ERR_UNSUPPORTED
+    assert f(B=-1) == sv.SV_ERR_INVALID_ARG
+    assert f(D=0) == sv.SV_ERR_INVALID_ARG
+    assert f(T=0.0) == sv.SV_ERR_INVALID_ARG
+    assert f(T=float("nan")) == sv.SV_ERR_INVALID_ARG
+    assert f(D=100) == sv.SV_ERR_UNSUPPORTED       # not a multiple of 128
+    assert f(K=2000) == sv.SV_ERR_UNSUPPORTED
+    assert f(h=None) == sv.SV_ERR_INVALID_ARG
+    assert f(d=None) == sv.SV_ERR_INVALID_ARG
+    assert f(us=None) == sv.SV_ERR_INVALID_ARG
+    assert f(h=ctypes.c_void_p((1 << 20) + 8)) == sv.SV_ERR_INVALID_ARG
+    assert f(ws=ctypes.c_void_p((1 << 20) + 64)) == sv.SV_ERR_INVALID_ARG
+    assert f() == sv.SV_ERR_WORKSPACE
+    assert f(K=0, d=None, x=None, ua=None) == sv.SV_ERR_WORKSPACE  # K = 0 needs no draft inputs
+    need = lib.sv_sample_lmhead_workspace_bytes(2, 3, 128, 100, sv.SV_BF16)
+    assert need > 0 and f(wsb=need - 1) == sv.SV_ERR_WORKSPACE
+    assert f(T=1e-40, wsb=need) == sv.SV_ERR_UNSUPPORTED
+    assert f(B=0, h=None, ws=None) == sv.SV_OK
+    assert lib.sv_sample_lmhead_workspace_bytes(2, 3, 100, 100, sv.SV_BF16) == 0
+    assert lib.sv_sample_lmhead_workspace_bytes(0, 3, 128, 100, sv.SV_BF16) == 0
+    # at the Qwen3-8B shape: B*(K+1) rows of 1187 (R, s) partials plus two fp32
+    # rows per request dominate
+    big = lib.sv_sample_lmhead_workspace_bytes(256, 7, 4096, 151936, sv.SV_BF16)
+    assert 2048 * 1187 * 12 + 2 * 256 * 151936 * 4 < big < 400 << 20
+
+
 def test_ngram_argument_checks(lib):
     def call(**kw):
         a = dict(c=FAKE, B=2, L=100, ln=FAKE, q=FAKE, n=3, cap=4, cnt=FAKE, pos=FAKE, st=None, ws=FAKE,

@@ -1,5 +1,6 @@
-"""GPU parity of greedy verification fused with the LM-head projection
-(spec_verify_greedy_lmhead / spec_verify_tree_lmhead) against oracle/lmhead.py.
+"""GPU parity of verification fused with the LM-head projection
+(spec_verify_greedy_lmhead / spec_verify_tree_lmhead / spec_verify_sample_lmhead)
+against oracle/lmhead.py.
 
 Exact-recipe inputs make every fp32 accumulation exact, so every output must
 match bit for bit.  General-recipe inputs round; requests whose decisive rows
@@ -13,7 +14,7 @@ import torch
 
 import draft_token_verification_04_amd as sv
 import workloads
-from gpu_helpers import dev, ints_to_dev, note
+from gpu_helpers import FLAG_EPS, check_sample, dev, f32_to_dev, ints_to_dev, note
 from oracle import lmhead
 
 pytestmark = pytest.mark.gpu
@@ -113,3 +114,102 @@ def test_tree_full_size_sampled():
     o = lmhead.verify_tree(w.hidden[reqs], w.lm_head, w.node_tokens[reqs], w.parents[reqs], exact=True)
     assert o["accept_len"].max() >= 2
     compare(g, o, ("accept_len", "path", "tokens", "status"), reqs=reqs)
+
+
+# ---- speculative sampling on the projection ------------------------------------
+
+def gpu_sample_lm(w, **kw):
+    if w.dtype == "bf16":
+        d = bf16_dev(w.draft)
+    else:
+        d = torch.from_numpy(np.ascontiguousarray(w.draft, np.float32)).to(dev())
+    g = sv.spec_verify_sample_lmhead(bf16_dev(w.hidden), bf16_dev(w.lm_head), d if w.K else None,
+                                     ints_to_dev(w.draft_tokens), f32_to_dev(w.u_accept),
+                                     f32_to_dev(w.u_sample), w.T, **kw)
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy() for k, v in g.items()}
+
+
+def oracle_sample_lm(w, reqs=None):
+    r = slice(None) if reqs is None else np.asarray(reqs)
+    return lmhead.verify_sample(w.hidden[r], w.lm_head, w.draft[r], w.draft_tokens[r], w.u_accept[r],
+                                w.u_sample[r], w.T)
+
+
+SAMPLE_EXACT = [
+    # B, K, D, V, draft dtype, T
+    (3, 2, 128, 77, "bf16", 1.0),
+    (5, 3, 128, 1000, "f32", 0.7),
+    (7, 7, 384, 1001, "bf16", 1.3),     # ragged V for bf16 drafts (unaligned path)
+    (40, 7, 256, 5000, "bf16", 0.7),
+    (2, 0, 128, 300, "bf16", 1.0),      # K = 0: bonus draw only
+    (33, 7, 128, 258, "f32", 1.0),      # V % 4 = 2: unaligned fp32 rows
+    (9, 3, 2560, 700, "bf16", 0.9),
+    (300, 1, 128, 520, "bf16", 1.0),    # several row tiles in both projection passes
+]
+
+
+@pytest.mark.parametrize("lse", [True, False], ids=["lse", "nolse"])
+@pytest.mark.parametrize("case", SAMPLE_EXACT, ids=lambda c: "B{}K{}D{}V{}{}T{}".format(*c))
+def test_sample_exact(case, lse):
+    B, K, D, V, dt, T = case
+    note(f"lmhead sample exact {case} lse={lse}")
+    w = workloads.make_sample_lmhead(B, K, D, V, exact=True, dtype=dt, T=T, seed=B * 10 + K)
+    if K >= 3 and B >= 3:  # out-of-range drafts reject at their position
+        w.draft_tokens[1, 0] = -3
+        w.draft_tokens[2, 2] = V
+    o = oracle_sample_lm(w)
+    g = gpu_sample_lm(w, lse=lse)
+    n_ok, n_flag, _ = check_sample(w, g, o)
+    assert n_ok >= B - 2
+
+
+def test_sample_general_recipe():
+    # fp32 accumulation rounds: requests whose margin is within the derived
+    # bound of a decision (lmhead.sample_flag_eps) are flagged and skipped;
+    # lse within the bound on a logit over T
+    B, K, D, V, T = 64, 7, 128, 400, 1.0
+    note("lmhead sample general")
+    w = workloads.make_sample_lmhead(B, K, D, V, exact=False, T=T, noise_sigma=0.5, seed=12)
+    o = oracle_sample_lm(w)
+    eps = lmhead.sample_flag_eps(w.hidden, w.lm_head, T)
+    g = gpu_sample_lm(w)
+    flagged = o["margin"] <= np.maximum(eps, 2 * eps / np.maximum(o["Z"], 1e-300)) + FLAG_EPS
+    print(f"eps {eps:.2e}: flagged {int(flagged.sum())}/{B}, mean accept {o['accept_len'].mean():.2f}")
+    assert flagged.sum() < B // 2
+    keep = ~flagged
+    assert np.array_equal(g["accept_len"][keep], o["accept_len"][keep])
+    assert np.array_equal(g["tokens"][keep], o["tokens"][keep])
+    E = lmhead.accumulation_bound(w.hidden, w.lm_head).max()
+    assert (np.abs(g["lse_target"] - o["lse_target"]) <= E / T + 1e-5 * np.abs(o["lse_target"]) + 1e-6).all()
+    assert (np.abs(g["lse_draft"] - o["lse_draft"]) <= 1e-5 * np.abs(o["lse_draft"]) + 1e-6).all()
+
+
+def test_sample_full_size_sampled():
+    # Qwen3-8B shape: B=256, K=7, D=4096, V=151936, bf16 draft logits, T=0.7;
+    # 16 sampled requests have draft logits shaped on the target's and are
+    # checked against the oracle
+    s = workloads.LMHEAD_SHAPE
+    reqs = np.arange(0, s["B"], s["B"] // 16)
+    note("lmhead sample full size")
+    w = workloads.make_sample_lmhead(s["B"], s["K"], s["D"], s["V"], exact=True, dtype="bf16", T=0.7,
+                                     seed=23, plant=reqs)
+    g = gpu_sample_lm(w)
+    o = oracle_sample_lm(w, reqs)
+    sub = {k: v[reqs] for k, v in g.items()}
+    n_ok, n_flag, _ = check_sample(w, sub, o)
+    print(f"unflagged {n_ok}/{len(reqs)}, mean accept {o['accept_len'].mean():.2f}")
+    assert n_ok >= len(reqs) - 1
+    assert o["accept_len"].mean() > 0.5
+    assert ((g["accept_len"] >= 0) & (g["accept_len"] <= s["K"])).all()
+    assert ((g["tokens"][np.arange(s["B"]), g["accept_len"]] >= 0)).all()
+
+
+def test_sample_trace_names_each_kernel():
+    note("lmhead sample trace")
+    w = workloads.make_sample_lmhead(8, 3, 128, 700, exact=True, seed=3)
+    sv.trace_begin(64)
+    gpu_sample_lm(w)
+    recs = sv.trace_end()
+    assert [r[0] for r in recs] == ["lmhead_stats", "rowstats", "accept", "lmhead_rows", "gather_rows",
+                                    "resid_mass", "resid_select"]

@@ -142,3 +142,48 @@ def test_general_recipe_flags_only_near_ties():
     assert (gap[~certain] <= 2 * E.max()).all()
     assert certain.mean() > 0.95
     assert o["flagged"].mean() < 0.2
+
+
+def _integer_logits(hidden_bits, lm_head_bits):
+    """Exact-recipe logits by integer arithmetic: H = i/8, W = j/64, so the
+    logit is (sum of i*j) / 512."""
+    hi = np.rint(lmhead.bf16_to_f64(hidden_bits) * 8).astype(np.int64)
+    wi = np.rint(lmhead.bf16_to_f64(lm_head_bits) * 64).astype(np.int64)
+    return (hi @ wi.T).astype(np.float64) / 512.0
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_sampling_on_the_projection_is_sampling_on_its_logits(dtype):
+    # exact recipe: the logits the fused oracle samples from are H W^T exactly
+    # (integer arithmetic here), and the rest is the pinned sampling oracle
+    w = workloads.make_sample_lmhead(12, 5, 128, 700, exact=True, dtype=dtype, T=0.8, seed=8)
+    L = _integer_logits(w.hidden, w.lm_head)
+    L32 = L.astype(np.float32)
+    assert np.array_equal(L32.astype(np.float64), L)
+    d = workloads.bf16_bits_to_f32(w.draft) if dtype == "bf16" else w.draft
+    o = lmhead.verify_sample(w.hidden, w.lm_head, w.draft, w.draft_tokens, w.u_accept, w.u_sample, w.T)
+    c = oracle.verify_sample(L32, np.ascontiguousarray(d, np.float32), w.draft_tokens, w.u_accept,
+                             w.u_sample, w.T)
+    for k in ("accept_len", "tokens", "status", "lse_target", "lse_draft", "margin", "Z"):
+        assert np.array_equal(o[k], c[k]), k
+    # the draft logits were shaped on the target's, so drafts do get accepted
+    assert o["accept_len"].mean() > 0.5
+
+
+def test_sampling_flag_threshold_bounds_fp32_sums_in_any_order():
+    # the relative error of every p(v) = softmax(L/T)(v) built on fp32 sums in
+    # any order stays within the eps the oracle derives from the bound
+    w = workloads.make_sample_lmhead(2, 3, 256, 300, exact=False, T=0.7, seed=9)
+    Hb = w.hidden.reshape(-1, 256)
+    H = lmhead.bf16_to_f64(Hb).astype(np.float32)
+    W = lmhead.bf16_to_f64(w.lm_head).astype(np.float32)
+    L = lmhead.logits(Hb, w.lm_head)
+    eps = lmhead.sample_flag_eps(w.hidden, w.lm_head, w.T)
+    p = np.exp(L / w.T - np.log(np.exp(L / w.T).sum(-1, keepdims=True)))
+    worst = 0.0
+    for order in ("forward", "reverse", "pairwise", "blocks16"):
+        Lf = _fp32_sums(H, W, order).astype(np.float64)
+        pf = np.exp(Lf / w.T - np.log(np.exp(Lf / w.T).sum(-1, keepdims=True)))
+        worst = max(worst, np.abs(pf / p - 1).max())
+    assert 0 < worst <= eps
+    assert eps < 1e-2

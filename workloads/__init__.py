@@ -359,6 +359,53 @@ def _lmhead_argmax(Hb: np.ndarray, Wb: np.ndarray, exact: bool) -> np.ndarray:
     return arg[np.argmax(best, axis=0), np.arange(Hb.shape[0])]
 
 
+def _lmhead_logits(Hb: np.ndarray, Wb: np.ndarray, exact: bool) -> np.ndarray:
+    """H W^T as float32 [rows, V], for shaping correlated draft logits (the exact
+    recipe is exact in fp32; the general one is formed in fp64 and rounded)."""
+    dt = np.float32 if exact else np.float64
+    h = bf16_bits_to_f32(Hb).astype(dt)
+    V = Wb.shape[0]
+    out = np.empty((Hb.shape[0], V), dtype=np.float32)
+
+    def job(v0):
+        out[:, v0:v0 + _LM_BLOCK] = h @ bf16_bits_to_f32(Wb[v0:v0 + _LM_BLOCK]).astype(dt).T
+
+    with ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(job, range(0, V, _LM_BLOCK)))
+    return out
+
+
+def make_sample_lmhead(B, K, D, V, exact=True, dtype="bf16", T=0.7, noise_sigma=1.0, seed=0,
+                       plant=None) -> Workload:
+    """Stochastic-chain inputs for the fused LM-head path: hidden [B,K+1,D] and
+    lm_head [V,D] as for the greedy form; draft logits [B,K,V] are the target
+    logits of the same position (H W^T) plus N(0, noise_sigma^2) for the
+    `plant` requests (all by default) and independent N(0, 3^2) rows for the
+    others; drafts are drawn from softmax(Lq/T) of the stored draft logits."""
+    ss = seed if isinstance(seed, np.random.SeedSequence) else np.random.SeedSequence(seed)
+    st = ss.spawn(6)
+    Hb, Wb = _lmhead_values(st[_S_TARGET], B * (K + 1), D, V, exact)
+    H3 = Hb.reshape(B, K + 1, D)
+    nrng = st[_S_NOISE].spawn(2)
+    dr = np.empty((B * K, V), dtype=np.float32)
+    _normal_rows(nrng[0], B * K, V, 3.0, dr)
+    dr = dr.reshape(B, K, V)
+    reqs = np.arange(B) if plant is None else np.asarray(plant)
+    if K > 0 and len(reqs):
+        L = _lmhead_logits(H3[reqs, :K].reshape(-1, D), Wb, exact)
+        noise = np.empty_like(L)
+        _normal_rows(nrng[1], L.shape[0], V, noise_sigma, noise)
+        dr[reqs] = (L + noise).reshape(len(reqs), K, V)
+        del L, noise
+    stored = _stored(dr, dtype)
+    del dr
+    drafts = _gumbel_draws(st[_S_DRAFTS], _as_f32(stored.reshape(B * K, V), dtype), T).reshape(B, K)
+    ua, us = _uniforms(st[_S_UNIF], B, K)
+    return Workload(mode="sample_lmhead", B=B, K=K, V=V, dtype=dtype, T=float(T), draft=stored,
+                    draft_tokens=drafts, u_accept=ua, u_sample=us, hidden=H3, lm_head=Wb,
+                    meta=dict(D=D, exact=exact, noise_sigma=noise_sigma))
+
+
 def make_greedy_lmhead(B, K, D, V, exact=True, p_match=0.8, seed=0, plant=None) -> Workload:
     """Greedy-chain inputs for the fused LM-head path: hidden [B,K+1,D], lm_head [V,D].
     `plant` limits the matching drafts to those requests (the others draw
