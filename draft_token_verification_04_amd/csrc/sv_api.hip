@@ -400,7 +400,7 @@ sv_status spec_verify_tree_lmhead(const void *hidden, const void *lm_head,
 
 namespace {
 struct SampleLmWs {
-    size_t part_Rt, part_st, xlog, part_Rd, part_sd, L2, rp, rows_p, rows_q, tiles, total;
+    size_t part_Rt, part_st, row_R, row_s, xlog, part_Rd, part_sd, L2, rp, rows_p, rows_q, tiles, total;
 };
 // gd: the draft rows' streaming geometry; gr: the fp32 rows the draw reads.
 SampleLmWs sample_lm_ws_layout(int B, int K, int V, const RowGeom &gd, const RowGeom &gr) {
@@ -413,6 +413,10 @@ SampleLmWs sample_lm_ws_layout(int B, int K, int V, const RowGeom &gd, const Row
     o = align_up(o + pt * sizeof(float));
     w.part_st = o;
     o = align_up(o + pt * sizeof(double));
+    w.row_R = o;
+    o = align_up(o + rows_t * sizeof(float));
+    w.row_s = o;
+    o = align_up(o + rows_t * sizeof(double));
     w.xlog = o;
     o = align_up(o + rows_t * sizeof(float));
     w.part_Rd = o;
@@ -472,6 +476,8 @@ sv_status spec_verify_sample_lmhead(const void *hidden, const void *lm_head, con
     char *ws = static_cast<char *>(workspace);
     float *part_Rt = reinterpret_cast<float *>(ws + L.part_Rt);
     double *part_st = reinterpret_cast<double *>(ws + L.part_st);
+    float *row_R = reinterpret_cast<float *>(ws + L.row_R);
+    double *row_s = reinterpret_cast<double *>(ws + L.row_s);
     float *xlog = reinterpret_cast<float *>(ws + L.xlog);
     float *part_Rd = reinterpret_cast<float *>(ws + L.part_Rd);
     double *part_sd = reinterpret_cast<double *>(ws + L.part_sd);
@@ -486,7 +492,12 @@ sv_status spec_verify_sample_lmhead(const void *hidden, const void *lm_head, con
     hipError_t e = traced(SV_K_LMHEAD_STATS, s, [&] {
         return launch_lmhead_stats(hidden, lm_head, B, K, D, V, draft_tokens, sc, part_Rt, part_st, xlog, s);
     });
-    // 2. draft rows: the streaming statistics pass
+    // 2. the target rows' partials merged to one per row; the draft rows'
+    //    partials from the streaming statistics pass
+    if (e == hipSuccess)
+        e = traced(SV_K_MERGE_PARTS, s, [&] {
+            return launch_merge_parts(part_Rt, part_st, rows_t, lmhead_segs(V), row_R, row_s, s);
+        });
     if (e == hipSuccess && K > 0)
         e = traced(SV_K_ROWSTATS, s, [&] {
             return launch_rowstats(nullptr, draft_logits, 0, static_cast<long long>(B) * K, V, gd, dt, sc,
@@ -495,7 +506,7 @@ sv_status spec_verify_sample_lmhead(const void *hidden, const void *lm_head, con
     // 3. merge, acceptance scan, lse outputs, draw parameters
     if (e == hipSuccess)
         e = traced(SV_K_ACCEPT, s, [&] {
-            const PartRows pt{part_Rt, part_st, lmhead_segs(V)};
+            const PartRows pt{row_R, row_s, 1};
             const PartRows pd{part_Rd, part_sd, gd.segs};
             return launch_accept(nullptr, draft_logits, draft_tokens, u_accept, u_sample, B, K, V, dt, sc, pt,
                                  pd, xlog, L2, accept_len, out_tokens, lse_target, lse_draft, req_status, rp, s);
@@ -606,7 +617,7 @@ const char *sv_kernel_name(int k) {
                                             "argmax", "match", "tree", "skip_stats",
                                             "skip_argmax", "commit", "lmhead", "ngram_count",
                                             "ngram_emit", "skip_tree", "read_probe", "lmhead_stats",
-                                            "lmhead_rows", "gather_rows"};
+                                            "lmhead_rows", "gather_rows", "merge_parts"};
     return (k >= 0 && k < SV_K_COUNT) ? names[k] : "unknown";
 }
 

@@ -178,6 +178,10 @@ hipError_t launch_lmhead_stats(const void *H, const void *W, int B, int K, int D
 // Row b of rows [B][V] (fp32) = the logits of H row b (K+1) + rp[b].pos.
 hipError_t launch_lmhead_rows(const void *H, const void *W, int B, int K, int D, int V,
                               const ResidParam *rp, float *rows, hipStream_t s);
+// One (R, s) partial per row out of `segs` per row (the merge k_accept does,
+// so that merging the single partial gives the same normaliser bit for bit).
+hipError_t launch_merge_parts(const float *R, const double *S, long long rows, int segs, float *outR,
+                              double *outS, hipStream_t s);
 // Row b of out [B][V] (fp32) = draft row b K + rp[b].pos widened, for requests
 // whose draw is a residual (rp[b].mode = 1); other rows are left alone.
 hipError_t launch_gather_draft_rows(const void *drf, sv_dtype dt, int B, int K, int V,

@@ -156,6 +156,14 @@ __global__ __launch_bounds__(kLmThreads, 1) void k_lmhead(const uint4 *__restric
 #undef SV_GOFF
     static_assert(kDmaPerOperand == 4, "four DMA instructions per operand per wave");
     const int nk = D / kTK;
+    // kEpiStats: the draft token scored by row m0 + wm 64 + lane (-1 if none),
+    // fetched now so the epilogue never waits on a load
+    int xdraft = -1;
+    if constexpr (EPI == kEpiStats) {
+        const int row = m0 + wm * 64 + lane;
+        const int req = row / (o.K + 1), i = row - req * (o.K + 1);
+        if (row < M && i < o.K) xdraft = o.drafts[static_cast<long long>(req) * o.K + i];
+    }
 #define SV_ISSUE(SRC, G0, G1, G2, G3, slab, step)                                                    \
     {                                                                                                \
         const int k0 = (step) * kChunks;                                                             \
@@ -321,22 +329,20 @@ __global__ __launch_bounds__(kLmThreads, 1) void k_lmhead(const uint4 *__restric
                 double sum = static_cast<double>(pairwise_sum(x));
 #pragma unroll
                 for (int off = 1; off < 32; off <<= 1) sum += __shfl_xor(sum, off, kWave);
+                // the draft token of this row, from the lane that fetched it
+                const int xt = __shfl(xdraft, row - (m0 + wm * 64), kWave);
                 if (row < M) {
                     if (lc == 0) {
                         const long long at = static_cast<long long>(row) * o.segs + seg;
                         o.part_R[at] = m == ninf ? ninf : R;
                         o.part_s[at] = sum;
                     }
-                    // the logit at draft i, if it falls in this wave's columns
-                    const int req = row / (o.K + 1), i = row - req * (o.K + 1);
-                    if (i < o.K) {
-                        const int xt = o.drafts[static_cast<long long>(req) * o.K + i];
-                        const int rel = xt - cb;
-                        if (rel >= 0 && rel < 128 && xt < V && lc == (rel & 31)) {
-                            const int bb = rel >> 5;
-                            o.xlog[row] = bb == 0 ? acc[a][0][r] : bb == 1 ? acc[a][1][r]
-                                        : bb == 2 ? acc[a][2][r] : acc[a][3][r];
-                        }
+                    // the logit at the draft, if it falls in this wave's columns
+                    const int rel = xt - cb;
+                    if (rel >= 0 && rel < 128 && xt < V && lc == (rel & 31)) {
+                        const int bb = rel >> 5;
+                        o.xlog[row] = bb == 0 ? acc[a][0][r] : bb == 1 ? acc[a][1][r]
+                                    : bb == 2 ? acc[a][2][r] : acc[a][3][r];
                     }
                 }
             }

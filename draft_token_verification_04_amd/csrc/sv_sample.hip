@@ -181,6 +181,36 @@ __global__ __launch_bounds__(kBlock) void k_rowstats(
 
 // ---- S2/S3: merge, gather, acceptance scan ----------------------------------------
 
+// One partial per row out of `segs` per row: (Rm, sum_k s_k 2^(R_k - Rm)), Rm
+// the largest R_k, summed lane-strided and then across the wave exactly as
+// k_accept merges a row.  k_accept merging that single partial then finds the
+// same L2 = Rm + log2(sum) bit for bit.  For rows with many segments (the
+// fused projection's 128-column partials): one wave per row.
+__global__ __launch_bounds__(kBlock) void k_merge_parts(const float *__restrict__ R, const double *__restrict__ S,
+                                                        long long rows, int segs, float *__restrict__ outR,
+                                                        double *__restrict__ outS) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const long long row = static_cast<long long>(blockIdx.x) * kWavesPerBlock + (threadIdx.x >> 6);
+    if (row >= rows) return;
+    const float *pR = R + row * segs;
+    const double *pS = S + row * segs;
+    float Rm = -__builtin_huge_valf();
+    for (int sg = lane; sg < segs; sg += kWave) Rm = fmaxf(Rm, pR[sg]);
+    Rm = wave_max(Rm);
+    double acc = 0.0;
+    if (Rm != -__builtin_huge_valf()) {
+        for (int sg = lane; sg < segs; sg += kWave) {
+            const double ss = pS[sg];
+            if (ss > 0.0) acc += ss * exp2(static_cast<double>(pR[sg]) - static_cast<double>(Rm));
+        }
+    }
+    acc = wave_sum(acc);
+    if (lane == 0) {
+        outR[row] = Rm;
+        outS[row] = acc;
+    }
+}
+
 // FUSED: the target rows were never written (their partials come from the
 // LM-head projection, which also kept the logit at each draft in xlog), and
 // the row each request draws from is formed afterwards at row b of a
@@ -865,6 +895,13 @@ hipError_t resid_select_t(const void *tgt, const void *drf, int B, int K, int V,
                          g.ntiles, sc.c_hi, sc.c_lo, rp, tile_mass, out_tokens);
 }
 }  // namespace
+
+hipError_t launch_merge_parts(const float *R, const double *S, long long rows, int segs, float *outR,
+                              double *outS, hipStream_t s) {
+    const long long blocks = (rows + kWavesPerBlock - 1) / kWavesPerBlock;
+    return launch_kernel(k_merge_parts, dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0, s, R, S, rows, segs,
+                         outR, outS);
+}
 
 hipError_t launch_gather_draft_rows(const void *drf, sv_dtype dt, int B, int K, int V,
                                     const ResidParam *rp, float *out, hipStream_t s) {
