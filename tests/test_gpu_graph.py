@@ -111,3 +111,74 @@ def test_concurrent_calls_on_two_streams():
                 assert np.array_equal(_np(a)[k], wa[k]), (rep, k)
             for k in wb:
                 assert np.array_equal(_np(b)[k], wb[k]), (rep, k)
+
+
+def test_fused_projection_forms_replay_inside_a_graph():
+    # the three LM-head entry points (the sampling form makes eight launches,
+    # two of them projections) captured once and replayed on rewritten inputs
+    note("graph capture of the fused LM-head forms")
+    B, K, D, V = 16, 7, 256, 3000
+    sa = [workloads.make_sample_lmhead(B, K, D, V, exact=True, dtype="bf16", T=0.8, seed=81 + i) for i in range(2)]
+    ga = [workloads.make_greedy_lmhead(B, K, D, V, exact=True, seed=83 + i) for i in range(2)]
+    ta = [workloads.make_tree_lmhead(8, D, V, exact=True, seed=85 + i) for i in range(2)]
+    assert ta[0].N == ta[1].N
+    bf = logits_to_dev
+    W_s, W_g, W_t = bf(sa[0].lm_head), bf(ga[0].lm_head), bf(ta[0].lm_head)
+    h_s, d_s = bf(sa[0].hidden), bf(sa[0].draft)
+    x_s, ua, us = ints_to_dev(sa[0].draft_tokens), f32_to_dev(sa[0].u_accept), f32_to_dev(sa[0].u_sample)
+    h_g, x_g = bf(ga[0].hidden), ints_to_dev(ga[0].draft_tokens)
+    h_t, tok, par = bf(ta[0].hidden), ints_to_dev(ta[0].node_tokens), ints_to_dev(ta[0].parents)
+
+    def load(i):
+        # every operand of set i, the projections included
+        W_s.copy_(bf(sa[i].lm_head))
+        W_g.copy_(bf(ga[i].lm_head))
+        W_t.copy_(bf(ta[i].lm_head))
+        h_s.copy_(bf(sa[i].hidden))
+        d_s.copy_(bf(sa[i].draft))
+        x_s.copy_(ints_to_dev(sa[i].draft_tokens))
+        ua.copy_(f32_to_dev(sa[i].u_accept))
+        us.copy_(f32_to_dev(sa[i].u_sample))
+        h_g.copy_(bf(ga[i].hidden))
+        x_g.copy_(ints_to_dev(ga[i].draft_tokens))
+        h_t.copy_(bf(ta[i].hidden))
+        tok.copy_(ints_to_dev(ta[i].node_tokens))
+        par.copy_(ints_to_dev(ta[i].parents))
+
+    def step():
+        return dict(sample=sv.spec_verify_sample_lmhead(h_s, W_s, d_s, x_s, ua, us, 0.8),
+                    greedy=sv.spec_verify_greedy_lmhead(h_g, W_g, x_g),
+                    tree=sv.spec_verify_tree_lmhead(h_t, W_t, tok, par))
+
+    def eager():
+        out = step()
+        torch.cuda.synchronize()
+        return {k: _np(v) for k, v in out.items()}
+
+    want = []
+    for i in range(2):
+        load(i)
+        want.append(eager())
+    # the sets accept different numbers of drafts, so a replay that kept old results would show
+    assert any((w["sample"]["accept_len"] < K).any() for w in want)
+    assert not np.array_equal(want[0]["greedy"]["accept_len"], want[1]["greedy"]["accept_len"])
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        captured = step()
+    for rep, i in enumerate((0, 1, 0, 1)):
+        load(i)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = {k: _np(v) for k, v in captured.items()}
+        for call, outs in want[i].items():
+            for key, ref in outs.items():
+                assert np.array_equal(got[call][key], ref), (rep, call, key)
+        eager()
