@@ -548,6 +548,37 @@ def time_graph_step(torch, calls, active, args):
     return (time.perf_counter() - t0) * 1e3 / args.steps
 
 
+def time_concurrent_step(torch, calls, active, args):
+    """ms per step when each mode's call runs on a stream of its own (same
+    buffers, every stream at the default priority), the step joining them:
+    the latency-bound row-skipping passes then share the chip.  None for a
+    single-mode step."""
+    if len(active) < 2:
+        return None
+    main = torch.cuda.current_stream()
+    streams = {m: torch.cuda.Stream() for m in active}
+    fns = {}
+    for m in active:
+        c = calls.on_stream(streams[m].cuda_stream)
+        fns[m] = {"sample": c.sample, "greedy": c.greedy, "tree": c.tree}[m]
+
+    def step():
+        for m in active:
+            streams[m].wait_stream(main)
+            fns[m]()
+        for m in active:
+            main.wait_stream(streams[m])
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / args.steps
+
+
 def time_step_without_lse(torch, calls, parts, active, args, w3, w4, w5):
     """The step with the stochastic chain called without lse outputs (its
     row-skipping pass runs); None when the stochastic chain is not in the step."""
@@ -644,6 +675,7 @@ def main():
         per_kernel.setdefault(name, []).append(ms)
 
     graph_ms_per_step = time_graph_step(torch, calls, active, args)
+    concurrent_ms_per_step = time_concurrent_step(torch, calls, active, args)
 
     step_no_lse = time_step_without_lse(torch, calls, parts, active, args, w3, w4, w5)
 
@@ -864,6 +896,10 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
         "graph_ms_per_step": round(graph_ms_per_step, 5),
+        "concurrent_step": None if concurrent_ms_per_step is None else {
+            "ms_per_step": round(concurrent_ms_per_step, 5),
+            "rows_per_s": round(rows_step / (concurrent_ms_per_step * 1e-3), 1),
+            "what": "the same calls, each mode on a stream of its own, joined per step"},
         "step_without_lse": step_no_lse,
         "higher_is_better": True,
         "scaling": "weak",
