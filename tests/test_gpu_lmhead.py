@@ -146,6 +146,8 @@ SAMPLE_EXACT = [
     (33, 7, 128, 258, "f32", 1.0),      # V % 4 = 2: unaligned fp32 rows
     (9, 3, 2560, 700, "bf16", 0.9),
     (300, 1, 128, 520, "bf16", 1.0),    # several row tiles in both projection passes
+    (2, 1024, 128, 300, "bf16", 1.0),   # the longest chain the library accepts
+    (4096, 1, 128, 200, "f32", 0.8),    # a wide batch: 16 row tiles in the rows pass
 ]
 
 
