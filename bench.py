@@ -307,7 +307,7 @@ def bench_greedy_b512(sv, torch, workloads, dev, per_call, with_cold, reps):
     """spec_verify_greedy on the greedy workload at its own batch (B=512 K=7)."""
     import numpy as np
 
-    w = workloads.make_config(4)
+    w = workloads.make_workload("greedy_b512_k7_qwen3")
     lib = sv.load_library()
     t = torch.from_numpy(w.target.view(np.int16)).view(torch.bfloat16).to(dev)
     x = torch.from_numpy(w.draft_tokens).to(dev)
@@ -638,9 +638,9 @@ def main():
     dev = torch.device("cuda:0")
 
     t_gen = time.perf_counter()
-    w3 = workloads.make_config(3)
-    w4 = workloads.make_config(4, B=256)
-    w5 = workloads.make_config(5)
+    w3 = workloads.make_workload("sample_b256_k7_qwen3_t07")
+    w4 = workloads.make_workload("greedy_b512_k7_qwen3", B=256)
+    w5 = workloads.make_workload("tree_b64_n33_qwen3")
     print(f"[bench] inputs generated in {time.perf_counter() - t_gen:.1f}s", file=sys.stderr, flush=True)
     calls = Calls(sv, torch, w3, w4, w5, dev)
     parts = {"sample": calls.sample, "greedy": calls.greedy, "tree": calls.tree}

@@ -108,7 +108,7 @@ def test_commit_after_tree_verification_at_full_size():
     # the tree workload's own accepted paths (B=64, N=33) on a cache shaped like
     # a 36-layer target with 8 KV heads of 128 bf16 values (2 KB rows)
     note("commit full size")
-    w = workloads.make_config(5)
+    w = workloads.make_workload("tree_b64_n33_qwen3")
     g = sv.spec_verify_tree(torch.from_numpy(w.target.view(np.int16)).view(torch.bfloat16).to(dev()),
                             ints_to_dev(w.node_tokens), ints_to_dev(w.parents))
     o = oracle.verify_tree(w.target, w.node_tokens, w.parents)

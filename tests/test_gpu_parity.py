@@ -59,10 +59,10 @@ def test_sample_grid(case, lse):
 
 
 @pytest.mark.parametrize("lse", [True, False], ids=["full", "skip"])
-@pytest.mark.parametrize("c", [1, 2, 3])
+@pytest.mark.parametrize("c", ["sample_b1_k4_v1000_f32", "sample_b32_k7_qwen3", "sample_b256_k7_qwen3_t07"])
 def test_sample_workloads_full_size(c, lse):
     note(f"sample workload {c} lse={lse}")
-    w = workloads.make_config(c)
+    w = workloads.make_workload(c)
     o = oracle_sample(w)
     g = gpu_sample(w, lse=lse)
     ncmp, nflag, ndiff = check_sample(w, g, o)
@@ -116,8 +116,8 @@ def test_greedy_acceptance_extremes(p_match):
 
 @pytest.mark.parametrize("B", [512, 256])
 def test_greedy_workload_full_size(B):
-    note(f"greedy workload 4 B={B}")
-    w = workloads.make_config(4, B=B)
+    note(f"greedy workload B={B} K=7 V=151936")
+    w = workloads.make_workload("greedy_b512_k7_qwen3", B=B)
     o = oracle.verify_greedy(w.target, w.draft_tokens)
     g = gpu_greedy(w)
     check_exact(g, o, ("accept_len", "tokens", "status"))
@@ -165,8 +165,8 @@ def test_tree_acceptance_extremes(p_match):
 
 
 def test_tree_workload_full_size():
-    note("tree workload 5")
-    w = workloads.make_config(5)
+    note("tree workload B=64 N=33 V=151936")
+    w = workloads.make_workload("tree_b64_n33_qwen3")
     o = oracle.verify_tree(w.target, w.node_tokens, w.parents)
     check_exact(gpu_tree(w), o, ("accept_len", "path", "tokens", "status"))
 

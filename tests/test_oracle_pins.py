@@ -52,9 +52,9 @@ def test_tree_brute_force(olib):
     pins.pin_tree(olib)
 
 
-def test_round_bounds_on_workload_1(olib):
+def test_round_bounds_on_the_small_fp32_workload(olib):
     """Every round emits n+1 tokens, 0 <= n <= K, the first n being the drafts."""
-    w = workloads.make_config(1)
+    w = workloads.make_workload("sample_b1_k4_v1000_f32")
     o = oracle.verify_sample(w.target, w.draft, w.draft_tokens, w.u_accept, w.u_sample, w.T, lib=olib)
     n = o["accept_len"]
     assert np.all((n >= 0) & (n <= w.K))

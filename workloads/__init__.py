@@ -12,20 +12,21 @@ the weights nor the datasets are available, so these generators produce logits
 of the same *shape* (Qwen3 vocabulary, V=151936; draft length K=7) with simple
 seeded distributions, and draft tokens/trees with a controlled agreement rate.
 
-Workloads (``CONFIGS``)
------------------------
-1. sample, B=1, K=4, V=1000, fp32, T=1.0: Lp ~ N(0, 2^2), Lq = Lp + N(0, 0.5^2).
-2. sample, B=32, K=7, V=151936, bf16, T=1.0: Lp ~ N(0, 3^2) with +8 added at 20
-   distinct random ids per row; Lq = Lp + N(0, 1^2).
-3. sample, B=256, K=7, V=151936, bf16, T=0.7: Lp as in 2; per request a noise
-   level sigma_b ~ U(0.1, 3.0); Lq = Lp + N(0, sigma_b^2).
-4. greedy, B=512 (also run at B=256), K=7, V=151936, bf16: Lt ~ N(0, 3^2); the
-   draft for position i+1 equals argmax(row i) with probability 0.8, else a
-   uniform vocabulary id.
-5. tree, B=64, N=33, V=151936, bf16: Lt ~ N(0, 3^2); the AdaPLD-shaped tree of
-   a root, an 8-node main copy path, 12 root branches each with one successor,
-   and 0-3 extra leaves per request; a node's token equals argmax(parent row)
-   with probability 0.7, else a uniform id.
+Named workloads (``WORKLOADS``, built by ``make_workload``)
+----------------------------------------------------------
+* ``sample_b1_k4_v1000_f32``: sample, B=1, K=4, V=1000, fp32, T=1.0:
+  Lp ~ N(0, 2^2), Lq = Lp + N(0, 0.5^2).
+* ``sample_b32_k7_qwen3``: sample, B=32, K=7, V=151936, bf16, T=1.0:
+  Lp ~ N(0, 3^2) with +8 added at 20 distinct random ids per row; Lq = Lp + N(0, 1^2).
+* ``sample_b256_k7_qwen3_t07``: sample, B=256, K=7, V=151936, bf16, T=0.7: Lp as in
+  the previous one; per request a noise level sigma_b ~ U(0.1, 3.0); Lq = Lp + N(0, sigma_b^2).
+* ``greedy_b512_k7_qwen3``: greedy, B=512 (also run at B=256), K=7, V=151936, bf16:
+  Lt ~ N(0, 3^2); the draft for position i+1 equals argmax(row i) with
+  probability 0.8, else a uniform vocabulary id.
+* ``tree_b64_n33_qwen3``: tree, B=64, N=33, V=151936, bf16: Lt ~ N(0, 3^2); the
+  AdaPLD-shaped tree of a root, an 8-node main copy path, 12 root branches each
+  with one successor, and 0-3 extra leaves per request; a node's token equals
+  argmax(parent row) with probability 0.7, else a uniform id.
 
 In the sampling workloads the draft tokens are drawn from softmax(Lq/T) of the
 *stored* (rounded) draft logits with the Gumbel-max trick, so the stored q is
@@ -36,8 +37,8 @@ and ``[..., :, 1]`` the residual/bonus draws (``[b, K, 0]`` is never used).
 Logits are drawn in float32 and rounded to bfloat16 with round-to-nearest-even
 (torch's CPU conversion).  bf16 arrays are returned as ``uint16`` bit patterns.
 
-Seeding: workload ``c`` uses ``numpy.random.SeedSequence(20261202 + c)`` (or the
-caller's seed) spawned into independent streams, further split per block of 64
+Seeding: each named workload has its own ``numpy.random.SeedSequence`` seed (or
+the caller's), spawned into independent streams, further split per block of 64
 rows so the result does not depend on the thread count.
 """
 
@@ -83,12 +84,13 @@ class Workload:
         return self.B * (self.N if self.mode.startswith("tree") else self.K + 1)
 
 
-CONFIGS = {
-    1: dict(mode="sample", B=1, K=4, V=1000, dtype="f32", T=1.0),
-    2: dict(mode="sample", B=32, K=7, V=VOCAB_QWEN3, dtype="bf16", T=1.0),
-    3: dict(mode="sample", B=256, K=7, V=VOCAB_QWEN3, dtype="bf16", T=0.7),
-    4: dict(mode="greedy", B=512, K=7, V=VOCAB_QWEN3, dtype="bf16"),
-    5: dict(mode="tree", B=64, N=33, V=VOCAB_QWEN3, dtype="bf16"),
+WORKLOADS = {
+    "sample_b1_k4_v1000_f32": dict(mode="sample", B=1, K=4, V=1000, dtype="f32", T=1.0, seed=20261203),
+    "sample_b32_k7_qwen3": dict(mode="sample", B=32, K=7, V=VOCAB_QWEN3, dtype="bf16", T=1.0, seed=20261204),
+    "sample_b256_k7_qwen3_t07": dict(mode="sample", B=256, K=7, V=VOCAB_QWEN3, dtype="bf16", T=0.7,
+                                     seed=20261205),
+    "greedy_b512_k7_qwen3": dict(mode="greedy", B=512, K=7, V=VOCAB_QWEN3, dtype="bf16", seed=20261206),
+    "tree_b64_n33_qwen3": dict(mode="tree", B=64, N=33, V=VOCAB_QWEN3, dtype="bf16", seed=20261207),
 }
 
 
@@ -268,25 +270,26 @@ def make_tree(B, V, dtype="bf16", sigma=3.0, p_match=0.7, n_main=8, n_branch=12,
                     node_tokens=tok, parents=parents, meta=dict(argmax=am))
 
 
-def make_config(c: int, seed=None, B=None) -> Workload:
-    """Workload c (1..5) of ``CONFIGS``; `B` overrides the batch (e.g. 256 for workload 4)."""
-    cfg = dict(CONFIGS[c])
-    ss = np.random.SeedSequence(20261202 + c if seed is None else seed)
+def make_workload(name: str, seed=None, B=None) -> Workload:
+    """The named workload of ``WORKLOADS``; `B` overrides the batch (e.g. 256 for
+    the greedy chain)."""
+    cfg = dict(WORKLOADS[name])
+    ss = np.random.SeedSequence(cfg["seed"] if seed is None else seed)
     if B is not None:
         cfg["B"] = B
-    if c == 1:
+    if name == "sample_b1_k4_v1000_f32":
         return make_sample(cfg["B"], cfg["K"], cfg["V"], "f32", 1.0, target_sigma=2.0, spikes=0,
                            noise_sigma=0.5, seed=ss)
-    if c == 2:
+    if name == "sample_b32_k7_qwen3":
         return make_sample(cfg["B"], cfg["K"], cfg["V"], "bf16", 1.0, noise_sigma=1.0, seed=ss)
-    if c == 3:
+    if name == "sample_b256_k7_qwen3_t07":
         return make_sample(cfg["B"], cfg["K"], cfg["V"], "bf16", 0.7,
                            noise_sigma_range=(0.1, 3.0), seed=ss)
-    if c == 4:
+    if name == "greedy_b512_k7_qwen3":
         return make_greedy(cfg["B"], cfg["K"], cfg["V"], "bf16", seed=ss)
-    if c == 5:
+    if name == "tree_b64_n33_qwen3":
         return make_tree(cfg["B"], cfg["V"], "bf16", seed=ss)
-    raise ValueError(f"unknown workload {c}")
+    raise ValueError(f"unknown workload {name}")
 
 
 # ---- LM-head workloads: hidden states and a vocabulary projection ----------------
