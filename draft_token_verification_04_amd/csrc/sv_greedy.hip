@@ -322,7 +322,7 @@ template <typename E, bool ALIGNED, int U>
 __global__ __launch_bounds__(kBlock) void k_skip_argmax(const typename E::storage *__restrict__ L,
                                                         const int32_t *__restrict__ drafts, int B, int K,
                                                         int V, int nvec, int segs, uint64_t *part_k,
-                                                        int32_t *amax, SkipCtl ctl,
+                                                        int32_t *amax, SkipCtl ctl, int early,
                                                         int32_t *__restrict__ accept_len,
                                                         int32_t *__restrict__ out_tokens,
                                                         int32_t *__restrict__ status) {
@@ -334,7 +334,7 @@ __global__ __launch_bounds__(kBlock) void k_skip_argmax(const typename E::storag
     const long long rem = wave - static_cast<long long>(p) * per_pos;
     const int b = static_cast<int>(rem / segs);
     const int sg = static_cast<int>(rem - static_cast<long long>(b) * segs);
-    if (uniform(shared_load(&ctl.finished[b]))) return;
+    if (early ? skip_row_dead(ctl, b, p) : uniform(shared_load(&ctl.finished[b])) != 0) return;
 
     const long long row = static_cast<long long>(b) * (K + 1) + p;
     const int v0 = static_cast<int>((static_cast<long long>(sg) * nvec) / segs);
@@ -599,7 +599,8 @@ hipError_t skip_argmax_t(const void *L, const int32_t *drafts, int B, int K, int
     const long long blocks = (nwaves + kWavesPerBlock - 1) / kWavesPerBlock;
     return launch_kernel(k_skip_argmax<E, ALIGNED, kGSkipVecsPerLane>, dim3(static_cast<unsigned>(blocks)),
                          dim3(kBlock), 0, s, static_cast<const T *>(L), drafts, B, K, V, g.nvec, g.segs,
-                         part_k, amax, ctl, accept_len, out_tokens, status);
+                         part_k, amax, ctl, static_cast<int>(skip_early(B, 1, V, sizeof(T))), accept_len,
+                         out_tokens, status);
 }
 
 template <typename E, bool ALIGNED>

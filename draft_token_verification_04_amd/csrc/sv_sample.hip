@@ -713,7 +713,7 @@ __global__ __launch_bounds__(kBlock) void k_skip_stats(
     const typename E::storage *__restrict__ tgt, const typename E::storage *__restrict__ drf,
     const int32_t *__restrict__ drafts, const float *__restrict__ ua, const float *__restrict__ us,
     int B, int K, int V, int nvec, int segs, double c, float c_hi, float c_lo, float *part_R,
-    double *part_s, double *L2, SkipCtl ctl, int32_t *__restrict__ accept_len,
+    double *part_s, double *L2, SkipCtl ctl, int early, int32_t *__restrict__ accept_len,
     int32_t *__restrict__ out_tokens, int32_t *__restrict__ status, ResidParam *__restrict__ rp) {
     const int lane = threadIdx.x & (kWave - 1);
     const long long wave = static_cast<long long>(blockIdx.x) * kWavesPerBlock + (threadIdx.x >> 6);
@@ -725,7 +725,7 @@ __global__ __launch_bounds__(kBlock) void k_skip_stats(
     const int r = static_cast<int>(rem - static_cast<long long>(b) * 2 * segs);
     const int kind = r / segs, sg = r - kind * segs;
     if (kind == 1 && p == K) return;  // no draft row at the bonus position
-    if (uniform(shared_load(&ctl.finished[b]))) return;
+    if (early ? skip_row_dead(ctl, b, p) : uniform(shared_load(&ctl.finished[b])) != 0) return;
 
     const long long rows_t = static_cast<long long>(B) * (K + 1);
     const long long gt = static_cast<long long>(b) * (K + 1) + p;
@@ -785,7 +785,8 @@ hipError_t skip_stats_t(const void *tgt, const void *drf, const int32_t *drafts,
     return launch_kernel(k_skip_stats<E, ALIGNED, kSkipVecsPerLane>, dim3(static_cast<unsigned>(blocks)),
                          dim3(kBlock), 0, s, static_cast<const T *>(tgt), static_cast<const T *>(drf),
                          drafts, ua, us, B, K, V, g.nvec, g.segs, sc.c, sc.c_hi, sc.c_lo, part_R, part_s,
-                         L2, ctl, accept_len, out_tokens, status, rp);
+                         L2, ctl, static_cast<int>(skip_early(B, 2, V, sizeof(T))), accept_len, out_tokens, status,
+                         rp);
 }
 
 template <typename E, bool ALIGNED>

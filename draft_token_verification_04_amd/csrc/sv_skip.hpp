@@ -38,6 +38,33 @@ struct SkipCtl {
 // bytes, 8-byte aligned) and enqueues the launch that zeroes them.
 hipError_t skip_ctl_init(void *base, int B, int K, SkipCtl *ctl, hipStream_t s);
 
+// True once a draft before position p is known rejected: only the rows up to
+// a chain's first rejection are ever needed, so the rows of position p are
+// dead, whether or not the positions before that rejection are decided yet.
+// Read from the request's mask, which a decision updates at once (the request
+// is finished only later, after its outputs are written).  Uniform; p <= 31.
+//
+// Which test a wave uses (this one, or the request's finished flag) depends
+// on the bytes of one position's rows across the batch, see skip_early.
+__device__ __forceinline__ bool skip_row_dead(const SkipCtl &ctl, int b, int p) {
+    const uint64_t m = uniform(shared_load(&ctl.mask[b]));
+    return (static_cast<unsigned>(m >> 32) & ((1u << p) - 1u)) != 0;
+}
+
+// Whether the row-skipping passes test the rejection bits (skip_row_dead)
+// rather than the finished flag.  Measured on MI355X (greedy chain, K = 7, V =
+// 151936 bf16): when one position's rows across the batch fit in what the chip
+// keeps in flight (about 80 MB), retiring dead waves at once only moves the
+// dispatch front sooner onto rows whose decisions have not landed, and the
+// pass gets slower (B = 256, 78 MB: 86 us against 75 us; B = 320: 101 against
+// 93); above that the earlier test saves reads and time (B = 384, 117 MB: 108
+// against 109 us; B = 448: 116 against 122; B = 512: 124 against 130; the
+// stochastic pass at B = 256, two rows per position, 156 MB: 147 against 150).
+constexpr double kEarlySkipPositionBytes = 110e6;
+inline bool skip_early(int B, int rows_per_position, int V, size_t elem) {
+    return static_cast<double>(B) * rows_per_position * V * static_cast<double>(elem) >= kEarlySkipPositionBytes;
+}
+
 // Records position p's decision `bits` (1 << p, plus 1 << (32 + p) for a
 // rejection) in request b's mask, once this wave's shared stores are complete.
 // Returns the request's accepted length n when this wave completes the decided
