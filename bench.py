@@ -342,10 +342,10 @@ def bench_greedy_b512(sv, torch, workloads, dev, per_call, with_cold, reps):
     return entry
 
 
-def alternate_best(torch, fused, unfused, r):
-    """ms per call of two callables, each the best of three rounds of r
-    back-to-back calls.  Both run near the board's power limit, so the clock
-    drifts with the work: both are warmed up, then the rounds alternate."""
+def alternate_best(torch, r, *fns):
+    """ms per call of each callable, the best of three rounds of r back-to-back
+    calls.  They run near the board's power limit, so the clock drifts with the
+    work: all are warmed up, then the rounds alternate."""
     def timed(fn):
         torch.cuda.synchronize()
         t0 = time.perf_counter()
@@ -355,13 +355,13 @@ def alternate_best(torch, fused, unfused, r):
         return (time.perf_counter() - t0) * 1e3 / r
 
     for _ in range(10):
-        fused()
-        unfused()
-    a, b = float("inf"), float("inf")
+        for fn in fns:
+            fn()
+    best = [float("inf")] * len(fns)
     for _ in range(3):
-        a = min(a, timed(fused))
-        b = min(b, timed(unfused))
-    return a, b
+        for i, fn in enumerate(fns):
+            best[i] = min(best[i], timed(fn))
+    return best
 
 
 def kernel_means(sv, torch, fn, r, kernels):
@@ -420,10 +420,27 @@ def bench_lmhead(sv, torch, workloads, dev, reps):
         if rc:
             raise RuntimeError(f"spec_verify_greedy failed: {rc}")
 
+    # the unfused form with the fused one's results: fp32 logits written (the
+    # library GEMM's fp32 output), then spec_verify_greedy reading them
+    f_ws = torch.empty(lib.sv_greedy_workspace_bytes(B, K + 1, V, sv.SV_F32), dtype=torch.uint8, device=dev)
+    L32 = [torch.mm(Hm, Wt.t(), out_dtype=torch.float32)]
+
+    def unfused32():
+        L32[0] = torch.mm(Hm, Wt.t(), out_dtype=torch.float32)
+        rc = lib.spec_verify_greedy(P(L32[0]), P(x), B, K, V, sv.SV_F32, P(n), P(tok), None, P(f_ws),
+                                    f_ws.numel(), stream)
+        if rc:
+            raise RuntimeError(f"spec_verify_greedy (f32) failed: {rc}")
+
+    # rows whose argmax moves when the logits are rounded to bf16 (first maximum on ties)
+    torch.matmul(Hm, Wt.t(), out=Lm)
+    moved = int((Lm.float().argmax(dim=1) != L32[0].argmax(dim=1)).sum().item())
+
     r = max(10, reps // 5)
-    call_ms, unfused_ms = alternate_best(torch, fused, unfused, r)
+    call_ms, unfused_ms, unfused32_ms = alternate_best(torch, r, fused, unfused, unfused32)
     per = kernel_means(sv, torch, fused, r, ("lmhead", "match"))
     k_ms = per["lmhead"]
+    del L32
     flop = 2.0 * M * D * V
     del L, Lm
     return {
@@ -437,7 +454,11 @@ def bench_lmhead(sv, torch, workloads, dev, reps):
                      "frac": round(flop / (k_ms * 1e-3) * 1e-12 / MFMA_BF16_PEAK_TFLOPS, 4),
                      "traffic": (stored_traffic("lmhead") or {}).get("bytes_per_launch")},
         "unfused_reference": {"what": "torch.matmul (bf16 logits written to HBM) + spec_verify_greedy",
-                              "call_ms": round(unfused_ms, 5)},
+                              "call_ms": round(unfused_ms, 5),
+                              "rows_whose_argmax_moves_in_bf16": moved},
+        "unfused_fp32_reference": {"what": "torch.mm with fp32 output (fp32 logits written to HBM) + "
+                                           "spec_verify_greedy: the fused path's results",
+                                   "call_ms": round(unfused32_ms, 5)},
         "timing": f"best of 3 rounds of {r} back-to-back calls each, fused and unfused alternating",
     }
 
@@ -493,7 +514,7 @@ def bench_sample_lmhead(sv, torch, workloads, dev, reps):
             raise RuntimeError(f"spec_verify_sample failed: {rc}")
 
     r = max(10, reps // 5)
-    call_ms, unfused_ms = alternate_best(torch, fused, unfused, r)
+    call_ms, unfused_ms = alternate_best(torch, r, fused, unfused)
     fused()
     torch.cuda.synchronize()
     mean_tokens = float(n.float().mean().item()) + 1.0
