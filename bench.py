@@ -15,13 +15,22 @@ value = target rows verified per second over the whole step
 before timing starts; outputs and workspaces are preallocated.  Per-kernel
 durations come from HIP events the library records around each launch on the
 stream it launches on (sv_trace_begin/sv_trace_end): the timed steps carry
-events around the streaming kernels (row statistics, argmax, and the greedy
-chain's row-skipping argmax) only; the per-kernel breakdown of the small kernels
-comes from a separate traced pass.  The greedy chain (K = 7 <= 31) reads only
-rows 0..n_b of each request, so its algorithmic bytes are sum_b (n_b + 1) rows.
+events around the streaming kernels (row statistics, and the greedy chain's and
+the tree's row-skipping passes) only; the per-kernel breakdown of the small
+kernels comes from a separate traced pass.  The greedy chain (K = 7 <= 31)
+reads only rows 0..n_b of each request, so its algorithmic bytes are
+sum_b (n_b + 1) rows; the tree's are the rows of each request's root and
+accepted nodes.
+
+Beside the step the JSON line reports: the step replayed as one HIP graph, with
+each mode on a stream of its own, and without lse outputs; each call alone
+(back to back, and cold after a cache-evicting write); the device's read
+ceiling; the CPU oracle on the same step; and extras outside the step (the tree
+KV commit, lexical retrieval, and the fused LM-head forms beside their unfused
+counterparts).
 
 Usage: python bench.py [--gpus 1] [--steps 200] [--warmup 50] [--mode all|sample|greedy|tree]
-                       [--no-cpu-baseline]
+                       [--no-cpu-baseline] [--no-lmhead] [--cpu-threads N] [--calib-copy-mib M]
 """
 
 from __future__ import annotations
