@@ -71,6 +71,9 @@ constexpr int kLmWaves = 8;
 constexpr int kLmThreads = kLmWaves * kWave;
 constexpr int kTileRows = 32;                  // rows (and columns) of one MFMA tile
 constexpr int kDmaPerOperand = kSlab / 1024 / kLmWaves;  // 1 KB DMA instructions per wave (4)
+constexpr int kEpiRowB = 272;                  // epilogue: bytes per tile row (32 x 8 + 16 of padding)
+constexpr int kEpiWaveB = 64 * kEpiRowB + 64 * 4;  // a wave's epilogue area: 64 rows + one float per row
+static_assert(kLmWaves * kEpiWaveB <= (kHSlots + kWSlots) * kSlab, "epilogue areas fit in the ring");
 
 // H slots first, then W slots
 __shared__ __align__(1024) char ring[(kHSlots + kWSlots) * kSlab];
@@ -284,15 +287,25 @@ __global__ __launch_bounds__(kLmThreads, 1) void k_lmhead(const uint4 *__restric
         }
         return;
     }
+    // The row reductions go through LDS, free once every wave is done with
+    // the ring: each lane reduces its own four columns of each of its 32
+    // rows and leaves the partial in its wave's area (one 272-byte row per
+    // tile row: 32 partials of up to 8 bytes, padded so that 16 lanes reading
+    // 16 bytes each from 16 rows hit distinct banks); then lane j reduces row
+    // j's 32 partials with 16 independent reads.  Cross-lane shuffle chains,
+    // 32 of them per wave, would leave the CU idle for their latency instead.
+    SV_BARRIER();
     const int seg = cb / kSegCols;
     if (seg >= o.segs) return;
+    char *area = ring + w * kEpiWaveB;
+    const int row_j = m0 + wm * 64 + lane;  // the row this lane reduces
+#define SV_RL(a, r) ((a) * kTileRows + 8 * ((r) >> 2) + 4 * (lane >> 5) + ((r) & 3))
+    if constexpr (EPI == kEpiArgmax) {
+        // each lane's first maximum over its four columns, as a 64-bit key
 #pragma unroll
-    for (int a = 0; a < 2; ++a) {
+        for (int a = 0; a < 2; ++a) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int row = m0 + wm * 64 + a * kTileRows + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-            if constexpr (EPI == kEpiArgmax) {
-                // the first maximum of the row's 128 columns
+            for (int r = 0; r < 16; ++r) {
                 float best = ninf;
                 int bi = INT_MAX;
 #pragma unroll
@@ -304,50 +317,96 @@ __global__ __launch_bounds__(kLmThreads, 1) void k_lmhead(const uint4 *__restric
                         bi = col;
                     }
                 }
-                uint64_t key = argmax_key(best, bi);
-#pragma unroll
-                for (int off = 1; off < 32; off <<= 1) {
-                    const uint64_t y = __shfl_xor(key, off, kWave);
-                    key = y > key ? y : key;
-                }
-                if (lc == 0 && row < M) o.keys[static_cast<long long>(row) * o.segs + seg] = key;
-            } else {
-                // (R, s) of the row's 128 columns: each lane's four terms summed
-                // pairwise in fp32, the 32 lanes in fp64 (every lane shuffles)
-                float x[4];
-                float m = ninf;
-#pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    x[b] = cb + lc + b * kTileRows < V ? acc[a][b][r] : ninf;
-                    m = fmaxf(m, x[b]);
-                }
-#pragma unroll
-                for (int off = 1; off < 32; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, kWave));
-                const float R = m == ninf ? 0.0f : m * o.c_hi;  // all -inf: every term is 0
-#pragma unroll
-                for (int b = 0; b < 4; ++b) x[b] = fast_exp2(fmaf(x[b], o.c_lo, fmaf(x[b], o.c_hi, -R)));
-                double sum = static_cast<double>(pairwise_sum(x));
-#pragma unroll
-                for (int off = 1; off < 32; off <<= 1) sum += __shfl_xor(sum, off, kWave);
-                // the draft token of this row, from the lane that fetched it
-                const int xt = __shfl(xdraft, row - (m0 + wm * 64), kWave);
-                if (row < M) {
-                    if (lc == 0) {
-                        const long long at = static_cast<long long>(row) * o.segs + seg;
-                        o.part_R[at] = m == ninf ? ninf : R;
-                        o.part_s[at] = sum;
-                    }
-                    // the logit at the draft, if it falls in this wave's columns
-                    const int rel = xt - cb;
-                    if (rel >= 0 && rel < 128 && xt < V && lc == (rel & 31)) {
-                        const int bb = rel >> 5;
-                        o.xlog[row] = bb == 0 ? acc[a][0][r] : bb == 1 ? acc[a][1][r]
-                                    : bb == 2 ? acc[a][2][r] : acc[a][3][r];
-                    }
-                }
+                *reinterpret_cast<uint64_t *>(area + SV_RL(a, r) * kEpiRowB + lc * 8) = argmax_key(best, bi);
             }
         }
+        asm volatile("" ::: "memory");
+        const uint4 *kp = reinterpret_cast<const uint4 *>(area + lane * kEpiRowB);
+        uint64_t mk = 0;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const uint4 v = kp[q];
+            const uint64_t k0 = static_cast<uint64_t>(v.x) | (static_cast<uint64_t>(v.y) << 32);
+            const uint64_t k1 = static_cast<uint64_t>(v.z) | (static_cast<uint64_t>(v.w) << 32);
+            mk = k0 > mk ? k0 : mk;
+            mk = k1 > mk ? k1 : mk;
+        }
+        if (row_j < M) o.keys[static_cast<long long>(row_j) * o.segs + seg] = mk;
+    } else {
+        // (R, s) as the streaming pass forms them: R = fp32(max * c_hi) over
+        // the 128 columns; each lane's four terms summed pairwise in fp32,
+        // the 32 lanes in fp64 in lane order
+        float *Rrow = reinterpret_cast<float *>(area + 64 * kEpiRowB);
+        bool valid[4];  // this lane's columns inside the vocabulary
+#pragma unroll
+        for (int b = 0; b < 4; ++b) valid[b] = cb + lc + b * kTileRows < V;
+#pragma unroll
+        for (int a = 0; a < 2; ++a) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float m = ninf;
+#pragma unroll
+                for (int b = 0; b < 4; ++b) m = fmaxf(m, valid[b] ? acc[a][b][r] : ninf);
+                *reinterpret_cast<float *>(area + SV_RL(a, r) * kEpiRowB + lc * 4) = m;
+            }
+        }
+        asm volatile("" ::: "memory");
+        float mrow = ninf;
+        {
+            const float4 *fp = reinterpret_cast<const float4 *>(area + lane * kEpiRowB);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const float4 v = fp[q];
+                mrow = fmaxf(fmaxf(mrow, fmaxf(v.x, v.y)), fmaxf(v.z, v.w));
+            }
+        }
+        const float Rj = mrow == ninf ? 0.0f : mrow * o.c_hi;  // all -inf: every term is 0
+        Rrow[lane] = Rj;
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int a = 0; a < 2; ++a) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int rl = SV_RL(a, r);
+                const float R = Rrow[rl];
+                float x[4];
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const float t = fast_exp2(fmaf(acc[a][b][r], o.c_lo, fmaf(acc[a][b][r], o.c_hi, -R)));
+                    x[b] = valid[b] ? t : 0.0f;
+                }
+                *reinterpret_cast<double *>(area + rl * kEpiRowB + lc * 8) = static_cast<double>(pairwise_sum(x));
+                // the logit at this row's draft, if it falls in this wave's columns
+                const int row = m0 + wm * 64 + rl;
+                const int xt = __shfl(xdraft, rl, kWave);
+                const int rel = xt - cb;
+                if (row < M && rel >= 0 && rel < 128 && xt < V && lc == (rel & 31)) {
+                    const int bb = rel >> 5;
+                    o.xlog[row] = bb == 0 ? acc[a][0][r] : bb == 1 ? acc[a][1][r]
+                                : bb == 2 ? acc[a][2][r] : acc[a][3][r];
+                }
+                // keep the next rows' loads from being hoisted here (register pressure)
+                if ((r & 3) == 3) asm volatile("" ::: "memory");
+            }
+        }
+        asm volatile("" ::: "memory");
+        double sum = 0.0;
+        {
+            const double2 *dp = reinterpret_cast<const double2 *>(area + lane * kEpiRowB);
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const double2 v = dp[q];
+                sum += v.x;
+                sum += v.y;
+            }
+        }
+        if (row_j < M) {
+            const long long at = static_cast<long long>(row_j) * o.segs + seg;
+            o.part_R[at] = mrow == ninf ? ninf : Rj;
+            o.part_s[at] = sum;
+        }
     }
+#undef SV_RL
 }
 
 template <int EPI>
