@@ -221,9 +221,9 @@ sv_status spec_verify_tree_lmhead(const void *hidden, const void *lm_head,
  *                 spec_verify_sample.
  * The target logit of id v at a row is the fp32 sum over k of
  * hidden[k] * lm_head[v][k] (products exact, fp32 accumulation in an
- * unspecified order; both passes over a row walk D in the same order, but the
- * row can sit at a different place in the tile, so the two may round apart
- * in the last bit); everything else is spec_verify_sample on those logits.  Every target row is formed whether or
+ * unspecified order; both passes over a row walk D in the same order, with the
+ * row at a different place in the tile, and were measured on MI355X to agree
+ * bit for bit); everything else is spec_verify_sample on those logits.  Every target row is formed whether or
  * not lse outputs are requested.
  * Workspace: sv_sample_lmhead_workspace_bytes(B, K, D, V, dt) (0 for invalid
  * or unsupported sizes).
