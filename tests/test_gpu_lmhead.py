@@ -45,7 +45,8 @@ def compare(g, o, keys, reqs=None, flagged=None):
 
 
 CHAIN_EXACT = [(3, 2, 128, 77), (5, 3, 128, 1000), (7, 7, 384, 1001), (40, 7, 256, 5000), (2, 0, 128, 300),
-               (33, 7, 128, 256), (1, 1, 128, 1), (9, 3, 2560, 700)]
+               (33, 7, 128, 256), (1, 1, 128, 1), (9, 3, 2560, 700),
+               (4, 3, 8192, 1500)]  # 128 steps of D; partial sums stay below 2^10, so still exact
 
 
 @pytest.mark.parametrize("case", CHAIN_EXACT, ids=lambda c: "B{}K{}D{}V{}".format(*c))
@@ -148,6 +149,7 @@ SAMPLE_EXACT = [
     (300, 1, 128, 520, "bf16", 1.0),    # several row tiles in both projection passes
     (2, 1024, 128, 300, "bf16", 1.0),   # the longest chain the library accepts
     (4096, 1, 128, 200, "f32", 0.8),    # a wide batch: 16 row tiles in the rows pass
+    (6, 3, 8192, 1500, "bf16", 0.9),    # 128 steps of D
 ]
 
 
