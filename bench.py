@@ -347,6 +347,7 @@ def bench_greedy_b512(sv, torch, workloads, dev, per_call, with_cold, reps):
              "dense_bytes": rows * R, "gbps": round(nbytes / (ms * 1e-3) / 1e9, 1),
              "mean_tokens_per_round": round(float(n_b.mean() + 1), 4)}
     with_cold(entry, call, nbytes, rows)
+    entry["cold_dense_gbps"] = round(rows * R / (entry["cold_ms"]["median"] * 1e-3) / 1e9, 1)
     del t
     return entry
 
@@ -778,10 +779,12 @@ def main():
         modes[m]["mean_tokens_per_round"] = round(float(emitted[m].mean()), 4)
         modes[m]["requests_per_s"] = round(batch[m] / kt, 1)
         modes[m]["tokens_per_s"] = round(float(emitted[m].sum()) / kt, 1)
-    if "greedy" in modes:
-        modes["greedy"]["dense_bytes"] = w4.B * (w4.K + 1) * R
-    if "tree" in modes:
-        modes["tree"]["dense_bytes"] = w5.B * w5.N * R
+    # the workloads' byte formula counts every row (B(K+1) R, B N R); the row-skipping passes
+    # read fewer, so beside their own bytes the rate at that formula is reported too
+    for m, dense in (("greedy", w4.B * (w4.K + 1) * R), ("tree", w5.B * w5.N * R)):
+        if m in modes:
+            modes[m]["dense_bytes"] = dense
+            modes[m]["dense_gbps"] = round(dense / (modes[m]["kernel_ms"] * 1e-3) / 1e9, 1)
 
     # each call on its own, back to back (launch gaps included)
     def per_call(fn, reps):
@@ -845,6 +848,9 @@ def main():
                 {"ms": round(ms, 5), "rows_per_s": round(rows_mode[name] / (ms * 1e-3), 1),
                  "bytes_read": bytes_mode[name], "gbps": round(bytes_mode[name] / (ms * 1e-3) / 1e9, 1)},
                 fn, bytes_mode[name], rows_mode[name])
+            dense = modes[name]["dense_bytes"]
+            calls_alone[name]["cold_dense_gbps"] = round(
+                dense / (calls_alone[name]["cold_ms"]["median"] * 1e-3) / 1e9, 1)
     if "greedy" in active:
         calls_alone["greedy_b512"] = bench_greedy_b512(sv, torch, workloads, dev, per_call, with_cold, reps)
     del evict
@@ -915,7 +921,8 @@ def main():
                          f"{secs:.2f}s wall each",
                "single_thread": {"value": round(rows_step / secs1, 1), "unit": "rows/s",
                                  "sample": f"the same step once, {secs1:.2f}s wall"},
-               "cpu_model": cpu_model()}
+               "cpu_model": cpu_model(),
+               "gpu_speedup": round(value / (rows_step / secs), 1)}
 
     out = {
         "metric": METRIC,
