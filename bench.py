@@ -352,6 +352,41 @@ def bench_greedy_b512(sv, torch, workloads, dev, per_call, with_cold, reps):
     return entry
 
 
+def bench_vocab_shard(sv, torch, workloads, dev, per_call, with_cold, reps):
+    """The step's three calls at one vocabulary shard's row length, V/8 = 18,992 (the
+    kernels one of eight GPUs would run if the LM head were split over the
+    vocabulary; the cross-GPU exchange of row statistics is not included)."""
+    import numpy as np
+
+    Vs = workloads.VOCAB_QWEN3 // 8
+    w3 = workloads.make_sample(256, 7, Vs, "bf16", 0.7, noise_sigma_range=(0.1, 3.0), seed=20261211)
+    w4 = workloads.make_greedy(256, 7, Vs, "bf16", seed=20261212)
+    w5 = workloads.make_tree(64, Vs, "bf16", seed=20261213)
+    c = Calls(sv, torch, w3, w4, w5, dev)
+    R = Vs * 2
+    c.sample()
+    c.greedy()
+    torch.cuda.synchronize()
+    n3, n4 = c.s_n.cpu().numpy(), c.g_n.cpu().numpy()
+    out = {"workload": f"V = {Vs} (Qwen3 vocabulary / 8), otherwise as the step: stochastic chain "
+                       "B=256 K=7 T=0.7 (lse on), greedy chain B=256 K=7, greedy tree B=64 N=33"}
+    for name, fn, rows, nbytes, dense in (
+            ("sample", c.sample, 256 * 8, (256 * 15 + int(np.where(n3 < 7, 2, 1).sum())) * R, None),
+            ("greedy", c.greedy, 256 * 8, int((n4 + 1).sum()) * R, 256 * 8 * R),
+            ("tree", c.tree, 64 * 33, None, 64 * 33 * R)):
+        ms = per_call(fn, reps)
+        e = {"ms": round(ms, 5), "rows_per_s": round(rows / (ms * 1e-3), 1)}
+        with_cold(e, fn, nbytes or dense, rows)
+        if nbytes is None:  # the tree's own minimum needs its argmaxes: report the formula only
+            e.pop("cold_gbps")
+        else:
+            e["bytes_read"] = nbytes
+        if dense is not None:
+            e["cold_dense_gbps"] = round(dense / (e["cold_ms"]["median"] * 1e-3) / 1e9, 1)
+        out[name] = e
+    return out
+
+
 def alternate_best(torch, r, *fns):
     """ms per call of each callable, the best of three rounds of r back-to-back
     calls.  They run near the board's power limit, so the clock drifts with the
@@ -853,6 +888,10 @@ def main():
                 dense / (calls_alone[name]["cold_ms"]["median"] * 1e-3) / 1e9, 1)
     if "greedy" in active:
         calls_alone["greedy_b512"] = bench_greedy_b512(sv, torch, workloads, dev, per_call, with_cold, reps)
+    # one GPU's share of a vocabulary-parallel LM head: the same calls on rows of V/8
+    vocab_shard = None
+    if args.mode == "all":
+        vocab_shard = bench_vocab_shard(sv, torch, workloads, dev, per_call, with_cold, reps)
     del evict
 
     # the read rate this device reaches: a read-only stream with the same loads
@@ -933,6 +972,7 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
         "graph_ms_per_step": round(graph_ms_per_step, 5),
+        "vocab_shard": vocab_shard,
         "concurrent_step": None if concurrent_ms_per_step is None else {
             "ms_per_step": round(concurrent_ms_per_step, 5),
             "rows_per_s": round(rows_step / (concurrent_ms_per_step * 1e-3), 1),
