@@ -32,8 +32,11 @@ workload recipe every partial sum is representable in fp32, so no row is
 flagged (``exact=True`` skips the bound).
 
 Pins: tests/test_lmhead_oracle.py (integer arithmetic on small cases, the
-bound against fp32 sums in several orders, the C oracle on exactly
-representable logits, brute-force tree walks).
+bound against fp32 sums in several orders and against a sum built to lose
+about half of it, the C oracle on exactly representable logits, brute-force
+tree walks, sampling on the projection against sampling on integer-exact
+logits).  tests/test_lmhead_oracle_mutants.py plants a mistake in one
+function at a time and checks that a pin fails.
 """
 
 from __future__ import annotations

@@ -70,6 +70,26 @@ def test_bound_holds_for_fp32_sums_in_any_order(order):
     assert E.max() < 1e-2 * np.abs(L).max()
 
 
+def test_bound_is_nearly_attained_by_an_adversarial_sum():
+    # products 1, then D-1 products just under 2^-25: each is below half an ulp of
+    # the running fp32 sum (1), so a forward fp32 sum stays at exactly 1 and loses
+    # (D-1) * 2^-25 (1 - 2^-8), about half the bound gamma_{D-1} * sum |h w|
+    D = 4096
+    h = np.full(D, 2.0 ** -13, np.float32)
+    w = np.full(D, 2.0 ** -12 * (1 - 2.0 ** -8), np.float32)
+    h[0] = w[0] = 1.0
+    Hb = workloads.to_bf16_bits(h[None, :])
+    Wb = workloads.to_bf16_bits(w[None, :])
+    assert np.array_equal(workloads.bf16_bits_to_f32(Hb)[0], h)  # exactly representable
+    assert np.array_equal(workloads.bf16_bits_to_f32(Wb)[0], w)
+    L = lmhead.logits(Hb, Wb)[0, 0]
+    E = lmhead.accumulation_bound(Hb, Wb)[0, 0]
+    got = float(_fp32_sums(h[None, :], w[None, :], "forward")[0, 0])
+    assert got == 1.0
+    assert abs(got - L) <= E
+    assert abs(got - L) >= 0.45 * E
+
+
 def test_certain_rows_survive_every_admissible_perturbation():
     rng = np.random.default_rng(3)
     L = rng.normal(size=(400, 50)).round(2)  # plenty of near ties
