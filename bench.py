@@ -563,7 +563,7 @@ def bench_sample_lmhead(sv, torch, workloads, dev, reps):
     fused()
     torch.cuda.synchronize()
     mean_tokens = float(n.float().mean().item()) + 1.0
-    kern = ("lmhead_stats", "merge_parts", "rowstats", "accept", "lmhead_rows", "gather_rows", "resid_mass",
+    kern = ("lmhead_stats", "merge_parts", "rowstats", "accept", "lmhead_rows", "resid_mass",
             "resid_select")
     per = kernel_means(sv, torch, fused, r, kern)
     k_ms = per["lmhead_stats"]

@@ -32,8 +32,7 @@ SV_F32, SV_BF16 = 0, 1
 SV_MAX_TREE_NODES = 2048
 KERNELS = ("rowstats", "accept", "resid_mass", "resid_select", "argmax", "match", "tree",
            "skip_stats", "skip_argmax", "commit", "lmhead", "ngram_count", "ngram_emit",
-           "skip_tree", "read_probe", "lmhead_stats", "lmhead_rows", "gather_rows",
-           "merge_parts")
+           "skip_tree", "read_probe", "lmhead_stats", "lmhead_rows", "merge_parts")
 
 EXPORTS = ("sv_sample_workspace_bytes", "sv_greedy_workspace_bytes", "spec_verify_sample",
            "spec_verify_greedy", "spec_verify_tree", "spec_commit_tree_kv", "sv_status_string",

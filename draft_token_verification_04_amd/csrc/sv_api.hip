@@ -234,11 +234,11 @@ sv_status spec_verify_sample(const void *target_logits, const void *draft_logits
     }
     if (e == hipSuccess)
         e = traced(SV_K_RESID_MASS, s, [&] {
-            return launch_resid_mass(target_logits, draft_logits, B, V, g, dt, sc, rp, tiles, s);
+            return launch_resid_mass(target_logits, draft_logits, B, V, g, dt, dt, sc, rp, tiles, s);
         });
     if (e == hipSuccess)
         e = traced(SV_K_RESID_SELECT, s, [&] {
-            return launch_resid_select(target_logits, draft_logits, B, K, V, g, dt, sc, rp, tiles,
+            return launch_resid_select(target_logits, draft_logits, B, K, V, g, dt, dt, sc, rp, tiles,
                                        out_tokens, s);
         });
     return e == hipSuccess ? SV_OK : SV_ERR_HIP;
@@ -400,7 +400,7 @@ sv_status spec_verify_tree_lmhead(const void *hidden, const void *lm_head,
 
 namespace {
 struct SampleLmWs {
-    size_t part_Rt, part_st, row_R, row_s, xlog, part_Rd, part_sd, L2, rp, rows_p, rows_q, tiles, total;
+    size_t part_Rt, part_st, row_R, row_s, xlog, part_Rd, part_sd, L2, rp, rows_p, tiles, total;
 };
 // gd: the draft rows' streaming geometry; gr: the fp32 rows the draw reads.
 SampleLmWs sample_lm_ws_layout(int B, int K, int V, const RowGeom &gd, const RowGeom &gr) {
@@ -429,8 +429,6 @@ SampleLmWs sample_lm_ws_layout(int B, int K, int V, const RowGeom &gd, const Row
     o = align_up(o + static_cast<size_t>(B) * sizeof(ResidParam));
     w.rows_p = o;
     o = align_up(o + static_cast<size_t>(B) * row_bytes);
-    w.rows_q = o;
-    o = align_up(o + (K > 0 ? static_cast<size_t>(B) * row_bytes : 0));
     w.tiles = o;
     o = align_up(o + static_cast<size_t>(B) * static_cast<size_t>(gr.ntiles) * sizeof(double));
     w.total = o;
@@ -484,7 +482,6 @@ sv_status spec_verify_sample_lmhead(const void *hidden, const void *lm_head, con
     double *L2 = reinterpret_cast<double *>(ws + L.L2);
     ResidParam *rp = reinterpret_cast<ResidParam *>(ws + L.rp);
     float *rows_p = reinterpret_cast<float *>(ws + L.rows_p);
-    float *rows_q = reinterpret_cast<float *>(ws + L.rows_q);
     double *tiles = reinterpret_cast<double *>(ws + L.tiles);
     hipStream_t s = static_cast<hipStream_t>(stream);
 
@@ -511,22 +508,19 @@ sv_status spec_verify_sample_lmhead(const void *hidden, const void *lm_head, con
             return launch_accept(nullptr, draft_logits, draft_tokens, u_accept, u_sample, B, K, V, dt, sc, pt,
                                  pd, xlog, L2, accept_len, out_tokens, lse_target, lse_draft, req_status, rp, s);
         });
-    // 4. the row each request draws from, formed again and written in fp32,
-    //    with its draft row beside it
+    // 4. the row each request draws from, formed again and written in fp32
     if (e == hipSuccess)
         e = traced(SV_K_LMHEAD_ROWS, s,
                    [&] { return launch_lmhead_rows(hidden, lm_head, B, K, D, V, rp, rows_p, s); });
-    if (e == hipSuccess && K > 0)
-        e = traced(SV_K_GATHER_ROWS, s,
-                   [&] { return launch_gather_draft_rows(draft_logits, dt, B, K, V, rp, rows_q, s); });
-    // 5. the draw
+    // 5. the draw, beside the draft row read where it lies
     if (e == hipSuccess)
         e = traced(SV_K_RESID_MASS, s, [&] {
-            return launch_resid_mass(rows_p, rows_q, B, V, gr, SV_F32, sc, rp, tiles, s);
+            return launch_resid_mass(rows_p, draft_logits, B, V, gr, SV_F32, dt, sc, rp, tiles, s);
         });
     if (e == hipSuccess)
         e = traced(SV_K_RESID_SELECT, s, [&] {
-            return launch_resid_select(rows_p, rows_q, B, K, V, gr, SV_F32, sc, rp, tiles, out_tokens, s);
+            return launch_resid_select(rows_p, draft_logits, B, K, V, gr, SV_F32, dt, sc, rp, tiles, out_tokens,
+                                       s);
         });
     return e == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
@@ -617,7 +611,7 @@ const char *sv_kernel_name(int k) {
                                             "argmax", "match", "tree", "skip_stats",
                                             "skip_argmax", "commit", "lmhead", "ngram_count",
                                             "ngram_emit", "skip_tree", "read_probe", "lmhead_stats",
-                                            "lmhead_rows", "gather_rows", "merge_parts"};
+                                            "lmhead_rows", "merge_parts"};
     return (k >= 0 && k < SV_K_COUNT) ? names[k] : "unknown";
 }
 

@@ -116,6 +116,57 @@ struct Staged<E, false> {
     }
 };
 
+// Four consecutive elements of a row (vector j holds elements 4j..4j+3),
+// widened to fp32: a row of type E read in step with an fp32 row.  For fp32 it
+// is Staged; for bf16 the aligned form is one 8-byte load (row 8-byte aligned,
+// V % 4 == 0).
+template <typename E, bool ALIGNED>
+struct Staged4 : Staged<E, ALIGNED> {
+    static_assert(E::kPerVec == 4, "fp32 rows are Staged as they are");
+};
+
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+template <>
+struct Staged4<BF16, true> {
+    uint2 w;
+    __device__ __forceinline__ void load(const uint16_t *__restrict__ row, int, int j) {
+#if SV_NT_LOADS
+        const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(row) + j);
+        w = make_uint2(v.x, v.y);
+#else
+        w = reinterpret_cast<const uint2 *>(row)[j];
+#endif
+    }
+    __device__ __forceinline__ void set_neg_inf() { w = make_uint2(BF16::kNegInfWord, BF16::kNegInfWord); }
+    __device__ __forceinline__ void get(float (&x)[4]) const {
+        x[0] = __uint_as_float(w.x << 16);
+        x[1] = __uint_as_float(w.x & 0xffff0000u);
+        x[2] = __uint_as_float(w.y << 16);
+        x[3] = __uint_as_float(w.y & 0xffff0000u);
+    }
+};
+
+template <>
+struct Staged4<BF16, false> {
+    float v[4];
+    __device__ __forceinline__ void load(const uint16_t *__restrict__ row, int V, int j) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int idx = j * 4 + e;
+            v[e] = idx < V ? bf16_to_f32(row[idx]) : -__builtin_huge_valf();
+        }
+    }
+    __device__ __forceinline__ void set_neg_inf() {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = -__builtin_huge_valf();
+    }
+    __device__ __forceinline__ void get(float (&x)[4]) const {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = v[e];
+    }
+};
+
 // Fixed-order pairwise sum of a small array.
 template <int P>
 __device__ __forceinline__ float pairwise_sum(float (&a)[P]) {

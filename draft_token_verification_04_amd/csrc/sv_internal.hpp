@@ -149,11 +149,13 @@ hipError_t launch_skip(const void *tgt, const void *drf, const int32_t *drafts, 
                        const Scale &sc, float *part_R, double *part_s, double *L2, void *ctl_base,
                        int32_t *accept_len, int32_t *out_tokens, int32_t *status, ResidParam *rp,
                        hipStream_t s);
+// dt: the target rows' type (g is their geometry); dq: the draft rows' type,
+// equal to dt or bf16 beside fp32 target rows.
 hipError_t launch_resid_mass(const void *tgt, const void *drf, int B, int V, const RowGeom &g,
-                             sv_dtype dt, const Scale &sc, const ResidParam *rp, double *tile_mass,
-                             hipStream_t s);
+                             sv_dtype dt, sv_dtype dq, const Scale &sc, const ResidParam *rp,
+                             double *tile_mass, hipStream_t s);
 hipError_t launch_resid_select(const void *tgt, const void *drf, int B, int K, int V,
-                               const RowGeom &g, sv_dtype dt, const Scale &sc,
+                               const RowGeom &g, sv_dtype dt, sv_dtype dq, const Scale &sc,
                                const ResidParam *rp, double *tile_mass, int32_t *out_tokens,
                                hipStream_t s);
 hipError_t launch_argmax(const void *L, long long rows, int V, const RowGeom &g, sv_dtype dt,
@@ -182,10 +184,6 @@ hipError_t launch_lmhead_rows(const void *H, const void *W, int B, int K, int D,
 // so that merging the single partial gives the same normaliser bit for bit).
 hipError_t launch_merge_parts(const float *R, const double *S, long long rows, int segs, float *outR,
                               double *outS, hipStream_t s);
-// Row b of out [B][V] (fp32) = draft row b K + rp[b].pos widened, for requests
-// whose draw is a residual (rp[b].mode = 1); other rows are left alone.
-hipError_t launch_gather_draft_rows(const void *drf, sv_dtype dt, int B, int K, int V,
-                                    const ResidParam *rp, float *out, hipStream_t s);
 hipError_t launch_commit(const void *src, void *dst, int G, int B, int S, int row_bytes,
                          const int32_t *tree_base, const int32_t *commit_base,
                          const int32_t *accept_len, const int32_t *path_nodes, int N,

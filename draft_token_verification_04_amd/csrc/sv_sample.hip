@@ -33,6 +33,7 @@
 // elements, the row merges, the acceptance ratios and the running masses of the
 // inverse CDF are fp64.
 #include <algorithm>
+#include <type_traits>
 
 #include "sv_device.hpp"
 #include "sv_internal.hpp"
@@ -214,7 +215,7 @@ __global__ __launch_bounds__(kBlock) void k_merge_parts(const float *__restrict_
 // FUSED: the target rows were never written (their partials come from the
 // LM-head projection, which also kept the logit at each draft in xlog), and
 // the row each request draws from is formed afterwards at row b of a
-// per-request buffer, as is its draft row.
+// per-request buffer; its draft row is read where it lies.
 template <typename E, bool FUSED>
 __global__ __launch_bounds__(kBlock) void k_accept(
     const typename E::storage *__restrict__ tgt, const typename E::storage *__restrict__ drf,
@@ -374,7 +375,7 @@ __global__ __launch_bounds__(kBlock) void k_accept(
         P.L2p = sL2[n];
         if (n < K) {
             P.mode = 1;
-            P.row_q = FUSED ? b : static_cast<long long>(b) * K + n;
+            P.row_q = static_cast<long long>(b) * K + n;
             P.L2q = sL2[K + 1 + n];
         } else {
             P.mode = 0;
@@ -430,12 +431,18 @@ __device__ __forceinline__ double lane_total(const float (&d)[P]) {
     return static_cast<double>(pairwise_sum(t));
 }
 
+// The draft row's stager: the target row's own type, or a bf16 draft row read
+// four elements at a time beside fp32 target rows.
+template <typename E, typename EQ, bool ALIGNED>
+using DraftStaged =
+    typename std::conditional<std::is_same<E, EQ>::value, Staged<E, ALIGNED>, Staged4<EQ, ALIGNED>>::type;
+
 // Residual (or bonus) mass of each 64-vector tile of the row each request
 // draws from.  A wave owns `tpw` consecutive tiles of one request and walks
 // them in groups of G, loading the next group before it sums the current one.
-template <typename E, bool ALIGNED, int G>
+template <typename E, typename EQ, bool ALIGNED, int G>
 __global__ __launch_bounds__(kBlock) void k_resid_mass(
-    const typename E::storage *__restrict__ tgt, const typename E::storage *__restrict__ drf,
+    const typename E::storage *__restrict__ tgt, const typename EQ::storage *__restrict__ drf,
     int B, int V, int nvec, int ntiles, int wpr, int tpw, float c_hi, float c_lo,
     const ResidParam *__restrict__ rp, double *__restrict__ tile_mass) {
     constexpr int P = E::kPerVec;
@@ -447,12 +454,13 @@ __global__ __launch_bounds__(kBlock) void k_resid_mass(
     const ResidParam Pm = rp[b];
     const Draw D = make_draw(Pm, c_hi, c_lo, Pm.mode);
     const typename E::storage *prow = tgt + Pm.row_p * static_cast<long long>(V);
-    const typename E::storage *qrow = D.mode ? drf + Pm.row_q * static_cast<long long>(V) : nullptr;
+    const typename EQ::storage *qrow = D.mode ? drf + Pm.row_q * static_cast<long long>(V) : nullptr;
     const int t_begin = w * tpw;
     const int t_end = min(ntiles, t_begin + tpw);
     double *out = tile_mass + static_cast<long long>(b) * ntiles;
 
-    auto load = [&](Staged<E, ALIGNED>(&sp)[G], Staged<E, ALIGNED>(&sq)[G], int t0) {
+    using QS = DraftStaged<E, EQ, ALIGNED>;
+    auto load = [&](Staged<E, ALIGNED>(&sp)[G], QS(&sq)[G], int t0) {
 #pragma unroll
         for (int k = 0; k < G; ++k) {
             const int j = (t0 + k) * kWave + lane;
@@ -468,7 +476,7 @@ __global__ __launch_bounds__(kBlock) void k_resid_mass(
             }
         }
     };
-    auto sum = [&](const Staged<E, ALIGNED>(&sp)[G], const Staged<E, ALIGNED>(&sq)[G], int t0) {
+    auto sum = [&](const Staged<E, ALIGNED>(&sp)[G], const QS(&sq)[G], int t0) {
 #pragma unroll
         for (int k = 0; k < G; ++k) {
             if (t0 + k < t_end) {  // uniform across the wave
@@ -481,7 +489,8 @@ __global__ __launch_bounds__(kBlock) void k_resid_mass(
             }
         }
     };
-    Staged<E, ALIGNED> ap[G], aq[G], bp[G], bq[G];
+    Staged<E, ALIGNED> ap[G], bp[G];
+    QS aq[G], bq[G];
     load(ap, aq, t_begin);
     for (int t0 = t_begin; t0 < t_end; t0 += 2 * G) {
         load(bp, bq, t0 + G);
@@ -491,9 +500,9 @@ __global__ __launch_bounds__(kBlock) void k_resid_mass(
     }
 }
 
-template <typename E, bool ALIGNED>
+template <typename E, typename EQ, bool ALIGNED>
 __global__ __launch_bounds__(kWave) void k_resid_select(
-    const typename E::storage *__restrict__ tgt, const typename E::storage *__restrict__ drf,
+    const typename E::storage *__restrict__ tgt, const typename EQ::storage *__restrict__ drf,
     int B, int K, int V, int nvec, int ntiles, float c_hi, float c_lo,
     const ResidParam *__restrict__ rp, double *__restrict__ tile_mass, int32_t *__restrict__ out_tokens) {
     constexpr int P = E::kPerVec;
@@ -502,7 +511,7 @@ __global__ __launch_bounds__(kWave) void k_resid_select(
     const ResidParam Pm = rp[b];
     Draw D = make_draw(Pm, c_hi, c_lo, Pm.mode);
     const typename E::storage *prow = tgt + Pm.row_p * static_cast<long long>(V);
-    const typename E::storage *qrow = D.mode ? drf + Pm.row_q * static_cast<long long>(V) : nullptr;
+    const typename EQ::storage *qrow = D.mode ? drf + Pm.row_q * static_cast<long long>(V) : nullptr;
     double *tm = tile_mass + static_cast<long long>(b) * ntiles;
     int32_t *dst = out_tokens + static_cast<long long>(b) * (K + 1) + Pm.pos;
 
@@ -584,9 +593,11 @@ __global__ __launch_bounds__(kWave) void k_resid_select(
     float xp[P], xq[P], d[P];
     if (j < nvec) {
         load_vec<E, ALIGNED>(prow, V, j, xp);
-        if (D.mode)
-            load_vec<E, ALIGNED>(qrow, V, j, xq);
-        else
+        if (D.mode) {
+            DraftStaged<E, EQ, ALIGNED> q;
+            q.load(qrow, V, j);
+            q.get(xq);
+        } else
 #pragma unroll
             for (int e = 0; e < P; ++e) xq[e] = -__builtin_huge_valf();
     } else {
@@ -617,35 +628,6 @@ __global__ __launch_bounds__(kWave) void k_resid_select(
         }
         if (pick < 0) pick = last;
         *dst = j * P + pick;
-    }
-}
-
-// Draft row b K + pos of each request that draws a residual, widened to fp32
-// into row b of out (the fused LM-head form, whose draw reads fp32 rows).  A
-// thread moves one 16-byte input vector.
-template <typename E, bool ALIGNED>
-__global__ __launch_bounds__(kBlock) void k_gather_draft_rows(const typename E::storage *__restrict__ drf,
-                                                              int K, int V, int nvec,
-                                                              const ResidParam *__restrict__ rp,
-                                                              float *__restrict__ out) {
-    constexpr int P = E::kPerVec;
-    const int b = blockIdx.y;
-    const int mode = rp[b].mode, pos = rp[b].pos;
-    if (mode != 1) return;
-    const typename E::storage *src = drf + (static_cast<long long>(b) * K + pos) * V;
-    float *dst = out + static_cast<long long>(b) * V;
-    for (int j = blockIdx.x * kBlock + threadIdx.x; j < nvec; j += gridDim.x * kBlock) {
-        float x[P];
-        load_vec<E, ALIGNED>(src, V, j, x);
-        if constexpr (ALIGNED) {
-#pragma unroll
-            for (int e = 0; e < P; e += 4)
-                *reinterpret_cast<float4 *>(dst + j * P + e) = make_float4(x[e], x[e + 1], x[e + 2], x[e + 3]);
-        } else {
-#pragma unroll
-            for (int e = 0; e < P; ++e)
-                if (j * P + e < V) dst[j * P + e] = x[e];
-        }
     }
 }
 
@@ -874,26 +856,42 @@ hipError_t launch_accept(const void *tgt, const void *drf, const int32_t *drafts
 }
 
 namespace {
-template <typename E, bool ALIGNED>
+template <typename E, typename EQ, bool ALIGNED>
 hipError_t resid_mass_t(const void *tgt, const void *drf, int B, int V, const RowGeom &g,
                         const Scale &sc, const ResidParam *rp, double *tile_mass, hipStream_t s) {
-    using T = typename E::storage;
     const int tpw = resid_tiles_per_wave(B, g.ntiles);
     const int wpr = (g.ntiles + tpw - 1) / tpw;
     const long long nwaves = static_cast<long long>(B) * wpr;
     const long long blocks = (nwaves + kWavesPerBlock - 1) / kWavesPerBlock;
-    return launch_kernel(k_resid_mass<E, ALIGNED, kResidGroup>, dim3(static_cast<unsigned>(blocks)),
-                         dim3(kBlock), 0, s, static_cast<const T *>(tgt), static_cast<const T *>(drf),
-                         B, V, g.nvec, g.ntiles, wpr, tpw, sc.c_hi, sc.c_lo, rp, tile_mass);
+    return launch_kernel(k_resid_mass<E, EQ, ALIGNED, kResidGroup>, dim3(static_cast<unsigned>(blocks)),
+                         dim3(kBlock), 0, s, static_cast<const typename E::storage *>(tgt),
+                         static_cast<const typename EQ::storage *>(drf), B, V, g.nvec, g.ntiles, wpr, tpw,
+                         sc.c_hi, sc.c_lo, rp, tile_mass);
 }
-template <typename E, bool ALIGNED>
+template <typename E, typename EQ, bool ALIGNED>
 hipError_t resid_select_t(const void *tgt, const void *drf, int B, int K, int V, const RowGeom &g,
                           const Scale &sc, const ResidParam *rp, double *tile_mass,
                           int32_t *out_tokens, hipStream_t s) {
-    using T = typename E::storage;
-    return launch_kernel(k_resid_select<E, ALIGNED>, dim3(B), dim3(kWave), 0, s,
-                         static_cast<const T *>(tgt), static_cast<const T *>(drf), B, K, V, g.nvec,
-                         g.ntiles, sc.c_hi, sc.c_lo, rp, tile_mass, out_tokens);
+    return launch_kernel(k_resid_select<E, EQ, ALIGNED>, dim3(B), dim3(kWave), 0, s,
+                         static_cast<const typename E::storage *>(tgt),
+                         static_cast<const typename EQ::storage *>(drf), B, K, V, g.nvec, g.ntiles, sc.c_hi,
+                         sc.c_lo, rp, tile_mass, out_tokens);
+}
+
+// The three pairings the draw reads: both rows bf16, both fp32, or fp32
+// target rows beside bf16 draft rows (the fused LM-head form).  `aligned`
+// extends g.aligned (the target rows) to the draft rows' own vector size.
+template <typename F>
+hipError_t resid_dispatch(sv_dtype dt, sv_dtype dq, const RowGeom &g, const void *drf, F &&f) {
+    if (dt == SV_BF16 && dq == SV_BF16)
+        return g.aligned ? f(BF16{}, BF16{}, std::true_type{}) : f(BF16{}, BF16{}, std::false_type{});
+    if (dt == SV_F32 && dq == SV_F32)
+        return g.aligned ? f(F32{}, F32{}, std::true_type{}) : f(F32{}, F32{}, std::false_type{});
+    if (dt == SV_F32 && dq == SV_BF16) {
+        const bool al = g.aligned && (reinterpret_cast<uintptr_t>(drf) & 7u) == 0;
+        return al ? f(F32{}, BF16{}, std::true_type{}) : f(F32{}, BF16{}, std::false_type{});
+    }
+    return hipErrorInvalidValue;
 }
 }  // namespace
 
@@ -904,40 +902,23 @@ hipError_t launch_merge_parts(const float *R, const double *S, long long rows, i
                          outR, outS);
 }
 
-hipError_t launch_gather_draft_rows(const void *drf, sv_dtype dt, int B, int K, int V,
-                                    const ResidParam *rp, float *out, hipStream_t s) {
-    // aligned: 16-byte input vectors, and 16-byte aligned fp32 output rows
-    const bool al = (reinterpret_cast<uintptr_t>(drf) & 15u) == 0 && (reinterpret_cast<uintptr_t>(out) & 15u) == 0 &&
-                    V % (dt == SV_BF16 ? 8 : 4) == 0;
-    const int P = dt == SV_BF16 ? 8 : 4;
-    const int nvec = (V + P - 1) / P;
-    const dim3 grid(static_cast<unsigned>(std::min(64, (nvec + kBlock - 1) / kBlock)), static_cast<unsigned>(B));
-#define SV_GD(E, A) launch_kernel(k_gather_draft_rows<E, A>, grid, dim3(kBlock), 0, s, \
-                                  static_cast<const typename E::storage *>(drf), K, V, nvec, rp, out)
-    if (dt == SV_BF16) return al ? SV_GD(BF16, true) : SV_GD(BF16, false);
-    return al ? SV_GD(F32, true) : SV_GD(F32, false);
-#undef SV_GD
-}
-
 hipError_t launch_resid_mass(const void *tgt, const void *drf, int B, int V, const RowGeom &g,
-                             sv_dtype dt, const Scale &sc, const ResidParam *rp, double *tile_mass,
-                             hipStream_t s) {
-    if (dt == SV_BF16)
-        return g.aligned ? resid_mass_t<BF16, true>(tgt, drf, B, V, g, sc, rp, tile_mass, s)
-                         : resid_mass_t<BF16, false>(tgt, drf, B, V, g, sc, rp, tile_mass, s);
-    return g.aligned ? resid_mass_t<F32, true>(tgt, drf, B, V, g, sc, rp, tile_mass, s)
-                     : resid_mass_t<F32, false>(tgt, drf, B, V, g, sc, rp, tile_mass, s);
+                             sv_dtype dt, sv_dtype dq, const Scale &sc, const ResidParam *rp,
+                             double *tile_mass, hipStream_t s) {
+    return resid_dispatch(dt, dq, g, drf, [&](auto e, auto eq, auto al) {
+        return resid_mass_t<decltype(e), decltype(eq), decltype(al)::value>(tgt, drf, B, V, g, sc, rp,
+                                                                              tile_mass, s);
+    });
 }
 
 hipError_t launch_resid_select(const void *tgt, const void *drf, int B, int K, int V,
-                               const RowGeom &g, sv_dtype dt, const Scale &sc,
+                               const RowGeom &g, sv_dtype dt, sv_dtype dq, const Scale &sc,
                                const ResidParam *rp, double *tile_mass, int32_t *out_tokens,
                                hipStream_t s) {
-    if (dt == SV_BF16)
-        return g.aligned ? resid_select_t<BF16, true>(tgt, drf, B, K, V, g, sc, rp, tile_mass, out_tokens, s)
-                         : resid_select_t<BF16, false>(tgt, drf, B, K, V, g, sc, rp, tile_mass, out_tokens, s);
-    return g.aligned ? resid_select_t<F32, true>(tgt, drf, B, K, V, g, sc, rp, tile_mass, out_tokens, s)
-                     : resid_select_t<F32, false>(tgt, drf, B, K, V, g, sc, rp, tile_mass, out_tokens, s);
+    return resid_dispatch(dt, dq, g, drf, [&](auto e, auto eq, auto al) {
+        return resid_select_t<decltype(e), decltype(eq), decltype(al)::value>(tgt, drf, B, K, V, g, sc, rp,
+                                                                                tile_mass, out_tokens, s);
+    });
 }
 
 }  // namespace sv

@@ -349,9 +349,8 @@ typedef enum {
     SV_K_READ_PROBE = 14,  /* read-only stream (measurement aid) */
     SV_K_LMHEAD_STATS = 15, /* LM-head projection + row statistics partials and draft logits */
     SV_K_LMHEAD_ROWS = 16,  /* LM-head projection of the rows tokens are drawn from, written */
-    SV_K_GATHER_ROWS = 17,  /* draft rows of residual draws, widened to fp32 */
-    SV_K_MERGE_PARTS = 18,  /* row partials merged to one per row (fused projection) */
-    SV_K_COUNT = 19
+    SV_K_MERGE_PARTS = 17,  /* row partials merged to one per row (fused projection) */
+    SV_K_COUNT = 18
 } sv_kernel_id;
 
 sv_status sv_trace_begin(int capacity, unsigned kernel_mask);

@@ -216,4 +216,4 @@ def test_sample_trace_names_each_kernel():
     gpu_sample_lm(w)
     recs = sv.trace_end()
     assert [r[0] for r in recs] == ["lmhead_stats", "merge_parts", "rowstats", "accept", "lmhead_rows",
-                                    "gather_rows", "resid_mass", "resid_select"]
+                                    "resid_mass", "resid_select"]
