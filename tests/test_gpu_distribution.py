@@ -99,3 +99,52 @@ def test_sampler_law_at_full_vocabulary():
     assert _chi2_pvalue(first, b0, m0) > 1e-3
     b1, m1 = _mass_bins(P1)
     assert _chi2_pvalue(bonus, b1, m1) > 1e-3
+
+
+def test_fused_lmhead_sampler_law():
+    """The same law through the LM-head projection (spec_verify_sample_lmhead):
+    K = 1, D = 128, V = 4096, T = 0.8, exact-recipe operands, so the target
+    logits z_0, z_1 are exact and p_0, p_1 follow from a plain fp64 product.
+    Every request carries the same two hidden rows and the same draft row (the
+    target's row 0 plus N(0, 1) noise, so about half the drafts pass); 25 calls
+    of 8192 requests with fresh uniforms give 204,800 rounds.  The acceptance
+    count, the first tokens and the bonus tokens are tested as above, so the
+    re-formed fp32 row and the bf16 draft row read beside it are checked
+    against p, not against the oracle."""
+    V, D, T, Bc, calls = 4096, 128, 0.8, 8192, 25
+    w = workloads.make_sample_lmhead(1, 1, D, V, exact=True, dtype="bf16", T=T, noise_sigma=1.0, seed=11)
+    h = workloads.bf16_bits_to_f32(w.hidden.reshape(2, D)).astype(np.float64)
+    Wf = workloads.bf16_bits_to_f32(w.lm_head).astype(np.float64)
+    z = h @ Wf.T  # exact: every product and partial sum is a multiple of 2^-9 below 2^10
+    q = workloads.bf16_bits_to_f32(w.draft.reshape(1, V)).astype(np.float64)[0]
+    P0, P1, Q0 = pins.softmax64(z[0], T), pins.softmax64(z[1], T), pins.softmax64(q, T)
+    a = np.minimum(P0, Q0).sum()
+    assert 0.2 < a < 0.9
+
+    note(f"fused LM-head law: V={V} D={D} K=1 B={Bc} x {calls} calls")
+    rng = np.random.default_rng(2027)
+    hid = logits_to_dev(w.hidden.reshape(1, 2, D)).expand(Bc, 2, D).contiguous()
+    lm = logits_to_dev(w.lm_head)
+    drf = logits_to_dev(w.draft.reshape(1, 1, V)).expand(Bc, 1, V).contiguous()
+    first, bonus, n_acc = [], [], 0
+    for c in range(calls):
+        x = rng.choice(V, size=(Bc, 1), p=Q0)
+        ua = rng.random((Bc, 1), dtype=np.float32)
+        us = rng.random((Bc, 2), dtype=np.float32)
+        g = sv.spec_verify_sample_lmhead(hid, lm, drf, ints_to_dev(x), f32_to_dev(ua), f32_to_dev(us), T,
+                                         lse=c % 2 == 1)
+        torch.cuda.synchronize()
+        tok, n = g["tokens"].cpu().numpy(), g["accept_len"].cpu().numpy()
+        assert set(np.unique(n)) <= {0, 1}
+        assert np.array_equal(tok[n == 1, 0], x[n == 1, 0])
+        assert (tok[n == 0, 1] == -1).all()
+        first.append(tok[:, 0])
+        bonus.append(tok[n == 1, 1])
+        n_acc += int(n.sum())
+    first, bonus = np.concatenate(first), np.concatenate(bonus)
+    assert stats.binomtest(n_acc, Bc * calls, a).pvalue > 1e-3
+    b0, m0 = _mass_bins(P0)
+    assert len(m0) >= 20
+    assert _chi2_pvalue(first, b0, m0) > 1e-3
+    b1, m1 = _mass_bins(P1)
+    assert _chi2_pvalue(bonus, b1, m1) > 1e-3
