@@ -879,16 +879,23 @@ hipError_t resid_select_t(const void *tgt, const void *drf, int B, int K, int V,
 }
 
 // The three pairings the draw reads: both rows bf16, both fp32, or fp32
-// target rows beside bf16 draft rows (the fused LM-head form).  `aligned`
-// extends g.aligned (the target rows) to the draft rows' own vector size.
+// target rows beside bf16 draft rows (the fused LM-head form).  The aligned
+// form needs g.aligned (the target rows) and the draft rows aligned to their
+// own vector: 16 bytes, or 8 for bf16 beside fp32 (V % 4 == 0 is part of
+// g.aligned, so every draft row then starts on that boundary too).
 template <typename F>
 hipError_t resid_dispatch(sv_dtype dt, sv_dtype dq, const RowGeom &g, const void *drf, F &&f) {
-    if (dt == SV_BF16 && dq == SV_BF16)
-        return g.aligned ? f(BF16{}, BF16{}, std::true_type{}) : f(BF16{}, BF16{}, std::false_type{});
-    if (dt == SV_F32 && dq == SV_F32)
-        return g.aligned ? f(F32{}, F32{}, std::true_type{}) : f(F32{}, F32{}, std::false_type{});
+    const uintptr_t q = reinterpret_cast<uintptr_t>(drf);
+    if (dt == SV_BF16 && dq == SV_BF16) {
+        const bool al = g.aligned && (q & 15u) == 0;
+        return al ? f(BF16{}, BF16{}, std::true_type{}) : f(BF16{}, BF16{}, std::false_type{});
+    }
+    if (dt == SV_F32 && dq == SV_F32) {
+        const bool al = g.aligned && (q & 15u) == 0;
+        return al ? f(F32{}, F32{}, std::true_type{}) : f(F32{}, F32{}, std::false_type{});
+    }
     if (dt == SV_F32 && dq == SV_BF16) {
-        const bool al = g.aligned && (reinterpret_cast<uintptr_t>(drf) & 7u) == 0;
+        const bool al = g.aligned && (q & 7u) == 0;
         return al ? f(F32{}, BF16{}, std::true_type{}) : f(F32{}, BF16{}, std::false_type{});
     }
     return hipErrorInvalidValue;

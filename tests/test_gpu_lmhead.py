@@ -168,6 +168,33 @@ def test_sample_exact(case, lse):
     assert n_ok >= B - 2
 
 
+@pytest.mark.parametrize("dt,offset", [("f32", 4), ("bf16", 2), ("bf16", 8)],
+                         ids=["f32+4B", "bf16+2B", "bf16+8B"])
+def test_sample_misaligned_drafts(dt, offset):
+    """Draft logits that start `offset` bytes past a 16-byte boundary: their
+    statistics and the draw read them with per-element loads (fp32 and bf16 at
+    +2 bytes) or 8-byte ones (bf16 at +8 bytes beside the fp32 rows)."""
+    B, K, D, V = 9, 3, 256, 1000
+    note(f"lmhead sample misaligned drafts {dt} +{offset} bytes")
+    w = workloads.make_sample_lmhead(B, K, D, V, exact=True, dtype=dt, T=0.9, seed=77 + offset)
+    esz = 4 if dt == "f32" else 2
+    base = torch.empty(w.draft.size + 16 // esz, dtype=torch.float32 if dt == "f32" else torch.bfloat16,
+                       device=dev())
+    d = base[offset // esz:offset // esz + w.draft.size].view(w.draft.shape)
+    assert d.data_ptr() % 16 == offset
+    if dt == "f32":
+        d.copy_(torch.from_numpy(np.ascontiguousarray(w.draft, np.float32)))
+    else:
+        d.copy_(bf16_dev(w.draft))
+    g = sv.spec_verify_sample_lmhead(bf16_dev(w.hidden), bf16_dev(w.lm_head), d, ints_to_dev(w.draft_tokens),
+                                     f32_to_dev(w.u_accept), f32_to_dev(w.u_sample), w.T)
+    torch.cuda.synchronize()
+    g = {k: v.cpu().numpy() for k, v in g.items()}
+    n_ok, _, _ = check_sample(w, g, oracle_sample_lm(w))
+    assert n_ok >= B - 1
+    assert (g["accept_len"] < K).sum() >= 2  # residual draws read the misaligned draft rows
+
+
 def test_sample_general_recipe():
     # fp32 accumulation rounds: requests whose margin is within the derived
     # bound of a decision (lmhead.sample_flag_eps) are flagged and skipped;
