@@ -186,23 +186,43 @@ __global__ __launch_bounds__(kBlock) void k_rowstats(
 // the largest R_k, summed lane-strided and then across the wave exactly as
 // k_accept merges a row.  k_accept merging that single partial then finds the
 // same L2 = Rm + log2(sum) bit for bit.  For rows with many segments (the
-// fused projection's 128-column partials): one wave per row.
+// fused projection's 128-column partials): one wave per row.  Each lane
+// loads kMergeUnroll of its partials before it uses any of them (the loop is
+// otherwise one memory latency per partial); the additions keep their order.
+constexpr int kMergeUnroll = 8;
 __global__ __launch_bounds__(kBlock) void k_merge_parts(const float *__restrict__ R, const double *__restrict__ S,
                                                         long long rows, int segs, float *__restrict__ outR,
                                                         double *__restrict__ outS) {
+    constexpr int U = kMergeUnroll;
     const int lane = threadIdx.x & (kWave - 1);
     const long long row = static_cast<long long>(blockIdx.x) * kWavesPerBlock + (threadIdx.x >> 6);
     if (row >= rows) return;
     const float *pR = R + row * segs;
     const double *pS = S + row * segs;
-    float Rm = -__builtin_huge_valf();
-    for (int sg = lane; sg < segs; sg += kWave) Rm = fmaxf(Rm, pR[sg]);
+    const float ninf = -__builtin_huge_valf();
+    float Rm = ninf;
+    for (int sg0 = lane; sg0 < segs; sg0 += U * kWave) {
+        float r[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) r[u] = sg0 + u * kWave < segs ? pR[sg0 + u * kWave] : ninf;
+#pragma unroll
+        for (int u = 0; u < U; ++u) Rm = fmaxf(Rm, r[u]);
+    }
     Rm = wave_max(Rm);
     double acc = 0.0;
-    if (Rm != -__builtin_huge_valf()) {
-        for (int sg = lane; sg < segs; sg += kWave) {
-            const double ss = pS[sg];
-            if (ss > 0.0) acc += ss * exp2(static_cast<double>(pR[sg]) - static_cast<double>(Rm));
+    if (Rm != ninf) {
+        for (int sg0 = lane; sg0 < segs; sg0 += U * kWave) {
+            float r[U];
+            double ss[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int sg = sg0 + u * kWave;
+                r[u] = sg < segs ? pR[sg] : ninf;
+                ss[u] = sg < segs ? pS[sg] : 0.0;
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (ss[u] > 0.0) acc += ss[u] * exp2(static_cast<double>(r[u]) - static_cast<double>(Rm));
         }
     }
     acc = wave_sum(acc);
