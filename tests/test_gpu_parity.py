@@ -271,6 +271,36 @@ def test_misaligned_pointers_take_the_general_path():
                 oracle.verify_greedy(wg.target, wg.draft_tokens), ("accept_len", "tokens"))
 
 
+@pytest.mark.parametrize("lse", [True, False], ids=["full", "skip"])
+def test_empty_residual_draws_from_p(lse):
+    """A rejected position whose draft row equals its target row: both sides
+    compute p and q there alike, so max(0, p - q) is 0 everywhere and the draw
+    falls back to p alone with the same uniform (the rounding rule of the
+    oracle's step 5).  The rejection is forced by an out-of-range draft (ratio
+    0); earlier drafts pass with u = 0.  The oracle flags such a draw (margin
+    0), so here the GPU token is held to the oracle's draw from p_j as a K = 0
+    bonus draw, whose own margin is checked."""
+    B, K, V = 8, 3, 4096
+    note(f"empty residual lse={lse}")
+    w = workloads.make_sample(B, K, V, "bf16", 1.0, spikes=3, noise_sigma=1.0, seed=31)
+    j = np.array([0, 1, 2, 0, 1, 2, 1, 0])
+    for b in range(B):
+        w.draft[b, j[b]] = w.target[b, j[b]]
+        w.draft_tokens[b, j[b]] = -1 if b % 2 else V
+        w.u_accept[b, :j[b]] = 0.0
+    o = oracle_sample(w)
+    assert np.array_equal(o["accept_len"], j) and (o["margin"] == 0.0).all()
+    rows = np.ascontiguousarray(w.target[np.arange(B), j][:, None, :])
+    ob = oracle.verify_sample(rows, np.zeros((B, 0, V), rows.dtype), np.zeros((B, 0), np.int32),
+                              np.zeros((B, 0), np.float32), w.u_sample[np.arange(B), j][:, None], w.T)
+    assert (ob["margin"] > 1e-6).all()
+    assert np.array_equal(o["tokens"][np.arange(B), j], ob["tokens"][:, 0])
+    g = gpu_sample(w, lse=lse)
+    assert np.array_equal(g["accept_len"], j)
+    assert np.array_equal(g["status"], np.ones(B, np.int32))
+    assert np.array_equal(g["tokens"], o["tokens"]), (g["tokens"], o["tokens"])
+
+
 def test_lse_only_rows_and_temperature_extremes():
     note("lse temperature extremes")
     for T in (0.05, 0.7, 4.0):
