@@ -26,6 +26,10 @@
 //                  acceptance in one launch that does not read the rows of
 //                  positions after each request's first rejection (protocol in
 //                  sv_skip.hpp); the residual kernels then run as above.
+//   k_merge_parts  the fused LM-head form's many 128-column partials per
+//                  target row merged to one per row before k_accept; there
+//                  the residual kernels read the re-formed fp32 target row
+//                  beside the draft row in its own type.
 //
 // Precision: per-element exponentials run in fp32 on v_exp_f32 with the
 // exponent formed by two fused multiply-adds against c = c_hi + c_lo, so the
