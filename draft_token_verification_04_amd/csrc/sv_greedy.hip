@@ -90,9 +90,13 @@ __global__ __launch_bounds__(kBlock) void k_argmax(const typename E::storage *__
 // (segs keys per row), written to out[0..nrows).  The keys of up to
 // `lds_rows` rows at a time are first copied into LDS with every load in
 // flight; then each wave reduces whole rows.  lds_rows = 0 reads global memory
-// directly (rows with too many segments to stage).
+// directly (rows with too many segments to stage).  Each thread loads
+// kKeyUnroll keys before it uses any of them: a row of the fused projection has
+// ~1200 keys, and one memory latency per key would dominate.
+constexpr int kKeyUnroll = 8;
 __device__ __forceinline__ void merge_rows(const uint64_t *__restrict__ keys, int nrows, int segs,
                                            int lds_rows, uint64_t *stage, int *out) {
+    constexpr int U = kKeyUnroll;
     const int tid = threadIdx.x, wid = tid >> 6, lane = tid & (kWave - 1);
     const int nw = blockDim.x >> 6;
     const int chunk = lds_rows > 0 ? lds_rows : nrows;
@@ -100,15 +104,31 @@ __device__ __forceinline__ void merge_rows(const uint64_t *__restrict__ keys, in
         const int nr = min(chunk, nrows - r0);
         const uint64_t *src = keys + static_cast<long long>(r0) * segs;
         if (lds_rows > 0) {
-            for (int i = tid; i < nr * segs; i += blockDim.x) stage[i] = src[i];
+            const int n = nr * segs;
+            for (int i0 = tid; i0 < n; i0 += U * static_cast<int>(blockDim.x)) {
+                uint64_t v[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int i = i0 + u * static_cast<int>(blockDim.x);
+                    v[u] = i < n ? src[i] : 0;
+                }
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int i = i0 + u * static_cast<int>(blockDim.x);
+                    if (i < n) stage[i] = v[u];
+                }
+            }
             __syncthreads();
             src = stage;
         }
         for (int rr = wid; rr < nr; rr += nw) {
             uint64_t mk = 0;
-            for (int s = lane; s < segs; s += kWave) {
-                const uint64_t k = src[rr * segs + s];
-                mk = k > mk ? k : mk;
+            for (int s0 = lane; s0 < segs; s0 += U * kWave) {
+                uint64_t v[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) v[u] = s0 + u * kWave < segs ? src[rr * segs + s0 + u * kWave] : 0;
+#pragma unroll
+                for (int u = 0; u < U; ++u) mk = v[u] > mk ? v[u] : mk;
             }
             mk = wave_max_u64(mk);
             if (lane == 0) out[r0 + rr] = argmax_key_index(mk);
