@@ -76,6 +76,18 @@ def test_tree_exact(case):
     compare(gpu_tree(w), o, ("accept_len", "path", "tokens", "status"))
 
 
+def test_tree_many_nodes():
+    """1017-node trees on a 20000-id vocabulary: 157 argmax keys per node row,
+    so a request's keys fill LDS several times over and the tree kernel merges
+    them in chunks of rows (the full-read tree path, N > 64)."""
+    note("lmhead tree many nodes")
+    w = workloads.make_tree_lmhead(2, 128, 20000, exact=True, p_match=0.9, n_main=16, n_branch=500, seed=5)
+    assert w.N == 1017
+    o = lmhead.verify_tree(w.hidden, w.lm_head, w.node_tokens, w.parents, exact=True)
+    assert o["accept_len"].max() >= 3
+    compare(gpu_tree(w), o, ("accept_len", "path", "tokens", "status"))
+
+
 def test_out_of_range_drafts_and_bad_parents():
     note("lmhead bad inputs")
     w = workloads.make_greedy_lmhead(6, 4, 128, 500, exact=True, seed=3)
