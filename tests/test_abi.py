@@ -43,6 +43,22 @@ def test_version_and_status_strings(lib):
     assert lib.sv_kernel_name(99) == b"unknown"
 
 
+def test_kernel_ids_agree_across_header_library_and_binding(lib):
+    """The sv_kernel_id enum in the header, the library's sv_kernel_name and the
+    binding's KERNELS tuple name the same kernels in the same order."""
+    text = open(HEADER).read()
+    body = text[text.index("SV_K_ROWSTATS"):text.index("} sv_kernel_id;")]
+    ids = {m.group(1): int(m.group(2)) for m in re.finditer(r"SV_K_([A-Z_]+)\s*=\s*(\d+)", body)}
+    count = ids.pop("COUNT")
+    assert sorted(ids.values()) == list(range(count))
+    assert len(sv.KERNELS) == count
+    for name, k in ids.items():
+        assert sv.KERNELS[k] == name.lower(), (k, name, sv.KERNELS[k])
+        assert lib.sv_kernel_name(k) == name.lower().encode()
+    assert lib.sv_kernel_name(count) == b"unknown"
+    assert lib.sv_kernel_name(-1) == b"unknown"
+
+
 def test_workspace_queries(lib):
     V = 151936
     a = lib.sv_sample_workspace_bytes(256, 7, V, sv.SV_BF16)
