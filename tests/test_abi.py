@@ -59,6 +59,17 @@ def test_kernel_ids_agree_across_header_library_and_binding(lib):
     assert lib.sv_kernel_name(-1) == b"unknown"
 
 
+def test_binding_constants_match_the_header():
+    """Status codes, dtype codes and size limits the binding passes through
+    ctypes are the header's own values."""
+    text = open(HEADER).read()
+    consts = {m.group(1): int(m.group(2)) for m in re.finditer(r"\b(SV_[A-Z0-9_]+)\s*=\s*(\d+)", text)}
+    consts.update({m.group(1): int(m.group(2)) for m in re.finditer(r"#define\s+(SV_[A-Z_]+)\s+(\d+)", text)})
+    for name in ("SV_OK", "SV_ERR_INVALID_ARG", "SV_ERR_UNSUPPORTED", "SV_ERR_WORKSPACE", "SV_ERR_HIP",
+                 "SV_F32", "SV_BF16", "SV_MAX_TREE_NODES"):
+        assert getattr(sv, name) == consts[name], name
+
+
 def test_workspace_queries(lib):
     V = 151936
     a = lib.sv_sample_workspace_bytes(256, 7, V, sv.SV_BF16)
