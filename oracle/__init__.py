@@ -39,7 +39,7 @@ def _bind(lib):
     P = ctypes.c_void_p
     I = ctypes.c_int
     D = ctypes.c_double
-    lib.sv_oracle_sample.argtypes = [P, P, I, P, P, P, I, I, I, D, P, P, P, P, P, P, P, I]
+    lib.sv_oracle_sample.argtypes = [P, P, I, P, P, P, I, I, I, D, P, P, P, P, P, P, P, P, P, I]
     lib.sv_oracle_greedy.argtypes = [P, I, P, I, I, I, P, P, P, I]
     lib.sv_oracle_tree.argtypes = [P, I, P, P, I, I, I, P, P, P, P, I]
     lib.sv_oracle_row_stats.argtypes = [P, I, I, I, D, P, P, P]
@@ -86,7 +86,10 @@ def _c(a, dtype):
 def verify_sample(target, draft, draft_tokens, u_accept, u_sample, T, threads=None, lib=None):
     """Stochastic chain verification.  Returns a dict of numpy arrays:
     accept_len [B], tokens [B,K+1], lse_target [B,K+1], lse_draft [B,K],
-    status [B], margin [B] (smallest consumed-draw margin), Z [B]."""
+    status [B], margin [B] (smallest consumed-draw margin), margin_accept [B]
+    (smallest margin of the consumed acceptance draws, which alone decide
+    accept_len; +inf when none), margin_sample [B] (the sample draw's margin),
+    Z [B]."""
     lib = lib or load()
     B, K1, V = target.shape
     K = K1 - 1
@@ -100,11 +103,13 @@ def verify_sample(target, draft, draft_tokens, u_accept, u_sample, T, threads=No
     us = _c(u_sample, np.float32).reshape(B, K + 1)
     out = dict(accept_len=np.empty(B, np.int32), tokens=np.empty((B, K + 1), np.int32),
                lse_target=np.empty((B, K + 1)), lse_draft=np.empty((B, K)),
-               status=np.empty(B, np.int32), margin=np.empty(B), Z=np.empty(B))
+               status=np.empty(B, np.int32), margin=np.empty(B), margin_accept=np.empty(B),
+               margin_sample=np.empty(B), Z=np.empty(B))
     rc = lib.sv_oracle_sample(_ptr(target), _ptr(draft), dt, _ptr(x), _ptr(ua), _ptr(us), B, K, V,
                               float(T), _ptr(out["accept_len"]), _ptr(out["tokens"]),
                               _ptr(out["lse_target"]), _ptr(out["lse_draft"]), _ptr(out["status"]),
-                              _ptr(out["margin"]), _ptr(out["Z"]), threads or default_threads())
+                              _ptr(out["margin"]), _ptr(out["margin_accept"]),
+                              _ptr(out["margin_sample"]), _ptr(out["Z"]), threads or default_threads())
     if rc:
         raise ValueError("oracle rejected the arguments")
     return out

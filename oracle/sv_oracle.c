@@ -174,13 +174,16 @@ static int orc_inverse_cdf(const orc_row *p, const orc_row *q, double u, double 
  * Outputs: accept_len [B], out_tokens [B][K+1] (n+1 valid, -1 pad),
  * lse_target [B][K+1], lse_draft [B][K] (may be NULL), req_status [B]
  * (0 ok, 1 a draft id outside [0,V)), margin [B] (smallest margin over the
- * consumed draws), Z [B] (mass of the distribution that was sampled).
+ * consumed draws), margin_accept [B] (smallest margin over the consumed
+ * acceptance draws alone, +inf when there is none: these draws alone decide
+ * accept_len), margin_sample [B] (the margin of the one sample draw), Z [B]
+ * (mass of the distribution that was sampled).  Every margin output may be NULL.
  */
 int sv_oracle_sample(const void *target, const void *draft, int dtype, const int32_t *draft_tokens,
                      const float *u_accept, const float *u_sample, int B, int K, int V, double T,
                      int32_t *accept_len, int32_t *out_tokens, double *lse_target,
-                     double *lse_draft, int32_t *req_status, double *margin, double *Zout,
-                     int nthreads) {
+                     double *lse_draft, int32_t *req_status, double *margin,
+                     double *margin_accept, double *margin_sample, double *Zout, int nthreads) {
     if (B < 0 || K < 0 || V <= 0 || !(T > 0.0)) return 1;
     if (nthreads < 1) nthreads = 1;
 #pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
@@ -248,6 +251,7 @@ int sv_oracle_sample(const void *target, const void *draft, int dtype, const int
         } else {
             t = orc_inverse_cdf(&p, NULL, us, &m2, &Z);
         }
+        double ma = mg;
         if (m2 < mg) mg = m2;
 
         for (int i = 0; i < n; ++i) tok[i] = x[i];
@@ -256,6 +260,8 @@ int sv_oracle_sample(const void *target, const void *draft, int dtype, const int
         accept_len[b] = n;
         if (req_status) req_status[b] = status;
         if (margin) margin[b] = mg;
+        if (margin_accept) margin_accept[b] = ma;
+        if (margin_sample) margin_sample[b] = m2;
         if (Zout) Zout[b] = Z;
     }
     return 0;

@@ -3,9 +3,13 @@ run the HIP path through the C ABI, run the oracle, and compare.
 
 Comparison rules:
 * greedy chains and trees: every output bit-exact;
-* stochastic chains: accept_len and tokens exact for every request whose
-  oracle margin (distance of a consumed uniform to its acceptance ratio or
-  inverse-CDF cell edge) exceeds 1e-6; such "flagged" requests are counted;
+* stochastic chains: accept_len exact for every request whose consumed
+  acceptance draws all lie more than 1e-6 from their ratios (the oracle's
+  margin_accept), and tokens exact for every request whose every consumed
+  draw, the sample draw's inverse-CDF cell edges included, lies more than
+  1e-6 from its boundary (the oracle's margin); requests inside the band are
+  "flagged" and counted, at most B // 32 + 1 of them, and at least one request
+  is compared, so the exact check can never be emptied by the flagging;
 * row log-sum-exp: |gpu - oracle| <= 1e-5 |oracle| (+1e-6 absolute floor for
   values near zero).
 """
@@ -84,13 +88,26 @@ def check_lse(gpu, ref):
     assert not bad.any(), f"lse mismatch at {np.argwhere(bad)[:5]}: {gpu[bad][:5]} vs {ref[bad][:5]}"
 
 
+def flag_ceiling(B: int) -> int:
+    """Most flagged requests a batch of B may hold.  A draw is flagged inside a
+    band 2e-6 wide around each decision boundary; on the workloads' rows this
+    catches about one request in 64 (1 of 32 and 4 of 256 on the two bf16
+    workloads), so B // 32 + 1 leaves room for seeds without letting the band
+    swallow the batch."""
+    return B // 32 + 1
+
+
 def check_sample(w, g, o):
     """Assert parity; return (#unflagged compared, #flagged, #flagged that differ)."""
     flagged = o["margin"] <= FLAG_EPS
     ok = ~flagged
-    na = np.nonzero(ok & (g["accept_len"] != o["accept_len"]))[0]
+    B = len(flagged)
+    assert ok.any(), "every request is flagged: the exact check would be empty"
+    assert flagged.sum() <= flag_ceiling(B), f"{flagged.sum()} of {B} requests flagged"
+    ok_a = o["margin_accept"] > FLAG_EPS
+    na = np.nonzero(ok_a & (g["accept_len"] != o["accept_len"]))[0]
     assert na.size == 0, (f"accept_len differs at {na[:8]}: gpu {g['accept_len'][na[:8]]} "
-                          f"oracle {o['accept_len'][na[:8]]} margins {o['margin'][na[:8]]}")
+                          f"oracle {o['accept_len'][na[:8]]} margins {o['margin_accept'][na[:8]]}")
     nt = np.nonzero(ok & (g["tokens"] != o["tokens"]).any(1))[0]
     assert nt.size == 0, (f"tokens differ at {nt[:8]}: gpu {g['tokens'][nt[:4]]} "
                           f"oracle {o['tokens'][nt[:4]]} margins {o['margin'][nt[:8]]} Z {o['Z'][nt[:8]]}")

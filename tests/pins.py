@@ -469,6 +469,144 @@ def pin_dead_rows(lib, seed=8):
     assert np.array_equal(g["tokens"], g2["tokens"])
 
 
+# ---------------------------------------------------------------- draw margins
+
+def _decode(a):
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def reference_draws(target, draft, x, ua, us, T):
+    """Accept lengths, drawn tokens and draw margins recomputed from the pages'
+    rule with library routines only (scipy softmax in float64, numpy cumsum and
+    searchsorted), never through the oracle.  The conventions are the oracle's
+    stated readings: accept iff u < p/q (q = 0 accepts, an id outside [0, V)
+    has ratio 0); the token is the first v whose running mass exceeds u*Z; an
+    empty residual falls back to p with the same draw and counts as a boundary.
+    The margin of an acceptance draw is |u - p/q| (finite ratios only); that of
+    the sample draw is the distance from u to the nearer end of the chosen
+    token's cell [C(v-1)/Z, C(v)/Z).  Returns a dict of arrays."""
+    B, K1, V = target.shape
+    K = K1 - 1
+    tg, dr = _decode(target), _decode(draft)
+    out = dict(accept_len=np.empty(B, np.int64), token=np.empty(B, np.int64),
+               margin_accept=np.full(B, np.inf), margin_sample=np.empty(B), Z=np.empty(B))
+    for b in range(B):
+        n = K
+        for i in range(K):
+            xi = int(x[b, i])
+            if 0 <= xi < V:
+                p = special.softmax(tg[b, i] / T)
+                q = special.softmax(dr[b, i] / T)
+                r = np.inf if q[xi] == 0.0 else p[xi] / q[xi]
+            else:
+                r = 0.0
+            u = float(ua[b, i])
+            if np.isfinite(r):
+                out["margin_accept"][b] = min(out["margin_accept"][b], abs(u - r))
+            if not u < r:
+                n = i
+                break
+        p = special.softmax(tg[b, n] / T)
+        mass = np.maximum(0.0, p - special.softmax(dr[b, n] / T)) if n < K else p
+        C = np.cumsum(mass)
+        fallback = not C[-1] > 0.0
+        if fallback:
+            C = np.cumsum(p)
+        Z = C[-1]
+        u = float(us[b, n])
+        v = int(np.searchsorted(C, u * Z, side="right"))
+        if v >= V:  # u*Z at or past the total: the last token with mass, a boundary
+            v = int(np.nonzero(np.diff(np.concatenate([[0.0], C])) > 0)[0][-1])
+            m = 0.0
+        else:
+            lo = C[v - 1] if v > 0 else 0.0
+            m = min(abs(u - lo / Z), abs(u - C[v] / Z))
+        out["accept_len"][b] = n
+        out["token"][b] = v
+        out["margin_sample"][b] = 0.0 if fallback else m
+        out["Z"][b] = Z
+    return out
+
+
+def check_margins(o, ref, tol=1e-9):
+    """The oracle's margins equal the recomputed ones within tol (both are
+    float64 with different summation orders); its decisions equal them
+    wherever the recomputed margins leave room for that rounding."""
+    B = len(ref["accept_len"])
+    ma, ms = o["margin_accept"], o["margin_sample"]
+    fin = np.isfinite(ref["margin_accept"])
+    assert np.array_equal(np.isfinite(ma), fin), "which requests have an acceptance margin"
+    assert np.all(np.abs(ma[fin] - ref["margin_accept"][fin]) <= tol), \
+        np.abs(ma[fin] - ref["margin_accept"][fin]).max()
+    assert np.all(np.abs(ms - ref["margin_sample"]) <= tol), np.abs(ms - ref["margin_sample"]).max()
+    assert np.all(o["margin"] == np.minimum(ma, ms)), "margin is the smaller of the two"
+    sure_a = ref["margin_accept"] > tol
+    assert np.array_equal(o["accept_len"][sure_a], ref["accept_len"][sure_a])
+    sure = sure_a & (ref["margin_sample"] > tol)
+    n = o["accept_len"]
+    assert np.array_equal(o["tokens"][np.arange(B), n][sure], ref["token"][sure])
+
+
+def pin_margins(lib, seed=13):
+    """Draw margins (which decide the flagged requests) recomputed independently:
+    random drafts and draws, draws planted on decision boundaries, ratios above 1,
+    and the empty-residual fallback."""
+    rng = np.random.default_rng(seed)
+    for (B, K, V, T) in ((300, 3, 6, 1.0), (200, 2, 40, 0.7), (64, 0, 9, 1.3)):
+        lp = (rng.standard_normal((B, K + 1, V)) * 1.5).astype(F32)
+        lq = (lp[:, :K] + rng.standard_normal((B, K, V))).astype(F32)
+        P, Q = softmax64(lp, T), softmax64(lq, T)
+        x = np.empty((B, K), np.int32)
+        for b in range(B):
+            for i in range(K):
+                x[b, i] = rng.choice(V, p=Q[b, i])
+        ua = rng.random((B, K), dtype=F32)
+        us = rng.random((B, K + 1), dtype=F32)
+        # plant draws on boundaries: an acceptance draw at its ratio, a sample
+        # draw at a cell edge of the bonus row
+        for b in range(0, B, 7):
+            if K:
+                r = P[b, 0, x[b, 0]] / Q[b, 0, x[b, 0]]
+                if r < 1:
+                    ua[b, 0] = F32(r)
+            us[b, K] = F32(np.cumsum(P[b, K])[rng.integers(0, V - 1)])
+        o = oracle.verify_sample(lp, lq, x, ua, us, T, threads=1, lib=lib)
+        ref = reference_draws(lp, lq, x, ua, us, T)
+        check_margins(o, ref)
+        assert (o["margin"] <= 1e-6).any() and (o["margin"] > 1e-6).any()
+        if K == 0:
+            assert np.all(np.isinf(o["margin_accept"]))
+    # empty residual: draft row = target row at a rejection forced by an
+    # out-of-range id; the draw from p is a boundary case (margin 0)
+    B, K, V = 8, 2, 12
+    lp = rng.standard_normal((B, K + 1, V)).astype(F32)
+    lq = rng.standard_normal((B, K, V)).astype(F32)
+    lq[:, 1] = lp[:, 1]
+    x = rng.integers(0, V, (B, K)).astype(np.int32)
+    x[:, 1] = np.where(np.arange(B) % 2, -1, V)
+    ua = np.zeros((B, K), F32)
+    us = rng.random((B, K + 1), dtype=F32)
+    o = oracle.verify_sample(lp, lq, x, ua, us, 1.0, threads=1, lib=lib)
+    ref = reference_draws(lp, lq, x, ua, us, 1.0)
+    check_margins(o, ref)
+    assert np.all(o["accept_len"] == 1) and np.all(o["margin_sample"] == 0.0)
+
+
+def pin_margins_full_vocab(lib, requests=4):
+    """The same recomputation on the first requests of the B=32 bf16 workload
+    at its full vocabulary (151936)."""
+    import workloads
+
+    w = workloads.make_workload("sample_b32_k7_qwen3")
+    sl = slice(0, requests)
+    args = (w.target[sl], w.draft[sl], w.draft_tokens[sl], w.u_accept[sl], w.u_sample[sl], w.T)
+    o = oracle.verify_sample(*args, lib=lib)
+    check_margins(o, reference_draws(*args))
+
+
 # ------------------------------------------------------------------------ trees
 
 def brute_force_tree(L, tok, par):
@@ -547,4 +685,5 @@ def pin_tree(lib, seed=10):
 
 
 ALL_FAST = (pin_position_lossless, pin_sequence_lossless, pin_expected_accept_length,
-            pin_special_cases, pin_lse, pin_greedy, pin_cross_mode, pin_dead_rows, pin_tree)
+            pin_special_cases, pin_lse, pin_greedy, pin_cross_mode, pin_dead_rows, pin_margins,
+            pin_tree)

@@ -55,7 +55,7 @@ def test_sample_grid(case, lse):
     o = oracle_sample(w)
     g = gpu_sample(w, lse=lse)
     ncmp, nflag, ndiff = check_sample(w, g, o)
-    assert ncmp + nflag == B
+    assert ncmp + nflag == B and ncmp >= 1
 
 
 @pytest.mark.parametrize("lse", [True, False], ids=["full", "skip"])

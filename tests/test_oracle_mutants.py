@@ -39,6 +39,17 @@ MUTANTS = {
     "tree_highest_on_ties": ("if (ok[j] && depth[j] > depth[best]) best = j;",
                              "if (ok[j] && depth[j] >= depth[best]) best = j;"),
     "tree_bonus_parent_row": ("out[d] = am[best];", "out[d] = am[par[best] < 0 ? 0 : par[best]];"),
+    # the draw margins, which decide the flagged requests
+    "margin_drops_left_edge": ("*margin = a < b ? a : b;", "*margin = b;"),
+    "margin_drops_right_edge": ("*margin = a < b ? a : b;", "*margin = a;"),
+    "margin_unnormalised": ("double a = fabs(u - Cprev / Z), b = fabs(u - C / Z);",
+                            "double a = fabs(t - Cprev), b = fabs(t - C);"),
+    "margin_skips_accept_draws": ("double d = fabs(u - r);", "double d = INFINITY;"),
+    "margin_clamped_ratio": ("double d = fabs(u - r);", "double d = fabs(u - (r < 1.0 ? r : 1.0));"),
+    "margin_skips_rejecting_draw": ("            if (isfinite(r)) {", "            if (isfinite(r) && u < r) {"),
+    "margin_skips_sample_draw": ("        if (m2 < mg) mg = m2;\n", ""),
+    "margin_fallback_not_boundary": ("                t = orc_inverse_cdf(&p, NULL, us, &m2, &Z);\n                m2 = 0.0;",
+                                     "                t = orc_inverse_cdf(&p, NULL, us, &m2, &Z);"),
 }
 
 

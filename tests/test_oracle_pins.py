@@ -48,6 +48,14 @@ def test_dead_rows_do_not_matter(olib):
     pins.pin_dead_rows(olib)
 
 
+def test_draw_margins_recomputed(olib):
+    pins.pin_margins(olib)
+
+
+def test_draw_margins_full_vocabulary(olib):
+    pins.pin_margins_full_vocab(olib)
+
+
 def test_tree_brute_force(olib):
     pins.pin_tree(olib)
 
