@@ -166,6 +166,19 @@ def _stream(torch, device, stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _hold(torch, device, stream, *tensors):
+    """The kernels of a call made with ``stream=`` run on that stream, while
+    this binding allocates the workspace and outputs on the current one.  When
+    the two differ, mark those blocks as in use on ``stream`` so the caching
+    allocator hands none of them to another allocation before the call's
+    kernels are done with it."""
+    if stream is None or stream.cuda_stream == torch.cuda.current_stream(device).cuda_stream:
+        return
+    for t in tensors:
+        if t is not None:
+            t.record_stream(stream)
+
+
 def _workspace(torch, nbytes, device, workspace):
     if workspace is None:
         return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
@@ -232,6 +245,7 @@ def spec_verify_sample(target, draft, draft_tokens, u_accept, u_sample, temperat
             ws.numel() * ws.element_size(), _stream(torch, dev, stream))
     if rc != SV_OK:
         raise SpecVerifyError(rc, "spec_verify_sample")
+    _hold(torch, dev, stream, ws if workspace is None else None, *out.values())
     return out
 
 
@@ -261,6 +275,7 @@ def spec_verify_greedy(target, draft_tokens, *, status=True, workspace=None, str
             ws.numel() * ws.element_size(), _stream(torch, dev, stream))
     if rc != SV_OK:
         raise SpecVerifyError(rc, "spec_verify_greedy")
+    _hold(torch, dev, stream, ws if workspace is None else None, *out.values())
     return out
 
 
@@ -291,6 +306,7 @@ def spec_verify_tree(target, node_tokens, parents, *, status=True, workspace=Non
             ws.numel() * ws.element_size(), _stream(torch, dev, stream))
     if rc != SV_OK:
         raise SpecVerifyError(rc, "spec_verify_tree")
+    _hold(torch, dev, stream, ws if workspace is None else None, *out.values())
     return out
 
 
@@ -331,6 +347,7 @@ def spec_verify_greedy_lmhead(hidden, lm_head, draft_tokens, *, status=True, wor
             ws.numel() * ws.element_size(), _stream(torch, dev, stream))
     if rc != SV_OK:
         raise SpecVerifyError(rc, "spec_verify_greedy_lmhead")
+    _hold(torch, dev, stream, ws if workspace is None else None, *out.values())
     return out
 
 
@@ -360,6 +377,7 @@ def spec_verify_tree_lmhead(hidden, lm_head, node_tokens, parents, *, status=Tru
             _ptr(ws), ws.numel() * ws.element_size(), _stream(torch, dev, stream))
     if rc != SV_OK:
         raise SpecVerifyError(rc, "spec_verify_tree_lmhead")
+    _hold(torch, dev, stream, ws if workspace is None else None, *out.values())
     return out
 
 
@@ -404,6 +422,7 @@ def spec_verify_sample_lmhead(hidden, lm_head, draft, draft_tokens, u_accept, u_
             ws.numel() * ws.element_size(), _stream(torch, dev, stream))
     if rc != SV_OK:
         raise SpecVerifyError(rc, "spec_verify_sample_lmhead")
+    _hold(torch, dev, stream, ws if workspace is None else None, *out.values())
     return out
 
 
@@ -433,6 +452,7 @@ def spec_ngram_candidates(context, lengths, queries, cap, *, status=True, worksp
                                        _stream(torch, dev, stream))
     if rc != SV_OK:
         raise SpecVerifyError(rc, "spec_ngram_candidates")
+    _hold(torch, dev, stream, ws if workspace is None else None, *out.values())
     return out
 
 
@@ -472,6 +492,7 @@ def spec_commit_tree_kv(kv, tree_base, commit_base, accept_len, path, *, out=Non
                                      _stream(torch, dev, stream))
     if rc != SV_OK:
         raise SpecVerifyError(rc, "spec_commit_tree_kv")
+    _hold(torch, dev, stream, st)
     return st
 
 
@@ -493,6 +514,7 @@ def sv_read_probe(buf, *, folds=None, stream=None):
         rc = lib.sv_read_probe(_ptr(buf), nbytes, _ptr(folds), _stream(torch, dev, stream))
     if rc != SV_OK:
         raise SpecVerifyError(rc, "sv_read_probe")
+    _hold(torch, dev, stream, folds)
     return folds
 
 

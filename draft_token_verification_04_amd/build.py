@@ -32,12 +32,44 @@ def flags() -> list:
     ]
 
 
+def source_digest(extra=()) -> str:
+    """Hash of everything the library is built from: the kernel and API sources,
+    the headers, and the compiler flags."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for d in (CSRC, INCLUDE):
+        for name in sorted(os.listdir(d)):
+            if name.endswith((".hip", ".hpp", ".h")):
+                h.update(name.encode())
+                with open(os.path.join(d, name), "rb") as f:
+                    h.update(f.read())
+    h.update(" ".join([*flags(), *extra, *SOURCES]).encode())
+    return h.hexdigest()
+
+
+def digest_path(out: str = LIB) -> str:
+    return out + ".srchash"
+
+
+def is_current(out: str = LIB) -> bool:
+    """True when `out` exists and was built from the sources as they are now."""
+    try:
+        with open(digest_path(out)) as f:
+            return os.path.exists(out) and f.read().strip() == source_digest()
+    except OSError:
+        return False
+
+
 def build(out: str = LIB, extra=()) -> str:
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
     tmp = out + ".tmp"
     cmd = [hipcc(), *flags(), *extra, *srcs, "-o", tmp]
     subprocess.run(cmd, check=True)
     os.replace(tmp, out)
+    if not extra:
+        with open(digest_path(out), "w") as f:
+            f.write(source_digest() + "\n")
     return out
 
 

@@ -184,7 +184,7 @@ sv_status spec_verify_sample(const void *target_logits, const void *draft_logits
                              const float *u_sample, int B, int K, int V, sv_dtype dt,
                              float temperature, int32_t *accept_len, int32_t *out_tokens,
                              float *lse_target, float *lse_draft, int32_t *req_status,
-                             void *workspace, size_t workspace_bytes, void *stream) {
+                             void *workspace, size_t workspace_bytes, hipStream_t stream) {
     if (!valid_dtype(dt)) return SV_ERR_UNSUPPORTED;
     if (B < 0 || K < 0 || V < 1 || !(temperature > 0.0f) || !isfinite(temperature))
         return SV_ERR_INVALID_ARG;
@@ -207,7 +207,7 @@ sv_status spec_verify_sample(const void *target_logits, const void *draft_logits
     double *tiles = reinterpret_cast<double *>(ws + L.tiles);
     const Scale sc = make_scale(static_cast<double>(temperature));
     if (!(sc.c < 0x1p127)) return SV_ERR_UNSUPPORTED;  // T below ~1e-38: log2(e)/T beyond fp32 range
-    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipStream_t s = stream;
     const long long rows_t = static_cast<long long>(B) * (K + 1);
     const long long rows_total = rows_t + static_cast<long long>(B) * K;
 
@@ -247,7 +247,7 @@ sv_status spec_verify_sample(const void *target_logits, const void *draft_logits
 sv_status spec_verify_greedy(const void *target_logits, const int32_t *draft_tokens, int B, int K,
                              int V, sv_dtype dt, int32_t *accept_len, int32_t *out_tokens,
                              int32_t *req_status, void *workspace, size_t workspace_bytes,
-                             void *stream) {
+                             hipStream_t stream) {
     if (!valid_dtype(dt)) return SV_ERR_UNSUPPORTED;
     if (B < 0 || K < 0 || V < 1) return SV_ERR_INVALID_ARG;
     if (K > SV_MAX_DRAFT_LEN || !sizes_ok(B, static_cast<long long>(K) + 1, V)) return SV_ERR_UNSUPPORTED;
@@ -261,7 +261,7 @@ sv_status spec_verify_greedy(const void *target_logits, const int32_t *draft_tok
     if (workspace_bytes < L.total) return SV_ERR_WORKSPACE;
     char *ws = static_cast<char *>(workspace);
     uint64_t *pk = reinterpret_cast<uint64_t *>(ws + L.part_k);
-    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipStream_t s = stream;
     hipError_t e = hipSuccess;
     if (SV_GREEDY_SKIP && skip_supported(K)) {
         // rows of positions after each request's first mismatch are not read
@@ -283,7 +283,7 @@ sv_status spec_verify_tree(const void *target_logits, const int32_t *node_tokens
                            const int32_t *parents, int B, int N, int V, sv_dtype dt,
                            int32_t *accept_len, int32_t *path_nodes, int32_t *out_tokens,
                            int32_t *req_status, void *workspace, size_t workspace_bytes,
-                           void *stream) {
+                           hipStream_t stream) {
     if (!valid_dtype(dt)) return SV_ERR_UNSUPPORTED;
     if (B < 0 || N < 1 || V < 1) return SV_ERR_INVALID_ARG;
     if (N > SV_MAX_TREE_NODES || !sizes_ok(B, N, V)) return SV_ERR_UNSUPPORTED;
@@ -298,7 +298,7 @@ sv_status spec_verify_tree(const void *target_logits, const int32_t *node_tokens
     if (workspace_bytes < L.total) return SV_ERR_WORKSPACE;
     char *ws = static_cast<char *>(workspace);
     uint64_t *pk = reinterpret_cast<uint64_t *>(ws + L.part_k);
-    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipStream_t s = stream;
     hipError_t e = hipSuccess;
     if (SV_GREEDY_SKIP && tree_skip_supported(N)) {
         // rows of rejected nodes are not read
@@ -343,7 +343,7 @@ static RowGeom lmhead_geom(int V) {
 sv_status spec_verify_greedy_lmhead(const void *hidden, const void *lm_head,
                                     const int32_t *draft_tokens, int B, int K, int D, int V,
                                     int32_t *accept_len, int32_t *out_tokens, int32_t *req_status,
-                                    void *workspace, size_t workspace_bytes, void *stream) {
+                                    void *workspace, size_t workspace_bytes, hipStream_t stream) {
     if (B < 0 || K < 0 || V < 1 || D < 1) return SV_ERR_INVALID_ARG;
     if (K > SV_MAX_DRAFT_LEN) return SV_ERR_UNSUPPORTED;
     if (B == 0) return SV_OK;
@@ -354,7 +354,7 @@ sv_status spec_verify_greedy_lmhead(const void *hidden, const void *lm_head,
     if (!aligned16(hidden) || !aligned16(lm_head) || !aligned256(workspace)) return SV_ERR_INVALID_ARG;
     if (workspace_bytes < sv_lmhead_workspace_bytes(static_cast<int>(rows), V)) return SV_ERR_WORKSPACE;
     uint64_t *pk = static_cast<uint64_t *>(workspace);
-    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipStream_t s = stream;
     hipError_t e = traced(SV_K_LMHEAD, s, [&] {
         return launch_lmhead_argmax(hidden, lm_head, static_cast<int>(rows), D, V, pk, s);
     });
@@ -370,7 +370,7 @@ sv_status spec_verify_tree_lmhead(const void *hidden, const void *lm_head,
                                   const int32_t *node_tokens, const int32_t *parents, int B, int N,
                                   int D, int V, int32_t *accept_len, int32_t *path_nodes,
                                   int32_t *out_tokens, int32_t *req_status, void *workspace,
-                                  size_t workspace_bytes, void *stream) {
+                                  size_t workspace_bytes, hipStream_t stream) {
     if (B < 0 || N < 1 || V < 1 || D < 1) return SV_ERR_INVALID_ARG;
     if (N > SV_MAX_TREE_NODES) return SV_ERR_UNSUPPORTED;
     if (B == 0) return SV_OK;
@@ -382,7 +382,7 @@ sv_status spec_verify_tree_lmhead(const void *hidden, const void *lm_head,
     if (!aligned16(hidden) || !aligned16(lm_head) || !aligned256(workspace)) return SV_ERR_INVALID_ARG;
     if (workspace_bytes < sv_lmhead_workspace_bytes(static_cast<int>(rows), V)) return SV_ERR_WORKSPACE;
     uint64_t *pk = static_cast<uint64_t *>(workspace);
-    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipStream_t s = stream;
     hipError_t e = traced(SV_K_LMHEAD, s, [&] {
         return launch_lmhead_argmax(hidden, lm_head, static_cast<int>(rows), D, V, pk, s);
     });
@@ -452,7 +452,7 @@ sv_status spec_verify_sample_lmhead(const void *hidden, const void *lm_head, con
                                     const float *u_sample, int B, int K, int D, int V, sv_dtype dt,
                                     float temperature, int32_t *accept_len, int32_t *out_tokens,
                                     float *lse_target, float *lse_draft, int32_t *req_status,
-                                    void *workspace, size_t workspace_bytes, void *stream) {
+                                    void *workspace, size_t workspace_bytes, hipStream_t stream) {
     if (!valid_dtype(dt)) return SV_ERR_UNSUPPORTED;
     if (B < 0 || K < 0 || V < 1 || D < 1 || !(temperature > 0.0f) || !isfinite(temperature))
         return SV_ERR_INVALID_ARG;
@@ -483,7 +483,7 @@ sv_status spec_verify_sample_lmhead(const void *hidden, const void *lm_head, con
     ResidParam *rp = reinterpret_cast<ResidParam *>(ws + L.rp);
     float *rows_p = reinterpret_cast<float *>(ws + L.rows_p);
     double *tiles = reinterpret_cast<double *>(ws + L.tiles);
-    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipStream_t s = stream;
 
     // 1. target rows: partials and the logit at each draft, from H W^T
     hipError_t e = traced(SV_K_LMHEAD_STATS, s, [&] {
@@ -540,7 +540,7 @@ size_t sv_ngram_workspace_bytes(int B, int L) {
 sv_status spec_ngram_candidates(const int32_t *context, int B, int L, const int32_t *lengths,
                                 const int32_t *queries, int n, int cap, int32_t *count,
                                 int32_t *positions, int32_t *req_status, void *workspace,
-                                size_t workspace_bytes, void *stream) {
+                                size_t workspace_bytes, hipStream_t stream) {
     if (B < 0 || L < 1 || n < 1 || cap < 0) return SV_ERR_INVALID_ARG;
     if (n > 64 || static_cast<long long>(B) * ngram_chunks(L) > 0x7fffffffLL) return SV_ERR_UNSUPPORTED;
     if (B == 0) return SV_OK;
@@ -548,7 +548,7 @@ sv_status spec_ngram_candidates(const int32_t *context, int B, int L, const int3
         return SV_ERR_INVALID_ARG;
     if (!aligned256(workspace)) return SV_ERR_INVALID_ARG;
     if (workspace_bytes < sv_ngram_workspace_bytes(B, L)) return SV_ERR_WORKSPACE;
-    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipStream_t s = stream;
     const hipError_t e = launch_ngram(context, B, L, lengths, queries, n, cap, static_cast<int32_t *>(workspace),
                                       count, positions, req_status, s);
     return e == hipSuccess ? SV_OK : SV_ERR_HIP;
@@ -557,7 +557,7 @@ sv_status spec_ngram_candidates(const int32_t *context, int B, int L, const int3
 sv_status spec_commit_tree_kv(const void *src_kv, void *dst_kv, int G, int B, int S, int row_bytes,
                               const int32_t *tree_base, const int32_t *commit_base,
                               const int32_t *accept_len, const int32_t *path_nodes, int N,
-                              int32_t *req_status, void *stream) {
+                              int32_t *req_status, hipStream_t stream) {
     if (G < 1 || B < 0 || S < 1 || N < 1 || row_bytes < 16 || row_bytes % 16 != 0)
         return SV_ERR_INVALID_ARG;
     if (N > SV_MAX_TREE_NODES || static_cast<long long>(G) * B > 0x7fffffffLL ||
@@ -569,7 +569,7 @@ sv_status spec_commit_tree_kv(const void *src_kv, void *dst_kv, int G, int B, in
     if (!src_kv || !dst_kv || !tree_base || !commit_base || !accept_len || !path_nodes)
         return SV_ERR_INVALID_ARG;
     if (!aligned16(src_kv) || !aligned16(dst_kv)) return SV_ERR_INVALID_ARG;
-    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipStream_t s = stream;
     const hipError_t e = traced(SV_K_COMMIT, s, [&] {
         return launch_commit(src_kv, dst_kv, G, B, S, row_bytes, tree_base, commit_base, accept_len,
                              path_nodes, N, req_status, s);
@@ -581,12 +581,12 @@ size_t sv_read_probe_folds(size_t bytes) {
     return static_cast<size_t>(read_probe_waves(static_cast<long long>(bytes / 16)));
 }
 
-sv_status sv_read_probe(const void *buf, size_t bytes, unsigned *folds, void *stream) {
+sv_status sv_read_probe(const void *buf, size_t bytes, unsigned *folds, hipStream_t stream) {
     if (bytes % 16 != 0) return SV_ERR_INVALID_ARG;
     if (bytes / 16 > (1ull << 40)) return SV_ERR_UNSUPPORTED;
     if (bytes == 0) return SV_OK;
     if (!buf || !folds || !aligned16(buf)) return SV_ERR_INVALID_ARG;
-    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipStream_t s = stream;
     const hipError_t e = traced(SV_K_READ_PROBE, s, [&] {
         return launch_read_probe(buf, static_cast<long long>(bytes / 16), folds, s);
     });

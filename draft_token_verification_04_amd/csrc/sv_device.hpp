@@ -249,6 +249,26 @@ __device__ __forceinline__ float fast_exp2(float a) { return __builtin_amdgcn_ex
 // The one ordering needed - a wave's shared stores complete before its next
 // counter update - comes from waiting on the wave's own outstanding memory
 // operations.  No wave ever waits for another.
+//
+// Why that is enough on gfx950.  In the LLVM AMDGPU memory model for
+// GFX942/GFX950, an agent-scope release is "buffer_wbl2 sc1; s_waitcnt
+// vmcnt(0)" before the releasing operation, and an agent-scope acquire is
+// "s_waitcnt vmcnt(0); buffer_inv sc1" after the acquiring one.  The L2
+// write-back and invalidate are there for ordinary (non-atomic) stores and
+// loads, which may sit in one XCD's L2.  Every word this hand-off shares is
+// written and read with agent-scope atomic instructions instead: relaxed
+// agent-scope loads and stores are emitted with the sc1 bit (the memory
+// model's coherent form for that scope) and read-modify-writes as global
+// atomics, the same instructions an acquire or release would use.  So the
+// release needs only the wait: on this gfx9-family part vmcnt counts stores
+// and atomics as well as loads, and it drops only when the memory system has
+// acknowledged them.  On the reading side, the loads of another wave's words
+// are control-dependent on the returned value of the ticket or mask atomic
+// (the branch that selects the deciding wave needs it), and a wave issues in
+// order without speculating past a branch, so they issue after it returns;
+// the logits they then read are inputs no kernel of the launch writes.
+// The waiting is an asm statement with a memory clobber, so the compiler can
+// move no memory access across it either.
 
 template <typename T>
 __device__ __forceinline__ void shared_store(T *p, T v) {
@@ -258,7 +278,9 @@ template <typename T>
 __device__ __forceinline__ T shared_load(T *p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void wait_own_stores() { __builtin_amdgcn_s_waitcnt(0); }
+__device__ __forceinline__ void wait_own_stores() {
+    asm volatile("s_waitcnt vmcnt(0) expcnt(0) lgkmcnt(0)" ::: "memory");
+}
 
 // Values every lane holds alike, moved to a scalar register so branches on
 // them are uniform.

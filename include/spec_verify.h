@@ -22,7 +22,7 @@
  * Conventions shared by all entry points:
  *   - Every pointer argument is a DEVICE pointer owned by the caller; the
  *     library keeps no reference after the call returns.
- *   - Calls are asynchronous on `stream` (a hipStream_t; 0 = the null stream).
+ *   - Calls are asynchronous on `stream` (NULL = the null stream).
  *     They return after enqueueing; results are valid once the stream reaches
  *     that point.
  *   - Scalar and pointer arguments are checked on the host before anything is
@@ -48,6 +48,13 @@
 
 #include <stddef.h>
 #include <stdint.h>
+
+/* The HIP stream handle, declared here as the HIP runtime declares it so that
+ * this header needs no HIP header; a C99 translation unit that also includes
+ * the HIP runtime header includes that one first. */
+#ifndef HIP_INCLUDE_HIP_HIP_RUNTIME_API_H
+typedef struct ihipStream_t *hipStream_t;
+#endif
 
 #ifdef __cplusplus
 extern "C" {
@@ -120,7 +127,7 @@ sv_status spec_verify_sample(const void *target_logits, const void *draft_logits
                              const float *u_sample, int B, int K, int V, sv_dtype dt,
                              float temperature, int32_t *accept_len, int32_t *out_tokens,
                              float *lse_target, float *lse_draft, int32_t *req_status,
-                             void *workspace, size_t workspace_bytes, void *stream);
+                             void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Greedy chain verification.
@@ -138,7 +145,7 @@ sv_status spec_verify_sample(const void *target_logits, const void *draft_logits
 sv_status spec_verify_greedy(const void *target_logits, const int32_t *draft_tokens, int B, int K,
                              int V, sv_dtype dt, int32_t *accept_len, int32_t *out_tokens,
                              int32_t *req_status, void *workspace, size_t workspace_bytes,
-                             void *stream);
+                             hipStream_t stream);
 
 /*
  * Greedy tree verification (AdaPLD-style draft trees).
@@ -170,7 +177,7 @@ sv_status spec_verify_tree(const void *target_logits, const int32_t *node_tokens
                            const int32_t *parents, int B, int N, int V, sv_dtype dt,
                            int32_t *accept_len, int32_t *path_nodes, int32_t *out_tokens,
                            int32_t *req_status, void *workspace, size_t workspace_bytes,
-                           void *stream);
+                           hipStream_t stream);
 
 /*
  * Greedy verification fused with the target's LM-head projection: the logits
@@ -196,13 +203,13 @@ size_t sv_lmhead_workspace_bytes(int rows, int V);
 sv_status spec_verify_greedy_lmhead(const void *hidden, const void *lm_head,
                                     const int32_t *draft_tokens, int B, int K, int D, int V,
                                     int32_t *accept_len, int32_t *out_tokens, int32_t *req_status,
-                                    void *workspace, size_t workspace_bytes, void *stream);
+                                    void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 sv_status spec_verify_tree_lmhead(const void *hidden, const void *lm_head,
                                   const int32_t *node_tokens, const int32_t *parents, int B, int N,
                                   int D, int V, int32_t *accept_len, int32_t *path_nodes,
                                   int32_t *out_tokens, int32_t *req_status, void *workspace,
-                                  size_t workspace_bytes, void *stream);
+                                  size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Stochastic chain verification (speculative sampling) fused with the target's
@@ -235,7 +242,7 @@ sv_status spec_verify_sample_lmhead(const void *hidden, const void *lm_head, con
                                     const float *u_sample, int B, int K, int D, int V, sv_dtype dt,
                                     float temperature, int32_t *accept_len, int32_t *out_tokens,
                                     float *lse_target, float *lse_draft, int32_t *req_status,
-                                    void *workspace, size_t workspace_bytes, void *stream);
+                                    void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Commit of a verified draft tree's accepted path in the target's KV cache
@@ -268,7 +275,7 @@ sv_status spec_verify_sample_lmhead(const void *hidden, const void *lm_head, con
 sv_status spec_commit_tree_kv(const void *src_kv, void *dst_kv, int G, int B, int S, int row_bytes,
                               const int32_t *tree_base, const int32_t *commit_base,
                               const int32_t *accept_len, const int32_t *path_nodes, int N,
-                              int32_t *req_status, void *stream);
+                              int32_t *req_status, hipStream_t stream);
 
 /*
  * AdaPLD lexical retrieval (AdaPLD page, section 3.2 and Algorithm 1,
@@ -293,7 +300,7 @@ size_t sv_ngram_workspace_bytes(int B, int L);
 sv_status spec_ngram_candidates(const int32_t *context, int B, int L, const int32_t *lengths,
                                 const int32_t *queries, int n, int cap, int32_t *count,
                                 int32_t *positions, int32_t *req_status, void *workspace,
-                                size_t workspace_bytes, void *stream);
+                                size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Measurement aid, not a step of the method: reads the `bytes` bytes at `buf`
@@ -305,7 +312,7 @@ sv_status spec_ngram_candidates(const int32_t *context, int B, int L, const int3
  * (kernel SV_K_READ_PROBE) it gives the read rate this device reaches.
  */
 size_t sv_read_probe_folds(size_t bytes);
-sv_status sv_read_probe(const void *buf, size_t bytes, unsigned *folds, void *stream);
+sv_status sv_read_probe(const void *buf, size_t bytes, unsigned *folds, hipStream_t stream);
 
 /* Human-readable name of a status code (static storage). */
 const char *sv_status_string(sv_status s);

@@ -278,10 +278,11 @@ def test_header_is_plain_c_and_links(tmp_path):
         '#include "spec_verify.h"\n'
         "#include <stdio.h>\n"
         "int main(void) {\n"
+        "    hipStream_t none = NULL; /* the header declares the stream type itself */\n"
         "    size_t a = sv_sample_workspace_bytes(256, 7, 151936, SV_BF16);\n"
         "    size_t b = sv_greedy_workspace_bytes(64, 33, 151936, SV_BF16);\n"
         "    printf(\"%s %zu %zu %s\\n\", sv_version(), a, b, sv_status_string(SV_ERR_WORKSPACE));\n"
-        "    return (a > 0 && b > 0) ? 0 : 1;\n"
+        "    return (a > 0 && b > 0 && none == NULL) ? 0 : 1;\n"
         "}\n")
     exe = tmp_path / "abi"
     libdir = os.path.dirname(sv.LIB_PATH)
@@ -290,3 +291,43 @@ def test_header_is_plain_c_and_links(tmp_path):
                    check=True)
     out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout
     assert "gfx950" in out and "workspace too small" in out
+
+
+def test_header_after_the_hip_runtime_header_compiles_as_c99(tmp_path):
+    # a C caller that includes the HIP runtime header first (the GPU C-caller
+    # test's program) compiles as C99 with warnings as errors: the header's own
+    # stream typedef steps aside for HIP's
+    import shutil
+    import subprocess
+
+    cc = shutil.which("gcc") or shutil.which("cc")
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    if cc is None or not os.path.exists(os.path.join(rocm, "include", "hip", "hip_runtime_api.h")):
+        pytest.skip("no C compiler or HIP headers")
+    here = os.path.dirname(os.path.abspath(__file__))
+    subprocess.run([cc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+                    f"-I{rocm}/include", f"-I{os.path.dirname(HEADER)}", "-c",
+                    os.path.join(here, "c_greedy_check.c"), "-o", str(tmp_path / "c.o")], check=True)
+
+
+def test_a_touched_source_makes_the_build_stale(tmp_path, monkeypatch):
+    # the build records a hash of its sources and flags; a changed source makes
+    # the library stale, so smoke() and bench.py rebuild before loading it
+    import shutil
+
+    from draft_token_verification_04_amd import build as hb
+
+    csrc, inc = tmp_path / "csrc", tmp_path / "include"
+    shutil.copytree(hb.CSRC, csrc, ignore=shutil.ignore_patterns("*.so", "__pycache__"))
+    shutil.copytree(hb.INCLUDE, inc)
+    monkeypatch.setattr(hb, "CSRC", str(csrc))
+    monkeypatch.setattr(hb, "INCLUDE", str(inc))
+    out = tmp_path / "lib.so"
+    out.write_bytes(b"built")
+    assert not hb.is_current(str(out))  # no record yet
+    with open(hb.digest_path(str(out)), "w") as f:
+        f.write(hb.source_digest() + "\n")
+    assert hb.is_current(str(out))
+    with open(csrc / "sv_greedy.hip", "a") as f:
+        f.write("\n// touched\n")
+    assert not hb.is_current(str(out))
