@@ -27,7 +27,8 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libspecverify.so")
 
-SV_OK, SV_ERR_INVALID_ARG, SV_ERR_UNSUPPORTED, SV_ERR_WORKSPACE, SV_ERR_HIP = range(5)
+SV_OK, SV_ERR_INVALID_ARG, SV_ERR_UNSUPPORTED, SV_ERR_WORKSPACE, SV_ERR_HIP, SV_ERR_SCRATCH = range(6)
+SV_NOALLOC_SCRATCH_BYTES = 8 << 20
 SV_F32, SV_BF16 = 0, 1
 SV_MAX_TREE_NODES = 2048
 KERNELS = ("rowstats", "accept", "resid_mass", "resid_select", "argmax", "match", "tree",
@@ -39,7 +40,7 @@ EXPORTS = ("sv_sample_workspace_bytes", "sv_greedy_workspace_bytes", "spec_verif
            "sv_version", "sv_lmhead_workspace_bytes", "spec_verify_greedy_lmhead",
            "spec_verify_tree_lmhead", "sv_ngram_workspace_bytes", "spec_ngram_candidates",
            "sv_read_probe", "sv_read_probe_folds", "sv_trace_begin", "sv_trace_end", "sv_kernel_name",
-           "sv_sample_lmhead_workspace_bytes", "spec_verify_sample_lmhead")
+           "sv_sample_lmhead_workspace_bytes", "spec_verify_sample_lmhead", "spec_verify_sample_noalloc")
 
 
 class SpecVerifyError(RuntimeError):
@@ -70,6 +71,8 @@ def load_library(path: str = LIB_PATH):
     lib.sv_greedy_workspace_bytes.restype = Z
     lib.spec_verify_sample.argtypes = [P, P, P, P, P, I, I, I, I, ctypes.c_float, P, P, P, P, P, P, Z, P]
     lib.spec_verify_sample.restype = I
+    lib.spec_verify_sample_noalloc.argtypes = [P, P, P, P, P, I, I, I, I, ctypes.c_float, P, P, P, P, P, P]
+    lib.spec_verify_sample_noalloc.restype = I
     lib.spec_verify_greedy.argtypes = [P, P, I, I, I, I, P, P, P, P, Z, P]
     lib.spec_verify_greedy.restype = I
     lib.spec_verify_tree.argtypes = [P, P, P, I, I, I, I, P, P, P, P, P, Z, P]
@@ -246,6 +249,57 @@ def spec_verify_sample(target, draft, draft_tokens, u_accept, u_sample, temperat
     if rc != SV_OK:
         raise SpecVerifyError(rc, "spec_verify_sample")
     _hold(torch, dev, stream, ws if workspace is None else None, *out.values())
+    return out
+
+
+def spec_verify_sample_noalloc(target, draft, draft_tokens, u_accept, u_sample, temperature, *,
+                               lse=True, status=True, out=None, stream=None):
+    """spec_verify_sample through the entry point that allocates nothing: its
+    workspace is the library's static scratch of the current device (calls
+    that overlap on one device race on it).  ``out`` may hold preallocated
+    outputs (the dict spec_verify_sample returns); the binding allocates any
+    that are missing.  Returns that dict."""
+    torch = _torch()
+    lib = load_library()
+    _check(target, "target", 3)
+    dev = target.device
+    B, K1, V = target.shape
+    K = K1 - 1
+    dt = _dtype_code(target)
+    if K > 0:
+        _check(draft, "draft", 3, target.dtype, dev)
+        if tuple(draft.shape) != (B, K, V):
+            raise ValueError(f"draft must be [{B},{K},{V}], got {tuple(draft.shape)}")
+        _check(draft_tokens, "draft_tokens", 2, torch.int32, dev)
+        _check(u_accept, "u_accept", 2, torch.float32, dev)
+        if tuple(draft_tokens.shape) != (B, K) or tuple(u_accept.shape) != (B, K):
+            raise ValueError("draft_tokens and u_accept must be [B, K]")
+    _check(u_sample, "u_sample", 2, torch.float32, dev)
+    if tuple(u_sample.shape) != (B, K + 1):
+        raise ValueError("u_sample must be [B, K+1]")
+    out = dict(out or {})
+    shapes = {"accept_len": ((B,), torch.int32), "tokens": ((B, K + 1), torch.int32)}
+    if lse:
+        shapes.update(lse_target=((B, K + 1), torch.float32), lse_draft=((B, K), torch.float32))
+    if status:
+        shapes["status"] = ((B,), torch.int32)
+    for name, (shape, dtype) in shapes.items():
+        if name in out:
+            _check(out[name], name, len(shape), dtype, dev)
+            if tuple(out[name].shape) != shape:
+                raise ValueError(f"{name} must be {list(shape)}")
+        else:
+            out[name] = torch.empty(shape, dtype=dtype, device=dev)
+    with torch.cuda.device(dev):
+        rc = lib.spec_verify_sample_noalloc(
+            _ptr(target), _ptr(draft if K > 0 else None), _ptr(draft_tokens if K > 0 else None),
+            _ptr(u_accept if K > 0 else None), _ptr(u_sample), B, K, V, dt, float(temperature),
+            _ptr(out["accept_len"]), _ptr(out["tokens"]), _ptr(out.get("lse_target") if lse else None),
+            _ptr(out.get("lse_draft") if lse else None), _ptr(out.get("status") if status else None),
+            _stream(torch, dev, stream))
+    if rc != SV_OK:
+        raise SpecVerifyError(rc, "spec_verify_sample_noalloc")
+    _hold(torch, dev, stream, *out.values())
     return out
 
 

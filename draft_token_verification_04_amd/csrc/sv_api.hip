@@ -179,27 +179,44 @@ size_t sv_greedy_workspace_bytes(int B, int rows_per_req, int V, sv_dtype dt) {
     return greedy_ws_layout(B, rows_per_req, g).total;
 }
 
-sv_status spec_verify_sample(const void *target_logits, const void *draft_logits,
-                             const int32_t *draft_tokens, const float *u_accept,
-                             const float *u_sample, int B, int K, int V, sv_dtype dt,
-                             float temperature, int32_t *accept_len, int32_t *out_tokens,
-                             float *lse_target, float *lse_draft, int32_t *req_status,
-                             void *workspace, size_t workspace_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Where a sample call's workspace comes from: the caller's buffer, or the
+// library's own scratch array of the current device (resolved only after
+// every host-side check has passed, so a rejected call touches no device).
+struct WsSource {
+    void *buf;
+    size_t bytes;
+    bool scratch;
+};
+
+sv_status device_scratch(void **out);
+
+sv_status sample_impl(const void *target_logits, const void *draft_logits, const int32_t *draft_tokens,
+                      const float *u_accept, const float *u_sample, int B, int K, int V, sv_dtype dt,
+                      float temperature, int32_t *accept_len, int32_t *out_tokens, float *lse_target,
+                      float *lse_draft, int32_t *req_status, WsSource src, hipStream_t stream) {
     if (!valid_dtype(dt)) return SV_ERR_UNSUPPORTED;
     if (B < 0 || K < 0 || V < 1 || !(temperature > 0.0f) || !isfinite(temperature))
         return SV_ERR_INVALID_ARG;
     if (K > SV_MAX_DRAFT_LEN || !sizes_ok(B, 2LL * K + 1, V)) return SV_ERR_UNSUPPORTED;
     if (B == 0) return SV_OK;
-    if (!target_logits || !u_sample || !accept_len || !out_tokens || !workspace)
+    if (!target_logits || !u_sample || !accept_len || !out_tokens || (!src.scratch && !src.buf))
         return SV_ERR_INVALID_ARG;
     if (K > 0 && (!draft_logits || !draft_tokens || !u_accept)) return SV_ERR_INVALID_ARG;
-    if (!aligned256(workspace)) return SV_ERR_INVALID_ARG;
+    if (!src.scratch && !aligned256(src.buf)) return SV_ERR_INVALID_ARG;
     const bool ptr_al = aligned16(target_logits) && (K == 0 || aligned16(draft_logits));
     const RowGeom g = row_geom(V, dt, ptr_al, kStatsVecsPerLane);
     const SampleWs L = sample_ws_layout(B, K, g);
-    if (workspace_bytes < L.total) return SV_ERR_WORKSPACE;
+    if (src.bytes < L.total) return src.scratch ? SV_ERR_SCRATCH : SV_ERR_WORKSPACE;
+    if (src.scratch) {
+        const sv_status st = device_scratch(&src.buf);
+        if (st != SV_OK) return st;
+    }
 
-    char *ws = static_cast<char *>(workspace);
+    char *ws = static_cast<char *>(src.buf);
     float *part_R = reinterpret_cast<float *>(ws + L.part_R);
     double *part_s = reinterpret_cast<double *>(ws + L.part_s);
     double *L2 = reinterpret_cast<double *>(ws + L.L2);
@@ -242,6 +259,62 @@ sv_status spec_verify_sample(const void *target_logits, const void *draft_logits
                                        out_tokens, s);
         });
     return e == hipSuccess ? SV_OK : SV_ERR_HIP;
+}
+
+}  // namespace
+
+// ---- the sampler's scratch for callers that cannot allocate ------------------------
+//
+// One array per device, loaded with the library's code object.  Host code
+// never passes `scratch` itself to a kernel (on the host it names a stand-in,
+// not device memory): each device's address comes from hipGetSymbolAddress,
+// taken once with that device current and kept below.
+static __device__ __align__(256) unsigned char scratch[SV_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxScratchDevices];
+
+sv_status device_scratch(void **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return SV_ERR_HIP;
+    if (dev < 0 || dev >= kMaxScratchDevices) return SV_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> g(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return SV_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return SV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+sv_status spec_verify_sample(const void *target_logits, const void *draft_logits,
+                             const int32_t *draft_tokens, const float *u_accept,
+                             const float *u_sample, int B, int K, int V, sv_dtype dt,
+                             float temperature, int32_t *accept_len, int32_t *out_tokens,
+                             float *lse_target, float *lse_draft, int32_t *req_status,
+                             void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    return sample_impl(target_logits, draft_logits, draft_tokens, u_accept, u_sample, B, K, V, dt,
+                       temperature, accept_len, out_tokens, lse_target, lse_draft, req_status,
+                       WsSource{workspace, workspace_bytes, false}, stream);
+}
+
+sv_status spec_verify_sample_noalloc(const void *target_logits, const void *draft_logits,
+                                     const int32_t *draft_tokens, const float *u_accept,
+                                     const float *u_sample, int B, int K, int V, sv_dtype dt,
+                                     float temperature, int32_t *accept_len, int32_t *out_tokens,
+                                     float *lse_target, float *lse_draft, int32_t *req_status,
+                                     hipStream_t stream) {
+    return sample_impl(target_logits, draft_logits, draft_tokens, u_accept, u_sample, B, K, V, dt,
+                       temperature, accept_len, out_tokens, lse_target, lse_draft, req_status,
+                       WsSource{nullptr, SV_NOALLOC_SCRATCH_BYTES, true}, stream);
 }
 
 sv_status spec_verify_greedy(const void *target_logits, const int32_t *draft_tokens, int B, int K,
@@ -600,6 +673,7 @@ const char *sv_status_string(sv_status st) {
         case SV_ERR_UNSUPPORTED: return "unsupported dtype or size";
         case SV_ERR_WORKSPACE: return "workspace too small";
         case SV_ERR_HIP: return "HIP runtime error";
+        case SV_ERR_SCRATCH: return "sizes need more than the library's static scratch";
     }
     return "unknown status";
 }

@@ -65,7 +65,9 @@ typedef enum {
     SV_ERR_INVALID_ARG = 1, /* bad scalar, NULL required pointer, misaligned workspace */
     SV_ERR_UNSUPPORTED = 2, /* dtype other than SV_F32/SV_BF16, or a size above a limit */
     SV_ERR_WORKSPACE = 3,   /* workspace_bytes below the required size */
-    SV_ERR_HIP = 4          /* the HIP runtime reported an error while enqueueing */
+    SV_ERR_HIP = 4,         /* the HIP runtime reported an error while enqueueing */
+    SV_ERR_SCRATCH = 5      /* spec_verify_sample_noalloc: the sizes need more than
+                               SV_NOALLOC_SCRATCH_BYTES of scratch */
 } sv_status;
 
 typedef enum { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
@@ -128,6 +130,35 @@ sv_status spec_verify_sample(const void *target_logits, const void *draft_logits
                              float temperature, int32_t *accept_len, int32_t *out_tokens,
                              float *lse_target, float *lse_draft, int32_t *req_status,
                              void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * spec_verify_sample without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * and harnesses that forbid allocation.  The call itself allocates nothing.
+ *
+ * Arguments, outputs, rows read and results are those of spec_verify_sample
+ * (the same kernels run), with the workspace taken from a scratch array of
+ * SV_NOALLOC_SCRATCH_BYTES (8 MiB) that the library holds in the device memory
+ * of every GPU it runs on, from the library's load until the process ends.
+ * The array of the current device is used, so `stream` must belong to the
+ * current device.  Sizes whose workspace (sv_sample_workspace_bytes) exceeds
+ * SV_NOALLOC_SCRATCH_BYTES return SV_ERR_SCRATCH and launch nothing; at
+ * V = 151936 bf16 and K = 7 that admits B up to about 1390.
+ *
+ * Every call on one device shares that device's array, which keeps the last
+ * call's contents (the kernels clear what must start at zero themselves):
+ * calls that overlap on one device - on two streams, or from two host threads
+ * without ordering between their streams - race on it and give wrong results.
+ * The first call on each device looks up the array's address there
+ * (hipGetSymbolAddress) and may return SV_ERR_HIP if that fails.
+ */
+#define SV_NOALLOC_SCRATCH_BYTES 8388608
+sv_status spec_verify_sample_noalloc(const void *target_logits, const void *draft_logits,
+                                     const int32_t *draft_tokens, const float *u_accept,
+                                     const float *u_sample, int B, int K, int V, sv_dtype dt,
+                                     float temperature, int32_t *accept_len, int32_t *out_tokens,
+                                     float *lse_target, float *lse_draft, int32_t *req_status,
+                                     hipStream_t stream);
 
 /*
  * Greedy chain verification.

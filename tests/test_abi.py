@@ -37,8 +37,8 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_version_and_status_strings(lib):
     assert b"gfx950" in lib.sv_version()
-    for code in range(5):
-        assert lib.sv_status_string(code)
+    for code in range(6):
+        assert lib.sv_status_string(code) != b"unknown status"
     assert lib.sv_kernel_name(0) == b"rowstats"
     assert lib.sv_kernel_name(99) == b"unknown"
 
@@ -66,7 +66,7 @@ def test_binding_constants_match_the_header():
     consts = {m.group(1): int(m.group(2)) for m in re.finditer(r"\b(SV_[A-Z0-9_]+)\s*=\s*(\d+)", text)}
     consts.update({m.group(1): int(m.group(2)) for m in re.finditer(r"#define\s+(SV_[A-Z_]+)\s+(\d+)", text)})
     for name in ("SV_OK", "SV_ERR_INVALID_ARG", "SV_ERR_UNSUPPORTED", "SV_ERR_WORKSPACE", "SV_ERR_HIP",
-                 "SV_F32", "SV_BF16", "SV_MAX_TREE_NODES"):
+                 "SV_ERR_SCRATCH", "SV_F32", "SV_BF16", "SV_MAX_TREE_NODES", "SV_NOALLOC_SCRATCH_BYTES"):
         assert getattr(sv, name) == consts[name], name
 
 
@@ -331,3 +331,20 @@ def test_a_touched_source_makes_the_build_stale(tmp_path, monkeypatch):
     with open(csrc / "sv_greedy.hip", "a") as f:
         f.write("\n// touched\n")
     assert not hb.is_current(str(out))
+
+
+def test_noalloc_sample_rejects_sizes_beyond_its_scratch(lib):
+    # checked on the host before the device is touched: no GPU needed
+    V = 151936
+    need = lib.sv_sample_workspace_bytes(2048, 7, V, sv.SV_BF16)
+    assert need > sv.SV_NOALLOC_SCRATCH_BYTES
+    F = ctypes.c_void_p(4096)
+    args = (F, F, F, F, F)
+    outs = (F, F, None, None, None, None)
+    assert lib.spec_verify_sample_noalloc(*args, 2048, 7, V, sv.SV_BF16, ctypes.c_float(1.0), *outs) \
+        == sv.SV_ERR_SCRATCH
+    assert b"scratch" in lib.sv_status_string(sv.SV_ERR_SCRATCH)
+    # the usual argument checks come first, and B = 0 is a no-op
+    assert lib.spec_verify_sample_noalloc(*args, 4, 7, V, sv.SV_BF16, ctypes.c_float(0.0), *outs) \
+        == sv.SV_ERR_INVALID_ARG
+    assert lib.spec_verify_sample_noalloc(*args, 0, 7, V, sv.SV_BF16, ctypes.c_float(1.0), *outs) == sv.SV_OK
