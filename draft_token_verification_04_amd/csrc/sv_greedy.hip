@@ -373,10 +373,33 @@ __global__ __launch_bounds__(kBlock) void k_skip_argmax(const typename E::storag
     const int32_t *xb = drafts + static_cast<long long>(b) * K;
     uint64_t bits = 1ull << p;
     if (p < K && uniform(xb[p]) != a) bits |= 1ull << (32 + p);
+#if SV_SKIP_FASTDECIDE
+    // amax holds each decided row's argmax plus one (0: not yet known); the
+    // store need not land before the decision, the finisher polls for it
+    uint64_t old = 0;
+    if (lane == 0) {
+        shared_store(&amax[row], a + 1);
+        old = __hip_atomic_fetch_or(&ctl.mask[b], bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    old = uniform(static_cast<uint64_t>(__shfl(static_cast<long long>(old), 0, kWave)));
+    if (skip_prefix(old, K) >= 0) return;  // the request was complete already
+    const int n = skip_prefix(old | bits, K);
+    if (n < 0) return;
+    int an = a;
+    if (n != p) {
+        int v = 0;
+        if (lane == 0) {
+            int32_t *w = &amax[static_cast<long long>(b) * (K + 1) + n];
+            for (int t = 0; t < (1 << 22) && (v = shared_load(w)) == 0; ++t) __builtin_amdgcn_s_sleep(1);
+        }
+        an = uniform(__shfl(v, 0, kWave)) - 1;
+    }
+#else
     if (lane == 0) shared_store(&amax[row], a);
     const int n = skip_decide(ctl, b, K, bits, lane);
     if (n < 0) return;
     const int an = n == p ? a : uniform(shared_load(&amax[static_cast<long long>(b) * (K + 1) + n]));
+#endif
     bool bad = false;
     int32_t *tok = out_tokens + static_cast<long long>(b) * (K + 1);
     for (int i = lane; i <= K; i += kWave) {
@@ -656,7 +679,15 @@ hipError_t launch_skip_match(const void *L, const int32_t *drafts, int B, int K,
                              void *ctl_base, int32_t *accept_len, int32_t *out_tokens,
                              int32_t *status, hipStream_t s) {
     SkipCtl ctl;
+#if SV_SKIP_FASTDECIDE
+    // the argmax words (placed just before the control words) start at 0 too
+    skip_ctl_carve(ctl_base, B, K, &ctl);
+    const size_t span = static_cast<size_t>(static_cast<char *>(ctl_base) - reinterpret_cast<char *>(amax)) +
+                        skip_ctl_bytes(B, K);
+    hipError_t e = clear_words(amax, span, s);
+#else
     hipError_t e = skip_ctl_init(ctl_base, B, K, &ctl, s);
+#endif
     if (e != hipSuccess) return e;
     trace_select(SV_K_SKIP_ARGMAX);
 #define SV_SK(E, A) skip_argmax_t<E, A>(L, drafts, B, K, V, g, part_k, amax, ctl, accept_len, out_tokens, status, s)

@@ -53,6 +53,14 @@ constexpr int kSkipChunks = SV_SKIP_CHUNKS;
 #define SV_GSKIP_CHUNKS 2
 #endif
 constexpr int kGSkipVecsPerLane = SV_GSKIP_VECS;
+// The greedy chain's skip pass records decisions with one atomic OR (the
+// decision that completes a request's decided prefix finishes it) and keeps
+// row argmaxes plus one, polled by the finisher (0: decide and wait as the
+// stochastic pass does).
+#ifndef SV_SKIP_FASTDECIDE
+#define SV_SKIP_FASTDECIDE 1
+#endif
+
 constexpr int kGSkipChunks = SV_GSKIP_CHUNKS;
 // Waves the residual-mass pass aims for: short waves of a few tiles each
 // (measured: 28 us per pass at B=256 against 32 us with 4096 longer waves).

@@ -834,12 +834,16 @@ hipError_t clear_words(void *base, size_t bytes, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t skip_ctl_init(void *base, int B, int K, SkipCtl *ctl, hipStream_t s) {
+void skip_ctl_carve(void *base, int B, int K, SkipCtl *ctl) {
     char *q = static_cast<char *>(base);
     ctl->mask = reinterpret_cast<uint64_t *>(q);
     ctl->ticket = reinterpret_cast<unsigned *>(ctl->mask + B);
     ctl->won = ctl->ticket + static_cast<size_t>(B) * (K + 1);
     ctl->finished = ctl->won + B;
+}
+
+hipError_t skip_ctl_init(void *base, int B, int K, SkipCtl *ctl, hipStream_t s) {
+    skip_ctl_carve(base, B, K, ctl);
     return clear_words(base, skip_ctl_bytes(B, K), s);
 }
 

@@ -13,7 +13,10 @@
 // (position K's bit means its bonus row is ready).  The request is decided once
 // the mask holds a rejection with every earlier position decided, or every
 // position 0..K decided without one; whichever decider completes that prefix
-// finishes the request (one winner by compare-and-swap) and raises the flag.
+// finishes the request and raises the flag.  The stochastic pass picks that
+// decider by compare-and-swap after its decision; the greedy pass takes the
+// one whose atomic OR turned the prefix from undecided to decided (at most one
+// can: see skip_prefix), which saves that round trip.
 // Rows of positions after the first rejection are read only by waves that
 // started before the decision was known.  Nothing waits.
 #pragma once
@@ -63,6 +66,26 @@ __device__ __forceinline__ bool skip_row_dead(const SkipCtl &ctl, int b, int p) 
 constexpr double kEarlySkipPositionBytes = 110e6;
 inline bool skip_early(int B, int rows_per_position, int V, size_t elem) {
     return static_cast<double>(B) * rows_per_position * V * static_cast<double>(elem) >= kEarlySkipPositionBytes;
+}
+
+// Carves the control words of a B x K chain out of `base` without clearing
+// them (the caller clears them together with other words).
+void skip_ctl_carve(void *base, int B, int K, SkipCtl *ctl);
+
+// The decided prefix of a request mask: the accepted length n once every
+// position up to the first rejection (or every position 0..K) is decided, else
+// -1.  Monotone: a mask with more bits set has the same prefix once it has one,
+// so among the decisions recorded with atomic ORs exactly one turns it from -1
+// into n.
+__device__ __forceinline__ int skip_prefix(uint64_t m, int K) {
+    const unsigned decided = static_cast<unsigned>(m), rejected = static_cast<unsigned>(m >> 32);
+    if (rejected) {
+        const int rj = __ffs(static_cast<int>(rejected)) - 1;
+        const unsigned below = rj == 0 ? 0u : (0xffffffffu >> (32 - rj));
+        return (decided & below) == below ? rj : -1;
+    }
+    const unsigned all = K == 31 ? 0xffffffffu : ((1u << (K + 1)) - 1u);
+    return (decided & all) == all ? K : -1;
 }
 
 // Records position p's decision `bits` (1 << p, plus 1 << (32 + p) for a
