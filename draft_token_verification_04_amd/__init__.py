@@ -25,7 +25,9 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libspecverify.so")
+# SPECVERIFY_LIB names another build of the library to load (the sanitizer
+# build of the host code, for instance); by default the in-tree one.
+LIB_PATH = os.environ.get("SPECVERIFY_LIB") or os.path.join(HERE, "libspecverify.so")
 
 SV_OK, SV_ERR_INVALID_ARG, SV_ERR_UNSUPPORTED, SV_ERR_WORKSPACE, SV_ERR_HIP, SV_ERR_SCRATCH = range(6)
 SV_NOALLOC_SCRATCH_BYTES = 8 << 20

@@ -674,6 +674,7 @@ const char *sv_status_string(sv_status st) {
         case SV_ERR_WORKSPACE: return "workspace too small";
         case SV_ERR_HIP: return "HIP runtime error";
         case SV_ERR_SCRATCH: return "sizes need more than the library's static scratch";
+        default: break;
     }
     return "unknown status";
 }

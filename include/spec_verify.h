@@ -66,11 +66,20 @@ typedef enum {
     SV_ERR_UNSUPPORTED = 2, /* dtype other than SV_F32/SV_BF16, or a size above a limit */
     SV_ERR_WORKSPACE = 3,   /* workspace_bytes below the required size */
     SV_ERR_HIP = 4,         /* the HIP runtime reported an error while enqueueing */
-    SV_ERR_SCRATCH = 5      /* spec_verify_sample_noalloc: the sizes need more than
+    SV_ERR_SCRATCH = 5,     /* spec_verify_sample_noalloc: the sizes need more than
                                SV_NOALLOC_SCRATCH_BYTES of scratch */
+    /* not statuses: they make the type span every int, so that any int a caller
+       passes is a value of the type (the library rejects those it does not know) */
+    SV_STATUS_MIN_ENUM = -0x7fffffff - 1,
+    SV_STATUS_MAX_ENUM = 0x7fffffff
 } sv_status;
 
-typedef enum { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
+typedef enum {
+    SV_F32 = 0,
+    SV_BF16 = 1,
+    SV_DTYPE_MIN_ENUM = -0x7fffffff - 1, /* not dtypes: the type spans every int */
+    SV_DTYPE_MAX_ENUM = 0x7fffffff
+} sv_dtype;
 
 /* Largest tree (nodes per request) spec_verify_tree accepts. */
 #define SV_MAX_TREE_NODES 2048
