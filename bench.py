@@ -228,6 +228,16 @@ def tree_needed_rows(torch, target, w5):
 
 
 def cpu_model() -> str:
+    """The host CPU's model name as lscpu prints it (/proc/cpuinfo if lscpu is absent)."""
+    import subprocess
+
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.strip().startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
@@ -238,22 +248,38 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def cpu_baseline(w3, w4, w5, mode, threads, runs=3):
-    """The oracle, as it stands, on the same step's inputs (wall time, median of `runs`)."""
+def cpu_baseline(w3, w4, w5, mode, threads, runs=3, keep=None):
+    """The oracle, as it stands, on the same step's inputs (wall time, median of
+    `runs`).  When `keep` is a dict, the first run's stochastic outputs go in it."""
     import oracle
 
     times = []
-    for _ in range(runs):
+    for r in range(runs):
         t0 = time.perf_counter()
         if mode in ("all", "sample"):
-            oracle.verify_sample(w3.target, w3.draft, w3.draft_tokens, w3.u_accept, w3.u_sample, w3.T,
-                                 threads=threads)
+            o = oracle.verify_sample(w3.target, w3.draft, w3.draft_tokens, w3.u_accept, w3.u_sample, w3.T,
+                                     threads=threads)
+            if keep is not None and r == 0:
+                keep["sample_b256_k7_qwen3_t07"] = o
         if mode in ("all", "greedy"):
             oracle.verify_greedy(w4.target, w4.draft_tokens, threads=threads)
         if mode in ("all", "tree"):
             oracle.verify_tree(w5.target, w5.node_tokens, w5.parents, threads=threads)
         times.append(time.perf_counter() - t0)
     return statistics.median(times)
+
+
+def sample_parity(gpu, o, eps=1e-6):
+    """Exact-match counts of a stochastic workload against the oracle: requests
+    compared (every consumed draw farther than eps from its boundary), flagged,
+    flagged and different, and unflagged and different (must be 0)."""
+    import numpy as np
+
+    flagged = o["margin"] <= eps
+    diff = (gpu["accept_len"] != o["accept_len"]) | (gpu["tokens"] != o["tokens"]).any(1)
+    return {"requests": int(len(flagged)), "compared": int((~flagged).sum()), "flagged": int(flagged.sum()),
+            "flagged_and_different": int((flagged & diff).sum()),
+            "unflagged_and_different": int((~flagged & diff).sum())}
 
 
 def bench_ngram(sv, torch, workloads, dev, reps):
@@ -347,7 +373,6 @@ def bench_greedy_b512(sv, torch, workloads, dev, per_call, with_cold, reps):
              "dense_bytes": rows * R, "gbps": round(nbytes / (ms * 1e-3) / 1e9, 1),
              "mean_tokens_per_round": round(float(n_b.mean() + 1), 4)}
     with_cold(entry, call, nbytes, rows)
-    entry["cold_dense_gbps"] = round(rows * R / (entry["cold_ms"]["median"] * 1e-3) / 1e9, 1)
     del t
     return entry
 
@@ -377,14 +402,114 @@ def bench_vocab_shard(sv, torch, workloads, dev, per_call, with_cold, reps):
         ms = per_call(fn, reps)
         e = {"ms": round(ms, 5), "rows_per_s": round(rows / (ms * 1e-3), 1)}
         with_cold(e, fn, nbytes or dense, rows)
-        if nbytes is None:  # the tree's own minimum needs its argmaxes: report the formula only
+        if nbytes is None:  # the tree's own minimum needs its argmaxes: no rate is reported
             e.pop("cold_gbps")
         else:
             e["bytes_read"] = nbytes
-        if dense is not None:
-            e["cold_dense_gbps"] = round(dense / (e["cold_ms"]["median"] * 1e-3) / 1e9, 1)
         out[name] = e
     return out
+
+
+class SampleCall:
+    """spec_verify_sample on one workload with preallocated buffers (lse on)."""
+
+    def __init__(self, sv, torch, w, dev):
+        import numpy as np
+
+        lib = sv.load_library()
+        self.lib, self.w = lib, w
+        dt = sv.SV_BF16 if w.dtype == "bf16" else sv.SV_F32
+
+        def logits(a):
+            if a.dtype == np.uint16:
+                return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+            return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)
+
+        i32 = dict(dtype=torch.int32, device=dev)
+        f32 = dict(dtype=torch.float32, device=dev)
+        B, K, V = w.B, w.K, w.V
+        self.t, self.d = logits(w.target), logits(w.draft)
+        self.x = torch.from_numpy(w.draft_tokens).to(dev)
+        self.ua, self.us = torch.from_numpy(w.u_accept).to(dev), torch.from_numpy(w.u_sample).to(dev)
+        self.n, self.tok = torch.empty(B, **i32), torch.empty((B, K + 1), **i32)
+        self.lt, self.ld, self.st = torch.empty((B, K + 1), **f32), torch.empty((B, K), **f32), torch.empty(B, **i32)
+        self.ws = torch.empty(lib.sv_sample_workspace_bytes(B, K, V, dt), dtype=torch.uint8, device=dev)
+        P = lambda a: ctypes.c_void_p(a.data_ptr())
+        self.args = (P(self.t), P(self.d), P(self.x), P(self.ua), P(self.us), B, K, V, dt, ctypes.c_float(w.T),
+                     P(self.n), P(self.tok), P(self.lt), P(self.ld), P(self.st), P(self.ws), self.ws.numel(),
+                     ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream))
+
+    def __call__(self):
+        rc = self.lib.spec_verify_sample(*self.args)
+        if rc:
+            raise RuntimeError(f"spec_verify_sample failed: {rc}")
+
+    def outputs(self):
+        return {"accept_len": self.n.cpu().numpy(), "tokens": self.tok.cpu().numpy()}
+
+
+def event_calls(torch, fn, reps=200):
+    """Median, p10 and p90 (ms) of single calls, each bracketed by events on its
+    stream (back to back, no eviction: the small workloads fit in cache anyway)."""
+    import numpy as np
+
+    for _ in range(10):
+        fn()
+    ev = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        ev.append((e0, e1))
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) for a, b in ev])
+    return {"median": round(float(np.median(t)), 5), "p10": round(float(np.percentile(t, 10)), 5),
+            "p90": round(float(np.percentile(t, 90)), 5), "calls": reps}
+
+
+def bench_small_samples(sv, torch, workloads, dev, per_call, with_cold, reps):
+    """The two smaller stochastic workloads, each on its own: the tiny fp32 chain
+    (B=1 K=4 V=1000, latency only) and the B=32 K=7 bf16 chain at T=1.0, with
+    lse outputs (every row read), as in the step."""
+    import numpy as np
+
+    out, keep = {}, {}
+    for name in ("sample_b1_k4_v1000_f32", "sample_b32_k7_qwen3"):
+        w = workloads.make_workload(name)
+        c = SampleCall(sv, torch, w, dev)
+        c()
+        torch.cuda.synchronize()
+        keep[name] = (w, c.outputs())
+        n = keep[name][1]["accept_len"]
+        es = 2 if w.dtype == "bf16" else 4
+        R = w.V * es
+        nbytes = (w.B * (2 * w.K + 1) + int(np.sum(np.where(n < w.K, 2, 1)))) * R
+        rows = w.B * (w.K + 1)
+        ms = per_call(c, reps)
+        sv.trace_begin(4096)
+        for _ in range(50):
+            c()
+        torch.cuda.synchronize()
+        per = {}
+        for k, t in sv.trace_end(4096):
+            per.setdefault(k, []).append(t)
+        kern = {k: round(statistics.median(v), 5) for k, v in per.items()}
+        ksum = sum(kern.values())
+        e = {"workload": f"stochastic chain B={w.B} K={w.K} V={w.V} {w.dtype} T={w.T}", "rows": rows,
+             "bytes": nbytes, "ms": round(ms, 5), "call_events_ms": event_calls(torch, c),
+             "kernel_median_ms": kern, "kernels_ms": round(ksum, 5)}
+        if w.B == 1:
+            e["us"] = {k: round(v * 1e3, 2) for k, v in e["call_events_ms"].items() if k != "calls"}
+        else:
+            with_cold(e, c, nbytes, rows)
+            e["rows_per_s"] = round(rows / (ms * 1e-3), 1)
+            e["gbps"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+            e["frac_of_peak"] = round(e["gbps"] / HBM_PEAK_GBPS, 4)
+            e["kernels_gbps"] = round(nbytes / (ksum * 1e-3) / 1e9, 1)
+        out[name] = e
+        del c
+    return out, keep
 
 
 def alternate_best(torch, r, *fns):
@@ -727,14 +852,14 @@ def main():
         step()
     torch.cuda.synchronize()
     # timed region: events only around the streaming kernels the rooflines are quoted on
-    timed_kernels = ("rowstats", "skip_argmax", "skip_tree")
-    sv.trace_begin(max(64, args.steps * 4 + 16), kernels=timed_kernels)
+    timed_kernels = ("rowstats", "resid_mass", "skip_argmax", "skip_tree")
+    sv.trace_begin(max(64, args.steps * 5 + 16), kernels=timed_kernels)
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    recs = sv.trace_end(args.steps * 4 + 16)
+    recs = sv.trace_end(args.steps * 5 + 16)
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     per_kernel = {}
     for name, ms in recs:
@@ -756,6 +881,11 @@ def main():
         per_all.setdefault(name, []).append(ms)
     kmean = {k: statistics.mean(v) for k, v in per_all.items()}
     kmean.update({k: statistics.mean(v) for k, v in per_kernel.items()})
+    # the rooflines use each traced kernel's median launch over the timed steps
+    # (the mean is kept beside it: a few slow early launches pull it up)
+    kstats = {k: {"median_ms": round(statistics.median(v), 5), "mean_ms": round(statistics.mean(v), 5),
+                  "p10_ms": round(float(np.percentile(v, 10)), 5), "p90_ms": round(float(np.percentile(v, 90)), 5),
+                  "launches": len(v)} for k, v in per_kernel.items()}
 
     R = w3.V * 2  # bytes of one bf16 row
     n3 = calls.s_n.cpu().numpy()
@@ -778,19 +908,25 @@ def main():
     hbm_gbps = bytes_step / (ms_per_step * 1e-3) / 1e9
 
     def roofline(kernel, nbytes, workload):
-        ms = kmean.get(kernel)
-        if not ms:
+        st = kstats.get(kernel)
+        if not st:
             return None
+        ms = st["median_ms"]
         ach = nbytes / (ms * 1e-3) / 1e9
         tr = stored_traffic(kernel)
         return {"bound": "hbm", "kernel": kernel, "workload": workload, "achieved": round(ach, 1),
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4),
                 "traffic": tr["bytes_per_launch"] if tr else None,
-                "bytes_per_launch": nbytes, "avg_launch_ms": round(ms, 5)}
+                "bytes_per_launch": nbytes, "launch_ms": st,
+                "timing": f"median of {st['launches']} launches over the {args.steps} timed steps "
+                          f"(after {args.warmup} warm-up steps), HIP events stamped by each dispatch"}
 
     others = {}
     if "sample" in active:
         roof = roofline("rowstats", w3.B * (2 * w3.K + 1) * R, "stochastic chain B=256 K=7")
+        others["resid_mass"] = roofline("resid_mass", resid_rows * R,
+                                        "stochastic chain B=256 K=7 (the pair of rows each rejected "
+                                        "request draws from, the bonus row of the others)")
     if "tree" in active:
         others["skip_tree"] = roofline("skip_tree", bytes_mode["tree"],
                                        "greedy tree B=64 N=33 (rows of the root and accepted nodes)")
@@ -799,6 +935,12 @@ def main():
                                          "greedy chain B=256 K=7 (rows 0..n_b per request)")
     if "sample" not in active:
         roof = others.pop("skip_tree" if "tree" in active else "skip_argmax")
+    others = {k: v for k, v in others.items() if v}
+    # every hot-path kernel's fraction of the HBM peak, beside the dominant one's
+    if roof:
+        roof["hot_path"] = {r["kernel"]: {"frac": r["frac"], "achieved": r["achieved"],
+                                          "median_ms": r["launch_ms"]["median_ms"]}
+                            for r in [roof, *others.values()]}
 
     modes = {}
     for m in active:
@@ -815,11 +957,11 @@ def main():
         modes[m]["requests_per_s"] = round(batch[m] / kt, 1)
         modes[m]["tokens_per_s"] = round(float(emitted[m].sum()) / kt, 1)
     # the workloads' byte formula counts every row (B(K+1) R, B N R); the row-skipping passes
-    # read fewer, so beside their own bytes the rate at that formula is reported too
+    # read fewer, and their rates above are on the bytes the rule needs (no rate is quoted on
+    # bytes that were never read)
     for m, dense in (("greedy", w4.B * (w4.K + 1) * R), ("tree", w5.B * w5.N * R)):
         if m in modes:
             modes[m]["dense_bytes"] = dense
-            modes[m]["dense_gbps"] = round(dense / (modes[m]["kernel_ms"] * 1e-3) / 1e9, 1)
 
     # each call on its own, back to back (launch gaps included)
     def per_call(fn, reps):
@@ -883,11 +1025,12 @@ def main():
                 {"ms": round(ms, 5), "rows_per_s": round(rows_mode[name] / (ms * 1e-3), 1),
                  "bytes_read": bytes_mode[name], "gbps": round(bytes_mode[name] / (ms * 1e-3) / 1e9, 1)},
                 fn, bytes_mode[name], rows_mode[name])
-            dense = modes[name]["dense_bytes"]
-            calls_alone[name]["cold_dense_gbps"] = round(
-                dense / (calls_alone[name]["cold_ms"]["median"] * 1e-3) / 1e9, 1)
     if "greedy" in active:
         calls_alone["greedy_b512"] = bench_greedy_b512(sv, torch, workloads, dev, per_call, with_cold, reps)
+    small_outputs = {}
+    if "sample" in active:
+        small, small_outputs = bench_small_samples(sv, torch, workloads, dev, per_call, with_cold, reps)
+        calls_alone.update(small)
     # one GPU's share of a vocabulary-parallel LM head: the same calls on rows of V/8
     vocab_shard = None
     if args.mode == "all":
@@ -951,8 +1094,12 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        threads = args.cpu_threads or max(1, min(16, os.cpu_count() or 1))
-        secs = cpu_baseline(w3, w4, w5, args.mode, threads)
+        # OpenMP threads: the host's logical CPUs, capped at 16 (the share of the
+        # host one GPU gets on the measuring machines)
+        host_cpus = os.cpu_count() or 1
+        threads = args.cpu_threads or max(1, min(16, host_cpus))
+        outs = {}
+        secs = cpu_baseline(w3, w4, w5, args.mode, threads, keep=outs)
         secs1 = cpu_baseline(w3, w4, w5, args.mode, 1, runs=1)
         cpu = {"value": round(rows_step / secs, 1), "unit": "rows/s", "cores": threads,
                "kind": "oracle",
@@ -960,8 +1107,20 @@ def main():
                          f"{secs:.2f}s wall each",
                "single_thread": {"value": round(rows_step / secs1, 1), "unit": "rows/s",
                                  "sample": f"the same step once, {secs1:.2f}s wall"},
-               "cpu_model": cpu_model(),
+               "cpu_model": cpu_model(), "host_logical_cpus": host_cpus,
+               "threads_rule": "min(16, host logical CPUs)",
                "gpu_speedup": round(value / (rows_step / secs), 1)}
+        # the oracle's outputs give the stochastic workloads' flag counts
+        if "sample" in active:
+            import oracle
+
+            par = {"sample_b256_k7_qwen3_t07": sample_parity(
+                {"accept_len": n3, "tokens": calls.s_tok.cpu().numpy()}, outs["sample_b256_k7_qwen3_t07"])}
+            for name, (w, g) in small_outputs.items():
+                o = oracle.verify_sample(w.target, w.draft, w.draft_tokens, w.u_accept, w.u_sample, w.T,
+                                         threads=threads)
+                par[name] = sample_parity(g, o)
+            cpu["stochastic_parity"] = par
 
     out = {
         "metric": METRIC,
