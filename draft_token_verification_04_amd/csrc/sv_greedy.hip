@@ -354,12 +354,44 @@ __global__ __launch_bounds__(kBlock) void k_skip_argmax(const typename E::storag
     const long long rem = wave - static_cast<long long>(p) * per_pos;
     const int b = static_cast<int>(rem / segs);
     const int sg = static_cast<int>(rem - static_cast<long long>(b) * segs);
-    if (early ? skip_row_dead(ctl, b, p) : uniform(shared_load(&ctl.finished[b])) != 0) return;
+    // position 0's rows are always needed: no test, no wait before their loads
+    if (p > 0 && (early ? skip_row_dead(ctl, b, p) : uniform(shared_load(&ctl.finished[b])) != 0)) return;
 
     const long long row = static_cast<long long>(b) * (K + 1) + p;
     const int v0 = static_cast<int>((static_cast<long long>(sg) * nvec) / segs);
     const int v1 = static_cast<int>((static_cast<long long>(sg + 1) * nvec) / segs);
     const uint64_t key = segment_argmax_chunked<E, ALIGNED, U, kGSkipChunks>(L + row * V, V, v0, v1, lane);
+#if SV_SKIP_POLL
+    // Every wave leaves its segment's key (never 0; the keys start at 0) and
+    // goes; the wave of the row's last segment, dispatched after all the
+    // others, collects them and decides.  A key it waits for is either on its
+    // way or was never written because its wave found the request already
+    // settled, which the same test then tells this wave too.
+    if (sg != segs - 1) {
+        if (lane == 0) shared_store(&part_k[row * segs + sg], key);
+        return;
+    }
+    uint64_t mk = key;
+    bool complete = false;
+    for (int t = 0; t < kSkipPollCap; ++t) {
+        uint64_t m = 0;
+        bool missing = false;
+        for (int s = lane; s < segs - 1; s += kWave) {
+            const uint64_t k = shared_load(&part_k[row * segs + s]);
+            missing |= k == 0;
+            m = k > m ? k : m;
+        }
+        if (ballot(missing) == 0) {
+            mk = wave_max_u64(m > mk ? m : mk);
+            complete = true;
+            break;
+        }
+        if (early ? skip_row_dead(ctl, b, p) : uniform(shared_load(&ctl.finished[b])) != 0) return;
+        __builtin_amdgcn_s_sleep(2);
+    }
+    if (!complete) return;  // never decide on part of a row
+    const int a = uniform(argmax_key_index(mk));
+#else
     if (lane == 0) shared_store(&part_k[row * segs + sg], key);
     if (!wave_arrive(&ctl.ticket[row], static_cast<unsigned>(segs), lane)) return;
 
@@ -370,6 +402,7 @@ __global__ __launch_bounds__(kBlock) void k_skip_argmax(const typename E::storag
         mk = k > mk ? k : mk;
     }
     const int a = uniform(argmax_key_index(wave_max_u64(mk)));
+#endif
     const int32_t *xb = drafts + static_cast<long long>(b) * K;
     uint64_t bits = 1ull << p;
     if (p < K && uniform(xb[p]) != a) bits |= 1ull << (32 + p);
@@ -390,7 +423,7 @@ __global__ __launch_bounds__(kBlock) void k_skip_argmax(const typename E::storag
         int v = 0;
         if (lane == 0) {
             int32_t *w = &amax[static_cast<long long>(b) * (K + 1) + n];
-            for (int t = 0; t < (1 << 22) && (v = shared_load(w)) == 0; ++t) __builtin_amdgcn_s_sleep(1);
+            for (int t = 0; t < kSkipPollCap && (v = shared_load(w)) == 0; ++t) __builtin_amdgcn_s_sleep(1);
         }
         an = uniform(__shfl(v, 0, kWave)) - 1;
     }
@@ -452,7 +485,7 @@ struct TreeCtl {
 // outside [0, j) counts as the root here (the walk flags such a request), so
 // the slots are always a permutation of the nodes.
 __global__ __launch_bounds__(kBlock) void k_tree_prep(const int32_t *__restrict__ par, int B, int N,
-                                                      TreeCtl ctl) {
+                                                      TreeCtl ctl, uint64_t *__restrict__ part_k, int segs) {
     const int lane = threadIdx.x & (kWave - 1);
     const int b = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
     if (b >= B) return;
@@ -477,6 +510,10 @@ __global__ __launch_bounds__(kBlock) void k_tree_prep(const int32_t *__restrict_
         ctl.state[base + lane] = 0u;
     }
     if (lane == 0) ctl.resolved[b] = 0u;
+    if (SV_SKIP_POLL) {  // the segment keys of the request's rows start at 0
+        uint64_t *pk = part_k + base * segs;
+        for (int i = lane; i < N * segs; i += kWave) pk[i] = 0;
+    }
 }
 
 // Node j's outputs of request b once every node is resolved (one wave).
@@ -567,12 +604,42 @@ __global__ __launch_bounds__(kBlock) void k_skip_tree(const typename E::storage 
     const int sg = static_cast<int>(rem - static_cast<long long>(b) * segs);
     const long long base = static_cast<long long>(b) * N;
     const int j = uniform(ctl.order[base + slot]);  // issued beside the state load
-    if (uniform(shared_load(&ctl.state[base + slot])) & kRejected) return;
+    // slot 0 holds the root, whose row is always needed
+    if (slot > 0 && (uniform(shared_load(&ctl.state[base + slot])) & kRejected)) return;
 
     const long long row = base + j;
     const int v0 = static_cast<int>((static_cast<long long>(sg) * nvec) / segs);
     const int v1 = static_cast<int>((static_cast<long long>(sg + 1) * nvec) / segs);
     const uint64_t key = segment_argmax_chunked<E, ALIGNED, U, kGSkipChunks>(L + row * V, V, v0, v1, lane);
+#if SV_SKIP_POLL
+    // keys handed to the row's last segment as in the chain pass (the prep
+    // launch zeroed them); a key never comes only if its wave found the node
+    // already rejected, which this wave then finds too
+    if (sg != segs - 1) {
+        if (lane == 0) shared_store(&part_k[row * segs + sg], key);
+        return;
+    }
+    uint64_t mk = key;
+    bool complete = false;
+    for (int t = 0; t < kSkipPollCap; ++t) {
+        uint64_t m = 0;
+        bool missing = false;
+        for (int s = lane; s < segs - 1; s += kWave) {
+            const uint64_t k = shared_load(&part_k[row * segs + s]);
+            missing |= k == 0;
+            m = k > m ? k : m;
+        }
+        if (ballot(missing) == 0) {
+            mk = wave_max_u64(m > mk ? m : mk);
+            complete = true;
+            break;
+        }
+        if (uniform(shared_load(&ctl.state[base + slot])) & kRejected) return;
+        __builtin_amdgcn_s_sleep(2);
+    }
+    if (!complete) return;  // never decide on part of a row
+    const int a = uniform(argmax_key_index(mk));
+#else
     if (lane == 0) shared_store(&part_k[row * segs + sg], key);
     if (!wave_arrive(&ctl.ticket[base + slot], static_cast<unsigned>(segs), lane)) return;
 
@@ -583,6 +650,7 @@ __global__ __launch_bounds__(kBlock) void k_skip_tree(const typename E::storage 
         mk = k > mk ? k : mk;
     }
     const int a = uniform(argmax_key_index(wave_max_u64(mk)));
+#endif
     if (lane == 0) shared_store(&amax[row], a);
     wait_own_stores();
     const bool in = lane < N;
@@ -629,7 +697,7 @@ hipError_t skip_tree_t(const void *L, const int32_t *tok, const int32_t *par, in
     const long long nwaves = static_cast<long long>(N) * B * g.segs;
     const long long blocks = (nwaves + kWavesPerBlock - 1) / kWavesPerBlock;
     return launch_kernel(k_skip_tree<E, ALIGNED, kGSkipVecsPerLane>, dim3(static_cast<unsigned>(blocks)),
-                         dim3(kBlock), 0, s, static_cast<const T *>(L), tok, par, B, N, V, g.nvec, g.segs,
+                         dim3(kBlock), SV_TSKIP_LDS, s, static_cast<const T *>(L), tok, par, B, N, V, g.nvec, g.segs,
                          part_k, amax, ctl, accept_len, path_nodes, out_tokens, status);
 }
 
@@ -641,7 +709,7 @@ hipError_t skip_argmax_t(const void *L, const int32_t *drafts, int B, int K, int
     const long long nwaves = static_cast<long long>(K + 1) * B * g.segs;
     const long long blocks = (nwaves + kWavesPerBlock - 1) / kWavesPerBlock;
     return launch_kernel(k_skip_argmax<E, ALIGNED, kGSkipVecsPerLane>, dim3(static_cast<unsigned>(blocks)),
-                         dim3(kBlock), 0, s, static_cast<const T *>(L), drafts, B, K, V, g.nvec, g.segs,
+                         dim3(kBlock), SV_GSKIP_LDS, s, static_cast<const T *>(L), drafts, B, K, V, g.nvec, g.segs,
                          part_k, amax, ctl, static_cast<int>(skip_early(B, 1, V, sizeof(T))), accept_len,
                          out_tokens, status);
 }
@@ -680,11 +748,12 @@ hipError_t launch_skip_match(const void *L, const int32_t *drafts, int B, int K,
                              int32_t *status, hipStream_t s) {
     SkipCtl ctl;
 #if SV_SKIP_FASTDECIDE
-    // the argmax words (placed just before the control words) start at 0 too
+    // the argmax words (placed just before the control words), and with
+    // SV_SKIP_POLL the segment keys before them, start at 0 too
     skip_ctl_carve(ctl_base, B, K, &ctl);
-    const size_t span = static_cast<size_t>(static_cast<char *>(ctl_base) - reinterpret_cast<char *>(amax)) +
-                        skip_ctl_bytes(B, K);
-    hipError_t e = clear_words(amax, span, s);
+    char *first = SV_SKIP_POLL ? reinterpret_cast<char *>(part_k) : reinterpret_cast<char *>(amax);
+    const size_t span = static_cast<size_t>(static_cast<char *>(ctl_base) - first) + skip_ctl_bytes(B, K);
+    hipError_t e = clear_words(first, span, s);
 #else
     hipError_t e = skip_ctl_init(ctl_base, B, K, &ctl, s);
 #endif
@@ -713,7 +782,7 @@ hipError_t launch_skip_tree(const void *L, const int32_t *node_tokens, const int
     ctl.resolved = reinterpret_cast<unsigned *>(ctl.rank + bn);
     trace_select(-1);  // the preparing launch is not traced
     hipLaunchKernelGGL(k_tree_prep, dim3(static_cast<unsigned>((B + kWavesPerBlock - 1) / kWavesPerBlock)),
-                       dim3(kBlock), 0, s, parents, B, N, ctl);
+                       dim3(kBlock), 0, s, parents, B, N, ctl, part_k, g.segs);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     trace_select(SV_K_SKIP_TREE);

@@ -60,6 +60,27 @@ constexpr int kGSkipVecsPerLane = SV_GSKIP_VECS;
 #ifndef SV_SKIP_FASTDECIDE
 #define SV_SKIP_FASTDECIDE 1
 #endif
+// ... and its waves hand their segment keys to the row's last segment without
+// a ticket (that wave polls for them; needs SV_SKIP_FASTDECIDE).
+#ifndef SV_SKIP_POLL
+#define SV_SKIP_POLL 1
+#endif
+#if SV_SKIP_POLL && !SV_SKIP_FASTDECIDE
+#error "SV_SKIP_POLL needs SV_SKIP_FASTDECIDE"
+#endif
+// Dynamic LDS each workgroup of the greedy chain's and the tree's skip passes
+// reserves, unused, to cap the workgroups per compute unit (0: as many as their
+// registers allow, five).  Measured on MI355X (us per pass, chain B=256 / chain
+// B=512 / tree B=64): no cap 69.6 / 116.1 / 70.0; 40 KB (four) 67.4 / 111.1 /
+// 71.9; 45 KB (three) 68.1 / 115.8 / 77.5; 54 KB (two) 75.6 / 143.8 / 92.9.
+#ifndef SV_GSKIP_LDS
+#define SV_GSKIP_LDS (40 * 1024)
+#endif
+#ifndef SV_TSKIP_LDS
+#define SV_TSKIP_LDS 0
+#endif
+// Bound on any poll of a word another wave is bound to write (never reached).
+constexpr int kSkipPollCap = 1 << 22;
 
 constexpr int kGSkipChunks = SV_GSKIP_CHUNKS;
 // Waves the residual-mass pass aims for: short waves of a few tiles each

@@ -63,7 +63,10 @@ __device__ __forceinline__ bool skip_row_dead(const SkipCtl &ctl, int b, int p) 
 // 93); above that the earlier test saves reads and time (B = 384, 117 MB: 108
 // against 109 us; B = 448: 116 against 122; B = 512: 124 against 130; the
 // stochastic pass at B = 256, two rows per position, 156 MB: 147 against 150).
-constexpr double kEarlySkipPositionBytes = 110e6;
+#ifndef SV_EARLY_SKIP_BYTES
+#define SV_EARLY_SKIP_BYTES 110e6
+#endif
+constexpr double kEarlySkipPositionBytes = SV_EARLY_SKIP_BYTES;
 inline bool skip_early(int B, int rows_per_position, int V, size_t elem) {
     return static_cast<double>(B) * rows_per_position * V * static_cast<double>(elem) >= kEarlySkipPositionBytes;
 }
