@@ -53,6 +53,9 @@ KERNEL_SOURCES = {
     "rowstats": ["draft_token_verification_04_amd/csrc/sv_sample.hip",
                  "draft_token_verification_04_amd/csrc/sv_device.hpp",
                  "draft_token_verification_04_amd/csrc/sv_internal.hpp"],
+    "resid_mass": ["draft_token_verification_04_amd/csrc/sv_sample.hip",
+                   "draft_token_verification_04_amd/csrc/sv_device.hpp",
+                   "draft_token_verification_04_amd/csrc/sv_internal.hpp"],
     "argmax": ["draft_token_verification_04_amd/csrc/sv_greedy.hip",
                "draft_token_verification_04_amd/csrc/sv_device.hpp",
                "draft_token_verification_04_amd/csrc/sv_internal.hpp"],
@@ -791,8 +794,11 @@ def time_step_without_lse(torch, calls, parts, active, args, w3, w4, w5):
             "rows_per_s": round(sum(rows[m] for m in active) / (ms * 1e-3), 1)}
 
 
-def read_ceiling(sv, torch, dev):
-    """GB/s of sv_read_probe over 4 GiB of random bytes (mean of 20 launches)."""
+def read_ceiling(sv, torch, dev, sizes=()):
+    """GB/s of sv_read_probe over 4 GiB of random bytes (mean of 20 launches), and
+    for each byte count in `sizes` the median rate of 20 launches reading that
+    many bytes, each from the next region of the 4 GiB buffer (so that, as in the
+    step, no launch finds its bytes in the 256 MB Infinity Cache)."""
     probe = torch.randint(-2**31, 2**31 - 1, (1 << 30,), dtype=torch.int32, device=dev)
     folds = sv.sv_read_probe(probe)
     for _ in range(2):
@@ -804,8 +810,22 @@ def read_ceiling(sv, torch, dev):
     torch.cuda.synchronize()
     ms = statistics.mean(t for _, t in sv.trace_end(64))
     gbps = probe.numel() * 4 / (ms * 1e-3) / 1e9
+    at = {}
+    for nbytes in sizes:
+        n = max(4, (int(nbytes) // 16) * 4)  # int32 elements, whole 16-byte vectors
+        regions = max(1, probe.numel() // n)
+        for i in range(3):
+            sv.sv_read_probe(probe[(i % regions) * n:(i % regions) * n + n], folds=folds)
+        torch.cuda.synchronize()
+        sv.trace_begin(64, kernels=("read_probe",))
+        for i in range(20):
+            r = (i + 3) % regions
+            sv.sv_read_probe(probe[r * n:r * n + n], folds=folds)
+        torch.cuda.synchronize()
+        t = statistics.median(x for _, x in sv.trace_end(64))
+        at[int(nbytes)] = round(n * 4 / (t * 1e-3) / 1e9, 1)
     del probe
-    return gbps
+    return gbps, at
 
 
 def main():
@@ -1037,8 +1057,10 @@ def main():
         vocab_shard = bench_vocab_shard(sv, torch, workloads, dev, per_call, with_cold, reps)
     del evict
 
-    # the read rate this device reaches: a read-only stream with the same loads
-    read_ceiling_gbps = read_ceiling(sv, torch, dev)
+    # the read rate this device reaches: a read-only stream with the same loads,
+    # over 4 GiB and over each roofline kernel's own byte count
+    roof_list = [r for r in [roof, *others.values()] if r]
+    read_ceiling_gbps, ceiling_at = read_ceiling(sv, torch, dev, sorted({r["bytes_per_launch"] for r in roof_list}))
 
     # beyond the verification step: committing the tree's accepted paths in a
     # KV cache shaped like a 36-layer target (K and V, 8 heads x 128 bf16 = 2 KB rows)
@@ -1153,7 +1175,8 @@ def main():
         "hbm_frac_of_peak": round(hbm_gbps / HBM_PEAK_GBPS, 4),
         "read_ceiling": {"gbps": round(read_ceiling_gbps, 1), "kernel": "read_probe",
                          "what": "read-only stream of 4 GiB of random bytes, mean of 20 launches",
-                         "frac_of_peak": round(read_ceiling_gbps / HBM_PEAK_GBPS, 4)},
+                         "frac_of_peak": round(read_ceiling_gbps / HBM_PEAK_GBPS, 4),
+                         "gbps_at_bytes": {str(k): v for k, v in ceiling_at.items()}},
         "roofline": roof,
         "roofline_others": others or None,
         "modes": modes,
@@ -1165,6 +1188,10 @@ def main():
     for r in [roof, *others.values()]:
         if r and r.get("unit") == "GB/s":
             r["frac_of_read_ceiling"] = round(r["achieved"] / read_ceiling_gbps, 4)
+            c = ceiling_at.get(r["bytes_per_launch"])
+            if c:
+                r["read_ceiling_at_size"] = {"gbps": c, "frac": round(r["achieved"] / c, 4),
+                                             "what": "the read probe over the same byte count, cold"}
     print(json.dumps(out), flush=True)
 
 
