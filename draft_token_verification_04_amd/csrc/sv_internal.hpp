@@ -85,7 +85,10 @@ constexpr int kSkipPollCap = 1 << 22;
 constexpr int kGSkipChunks = SV_GSKIP_CHUNKS;
 // Waves the residual-mass pass aims for: short waves of a few tiles each
 // (measured: 28 us per pass at B=256 against 32 us with 4096 longer waves).
-constexpr int kResidTargetWaves = 32768;
+#ifndef SV_RESID_WAVES
+#define SV_RESID_WAVES 32768
+#endif
+constexpr int kResidTargetWaves = SV_RESID_WAVES;
 // Bytes of LDS the per-request merge kernels use to stage row partials.
 constexpr int kMergeLdsBytes = 24 * 1024;
 

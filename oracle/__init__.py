@@ -83,9 +83,10 @@ def _c(a, dtype):
     return np.ascontiguousarray(a, dtype=dtype)
 
 
-def verify_sample(target, draft, draft_tokens, u_accept, u_sample, T, threads=None, lib=None):
+def verify_sample(target, draft, draft_tokens, u_accept, u_sample, T, threads=None, lib=None, lse=True):
     """Stochastic chain verification.  Returns a dict of numpy arrays:
-    accept_len [B], tokens [B,K+1], lse_target [B,K+1], lse_draft [B,K],
+    accept_len [B], tokens [B,K+1], lse_target [B,K+1], lse_draft [B,K] (left
+    out with lse=False, which spares the rows no draw consumes),
     status [B], margin [B] (smallest consumed-draw margin), margin_accept [B]
     (smallest margin of the consumed acceptance draws, which alone decide
     accept_len; +inf when none), margin_sample [B] (the sample draw's margin),
@@ -102,12 +103,13 @@ def verify_sample(target, draft, draft_tokens, u_accept, u_sample, T, threads=No
     ua = _c(u_accept, np.float32).reshape(B, K)
     us = _c(u_sample, np.float32).reshape(B, K + 1)
     out = dict(accept_len=np.empty(B, np.int32), tokens=np.empty((B, K + 1), np.int32),
-               lse_target=np.empty((B, K + 1)), lse_draft=np.empty((B, K)),
                status=np.empty(B, np.int32), margin=np.empty(B), margin_accept=np.empty(B),
                margin_sample=np.empty(B), Z=np.empty(B))
+    if lse:
+        out.update(lse_target=np.empty((B, K + 1)), lse_draft=np.empty((B, K)))
     rc = lib.sv_oracle_sample(_ptr(target), _ptr(draft), dt, _ptr(x), _ptr(ua), _ptr(us), B, K, V,
                               float(T), _ptr(out["accept_len"]), _ptr(out["tokens"]),
-                              _ptr(out["lse_target"]), _ptr(out["lse_draft"]), _ptr(out["status"]),
+                              _ptr(out.get("lse_target")), _ptr(out.get("lse_draft")), _ptr(out["status"]),
                               _ptr(out["margin"]), _ptr(out["margin_accept"]),
                               _ptr(out["margin_sample"]), _ptr(out["Z"]), threads or default_threads())
     if rc:
