@@ -182,3 +182,57 @@ def test_fused_projection_forms_replay_inside_a_graph():
             for key, ref in outs.items():
                 assert np.array_equal(got[call][key], ref), (rep, call, key)
         eager()
+
+
+def test_noalloc_sampler_replays_inside_a_graph():
+    """The no-allocation entry point is for callers under graph capture: with
+    its outputs given, the captured call allocates nothing (its scratch is the
+    library's own, looked up by the eager warm-up call).  Replays with the
+    inputs rewritten, and eager calls of both sampler entry points between
+    them, each equal the eager call."""
+    note("graph capture of the no-allocation sampler")
+    wa = workloads.make_sample(48, 7, 30000, "bf16", 0.7, spikes=10, noise_sigma=1.0, seed=71)
+    wb = workloads.make_sample(48, 7, 30000, "bf16", 0.7, spikes=10, noise_sigma=2.5, seed=72)
+    t, d = logits_to_dev(wa.target), logits_to_dev(wa.draft)
+    x, ua, us = ints_to_dev(wa.draft_tokens), f32_to_dev(wa.u_accept), f32_to_dev(wa.u_sample)
+
+    def load(w):
+        t.copy_(logits_to_dev(w.target))
+        d.copy_(logits_to_dev(w.draft))
+        x.copy_(ints_to_dev(w.draft_tokens))
+        ua.copy_(f32_to_dev(w.u_accept))
+        us.copy_(f32_to_dev(w.u_sample))
+
+    want = {}
+    for name, w in (("a", wa), ("b", wb)):
+        load(w)
+        want[name] = _np(sv.spec_verify_sample(t, d, x, ua, us, w.T))
+    B, K = wa.B, wa.K
+    outs = {"accept_len": torch.empty(B, dtype=torch.int32, device=dev()),
+            "tokens": torch.empty((B, K + 1), dtype=torch.int32, device=dev()),
+            "lse_target": torch.empty((B, K + 1), dtype=torch.float32, device=dev()),
+            "lse_draft": torch.empty((B, K), dtype=torch.float32, device=dev()),
+            "status": torch.empty(B, dtype=torch.int32, device=dev())}
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        sv.spec_verify_sample_noalloc(t, d, x, ua, us, wa.T, out=outs)  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        sv.spec_verify_sample_noalloc(t, d, x, ua, us, wa.T, out=outs)
+    for rep, name in enumerate(("a", "b", "a", "b")):
+        load(wa if name == "a" else wb)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = _np(outs)
+        for key, ref in want[name].items():
+            assert np.array_equal(got[key], ref), (rep, key)
+        # eager work between replays, the no-allocation call included
+        e1 = _np(sv.spec_verify_sample_noalloc(t, d, x, ua, us, wa.T, lse=False))
+        e2 = _np(sv.spec_verify_sample(t, d, x, ua, us, wa.T, lse=False))
+        torch.cuda.synchronize()
+        for key in e2:
+            assert np.array_equal(e1[key], e2[key]), (rep, key)
