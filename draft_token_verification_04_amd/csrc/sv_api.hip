@@ -41,12 +41,13 @@ SampleWs sample_ws_layout(int B, int K, const RowGeom &g) {
     o = align_up(o + parts * sizeof(double));
     w.L2 = o;
     o = align_up(o + rows * sizeof(double));
+    // the row-skipping pass clears part_R through the control words at once
+    w.skipctl = o;
+    o = align_up(o + skip_ctl_bytes(B, K));
     w.rp = o;
     o = align_up(o + static_cast<size_t>(B) * sizeof(ResidParam));
     w.tiles = o;
     o = align_up(o + static_cast<size_t>(B) * static_cast<size_t>(g.ntiles) * sizeof(double));
-    w.skipctl = o;
-    o = align_up(o + skip_ctl_bytes(B, K));
     w.total = o;
     return w;
 }

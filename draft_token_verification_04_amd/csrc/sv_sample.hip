@@ -667,6 +667,7 @@ __global__ __launch_bounds__(kBlock) void k_zero_words(uint32_t *__restrict__ p,
         p[i] = 0;
 }
 
+#if !SV_SKIP_POLL
 // log2 sum_v 2^(L[v] c) of one row from segment partials read as shared words.
 __device__ __forceinline__ double merge_row_shared(float *pR, double *pS, int segs, int lane) {
     float Rm = -__builtin_huge_valf();
@@ -682,6 +683,66 @@ __device__ __forceinline__ double merge_row_shared(float *pR, double *pS, int se
     acc = wave_sum(acc);
     return acc > 0.0 ? static_cast<double>(Rm) + log2(acc) : -__builtin_huge_val();
 }
+#endif
+
+#if SV_SKIP_POLL
+// Words a wave hands to another without a ticket are marked so that a written
+// word is never 0 (the words start at 0): a segment's R as its bits with the
+// sign flipped (-0 taken as +0 first), its s >= 0 with the sign bit set, a
+// row's log-sum like R.
+__device__ __forceinline__ uint32_t mark_R(float R) {
+    uint32_t u = __float_as_uint(R);
+    if (u == 0x80000000u) u = 0u;
+    return u ^ 0x80000000u;
+}
+__device__ __forceinline__ float unmark_R(uint32_t w) { return __uint_as_float(w ^ 0x80000000u); }
+__device__ __forceinline__ float canonical_R(float R) { return unmark_R(mark_R(R)); }
+__device__ __forceinline__ uint64_t mark_s(double s) {
+    return static_cast<uint64_t>(__double_as_longlong(s)) | (1ull << 63);
+}
+__device__ __forceinline__ double unmark_s(uint64_t w) {
+    return __longlong_as_double(static_cast<long long>(w & ~(1ull << 63)));
+}
+__device__ __forceinline__ uint64_t mark_L2(double v) {
+    uint64_t u = static_cast<uint64_t>(__double_as_longlong(v));
+    if (u == (1ull << 63)) u = 0;
+    return u ^ (1ull << 63);
+}
+__device__ __forceinline__ double unmark_L2(uint64_t w) {
+    return __longlong_as_double(static_cast<long long>(w ^ (1ull << 63)));
+}
+
+// The row merge over partials held one per lane, by the lanes where `member`.
+__device__ __forceinline__ double merge_lanes(float R, double s, bool member) {
+    const float Rm = wave_max(member ? R : -__builtin_huge_valf());
+    double acc = 0.0;
+    if (Rm != -__builtin_huge_valf() && member && s > 0.0)
+        acc = s * exp2(static_cast<double>(R) - static_cast<double>(Rm));
+    acc = wave_sum(acc);
+    return acc > 0.0 ? static_cast<double>(Rm) + log2(acc) : -__builtin_huge_val();
+}
+
+// The row merge over marked words [base, base + segs), all written, except
+// segment `own` (segs: none), which is this wave's (R, s).
+__device__ __forceinline__ double merge_row_marked(uint32_t *wR, uint64_t *wS, long long base, int segs,
+                                                   int own, float R, double s, int lane) {
+    float Rm = -__builtin_huge_valf();
+    for (int sg = lane; sg < segs; sg += kWave)
+        Rm = fmaxf(Rm, sg == own ? canonical_R(R) : unmark_R(shared_load(&wR[base + sg])));
+    Rm = wave_max(Rm);
+    double acc = 0.0;
+    if (Rm != -__builtin_huge_valf()) {
+        for (int sg = lane; sg < segs; sg += kWave) {
+            const double ss = sg == own ? s : unmark_s(shared_load(&wS[base + sg]));
+            const float Rs = sg == own ? canonical_R(R) : unmark_R(shared_load(&wR[base + sg]));
+            if (ss > 0.0) acc += ss * exp2(static_cast<double>(Rs) - static_cast<double>(Rm));
+        }
+    }
+    acc = wave_sum(acc);
+    return acc > 0.0 ? static_cast<double>(Rm) + log2(acc) : -__builtin_huge_val();
+}
+
+#endif
 
 // Outputs of request b decided at n (mode 1: rejection at n, residual of
 // rows n; mode 0: bonus from target row K), written by one wave.
@@ -744,6 +805,63 @@ __global__ __launch_bounds__(kBlock) void k_skip_stats(
     float R;
     double sum;
     segment_stats_chunked<E, ALIGNED, U, kSkipChunks>(base, V, v0, v1, c_hi, c_lo, lane, R, sum);
+    const int nrows = 2 * K + 1;
+    double *L2b = L2 + static_cast<long long>(b) * nrows;
+#if SV_SKIP_POLL
+    // Every wave but the last of (b, p) leaves its partial as two marked words
+    // (never 0; they start at 0) and goes.  The last one, the draft row's last
+    // segment (the target row's at the bonus position), is dispatched after
+    // the others: it collects their partials, or learns from the same test
+    // they made that they skipped theirs and the request is settled.
+    uint32_t *wR = reinterpret_cast<uint32_t *>(part_R);
+    uint64_t *wS = reinterpret_cast<uint64_t *>(part_s);
+    const int nparts = (p < K ? 2 : 1) * segs, mine = nparts - 1;
+    if (r != mine) {
+        if (lane == 0) {
+            shared_store(&wR[g * segs + sg], mark_R(R));
+            shared_store(&wS[g * segs + sg], mark_s(sum));
+        }
+        return;
+    }
+    // partial i of (b, p): segment i % segs of the target row (i < segs) or of
+    // the draft row
+    auto part_index = [&](int i) { return i < segs ? gt * segs + i : gd * segs + (i - segs); };
+    float Ri = -__builtin_huge_valf();
+    double si = 0.0;
+    bool complete = false;
+    for (int t = 0; t < kSkipPollCap; ++t) {
+        bool missing = false;
+        for (int i = lane; i < mine; i += kWave) {
+            const uint32_t a = shared_load(&wR[part_index(i)]);
+            const uint64_t s2 = shared_load(&wS[part_index(i)]);
+            missing |= a == 0 || s2 == 0;
+            if (i == lane) {
+                Ri = unmark_R(a);
+                si = unmark_s(s2);
+            }
+        }
+        if (ballot(missing) == 0) {
+            complete = true;
+            break;
+        }
+        if (early ? skip_row_dead(ctl, b, p) : uniform(shared_load(&ctl.finished[b])) != 0) return;
+        __builtin_amdgcn_s_sleep(2);
+    }
+    if (!complete) return;  // never decide on part of a row
+    if (lane == mine) {
+        Ri = canonical_R(R);
+        si = sum;
+    }
+    double L2p, L2q = 0.0;
+    if (nparts <= kWave) {  // every partial is held by the lane of its index
+        const bool tl = lane < segs, dl = lane >= segs && lane < nparts;
+        L2p = merge_lanes(Ri, si, tl);
+        if (p < K) L2q = merge_lanes(Ri, si, dl);
+    } else {
+        L2p = merge_row_marked(wR, wS, gt * segs, segs, p < K ? segs : segs - 1, R, sum, lane);
+        if (p < K) L2q = merge_row_marked(wR, wS, gd * segs, segs, segs - 1, R, sum, lane);
+    }
+#else
     if (lane == 0) {
         shared_store(&part_R[g * segs + sg], R);
         shared_store(&part_s[g * segs + sg], sum);
@@ -752,12 +870,12 @@ __global__ __launch_bounds__(kBlock) void k_skip_stats(
     if (!wave_arrive(&ctl.ticket[gt], parts, lane)) return;
 
     // last segment of (b, p): decide position p
-    const int nrows = 2 * K + 1;
-    double *L2b = L2 + static_cast<long long>(b) * nrows;
     const double L2p = merge_row_shared(part_R + gt * segs, part_s + gt * segs, segs, lane);
+    double L2q = 0.0;
+    if (p < K) L2q = merge_row_shared(part_R + gd * segs, part_s + gd * segs, segs, lane);
+#endif
     uint64_t bits = 1ull << p;
     if (p < K) {
-        const double L2q = merge_row_shared(part_R + gd * segs, part_s + gd * segs, segs, lane);
         const int x = uniform(drafts[static_cast<long long>(b) * K + p]);
         double ratio = 0.0;
         if (x >= 0 && x < V) {
@@ -767,13 +885,45 @@ __global__ __launch_bounds__(kBlock) void k_skip_stats(
         }
         const double u = static_cast<double>(ua[static_cast<long long>(b) * K + p]);
         if (!(u < ratio)) bits |= 1ull << (32 + p);
+#if !SV_SKIP_POLL
         if (lane == 0) shared_store(&L2b[K + 1 + p], L2q);
+#endif
     }
+#if SV_SKIP_POLL
+    // The decision is one atomic OR; the wave whose OR completes the request's
+    // decided prefix finishes it.  The log-sums of a decided position are
+    // marked words too and need not land before its OR: the finisher polls for
+    // those of the position it draws from.
+    uint64_t *wL = reinterpret_cast<uint64_t *>(L2b);
+    uint64_t old = 0;
+    if (lane == 0) {
+        if (p < K) shared_store(&wL[K + 1 + p], mark_L2(L2q));
+        shared_store(&wL[p], mark_L2(L2p));
+        old = __hip_atomic_fetch_or(&ctl.mask[b], bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    old = uniform(static_cast<uint64_t>(__shfl(static_cast<long long>(old), 0, kWave)));
+    if (skip_prefix(old, K) >= 0) return;  // the request was complete already
+    const int n = skip_prefix(old | bits, K);
+    if (n < 0) return;
+    double L2pn = L2p, L2qn = L2q;
+    if (n != p) {
+        uint64_t w = 0;
+        if (lane < (n < K ? 2 : 1)) {
+            uint64_t *q = &wL[lane == 0 ? n : K + 1 + n];
+            for (int t = 0; t < kSkipPollCap && (w = shared_load(q)) == 0; ++t) __builtin_amdgcn_s_sleep(1);
+        }
+        const long long w0 = __shfl(static_cast<long long>(w), 0, kWave);
+        const long long w1 = __shfl(static_cast<long long>(w), 1, kWave);
+        L2pn = unmark_L2(static_cast<uint64_t>(w0));
+        L2qn = n < K ? unmark_L2(static_cast<uint64_t>(w1)) : 0.0;
+    }
+#else
     if (lane == 0) shared_store(&L2b[p], L2p);
     const int n = skip_decide(ctl, b, K, bits, lane);
     if (n < 0) return;
     const double L2pn = shared_load(&L2b[n]);
     const double L2qn = n < K ? shared_load(&L2b[K + 1 + n]) : 0.0;
+#endif
     skip_finish(drafts + static_cast<long long>(b) * K, us, b, K, V, n, n < K ? 1 : 0, L2pn, L2qn,
                 accept_len, out_tokens, status, rp, lane);
     skip_finished(ctl, b, lane);
@@ -853,7 +1003,19 @@ hipError_t launch_skip(const void *tgt, const void *drf, const int32_t *drafts, 
                        int32_t *accept_len, int32_t *out_tokens, int32_t *status, ResidParam *rp,
                        hipStream_t s) {
     SkipCtl ctl;
+#if SV_SKIP_POLL
+    // the partials, the log-sums and the control words are marked words that
+    // start at 0; the workspace holds them in that order, back to back
+    skip_ctl_carve(ctl_base, B, K, &ctl);
+    char *first = reinterpret_cast<char *>(part_R);
+    char *end = static_cast<char *>(ctl_base) + skip_ctl_bytes(B, K);
+    if (first > reinterpret_cast<char *>(part_s) || reinterpret_cast<char *>(part_s) > reinterpret_cast<char *>(L2) ||
+        reinterpret_cast<char *>(L2) > static_cast<char *>(ctl_base))
+        return hipErrorInvalidValue;
+    hipError_t e = clear_words(first, static_cast<size_t>(end - first), s);
+#else
     hipError_t e = skip_ctl_init(ctl_base, B, K, &ctl, s);
+#endif
     if (e != hipSuccess) return e;
     trace_select(SV_K_SKIP_STATS);
 #define SV_SK(E, A) skip_stats_t<E, A>(tgt, drf, drafts, ua, us, B, K, V, g, sc, part_R, part_s, L2, ctl, accept_len, out_tokens, status, rp, s)
