@@ -22,10 +22,10 @@ namespace sv {
 #define SV_RESID_GROUP 2
 #endif
 #ifndef SV_SKIP_VECS
-#define SV_SKIP_VECS 8
+#define SV_SKIP_VECS 6
 #endif
 #ifndef SV_SKIP_CHUNKS
-#define SV_SKIP_CHUNKS 4
+#define SV_SKIP_CHUNKS 2
 #endif
 // Greedy chains with K <= 31 take the row-skipping pass (0: always read every row).
 #ifndef SV_GREEDY_SKIP
@@ -39,8 +39,10 @@ constexpr int kArgmaxVecsPerLane = SV_ARGMAX_VECS;
 // walks its tiles in such groups, loading the next group before summing one.
 constexpr int kResidGroup = SV_RESID_GROUP;
 // The row-skipping pass: a wave streams SV_SKIP_CHUNKS chunks of
-// SV_SKIP_VECS vectors per lane, loading each chunk while it sums the last,
-// so its fixed costs (the request flag, the hand-off) cover more bytes.
+// SV_SKIP_VECS vectors per lane, loading each chunk while it sums the last.
+// Measured on MI355X (us per pass, B = 256 / B = 32, K = 7, V = 151936 bf16):
+// 6 x 2 (12 KB per wave) 93.9 / 31.6; 6 x 3 93.5 / 33.4; 4 x 3 94.7 / 33.3;
+// 8 x 2 99.2 / -; 8 x 4 103.6 / -; 12 x 1 99.5 / 30.3; 4 x 6 102.6 / 35.3.
 constexpr int kSkipVecsPerLane = SV_SKIP_VECS;
 constexpr int kSkipChunks = SV_SKIP_CHUNKS;
 // The same shape for the greedy chain's row-skipping pass (its waves are best

@@ -40,6 +40,7 @@ SAMPLE_GRID = [
     (2, 7, 151936, "bf16", 0.7, 20, 0.3),   # many segments and tiles per row
     (9, 1, 70001, "f32", 1.0, 3, 0.1),      # high acceptance, ragged
     (16, 0, 5000, "bf16", 1.0, 0, 1.0),     # K = 0: bonus draw only
+    (3, 3, 151936, "f32", 1.0, 20, 0.5),    # a position has more segments than a wave has lanes
 ]
 
 
