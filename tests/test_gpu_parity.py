@@ -41,6 +41,9 @@ SAMPLE_GRID = [
     (9, 1, 70001, "f32", 1.0, 3, 0.1),      # high acceptance, ragged
     (16, 0, 5000, "bf16", 1.0, 0, 1.0),     # K = 0: bonus draw only
     (3, 3, 151936, "f32", 1.0, 20, 0.5),    # a position has more segments than a wave has lanes
+    (4, 31, 2000, "bf16", 1.0, 0, 0.2),     # the largest K of the row-skipping pass
+    (4, 32, 2000, "f32", 1.0, 0, 0.2),      # the smallest K beyond it: every row read
+    (3, 40, 3000, "bf16", 1.0, 0, 0.3),
 ]
 
 
@@ -343,6 +346,12 @@ def test_trace_records_each_kernel():
     gpu_sample(w, lse=False)
     recs = sv.trace_end()
     assert [r[0] for r in recs] == ["skip_stats", "resid_mass", "resid_select"]
+    # beyond 31 drafts every row is read, lse outputs or not
+    wl = workloads.make_sample(2, 40, 3000, "bf16", 1.0, seed=7)
+    sv.trace_begin(64)
+    gpu_sample(wl, lse=False)
+    recs = sv.trace_end()
+    assert [r[0] for r in recs] == ["rowstats", "accept", "resid_mass", "resid_select"]
     wg = workloads.make_greedy(8, 3, 5000, "bf16", seed=6)
     sv.trace_begin(64)
     gpu_greedy(wg)
