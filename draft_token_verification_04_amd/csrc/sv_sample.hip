@@ -792,7 +792,8 @@ __global__ __launch_bounds__(kBlock) void k_skip_stats(
     const int r = static_cast<int>(rem - static_cast<long long>(b) * 2 * segs);
     const int kind = r / segs, sg = r - kind * segs;
     if (kind == 1 && p == K) return;  // no draft row at the bonus position
-    if (early ? skip_row_dead(ctl, b, p) : uniform(shared_load(&ctl.finished[b])) != 0) return;
+    // position 0's rows are always needed: no test, no wait before their loads
+    if (p > 0 && (early ? skip_row_dead(ctl, b, p) : uniform(shared_load(&ctl.finished[b])) != 0)) return;
 
     const long long rows_t = static_cast<long long>(B) * (K + 1);
     const long long gt = static_cast<long long>(b) * (K + 1) + p;
