@@ -285,12 +285,13 @@ def sample_parity(gpu, o, eps=1e-6):
             "unflagged_and_different": int((~flagged & diff).sum())}
 
 
-def bench_ngram(sv, torch, workloads, dev, reps):
+def bench_ngram(sv, torch, workloads, dev, reps, long=False):
     """spec_ngram_candidates on seeded repetitive token streams (B=256, up to
-    L=32768 tokens, 3-gram queries, 64 positions kept)."""
-    shp = workloads.NGRAM_SHAPE
+    L=32768 tokens, 3-gram queries, 64 positions kept; long: 64K..128K tokens)."""
+    shp = workloads.NGRAM_LONG_SHAPE if long else workloads.NGRAM_SHAPE
     B, L, n, cap = shp["B"], shp["L"], shp["n"], shp["cap"]
-    w = workloads.make_ngram(B, L, n, seed=20261207)
+    w = (workloads.make_ngram_long(B, L, n, seed=20261208) if long
+         else workloads.make_ngram(B, L, n, seed=20261207))
     ctx = torch.from_numpy(w["context"]).to(dev)
     lens = torch.from_numpy(w["lengths"]).to(dev)
     q = torch.from_numpy(w["queries"]).to(dev)
@@ -326,8 +327,8 @@ def bench_ngram(sv, torch, workloads, dev, reps):
     nbytes = tokens * 4  # every token read once
     kc, ke = statistics.mean(per["ngram_count"]), statistics.mean(per["ngram_emit"])
     return {
-        "workload": f"AdaPLD lexical retrieval: B={B} token streams of {L // 4}..{L} tokens, {n}-gram queries, "
-                    f"first {cap} candidates kept",
+        "workload": f"AdaPLD lexical retrieval: B={B} token streams of {L // 2 if long else L // 4}..{L} tokens, "
+                    f"{n}-gram queries, first {cap} candidates kept",
         "tokens": tokens, "bytes": nbytes, "call_ms": round(call_ms, 5),
         "count_ms": round(kc, 5), "emit_ms": round(ke, 5),
         "mean_candidates": round(float(cnt.float().mean().item()), 3),
@@ -1107,6 +1108,7 @@ def main():
     # AdaPLD lexical retrieval over 256 token streams of up to 32K tokens
     if "tree" in active:
         extras["ngram_candidates"] = bench_ngram(sv, torch, workloads, dev, reps)
+        extras["ngram_candidates_long"] = bench_ngram(sv, torch, workloads, dev, reps, long=True)
 
     # the greedy chain with the LM-head projection fused in (hidden states in,
     # logits never written), at the Qwen3-8B shape B=256 K=7 D=4096 V=151936

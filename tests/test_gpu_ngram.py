@@ -55,6 +55,50 @@ def test_windows_across_rows_and_chunks():
         assert o["count"][0] == len(ends)
 
 
+@pytest.mark.parametrize("n", [2, 5, 64])
+def test_windows_across_lanes_rows_and_chunks_of_four_token_lanes(n):
+    # a lane holds four consecutive positions of each 256-position row and a
+    # wave 2048 positions: windows planted to end at every offset around lane,
+    # row and chunk starts, and to reach back across them
+    note(f"ngram lane/row/chunk boundaries n={n}")
+    B, L = 4, 6400
+    rng = np.random.default_rng(11 + n)
+    ctx = rng.integers(1000, 1100, size=(B, L)).astype(np.int32)
+    gram = np.arange(1, n + 1, dtype=np.int32)
+    ends = [e for e in (63, 64, 67, 68, 255, 256, 258, 259, 511, 2047, 2048, 2049, 2050, 2111, 4095,
+                        4096, 6143, 6144, 6397) if e >= n - 1]
+    # keep the windows apart so each end is one candidate
+    chosen = []
+    for e in ends:
+        if all(abs(e - c) >= n for c in chosen):
+            chosen.append(e)
+    for b in range(B):
+        for e in chosen:
+            ctx[b, e - n + 1:e + 1] = gram
+    lens = np.array([6400, 6399, 4097, 2050], dtype=np.int32)
+    o = check(ctx, lens, np.tile(gram, (B, 1)), 32)
+    assert o["count"][0] == len(chosen)
+
+
+def test_unaligned_context():
+    # rows that are not 16-byte aligned (L % 4 != 0, and a base 4 bytes past
+    # an aligned address) take the element-by-element loads
+    note("ngram unaligned rows")
+    B, L, n = 5, 3001, 3
+    w = workloads.make_ngram(B, L, n, seed=9)
+    ctx, lens, q = w["context"], w["lengths"], w["queries"]
+    o = ngram.ngram_candidates(ctx, lens, q, 16)
+    buf = torch.zeros(B * L + 4, dtype=torch.int32, device="cuda")
+    view = buf[1:1 + B * L].view(B, L)
+    view.copy_(torch.from_numpy(ctx).cuda())
+    assert view.data_ptr() % 16 != 0
+    g = sv.spec_ngram_candidates(view, ints_to_dev(lens), ints_to_dev(q), 16)
+    torch.cuda.synchronize()
+    for k in ("count", "status", "positions"):
+        assert np.array_equal(g[k].cpu().numpy(), o[k]), k
+    assert o["count"].sum() > 0
+
+
 def test_longest_query_and_lengths_at_the_edges():
     note("ngram n=64 and edge lengths")
     B, L = 9, 1500
@@ -77,3 +121,13 @@ def test_full_size():
     w = workloads.make_ngram(s["B"], s["L"], s["n"], seed=20261207)
     o = check(w["context"], w["lengths"], w["queries"], s["cap"])
     assert (o["count"] > 0).mean() > 0.5
+
+
+def test_long_contexts_full_size():
+    # the bench's long shape: 256 streams of 64K..128K tokens
+    shp = workloads.NGRAM_LONG_SHAPE
+    note(f"ngram long contexts {shp}")
+    w = workloads.make_ngram_long(shp["B"], shp["L"], shp["n"], seed=20261208)
+    o = check(w["context"], w["lengths"], w["queries"], shp["cap"])
+    assert o["count"].sum() > shp["B"]
+

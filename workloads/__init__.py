@@ -479,7 +479,7 @@ def make_ngram(B, L, n, lengths=None, p_copy=0.3, p_tail_copy=0.6, working=4000,
     lengths = np.asarray(lengths, dtype=np.int32)
     ids = rng0.choice(V, size=working, replace=False).astype(np.int32)
     zipf = 1.0 / np.arange(1, working + 1)
-    zipf /= zipf.sum()
+    cdf = np.cumsum(zipf / zipf.sum())
     ctx = np.zeros((B, L), dtype=np.int32)
 
     def job(b):
@@ -496,11 +496,36 @@ def make_ngram(B, L, n, lengths=None, p_copy=0.3, p_tail_copy=0.6, working=4000,
                 src = int(rng.integers(0, t - seg)) if t - seg > 0 else 0
                 row[t:t + seg] = row[src:src + seg]
             else:
-                row[t:t + seg] = ids[rng.choice(working, size=seg, p=zipf)]
+                # Zipf draws by inverse CDF
+                row[t:t + seg] = ids[np.minimum(np.searchsorted(cdf, rng.random(seg), side="right"), working - 1)]
             t += seg
 
     with ThreadPoolExecutor(_threads()) as ex:
         list(ex.map(job, range(B)))
     q = np.stack([ctx[b, max(0, lengths[b] - n):lengths[b]] if lengths[b] >= n
                   else np.zeros(n, np.int32) for b in range(B)]).astype(np.int32)
+    return dict(context=ctx, lengths=lengths, queries=q, n=n)
+
+
+# Long contexts (128K tokens, a long-document reuse context): each request's
+# stream is its own base stream followed by the base streams of the next
+# requests in turn, so spans recur across the whole context as in a long
+# conversation that quotes earlier turns.  Built from make_ngram's streams by
+# concatenation only, so it costs no more to generate than the base shape.
+NGRAM_LONG_SHAPE = dict(B=256, L=131072, n=3, cap=64)
+
+
+def make_ngram_long(B, L, n, base_L=32768, seed=0) -> dict:
+    """Token streams [B, L] (L a multiple of base_L), lengths [B] between L/2 and
+    L, and queries [B, n] (the last n tokens before each length)."""
+    if L % base_L:
+        raise ValueError("L must be a multiple of base_L")
+    ss = seed if isinstance(seed, np.random.SeedSequence) else np.random.SeedSequence(seed)
+    s_base, s_len = ss.spawn(2)
+    base = make_ngram(B, base_L, n, lengths=np.full(B, base_L), seed=s_base)["context"]
+    reps = L // base_L
+    idx = (np.arange(B)[:, None] + np.arange(reps)[None, :]) % B
+    ctx = np.ascontiguousarray(base[idx].reshape(B, L))
+    lengths = np.random.default_rng(s_len).integers(L // 2, L + 1, size=B).astype(np.int32)
+    q = np.stack([ctx[b, lengths[b] - n:lengths[b]] for b in range(B)]).astype(np.int32)
     return dict(context=ctx, lengths=lengths, queries=q, n=n)
