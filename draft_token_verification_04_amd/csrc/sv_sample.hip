@@ -508,8 +508,9 @@ __global__ __launch_bounds__(kBlock) void k_resid_mass(
                 sp[k].get(xp);
                 sq[k].get(xq);
                 masses(xp, xq, D, d);
-                const double incl = wave_incl_scan(lane_total(d), lane);
-                if (lane == kWave - 1) out[t0 + k] = incl;
+                // the tile's total (only the total is kept)
+                const double tot = wave_sum(lane_total(d));
+                if (lane == kWave - 1) out[t0 + k] = tot;
             }
         }
     };
@@ -560,8 +561,8 @@ __global__ __launch_bounds__(kWave) void k_resid_select(
 #pragma unroll
                 for (int e = 0; e < P; ++e) xp[e] = -__builtin_huge_valf();
             masses(xp, xp, D, d);
-            const double inc = wave_incl_scan(lane_total(d), lane);
-            if (lane == kWave - 1) tm[t] = inc;
+            const double tot = wave_sum(lane_total(d));
+            if (lane == kWave - 1) tm[t] = tot;
         }
         __syncthreads();
         ls = 0.0;
