@@ -10,6 +10,7 @@
 
 #include "sv_device.hpp"
 #include "sv_internal.hpp"
+#include "sv_skip.hpp"
 
 namespace sv {
 
@@ -230,7 +231,9 @@ sv_status sample_impl(const void *target_logits, const void *draft_logits, const
     const long long rows_total = rows_t + static_cast<long long>(B) * K;
 
     hipError_t e = hipSuccess;
-    if (lse_target || lse_draft || !skip_supported(K)) {
+    const RowGeom gs = row_geom(V, dt, ptr_al, kSkipVecsPerLane * kSkipChunks);
+    if (lse_target || lse_draft || !skip_supported(K) ||
+        !skip_grid_fits(static_cast<long long>(K + 1) * B * 2 * gs.segs, gs.segs)) {
         // every row is read (its statistics feed the lse outputs)
         e = traced(SV_K_ROWSTATS, s, [&] {
             return launch_rowstats(target_logits, draft_logits, rows_t, rows_total, V, g, dt, sc, part_R,
@@ -246,7 +249,6 @@ sv_status sample_impl(const void *target_logits, const void *draft_logits, const
             });
     } else {
         // rows of positions after each request's first rejection are not read
-        const RowGeom gs = row_geom(V, dt, ptr_al, kSkipVecsPerLane * kSkipChunks);
         e = launch_skip(target_logits, draft_logits, draft_tokens, u_accept, u_sample, B, K, V, gs, dt, sc,
                         part_R, part_s, L2, ws + L.skipctl, accept_len, out_tokens, req_status, rp, s);
     }
@@ -337,9 +339,10 @@ sv_status spec_verify_greedy(const void *target_logits, const int32_t *draft_tok
     uint64_t *pk = reinterpret_cast<uint64_t *>(ws + L.part_k);
     hipStream_t s = stream;
     hipError_t e = hipSuccess;
-    if (SV_GREEDY_SKIP && skip_supported(K)) {
+    const RowGeom gs = row_geom(V, dt, aligned16(target_logits), kGSkipVecsPerLane * kGSkipChunks);
+    if (SV_GREEDY_SKIP && skip_supported(K) &&
+        skip_grid_fits(static_cast<long long>(K + 1) * B * gs.segs, gs.segs)) {
         // rows of positions after each request's first mismatch are not read
-        const RowGeom gs = row_geom(V, dt, aligned16(target_logits), kGSkipVecsPerLane * kGSkipChunks);
         e = launch_skip_match(target_logits, draft_tokens, B, K, V, gs, dt, pk,
                               reinterpret_cast<int32_t *>(ws + L.amax), ws + L.skipctl, accept_len,
                               out_tokens, req_status, s);
@@ -374,9 +377,10 @@ sv_status spec_verify_tree(const void *target_logits, const int32_t *node_tokens
     uint64_t *pk = reinterpret_cast<uint64_t *>(ws + L.part_k);
     hipStream_t s = stream;
     hipError_t e = hipSuccess;
-    if (SV_GREEDY_SKIP && tree_skip_supported(N)) {
+    const RowGeom gs = row_geom(V, dt, aligned16(target_logits), kGSkipVecsPerLane * kGSkipChunks);
+    if (SV_GREEDY_SKIP && tree_skip_supported(N) &&
+        skip_grid_fits(static_cast<long long>(N) * B * gs.segs, gs.segs)) {
         // rows of rejected nodes are not read
-        const RowGeom gs = row_geom(V, dt, aligned16(target_logits), kGSkipVecsPerLane * kGSkipChunks);
         e = launch_skip_tree(target_logits, node_tokens, parents, B, N, V, gs, dt, pk,
                              reinterpret_cast<int32_t *>(ws + L.amax), ws + L.skipctl, accept_len, path_nodes,
                              out_tokens, req_status, s);

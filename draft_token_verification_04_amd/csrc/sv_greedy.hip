@@ -347,19 +347,19 @@ __global__ __launch_bounds__(kBlock) void k_skip_argmax(const typename E::storag
                                                         int32_t *__restrict__ out_tokens,
                                                         int32_t *__restrict__ status) {
     const int lane = threadIdx.x & (kWave - 1);
-    const long long wave = static_cast<long long>(blockIdx.x) * kWavesPerBlock + (threadIdx.x >> 6);
-    const long long per_pos = static_cast<long long>(B) * segs;
-    if (wave >= per_pos * (K + 1)) return;
+    const unsigned wave = skip_wave_index();
+    const unsigned per_pos = static_cast<unsigned>(B) * static_cast<unsigned>(segs);
+    if (wave >= per_pos * static_cast<unsigned>(K + 1)) return;
     const int p = static_cast<int>(wave / per_pos);
-    const long long rem = wave - static_cast<long long>(p) * per_pos;
-    const int b = static_cast<int>(rem / segs);
-    const int sg = static_cast<int>(rem - static_cast<long long>(b) * segs);
+    const unsigned rem = wave - static_cast<unsigned>(p) * per_pos;
+    const int b = static_cast<int>(rem / static_cast<unsigned>(segs));
+    const int sg = static_cast<int>(rem - static_cast<unsigned>(b) * static_cast<unsigned>(segs));
     // position 0's rows are always needed: no test, no wait before their loads
     if (p > 0 && (early ? skip_row_dead(ctl, b, p) : uniform(shared_load(&ctl.finished[b])) != 0)) return;
 
     const long long row = static_cast<long long>(b) * (K + 1) + p;
-    const int v0 = static_cast<int>((static_cast<long long>(sg) * nvec) / segs);
-    const int v1 = static_cast<int>((static_cast<long long>(sg + 1) * nvec) / segs);
+    int v0, v1;
+    skip_segment(sg, nvec, segs, v0, v1);
     const uint64_t key = segment_argmax_chunked<E, ALIGNED, U, kGSkipChunks>(L + row * V, V, v0, v1, lane);
 #if SV_SKIP_POLL
     // Every wave leaves its segment's key (never 0; the keys start at 0) and
@@ -595,21 +595,21 @@ __global__ __launch_bounds__(kBlock) void k_skip_tree(const typename E::storage 
                                                       int32_t *__restrict__ out_tokens,
                                                       int32_t *__restrict__ status) {
     const int lane = threadIdx.x & (kWave - 1);
-    const long long wave = static_cast<long long>(blockIdx.x) * kWavesPerBlock + (threadIdx.x >> 6);
-    const long long per_slot = static_cast<long long>(B) * segs;
-    if (wave >= per_slot * N) return;
+    const unsigned wave = skip_wave_index();
+    const unsigned per_slot = static_cast<unsigned>(B) * static_cast<unsigned>(segs);
+    if (wave >= per_slot * static_cast<unsigned>(N)) return;
     const int slot = static_cast<int>(wave / per_slot);
-    const long long rem = wave - static_cast<long long>(slot) * per_slot;
-    const int b = static_cast<int>(rem / segs);
-    const int sg = static_cast<int>(rem - static_cast<long long>(b) * segs);
+    const unsigned rem = wave - static_cast<unsigned>(slot) * per_slot;
+    const int b = static_cast<int>(rem / static_cast<unsigned>(segs));
+    const int sg = static_cast<int>(rem - static_cast<unsigned>(b) * static_cast<unsigned>(segs));
     const long long base = static_cast<long long>(b) * N;
     const int j = uniform(ctl.order[base + slot]);  // issued beside the state load
     // slot 0 holds the root, whose row is always needed
     if (slot > 0 && (uniform(shared_load(&ctl.state[base + slot])) & kRejected)) return;
 
     const long long row = base + j;
-    const int v0 = static_cast<int>((static_cast<long long>(sg) * nvec) / segs);
-    const int v1 = static_cast<int>((static_cast<long long>(sg + 1) * nvec) / segs);
+    int v0, v1;
+    skip_segment(sg, nvec, segs, v0, v1);
     const uint64_t key = segment_argmax_chunked<E, ALIGNED, U, kGSkipChunks>(L + row * V, V, v0, v1, lane);
 #if SV_SKIP_POLL
     // keys handed to the row's last segment as in the chain pass (the prep

@@ -784,13 +784,13 @@ __global__ __launch_bounds__(kBlock) void k_skip_stats(
     double *part_s, double *L2, SkipCtl ctl, int early, int32_t *__restrict__ accept_len,
     int32_t *__restrict__ out_tokens, int32_t *__restrict__ status, ResidParam *__restrict__ rp) {
     const int lane = threadIdx.x & (kWave - 1);
-    const long long wave = static_cast<long long>(blockIdx.x) * kWavesPerBlock + (threadIdx.x >> 6);
-    const long long per_pos = static_cast<long long>(B) * 2 * segs;
-    if (wave >= per_pos * (K + 1)) return;
+    const unsigned wave = skip_wave_index();
+    const unsigned per_pos = static_cast<unsigned>(B) * 2u * static_cast<unsigned>(segs);
+    if (wave >= per_pos * static_cast<unsigned>(K + 1)) return;
     const int p = static_cast<int>(wave / per_pos);
-    const long long rem = wave - static_cast<long long>(p) * per_pos;
-    const int b = static_cast<int>(rem / (2 * segs));
-    const int r = static_cast<int>(rem - static_cast<long long>(b) * 2 * segs);
+    const unsigned rem = wave - static_cast<unsigned>(p) * per_pos;
+    const int b = static_cast<int>(rem / (2u * static_cast<unsigned>(segs)));
+    const int r = static_cast<int>(rem - static_cast<unsigned>(b) * 2u * static_cast<unsigned>(segs));
     const int kind = r / segs, sg = r - kind * segs;
     if (kind == 1 && p == K) return;  // no draft row at the bonus position
     // position 0's rows are always needed: no test, no wait before their loads
@@ -802,8 +802,8 @@ __global__ __launch_bounds__(kBlock) void k_skip_stats(
     const long long g = kind == 0 ? gt : gd;
     const typename E::storage *base = kind == 0 ? tgt + gt * static_cast<long long>(V)
                                                 : drf + (static_cast<long long>(b) * K + p) * static_cast<long long>(V);
-    const int v0 = static_cast<int>((static_cast<long long>(sg) * nvec) / segs);
-    const int v1 = static_cast<int>((static_cast<long long>(sg + 1) * nvec) / segs);
+    int v0, v1;
+    skip_segment(sg, nvec, segs, v0, v1);
     float R;
     double sum;
     segment_stats_chunked<E, ALIGNED, U, kSkipChunks>(base, V, v0, v1, c_hi, c_lo, lane, R, sum);

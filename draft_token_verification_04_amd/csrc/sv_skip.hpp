@@ -75,6 +75,30 @@ inline bool skip_early(int B, int rows_per_position, int V, size_t elem) {
 // them (the caller clears them together with other words).
 void skip_ctl_carve(void *base, int B, int K, SkipCtl *ctl);
 
+// The skip passes find a wave's position, request and segment with 32-bit
+// scalar arithmetic (a few instructions, against a long 64-bit vector
+// division every wave - the many that find their row settled included -
+// would otherwise run first): the grid and the segment count must fit.
+inline bool skip_grid_fits(long long waves, int segs) {
+    return waves + kWavesPerBlock <= 0x7fffffffLL && segs >= 1 && segs <= 46340;
+}
+
+// This wave's index in the grid, as a scalar.
+__device__ __forceinline__ unsigned skip_wave_index() {
+    return blockIdx.x * static_cast<unsigned>(kWavesPerBlock) + uniform(static_cast<unsigned>(threadIdx.x >> 6));
+}
+
+// Vectors [v0, v1) of segment sg when a row's nvec vectors are cut into segs:
+// v0 = floor(sg nvec / segs), computed as sg q + floor(sg r / segs) with
+// (q, r) = nvec divmod segs, so that no product leaves 32 bits (segs <= 46340).
+__device__ __forceinline__ void skip_segment(int sg, int nvec, int segs, int &v0, int &v1) {
+    const unsigned q = static_cast<unsigned>(nvec) / static_cast<unsigned>(segs);
+    const unsigned r = static_cast<unsigned>(nvec) - q * static_cast<unsigned>(segs);
+    const unsigned s0 = static_cast<unsigned>(sg), s1 = s0 + 1u;
+    v0 = static_cast<int>(s0 * q + (s0 * r) / static_cast<unsigned>(segs));
+    v1 = static_cast<int>(s1 * q + (s1 * r) / static_cast<unsigned>(segs));
+}
+
 // The decided prefix of a request mask: the accepted length n once every
 // position up to the first rejection (or every position 0..K) is decided, else
 // -1.  Monotone: a mask with more bits set has the same prefix once it has one,
