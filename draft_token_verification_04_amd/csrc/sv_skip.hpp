@@ -5,20 +5,24 @@
 // mismatched) draft: every draft after it is discarded, and the one drawn token
 // comes from the rejected position's row.  A row-skipping pass is one launch
 // over every (position p, request b, segment) in position-major order, so the
-// segments of position p are handed out before those of p+1.  A wave first
-// reads its request's `finished` flag and skips its segment when the request
-// is already decided.  The last wave to finish the segments of (b, p), found by
-// a per-(b, p) ticket, takes the decision of position p and records it in the
-// request's mask: bit p = "position p decided", bit 32+p = "draft p rejected"
-// (position K's bit means its bonus row is ready).  The request is decided once
-// the mask holds a rejection with every earlier position decided, or every
-// position 0..K decided without one; whichever decider completes that prefix
-// finishes the request and raises the flag.  The stochastic pass picks that
-// decider by compare-and-swap after its decision; the greedy pass takes the
-// one whose atomic OR turned the prefix from undecided to decided (at most one
-// can: see skip_prefix), which saves that round trip.
-// Rows of positions after the first rejection are read only by waves that
-// started before the decision was known.  Nothing waits.
+// segments of position p are handed out before those of p+1.  A wave of a
+// position after 0 first tests whether its request is settled (its finished
+// flag, or a rejection already recorded at an earlier position, see
+// skip_early) and skips its segment if so.  Every other wave of (b, p) leaves
+// its segment's partial in a word that starts at 0 and is never 0 once
+// written, and ends; the wave of the last segment, dispatched after them,
+// polls for those words (a word that never comes belongs to a wave that found
+// the request settled, which the poller then finds too), takes the decision of
+// position p and records it in the request's mask with one atomic OR: bit p =
+// "position p decided", bit 32+p = "draft p rejected" (position K's bit means
+// its bonus row is ready).  The request is decided once the mask holds a
+// rejection with every earlier position decided, or every position 0..K
+// decided without one; the decider whose OR turned that prefix from undecided
+// to decided (exactly one can: see skip_prefix) finishes the request and
+// raises the flag.  Rows of positions after the first rejection are read only
+// by waves that started before the decision was known.  The forms with a
+// per-(b, p) ticket and a compare-and-swap for the finisher remain as
+// compile-time alternatives (SV_SKIP_POLL, SV_SKIP_FASTDECIDE).
 #pragma once
 
 #include "sv_device.hpp"
