@@ -68,6 +68,9 @@ KERNEL_SOURCES = {
     "ngram": ["draft_token_verification_04_amd/csrc/sv_ngram.hip",
               "draft_token_verification_04_amd/csrc/sv_device.hpp",
               "draft_token_verification_04_amd/csrc/sv_internal.hpp"],
+    "ngram_long": ["draft_token_verification_04_amd/csrc/sv_ngram.hip",
+                   "draft_token_verification_04_amd/csrc/sv_device.hpp",
+                   "draft_token_verification_04_amd/csrc/sv_internal.hpp"],
     "commit": ["draft_token_verification_04_amd/csrc/sv_commit.hip",
                "draft_token_verification_04_amd/csrc/sv_device.hpp",
                "draft_token_verification_04_amd/csrc/sv_internal.hpp"],
@@ -335,7 +338,7 @@ def bench_ngram(sv, torch, workloads, dev, reps, long=False):
         "roofline": {"bound": "hbm", "kernel": "ngram_count", "achieved": round(nbytes / (kc * 1e-3) / 1e9, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(nbytes / (kc * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-                     "traffic": (stored_traffic("ngram") or {}).get("bytes_per_launch")},
+                     "traffic": (stored_traffic("ngram_long" if long else "ngram") or {}).get("bytes_per_launch")},
     }
 
 
