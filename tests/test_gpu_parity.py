@@ -44,6 +44,7 @@ SAMPLE_GRID = [
     (4, 31, 2000, "bf16", 1.0, 0, 0.2),     # the largest K of the row-skipping pass
     (4, 32, 2000, "f32", 1.0, 0, 0.2),      # the smallest K beyond it: every row read
     (3, 40, 3000, "bf16", 1.0, 0, 0.3),
+    (4, 5, 262144, "bf16", 0.8, 10, 0.3),   # a 256K vocabulary: 86 segment partials per position
 ]
 
 
@@ -77,7 +78,8 @@ def test_sample_workloads_full_size(c, lse):
 # K <= 31 takes the row-skipping pass, larger K the full read (argmax + match).
 GREEDY_GRID = [(1, 0, 8, "f32"), (5, 3, 1000, "bf16"), (6, 7, 1001, "bf16"), (33, 7, 4100, "f32"),
                (3, 7, 151936, "bf16"), (64, 70, 333, "bf16"), (2, 1, 1, "f32"),
-               (40, 31, 2500, "bf16"), (40, 32, 2500, "bf16"), (7, 31, 20001, "f32")]
+               (40, 31, 2500, "bf16"), (40, 32, 2500, "bf16"), (7, 31, 20001, "f32"),
+               (4, 7, 262144, "bf16")]
 
 
 @pytest.mark.parametrize("case", GREEDY_GRID, ids=lambda c: "B{}K{}V{}{}".format(*c))
@@ -133,7 +135,7 @@ def test_tree_small_random_and_degenerate():
     # N <= 64 takes the row-skipping pass, larger N the full read (argmax + tree walk)
     for (B, N, V, dt) in [(50, 12, 4, "f32"), (40, 33, 1001, "bf16"), (8, 300, 64, "bf16"),
                           (3, 1, 100, "f32"), (30, 64, 500, "bf16"), (30, 65, 500, "bf16"),
-                          (15, 2, 7, "f32")]:
+                          (15, 2, 7, "f32"), (4, 17, 262144, "bf16")]:
         L = rng.integers(-1, 2, size=(B, N, V)).astype(np.float32) if V < 10 else \
             rng.standard_normal((B, N, V)).astype(np.float32)
         LL = L if dt == "f32" else workloads.to_bf16_bits(L)
