@@ -198,6 +198,44 @@ __device__ __forceinline__ double wave_sum(double v) {
     return v;
 }
 
+// One DPP step of a row (16-lane) reduction on a double: v + v[lane ^ ...]
+// for the given row-local pattern, moved as two 32-bit halves.
+template <int CTRL>
+__device__ __forceinline__ double row_step(double v) {
+    const unsigned long long u = __double_as_longlong(v);
+    const int lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(u), CTRL, 0xf, 0xf, false);
+    const int hi = __builtin_amdgcn_update_dpp(0, static_cast<int>(u >> 32), CTRL, 0xf, 0xf, false);
+    return v + __longlong_as_double(static_cast<long long>((static_cast<unsigned long long>(static_cast<unsigned>(hi)) << 32) |
+                                                          static_cast<unsigned>(lo)));
+}
+
+// The totals of two per-lane values over the wave, with cross-lane moves only
+// (no LDS round trips): lanes 0..31 end with a's total, lanes 32..63 with b's.
+// The half-wave swap puts a's two halves beside each other in lanes 0..31 and
+// b's in 32..63 (one add then leaves 32 partials of each), the row swap pairs
+// rows 0 with 1 and 2 with 3, and four DPP steps (neighbour, pair of
+// neighbours, half-row mirror, row mirror) finish each row.
+__device__ __forceinline__ double wave_sum_pair(double a, double b) {
+    const unsigned long long ua = __double_as_longlong(a), ub = __double_as_longlong(b);
+    const auto lo = __builtin_amdgcn_permlane32_swap(static_cast<unsigned>(ua), static_cast<unsigned>(ub), false, false);
+    const auto hi = __builtin_amdgcn_permlane32_swap(static_cast<unsigned>(ua >> 32), static_cast<unsigned>(ub >> 32),
+                                                     false, false);
+    auto join = [](unsigned l, unsigned h) {
+        return __longlong_as_double(static_cast<long long>((static_cast<unsigned long long>(h) << 32) | l));
+    };
+    double v = join(lo[0], hi[0]) + join(lo[1], hi[1]);
+    const unsigned long long uv = __double_as_longlong(v);
+    const auto lo2 = __builtin_amdgcn_permlane16_swap(static_cast<unsigned>(uv), static_cast<unsigned>(uv), false, false);
+    const auto hi2 = __builtin_amdgcn_permlane16_swap(static_cast<unsigned>(uv >> 32), static_cast<unsigned>(uv >> 32),
+                                                      false, false);
+    v = join(lo2[0], hi2[0]) + join(lo2[1], hi2[1]);
+    v = row_step<0xb1>(v);   // quad_perm [1, 0, 3, 2]
+    v = row_step<0x4e>(v);   // quad_perm [2, 3, 0, 1]
+    v = row_step<0x141>(v);  // row_half_mirror
+    v = row_step<0x140>(v);  // row_mirror
+    return v;
+}
+
 // Inclusive prefix sum over lanes (Hillis-Steele; fixed order).
 __device__ __forceinline__ double wave_incl_scan(double v, int lane) {
 #pragma unroll

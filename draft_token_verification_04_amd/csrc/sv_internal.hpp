@@ -115,6 +115,10 @@ struct ResidParam {
     long long row_q;  // global draft row index (pair mode only)
     int mode;      // 1 = residual max(0, p - q), 0 = p alone (bonus)
     int pos;       // output slot n (= accept_len)
+    // The draw's per-row constants: with R = L2 + 1 split as R_hi + R_lo
+    // (R_hi the nearest float), Rp_hi and Rq_hi for the two rows, and
+    // r = 2^(Rq_lo - Rp_lo) (1 for the bonus).
+    float Rp_hi, Rq_hi, r;
 };
 
 // Byte offsets of the workspace regions.

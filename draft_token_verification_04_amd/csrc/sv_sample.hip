@@ -48,6 +48,24 @@ namespace {
 
 constexpr double kLn2 = 0.6931471805599453094172321214581766;
 
+// The draw's per-row constants (used by the residual kernels): half the
+// probability of logit x in a row with log2-normaliser L2 is 2^(x c - R),
+// R = L2 + 1.  With R = R_hi + R_lo, R_hi the nearest float, the kernels form
+// t(x) = x c_lo + (x c_hi - R_hi) with two fmas; 2^t(x) then differs from the
+// half-probability by the factor 2^R_lo, the same for a whole row.  The draw
+// only compares masses of one row pair, so the target row's factor is carried
+// over to the draft row's as r = 2^(Rq_lo - Rp_lo), and the common factor
+// that remains is dropped.  A row with no finite logit (R = -inf) keeps
+// R_lo = 0.
+__device__ __forceinline__ void draw_constants(ResidParam &P) {
+    const double Rp = P.L2p + 1.0, Rq = P.mode ? P.L2q + 1.0 : 1.0;
+    P.Rp_hi = static_cast<float>(Rp);
+    P.Rq_hi = static_cast<float>(Rq);
+    const double lp = isfinite(Rp) ? Rp - static_cast<double>(P.Rp_hi) : 0.0;
+    const double lq = isfinite(Rq) ? Rq - static_cast<double>(P.Rq_hi) : 0.0;
+    P.r = P.mode ? static_cast<float>(exp2(lq - lp)) : 1.0f;
+}
+
 // ---- S1: per-segment row statistics ---------------------------------------------
 
 // One wave's (R, s) over vectors [v0, v1) of a row: R = fp32(max * c_hi) and
@@ -406,16 +424,18 @@ __global__ __launch_bounds__(kBlock) void k_accept(
             P.row_q = 0;
             P.L2q = 0.0;
         }
+        draw_constants(P);
         rp[b] = P;
     }
 }
 
 // ---- S4/S5: the drawn token -------------------------------------------------------
 
-// Per-request constants of the draw: p(v) = 2^(x c - L2p), split so that
-// x*c_hi - Rp_hi and x*c_lo - Rp_lo are each one correctly rounded fma.
+// Per-request constants of the draw (see draw_constants): element masses are
+// taken up to a factor common to the request's row pair, which the inverse
+// CDF over them does not see.
 struct Draw {
-    float c_hi, c_lo, Rp_hi, Rp_lo, Rq_hi, Rq_lo;
+    float c_hi, c_lo, Rp, Rq, r;
     int mode;
 };
 
@@ -423,28 +443,45 @@ __device__ __forceinline__ Draw make_draw(const ResidParam &P, float c_hi, float
     Draw d;
     d.c_hi = c_hi;
     d.c_lo = c_lo;
-    d.Rp_hi = static_cast<float>(P.L2p);
-    d.Rp_lo = static_cast<float>(P.L2p - static_cast<double>(d.Rp_hi));
-    d.Rq_hi = static_cast<float>(P.L2q);
-    d.Rq_lo = static_cast<float>(P.L2q - static_cast<double>(d.Rq_hi));
+    d.Rp = P.Rp_hi;
+    d.Rq = P.Rq_hi;
+    d.r = P.r;
     d.mode = mode;
     return d;
 }
 
-// Mass of each element of one vector: max(0, p - q) (mode 1) or p (mode 0).
-template <int P>
+// 2^t(x), t(x) = x c_lo + (x c_hi - R): the first fma cancels exactly
+// against R, the second adds the low part of the scale (c_lo > 0, so -inf
+// stays -inf).
+__device__ __forceinline__ float half_prob(float x, const Draw &D, float R) {
+    return fast_exp2(fmaf(x, D.c_lo, fmaf(x, D.c_hi, -R)));
+}
+
+// Mass of each element of one vector, up to the row pair's common factor:
+// max(0, p - q) (PAIR) or p.  A pair's element mass is below 1 (the halving
+// in draw_constants), so max(0, .) is the clamp to [0, 1], which the
+// hardware applies to the fma's result at no cost (a NaN, as from a row with
+// no finite logit, clamps to 0 as fmaxf would make it).
+template <bool PAIR, int P>
 __device__ __forceinline__ void masses(const float (&xp)[P], const float (&xq)[P], const Draw &D,
                                        float (&d)[P]) {
 #pragma unroll
     for (int e = 0; e < P; ++e) {
-        const float p = fast_exp2(fmaf(xp[e], D.c_hi, -D.Rp_hi) + fmaf(xp[e], D.c_lo, -D.Rp_lo));
-        if (D.mode) {
-            const float q = fast_exp2(fmaf(xq[e], D.c_hi, -D.Rq_hi) + fmaf(xq[e], D.c_lo, -D.Rq_lo));
-            d[e] = fmaxf(p - q, 0.0f);
-        } else {
+        const float p = half_prob(xp[e], D, D.Rp);
+        if (PAIR)
+            d[e] = __builtin_amdgcn_fmed3f(fmaf(p, D.r, -half_prob(xq[e], D, D.Rq)), 0.0f, 1.0f);
+        else
             d[e] = p;
-        }
     }
+}
+
+template <int P>
+__device__ __forceinline__ void masses(const float (&xp)[P], const float (&xq)[P], const Draw &D,
+                                       float (&d)[P]) {
+    if (D.mode)
+        masses<true>(xp, xq, D, d);
+    else
+        masses<false>(xp, xq, D, d);
 }
 
 template <int P>
@@ -461,68 +498,93 @@ template <typename E, typename EQ, bool ALIGNED>
 using DraftStaged =
     typename std::conditional<std::is_same<E, EQ>::value, Staged<E, ALIGNED>, Staged4<EQ, ALIGNED>>::type;
 
-// Residual (or bonus) mass of each 64-vector tile of the row each request
-// draws from.  A wave owns `tpw` consecutive tiles of one request and walks
-// them in groups of G, loading the next group before it sums the current one.
-template <typename E, typename EQ, bool ALIGNED, int G>
-__global__ __launch_bounds__(kBlock) void k_resid_mass(
-    const typename E::storage *__restrict__ tgt, const typename EQ::storage *__restrict__ drf,
-    int B, int V, int nvec, int ntiles, int wpr, int tpw, float c_hi, float c_lo,
-    const ResidParam *__restrict__ rp, double *__restrict__ tile_mass) {
+// Tiles [t_begin, t_end) of one request's draw row(s), walked in groups of G
+// with the next group's loads in flight while one group is summed.  Every
+// load of the aligned form is issued unconditionally, so that the wait before
+// a group's sums covers that group's loads only: a vector past the row's end
+// re-reads the row's last vector, and its masses are zeroed afterwards.
+template <typename E, typename EQ, bool ALIGNED, int G, bool PAIR>
+__device__ __forceinline__ void resid_tiles(const typename E::storage *__restrict__ prow,
+                                            const typename EQ::storage *__restrict__ qrow, int V, int nvec,
+                                            int t_begin, int t_end, const Draw &D, int lane,
+                                            double *__restrict__ out) {
     constexpr int P = E::kPerVec;
-    const int lane = threadIdx.x & (kWave - 1);
-    const long long wave = static_cast<long long>(blockIdx.x) * kWavesPerBlock + (threadIdx.x >> 6);
-    if (wave >= static_cast<long long>(B) * wpr) return;
-    const int b = static_cast<int>(wave / wpr);
-    const int w = static_cast<int>(wave - static_cast<long long>(b) * wpr);
-    const ResidParam Pm = rp[b];
-    const Draw D = make_draw(Pm, c_hi, c_lo, Pm.mode);
-    const typename E::storage *prow = tgt + Pm.row_p * static_cast<long long>(V);
-    const typename EQ::storage *qrow = D.mode ? drf + Pm.row_q * static_cast<long long>(V) : nullptr;
-    const int t_begin = w * tpw;
-    const int t_end = min(ntiles, t_begin + tpw);
-    double *out = tile_mass + static_cast<long long>(b) * ntiles;
-
     using QS = DraftStaged<E, EQ, ALIGNED>;
     auto load = [&](Staged<E, ALIGNED>(&sp)[G], QS(&sq)[G], int t0) {
 #pragma unroll
         for (int k = 0; k < G; ++k) {
-            const int j = (t0 + k) * kWave + lane;
-            if (t0 + k < t_end && j < nvec) {
-                sp[k].load(prow, V, j);
-                if (D.mode)
-                    sq[k].load(qrow, V, j);
-                else
-                    sq[k].set_neg_inf();
-            } else {
-                sp[k].set_neg_inf();
-                sq[k].set_neg_inf();
-            }
+            const int j = min((t0 + k) * kWave + lane, nvec - 1);
+            sp[k].load(prow, V, j);
+            if (PAIR) sq[k].load(qrow, V, j);
         }
     };
+    // the tiles' totals (only the totals are kept), two tiles per reduction
     auto sum = [&](const Staged<E, ALIGNED>(&sp)[G], const QS(&sq)[G], int t0) {
+        double part[G];
 #pragma unroll
         for (int k = 0; k < G; ++k) {
-            if (t0 + k < t_end) {  // uniform across the wave
+            const int t = t0 + k;
+            part[k] = 0.0;
+            if (t < t_end) {  // uniform across the wave
                 float xp[P], xq[P], d[P];
                 sp[k].get(xp);
-                sq[k].get(xq);
-                masses(xp, xq, D, d);
-                // the tile's total (only the total is kept)
-                const double tot = wave_sum(lane_total(d));
-                if (lane == kWave - 1) out[t0 + k] = tot;
+                if (PAIR) sq[k].get(xq);
+                masses<PAIR>(xp, xq, D, d);
+                const float lt = pairwise_sum(d);
+                part[k] = t * kWave + lane < nvec ? static_cast<double>(lt) : 0.0;  // else a re-read past the row's end
             }
+        }
+#pragma unroll
+        for (int k = 0; k < G; k += 2) {
+            const double tot = wave_sum_pair(part[k], k + 1 < G ? part[k + 1] : 0.0);
+            if (lane == 0 && t0 + k < t_end) out[t0 + k] = tot;
+            if (lane == kWave / 2 && k + 1 < G && t0 + k + 1 < t_end) out[t0 + k + 1] = tot;
         }
     };
     Staged<E, ALIGNED> ap[G], bp[G];
     QS aq[G], bq[G];
-    load(ap, aq, t_begin);
-    for (int t0 = t_begin; t0 < t_end; t0 += 2 * G) {
+    int t0 = t_begin;
+    load(ap, aq, t0);
+    // whole pairs of groups while another group follows them
+    for (; t0 + 2 * G < t_end; t0 += 2 * G) {
         load(bp, bq, t0 + G);
         sum(ap, aq, t0);
         load(ap, aq, t0 + 2 * G);
         sum(bp, bq, t0 + G);
     }
+    if (t0 + G < t_end) {
+        load(bp, bq, t0 + G);
+        sum(ap, aq, t0);
+        sum(bp, bq, t0 + G);
+    } else {
+        sum(ap, aq, t0);
+    }
+}
+
+// Residual (or bonus) mass of each 64-vector tile of the row each request
+// draws from.  A wave owns `tpw` consecutive tiles of one request; its
+// position, request and draw mode are scalars.
+template <typename E, typename EQ, bool ALIGNED, int G>
+__global__ __launch_bounds__(kBlock) void k_resid_mass(
+    const typename E::storage *__restrict__ tgt, const typename EQ::storage *__restrict__ drf,
+    int B, int V, int nvec, int ntiles, int wpr, int tpw, float c_hi, float c_lo,
+    const ResidParam *__restrict__ rp, double *__restrict__ tile_mass) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const unsigned wave = blockIdx.x * static_cast<unsigned>(kWavesPerBlock) + uniform(static_cast<unsigned>(threadIdx.x >> 6));
+    if (wave >= static_cast<unsigned>(B) * static_cast<unsigned>(wpr)) return;
+    const int b = static_cast<int>(wave / static_cast<unsigned>(wpr));
+    const int w = static_cast<int>(wave - static_cast<unsigned>(b) * static_cast<unsigned>(wpr));
+    const ResidParam &Pm = rp[b];
+    const Draw D = make_draw(Pm, c_hi, c_lo, uniform(Pm.mode));
+    const typename E::storage *prow = tgt + Pm.row_p * static_cast<long long>(V);
+    const int t_begin = w * tpw;
+    const int t_end = min(ntiles, t_begin + tpw);
+    double *out = tile_mass + static_cast<long long>(b) * ntiles;
+    if (D.mode)
+        resid_tiles<E, EQ, ALIGNED, G, true>(prow, drf + Pm.row_q * static_cast<long long>(V), V, nvec, t_begin,
+                                             t_end, D, lane, out);
+    else
+        resid_tiles<E, EQ, ALIGNED, G, false>(prow, nullptr, V, nvec, t_begin, t_end, D, lane, out);
 }
 
 template <typename E, typename EQ, bool ALIGNED>
@@ -772,6 +834,7 @@ __device__ __forceinline__ void skip_finish(const int32_t *__restrict__ xb, cons
         P.mode = mode;
         P.row_q = mode ? static_cast<long long>(b) * K + n : 0;
         P.L2q = mode ? L2q : 0.0;
+        draw_constants(P);
         rp[b] = P;
     }
 }
@@ -781,7 +844,7 @@ __global__ __launch_bounds__(kBlock) void k_skip_stats(
     const typename E::storage *__restrict__ tgt, const typename E::storage *__restrict__ drf,
     const int32_t *__restrict__ drafts, const float *__restrict__ ua, const float *__restrict__ us,
     int B, int K, int V, int nvec, int segs, double c, float c_hi, float c_lo, float *part_R,
-    double *part_s, double *L2, SkipCtl ctl, int early, int32_t *__restrict__ accept_len,
+    double *part_s, double *L2, SkipCtl ctl, int early, int rot, int32_t *__restrict__ accept_len,
     int32_t *__restrict__ out_tokens, int32_t *__restrict__ status, ResidParam *__restrict__ rp) {
     const int lane = threadIdx.x & (kWave - 1);
     const unsigned wave = skip_wave_index();
@@ -789,9 +852,10 @@ __global__ __launch_bounds__(kBlock) void k_skip_stats(
     if (wave >= per_pos * static_cast<unsigned>(K + 1)) return;
     const int p = static_cast<int>(wave / per_pos);
     const unsigned rem = wave - static_cast<unsigned>(p) * per_pos;
-    const int b = static_cast<int>(rem / (2u * static_cast<unsigned>(segs)));
-    const int r = static_cast<int>(rem - static_cast<unsigned>(b) * 2u * static_cast<unsigned>(segs));
+    const unsigned slot = rem / (2u * static_cast<unsigned>(segs));
+    const int r = static_cast<int>(rem - slot * 2u * static_cast<unsigned>(segs));
     const int kind = r / segs, sg = r - kind * segs;
+    const int b = skip_request(slot, p, B, rot);
     if (kind == 1 && p == K) return;  // no draft row at the bonus position
     // position 0's rows are always needed: no test, no wait before their loads
     if (p > 0 && (early ? skip_row_dead(ctl, b, p) : uniform(shared_load(&ctl.finished[b])) != 0)) return;
@@ -940,10 +1004,11 @@ hipError_t skip_stats_t(const void *tgt, const void *drf, const int32_t *drafts,
     using T = typename E::storage;
     const long long nwaves = static_cast<long long>(K + 1) * B * 2 * g.segs;
     const long long blocks = (nwaves + kWavesPerBlock - 1) / kWavesPerBlock;
+    const bool early = skip_early(B, 2, V, sizeof(T));
     return launch_kernel(k_skip_stats<E, ALIGNED, kSkipVecsPerLane>, dim3(static_cast<unsigned>(blocks)),
                          dim3(kBlock), 0, s, static_cast<const T *>(tgt), static_cast<const T *>(drf),
                          drafts, ua, us, B, K, V, g.nvec, g.segs, sc.c, sc.c_hi, sc.c_lo, part_R, part_s,
-                         L2, ctl, static_cast<int>(skip_early(B, 2, V, sizeof(T))), accept_len, out_tokens, status,
+                         L2, ctl, static_cast<int>(early), skip_rotation(B, early), accept_len, out_tokens, status,
                          rp);
 }
 
