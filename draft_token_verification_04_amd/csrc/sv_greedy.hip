@@ -342,7 +342,7 @@ template <typename E, bool ALIGNED, int U>
 __global__ __launch_bounds__(kBlock) void k_skip_argmax(const typename E::storage *__restrict__ L,
                                                         const int32_t *__restrict__ drafts, int B, int K,
                                                         int V, int nvec, int segs, uint64_t *part_k,
-                                                        int32_t *amax, SkipCtl ctl, int early,
+                                                        int32_t *amax, SkipCtl ctl, int early, int rot,
                                                         int32_t *__restrict__ accept_len,
                                                         int32_t *__restrict__ out_tokens,
                                                         int32_t *__restrict__ status) {
@@ -352,8 +352,9 @@ __global__ __launch_bounds__(kBlock) void k_skip_argmax(const typename E::storag
     if (wave >= per_pos * static_cast<unsigned>(K + 1)) return;
     const int p = static_cast<int>(wave / per_pos);
     const unsigned rem = wave - static_cast<unsigned>(p) * per_pos;
-    const int b = static_cast<int>(rem / static_cast<unsigned>(segs));
-    const int sg = static_cast<int>(rem - static_cast<unsigned>(b) * static_cast<unsigned>(segs));
+    const unsigned slot = rem / static_cast<unsigned>(segs);
+    const int sg = static_cast<int>(rem - slot * static_cast<unsigned>(segs));
+    const int b = skip_request(slot, p, B, rot);
     // position 0's rows are always needed: no test, no wait before their loads
     if (p > 0 && (early ? skip_row_dead(ctl, b, p) : uniform(shared_load(&ctl.finished[b])) != 0)) return;
 
@@ -589,8 +590,8 @@ template <typename E, bool ALIGNED, int U>
 __global__ __launch_bounds__(kBlock) void k_skip_tree(const typename E::storage *__restrict__ L,
                                                       const int32_t *__restrict__ tok,
                                                       const int32_t *__restrict__ par, int B, int N, int V,
-                                                      int nvec, int segs, uint64_t *part_k, int32_t *amax,
-                                                      TreeCtl ctl, int32_t *__restrict__ accept_len,
+                                                      int nvec, int segs, int rot, uint64_t *part_k,
+                                                      int32_t *amax, TreeCtl ctl, int32_t *__restrict__ accept_len,
                                                       int32_t *__restrict__ path_nodes,
                                                       int32_t *__restrict__ out_tokens,
                                                       int32_t *__restrict__ status) {
@@ -600,8 +601,9 @@ __global__ __launch_bounds__(kBlock) void k_skip_tree(const typename E::storage 
     if (wave >= per_slot * static_cast<unsigned>(N)) return;
     const int slot = static_cast<int>(wave / per_slot);
     const unsigned rem = wave - static_cast<unsigned>(slot) * per_slot;
-    const int b = static_cast<int>(rem / static_cast<unsigned>(segs));
-    const int sg = static_cast<int>(rem - static_cast<unsigned>(b) * static_cast<unsigned>(segs));
+    const unsigned bslot = rem / static_cast<unsigned>(segs);
+    const int sg = static_cast<int>(rem - bslot * static_cast<unsigned>(segs));
+    const int b = skip_request(bslot, slot, B, rot);
     const long long base = static_cast<long long>(b) * N;
     const int j = uniform(ctl.order[base + slot]);  // issued beside the state load
     // slot 0 holds the root, whose row is always needed
@@ -698,7 +700,7 @@ hipError_t skip_tree_t(const void *L, const int32_t *tok, const int32_t *par, in
     const long long blocks = (nwaves + kWavesPerBlock - 1) / kWavesPerBlock;
     return launch_kernel(k_skip_tree<E, ALIGNED, kGSkipVecsPerLane>, dim3(static_cast<unsigned>(blocks)),
                          dim3(kBlock), SV_TSKIP_LDS, s, static_cast<const T *>(L), tok, par, B, N, V, g.nvec, g.segs,
-                         part_k, amax, ctl, accept_len, path_nodes, out_tokens, status);
+                         tree_rotation(B), part_k, amax, ctl, accept_len, path_nodes, out_tokens, status);
 }
 
 template <typename E, bool ALIGNED>
@@ -708,9 +710,10 @@ hipError_t skip_argmax_t(const void *L, const int32_t *drafts, int B, int K, int
     using T = typename E::storage;
     const long long nwaves = static_cast<long long>(K + 1) * B * g.segs;
     const long long blocks = (nwaves + kWavesPerBlock - 1) / kWavesPerBlock;
+    const bool early = skip_early(B, 1, V, sizeof(T));
     return launch_kernel(k_skip_argmax<E, ALIGNED, kGSkipVecsPerLane>, dim3(static_cast<unsigned>(blocks)),
                          dim3(kBlock), SV_GSKIP_LDS, s, static_cast<const T *>(L), drafts, B, K, V, g.nvec, g.segs,
-                         part_k, amax, ctl, static_cast<int>(skip_early(B, 1, V, sizeof(T))), accept_len,
+                         part_k, amax, ctl, static_cast<int>(early), skip_rotation(B, early), accept_len,
                          out_tokens, status);
 }
 

@@ -5,7 +5,8 @@
 // mismatched) draft: every draft after it is discarded, and the one drawn token
 // comes from the rejected position's row.  A row-skipping pass is one launch
 // over every (position p, request b, segment) in position-major order, so the
-// segments of position p are handed out before those of p+1.  A wave of a
+// segments of position p are handed out before those of p+1 (the requests of
+// a position in an order that may be rotated, see skip_request).  A wave of a
 // position after 0 first tests whether its request is settled (its finished
 // flag, or a rejection already recorded at an earlier position, see
 // skip_early) and skips its segment if so.  Every other wave of (b, p) leaves
@@ -101,6 +102,30 @@ __device__ __forceinline__ void skip_segment(int sg, int nvec, int segs, int &v0
     const unsigned s0 = static_cast<unsigned>(sg), s1 = s0 + 1u;
     v0 = static_cast<int>(s0 * q + (s0 * r) / static_cast<unsigned>(segs));
     v1 = static_cast<int>(s1 * q + (s1 * r) / static_cast<unsigned>(segs));
+}
+
+// Each position hands out its requests' rows in an order rotated by `rot`
+// requests from the position before's: request b's row of position p comes
+// at slot (b + p rot) mod B.  A decision lands about one position's span of
+// reads after its row is handed out, so in plain order the next position's
+// row of the same request is mostly handed out just before the decision that
+// could skip it; rotated, a part of the requests get that row later (and the
+// rest sooner).  Measured on MI355X (greedy chain, K = 7, V = 151936 bf16, us
+// per pass, plain / rotated by B/2): B = 256 66.8 / 64.4, B = 320 80.6 /
+// 75.7 with the finished-flag test; B = 384 89.5 / 93.0, B = 512 108.8 /
+// 120.6, and the stochastic pass at B = 256 88.9 / 92, with the rejection-bit
+// test (skip_early), which retires dead waves as soon as the rejection is
+// known and gains nothing from the later hand-out.  The tree pass, over its
+// depth-ranked node slots, at B = 64 with N = 33: 70.9 plain, 69.4-69.9
+// rotated by B/8, 70.0-70.3 by B/16, B/4 or 3B/8.
+inline int skip_rotation(int B, bool early) { return early ? 0 : B / 2; }
+inline int tree_rotation(int B) { return B / 8; }
+
+__device__ __forceinline__ int skip_request(unsigned slot, int p, int B, int rot) {
+    if (rot == 0) return static_cast<int>(slot);
+    // slot = (b + p rot) mod B, so b = (slot + p (B - rot)) mod B; p B < 2^31
+    const unsigned b = (slot + static_cast<unsigned>(p) * static_cast<unsigned>(B - rot)) % static_cast<unsigned>(B);
+    return static_cast<int>(b);
 }
 
 // The decided prefix of a request mask: the accepted length n once every
