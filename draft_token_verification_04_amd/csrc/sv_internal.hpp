@@ -73,13 +73,17 @@ constexpr int kGSkipVecsPerLane = SV_GSKIP_VECS;
 // Dynamic LDS each workgroup of the greedy chain's and the tree's skip passes
 // reserves, unused, to cap the workgroups per compute unit (0: as many as their
 // registers allow, five).  Measured on MI355X (us per pass, chain B=256 / chain
-// B=512 / tree B=64): no cap 69.6 / 116.1 / 70.0; 40 KB (four) 67.4 / 111.1 /
-// 71.9; 45 KB (three) 68.1 / 115.8 / 77.5; 54 KB (two) 75.6 / 143.8 / 92.9.
+// B=512 / tree B=64), in plain request order: no cap 69.6 / 116.1 / 70.0;
+// 40 KB (four) 67.4 / 111.1 / 71.9; 45 KB (three) 68.1 / 115.8 / 77.5; 54 KB
+// (two) 75.6 / 143.8 / 92.9.  With the rotated orders (skip_request): chain
+// 32 KB / 40 KB / 52 KB 64.4 / 64.4 / 64.5 (B=256), 109.2 / 109.1 / 111.9
+// (B=512); tree no cap 70.3-70.7, 40 KB 67.7-68.0, 32 KB 68.0, 24 KB 69.6,
+// 20 KB 69.8.
 #ifndef SV_GSKIP_LDS
 #define SV_GSKIP_LDS (40 * 1024)
 #endif
 #ifndef SV_TSKIP_LDS
-#define SV_TSKIP_LDS 0
+#define SV_TSKIP_LDS (40 * 1024)
 #endif
 // Bound on any poll of a word another wave is bound to write (never reached).
 constexpr int kSkipPollCap = 1 << 22;

@@ -116,8 +116,9 @@ __device__ __forceinline__ void skip_segment(int sg, int nvec, int segs, int &v0
 // 120.6, and the stochastic pass at B = 256 88.9 / 92, with the rejection-bit
 // test (skip_early), which retires dead waves as soon as the rejection is
 // known and gains nothing from the later hand-out.  The tree pass, over its
-// depth-ranked node slots, at B = 64 with N = 33: 70.9 plain, 69.4-69.9
-// rotated by B/8, 70.0-70.3 by B/16, B/4 or 3B/8.
+// depth-ranked node slots, at B = 64 with N = 33 (four workgroups per compute
+// unit): 68.9-69.2 plain, 67.5 rotated by B/16, 67.7-68.0 by B/8, 68.3 by B/4
+// or B/2.
 inline int skip_rotation(int B, bool early) { return early ? 0 : B / 2; }
 inline int tree_rotation(int B) { return B / 8; }
 
