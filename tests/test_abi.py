@@ -95,6 +95,16 @@ def _sample(lib, **kw):
                                   a["ws"], a["wsb"], a["s"])
 
 
+def test_noalloc_batch_limit_in_the_header(lib):
+    # the header states the largest batch the no-allocation entry's scratch
+    # admits at K = 7, V = 151936 bf16: it must be what the workspace query gives
+    text = open(HEADER).read()
+    stated = int(re.search(r"admits B up to (\d+)", text).group(1))
+    cap = int(re.search(r"#define SV_NOALLOC_SCRATCH_BYTES (\d+)", text).group(1))
+    fits = lambda B: 0 < lib.sv_sample_workspace_bytes(B, 7, 151936, sv.SV_BF16) <= cap
+    assert fits(stated) and not fits(stated + 1)
+
+
 def test_sample_argument_checks(lib):
     assert _sample(lib, dt=5) == sv.SV_ERR_UNSUPPORTED
     assert _sample(lib, B=-1) == sv.SV_ERR_INVALID_ARG
