@@ -710,11 +710,12 @@ hipError_t skip_argmax_t(const void *L, const int32_t *drafts, int B, int K, int
     using T = typename E::storage;
     const long long nwaves = static_cast<long long>(K + 1) * B * g.segs;
     const long long blocks = (nwaves + kWavesPerBlock - 1) / kWavesPerBlock;
-    const bool early = skip_early(B, 1, V, sizeof(T));
+    // the greedy chain always tests the rejection bits, and rotates where the
+    // stochastic pass would test the finished flag (see greedy_rotation)
+    const bool rotate = !skip_early(B, 1, V, sizeof(T));
     return launch_kernel(k_skip_argmax<E, ALIGNED, kGSkipVecsPerLane>, dim3(static_cast<unsigned>(blocks)),
                          dim3(kBlock), SV_GSKIP_LDS, s, static_cast<const T *>(L), drafts, B, K, V, g.nvec, g.segs,
-                         part_k, amax, ctl, static_cast<int>(early), skip_rotation(B, early), accept_len,
-                         out_tokens, status);
+                         part_k, amax, ctl, 1, greedy_rotation(B, rotate), accept_len, out_tokens, status);
 }
 
 template <typename E, bool ALIGNED>

@@ -121,6 +121,14 @@ __device__ __forceinline__ void skip_segment(int sg, int nvec, int segs, int &v0
 // or B/2.
 inline int skip_rotation(int B, bool early) { return early ? 0 : B / 2; }
 inline int tree_rotation(int B) { return B / 8; }
+// The greedy chain, rotated, is faster still with the rejection-bit test
+// (us per pass, rotated by B/2, finished flag / rejection bits): B = 256 64.9
+// / 63.2, B = 320 76.0 / 76.6; without rotation the bits win from B = 384 on
+// (see skip_early), and rotation there costs (B = 512: 109.4 against 120.5).
+// So it always tests the bits and rotates where a position's rows are below
+// the early-test threshold.  The stochastic pass keeps the flag below it (the
+// bits with rotation: B = 32 34.0 against 32.2).
+inline int greedy_rotation(int B, bool rotate) { return rotate ? B / 2 : 0; }
 
 __device__ __forceinline__ int skip_request(unsigned slot, int p, int B, int rot) {
     if (rot == 0) return static_cast<int>(slot);
