@@ -31,6 +31,16 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
 }
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(uint16_t h) { return bf16_to_f32(h); }
+// A stored element's bits, and the element from them.
+__device__ __forceinline__ unsigned storage_bits(float x) { return __float_as_uint(x); }
+__device__ __forceinline__ unsigned storage_bits(uint16_t h) { return h; }
+template <typename E>
+__device__ __forceinline__ float from_bits(unsigned u) {
+    if constexpr (sizeof(typename E::storage) == 2)
+        return bf16_to_f32(static_cast<uint16_t>(u));
+    else
+        return __uint_as_float(u);
+}
 
 // Unpack one 16-byte vector into kPerVec floats (exact widening).
 __device__ __forceinline__ void unpack(const uint4 &w, float (&x)[4]) {

@@ -361,6 +361,11 @@ __global__ __launch_bounds__(kBlock) void k_skip_argmax(const typename E::storag
     const long long row = static_cast<long long>(b) * (K + 1) + p;
     int v0, v1;
     skip_segment(sg, nvec, segs, v0, v1);
+    // the row's last segment decides position p: its draft is fetched first,
+    // by a vector load read through readfirstlane only at the decision, so
+    // that nothing waits for it before the segment's loads
+    const int32_t *xb = drafts + static_cast<long long>(b) * K;
+    const int xd_raw = sg == segs - 1 && p < K ? shared_load(const_cast<int32_t *>(xb + p)) : 0;
     const uint64_t key = segment_argmax_chunked<E, ALIGNED, U, kGSkipChunks>(L + row * V, V, v0, v1, lane);
 #if SV_SKIP_POLL
     // Every wave leaves its segment's key (never 0; the keys start at 0) and
@@ -404,9 +409,8 @@ __global__ __launch_bounds__(kBlock) void k_skip_argmax(const typename E::storag
     }
     const int a = uniform(argmax_key_index(wave_max_u64(mk)));
 #endif
-    const int32_t *xb = drafts + static_cast<long long>(b) * K;
     uint64_t bits = 1ull << p;
-    if (p < K && uniform(xb[p]) != a) bits |= 1ull << (32 + p);
+    if (p < K && uniform(xd_raw) != a) bits |= 1ull << (32 + p);
 #if SV_SKIP_FASTDECIDE
     // amax holds each decided row's argmax plus one (0: not yet known); the
     // store need not land before the decision, the finisher polls for it

@@ -868,6 +868,23 @@ __global__ __launch_bounds__(kBlock) void k_skip_stats(
                                                 : drf + (static_cast<long long>(b) * K + p) * static_cast<long long>(V);
     int v0, v1;
     skip_segment(sg, nvec, segs, v0, v1);
+    // the wave that will decide position p (the last of its partials, see
+    // below) fetches the draft, the two logits it is scored with and its
+    // uniform now, so that no load waits after the partials are in
+    const bool decider = r == (p < K ? 2 : 1) * segs - 1;
+    int xd = -1;
+    float ud = 0.0f;
+    // raw storage bits, read through readfirstlane only where they are used
+    // (that keeps the wait for them there, not before the segment's loads)
+    unsigned xp_raw = 0, xq_raw = 0;
+    if (decider && p < K) {
+        xd = uniform(drafts[static_cast<long long>(b) * K + p]);
+        ud = ua[static_cast<long long>(b) * K + p];
+        if (xd >= 0 && xd < V) {
+            xp_raw = storage_bits(tgt[gt * V + xd]);
+            xq_raw = storage_bits(drf[(static_cast<long long>(b) * K + p) * V + xd]);
+        }
+    }
     float R;
     double sum;
     segment_stats_chunked<E, ALIGNED, U, kSkipChunks>(base, V, v0, v1, c_hi, c_lo, lane, R, sum);
@@ -942,15 +959,13 @@ __global__ __launch_bounds__(kBlock) void k_skip_stats(
 #endif
     uint64_t bits = 1ull << p;
     if (p < K) {
-        const int x = uniform(drafts[static_cast<long long>(b) * K + p]);
         double ratio = 0.0;
-        if (x >= 0 && x < V) {
-            const double px = exp2(static_cast<double>(to_f32(tgt[gt * V + x])) * c - L2p);
-            const double qx = exp2(static_cast<double>(to_f32(drf[(static_cast<long long>(b) * K + p) * V + x])) * c - L2q);
+        if (xd >= 0 && xd < V) {
+            const double px = exp2(static_cast<double>(from_bits<E>(uniform(xp_raw))) * c - L2p);
+            const double qx = exp2(static_cast<double>(from_bits<E>(uniform(xq_raw))) * c - L2q);
             ratio = qx == 0.0 ? __builtin_huge_val() : px / qx;
         }
-        const double u = static_cast<double>(ua[static_cast<long long>(b) * K + p]);
-        if (!(u < ratio)) bits |= 1ull << (32 + p);
+        if (!(static_cast<double>(ud) < ratio)) bits |= 1ull << (32 + p);
 #if !SV_SKIP_POLL
         if (lane == 0) shared_store(&L2b[K + 1 + p], L2q);
 #endif
