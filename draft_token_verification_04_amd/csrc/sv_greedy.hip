@@ -616,6 +616,15 @@ __global__ __launch_bounds__(kBlock) void k_skip_tree(const typename E::storage 
     const long long row = base + j;
     int v0, v1;
     skip_segment(sg, nvec, segs, v0, v1);
+    // the row's last segment decides node j's children: the request's parents,
+    // tokens and slot ranks (one node per lane) are fetched before its loads
+    const bool in = lane < N;
+    int p = -1, t = 0, rk = 0;
+    if (sg == segs - 1 && in) {
+        p = par[base + lane];
+        t = tok[base + lane];
+        rk = ctl.rank[base + lane];
+    }
     const uint64_t key = segment_argmax_chunked<E, ALIGNED, U, kGSkipChunks>(L + row * V, V, v0, v1, lane);
 #if SV_SKIP_POLL
     // keys handed to the row's last segment as in the chain pass (the prep
@@ -659,12 +668,11 @@ __global__ __launch_bounds__(kBlock) void k_skip_tree(const typename E::storage 
 #endif
     if (lane == 0) shared_store(&amax[row], a);
     wait_own_stores();
-    const bool in = lane < N;
-    const int p = in ? par[base + lane] : -1;
-    const int t = in ? tok[base + lane] : 0;
-    const int rk = in ? ctl.rank[base + lane] : 0;
     // states as they stand, plus this row done and this row's mismatching children
-    unsigned st = in ? shared_load(&ctl.state[base + rk]) : 0u;
+    // the state word of each lane's node (the rank taken unsigned: its 64-bit
+    // address then needs no value of it before the segment's loads)
+    unsigned *st_word = ctl.state + base + static_cast<unsigned>(rk);
+    unsigned st = in ? shared_load(st_word) : 0u;
     uint64_t rej = ballot(in && ((st & kRejected) || (lane > 0 && p == j && t != a)));
     // close the rejection over the tree: a node under a rejected parent is rejected
     for (int it = 0; it < N; ++it) {
@@ -678,7 +686,7 @@ __global__ __launch_bounds__(kBlock) void k_skip_tree(const typename E::storage 
     if (in && ((rej >> lane) & 1ull)) mark |= kRejected;
     int newly = 0;
     if (mark) {
-        const unsigned old = __hip_atomic_fetch_or(&ctl.state[base + rk], mark, __ATOMIC_RELAXED,
+        const unsigned old = __hip_atomic_fetch_or(st_word, mark, __ATOMIC_RELAXED,
                                                    __HIP_MEMORY_SCOPE_AGENT);
         newly = old == 0 ? 1 : 0;
     }
