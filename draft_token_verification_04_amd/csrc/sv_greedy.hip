@@ -361,11 +361,11 @@ __global__ __launch_bounds__(kBlock) void k_skip_argmax(const typename E::storag
     const long long row = static_cast<long long>(b) * (K + 1) + p;
     int v0, v1;
     skip_segment(sg, nvec, segs, v0, v1);
-    // the row's last segment decides position p: its draft is fetched first,
-    // by a vector load read through readfirstlane only at the decision, so
-    // that nothing waits for it before the segment's loads
+    // the row's last segment decides position p: the request's drafts (one
+    // per lane, K <= 31) are fetched before the segment's loads and read only
+    // at the decision, and by the finisher
     const int32_t *xb = drafts + static_cast<long long>(b) * K;
-    const int xd_raw = sg == segs - 1 && p < K ? shared_load(const_cast<int32_t *>(xb + p)) : 0;
+    const int xl = sg == segs - 1 && lane < K ? xb[lane] : 0;
     const uint64_t key = segment_argmax_chunked<E, ALIGNED, U, kGSkipChunks>(L + row * V, V, v0, v1, lane);
 #if SV_SKIP_POLL
     // Every wave leaves its segment's key (never 0; the keys start at 0) and
@@ -410,7 +410,7 @@ __global__ __launch_bounds__(kBlock) void k_skip_argmax(const typename E::storag
     const int a = uniform(argmax_key_index(wave_max_u64(mk)));
 #endif
     uint64_t bits = 1ull << p;
-    if (p < K && uniform(xd_raw) != a) bits |= 1ull << (32 + p);
+    if (p < K && uniform(__shfl(xl, p, kWave)) != a) bits |= 1ull << (32 + p);
 #if SV_SKIP_FASTDECIDE
     // amax holds each decided row's argmax plus one (0: not yet known); the
     // store need not land before the decision, the finisher polls for it
@@ -440,8 +440,8 @@ __global__ __launch_bounds__(kBlock) void k_skip_argmax(const typename E::storag
 #endif
     bool bad = false;
     int32_t *tok = out_tokens + static_cast<long long>(b) * (K + 1);
-    for (int i = lane; i <= K; i += kWave) {
-        const int x = i < K ? xb[i] : 0;
+    for (int i = lane; i <= K; i += kWave) {  // K <= 31: lane i holds draft i
+        const int x = i < K ? xl : 0;
         if (i < K && (x < 0 || x >= V)) bad = true;
         tok[i] = i < n ? x : (i == n ? an : -1);
     }
@@ -521,17 +521,19 @@ __global__ __launch_bounds__(kBlock) void k_tree_prep(const int32_t *__restrict_
     }
 }
 
-// Node j's outputs of request b once every node is resolved (one wave).
-__device__ __forceinline__ void tree_finish(const int32_t *__restrict__ tok, const int32_t *__restrict__ par,
-                                            const int32_t *amax, const TreeCtl &ctl, int b, int N, int V,
+// Node j's outputs of request b once every node is resolved (one wave); the
+// caller holds the request's parents, tokens and slot ranks one node per lane
+// (lanes past N: any values).
+__device__ __forceinline__ void tree_finish(int p_in, int t_in, int rk_in, const int32_t *amax,
+                                            const TreeCtl &ctl, int b, int N, int V,
                                             int32_t *__restrict__ accept_len, int32_t *__restrict__ path_nodes,
                                             int32_t *__restrict__ out_tokens, int32_t *__restrict__ status,
                                             int lane) {
     const long long base = static_cast<long long>(b) * N;
     const bool in = lane < N;
-    const int p = in ? par[base + lane] : 0;
-    const int t = in ? tok[base + lane] : 0;
-    const int rk = in ? ctl.rank[base + lane] : 0;
+    const int p = in ? p_in : 0;
+    const int t = in ? t_in : 0;
+    const int rk = in ? rk_in : 0;
     const unsigned st = in ? shared_load(&ctl.state[base + rk]) : 0u;
     const int a = in && (st & kRowDone) ? shared_load(const_cast<int32_t *>(&amax[base + lane])) : -1;
     const bool bad_par = ballot(in && (lane == 0 ? p != -1 : (p < 0 || p >= lane))) != 0;
@@ -699,7 +701,7 @@ __global__ __launch_bounds__(kBlock) void k_skip_tree(const typename E::storage 
                                         __HIP_MEMORY_SCOPE_AGENT);
     before = uniform(static_cast<unsigned>(__shfl(static_cast<int>(before), 0, kWave)));
     if (before + static_cast<unsigned>(cnt) != static_cast<unsigned>(N)) return;
-    tree_finish(tok, par, amax, ctl, b, N, V, accept_len, path_nodes, out_tokens, status, lane);
+    tree_finish(p, t, rk, amax, ctl, b, N, V, accept_len, path_nodes, out_tokens, status, lane);
 }
 
 template <typename E, bool ALIGNED>

@@ -808,27 +808,28 @@ __device__ __forceinline__ double merge_row_marked(uint32_t *wR, uint64_t *wS, l
 #endif
 
 // Outputs of request b decided at n (mode 1: rejection at n, residual of
-// rows n; mode 0: bonus from target row K), written by one wave.
-__device__ __forceinline__ void skip_finish(const int32_t *__restrict__ xb, const float *__restrict__ us,
-                                            int b, int K, int V, int n, int mode, double L2p, double L2q,
-                                            int32_t *__restrict__ accept_len,
+// rows n; mode 0: bonus from target row K), written by one wave that holds
+// draft i and the draw uniform of position i in lane i (K <= 31).
+__device__ __forceinline__ void skip_finish(int xl, float usl, int b, int K, int V, int n, int mode,
+                                            double L2p, double L2q, int32_t *__restrict__ accept_len,
                                             int32_t *__restrict__ out_tokens,
                                             int32_t *__restrict__ status, ResidParam *__restrict__ rp,
                                             int lane) {
     bool bad = false;
     int32_t *tok = out_tokens + static_cast<long long>(b) * (K + 1);
     for (int i = lane; i <= K; i += kWave) {
-        const int x = i < K ? xb[i] : 0;
+        const int x = i < K ? xl : 0;
         if (i < K && (x < 0 || x >= V)) bad = true;
         tok[i] = i < n ? x : -1;
     }
     const bool any_bad = ballot(bad) != 0;
+    const float u_n = __shfl(usl, n, kWave);
     if (lane == 0) {
         accept_len[b] = n;
         if (status) status[b] = any_bad ? 1 : 0;
         ResidParam P;
         P.pos = n;
-        P.u = static_cast<double>(us[static_cast<long long>(b) * (K + 1) + n]);
+        P.u = static_cast<double>(u_n);
         P.row_p = static_cast<long long>(b) * (K + 1) + n;
         P.L2p = L2p;
         P.mode = mode;
@@ -877,6 +878,14 @@ __global__ __launch_bounds__(kBlock) void k_skip_stats(
     // raw storage bits, read through readfirstlane only where they are used
     // (that keeps the wait for them there, not before the segment's loads)
     unsigned xp_raw = 0, xq_raw = 0;
+    // and for the request's finish: draft i and the draw uniform of position
+    // i in lane i (K <= 31)
+    int xl = 0;
+    float usl = 0.0f;
+    if (decider) {
+        if (lane < K) xl = drafts[static_cast<long long>(b) * K + lane];
+        if (lane <= K) usl = us[static_cast<long long>(b) * (K + 1) + lane];
+    }
     if (decider && p < K) {
         xd = uniform(drafts[static_cast<long long>(b) * K + p]);
         ud = ua[static_cast<long long>(b) * K + p];
@@ -1005,8 +1014,7 @@ __global__ __launch_bounds__(kBlock) void k_skip_stats(
     const double L2pn = shared_load(&L2b[n]);
     const double L2qn = n < K ? shared_load(&L2b[K + 1 + n]) : 0.0;
 #endif
-    skip_finish(drafts + static_cast<long long>(b) * K, us, b, K, V, n, n < K ? 1 : 0, L2pn, L2qn,
-                accept_len, out_tokens, status, rp, lane);
+    skip_finish(xl, usl, b, K, V, n, n < K ? 1 : 0, L2pn, L2qn, accept_len, out_tokens, status, rp, lane);
     skip_finished(ctl, b, lane);
 }
 
