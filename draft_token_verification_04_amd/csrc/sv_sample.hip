@@ -602,11 +602,24 @@ __global__ __launch_bounds__(kWave) void k_resid_select(
     double *tm = tile_mass + static_cast<long long>(b) * ntiles;
     int32_t *dst = out_tokens + static_cast<long long>(b) * (K + 1) + Pm.pos;
 
-    // tiles [lt0, lt1) belong to this lane; prefix over lanes in tile order
+    // tiles [lt0, lt1) belong to this lane; prefix over lanes in tile order.
+    // The lane's first kSelRegs masses are loaded at once into registers (the
+    // rest, for rows of more than 64 kSelRegs tiles, one by one) and summed in
+    // tile order.
+    constexpr int kSelRegs = 16;
     const int tpl = (ntiles + kWave - 1) / kWave;
     const int lt0 = min(ntiles, lane * tpl), lt1 = min(ntiles, lt0 + tpl);
-    double ls = 0.0;
-    for (int t = lt0; t < lt1; ++t) ls += tm[t];
+    double tmr[kSelRegs];
+    auto lane_masses = [&]() {
+#pragma unroll
+        for (int k = 0; k < kSelRegs; ++k) tmr[k] = lt0 + k < lt1 ? tm[lt0 + k] : 0.0;
+        double acc = 0.0;
+#pragma unroll
+        for (int k = 0; k < kSelRegs; ++k) acc += tmr[k];
+        for (int t = lt0 + kSelRegs; t < lt1; ++t) acc += tm[t];
+        return acc;
+    };
+    double ls = lane_masses();
     double incl = wave_incl_scan(ls, lane);
     double Z = __shfl(incl, kWave - 1, kWave);
 
@@ -627,8 +640,7 @@ __global__ __launch_bounds__(kWave) void k_resid_select(
             if (lane == kWave - 1) tm[t] = tot;
         }
         __syncthreads();
-        ls = 0.0;
-        for (int t = lt0; t < lt1; ++t) ls += tm[t];
+        ls = lane_masses();
         incl = wave_incl_scan(ls, lane);
         Z = __shfl(incl, kWave - 1, kWave);
     }
@@ -651,7 +663,11 @@ __global__ __launch_bounds__(kWave) void k_resid_select(
         double run = excl, run_last = 0.0;
         int last = -1;
         for (int t = lt0; t < lt1; ++t) {
-            const double m = tm[t];
+            const int k = t - lt0;
+            double m = 0.0;
+#pragma unroll
+            for (int q = 0; q < kSelRegs; ++q) m = q == k ? tmr[q] : m;  // registers, not memory
+            if (k >= kSelRegs) m = tm[t];
             if (m > 0.0) {
                 if (run + m > target) {
                     tsel = t;
