@@ -278,32 +278,45 @@ __global__ __launch_bounds__(kBlock) void k_accept(
     const int tid = threadIdx.x, wid = tid >> 6, lane = tid & (kWave - 1);
     const double inf = __builtin_huge_val();
     // partials of row r of this request: target rows 0..K, then draft rows
+    // (the two argument structs' fields taken as scalars once, so that picking
+    // a row selects between scalars rather than loading through a pointer)
+    const float *const ptR = pt.R, *const pdR = pd.R;
+    const double *const ptS = pt.s, *const pdS = pd.s;
+    const int tsegs = pt.segs, dsegs = pd.segs;
     auto row_R = [&](int r) {
-        return r <= K ? pt.R + (static_cast<long long>(b) * (K + 1) + r) * pt.segs
-                      : pd.R + (static_cast<long long>(b) * K + (r - K - 1)) * pd.segs;
+        return r <= K ? ptR + (static_cast<long long>(b) * (K + 1) + r) * tsegs
+                      : pdR + (static_cast<long long>(b) * K + (r - K - 1)) * dsegs;
     };
     auto row_s = [&](int r) {
-        return r <= K ? pt.s + (static_cast<long long>(b) * (K + 1) + r) * pt.segs
-                      : pd.s + (static_cast<long long>(b) * K + (r - K - 1)) * pd.segs;
+        return r <= K ? ptS + (static_cast<long long>(b) * (K + 1) + r) * tsegs
+                      : pdS + (static_cast<long long>(b) * K + (r - K - 1)) * dsegs;
     };
-    // the target logit at draft i (its row scores draft i)
-    auto tgt_at = [&](int i, int x) {
+    // the target logit at draft i (its row scores draft i), as stored bits
+    auto tgt_bits = [&](int i, int x) {
         if constexpr (FUSED)
-            return xlog[static_cast<long long>(b) * (K + 1) + i];
+            return __float_as_uint(xlog[static_cast<long long>(b) * (K + 1) + i]);
         else
-            return to_f32(tgt[(static_cast<long long>(b) * (K + 1) + i) * V + x]);
+            return storage_bits(tgt[(static_cast<long long>(b) * (K + 1) + i) * V + x]);
+    };
+    auto tgt_value = [&](unsigned u) {
+        if constexpr (FUSED)
+            return __uint_as_float(u);
+        else
+            return from_bits<E>(u);
     };
 
     // The drafts and the two logits each one is scored with, fetched for the
-    // first 64 positions while the partials are merged.
+    // first 64 positions while the partials are merged (kept as loaded, and
+    // converted only where they are used, so that nothing waits for them
+    // before the merge).
     const int32_t *xb = drafts + static_cast<long long>(b) * K;
     int x0 = -1;
-    float xp0 = 0.0f, xq0 = 0.0f;
+    unsigned xp0b = 0, xq0b = 0;
     if (tid < K) {
         x0 = xb[tid];
         if (x0 >= 0 && x0 < V) {
-            xp0 = tgt_at(tid, x0);
-            xq0 = to_f32(drf[(static_cast<long long>(b) * K + tid) * V + x0]);
+            xp0b = tgt_bits(tid, x0);
+            xq0b = storage_bits(drf[(static_cast<long long>(b) * K + tid) * V + x0]);
         }
     }
 
@@ -312,10 +325,28 @@ __global__ __launch_bounds__(kBlock) void k_accept(
     for (int r0 = 0; r0 < nrows; r0 += chunk) {
         const int nr = min(chunk, nrows - r0);
         if (lds_rows > 0) {
-            for (int i = tid; i < nr * segs; i += kBlock) {
-                const int rr = i / segs, sg = i - rr * segs;
-                stR[i] = row_R(r0 + rr)[sg];
-                stS[i] = row_s(r0 + rr)[sg];
+            // kStage loads per thread issued before any is stored
+            constexpr int kStage = 4;
+            for (int i0 = tid; i0 < nr * segs; i0 += kStage * kBlock) {
+                float sr[kStage];
+                double ssv[kStage];
+#pragma unroll
+                for (int u = 0; u < kStage; ++u) {
+                    const int i = i0 + u * kBlock;
+                    if (i < nr * segs) {
+                        const int rr = i / segs, sg = i - rr * segs;
+                        sr[u] = row_R(r0 + rr)[sg];
+                        ssv[u] = row_s(r0 + rr)[sg];
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < kStage; ++u) {
+                    const int i = i0 + u * kBlock;
+                    if (i < nr * segs) {
+                        stR[i] = sr[u];
+                        stS[i] = ssv[u];
+                    }
+                }
             }
             __syncthreads();
         }
@@ -342,7 +373,7 @@ __global__ __launch_bounds__(kBlock) void k_accept(
                 } else {
                     pR[q] = row_R(r0 + rc);
                     pS[q] = row_s(r0 + rc);
-                    ns[q] = r0 + rc <= K ? pt.segs : pd.segs;
+                    ns[q] = r0 + rc <= K ? tsegs : dsegs;
                 }
                 Rm[q] = -__builtin_huge_valf();
                 for (int sg = lane; sg < ns[q]; sg += kWave) Rm[q] = fmaxf(Rm[q], pR[q][sg]);
@@ -378,6 +409,9 @@ __global__ __launch_bounds__(kBlock) void k_accept(
         __syncthreads();
     }
     if (wid != 0) return;
+    // the prefetched logits are needed from here on
+    asm volatile("" : "+v"(xp0b), "+v"(xq0b));
+    const float xp0 = tgt_value(xp0b), xq0 = from_bits<E>(xq0b);
 
     // 2. p_i(x_i) / q_i(x_i) for every position at once; the first failing test wins.
     int n = K;
@@ -389,7 +423,7 @@ __global__ __launch_bounds__(kBlock) void k_accept(
             const int x = i0 == 0 ? x0 : xb[i];
             double r = 0.0;
             if (x >= 0 && x < V) {
-                const double xp = i0 == 0 ? xp0 : tgt_at(i, x);
+                const double xp = i0 == 0 ? xp0 : tgt_value(tgt_bits(i, x));
                 const double xq = i0 == 0 ? xq0 : to_f32(drf[(static_cast<long long>(b) * K + i) * V + x]);
                 const double px = exp2(xp * c - sL2[i]);
                 const double qx = exp2(xq * c - sL2[K + 1 + i]);
