@@ -123,6 +123,24 @@ def test_full_size():
     assert (o["count"] > 0).mean() > 0.5
 
 
+def test_many_candidates_far_above_cap():
+    # a full-size batch where half the streams match at every position (count
+    # far above cap) and the rest sparsely, so that ranks run across many
+    # chunks of a request; two caps
+    note("ngram many candidates")
+    B, L = 256, 20000
+    rng = np.random.default_rng(17)
+    ctx = rng.integers(0, 3, size=(B, L)).astype(np.int32)
+    ctx[: B // 2] = 7
+    lens = rng.integers(L // 2, L + 1, size=B).astype(np.int32)
+    lens[0] = L
+    q = np.full((B, 3), 7, np.int32)
+    q[B // 2:] = rng.integers(0, 3, size=(B - B // 2, 3))
+    for cap in (64, 5000):
+        o = check(ctx, lens, q, cap)
+        assert o["count"][0] == L - 3 and (o["count"][B // 2:] > 0).all()
+
+
 def test_long_contexts_full_size():
     # the bench's long shape: 256 streams of 64K..128K tokens
     shp = workloads.NGRAM_LONG_SHAPE
