@@ -478,26 +478,104 @@ constexpr unsigned kRowDone = 1u, kRejected = 2u;
 constexpr int kTreeSkipMaxN = kWave;
 
 struct TreeCtl {
+    uint64_t *ckey;      // [B*N] argmax key of each node's token in its parent's row
     unsigned *ticket;    // [B*N] segments finished, per slot
     unsigned *state;     // [B*N] kRowDone | kRejected of the node in each slot
     unsigned *resolved;  // [B] nodes resolved
     int32_t *order;      // [B*N] node of each slot (ascending depth, then index)
     int32_t *rank;       // [B*N] slot of each node
+    unsigned *nlive;     // [B] nodes not rejected by the row samples (slots 0 .. nlive-1)
 };
 
-// Per request (one wave): clear its control words and rank its nodes by
-// (depth, index).  Depths come from pointer jumping over the lanes; a parent
-// outside [0, j) counts as the root here (the walk flags such a request), so
-// the slots are always a permutation of the nodes.
-__global__ __launch_bounds__(kBlock) void k_tree_prep(const int32_t *__restrict__ par, int B, int N,
-                                                      TreeCtl ctl, uint64_t *__restrict__ part_k, int segs) {
+// Per request (one workgroup): sample each node's row, clear the request's
+// control words and rank its nodes.  The sample is the row's first 64 vectors
+// (512 bf16 logits).  A child whose token's logit in its parent's row is below
+// the largest logit of that row's sample cannot be the row's argmax, so it is
+// rejected before any row is streamed, with every node under it.  With drafts
+// that are either the argmax or an unrelated token this settles almost every
+// rejection at once (an unrelated token tops a 512-logit sample about once in
+// 500); the rest are left to the decisions.  Depths come from pointer jumping
+// over the lanes; a parent outside [0, j) counts as the root for the depth and
+// passes no rejection down (the walk flags such a request).  The live nodes
+// take slots 0 .. nlive-1 by (depth, index), the rejected ones the slots after
+// them, so the slots are always a permutation of the nodes.
+template <typename E, bool ALIGNED>
+__global__ __launch_bounds__(kBlock) void k_tree_prep(const typename E::storage *__restrict__ L,
+                                                      const int32_t *__restrict__ par,
+                                                      const int32_t *__restrict__ tok, int B, int N, int V,
+                                                      int nvec, TreeCtl ctl, uint64_t *__restrict__ part_k,
+                                                      int segs) {
+    constexpr int P = E::kPerVec;
+    constexpr int R = kTreeSkipMaxN / kWavesPerBlock;  // rows sampled per wave
+    constexpr int kPad = kWave + 4;                    // 16-byte aligned rows of partial maxima
+    __shared__ __align__(16) float s_part[kTreeSkipMaxN * kPad];
     const int lane = threadIdx.x & (kWave - 1);
-    const int b = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+    const int wid = threadIdx.x >> 6;
+    const int b = blockIdx.x;
     if (b >= B) return;
     const long long base = static_cast<long long>(b) * N;
     const bool in = lane < N;
-    const int p = in ? par[base + lane] : 0;
-    int anc = (lane == 0 || !in || p < 0 || p >= lane) ? 0 : p;
+    // wave 0 fetches the request's parents and tokens, then each node's token
+    // logit in its parent's row, while every wave samples its rows
+    int p = 0, t = 0;
+    if (wid == 0 && in) {
+        p = par[base + lane];
+        t = tok[base + lane];
+    }
+    const int sv = min(nvec, kWave);
+    Staged<E, ALIGNED> st[R];
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+        const int j = wid + k * kWavesPerBlock;
+        if (j < N && lane < sv)
+            st[k].load(L + (base + j) * static_cast<long long>(V), V, lane);
+        else
+            st[k].set_neg_inf();
+    }
+    const bool pv = wid == 0 && in && lane > 0 && p >= 0 && p < N;
+    const bool tv = t >= 0 && t < V;
+    unsigned xb = 0;
+    if (pv && tv) xb = storage_bits(L[(base + p) * static_cast<long long>(V) + t]);
+    // each lane's largest sampled logit of each row, reduced per row below
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+        const int j = wid + k * kWavesPerBlock;
+        if (j < N) {  // uniform
+            float x[P];
+            st[k].get(x);
+            float m = x[0];
+#pragma unroll
+            for (int e = 1; e < P; ++e) m = fmaxf(m, x[e]);
+            s_part[j * kPad + lane] = m;
+        }
+    }
+    if (SV_SKIP_POLL) {  // the segment keys of the request's rows start at 0
+        uint64_t *pk = part_k + base * segs;
+        for (int i = threadIdx.x; i < N * segs; i += kBlock) pk[i] = 0;
+    }
+    __syncthreads();
+    if (wid != 0) return;
+
+    float smax = -__builtin_huge_valf();  // lane j: the largest sampled logit of row j
+    if (in) {
+        const float4 *r4 = reinterpret_cast<const float4 *>(s_part + lane * kPad);
+#pragma unroll
+        for (int i = 0; i < kWave / 4; ++i) {
+            const float4 v = r4[i];
+            smax = fmaxf(smax, fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w)));
+        }
+    }
+    const float sp = __shfl(smax, pv ? p : 0, kWave);
+    // a token outside the vocabulary can never be the argmax
+    const bool topo = lane > 0 && p >= 0 && p < lane;  // a parent listed before its child
+    uint64_t dead = ballot(pv && (!tv || sp > from_bits<E>(xb)));
+    for (int it = 0; it < N; ++it) {  // close over the tree, as the decisions do
+        const uint64_t d2 = dead | ballot(in && topo && ((dead >> p) & 1ull));
+        if (d2 == dead) break;  // uniform
+        dead = d2;
+    }
+    const bool is_dead = in && ((dead >> lane) & 1ull);
+    int anc = (lane == 0 || !in || !topo) ? 0 : p;
     int dep = (lane == 0 || !in) ? 0 : 1;
     for (int span = 1; span < N; span <<= 1) {
         const int d2 = __shfl(dep, anc, kWave);
@@ -505,19 +583,29 @@ __global__ __launch_bounds__(kBlock) void k_tree_prep(const int32_t *__restrict_
         dep += d2;
         anc = a2;
     }
-    const unsigned key = in ? ((static_cast<unsigned>(dep) << 8) | static_cast<unsigned>(lane)) : 0xffffffffu;
+    const unsigned key = in ? ((is_dead ? 1u << 16 : 0u) | (static_cast<unsigned>(dep) << 8) | static_cast<unsigned>(lane))
+                            : 0xffffffffu;
     int rk = 0;
-    for (int o = 0; o < N; ++o) rk += static_cast<unsigned>(__shfl(static_cast<int>(key), o, kWave)) < key;
+    for (int o = 0; o < N; ++o)
+        rk += static_cast<unsigned>(__builtin_amdgcn_readlane(static_cast<int>(key), o)) < key;
+    const int ndead = __popcll(dead);
     if (in) {
         ctl.order[base + rk] = lane;
         ctl.rank[base + lane] = rk;
         ctl.ticket[base + lane] = 0u;
-        ctl.state[base + lane] = 0u;
+        ctl.state[base + rk] = is_dead ? kRejected : 0u;
+        // the key of the node's token in its parent's row, tested by the
+        // parent row's first segment (a rejected node needs no second test)
+        uint64_t ck = 0;
+        if (is_dead || !pv)
+            ck = ~0ull;
+        else if (tv)
+            ck = argmax_key(from_bits<E>(xb), t);
+        ctl.ckey[base + lane] = ck;
     }
-    if (lane == 0) ctl.resolved[b] = 0u;
-    if (SV_SKIP_POLL) {  // the segment keys of the request's rows start at 0
-        uint64_t *pk = part_k + base * segs;
-        for (int i = lane; i < N * segs; i += kWave) pk[i] = 0;
+    if (lane == 0) {
+        ctl.resolved[b] = static_cast<unsigned>(ndead);
+        ctl.nlive[b] = static_cast<unsigned>(N - ndead);
     }
 }
 
@@ -592,6 +680,52 @@ __device__ __forceinline__ void tree_finish(int p_in, int t_in, int rk_in, const
     }
 }
 
+// Marks the nodes of `rej` rejected together with every node under them, and
+// node `done` (-1: none) as having its row's argmax; counts the nodes whose
+// state this changes from unresolved, and the wave whose count completes the
+// request's N nodes writes its outputs.  The caller holds the request's
+// parents, tokens and slot ranks one node per lane.
+__device__ __forceinline__ void tree_mark(uint64_t rej, int done, int p, int t, int rk, const int32_t *amax,
+                                          const TreeCtl &ctl, int b, int N, int V,
+                                          int32_t *__restrict__ accept_len, int32_t *__restrict__ path_nodes,
+                                          int32_t *__restrict__ out_tokens, int32_t *__restrict__ status,
+                                          int lane) {
+    const long long base = static_cast<long long>(b) * N;
+    const bool in = lane < N;
+    // close the rejection over the tree: a node under a rejected parent is rejected
+    for (int it = 0; it < N; ++it) {
+        const bool under = in && p >= 0 && p < lane && ((rej >> p) & 1ull);
+        const uint64_t r2 = rej | ballot(under);
+        if (r2 == rej) break;  // uniform
+        rej = r2;
+    }
+    unsigned mark = 0;
+    if (lane == done) mark |= kRowDone;
+    if (in && ((rej >> lane) & 1ull)) mark |= kRejected;
+    int newly = 0;
+    if (mark) {
+        const unsigned old = __hip_atomic_fetch_or(ctl.state + base + static_cast<unsigned>(rk), mark,
+                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        newly = old == 0 ? 1 : 0;
+    }
+    const int cnt = __popcll(ballot(newly != 0));
+    if (cnt == 0) return;
+    wait_own_stores();
+    unsigned before = 0;
+    if (lane == 0)
+        before = __hip_atomic_fetch_add(&ctl.resolved[b], static_cast<unsigned>(cnt), __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT);
+    before = uniform(static_cast<unsigned>(__shfl(static_cast<int>(before), 0, kWave)));
+    if (before + static_cast<unsigned>(cnt) != static_cast<unsigned>(N)) return;
+    tree_finish(p, t, rk, amax, ctl, b, N, V, accept_len, path_nodes, out_tokens, status, lane);
+}
+
+// Whether the first segment of each node's row rejects the node's children
+// whose tokens it already beats, before the row's last segment decides.
+#ifndef SV_TREE_EARLY
+#define SV_TREE_EARLY 1
+#endif
+
 template <typename E, bool ALIGNED, int U>
 __global__ __launch_bounds__(kBlock) void k_skip_tree(const typename E::storage *__restrict__ L,
                                                       const int32_t *__restrict__ tok,
@@ -611,21 +745,30 @@ __global__ __launch_bounds__(kBlock) void k_skip_tree(const typename E::storage 
     const int sg = static_cast<int>(rem - bslot * static_cast<unsigned>(segs));
     const int b = skip_request(bslot, slot, B, rot);
     const long long base = static_cast<long long>(b) * N;
+    // slots past the live count hold nodes the row samples rejected; the node
+    // of a live slot may have been rejected since by a decision
+    const unsigned nlive = uniform(ctl.nlive[b]);
     const int j = uniform(ctl.order[base + slot]);  // issued beside the state load
+    if (static_cast<unsigned>(slot) >= nlive) return;
     // slot 0 holds the root, whose row is always needed
     if (slot > 0 && (uniform(shared_load(&ctl.state[base + slot])) & kRejected)) return;
 
     const long long row = base + j;
     int v0, v1;
     skip_segment(sg, nvec, segs, v0, v1);
-    // the row's last segment decides node j's children: the request's parents,
-    // tokens and slot ranks (one node per lane) are fetched before its loads
+    // the row's last segment decides node j's children, and its first may
+    // reject some of them sooner: the request's parents, tokens and slot ranks
+    // (one node per lane), and for the first segment the keys of the nodes'
+    // tokens in their parents' rows, are fetched before the segment's loads
     const bool in = lane < N;
+    const bool early = SV_TREE_EARLY && sg == 0 && segs > 1;
     int p = -1, t = 0, rk = 0;
-    if (sg == segs - 1 && in) {
+    uint64_t ck = ~0ull;
+    if ((sg == segs - 1 || early) && in) {
         p = par[base + lane];
         t = tok[base + lane];
         rk = ctl.rank[base + lane];
+        if (early) ck = ctl.ckey[base + lane];
     }
     const uint64_t key = segment_argmax_chunked<E, ALIGNED, U, kGSkipChunks>(L + row * V, V, v0, v1, lane);
 #if SV_SKIP_POLL
@@ -634,11 +777,18 @@ __global__ __launch_bounds__(kBlock) void k_skip_tree(const typename E::storage 
     // already rejected, which this wave then finds too
     if (sg != segs - 1) {
         if (lane == 0) shared_store(&part_k[row * segs + sg], key);
+        // a child of j whose token's key this segment beats is not the row's
+        // argmax, so the decision will reject it: mark it now
+        if (early) {
+            const uint64_t rej = ballot(in && lane > 0 && p == j && key > ck);
+            if (rej) tree_mark(rej, -1, p, t, rk, amax, ctl, b, N, V, accept_len, path_nodes, out_tokens, status,
+                               lane);
+        }
         return;
     }
     uint64_t mk = key;
     bool complete = false;
-    for (int t = 0; t < kSkipPollCap; ++t) {
+    for (int it = 0; it < kSkipPollCap; ++it) {
         uint64_t m = 0;
         bool missing = false;
         for (int s = lane; s < segs - 1; s += kWave) {
@@ -675,33 +825,8 @@ __global__ __launch_bounds__(kBlock) void k_skip_tree(const typename E::storage 
     // address then needs no value of it before the segment's loads)
     unsigned *st_word = ctl.state + base + static_cast<unsigned>(rk);
     unsigned st = in ? shared_load(st_word) : 0u;
-    uint64_t rej = ballot(in && ((st & kRejected) || (lane > 0 && p == j && t != a)));
-    // close the rejection over the tree: a node under a rejected parent is rejected
-    for (int it = 0; it < N; ++it) {
-        const bool under = in && p >= 0 && p < lane && ((rej >> p) & 1ull);
-        const uint64_t r2 = rej | ballot(under);
-        if (r2 == rej) break;  // uniform
-        rej = r2;
-    }
-    unsigned mark = 0;
-    if (lane == j) mark |= kRowDone;
-    if (in && ((rej >> lane) & 1ull)) mark |= kRejected;
-    int newly = 0;
-    if (mark) {
-        const unsigned old = __hip_atomic_fetch_or(st_word, mark, __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_AGENT);
-        newly = old == 0 ? 1 : 0;
-    }
-    const int cnt = __popcll(ballot(newly != 0));
-    if (cnt == 0) return;
-    wait_own_stores();
-    unsigned before = 0;
-    if (lane == 0)
-        before = __hip_atomic_fetch_add(&ctl.resolved[b], static_cast<unsigned>(cnt), __ATOMIC_RELAXED,
-                                        __HIP_MEMORY_SCOPE_AGENT);
-    before = uniform(static_cast<unsigned>(__shfl(static_cast<int>(before), 0, kWave)));
-    if (before + static_cast<unsigned>(cnt) != static_cast<unsigned>(N)) return;
-    tree_finish(p, t, rk, amax, ctl, b, N, V, accept_len, path_nodes, out_tokens, status, lane);
+    const uint64_t rej = ballot(in && ((st & kRejected) || (lane > 0 && p == j && t != a)));
+    tree_mark(rej, j, p, t, rk, amax, ctl, b, N, V, accept_len, path_nodes, out_tokens, status, lane);
 }
 
 template <typename E, bool ALIGNED>
@@ -785,7 +910,9 @@ hipError_t launch_skip_match(const void *L, const int32_t *drafts, int B, int K,
 
 bool tree_skip_supported(int N) { return N <= kTreeSkipMaxN; }
 
-size_t tree_ctl_bytes(int B, int N) { return sizeof(unsigned) * (4 * static_cast<size_t>(B) * N + B); }
+size_t tree_ctl_bytes(int B, int N) {
+    return sizeof(uint64_t) * static_cast<size_t>(B) * N + sizeof(unsigned) * (4 * static_cast<size_t>(B) * N + 2 * B);
+}
 
 hipError_t launch_skip_tree(const void *L, const int32_t *node_tokens, const int32_t *parents, int B, int N,
                             int V, const RowGeom &g, sv_dtype dt, uint64_t *part_k, int32_t *amax,
@@ -793,14 +920,30 @@ hipError_t launch_skip_tree(const void *L, const int32_t *node_tokens, const int
                             int32_t *status, hipStream_t s) {
     TreeCtl ctl;
     const size_t bn = static_cast<size_t>(B) * N;
-    ctl.ticket = static_cast<unsigned *>(ctl_base);
+    ctl.ckey = static_cast<uint64_t *>(ctl_base);
+    ctl.ticket = reinterpret_cast<unsigned *>(ctl.ckey + bn);
     ctl.state = ctl.ticket + bn;
     ctl.order = reinterpret_cast<int32_t *>(ctl.state + bn);
     ctl.rank = ctl.order + bn;
     ctl.resolved = reinterpret_cast<unsigned *>(ctl.rank + bn);
+    ctl.nlive = ctl.resolved + B;
     trace_select(-1);  // the preparing launch is not traced
-    hipLaunchKernelGGL(k_tree_prep, dim3(static_cast<unsigned>((B + kWavesPerBlock - 1) / kWavesPerBlock)),
-                       dim3(kBlock), 0, s, parents, B, N, ctl, part_k, g.segs);
+    const dim3 prep_grid(static_cast<unsigned>(B));
+#define SV_TP(E, A, T)                                                                                          \
+    hipLaunchKernelGGL((k_tree_prep<E, A>), prep_grid, dim3(kBlock), 0, s, static_cast<const T *>(L), parents, \
+                       node_tokens, B, N, V, g.nvec, ctl, part_k, g.segs)
+    if (dt == SV_BF16) {
+        if (g.aligned)
+            SV_TP(BF16, true, uint16_t);
+        else
+            SV_TP(BF16, false, uint16_t);
+    } else {
+        if (g.aligned)
+            SV_TP(F32, true, float);
+        else
+            SV_TP(F32, false, float);
+    }
+#undef SV_TP
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     trace_select(SV_K_SKIP_TREE);

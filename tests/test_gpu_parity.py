@@ -170,6 +170,47 @@ def test_tree_acceptance_extremes(p_match):
         assert (o["accept_len"] <= 1).all()
 
 
+def test_tree_plausible_mismatches_and_sample_ties():
+    # The tree pass rejects a child before streaming when its token's logit is
+    # below the largest logit of the first 512 of its parent's row.  Here the
+    # mismatching children carry tokens that sample cannot reject: the row's
+    # second-best token, or a token past the sample whose logit equals the
+    # sample's maximum (a tie, left to the full decision), beside argmax and
+    # random tokens; the first case also puts the argmax inside the sample.
+    note("tree plausible mismatches")
+    rng = np.random.default_rng(77)
+    B, V = 40, 5000
+    par = np.stack([workloads.adapld_parents(int(rng.integers(0, 4)), rng=rng) for _ in range(B)])
+    N = par.shape[1]
+    L = workloads.to_bf16_bits(rng.standard_normal((B, N, V)).astype(np.float32) * 3)
+    Lf = workloads.bf16_bits_to_f32(L)
+    L[0, :, 7] = workloads.to_bf16_bits(np.full(N, 20.0, np.float32))  # argmax in the sample
+    Lf = workloads.bf16_bits_to_f32(L)
+    tok = np.zeros((B, N), np.int32)
+    for b in range(B):
+        for c in range(1, N):
+            p = par[b, c]
+            row = Lf[b, p]
+            order = np.argsort(-row, kind="stable")
+            mode = rng.integers(0, 4)
+            if mode == 0:
+                tok[b, c] = order[0]
+            elif mode == 1:
+                tok[b, c] = order[1]
+            elif mode == 2:
+                t = int(rng.integers(512, V))
+                L[b, p, t] = L[b, p, int(np.argmax(Lf[b, p, :512]))]
+                Lf[b, p, t] = workloads.bf16_bits_to_f32(L[b, p, t:t + 1])[0]
+                tok[b, c] = t
+            else:
+                tok[b, c] = int(rng.integers(0, V))
+    # the argmax of a row changed by a planted tie is recomputed by the oracle
+    w = workloads.Workload(mode="tree", B=B, N=N, V=V, dtype="bf16", target=L, node_tokens=tok, parents=par)
+    o = oracle.verify_tree(L, tok, par)
+    check_exact(gpu_tree(w), o, ("accept_len", "path", "tokens", "status"))
+    assert (o["accept_len"] >= 2).any()
+
+
 def test_tree_workload_full_size():
     note("tree workload B=64 N=33 V=151936")
     w = workloads.make_workload("tree_b64_n33_qwen3")
