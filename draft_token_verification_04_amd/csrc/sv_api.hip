@@ -76,7 +76,7 @@ GreedyWs greedy_ws_layout(int B, int rows_per_req, const RowGeom &g) {
     w.amax = o;
     if (skip) o = align_up(o + rows * sizeof(int32_t));
     w.skipctl = o;
-    const size_t ctl = std::max(chain ? skip_ctl_bytes(B, rows_per_req - 1) : 0,
+    const size_t ctl = std::max(chain ? skip_ctl_bytes(B, rows_per_req - 1) + sizeof(unsigned) * B : 0,
                                 tree ? tree_ctl_bytes(B, rows_per_req) : 0);
     if (skip) o = align_up(o + ctl);
     w.total = o;

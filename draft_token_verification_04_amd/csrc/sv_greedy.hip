@@ -355,8 +355,19 @@ __global__ __launch_bounds__(kBlock) void k_skip_argmax(const typename E::storag
     const unsigned slot = rem / static_cast<unsigned>(segs);
     const int sg = static_cast<int>(rem - slot * static_cast<unsigned>(segs));
     const int b = skip_request(slot, p, B, rot);
-    // position 0's rows are always needed: no test, no wait before their loads
-    if (p > 0 && (early ? skip_row_dead(ctl, b, p) : uniform(shared_load(&ctl.finished[b])) != 0)) return;
+    // position 0's rows are always needed: no test, no wait before their loads.
+    // Rows past the request's sampled rejection are dead from the start (a
+    // plain word the preparing launch wrote); the others are tested against
+    // the decisions recorded so far
+    if (p > 0) {
+#if SV_SKIP_FASTDECIDE && SV_SKIP_POLL
+        const unsigned lim = uniform(ctl.lim[b]);
+#else
+        const unsigned lim = static_cast<unsigned>(K);  // no preparing launch
+#endif
+        const bool dead = early ? skip_row_dead(ctl, b, p) : uniform(shared_load(&ctl.finished[b])) != 0;
+        if (static_cast<unsigned>(p) > lim || dead) return;
+    }
 
     const long long row = static_cast<long long>(b) * (K + 1) + p;
     int v0, v1;
@@ -451,6 +462,86 @@ __global__ __launch_bounds__(kBlock) void k_skip_argmax(const typename E::storag
         if (status) status[b] = any_bad ? 1 : 0;
     }
     skip_finished(ctl, b, lane);
+}
+
+// Per request of a greedy chain (one workgroup): clear the request's control
+// words, segment keys and argmax words, and sample the rows of its drafts.
+// The sample is a row's first 64 vectors (512 bf16 logits); when its largest
+// logit is above the logit of the row's draft, that draft is not the row's
+// argmax and is rejected.  The first such position r is recorded before any
+// row is streamed as the limit past which no row of the request is read; row
+// r itself is read, and its decision (a mismatch) records the rejection and
+// supplies the emitted argmax, so the decisions run as without the sample.
+// A draft outside the vocabulary counts as rejected, as in the decision.  With drafts that are either the
+// argmax or an unrelated token this finds almost every mismatch at once (an
+// unrelated token tops a 512-logit sample about once in 500); the others are
+// left to the decisions.
+constexpr int kChainPrepRows = kSkipMaxK / kWavesPerBlock + 1;  // sampled rows per wave
+template <typename E, bool ALIGNED>
+__global__ __launch_bounds__(kBlock) void k_chain_prep(const typename E::storage *__restrict__ L,
+                                                       const int32_t *__restrict__ drafts, int B, int K, int V,
+                                                       int nvec, int segs, SkipCtl ctl,
+                                                       uint64_t *__restrict__ part_k, int32_t *__restrict__ amax) {
+    constexpr int R = kChainPrepRows;
+    constexpr int kPad = kWave + 4;
+    __shared__ __align__(16) float s_part[(kSkipMaxK + 1) * kPad];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wid = threadIdx.x >> 6;
+    const int b = blockIdx.x;
+    if (b >= B) return;
+    const long long r0 = static_cast<long long>(b) * (K + 1);
+    int d = -1;
+    if (wid == 0 && lane < K) d = drafts[static_cast<long long>(b) * K + lane];
+    const int sv = min(nvec, kWave);
+    Staged<E, ALIGNED> st[R];
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+        const int p = wid + k * kWavesPerBlock;
+        if (p < K && lane < sv)
+            st[k].load(L + (r0 + p) * static_cast<long long>(V), V, lane);
+        else
+            st[k].set_neg_inf();
+    }
+    const bool dv = wid == 0 && lane < K && d >= 0 && d < V;
+    unsigned xb = 0;
+    if (dv) xb = storage_bits(L[(r0 + lane) * static_cast<long long>(V) + d]);
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+        const int p = wid + k * kWavesPerBlock;
+        if (p < K) {  // uniform
+            float x[E::kPerVec];
+            st[k].get(x);
+            float m = x[0];
+#pragma unroll
+            for (int e = 1; e < E::kPerVec; ++e) m = fmaxf(m, x[e]);
+            s_part[p * kPad + lane] = m;
+        }
+    }
+    // the words every wave of the request's rows reads start at 0
+    for (int i = threadIdx.x; i < (K + 1) * segs; i += kBlock) part_k[r0 * segs + i] = 0;
+    if (threadIdx.x <= K) {
+        amax[r0 + threadIdx.x] = 0;
+        ctl.ticket[r0 + threadIdx.x] = 0u;
+    }
+    __syncthreads();
+    if (wid != 0) return;
+    float smax = -__builtin_huge_valf();
+    if (lane < K) {
+        const float4 *r4 = reinterpret_cast<const float4 *>(s_part + lane * kPad);
+#pragma unroll
+        for (int i = 0; i < kWave / 4; ++i) {
+            const float4 v = r4[i];
+            smax = fmaxf(smax, fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w)));
+        }
+    }
+    const uint64_t rej = ballot(lane < K && (!dv || smax > from_bits<E>(xb)));
+    const int r = rej ? first_lane(rej) : K;
+    if (lane == 0) {
+        ctl.mask[b] = 0ull;
+        ctl.won[b] = 0u;
+        ctl.finished[b] = 0u;
+        ctl.lim[b] = static_cast<unsigned>(r);
+    }
 }
 
 // ---- trees: rows of rejected nodes are not read (N <= 64) ------------------------
@@ -890,13 +981,32 @@ hipError_t launch_skip_match(const void *L, const int32_t *drafts, int B, int K,
                              void *ctl_base, int32_t *accept_len, int32_t *out_tokens,
                              int32_t *status, hipStream_t s) {
     SkipCtl ctl;
-#if SV_SKIP_FASTDECIDE
-    // the argmax words (placed just before the control words), and with
-    // SV_SKIP_POLL the segment keys before them, start at 0 too
+#if SV_SKIP_FASTDECIDE && SV_SKIP_POLL
+    // one workgroup per request clears its words and samples its rows
     skip_ctl_carve(ctl_base, B, K, &ctl);
-    char *first = SV_SKIP_POLL ? reinterpret_cast<char *>(part_k) : reinterpret_cast<char *>(amax);
-    const size_t span = static_cast<size_t>(static_cast<char *>(ctl_base) - first) + skip_ctl_bytes(B, K);
-    hipError_t e = clear_words(first, span, s);
+    trace_select(-1);  // the preparing launch is not traced
+#define SV_CP(E, A, T)                                                                                           \
+    hipLaunchKernelGGL((k_chain_prep<E, A>), dim3(static_cast<unsigned>(B)), dim3(kBlock), 0, s,               \
+                       static_cast<const T *>(L), drafts, B, K, V, g.nvec, g.segs, ctl, part_k, amax)
+    if (dt == SV_BF16) {
+        if (g.aligned)
+            SV_CP(BF16, true, uint16_t);
+        else
+            SV_CP(BF16, false, uint16_t);
+    } else {
+        if (g.aligned)
+            SV_CP(F32, true, float);
+        else
+            SV_CP(F32, false, float);
+    }
+#undef SV_CP
+    hipError_t e = hipGetLastError();
+#elif SV_SKIP_FASTDECIDE
+    // the argmax words (placed just before the control words) start at 0 too
+    skip_ctl_carve(ctl_base, B, K, &ctl);
+    const size_t span = static_cast<size_t>(static_cast<char *>(ctl_base) - reinterpret_cast<char *>(amax)) +
+                        skip_ctl_bytes(B, K);
+    hipError_t e = clear_words(amax, span, s);
 #else
     hipError_t e = skip_ctl_init(ctl_base, B, K, &ctl, s);
 #endif

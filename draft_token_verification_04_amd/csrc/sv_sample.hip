@@ -1130,6 +1130,7 @@ void skip_ctl_carve(void *base, int B, int K, SkipCtl *ctl) {
     ctl->ticket = reinterpret_cast<unsigned *>(ctl->mask + B);
     ctl->won = ctl->ticket + static_cast<size_t>(B) * (K + 1);
     ctl->finished = ctl->won + B;
+    ctl->lim = ctl->finished + B;  // past skip_ctl_bytes: only the greedy chain's words hold it
 }
 
 hipError_t skip_ctl_init(void *base, int B, int K, SkipCtl *ctl, hipStream_t s) {

@@ -40,6 +40,8 @@ struct SkipCtl {
     uint64_t *mask;      // [B] decided | rejected << 32
     unsigned *won;       // [B] 1 once a decider has claimed finishing the request
     unsigned *finished;  // [B] raised after the request's outputs are written
+    unsigned *lim;       // [B] last position whose row can be needed, from row samples (greedy
+                         // chain only, whose workspace holds B more words than skip_ctl_bytes)
 };
 
 // Carves the control words of a B x K chain out of `base` (skip_ctl_bytes

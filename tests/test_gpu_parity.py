@@ -120,6 +120,40 @@ def test_greedy_acceptance_extremes(p_match):
         assert (o["accept_len"] == 7).all()
 
 
+def test_greedy_plausible_mismatches_and_sample_ties():
+    # The chain pass stops reading a request at the first draft whose logit is
+    # below the largest of the first 512 logits of its row.  Here mismatching
+    # drafts carry tokens that sample cannot reject: the row's second-best
+    # token, or a token past the sample whose logit equals the sample's
+    # maximum (a tie, left to the full decision), beside argmax and random
+    # drafts and rows whose argmax lies inside the sample.
+    note("greedy plausible mismatches")
+    rng = np.random.default_rng(78)
+    B, K, V = 96, 7, 5000
+    L = workloads.to_bf16_bits(rng.standard_normal((B, K + 1, V)).astype(np.float32) * 3)
+    L[:8, :, 11] = workloads.to_bf16_bits(np.full((8, K + 1), 20.0, np.float32))  # argmax in the sample
+    Lf = workloads.bf16_bits_to_f32(L)
+    x = np.zeros((B, K), np.int32)
+    for b in range(B):
+        for p in range(K):
+            order = np.argsort(-Lf[b, p], kind="stable")
+            mode = rng.choice(4, p=[0.7, 0.1, 0.1, 0.1])
+            if mode == 0:
+                x[b, p] = order[0]
+            elif mode == 1:
+                x[b, p] = order[1]
+            elif mode == 2:
+                t = int(rng.integers(512, V))
+                L[b, p, t] = L[b, p, int(np.argmax(Lf[b, p, :512]))]
+                x[b, p] = t
+            else:
+                x[b, p] = int(rng.integers(0, V))
+    w = workloads.Workload(mode="greedy", B=B, K=K, V=V, dtype="bf16", target=L, draft_tokens=x)
+    o = oracle.verify_greedy(L, x)
+    check_exact(gpu_greedy(w), o, ("accept_len", "tokens", "status"))
+    assert (o["accept_len"] >= 3).any() and (o["accept_len"] == 0).any()
+
+
 @pytest.mark.parametrize("B", [512, 256])
 def test_greedy_workload_full_size(B):
     note(f"greedy workload B={B} K=7 V=151936")
