@@ -627,6 +627,19 @@ __global__ __launch_bounds__(kBlock) void k_tree_prep(const typename E::storage 
     const bool tv = t >= 0 && t < V;
     unsigned xb = 0;
     if (pv && tv) xb = storage_bits(L[(base + p) * static_cast<long long>(V) + t]);
+    // depths (wave 0), while the samples and the token logits are in flight
+    const bool topo = lane > 0 && p >= 0 && p < lane;  // a parent listed before its child
+    int dep = 0;
+    if (wid == 0) {
+        int anc = (lane == 0 || !in || !topo) ? 0 : p;
+        dep = (lane == 0 || !in) ? 0 : 1;
+        for (int span = 1; span < N; span <<= 1) {
+            const int d2 = __shfl(dep, anc, kWave);
+            const int a2 = __shfl(anc, anc, kWave);
+            dep += d2;
+            anc = a2;
+        }
+    }
     // each lane's largest sampled logit of each row, reduced per row below
 #pragma unroll
     for (int k = 0; k < R; ++k) {
@@ -658,7 +671,6 @@ __global__ __launch_bounds__(kBlock) void k_tree_prep(const typename E::storage 
     }
     const float sp = __shfl(smax, pv ? p : 0, kWave);
     // a token outside the vocabulary can never be the argmax
-    const bool topo = lane > 0 && p >= 0 && p < lane;  // a parent listed before its child
     uint64_t dead = ballot(pv && (!tv || sp > from_bits<E>(xb)));
     for (int it = 0; it < N; ++it) {  // close over the tree, as the decisions do
         const uint64_t d2 = dead | ballot(in && topo && ((dead >> p) & 1ull));
@@ -666,14 +678,6 @@ __global__ __launch_bounds__(kBlock) void k_tree_prep(const typename E::storage 
         dead = d2;
     }
     const bool is_dead = in && ((dead >> lane) & 1ull);
-    int anc = (lane == 0 || !in || !topo) ? 0 : p;
-    int dep = (lane == 0 || !in) ? 0 : 1;
-    for (int span = 1; span < N; span <<= 1) {
-        const int d2 = __shfl(dep, anc, kWave);
-        const int a2 = __shfl(anc, anc, kWave);
-        dep += d2;
-        anc = a2;
-    }
     const unsigned key = in ? ((is_dead ? 1u << 16 : 0u) | (static_cast<unsigned>(dep) << 8) | static_cast<unsigned>(lane))
                             : 0xffffffffu;
     int rk = 0;
