@@ -20,14 +20,17 @@
 //             parent-array check in parallel, acceptance and depth of every
 //             node by pointer jumping (log2 N rounds), the deepest accepted
 //             node by an LDS max, then the path write-out.
-//   k_skip_argmax  chains with K <= 31 in one launch that does not read the
-//             rows after each request's first mismatch (the protocol is
-//             described with SkipCtl); the decision of position p is the row
-//             argmax compared with draft p.
+//   k_chain_prep, k_skip_argmax  chains with K <= 31: a small launch clears
+//             each request's words and finds, from a sample of each draft's
+//             row, the first draft that cannot be the argmax; then one launch
+//             that does not read the rows after each request's first mismatch
+//             (the protocol is described with SkipCtl); the decision of
+//             position p is the row argmax compared with draft p.
 //   k_tree_prep, k_skip_tree  trees with N <= 64: a small launch clears the
-//             control words and ranks each request's nodes by depth, then one
-//             launch reads the node rows level by level, skipping the rows of
-//             nodes already known rejected (described with TreeCtl).
+//             control words, rejects the nodes a sample of their parent's row
+//             rules out and ranks the rest by depth, then one launch reads
+//             the node rows level by level, skipping the rows of nodes
+//             already known rejected (described with TreeCtl).
 #include <limits.h>
 
 #include <algorithm>
@@ -548,15 +551,18 @@ __global__ __launch_bounds__(kBlock) void k_chain_prep(const typename E::storage
 //
 // A node's row is needed only when the node is accepted: its argmax decides its
 // children and, for the chosen node, the bonus.  A first small launch
-// (k_tree_prep, one wave per request) clears the control words and ranks each
-// request's nodes by (depth, index): slot i of the request holds the node of
-// rank i.  The main launch runs over every (slot i, request b, segment) in
+// (k_tree_prep, one workgroup per request) clears the control words, rejects
+// the nodes that a sample of their parent's row already rules out, and ranks
+// the request's live nodes by (depth, index) ahead of the rejected ones: slot
+// i of the request holds the node of rank i, and the slots from the live count
+// on are never read.  The main launch runs over every (slot i, request b, segment) in
 // slot order, so every node of depth d is read before any of depth d + 1 and
 // the decisions about a level have usually landed before the next level's
 // waves start (in plain index order, a deep chain listed early would be read
 // before its first node is decided).  A wave skips its segment when the node of
-// its slot is already known rejected.  The last wave of a row (found by a
-// ticket) takes its argmax a_j, marks the row done, and rejects every child
+// its slot is already known rejected.  The first wave of a row rejects the
+// children whose token keys its segment beats; the last wave of a row takes
+// its argmax a_j, marks the row done, and rejects every child
 // whose token differs from a_j together with the descendants of every rejected
 // node (parents, tokens and states of the request's nodes held one per lane,
 // the rejection closed over the tree by ballots).  Each node is resolved once -
