@@ -120,34 +120,37 @@ def test_greedy_acceptance_extremes(p_match):
         assert (o["accept_len"] == 7).all()
 
 
-def test_greedy_plausible_mismatches_and_sample_ties():
+@pytest.mark.parametrize("B,K,V", [(96, 7, 5000), (384, 7, 151936), (40, 31, 3000)],
+                         ids=["B96K7V5000", "B384K7V151936", "B40K31V3000"])
+def test_greedy_plausible_mismatches_and_sample_ties(B, K, V):
     # The chain pass stops reading a request at the first draft whose logit is
     # below the largest of the first 512 logits of its row.  Here mismatching
     # drafts carry tokens that sample cannot reject: the row's second-best
     # token, or a token past the sample whose logit equals the sample's
     # maximum (a tie, left to the full decision), beside argmax and random
-    # drafts and rows whose argmax lies inside the sample.
-    note("greedy plausible mismatches")
-    rng = np.random.default_rng(78)
-    B, K, V = 96, 7, 5000
+    # drafts and rows whose argmax lies inside the sample.  B=384 at the full
+    # vocabulary takes the pass's early rejection test without rotation.
+    note(f"greedy plausible mismatches B={B} K={K} V={V}")
+    rng = np.random.default_rng(78 + B)
     L = workloads.to_bf16_bits(rng.standard_normal((B, K + 1, V)).astype(np.float32) * 3)
     L[:8, :, 11] = workloads.to_bf16_bits(np.full((8, K + 1), 20.0, np.float32))  # argmax in the sample
     Lf = workloads.bf16_bits_to_f32(L)
-    x = np.zeros((B, K), np.int32)
-    for b in range(B):
-        for p in range(K):
-            order = np.argsort(-Lf[b, p], kind="stable")
-            mode = rng.choice(4, p=[0.7, 0.1, 0.1, 0.1])
-            if mode == 0:
-                x[b, p] = order[0]
-            elif mode == 1:
-                x[b, p] = order[1]
-            elif mode == 2:
-                t = int(rng.integers(512, V))
-                L[b, p, t] = L[b, p, int(np.argmax(Lf[b, p, :512]))]
-                x[b, p] = t
-            else:
-                x[b, p] = int(rng.integers(0, V))
+    first = Lf.argmax(-1)                                  # lowest index among equals
+    masked = Lf.copy()
+    np.put_along_axis(masked, first[..., None], -np.inf, axis=-1)
+    second = masked.argmax(-1)
+    del masked
+    smax_at = Lf[..., :512].argmax(-1)
+    mode = rng.choice(4, size=(B, K), p=[0.7, 0.1, 0.1, 0.1])
+    x = rng.integers(0, V, size=(B, K)).astype(np.int32)
+    x = np.where(mode == 0, first[:, :K], x)
+    x = np.where(mode == 1, second[:, :K], x)
+    tie = np.argwhere(mode == 2)
+    for b, p in tie:
+        t = int(rng.integers(512, V))
+        L[b, p, t] = L[b, p, smax_at[b, p]]
+        x[b, p] = t
+    x = x.astype(np.int32)
     w = workloads.Workload(mode="greedy", B=B, K=K, V=V, dtype="bf16", target=L, draft_tokens=x)
     o = oracle.verify_greedy(L, x)
     check_exact(gpu_greedy(w), o, ("accept_len", "tokens", "status"))
@@ -204,41 +207,47 @@ def test_tree_acceptance_extremes(p_match):
         assert (o["accept_len"] <= 1).all()
 
 
-def test_tree_plausible_mismatches_and_sample_ties():
+@pytest.mark.parametrize("B,V,shape", [(40, 5000, "adapld"), (64, 151936, "adapld"), (24, 3000, "random64")])
+def test_tree_plausible_mismatches_and_sample_ties(B, V, shape):
     # The tree pass rejects a child before streaming when its token's logit is
     # below the largest logit of the first 512 of its parent's row.  Here the
     # mismatching children carry tokens that sample cannot reject: the row's
     # second-best token, or a token past the sample whose logit equals the
     # sample's maximum (a tie, left to the full decision), beside argmax and
-    # random tokens; the first case also puts the argmax inside the sample.
-    note("tree plausible mismatches")
-    rng = np.random.default_rng(77)
-    B, V = 40, 5000
-    par = np.stack([workloads.adapld_parents(int(rng.integers(0, 4)), rng=rng) for _ in range(B)])
+    # random tokens; the first requests also put the argmax inside the sample.
+    note(f"tree plausible mismatches B={B} V={V} {shape}")
+    rng = np.random.default_rng(77 + B)
+    if shape == "adapld":
+        par = np.stack([workloads.adapld_parents(int(rng.integers(0, 4)), rng=rng) for _ in range(B)])
+    else:
+        N = 64
+        par = np.empty((B, N), np.int32)
+        par[:, 0] = -1
+        for j in range(1, N):
+            par[:, j] = rng.integers(0, j, size=B)
     N = par.shape[1]
     L = workloads.to_bf16_bits(rng.standard_normal((B, N, V)).astype(np.float32) * 3)
+    L[:4, :, 7] = workloads.to_bf16_bits(np.full((4, N), 20.0, np.float32))  # argmax in the sample
     Lf = workloads.bf16_bits_to_f32(L)
-    L[0, :, 7] = workloads.to_bf16_bits(np.full(N, 20.0, np.float32))  # argmax in the sample
-    Lf = workloads.bf16_bits_to_f32(L)
-    tok = np.zeros((B, N), np.int32)
-    for b in range(B):
-        for c in range(1, N):
-            p = par[b, c]
-            row = Lf[b, p]
-            order = np.argsort(-row, kind="stable")
-            mode = rng.integers(0, 4)
-            if mode == 0:
-                tok[b, c] = order[0]
-            elif mode == 1:
-                tok[b, c] = order[1]
-            elif mode == 2:
-                t = int(rng.integers(512, V))
-                L[b, p, t] = L[b, p, int(np.argmax(Lf[b, p, :512]))]
-                Lf[b, p, t] = workloads.bf16_bits_to_f32(L[b, p, t:t + 1])[0]
-                tok[b, c] = t
-            else:
-                tok[b, c] = int(rng.integers(0, V))
-    # the argmax of a row changed by a planted tie is recomputed by the oracle
+    first = Lf.argmax(-1)
+    masked = Lf.copy()
+    np.put_along_axis(masked, first[..., None], -np.inf, axis=-1)
+    second = masked.argmax(-1)
+    del masked
+    smax_at = Lf[..., :512].argmax(-1)
+    pp = np.maximum(par, 0)
+    mode = rng.integers(0, 4, size=(B, N))
+    tok = rng.integers(0, V, size=(B, N)).astype(np.int32)
+    tok = np.where(mode == 0, np.take_along_axis(first, pp, 1), tok)
+    tok = np.where(mode == 1, np.take_along_axis(second, pp, 1), tok)
+    for b, c in np.argwhere(mode == 2):
+        if c == 0:
+            continue
+        p = par[b, c]
+        t = int(rng.integers(512, V))
+        L[b, p, t] = L[b, p, smax_at[b, p]]  # a tie past the sample; the row's argmax stays
+        tok[b, c] = t
+    tok = tok.astype(np.int32)
     w = workloads.Workload(mode="tree", B=B, N=N, V=V, dtype="bf16", target=L, node_tokens=tok, parents=par)
     o = oracle.verify_tree(L, tok, par)
     check_exact(gpu_tree(w), o, ("accept_len", "path", "tokens", "status"))
