@@ -89,10 +89,13 @@ constexpr int kGSkipVecsPerLane = SV_GSKIP_VECS;
 constexpr int kSkipPollCap = 1 << 22;
 
 constexpr int kGSkipChunks = SV_GSKIP_CHUNKS;
-// Waves the residual-mass pass aims for: short waves of a few tiles each
-// (measured: 28 us per pass at B=256 against 32 us with 4096 longer waves).
+// Waves the residual-mass pass aims for: short waves of a few tiles each.
+// Measured on MI355X at B=256 (V=151936 bf16, rows evicted before each call,
+// as they are after the statistics pass): 49152 (one group of 2 tiles per
+// wave) 24.9-25.0 us, 32768 (4 tiles) 26.0-26.2, 16384 (6 tiles) 26.2, and
+// one tile per wave 27.4-28.8; 4096 longer waves ran 32 us.
 #ifndef SV_RESID_WAVES
-#define SV_RESID_WAVES 32768
+#define SV_RESID_WAVES 49152
 #endif
 constexpr int kResidTargetWaves = SV_RESID_WAVES;
 // Bytes of LDS the per-request merge kernels use to stage row partials.
