@@ -294,9 +294,11 @@ __device__ __forceinline__ float fast_exp2(float a) { return __builtin_amdgcn_ex
 // stores for those words: the hardware keeps them coherent across the XCDs'
 // separate L2 caches without the whole-cache write-back and invalidation a
 // device-scope fence costs there (tens of microseconds per fence, measured).
-// The one ordering needed - a wave's shared stores complete before its next
-// counter update - comes from waiting on the wave's own outstanding memory
-// operations.  No wave ever waits for another.
+// The one ordering needed - a wave's shared stores complete before the atomic
+// that publishes its decision - comes from waiting on the wave's own
+// outstanding memory operations.  A wave waits for another only by polling a
+// word written once, by a wave dispatched before it, which either writes it
+// or, having found the request settled, lets the poller find that too.
 //
 // Why that is enough on gfx950.  In the LLVM AMDGPU memory model for
 // GFX942/GFX950, an agent-scope release is "buffer_wbl2 sc1; s_waitcnt
@@ -311,10 +313,11 @@ __device__ __forceinline__ float fast_exp2(float a) { return __builtin_amdgcn_ex
 // release needs only the wait: on this gfx9-family part vmcnt counts stores
 // and atomics as well as loads, and it drops only when the memory system has
 // acknowledged them.  On the reading side, the loads of another wave's words
-// are control-dependent on the returned value of the ticket or mask atomic
-// (the branch that selects the deciding wave needs it), and a wave issues in
-// order without speculating past a branch, so they issue after it returns;
-// the logits they then read are inputs no kernel of the launch writes.
+// are control-dependent on the value a poll returned or on the returned value
+// of the mask atomic (the branch that selects the deciding or finishing wave
+// needs it), and a wave issues in order without speculating past a branch, so
+// they issue after it returns; the logits they then read are inputs no kernel
+// of the launch writes.
 // The waiting is an asm statement with a memory clobber, so the compiler can
 // move no memory access across it either.
 
@@ -339,16 +342,6 @@ __device__ __forceinline__ unsigned uniform(unsigned v) {
 __device__ __forceinline__ uint64_t uniform(uint64_t v) {
     const unsigned lo = uniform(static_cast<unsigned>(v)), hi = uniform(static_cast<unsigned>(v >> 32));
     return (static_cast<uint64_t>(hi) << 32) | lo;
-}
-
-// Count one arrival at *t once this wave's shared stores are complete; true
-// for the arrival that completes `total` (all earlier arrivals' shared
-// stores are complete by then).
-__device__ __forceinline__ bool wave_arrive(unsigned *t, unsigned total, int lane) {
-    wait_own_stores();
-    unsigned old = 0;
-    if (lane == 0) old = __hip_atomic_fetch_add(t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return uniform(static_cast<unsigned>(__shfl(static_cast<int>(old), 0, kWave))) + 1 == total;
 }
 
 }  // namespace sv

@@ -363,11 +363,7 @@ __global__ __launch_bounds__(kBlock) void k_skip_argmax(const typename E::storag
     // plain word the preparing launch wrote); the others are tested against
     // the decisions recorded so far
     if (p > 0) {
-#if SV_SKIP_FASTDECIDE && SV_SKIP_POLL
         const unsigned lim = uniform(ctl.lim[b]);
-#else
-        const unsigned lim = static_cast<unsigned>(K);  // no preparing launch
-#endif
         const bool dead = early ? skip_row_dead(ctl, b, p) : uniform(shared_load(&ctl.finished[b])) != 0;
         if (static_cast<unsigned>(p) > lim || dead) return;
     }
@@ -381,7 +377,6 @@ __global__ __launch_bounds__(kBlock) void k_skip_argmax(const typename E::storag
     const int32_t *xb = drafts + static_cast<long long>(b) * K;
     const int xl = sg == segs - 1 && lane < K ? xb[lane] : 0;
     const uint64_t key = segment_argmax_chunked<E, ALIGNED, U, kGSkipChunks>(L + row * V, V, v0, v1, lane);
-#if SV_SKIP_POLL
     // Every wave leaves its segment's key (never 0; the keys start at 0) and
     // goes; the wave of the row's last segment, dispatched after all the
     // others, collects them and decides.  A key it waits for is either on its
@@ -411,21 +406,8 @@ __global__ __launch_bounds__(kBlock) void k_skip_argmax(const typename E::storag
     }
     if (!complete) return;  // never decide on part of a row
     const int a = uniform(argmax_key_index(mk));
-#else
-    if (lane == 0) shared_store(&part_k[row * segs + sg], key);
-    if (!wave_arrive(&ctl.ticket[row], static_cast<unsigned>(segs), lane)) return;
-
-    // last segment of (b, p): the row argmax decides position p
-    uint64_t mk = 0;
-    for (int s = lane; s < segs; s += kWave) {
-        const uint64_t k = shared_load(&part_k[row * segs + s]);
-        mk = k > mk ? k : mk;
-    }
-    const int a = uniform(argmax_key_index(wave_max_u64(mk)));
-#endif
     uint64_t bits = 1ull << p;
     if (p < K && uniform(__shfl(xl, p, kWave)) != a) bits |= 1ull << (32 + p);
-#if SV_SKIP_FASTDECIDE
     // amax holds each decided row's argmax plus one (0: not yet known); the
     // store need not land before the decision, the finisher polls for it
     uint64_t old = 0;
@@ -446,12 +428,6 @@ __global__ __launch_bounds__(kBlock) void k_skip_argmax(const typename E::storag
         }
         an = uniform(__shfl(v, 0, kWave)) - 1;
     }
-#else
-    if (lane == 0) shared_store(&amax[row], a);
-    const int n = skip_decide(ctl, b, K, bits, lane);
-    if (n < 0) return;
-    const int an = n == p ? a : uniform(shared_load(&amax[static_cast<long long>(b) * (K + 1) + n]));
-#endif
     bool bad = false;
     int32_t *tok = out_tokens + static_cast<long long>(b) * (K + 1);
     for (int i = lane; i <= K; i += kWave) {  // K <= 31: lane i holds draft i
@@ -522,10 +498,7 @@ __global__ __launch_bounds__(kBlock) void k_chain_prep(const typename E::storage
     }
     // the words every wave of the request's rows reads start at 0
     for (int i = threadIdx.x; i < (K + 1) * segs; i += kBlock) part_k[r0 * segs + i] = 0;
-    if (threadIdx.x <= K) {
-        amax[r0 + threadIdx.x] = 0;
-        ctl.ticket[r0 + threadIdx.x] = 0u;
-    }
+    if (threadIdx.x <= K) amax[r0 + threadIdx.x] = 0;
     __syncthreads();
     if (wid != 0) return;
     float smax = -__builtin_huge_valf();
@@ -541,7 +514,6 @@ __global__ __launch_bounds__(kBlock) void k_chain_prep(const typename E::storage
     const int r = rej ? first_lane(rej) : K;
     if (lane == 0) {
         ctl.mask[b] = 0ull;
-        ctl.won[b] = 0u;
         ctl.finished[b] = 0u;
         ctl.lim[b] = static_cast<unsigned>(r);
     }
@@ -576,7 +548,6 @@ constexpr int kTreeSkipMaxN = kWave;
 
 struct TreeCtl {
     uint64_t *ckey;      // [B*N] argmax key of each node's token in its parent's row
-    unsigned *ticket;    // [B*N] segments finished, per slot
     unsigned *state;     // [B*N] kRowDone | kRejected of the node in each slot
     unsigned *resolved;  // [B] nodes resolved
     int32_t *order;      // [B*N] node of each slot (ascending depth, then index)
@@ -659,7 +630,7 @@ __global__ __launch_bounds__(kBlock) void k_tree_prep(const typename E::storage 
             s_part[j * kPad + lane] = m;
         }
     }
-    if (SV_SKIP_POLL) {  // the segment keys of the request's rows start at 0
+    {  // the segment keys of the request's rows start at 0
         uint64_t *pk = part_k + base * segs;
         for (int i = threadIdx.x; i < N * segs; i += kBlock) pk[i] = 0;
     }
@@ -693,7 +664,6 @@ __global__ __launch_bounds__(kBlock) void k_tree_prep(const typename E::storage 
     if (in) {
         ctl.order[base + rk] = lane;
         ctl.rank[base + lane] = rk;
-        ctl.ticket[base + lane] = 0u;
         ctl.state[base + rk] = is_dead ? kRejected : 0u;
         // the key of the node's token in its parent's row, tested by the
         // parent row's first segment (a rejected node needs no second test)
@@ -872,7 +842,6 @@ __global__ __launch_bounds__(kBlock) void k_skip_tree(const typename E::storage 
         if (early) ck = ctl.ckey[base + lane];
     }
     const uint64_t key = segment_argmax_chunked<E, ALIGNED, U, kGSkipChunks>(L + row * V, V, v0, v1, lane);
-#if SV_SKIP_POLL
     // keys handed to the row's last segment as in the chain pass (the prep
     // launch zeroed them); a key never comes only if its wave found the node
     // already rejected, which this wave then finds too
@@ -907,18 +876,6 @@ __global__ __launch_bounds__(kBlock) void k_skip_tree(const typename E::storage 
     }
     if (!complete) return;  // never decide on part of a row
     const int a = uniform(argmax_key_index(mk));
-#else
-    if (lane == 0) shared_store(&part_k[row * segs + sg], key);
-    if (!wave_arrive(&ctl.ticket[base + slot], static_cast<unsigned>(segs), lane)) return;
-
-    // last segment of node j's row: its argmax decides j's children
-    uint64_t mk = 0;
-    for (int s = lane; s < segs; s += kWave) {
-        const uint64_t k = shared_load(&part_k[row * segs + s]);
-        mk = k > mk ? k : mk;
-    }
-    const int a = uniform(argmax_key_index(wave_max_u64(mk)));
-#endif
     if (lane == 0) shared_store(&amax[row], a);
     wait_own_stores();
     // states as they stand, plus this row done and this row's mismatching children
@@ -991,7 +948,6 @@ hipError_t launch_skip_match(const void *L, const int32_t *drafts, int B, int K,
                              void *ctl_base, int32_t *accept_len, int32_t *out_tokens,
                              int32_t *status, hipStream_t s) {
     SkipCtl ctl;
-#if SV_SKIP_FASTDECIDE && SV_SKIP_POLL
     // one workgroup per request clears its words and samples its rows
     skip_ctl_carve(ctl_base, B, K, &ctl);
     trace_select(-1);  // the preparing launch is not traced
@@ -1011,15 +967,6 @@ hipError_t launch_skip_match(const void *L, const int32_t *drafts, int B, int K,
     }
 #undef SV_CP
     hipError_t e = hipGetLastError();
-#elif SV_SKIP_FASTDECIDE
-    // the argmax words (placed just before the control words) start at 0 too
-    skip_ctl_carve(ctl_base, B, K, &ctl);
-    const size_t span = static_cast<size_t>(static_cast<char *>(ctl_base) - reinterpret_cast<char *>(amax)) +
-                        skip_ctl_bytes(B, K);
-    hipError_t e = clear_words(amax, span, s);
-#else
-    hipError_t e = skip_ctl_init(ctl_base, B, K, &ctl, s);
-#endif
     if (e != hipSuccess) return e;
     trace_select(SV_K_SKIP_ARGMAX);
 #define SV_SK(E, A) skip_argmax_t<E, A>(L, drafts, B, K, V, g, part_k, amax, ctl, accept_len, out_tokens, status, s)
@@ -1031,7 +978,7 @@ hipError_t launch_skip_match(const void *L, const int32_t *drafts, int B, int K,
 bool tree_skip_supported(int N) { return N <= kTreeSkipMaxN; }
 
 size_t tree_ctl_bytes(int B, int N) {
-    return sizeof(uint64_t) * static_cast<size_t>(B) * N + sizeof(unsigned) * (4 * static_cast<size_t>(B) * N + 2 * B);
+    return sizeof(uint64_t) * static_cast<size_t>(B) * N + sizeof(unsigned) * (3 * static_cast<size_t>(B) * N + 2 * B);
 }
 
 hipError_t launch_skip_tree(const void *L, const int32_t *node_tokens, const int32_t *parents, int B, int N,
@@ -1041,8 +988,7 @@ hipError_t launch_skip_tree(const void *L, const int32_t *node_tokens, const int
     TreeCtl ctl;
     const size_t bn = static_cast<size_t>(B) * N;
     ctl.ckey = static_cast<uint64_t *>(ctl_base);
-    ctl.ticket = reinterpret_cast<unsigned *>(ctl.ckey + bn);
-    ctl.state = ctl.ticket + bn;
+    ctl.state = reinterpret_cast<unsigned *>(ctl.ckey + bn);
     ctl.order = reinterpret_cast<int32_t *>(ctl.state + bn);
     ctl.rank = ctl.order + bn;
     ctl.resolved = reinterpret_cast<unsigned *>(ctl.rank + bn);

@@ -55,21 +55,6 @@ constexpr int kSkipChunks = SV_SKIP_CHUNKS;
 #define SV_GSKIP_CHUNKS 2
 #endif
 constexpr int kGSkipVecsPerLane = SV_GSKIP_VECS;
-// The greedy chain's skip pass records decisions with one atomic OR (the
-// decision that completes a request's decided prefix finishes it) and keeps
-// row argmaxes plus one, polled by the finisher (0: decide and wait as the
-// stochastic pass does).
-#ifndef SV_SKIP_FASTDECIDE
-#define SV_SKIP_FASTDECIDE 1
-#endif
-// ... and its waves hand their segment keys to the row's last segment without
-// a ticket (that wave polls for them; needs SV_SKIP_FASTDECIDE).
-#ifndef SV_SKIP_POLL
-#define SV_SKIP_POLL 1
-#endif
-#if SV_SKIP_POLL && !SV_SKIP_FASTDECIDE
-#error "SV_SKIP_POLL needs SV_SKIP_FASTDECIDE"
-#endif
 // Dynamic LDS each workgroup of the greedy chain's and the tree's skip passes
 // reserves, unused, to cap the workgroups per compute unit (0: as many as their
 // registers allow, five).  Measured on MI355X (us per pass, chain B=256 / chain

@@ -780,25 +780,6 @@ __global__ __launch_bounds__(kBlock) void k_zero_words(uint32_t *__restrict__ p,
         p[i] = 0;
 }
 
-#if !SV_SKIP_POLL
-// log2 sum_v 2^(L[v] c) of one row from segment partials read as shared words.
-__device__ __forceinline__ double merge_row_shared(float *pR, double *pS, int segs, int lane) {
-    float Rm = -__builtin_huge_valf();
-    for (int sg = lane; sg < segs; sg += kWave) Rm = fmaxf(Rm, shared_load(&pR[sg]));
-    Rm = wave_max(Rm);
-    double acc = 0.0;
-    if (Rm != -__builtin_huge_valf()) {
-        for (int sg = lane; sg < segs; sg += kWave) {
-            const double ss = shared_load(&pS[sg]);
-            if (ss > 0.0) acc += ss * exp2(static_cast<double>(shared_load(&pR[sg])) - static_cast<double>(Rm));
-        }
-    }
-    acc = wave_sum(acc);
-    return acc > 0.0 ? static_cast<double>(Rm) + log2(acc) : -__builtin_huge_val();
-}
-#endif
-
-#if SV_SKIP_POLL
 // Words a wave hands to another without a ticket are marked so that a written
 // word is never 0 (the words start at 0): a segment's R as its bits with the
 // sign flipped (-0 taken as +0 first), its s >= 0 with the sign bit set, a
@@ -854,8 +835,6 @@ __device__ __forceinline__ double merge_row_marked(uint32_t *wR, uint64_t *wS, l
     acc = wave_sum(acc);
     return acc > 0.0 ? static_cast<double>(Rm) + log2(acc) : -__builtin_huge_val();
 }
-
-#endif
 
 // Outputs of request b decided at n (mode 1: rejection at n, residual of
 // rows n; mode 0: bonus from target row K), written by one wave that holds
@@ -949,7 +928,6 @@ __global__ __launch_bounds__(kBlock) void k_skip_stats(
     segment_stats_chunked<E, ALIGNED, U, kSkipChunks>(base, V, v0, v1, c_hi, c_lo, lane, R, sum);
     const int nrows = 2 * K + 1;
     double *L2b = L2 + static_cast<long long>(b) * nrows;
-#if SV_SKIP_POLL
     // Every wave but the last of (b, p) leaves its partial as two marked words
     // (never 0; they start at 0) and goes.  The last one, the draft row's last
     // segment (the target row's at the bonus position), is dispatched after
@@ -1003,19 +981,6 @@ __global__ __launch_bounds__(kBlock) void k_skip_stats(
         L2p = merge_row_marked(wR, wS, gt * segs, segs, p < K ? segs : segs - 1, R, sum, lane);
         if (p < K) L2q = merge_row_marked(wR, wS, gd * segs, segs, segs - 1, R, sum, lane);
     }
-#else
-    if (lane == 0) {
-        shared_store(&part_R[g * segs + sg], R);
-        shared_store(&part_s[g * segs + sg], sum);
-    }
-    const unsigned parts = static_cast<unsigned>((p < K ? 2 : 1) * segs);
-    if (!wave_arrive(&ctl.ticket[gt], parts, lane)) return;
-
-    // last segment of (b, p): decide position p
-    const double L2p = merge_row_shared(part_R + gt * segs, part_s + gt * segs, segs, lane);
-    double L2q = 0.0;
-    if (p < K) L2q = merge_row_shared(part_R + gd * segs, part_s + gd * segs, segs, lane);
-#endif
     uint64_t bits = 1ull << p;
     if (p < K) {
         double ratio = 0.0;
@@ -1025,11 +990,7 @@ __global__ __launch_bounds__(kBlock) void k_skip_stats(
             ratio = qx == 0.0 ? __builtin_huge_val() : px / qx;
         }
         if (!(static_cast<double>(ud) < ratio)) bits |= 1ull << (32 + p);
-#if !SV_SKIP_POLL
-        if (lane == 0) shared_store(&L2b[K + 1 + p], L2q);
-#endif
     }
-#if SV_SKIP_POLL
     // The decision is one atomic OR; the wave whose OR completes the request's
     // decided prefix finishes it.  The log-sums of a decided position are
     // marked words too and need not land before its OR: the finisher polls for
@@ -1057,13 +1018,6 @@ __global__ __launch_bounds__(kBlock) void k_skip_stats(
         L2pn = unmark_L2(static_cast<uint64_t>(w0));
         L2qn = n < K ? unmark_L2(static_cast<uint64_t>(w1)) : 0.0;
     }
-#else
-    if (lane == 0) shared_store(&L2b[p], L2p);
-    const int n = skip_decide(ctl, b, K, bits, lane);
-    if (n < 0) return;
-    const double L2pn = shared_load(&L2b[n]);
-    const double L2qn = n < K ? shared_load(&L2b[K + 1 + n]) : 0.0;
-#endif
     skip_finish(xl, usl, b, K, V, n, n < K ? 1 : 0, L2pn, L2qn, accept_len, out_tokens, status, rp, lane);
     skip_finished(ctl, b, lane);
 }
@@ -1111,9 +1065,7 @@ hipError_t launch_rowstats(const void *tgt, const void *drf, long long rows_t, l
 
 bool skip_supported(int K) { return K <= kSkipMaxK; }
 
-size_t skip_ctl_bytes(int B, int K) {
-    return sizeof(uint64_t) * B + sizeof(unsigned) * static_cast<size_t>(B) * (K + 1) + 2 * sizeof(unsigned) * B;
-}
+size_t skip_ctl_bytes(int B, int) { return sizeof(uint64_t) * B + sizeof(unsigned) * static_cast<size_t>(B); }
 
 hipError_t clear_words(void *base, size_t bytes, hipStream_t s) {
     const long long words = static_cast<long long>(bytes / sizeof(uint32_t));
@@ -1124,18 +1076,10 @@ hipError_t clear_words(void *base, size_t bytes, hipStream_t s) {
     return hipGetLastError();
 }
 
-void skip_ctl_carve(void *base, int B, int K, SkipCtl *ctl) {
-    char *q = static_cast<char *>(base);
-    ctl->mask = reinterpret_cast<uint64_t *>(q);
-    ctl->ticket = reinterpret_cast<unsigned *>(ctl->mask + B);
-    ctl->won = ctl->ticket + static_cast<size_t>(B) * (K + 1);
-    ctl->finished = ctl->won + B;
+void skip_ctl_carve(void *base, int B, int, SkipCtl *ctl) {
+    ctl->mask = static_cast<uint64_t *>(base);
+    ctl->finished = reinterpret_cast<unsigned *>(ctl->mask + B);
     ctl->lim = ctl->finished + B;  // past skip_ctl_bytes: only the greedy chain's words hold it
-}
-
-hipError_t skip_ctl_init(void *base, int B, int K, SkipCtl *ctl, hipStream_t s) {
-    skip_ctl_carve(base, B, K, ctl);
-    return clear_words(base, skip_ctl_bytes(B, K), s);
 }
 
 hipError_t launch_skip(const void *tgt, const void *drf, const int32_t *drafts, const float *ua,
@@ -1144,7 +1088,6 @@ hipError_t launch_skip(const void *tgt, const void *drf, const int32_t *drafts, 
                        int32_t *accept_len, int32_t *out_tokens, int32_t *status, ResidParam *rp,
                        hipStream_t s) {
     SkipCtl ctl;
-#if SV_SKIP_POLL
     // the partials, the log-sums and the control words are marked words that
     // start at 0; the workspace holds them in that order, back to back
     skip_ctl_carve(ctl_base, B, K, &ctl);
@@ -1154,9 +1097,6 @@ hipError_t launch_skip(const void *tgt, const void *drf, const int32_t *drafts, 
         reinterpret_cast<char *>(L2) > static_cast<char *>(ctl_base))
         return hipErrorInvalidValue;
     hipError_t e = clear_words(first, static_cast<size_t>(end - first), s);
-#else
-    hipError_t e = skip_ctl_init(ctl_base, B, K, &ctl, s);
-#endif
     if (e != hipSuccess) return e;
     trace_select(SV_K_SKIP_STATS);
 #define SV_SK(E, A) skip_stats_t<E, A>(tgt, drf, drafts, ua, us, B, K, V, g, sc, part_R, part_s, L2, ctl, accept_len, out_tokens, status, rp, s)

@@ -21,9 +21,7 @@
 // decided without one; the decider whose OR turned that prefix from undecided
 // to decided (exactly one can: see skip_prefix) finishes the request and
 // raises the flag.  Rows of positions after the first rejection are read only
-// by waves that started before the decision was known.  The forms with a
-// per-(b, p) ticket and a compare-and-swap for the finisher remain as
-// compile-time alternatives (SV_SKIP_POLL, SV_SKIP_FASTDECIDE).
+// by waves that started before the decision was known.
 #pragma once
 
 #include "sv_device.hpp"
@@ -36,17 +34,11 @@ namespace sv {
 constexpr int kSkipMaxK = 31;
 
 struct SkipCtl {
-    unsigned *ticket;    // [B*(K+1)] segments finished per (request, position)
     uint64_t *mask;      // [B] decided | rejected << 32
-    unsigned *won;       // [B] 1 once a decider has claimed finishing the request
     unsigned *finished;  // [B] raised after the request's outputs are written
     unsigned *lim;       // [B] last position whose row can be needed, from row samples (greedy
                          // chain only, whose workspace holds B more words than skip_ctl_bytes)
 };
-
-// Carves the control words of a B x K chain out of `base` (skip_ctl_bytes
-// bytes, 8-byte aligned) and enqueues the launch that zeroes them.
-hipError_t skip_ctl_init(void *base, int B, int K, SkipCtl *ctl, hipStream_t s);
 
 // True once a draft before position p is known rejected: only the rows up to
 // a chain's first rejection are ever needed, so the rows of position p are
@@ -153,37 +145,6 @@ __device__ __forceinline__ int skip_prefix(uint64_t m, int K) {
     }
     const unsigned all = K == 31 ? 0xffffffffu : ((1u << (K + 1)) - 1u);
     return (decided & all) == all ? K : -1;
-}
-
-// Records position p's decision `bits` (1 << p, plus 1 << (32 + p) for a
-// rejection) in request b's mask, once this wave's shared stores are complete.
-// Returns the request's accepted length n when this wave completes the decided
-// prefix and wins the right to finish the request; -1 otherwise.  Uniform.
-__device__ __forceinline__ int skip_decide(const SkipCtl &ctl, int b, int K, uint64_t bits, int lane) {
-    wait_own_stores();
-    uint64_t old = 0;
-    if (lane == 0) old = __hip_atomic_fetch_or(&ctl.mask[b], bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const uint64_t m = uniform(static_cast<uint64_t>(__shfl(static_cast<long long>(old), 0, kWave))) | bits;
-    const unsigned decided = static_cast<unsigned>(m), rejected = static_cast<unsigned>(m >> 32);
-    int n = -1;
-    if (rejected) {
-        const int rj = __ffs(static_cast<int>(rejected)) - 1;
-        const unsigned below = rj == 0 ? 0u : (0xffffffffu >> (32 - rj));
-        if ((decided & below) == below) n = rj;
-    } else {
-        const unsigned all = K == 31 ? 0xffffffffu : ((1u << (K + 1)) - 1u);
-        if ((decided & all) == all) n = K;
-    }
-    if (n < 0) return -1;
-    unsigned lost = 1;
-    if (lane == 0) {
-        unsigned expect = 0;
-        lost = __hip_atomic_compare_exchange_strong(&ctl.won[b], &expect, 1u, __ATOMIC_RELAXED,
-                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                   ? 0u
-                   : 1u;
-    }
-    return uniform(static_cast<unsigned>(__shfl(static_cast<int>(lost), 0, kWave))) != 0 ? -1 : n;
 }
 
 // Raises request b's flag once this wave's output stores are complete.

@@ -152,7 +152,7 @@ sv_status spec_verify_sample(const void *target_logits, const void *draft_logits
  * The array of the current device is used, so `stream` must belong to the
  * current device.  Sizes whose workspace (sv_sample_workspace_bytes) exceeds
  * SV_NOALLOC_SCRATCH_BYTES return SV_ERR_SCRATCH and launch nothing; at
- * V = 151936 bf16 and K = 7 that admits B up to 1180.
+ * V = 151936 bf16 and K = 7 that admits B up to 1186.
  *
  * Every call on one device shares that device's array, which keeps the last
  * call's contents (the kernels clear what must start at zero themselves):
