@@ -24,7 +24,9 @@ accepted nodes.
 
 Beside the step the JSON line reports: the step replayed as one HIP graph, with
 each mode on a stream of its own, and without lse outputs; each call alone
-(back to back, and cold after a cache-evicting write); the device's read
+(back to back, and cold after a cache-evicting write), and the greedy chain and
+tree again with their mismatching drafts replaced by each row's second-best
+token (rejections no row sample can show); the device's read
 ceiling; the CPU oracle on the same step; and extras outside the step (the tree
 KV commit, lexical retrieval, and the fused LM-head forms beside their unfused
 counterparts).
@@ -382,6 +384,76 @@ def bench_greedy_b512(sv, torch, workloads, dev, per_call, with_cold, reps):
     with_cold(entry, call, nbytes, rows)
     del t
     return entry
+
+
+def bench_plausible(sv, torch, calls, evict, bytes_greedy, bytes_tree, reps):
+    """The step's greedy chain and tree with every mismatching draft (or node
+    token) replaced by the second-best token of its row.  A 512-logit sample of
+    the row cannot rule such a token out, so the preparing launches find no
+    rejection and every one is found by a row's full decision, as with drafts
+    from a real model that miss with a plausible token.  The accepted lengths,
+    and the bytes the rule needs, are those of the step's inputs.  Cold calls
+    (an evicting write before each); kernel medians from the library's tracer."""
+    import numpy as np
+
+    def first_second(t):
+        f = t.float()
+        a = torch.argmax(f, dim=-1)  # first maximum
+        f.scatter_(-1, a.unsqueeze(-1), -float("inf"))
+        b = torch.argmax(f, dim=-1)
+        del f
+        return a.to(torch.int32), b.to(torch.int32)
+
+    P = lambda a: ctypes.c_void_p(a.data_ptr())
+    out = {}
+    # greedy chain
+    a, b2 = first_second(calls.g_t)
+    K = calls.w4.K
+    x = calls.g_x
+    x2 = torch.where(x != a[:, :K], b2[:, :K], x).contiguous()
+    g_args = list(calls.greedy_args)
+    g_args[1] = P(x2)
+    # tree
+    ta, tb = first_second(calls.t_t)
+    par = calls.t_par.long().clamp(min=0)
+    pa, pb = torch.gather(ta, 1, par), torch.gather(tb, 1, par)
+    tok = calls.t_tok
+    col = torch.arange(tok.shape[1], device=tok.device).unsqueeze(0)
+    tok2 = torch.where((tok != pa) & (col > 0), pb, tok).contiguous()
+    t_args = list(calls.tree_args)
+    t_args[1] = P(tok2)
+    del a, b2, ta, tb
+    for name, fn_name, args, kernel, nbytes, n_buf in (
+            ("greedy", "spec_verify_greedy", g_args, "skip_argmax", bytes_greedy, calls.g_n),
+            ("tree", "spec_verify_tree", t_args, "skip_tree", bytes_tree, calls.t_n)):
+        fn = getattr(calls.lib, fn_name)
+        getattr(calls, name)()  # the step's inputs: the reference accepted lengths
+        torch.cuda.synchronize()
+        ref = n_buf.clone()
+        rc = fn(*args)
+        torch.cuda.synchronize()
+        if rc or not torch.equal(n_buf, ref):
+            raise RuntimeError(f"{name} with plausible mismatches: rc {rc} or accepted lengths differ")
+        kt, ct = [], []
+        for i in range(reps):
+            evict.fill_(i & 0xFF)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            sv.trace_begin(8, kernels=(kernel,))
+            e0.record()
+            fn(*args)
+            e1.record()
+            torch.cuda.synchronize()
+            kt += [ms for _, ms in sv.trace_end(8)]
+            ct.append(e0.elapsed_time(e1))
+        km = float(np.median(kt))
+        out[name] = {"kernel": kernel, "kernel_median_ms": round(km, 5),
+                     "cold_call_median_ms": round(float(np.median(ct)), 5), "bytes_needed": nbytes,
+                     "gbps_needed": round(nbytes / (km * 1e-3) / 1e9, 1),
+                     "frac_of_peak": round(nbytes / (km * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+    calls.greedy()  # leave the step's outputs in the buffers
+    calls.tree()
+    torch.cuda.synchronize()
+    return out
 
 
 def bench_vocab_shard(sv, torch, workloads, dev, per_call, with_cold, reps):
@@ -1051,6 +1123,9 @@ def main():
                 fn, bytes_mode[name], rows_mode[name])
     if "greedy" in active:
         calls_alone["greedy_b512"] = bench_greedy_b512(sv, torch, workloads, dev, per_call, with_cold, reps)
+    if "greedy" in active and "tree" in active:
+        calls_alone["plausible_mismatches"] = bench_plausible(sv, torch, calls, evict, bytes_mode["greedy"],
+                                                              bytes_mode["tree"], max(30, reps // 4))
     small_outputs = {}
     if "sample" in active:
         small, small_outputs = bench_small_samples(sv, torch, workloads, dev, per_call, with_cold, reps)
