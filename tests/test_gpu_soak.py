@@ -8,8 +8,9 @@ varies what decides the rows each request needs over 200 seeds: the draft
 tokens of the greedy chain (B=256 K=7 V=151936, a draft equals its row's
 argmax with probability 0.8), the node tokens and extra leaves of the tree
 (B=64 N=33), and the uniforms of the stochastic chain without lse outputs
-(B=256 K=7 T=0.7).  Every call is compared with the oracle, and each test
-stops at its first mismatch.  No known failure is targeted.
+(B=256 K=7 T=0.7); and, for the chain and tree passes' sampled rejections,
+1000 seeded random shapes.  Every call is compared with the oracle, and each
+test stops at its first mismatch.  No known failure is targeted.
 """
 
 import numpy as np
@@ -67,3 +68,46 @@ def test_soak_stochastic_chain_without_lse(half):
         o = oracle.verify_sample(w.target, w.draft, w.draft_tokens, w.u_accept, w.u_sample, w.T, lse=False)
         ncmp, nflag, _ = check_sample(w, gpu_sample(w, lse=False), o)
         assert ncmp >= 1
+
+
+def test_soak_sampled_rejections_random_shapes():
+    # The chain and tree passes settle some rejections before streaming, from a
+    # 512-logit sample of each row.  1000 seeded random shapes (batch,
+    # vocabulary, dtype, draft length or tree acceptance), half of them with
+    # every mismatching token replaced by its row's second-best token, which
+    # no sample can rule out; every call is compared with the oracle.
+    rng = np.random.default_rng(20261303)
+    for i in range(1000):
+        mode = ("greedy", "tree")[i % 2]
+        B = int(rng.choice([1, 2, 5, 16, 33, 64, 128]))
+        V = int(rng.choice([7, 100, 513, 1000, 4099, 8192, 20011, 65536]))
+        dt = str(rng.choice(["f32", "bf16"]))
+        seed = int(rng.integers(1 << 30))
+        plausible = bool(rng.integers(0, 2))
+        if i % 100 == 0:
+            note(f"soak sampled rejections case {i}")
+        if mode == "greedy":
+            K = int(rng.choice([0, 1, 3, 7, 15, 31]))
+            w = workloads.make_greedy(B, K, V, dt, seed=seed, p_match=float(rng.choice([0.0, 0.5, 0.8, 1.0])))
+        else:
+            w = workloads.make_tree(B, V, dt, seed=seed, p_match=float(rng.choice([0.0, 0.3, 0.7, 1.0])))
+        if plausible:
+            L = workloads.bf16_bits_to_f32(w.target) if dt == "bf16" else w.target
+            first = L.argmax(-1)
+            masked = L.copy()
+            np.put_along_axis(masked, first[..., None], -np.inf, -1)
+            second = masked.argmax(-1)
+            if mode == "greedy" and K > 0:
+                x = w.draft_tokens
+                w.draft_tokens = np.where(x != first[:, :K], second[:, :K], x).astype(np.int32)
+            elif mode == "tree":
+                pp = np.maximum(w.parents, 0)
+                pa, pb = np.take_along_axis(first, pp, 1), np.take_along_axis(second, pp, 1)
+                col = np.arange(w.N)[None, :]
+                w.node_tokens = np.where((w.node_tokens != pa) & (col > 0), pb, w.node_tokens).astype(np.int32)
+        if mode == "greedy":
+            check_exact(gpu_greedy(w), oracle.verify_greedy(w.target, w.draft_tokens),
+                        ("accept_len", "tokens", "status"))
+        else:
+            check_exact(gpu_tree(w), oracle.verify_tree(w.target, w.node_tokens, w.parents),
+                        ("accept_len", "path", "tokens", "status"))
