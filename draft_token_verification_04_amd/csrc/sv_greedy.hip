@@ -532,9 +532,8 @@ __global__ __launch_bounds__(kBlock) void k_chain_prep(const typename E::storage
 // the decisions about a level have usually landed before the next level's
 // waves start (in plain index order, a deep chain listed early would be read
 // before its first node is decided).  A wave skips its segment when the node of
-// its slot is already known rejected.  The first wave of a row rejects the
-// children whose token keys its segment beats; the last wave of a row takes
-// its argmax a_j, marks the row done, and rejects every child
+// its slot is already known rejected.  The last wave of a row takes its
+// argmax a_j, marks the row done, and rejects every child
 // whose token differs from a_j together with the descendants of every rejected
 // node (parents, tokens and states of the request's nodes held one per lane,
 // the rejection closed over the tree by ballots).  Each node is resolved once -
@@ -547,7 +546,6 @@ constexpr unsigned kRowDone = 1u, kRejected = 2u;
 constexpr int kTreeSkipMaxN = kWave;
 
 struct TreeCtl {
-    uint64_t *ckey;      // [B*N] argmax key of each node's token in its parent's row
     unsigned *state;     // [B*N] kRowDone | kRejected of the node in each slot
     unsigned *resolved;  // [B] nodes resolved
     int32_t *order;      // [B*N] node of each slot (ascending depth, then index)
@@ -665,14 +663,6 @@ __global__ __launch_bounds__(kBlock) void k_tree_prep(const typename E::storage 
         ctl.order[base + rk] = lane;
         ctl.rank[base + lane] = rk;
         ctl.state[base + rk] = is_dead ? kRejected : 0u;
-        // the key of the node's token in its parent's row, tested by the
-        // parent row's first segment (a rejected node needs no second test)
-        uint64_t ck = 0;
-        if (is_dead || !pv)
-            ck = ~0ull;
-        else if (tv)
-            ck = argmax_key(from_bits<E>(xb), t);
-        ctl.ckey[base + lane] = ck;
     }
     if (lane == 0) {
         ctl.resolved[b] = static_cast<unsigned>(ndead);
@@ -791,12 +781,6 @@ __device__ __forceinline__ void tree_mark(uint64_t rej, int done, int p, int t, 
     tree_finish(p, t, rk, amax, ctl, b, N, V, accept_len, path_nodes, out_tokens, status, lane);
 }
 
-// Whether the first segment of each node's row rejects the node's children
-// whose tokens it already beats, before the row's last segment decides.
-#ifndef SV_TREE_EARLY
-#define SV_TREE_EARLY 1
-#endif
-
 template <typename E, bool ALIGNED, int U>
 __global__ __launch_bounds__(kBlock) void k_skip_tree(const typename E::storage *__restrict__ L,
                                                       const int32_t *__restrict__ tok,
@@ -827,19 +811,15 @@ __global__ __launch_bounds__(kBlock) void k_skip_tree(const typename E::storage 
     const long long row = base + j;
     int v0, v1;
     skip_segment(sg, nvec, segs, v0, v1);
-    // the row's last segment decides node j's children, and its first may
-    // reject some of them sooner: the request's parents, tokens and slot ranks
-    // (one node per lane), and for the first segment the keys of the nodes'
-    // tokens in their parents' rows, are fetched before the segment's loads
+    // the row's last segment decides node j's children: the request's
+    // parents, tokens and slot ranks (one node per lane) are fetched before
+    // the segment's loads
     const bool in = lane < N;
-    const bool early = SV_TREE_EARLY && sg == 0 && segs > 1;
     int p = -1, t = 0, rk = 0;
-    uint64_t ck = ~0ull;
-    if ((sg == segs - 1 || early) && in) {
+    if (sg == segs - 1 && in) {
         p = par[base + lane];
         t = tok[base + lane];
         rk = ctl.rank[base + lane];
-        if (early) ck = ctl.ckey[base + lane];
     }
     const uint64_t key = segment_argmax_chunked<E, ALIGNED, U, kGSkipChunks>(L + row * V, V, v0, v1, lane);
     // keys handed to the row's last segment as in the chain pass (the prep
@@ -847,13 +827,6 @@ __global__ __launch_bounds__(kBlock) void k_skip_tree(const typename E::storage 
     // already rejected, which this wave then finds too
     if (sg != segs - 1) {
         if (lane == 0) shared_store(&part_k[row * segs + sg], key);
-        // a child of j whose token's key this segment beats is not the row's
-        // argmax, so the decision will reject it: mark it now
-        if (early) {
-            const uint64_t rej = ballot(in && lane > 0 && p == j && key > ck);
-            if (rej) tree_mark(rej, -1, p, t, rk, amax, ctl, b, N, V, accept_len, path_nodes, out_tokens, status,
-                               lane);
-        }
         return;
     }
     uint64_t mk = key;
@@ -977,9 +950,7 @@ hipError_t launch_skip_match(const void *L, const int32_t *drafts, int B, int K,
 
 bool tree_skip_supported(int N) { return N <= kTreeSkipMaxN; }
 
-size_t tree_ctl_bytes(int B, int N) {
-    return sizeof(uint64_t) * static_cast<size_t>(B) * N + sizeof(unsigned) * (3 * static_cast<size_t>(B) * N + 2 * B);
-}
+size_t tree_ctl_bytes(int B, int N) { return sizeof(unsigned) * (3 * static_cast<size_t>(B) * N + 2 * static_cast<size_t>(B)); }
 
 hipError_t launch_skip_tree(const void *L, const int32_t *node_tokens, const int32_t *parents, int B, int N,
                             int V, const RowGeom &g, sv_dtype dt, uint64_t *part_k, int32_t *amax,
@@ -987,8 +958,7 @@ hipError_t launch_skip_tree(const void *L, const int32_t *node_tokens, const int
                             int32_t *status, hipStream_t s) {
     TreeCtl ctl;
     const size_t bn = static_cast<size_t>(B) * N;
-    ctl.ckey = static_cast<uint64_t *>(ctl_base);
-    ctl.state = reinterpret_cast<unsigned *>(ctl.ckey + bn);
+    ctl.state = static_cast<unsigned *>(ctl_base);
     ctl.order = reinterpret_cast<int32_t *>(ctl.state + bn);
     ctl.rank = ctl.order + bn;
     ctl.resolved = reinterpret_cast<unsigned *>(ctl.rank + bn);
